@@ -1,0 +1,91 @@
+"""Host-side generators for every input of the five workloads.
+
+Distributions (the workloads' recipe): activations x ~ N(0,1) rounded to bf16;
+router logits ~ N(0,1) fp32; shared-expert gate logit z ~ N(0,1) fp32;
+codes ~ U{0..15}; scales ~ U(0.005, 0.02) bf16; biases ~ U(-0.1, 0.1) bf16;
+GDN state S ~ N(0, 0.1^2) fp32; q, k ~ N(0,1) then L2-normalised per (row,
+head); v ~ N(0,1); beta = sigmoid(N(0,1)); g = exp(-softplus(N(0,1)));
+accepted prefix j ~ U{0..k}.
+"""
+
+from collections import namedtuple
+
+import numpy as np
+
+from .counter import SEED, derive_key, q4_rows, bf16_bits_from_f32
+
+BankKeys = namedtuple("BankKeys", "codes scales biases")
+
+# bank kinds (part of the stream keys)
+DENSE_W, GATEUP, DOWN, SHARED_GATEUP, SHARED_DOWN = 0, 1, 2, 3, 4
+# tensor ids (part of the numpy seeds)
+T_X, T_LOGITS, T_Z, T_S, T_Q, T_K, T_V, T_G, T_BETA, T_J = 10, 11, 12, 20, 21, 22, 23, 24, 25, 30
+
+
+def bank_keys(cfg_id, kind, layer):
+    return BankKeys(*(derive_key(cfg_id, kind, layer, part) for part in (1, 2, 3)))
+
+
+def _rng(*ids):
+    return np.random.default_rng([SEED, *[int(i) for i in ids]])
+
+
+def dense_weight(cfg_id, kind, layer, n, k):
+    """A full dense Q4 matrix ``[N, K]`` (E = 1) as host arrays."""
+    return q4_rows(bank_keys(cfg_id, kind, layer), 1, n, k, expert=0)
+
+
+def bf16_normal(rng, shape):
+    return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+
+
+def moe_layer_inputs(cfg_id, layer, rows, hidden, experts, step=0):
+    """x (bf16 bits [rows, hidden]), router logits (fp32 [rows, E]) and the
+    shared-expert gate logit z (fp32 [rows]) of one MoE layer."""
+    x = bf16_normal(_rng(cfg_id, T_X, layer, step), (rows, hidden))
+    logits = _rng(cfg_id, T_LOGITS, layer, step).standard_normal((rows, experts), dtype=np.float32)
+    z = _rng(cfg_id, T_Z, layer, step).standard_normal((rows,), dtype=np.float32)
+    return {"x": x, "logits": logits, "z": z}
+
+
+def gdn_state(cfg_id, layer, hv, dv, dk):
+    s = 0.1 * _rng(cfg_id, T_S, layer).standard_normal((hv, dv, dk))
+    return s.astype(np.float32)
+
+
+def _l2n(a):
+    return a / np.sqrt(np.sum(a * a, axis=-1, keepdims=True))
+
+
+def gdn_layer_inputs(cfg_id, layer, rows, hv, hk, dk, dv, step=0):
+    """Per-row GDN inputs of one layer: q, k fp32 [rows, Hk, Dk] (unit norm per
+    head), v fp32 [rows, Hv, Dv], g and beta fp32 [rows, Hv]."""
+    q = _l2n(_rng(cfg_id, T_Q, layer, step).standard_normal((rows, hk, dk))).astype(np.float32)
+    k = _l2n(_rng(cfg_id, T_K, layer, step).standard_normal((rows, hk, dk))).astype(np.float32)
+    v = _rng(cfg_id, T_V, layer, step).standard_normal((rows, hv, dv)).astype(np.float32)
+    a = _rng(cfg_id, T_G, layer, step).standard_normal((rows, hv))
+    g = np.exp(-np.logaddexp(0.0, a)).astype(np.float32)
+    b = _rng(cfg_id, T_BETA, layer, step).standard_normal((rows, hv))
+    beta = (1.0 / (1.0 + np.exp(-b))).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta}
+
+
+def accepted_prefix(cfg_id, step, rows):
+    """Accepted-prefix length j ~ U{0..rows} for one verify step."""
+    return int(_rng(cfg_id, T_J, step).integers(0, rows + 1))
+
+
+def integer_exact_weight(seed, n, k, rows):
+    """A Q4 matrix and activations whose products and sums are exact in fp32.
+
+    scale = 2^-6, bias = m * 2^-6 with m in [-6, 6], x integers in [-8, 8]:
+    every partial sum is a multiple of 2^-6 below 2^24 * 2^-6 in magnitude,
+    so any summation order gives the same fp32 result."""
+    rng = np.random.default_rng([SEED, 99, seed])
+    g = k // 64
+    codes = rng.integers(0, 1 << 32, size=(n, k // 8), dtype=np.uint64).astype(np.uint32)
+    scales = np.full((n, g), 0x3C80, dtype=np.uint16)            # bf16 of 2^-6
+    m = rng.integers(-6, 7, size=(n, g)).astype(np.float32)
+    biases = bf16_bits_from_f32(m * np.float32(2.0 ** -6))
+    x = bf16_bits_from_f32(rng.integers(-8, 9, size=(rows, k)).astype(np.float32))
+    return codes, scales, biases, x

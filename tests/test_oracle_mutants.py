@@ -1,0 +1,58 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is a textual edit of oracle/ref.py (a dropped term, a wrong sign,
+index or order, a transposed operand), loaded as a separate module on the
+CPU.  The real oracle is never modified."""
+
+import os
+import types
+
+import pytest
+
+from tests.oracle_pins import ALL_CHECKS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "ref.py")
+
+MUTANTS = {
+    "nibble_order_reversed": ("(4 * np.arange(8, dtype=np.uint32))", "(28 - 4 * np.arange(8, dtype=np.uint32))"),
+    "bias_dropped": ("return s * q + b", "return s * q"),
+    "bias_sign": ("return s * q + b", "return s * q - b"),
+    "scale_bias_swapped": ("s = np.repeat(bf16_to_f64(scales)", "s = np.repeat(bf16_to_f64(biases)"),
+    "group_of_32": ("GROUP = 64", "GROUP = 32"),
+    "tie_to_higher_index": ("np.lexsort((np.arange(e), -l[r]))", "np.lexsort((-np.arange(e), -l[r]))"),
+    "softmax_unnormalised": ("p = ex / ex.sum()", "p = ex"),
+    "renorm_dropped": ("w[r] = w[r] / w[r].sum()", "w[r] = w[r]"),
+    "sigmoid_sign": ("p = 1.0 / (1.0 + np.exp(-l[r]))", "p = 1.0 / (1.0 + np.exp(l[r]))"),
+    "union_rows_descending": ("        for r in range(k):\n            hits", "        for r in reversed(range(k)):\n            hits"),
+    "swiglu_gate_up_swapped": ("return silu(a[..., :i]) * a[..., i:]", "return silu(a[..., i:]) * a[..., :i]"),
+    "combine_slot_mismatch": ("y[r] = y[r] + w[r, s] * partial[r, s]", "y[r] = y[r] + w[r, topk - 1 - s] * partial[r, s]"),
+    "shared_gate_dropped": ("y[r] = y[r] + gate[r] * shared[r]", "y[r] = y[r] + shared[r]"),
+    "gdn_update_transposed": ("np.outer(delta, kt)", "np.outer(kt, delta)"),
+    "gdn_decay_dropped": ("S[h] = g[t, h] * S[h]", "S[h] = S[h]"),
+    "gdn_head_interleaved": ("c = h // ratio", "c = h % hk"),
+    "gdn_delta_sign": ("delta = beta[t, h] * (v[t, h] - m)", "delta = beta[t, h] * (v[t, h] + m)"),
+    "gdn_beta_misplaced": ("delta = beta[t, h] * (v[t, h] - m)", "delta = beta[t, h] * v[t, h] - m"),
+    "gdn_readout_before_update": ("y[t, h] = S[h] @ qt", "y[t, h] = (S[h] - np.outer(delta, kt)) @ qt"),
+    "gdn_kvmem_uses_q": ("m = S[h] @ kt", "m = S[h] @ qt"),
+    "rollback_off_by_one": ("else np.array(snaps[j - 1], copy=True)", "else np.array(snaps[min(j, rows - 1)], copy=True)"),
+}
+
+
+def _load(old, new):
+    src = open(SRC).read()
+    assert old in src, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load(*MUTANTS[name])
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:  # AssertionError, or a crash from a broken shape
+            failed.append(check.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
