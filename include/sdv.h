@@ -1,0 +1,232 @@
+/*
+ * sdv.h -- C ABI of libsdv: exact k-row speculative-verification kernels for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one verification step of a Gated-DeltaNet / MoE
+ * hybrid layer for k = 1..9 draft rows at once:
+ *
+ *   - affine-Q4 (group 64, bf16 scale and bias) multi-row matvec that decodes
+ *     each packed weight once for all k rows, dense and gathered-expert
+ *     (top-k of E experts, fused gate/up with SwiGLU) -- the exact multi-row
+ *     projection and gathered-expert kernels of the mere.run transfer report
+ *     ("Flash-Next optimization transfer to Ornith and Qwen 27B", sections
+ *     "Shared architecture and implemented paths" and "Exact verification
+ *     kernels and benchmark admission") and Red Lite dev45's two-vector
+ *     kernels, router dispatch and merged experts ("What it is");
+ *   - the multi-row Gated DeltaNet delta-rule recurrence on an fp32
+ *     [Hv, Dv, Dk] state with a snapshot after every row, and rollback to the
+ *     accepted prefix by selecting a snapshot (Flash-Next plan QWEN38FLASH.md,
+ *     "2.1 Gated DeltaNet"; Red Lite dev45, "What it is": in-kernel snapshots
+ *     and pointer-swap rejection).
+ *
+ * Conventions for every entry point
+ *   - Return value: SDV_OK (0) or a negative SDV_E* status.  Arguments are
+ *     validated on the host before any launch; on error nothing is launched
+ *     and no device memory is written.  sdv_last_error() gives a message for
+ *     the calling thread's most recent failure.
+ *   - Pointers named "device" are device memory owned by the caller; the
+ *     library never allocates or frees device memory and keeps no pointer
+ *     after a call returns.  Device pointers must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  Results are visible after the stream reaches the
+ *     call.  Calls are reentrant; two calls whose outputs overlap race.
+ *   - Row width k must be 1..SDV_MAX_ROWS (9), the widths the pages verify.
+ *   - Every row of a width-k call is bit-identical to the same row computed
+ *     by a width-1 call (fixed per-output reduction order, independent of k
+ *     and of which other rows share an expert).
+ *   - bf16 values are passed as their uint16_t bit patterns.
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef SDV_API
+#define SDV_API __attribute__((visibility("default")))
+#endif
+
+typedef void *sdv_stream_t; /* hipStream_t */
+
+/* status codes */
+#define SDV_OK 0
+#define SDV_EINVAL (-1)  /* null pointer, bad shape or count, misaligned pointer */
+#define SDV_EWIDTH (-2)  /* k outside 1..SDV_MAX_ROWS */
+#define SDV_ELAYOUT (-3) /* group != 64, K % 64 != 0, unsupported head dim or fused layout */
+#define SDV_ERANGE (-4)  /* accepted prefix outside 0..k, topk outside 1..min(E,16), E > 1024 */
+#define SDV_EALIAS (-5)  /* an output overlaps an input or another output */
+#define SDV_EHIP (-6)    /* the HIP runtime reported an error at launch */
+
+#define SDV_MAX_ROWS 9
+#define SDV_GROUP 64
+#define SDV_MAX_EXPERTS 1024
+#define SDV_MAX_TOPK 16
+
+/* product modes */
+#define SDV_MODE_PLAIN 0         /* y[r, n] = W[n, :] . a[r, :] */
+#define SDV_MODE_GATEUP_SWIGLU 1 /* W rows [0, N/2) gate, [N/2, N) up: y[r, i] = silu(gate_i) * up_i */
+
+/* activation types */
+#define SDV_ACT_BF16 0 /* bf16 bits */
+#define SDV_ACT_F32 1  /* fp32 */
+
+/* router score functions */
+#define SDV_ROUTE_SOFTMAX 0 /* softmax over all E logits */
+#define SDV_ROUTE_SIGMOID 1 /* independent sigmoid per logit */
+
+/*
+ * An affine-Q4, group-64 weight: E matrices of N rows by K inputs.
+ *   codes  [E][N][K/8] uint32: element 8w+i of a row in bits [4i, 4i+4) of word w,
+ *          an unsigned code q in 0..15
+ *   scales [E][N][K/64] bf16, biases [E][N][K/64] bf16
+ *   value  W[e][n][c] = scales[e][n][c/64] * q + biases[e][n][c/64]
+ * E = 1 is a dense matrix.  group must be 64 and K a positive multiple of 64.
+ * (mere.run transfer report, "Shared architecture and implemented paths":
+ * affine Q4, group size 64, compatible bf16 tensors; the nibble order is this
+ * library's definition.)
+ */
+typedef struct sdv_q4 {
+  const uint32_t *codes;
+  const uint16_t *scales;
+  const uint16_t *biases;
+  int32_t E, N, K, group;
+} sdv_q4;
+
+/*
+ * sdv_qmv_k -- dense multi-row affine-Q4 matvec (E must be 1).
+ * The width-k product decodes each weight once for all k rows; each row
+ * equals the width-1 result bit for bit (mere.run report, "Exact verification
+ * kernels and benchmark admission": small-batch Q4 kernel against serial QMV
+ * with exact agreement at widths 4, 8, 9; Red Lite dev45 "What it is": decode
+ * each weight once and compute each row in the 1-row kernel's order).
+ *   W         weight descriptor (host struct, device arrays)
+ *   act       device, [k][K]: bf16 bits (act_dtype SDV_ACT_BF16) or fp32 (SDV_ACT_F32)
+ *   k         rows, 1..9
+ *   mode      SDV_MODE_PLAIN: y [k][N];  SDV_MODE_GATEUP_SWIGLU: N even, y [k][N/2]
+ *   y         device fp32 output
+ * Errors: EINVAL, EWIDTH, ELAYOUT, EALIAS, EHIP.
+ */
+SDV_API int sdv_qmv_k(const sdv_q4 *W, const void *act, int act_dtype, int k, int mode, float *y,
+              sdv_stream_t stream);
+
+/*
+ * sdv_moe_route_k -- one router dispatch for all k rows: per-row top-k, the
+ * routing weights, the union of the rows' experts and the (expert, row, slot)
+ * pairs, all on the device with no host synchronisation (Red Lite dev45,
+ * "What it is": one router dispatch for both rows; "Scope boundary": the
+ * union of the rows' experts; Flash-Next plan "2.3 MoE": top-10 of 512).
+ *   logits     device fp32 [k][E]
+ *   score_mode SDV_ROUTE_SOFTMAX (over all E) or SDV_ROUTE_SIGMOID
+ *   renorm     nonzero: weights divided by their sum over the row's top-k
+ *   idx        device int32 [k][topk]: experts by logit descending, ties to the lower index
+ *   w          device fp32 [k][topk]: weight of each slot
+ *   union_ids  device int32 [k*topk]: distinct experts ascending (first n_union valid)
+ *   n_union    device int32 [1]
+ *   pair_off   device int32 [k*topk + 1]: pairs of union entry u are [pair_off[u], pair_off[u+1])
+ *   pair_row, pair_slot  device int32 [k*topk]: ordered by (expert, row) ascending
+ * E in topk..1024, topk in 1..16.  Errors: EINVAL, EWIDTH, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_moe_route_k(const float *logits, int k, int E, int topk, int score_mode, int renorm,
+                    int32_t *idx, float *w, int32_t *union_ids, int32_t *n_union,
+                    int32_t *pair_off, int32_t *pair_row, int32_t *pair_slot,
+                    sdv_stream_t stream);
+
+/*
+ * sdv_gather_qmv_k -- multi-row affine-Q4 product over the union of the rows'
+ * experts: each union expert's weights are decoded once for all rows routed
+ * to it (mere.run report, "Exact verification kernels and benchmark
+ * admission": gathered expert kernel, affine Q4/group 64, widths 2..9, fused
+ * gate/up weights, unsupported layouts rejected; Red Lite dev45: the (expert,
+ * row) pairs share one pool encode with a two-input gate/up pipeline).
+ *   bank       weight descriptor, E experts of [N][K]
+ *   mode       SDV_MODE_GATEUP_SWIGLU (fused [gate; up] rows, output N/2) or SDV_MODE_PLAIN
+ *   act        device: SDV_ACT_BF16 shared rows [k][K] (row r's input for every slot),
+ *              or SDV_ACT_F32 per pair [k][topk][K] (e.g. the SwiGLU output)
+ *   union_ids, n_union, pair_off, pair_row, pair_slot  device, as written by sdv_moe_route_k
+ *   out        device fp32 [k][topk][N or N/2]; entry (r, s) holds expert idx[r][s]'s output
+ * The grid covers k*topk union entries and entries past n_union exit; expert
+ * ids, rows and slots outside their ranges are skipped on the device.
+ * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_gather_qmv_k(const sdv_q4 *bank, int mode, const void *act, int act_dtype,
+                     const int32_t *union_ids, const int32_t *n_union, const int32_t *pair_off,
+                     const int32_t *pair_row, const int32_t *pair_slot, int k, int topk,
+                     float *out, sdv_stream_t stream);
+
+/*
+ * sdv_moe_combine_k -- one MoE tail for all rows (Red Lite dev45, "What it
+ * is": one tail for both rows; Flash-Next plan "5.3 MoE deltas": fixed-width
+ * weighted expert sum):
+ *   y[r][n] = sum_{s = 0..topk-1, ascending} w[r][s] * partial[r][s][n]
+ *             + sigmoid(shared_logit[r]) * shared_out[r][n]
+ * shared_out may be NULL (no shared expert); shared_logit may be NULL (gate 1).
+ *   partial device fp32 [k][topk][H], w device fp32 [k][topk],
+ *   shared_out device fp32 [k][H] or NULL, shared_logit device fp32 [k] or NULL,
+ *   y device fp32 [k][H].
+ * Errors: EINVAL, EWIDTH, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_moe_combine_k(const float *partial, const float *w, const float *shared_out,
+                      const float *shared_logit, int k, int topk, int H, float *y,
+                      sdv_stream_t stream);
+
+/*
+ * sdv_gdn_verify_k -- k-row Gated DeltaNet recurrence with a state snapshot
+ * after every row (Flash-Next plan, "2.1 Gated DeltaNet": decay, kv_mem,
+ * delta, rank-1 update, readout on an fp32 [Hv, Dv, Dk] state; "3.1": per-head
+ * scalar decay and beta, each qk head shared by Hv/Hk v heads; Red Lite
+ * dev45 "What it is": row t runs from row t-1's state and the state after
+ * each row is written from inside the kernel).  For t = 0..k-1, v head h,
+ * qk head c = h / (Hv/Hk), value row i:
+ *   S_h <- g[t][h] * S_h;  m_i = sum_j S_h[i][j] k[t][c][j];
+ *   d_i = beta[t][h] * (v[t][h][i] - m_i);  S_h[i][j] += d_i * k[t][c][j];
+ *   y[t][h][i] = sum_j S_h[i][j] q[t][c][j];  snaps[t] = S.
+ *   S_in   device fp32 [Hv][Dv][Dk], read only (never written)
+ *   q, kk  device fp32 [k][Hk][Dk];  v device fp32 [k][Hv][Dv];  g, beta device fp32 [k][Hv]
+ *   y      device fp32 [k][Hv][Dv]
+ *   snaps  host array of k device pointers, each an fp32 [Hv][Dv][Dk] state;
+ *          they must not overlap S_in, the inputs, y or each other
+ * Dk must be 64 or 128; Hv a multiple of Hk.
+ * Errors: EINVAL, EWIDTH, ELAYOUT, EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_verify_k(const float *S_in, const float *q, const float *kk, const float *v,
+                     const float *g, const float *beta, int k, int Hv, int Hk, int Dk, int Dv,
+                     float *y, float *const *snaps, sdv_stream_t stream);
+
+/*
+ * sdv_gdn_rollback -- select the state for an accepted prefix of length j
+ * (mere.run report: accepted-prefix rollback, every prefix at widths 4, 8, 9;
+ * Red Lite dev45 "What it is": a rejected draft is undone by swapping the
+ * state pointers with the snapshots).  Host only, no device work:
+ *   *selected_slot = 0 (the verify call's S_in) for j = 0, else j (snaps[j-1]).
+ * Errors: EINVAL (null), EWIDTH, ERANGE (j outside 0..k).
+ */
+SDV_API int sdv_gdn_rollback(int k, int j, int *selected_slot);
+
+/*
+ * sdv_gdn_rollback_copy -- the same selection, copied into a caller-owned
+ * state at a fixed address: dst <- (j == 0 ? S_in : snaps[j-1]), state_elems
+ * floats, enqueued on `stream` (device-to-device).  dst may equal the selected
+ * source (then nothing is copied) but may not partially overlap it.
+ * Errors: EINVAL, EWIDTH, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_rollback_copy(float *dst, const float *S_in, float *const *snaps, int k, int j,
+                          size_t state_elems, sdv_stream_t stream);
+
+/* Static text for a status code. */
+SDV_API const char *sdv_status_string(int status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+SDV_API const char *sdv_last_error(void);
+
+/* Library version and build target, e.g. "sdv 0.1 gfx950". */
+SDV_API const char *sdv_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV_H */

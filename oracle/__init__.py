@@ -38,7 +38,7 @@ in the function's docstring.
 """
 
 from .ref import (bf16_to_f64, unpack_q4, dequant, qmv, route, union_pairs, silu, swiglu,
-                  moe_verify, gdn_verify, rollback)
+                  combine, moe_verify, gdn_verify, rollback)
 
 __all__ = ["bf16_to_f64", "unpack_q4", "dequant", "qmv", "route", "union_pairs", "silu",
-           "swiglu", "moe_verify", "gdn_verify", "rollback"]
+           "swiglu", "combine", "moe_verify", "gdn_verify", "rollback"]

@@ -148,6 +148,26 @@ def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
 
 
+def combine(partial, w, shared=None, z=None):
+    """MoE tail: ``y[r] = sum_s w[r, s] * partial[r, s]`` in slot order, then
+    ``+ sigmoid(z[r]) * shared[r]`` (gate 1 when ``z`` is None) when a shared
+    expert output is given.  Slot order, then the shared expert last, is our
+    reading (parity unpinned by the pages)."""
+    partial = np.asarray(partial, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    k, topk = w.shape
+    y = np.zeros((k, partial.shape[-1]), dtype=np.float64)
+    for r in range(k):
+        for s in range(topk):
+            y[r] = y[r] + w[r, s] * partial[r, s]
+    if shared is not None:
+        shared = np.asarray(shared, dtype=np.float64)
+        gate = np.ones(k) if z is None else _sigmoid(z)
+        for r in range(k):
+            y[r] = y[r] + gate[r] * shared[r]
+    return y
+
+
 def moe_verify(x, logits, gate_up, down, topk, mode, renorm, z=None, shared_gate_up=None,
                shared_down=None):
     """One MoE layer for k rows (fp64).
@@ -185,18 +205,12 @@ def moe_verify(x, logits, gate_up, down, topk, mode, renorm, z=None, shared_gate
         partial.append(pr)
     h = np.array(h)
     partial = np.array(partial)
-    y = np.zeros((k, partial.shape[-1]), dtype=np.float64)
-    for r in range(k):
-        for s in range(topk):
-            y[r] = y[r] + w[r, s] * partial[r, s]
     shared = None
     if shared_gate_up is not None:
-        shared = np.empty_like(y)
+        shared = np.empty((k, partial.shape[-1]), dtype=np.float64)
         for r in range(k):
             shared[r] = shared_down @ swiglu(shared_gate_up @ x[r])
-        gate = np.ones(k) if z is None else _sigmoid(z)
-        for r in range(k):
-            y[r] = y[r] + gate[r] * shared[r]
+    y = combine(partial, w, shared, z)
     return {"idx": idx, "w": w, "union_ids": union_ids, "pair_off": pair_off,
             "pair_row": pair_row, "pair_slot": pair_slot, "h": h, "partial": partial,
             "shared": shared, "y": y, "n_union": len(union_ids)}

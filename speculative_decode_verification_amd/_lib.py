@@ -1,0 +1,71 @@
+"""ctypes loader for libsdv.so (the C ABI declared in include/sdv.h)."""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdv.so")
+
+SDV_OK, SDV_EINVAL, SDV_EWIDTH, SDV_ELAYOUT, SDV_ERANGE, SDV_EALIAS, SDV_EHIP = 0, -1, -2, -3, -4, -5, -6
+MAX_ROWS, GROUP, MAX_EXPERTS, MAX_TOPK = 9, 64, 1024, 16
+MODE_PLAIN, MODE_GATEUP_SWIGLU = 0, 1
+ACT_BF16, ACT_F32 = 0, 1
+ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1
+
+EXPORTS = ("sdv_qmv_k", "sdv_moe_route_k", "sdv_gather_qmv_k", "sdv_moe_combine_k", "sdv_gdn_verify_k",
+           "sdv_gdn_rollback", "sdv_gdn_rollback_copy", "sdv_status_string", "sdv_last_error",
+           "sdv_build_info")
+
+
+class SdvQ4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("group", ctypes.c_int32)]
+
+
+class SdvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_LIB = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "sdv_qmv_k": [ctypes.POINTER(SdvQ4), _P, _I, _I, _I, _P, _P],
+    "sdv_moe_route_k": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
+    "sdv_gather_qmv_k": [ctypes.POINTER(SdvQ4), _I, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P],
+    "sdv_moe_combine_k": [_P, _P, _P, _P, _I, _I, _I, _P, _P],
+    "sdv_gdn_verify_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_P), _P],
+    "sdv_gdn_rollback": [_I, _I, ctypes.POINTER(_I)],
+    "sdv_gdn_rollback_copy": [_P, _P, ctypes.POINTER(_P), _I, _I, ctypes.c_size_t, _P],
+    "sdv_status_string": [_I],
+    "sdv_last_error": [],
+    "sdv_build_info": [],
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built (there is no fallback)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py build` "
+                               "(hipcc, gfx950); there is no non-HIP implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name in ("sdv_status_string", "sdv_last_error",
+                                                     "sdv_build_info") else ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def check(status):
+    if status != SDV_OK:
+        L = lib()
+        msg = L.sdv_last_error().decode() or L.sdv_status_string(status).decode()
+        raise SdvError(status, msg)
+    return status

@@ -1,0 +1,318 @@
+// C ABI of libsdv: argument validation (host only, before any launch) and
+// dispatch to the kernels.  Declarations and contracts: include/sdv.h.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace sdv {
+hipError_t q4_launch(const sdv_q4& W, int mode, const void* act, int act_dtype, bool gather,
+                     const int32_t* union_ids, const int32_t* n_union, const int32_t* pair_off,
+                     const int32_t* pair_row, const int32_t* pair_slot, int k, int topk, float* out,
+                     hipStream_t st);
+int q4_waves_for(int K);
+size_t q4_lds_bytes(int K, int vrow_cap, int nw);
+hipError_t route_launch(const float* logits, int k, int E, int topk, int mode, int renorm,
+                        int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
+                        int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot, hipStream_t st);
+hipError_t combine_launch(const float* partial, const float* w, const float* shared_out,
+                          const float* shared_logit, int k, int topk, int H, float* y,
+                          hipStream_t st);
+hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
+                      const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
+                      float* y, float* const* snaps, hipStream_t st);
+}  // namespace sdv
+
+namespace {
+
+// LDS available to one workgroup on gfx950.
+constexpr size_t kMaxLds = 160 * 1024;
+
+thread_local char g_err[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SDV_OK;
+}
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every input and from the other outputs.
+int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(SDV_EALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SDV_EALIAS, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+  return SDV_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(SDV_EINVAL, "%s is NULL", name);
+  if ((uintptr_t)p % 16) return fail(SDV_EINVAL, "%s is not 16-byte aligned", name);
+  return SDV_OK;
+}
+
+int check_width(int k) {
+  if (k < 1 || k > SDV_MAX_ROWS) return fail(SDV_EWIDTH, "k=%d outside 1..%d", k, SDV_MAX_ROWS);
+  return SDV_OK;
+}
+
+int check_q4(const sdv_q4* W, const char* what) {
+  if (!W) return fail(SDV_EINVAL, "%s descriptor is NULL", what);
+  if (W->group != SDV_GROUP) return fail(SDV_ELAYOUT, "%s group=%d, only 64 is supported", what, W->group);
+  if (W->K <= 0 || W->K % SDV_GROUP) return fail(SDV_ELAYOUT, "%s K=%d is not a positive multiple of 64", what, W->K);
+  if (W->N <= 0 || W->E <= 0) return fail(SDV_EINVAL, "%s E=%d N=%d must be positive", what, W->E, W->N);
+  int st;
+  if ((st = check_ptr(W->codes, "codes"))) return st;
+  if ((st = check_ptr(W->scales, "scales"))) return st;
+  if ((st = check_ptr(W->biases, "biases"))) return st;
+  return SDV_OK;
+}
+
+size_t q4_codes_bytes(const sdv_q4& W) { return (size_t)W.E * W.N * (W.K / 8) * 4; }
+size_t q4_sb_bytes(const sdv_q4& W) { return (size_t)W.E * W.N * (W.K / 64) * 2; }
+
+int check_mode(int mode, int act_dtype, int N) {
+  if (mode != SDV_MODE_PLAIN && mode != SDV_MODE_GATEUP_SWIGLU)
+    return fail(SDV_EINVAL, "unknown mode %d", mode);
+  if (act_dtype != SDV_ACT_BF16 && act_dtype != SDV_ACT_F32)
+    return fail(SDV_EINVAL, "unknown activation type %d", act_dtype);
+  if (mode == SDV_MODE_GATEUP_SWIGLU && (N % 2))
+    return fail(SDV_ELAYOUT, "fused gate/up needs an even N (got %d)", N);
+  return SDV_OK;
+}
+
+int check_lds(const sdv_q4& W, int act_dtype, int k) {
+  const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
+  const size_t lds = sdv::q4_lds_bytes(W.K, cap, sdv::q4_waves_for(W.K));
+  if (lds > kMaxLds)
+    return fail(SDV_ELAYOUT, "K=%d with %d activation rows needs %zu bytes of LDS (max %zu)", W.K, cap,
+                lds, kMaxLds);
+  return SDV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SDV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdv_status_string(int status) {
+  switch (status) {
+    case SDV_OK: return "ok";
+    case SDV_EINVAL: return "invalid argument";
+    case SDV_EWIDTH: return "unsupported row width";
+    case SDV_ELAYOUT: return "unsupported layout";
+    case SDV_ERANGE: return "value out of range";
+    case SDV_EALIAS: return "output aliases another buffer";
+    case SDV_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sdv_last_error(void) { return g_err; }
+
+const char* sdv_build_info(void) { return "sdv 0.1 gfx950"; }
+
+int sdv_qmv_k(const sdv_q4* W, const void* act, int act_dtype, int k, int mode, float* y,
+              sdv_stream_t stream) {
+  int st;
+  if ((st = check_q4(W, "W"))) return st;
+  if (W->E != 1) return fail(SDV_EINVAL, "dense product needs E=1 (got %d)", W->E);
+  if ((st = check_width(k))) return st;
+  if ((st = check_mode(mode, act_dtype, W->N))) return st;
+  if ((st = check_ptr(act, "act"))) return st;
+  if ((st = check_ptr(y, "y"))) return st;
+  if ((st = check_lds(*W, act_dtype, k))) return st;
+  const size_t act_bytes = (size_t)k * W->K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
+  const size_t n_out = mode == SDV_MODE_PLAIN ? W->N : W->N / 2;
+  Range outs[] = {{y, (size_t)k * n_out * 4, "y"}};
+  Range ins[] = {{W->codes, q4_codes_bytes(*W), "codes"},
+                 {W->scales, q4_sb_bytes(*W), "scales"},
+                 {W->biases, q4_sb_bytes(*W), "biases"},
+                 {act, act_bytes, "act"}};
+  if ((st = check_alias(outs, 1, ins, 4))) return st;
+  return hip_status(sdv::q4_launch(*W, mode, act, act_dtype, false, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr, k, 1, y, (hipStream_t)stream),
+                    "sdv_qmv_k launch");
+}
+
+int sdv_moe_route_k(const float* logits, int k, int E, int topk, int score_mode, int renorm,
+                    int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
+                    int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot,
+                    sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (E < 1 || E > SDV_MAX_EXPERTS) return fail(SDV_ERANGE, "E=%d outside 1..%d", E, SDV_MAX_EXPERTS);
+  if (topk < 1 || topk > SDV_MAX_TOPK || topk > E)
+    return fail(SDV_ERANGE, "topk=%d outside 1..min(E,%d)", topk, SDV_MAX_TOPK);
+  if (score_mode != SDV_ROUTE_SOFTMAX && score_mode != SDV_ROUTE_SIGMOID)
+    return fail(SDV_EINVAL, "unknown score mode %d", score_mode);
+  const void* ptrs[] = {logits, idx, w, union_ids, n_union, pair_off, pair_row, pair_slot};
+  const char* names[] = {"logits", "idx", "w", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot"};
+  for (int i = 0; i < 8; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  const size_t kt = (size_t)k * topk;
+  Range outs[] = {{idx, kt * 4, "idx"},           {w, kt * 4, "w"},
+                  {union_ids, kt * 4, "union_ids"}, {n_union, 4, "n_union"},
+                  {pair_off, (kt + 1) * 4, "pair_off"}, {pair_row, kt * 4, "pair_row"},
+                  {pair_slot, kt * 4, "pair_slot"}};
+  Range ins[] = {{logits, (size_t)k * E * 4, "logits"}};
+  if ((st = check_alias(outs, 7, ins, 1))) return st;
+  return hip_status(sdv::route_launch(logits, k, E, topk, score_mode, renorm, idx, w, union_ids,
+                                      n_union, pair_off, pair_row, pair_slot, (hipStream_t)stream),
+                    "sdv_moe_route_k launch");
+}
+
+int sdv_gather_qmv_k(const sdv_q4* bank, int mode, const void* act, int act_dtype,
+                     const int32_t* union_ids, const int32_t* n_union, const int32_t* pair_off,
+                     const int32_t* pair_row, const int32_t* pair_slot, int k, int topk,
+                     float* out, sdv_stream_t stream) {
+  int st;
+  if ((st = check_q4(bank, "bank"))) return st;
+  if ((st = check_width(k))) return st;
+  if (topk < 1 || topk > SDV_MAX_TOPK || topk > bank->E)
+    return fail(SDV_ERANGE, "topk=%d outside 1..min(E,%d)", topk, SDV_MAX_TOPK);
+  if ((st = check_mode(mode, act_dtype, bank->N))) return st;
+  if ((st = check_lds(*bank, act_dtype, k))) return st;
+  const void* ptrs[] = {act, union_ids, n_union, pair_off, pair_row, pair_slot, out};
+  const char* names[] = {"act", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot", "out"};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  const size_t kt = (size_t)k * topk;
+  const size_t act_bytes = act_dtype == SDV_ACT_F32 ? kt * bank->K * 4 : (size_t)k * bank->K * 2;
+  const size_t n_out = mode == SDV_MODE_PLAIN ? bank->N : bank->N / 2;
+  Range outs[] = {{out, kt * n_out * 4, "out"}};
+  Range ins[] = {{bank->codes, q4_codes_bytes(*bank), "codes"},
+                 {bank->scales, q4_sb_bytes(*bank), "scales"},
+                 {bank->biases, q4_sb_bytes(*bank), "biases"},
+                 {act, act_bytes, "act"},
+                 {union_ids, kt * 4, "union_ids"},
+                 {n_union, 4, "n_union"},
+                 {pair_off, (kt + 1) * 4, "pair_off"},
+                 {pair_row, kt * 4, "pair_row"},
+                 {pair_slot, kt * 4, "pair_slot"}};
+  if ((st = check_alias(outs, 1, ins, 9))) return st;
+  return hip_status(sdv::q4_launch(*bank, mode, act, act_dtype, true, union_ids, n_union, pair_off,
+                                   pair_row, pair_slot, k, topk, out, (hipStream_t)stream),
+                    "sdv_gather_qmv_k launch");
+}
+
+int sdv_moe_combine_k(const float* partial, const float* w, const float* shared_out,
+                      const float* shared_logit, int k, int topk, int H, float* y,
+                      sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (topk < 1 || topk > SDV_MAX_TOPK) return fail(SDV_ERANGE, "topk=%d outside 1..%d", topk, SDV_MAX_TOPK);
+  if (H < 4 || H % 4) return fail(SDV_EINVAL, "H=%d must be a positive multiple of 4", H);
+  if ((st = check_ptr(partial, "partial"))) return st;
+  if ((st = check_ptr(w, "w"))) return st;
+  if ((st = check_ptr(y, "y"))) return st;
+  if (shared_out && (st = check_ptr(shared_out, "shared_out"))) return st;
+  if (shared_logit && !shared_out) return fail(SDV_EINVAL, "shared_logit given without shared_out");
+  if (shared_logit && (st = check_ptr(shared_logit, "shared_logit"))) return st;
+  Range outs[] = {{y, (size_t)k * H * 4, "y"}};
+  Range ins[] = {{partial, (size_t)k * topk * H * 4, "partial"},
+                 {w, (size_t)k * topk * 4, "w"},
+                 {shared_out, shared_out ? (size_t)k * H * 4 : 0, "shared_out"},
+                 {shared_logit, shared_logit ? (size_t)k * 4 : 0, "shared_logit"}};
+  if ((st = check_alias(outs, 1, ins, 4))) return st;
+  return hip_status(sdv::combine_launch(partial, w, shared_out, shared_logit, k, topk, H, y,
+                                        (hipStream_t)stream),
+                    "sdv_moe_combine_k launch");
+}
+
+int sdv_gdn_verify_k(const float* S_in, const float* q, const float* kk, const float* v,
+                     const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
+                     float* y, float* const* snaps, sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (Dk != 64 && Dk != 128) return fail(SDV_ELAYOUT, "Dk=%d, only 64 and 128 are supported", Dk);
+  if (Hv < 1 || Hk < 1 || Dv < 1) return fail(SDV_EINVAL, "Hv=%d Hk=%d Dv=%d must be positive", Hv, Hk, Dv);
+  if (Hv % Hk) return fail(SDV_ELAYOUT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
+  if ((long)Hv * Dv > (1L << 26)) return fail(SDV_EINVAL, "Hv*Dv=%ld too large", (long)Hv * Dv);
+  const void* ptrs[] = {S_in, q, kk, v, g, beta, y};
+  const char* names[] = {"S_in", "q", "kk", "v", "g", "beta", "y"};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  if (!snaps) return fail(SDV_EINVAL, "snaps is NULL");
+  const size_t state = (size_t)Hv * Dv * Dk * 4;
+  Range ins[] = {{S_in, state, "S_in"},
+                 {q, (size_t)k * Hk * Dk * 4, "q"},
+                 {kk, (size_t)k * Hk * Dk * 4, "kk"},
+                 {v, (size_t)k * Hv * Dv * 4, "v"},
+                 {g, (size_t)k * Hv * 4, "g"},
+                 {beta, (size_t)k * Hv * 4, "beta"}};
+  Range outs[SDV_MAX_ROWS + 1];
+  outs[0] = {y, (size_t)k * Hv * Dv * 4, "y"};
+  static const char* snap_names[SDV_MAX_ROWS] = {"snaps[0]", "snaps[1]", "snaps[2]", "snaps[3]", "snaps[4]",
+                                                  "snaps[5]", "snaps[6]", "snaps[7]", "snaps[8]"};
+  for (int t = 0; t < k; ++t) {
+    if ((st = check_ptr(snaps[t], snap_names[t]))) return st;
+    outs[t + 1] = {snaps[t], state, snap_names[t]};
+  }
+  if ((st = check_alias(outs, k + 1, ins, 6))) return st;
+  return hip_status(sdv::gdn_launch(S_in, q, kk, v, g, beta, k, Hv, Hk, Dk, Dv, y, snaps,
+                                    (hipStream_t)stream),
+                    "sdv_gdn_verify_k launch");
+}
+
+int sdv_gdn_rollback(int k, int j, int* selected_slot) {
+  int st;
+  if (!selected_slot) return fail(SDV_EINVAL, "selected_slot is NULL");
+  if ((st = check_width(k))) return st;
+  if (j < 0 || j > k) return fail(SDV_ERANGE, "accepted prefix %d outside 0..%d", j, k);
+  *selected_slot = j;
+  return ok();
+}
+
+int sdv_gdn_rollback_copy(float* dst, const float* S_in, float* const* snaps, int k, int j,
+                          size_t state_elems, sdv_stream_t stream) {
+  int st, slot = 0;
+  if ((st = sdv_gdn_rollback(k, j, &slot))) return st;
+  if ((st = check_ptr(dst, "dst"))) return st;
+  if (state_elems == 0) return fail(SDV_EINVAL, "state_elems is 0");
+  const float* src = nullptr;
+  if (slot == 0) {
+    src = S_in;
+  } else {
+    if (!snaps) return fail(SDV_EINVAL, "snaps is NULL");
+    src = snaps[slot - 1];
+  }
+  if ((st = check_ptr(src, slot == 0 ? "S_in" : "selected snapshot"))) return st;
+  if (src == dst) return ok();
+  Range a{dst, state_elems * 4, "dst"}, b{src, state_elems * 4, "source"};
+  if (overlap(a, b)) return fail(SDV_EALIAS, "dst partially overlaps the selected state");
+  return hip_status(hipMemcpyAsync(dst, src, state_elems * 4, hipMemcpyDeviceToDevice, (hipStream_t)stream),
+                    "sdv_gdn_rollback_copy");
+}
+
+}  // extern "C"

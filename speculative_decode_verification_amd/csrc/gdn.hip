@@ -1,0 +1,132 @@
+// k-row Gated DeltaNet verification with in-kernel snapshots (gfx950).
+//
+// Flash-Next plan, "2.1 Gated DeltaNet": per v head h the fp32 state S_h
+// [Dv, Dk] takes, for every row t, decay S <- g S, kv_mem m = S k, delta
+// d = beta (v - m), rank-1 update S += d k^T, readout y = S q.  "3.1": g and
+// beta are per-head scalars and each qk head serves Hv/Hk consecutive v heads.
+// Red Lite dev45, "What it is": row t runs from row t-1's state and the state
+// after each row is written to a snapshot from inside the kernel, so a
+// rejected draft is undone by selecting a snapshot.
+//
+// Every value row S_h[i, :] is independent; only t is serial.  A value row
+// lives in registers of 16 lanes (one DPP row) for all k rows of the call:
+// lane p holds elements 4p + 64j .. +3 (j < Dk/64), so each float4 access of
+// the 16 lanes covers 256 contiguous bytes.  Dot products are an in-lane fma
+// chain followed by a fixed 16-lane DPP sum, the same instructions for every
+// t, so row t of a width-k call equals a width-1 call fed the snapshot after
+// row t-1, bit for bit.  HBM traffic per layer: the state once in, k
+// snapshots out, plus the small per-row vectors.
+
+#include "common.h"
+
+namespace sdv {
+
+namespace {
+
+struct GdnArgs {
+  const float* S_in;
+  const float* q;
+  const float* kk;
+  const float* v;
+  const float* g;
+  const float* beta;
+  int k, Hv, Hk, Dv;
+  float* y;
+  float* snaps[SDV_MAX_ROWS];
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
+  constexpr int NV4 = DK / 64;  // float4 per lane
+  const int sub = threadIdx.x & 15;
+  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 4;  // h * Dv + i
+  const long nrows = (long)a.Hv * a.Dv;
+  if (row >= nrows) return;  // whole 16-lane groups leave together
+  const int h = (int)(row / a.Dv);
+  const int i = (int)(row - (long)h * a.Dv);
+  const int c = h / (a.Hv / a.Hk);
+
+  float4 S[NV4];
+  const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + row * DK);
+#pragma unroll
+  for (int j = 0; j < NV4; ++j) S[j] = sin4[sub + 16 * j];
+
+  for (int t = 0; t < a.k; ++t) {
+    const float gt = a.g[t * a.Hv + h];
+    const float bt = a.beta[t * a.Hv + h];
+    const float vt = a.v[((long)t * a.Hv + h) * a.Dv + i];
+    const float4* k4 = reinterpret_cast<const float4*>(a.kk + ((long)t * a.Hk + c) * DK);
+    const float4* q4 = reinterpret_cast<const float4*>(a.q + ((long)t * a.Hk + c) * DK);
+    float4 kt[NV4], qt[NV4];
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) {
+      kt[j] = k4[sub + 16 * j];
+      qt[j] = q4[sub + 16 * j];
+    }
+    // decay, then kv_mem on the decayed state
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) {
+      S[j].x = gt * S[j].x;
+      S[j].y = gt * S[j].y;
+      S[j].z = gt * S[j].z;
+      S[j].w = gt * S[j].w;
+      m = fmaf(S[j].x, kt[j].x, m);
+      m = fmaf(S[j].y, kt[j].y, m);
+      m = fmaf(S[j].z, kt[j].z, m);
+      m = fmaf(S[j].w, kt[j].w, m);
+    }
+    m = row16_sum(m);
+    const float d = bt * (vt - m);
+    // rank-1 update and readout
+    float o = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) {
+      S[j].x = fmaf(d, kt[j].x, S[j].x);
+      S[j].y = fmaf(d, kt[j].y, S[j].y);
+      S[j].z = fmaf(d, kt[j].z, S[j].z);
+      S[j].w = fmaf(d, kt[j].w, S[j].w);
+      o = fmaf(S[j].x, qt[j].x, o);
+      o = fmaf(S[j].y, qt[j].y, o);
+      o = fmaf(S[j].z, qt[j].z, o);
+      o = fmaf(S[j].w, qt[j].w, o);
+    }
+    o = row16_sum(o);
+    if (sub == 0) a.y[((long)t * a.Hv + h) * a.Dv + i] = o;
+    float4* dst = reinterpret_cast<float4*>(a.snaps[t] + row * DK);
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) dst[sub + 16 * j] = S[j];
+  }
+}
+
+}  // namespace
+
+hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
+                      const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
+                      float* y, float* const* snaps, hipStream_t st) {
+  GdnArgs a;
+  a.S_in = S_in;
+  a.q = q;
+  a.kk = kk;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.k = k;
+  a.Hv = Hv;
+  a.Hk = Hk;
+  a.Dv = Dv;
+  a.y = y;
+  for (int t = 0; t < SDV_MAX_ROWS; ++t) a.snaps[t] = t < k ? snaps[t] : nullptr;
+  const long threads_total = (long)Hv * Dv * 16;
+  const int block = 256;
+  const long blocks = (threads_total + block - 1) / block;
+  if (Dk == 64)
+    hipLaunchKernelGGL(gdn_verify_kernel<64>, dim3((unsigned)blocks), dim3(block), 0, st, a);
+  else if (Dk == 128)
+    hipLaunchKernelGGL(gdn_verify_kernel<128>, dim3((unsigned)blocks), dim3(block), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sdv

@@ -1,0 +1,206 @@
+"""Python binding of libsdv: argument marshalling over the C ABI.
+
+Every function checks that the tensors it is handed are CUDA, contiguous, of
+the expected dtype and large enough for the sizes it passes, then calls the
+matching ``sdv_*`` entry point on the current stream.  All arithmetic runs in
+the library's HIP kernels; nothing here computes results.
+"""
+
+import ctypes
+from collections import namedtuple
+
+import torch
+
+from ._lib import (ACT_BF16, ACT_F32, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX,
+                   SdvError, SdvQ4, check, lib)
+
+__all__ = ["Q4Weight", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
+           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "SdvError", "MODE_PLAIN",
+           "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
+
+RouteResult = namedtuple("RouteResult", "idx w union_ids n_union pair_off pair_row pair_slot")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, numel=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Q4Weight:
+    """Affine-Q4/g64 weights on the device: codes int32 (bit patterns of the
+    u32 words) [E, N, K/8], scales and biases int16 (bf16 bits) [E, N, K/64].
+    A 2-D layout [N, K/8] is a dense matrix (E = 1)."""
+
+    def __init__(self, codes, scales, biases):
+        if codes.dim() == 2:
+            codes, scales, biases = codes[None], scales[None], biases[None]
+        if codes.dim() != 3 or scales.shape != biases.shape or scales.dim() != 3:
+            raise ValueError("codes [E,N,K/8], scales/biases [E,N,K/64] expected")
+        self.E, self.N, kw = codes.shape
+        self.K = kw * 8
+        if scales.shape != (self.E, self.N, self.K // 64):
+            raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+        self.codes, self.scales, self.biases = codes, scales, biases
+        self.device = codes.device
+        self._desc = SdvQ4(_need(codes, "codes", torch.int32).value,
+                           _need(scales, "scales", torch.int16, device=self.device).value,
+                           _need(biases, "biases", torch.int16, device=self.device).value,
+                           self.E, self.N, self.K, 64)
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def nbytes(self):
+        return self.E * self.N * (self.K // 2 + (self.K // 64) * 4)
+
+
+def _act_kind(act):
+    if act.dtype == torch.int16:
+        return ACT_BF16
+    if act.dtype == torch.float32:
+        return ACT_F32
+    raise TypeError("activations must be bf16 bits (torch.int16) or float32")
+
+
+def qmv_k(W, act, mode=MODE_PLAIN, out=None):
+    """Dense k-row product: act [k, K] (bf16 bits as int16, or fp32) -> fp32
+    [k, N] (plain) or [k, N/2] (fused gate/up with SwiGLU)."""
+    k = act.shape[0]
+    kind = _act_kind(act)
+    if act.dim() != 2 or act.shape[1] != W.K:
+        raise ValueError(f"act must be [k, {W.K}]")
+    n_out = W.N if mode == MODE_PLAIN else W.N // 2
+    if out is None:
+        out = torch.empty((k, n_out), dtype=torch.float32, device=W.device)
+    pa = _need(act, "act", act.dtype, device=W.device)
+    py = _need(out, "out", torch.float32, k * n_out, device=W.device)
+    check(lib().sdv_qmv_k(W.desc, pa, kind, k, mode, py, _stream(out)))
+    return out
+
+
+def route_buffers(k, topk, device):
+    kt = k * topk
+    return RouteResult(
+        idx=torch.empty((k, topk), dtype=torch.int32, device=device),
+        w=torch.empty((k, topk), dtype=torch.float32, device=device),
+        union_ids=torch.empty((kt,), dtype=torch.int32, device=device),
+        n_union=torch.empty((1,), dtype=torch.int32, device=device),
+        pair_off=torch.empty((kt + 1,), dtype=torch.int32, device=device),
+        pair_row=torch.empty((kt,), dtype=torch.int32, device=device),
+        pair_slot=torch.empty((kt,), dtype=torch.int32, device=device))
+
+
+def moe_route_k(logits, topk, score_mode, renorm, out=None):
+    """Per-row top-k, weights, union and pairs for logits fp32 [k, E]."""
+    k, E = logits.shape
+    if out is None:
+        out = route_buffers(k, topk, logits.device)
+    kt = k * topk
+    dev = logits.device
+    args = [_need(logits, "logits", torch.float32)]
+    check(lib().sdv_moe_route_k(args[0], k, E, topk, score_mode, int(bool(renorm)),
+                                _need(out.idx, "idx", torch.int32, kt, dev),
+                                _need(out.w, "w", torch.float32, kt, dev),
+                                _need(out.union_ids, "union_ids", torch.int32, kt, dev),
+                                _need(out.n_union, "n_union", torch.int32, 1, dev),
+                                _need(out.pair_off, "pair_off", torch.int32, kt + 1, dev),
+                                _need(out.pair_row, "pair_row", torch.int32, kt, dev),
+                                _need(out.pair_slot, "pair_slot", torch.int32, kt, dev),
+                                _stream(logits)))
+    return out
+
+
+def gather_qmv_k(bank, mode, act, route, k, topk, out=None):
+    """Gathered-expert product over the union in ``route``.  act: bf16 bits
+    [k, K] shared by a row's slots, or fp32 [k, topk, K] per pair.  Returns
+    fp32 [k, topk, N or N/2]; entry (r, s) is expert idx[r, s]'s output."""
+    kind = _act_kind(act)
+    kt = k * topk
+    need_act = kt * bank.K if kind == ACT_F32 else k * bank.K
+    n_out = bank.N if mode == MODE_PLAIN else bank.N // 2
+    if out is None:
+        out = torch.empty((k, topk, n_out), dtype=torch.float32, device=bank.device)
+    dev = bank.device
+    check(lib().sdv_gather_qmv_k(bank.desc, mode, _need(act, "act", act.dtype, need_act, dev), kind,
+                                 _need(route.union_ids, "union_ids", torch.int32, kt, dev),
+                                 _need(route.n_union, "n_union", torch.int32, 1, dev),
+                                 _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
+                                 _need(route.pair_row, "pair_row", torch.int32, kt, dev),
+                                 _need(route.pair_slot, "pair_slot", torch.int32, kt, dev),
+                                 k, topk, _need(out, "out", torch.float32, kt * n_out, dev), _stream(out)))
+    return out
+
+
+def moe_combine_k(partial, w, shared_out=None, shared_logit=None, out=None):
+    """y[r] = sum_s w[r, s] partial[r, s] (slot order) + sigmoid(z_r) shared[r]."""
+    k, topk, H = partial.shape
+    dev = partial.device
+    if out is None:
+        out = torch.empty((k, H), dtype=torch.float32, device=dev)
+    ps = _need(shared_out, "shared_out", torch.float32, k * H, dev) if shared_out is not None else None
+    pz = _need(shared_logit, "shared_logit", torch.float32, k, dev) if shared_logit is not None else None
+    check(lib().sdv_moe_combine_k(_need(partial, "partial", torch.float32, k * topk * H, dev),
+                                  _need(w, "w", torch.float32, k * topk, dev), ps, pz, k, topk, H,
+                                  _need(out, "out", torch.float32, k * H, dev), _stream(out)))
+    return out
+
+
+def gdn_verify_k(S_in, q, kk, v, g, beta, snaps, y=None):
+    """k-row Gated DeltaNet step with a snapshot after every row.
+
+    S_in fp32 [Hv, Dv, Dk]; q, kk [k, Hk, Dk]; v [k, Hv, Dv]; g, beta [k, Hv];
+    snaps: k fp32 tensors of S_in's shape (written).  Returns y [k, Hv, Dv]."""
+    Hv, Dv, Dk = S_in.shape
+    k, Hk, dk2 = q.shape
+    dev = S_in.device
+    if dk2 != Dk or tuple(kk.shape) != (k, Hk, Dk) or tuple(v.shape) != (k, Hv, Dv):
+        raise ValueError("q/kk/v shapes do not match S_in")
+    if tuple(g.shape) != (k, Hv) or tuple(beta.shape) != (k, Hv):
+        raise ValueError("g/beta must be [k, Hv]")
+    if len(snaps) != k:
+        raise ValueError(f"{len(snaps)} snapshot buffers for k={k} rows")
+    if y is None:
+        y = torch.empty((k, Hv, Dv), dtype=torch.float32, device=dev)
+    st = Hv * Dv * Dk
+    arr = (ctypes.c_void_p * k)(*[_need(s, f"snaps[{t}]", torch.float32, st, dev).value for t, s in enumerate(snaps)])
+    check(lib().sdv_gdn_verify_k(_need(S_in, "S_in", torch.float32, st, dev), _need(q, "q", torch.float32, device=dev),
+                                 _need(kk, "kk", torch.float32, device=dev), _need(v, "v", torch.float32, device=dev),
+                                 _need(g, "g", torch.float32, device=dev), _need(beta, "beta", torch.float32, device=dev),
+                                 k, Hv, Hk, Dk, Dv, _need(y, "y", torch.float32, k * Hv * Dv, dev), arr,
+                                 _stream(y)))
+    return y
+
+
+def gdn_rollback(k, j):
+    """Slot holding the state after an accepted prefix of j rows: 0 = the
+    verify call's input state, t = snapshot t-1."""
+    slot = ctypes.c_int(-1)
+    check(lib().sdv_gdn_rollback(k, j, ctypes.byref(slot)))
+    return slot.value
+
+
+def gdn_rollback_copy(dst, S_in, snaps, j):
+    """dst <- the selected state (device copy on the current stream)."""
+    k = len(snaps)
+    dev = dst.device
+    n = S_in.numel()
+    arr = (ctypes.c_void_p * k)(*[_need(s, f"snaps[{t}]", torch.float32, n, dev).value for t, s in enumerate(snaps)])
+    check(lib().sdv_gdn_rollback_copy(_need(dst, "dst", torch.float32, n, dev), _need(S_in, "S_in", torch.float32, n, dev),
+                                      arr, k, j, n, _stream(dst)))
+    return dst

@@ -1,0 +1,85 @@
+"""One verification step composed from the library's entry points.
+
+``MoeLayer`` runs the MoE half of a layer for k rows: router dispatch and
+union, gathered fused gate/up with SwiGLU, gathered down projection, the
+optional shared expert (dense gate/up + down) and the fixed-order combine,
+all on the device with no host synchronisation.  ``GdnLayer`` keeps a pool of
+k+1 state buffers per layer: the live state and k snapshot slots.  A verify
+call writes the snapshots; rollback to an accepted prefix j only swaps which
+buffer is live (Red Lite dev45, "What it is": pointer swap with the
+snapshots), so no state is copied.
+"""
+
+import torch
+
+from . import ops
+from ._lib import MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX
+
+
+class MoeLayer:
+    def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None):
+        self.gate_up, self.down = gate_up, down
+        self.shared_gate_up, self.shared_down = shared_gate_up, shared_down
+        self.k, self.topk = k, topk
+        self.score_mode, self.renorm = score_mode, renorm
+        dev = gate_up.device
+        self.H = gate_up.K
+        self.I = gate_up.N // 2
+        if down.K != self.I or down.N != self.H:
+            raise ValueError("down bank must be [E, H, I]")
+        self.route = ops.route_buffers(k, topk, dev)
+        self.h = torch.empty((k, topk, self.I), dtype=torch.float32, device=dev)
+        self.partial = torch.empty((k, topk, self.H), dtype=torch.float32, device=dev)
+        self.y = torch.empty((k, self.H), dtype=torch.float32, device=dev)
+        if shared_gate_up is not None:
+            self.sh_h = torch.empty((k, shared_gate_up.N // 2), dtype=torch.float32, device=dev)
+            self.sh_out = torch.empty((k, self.H), dtype=torch.float32, device=dev)
+        else:
+            self.sh_h = self.sh_out = None
+
+    def __call__(self, x, logits, z=None):
+        """x: bf16 bits [k, H] (int16); logits fp32 [k, E]; z fp32 [k] or None."""
+        ops.moe_route_k(logits, self.topk, self.score_mode, self.renorm, out=self.route)
+        ops.gather_qmv_k(self.gate_up, MODE_GATEUP_SWIGLU, x, self.route, self.k, self.topk, out=self.h)
+        ops.gather_qmv_k(self.down, MODE_PLAIN, self.h, self.route, self.k, self.topk, out=self.partial)
+        if self.shared_gate_up is not None:
+            ops.qmv_k(self.shared_gate_up, x, MODE_GATEUP_SWIGLU, out=self.sh_h)
+            ops.qmv_k(self.shared_down, self.sh_h, MODE_PLAIN, out=self.sh_out)
+        ops.moe_combine_k(self.partial, self.route.w, self.sh_out, z if self.sh_out is not None else None,
+                          out=self.y)
+        return self.y
+
+
+class GdnLayer:
+    """State pool of one GDN layer: slot ``live`` holds the current state, the
+    other k slots receive the next verify call's snapshots."""
+
+    def __init__(self, S0, k):
+        self.k = k
+        self.Hv, self.Dv, self.Dk = S0.shape
+        self.slots = [S0.contiguous()] + [torch.empty_like(S0) for _ in range(k)]
+        self.live = 0
+        self.snap_ids = None
+        self.y = torch.empty((k, self.Hv, self.Dv), dtype=torch.float32, device=S0.device)
+
+    @property
+    def state(self):
+        return self.slots[self.live]
+
+    def verify(self, q, kk, v, g, beta):
+        rows = q.shape[0]
+        self.snap_ids = [i for i in range(len(self.slots)) if i != self.live][:rows]
+        y = self.y[:rows]
+        ops.gdn_verify_k(self.state, q, kk, v, g, beta, [self.slots[i] for i in self.snap_ids], y=y)
+        return y
+
+    def rollback(self, j):
+        """Make the state after the accepted prefix of j rows live (no copy)."""
+        slot = ops.gdn_rollback(len(self.snap_ids), j)
+        if slot > 0:
+            self.live = self.snap_ids[slot - 1]
+        self.snap_ids = None
+        return self.state
+
+
+__all__ = ["MoeLayer", "GdnLayer", "MODE_PLAIN", "MODE_GATEUP_SWIGLU", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]

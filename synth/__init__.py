@@ -21,12 +21,12 @@ Two generators are used:
 from .counter import (GAMMA, SEED, derive_key, mix64, rand64, bf16_bits_from_f32,
                       q4_code_words, q4_affine_bf16, q4_rows)
 from . import configs
-from .inputs import (BankKeys, bank_keys, dense_weight, moe_layer_inputs, gdn_layer_inputs,
+from .inputs import (BankKeys, bank_keys, activations, dense_weight, moe_layer_inputs, gdn_layer_inputs,
                      gdn_state, accepted_prefix, integer_exact_weight)
 
 __all__ = [
     "GAMMA", "SEED", "derive_key", "mix64", "rand64", "bf16_bits_from_f32",
-    "q4_code_words", "q4_affine_bf16", "q4_rows", "configs", "BankKeys", "bank_keys",
+    "q4_code_words", "q4_affine_bf16", "q4_rows", "configs", "BankKeys", "bank_keys", "activations",
     "dense_weight", "moe_layer_inputs", "gdn_layer_inputs", "gdn_state",
     "accepted_prefix", "integer_exact_weight",
 ]

@@ -39,6 +39,11 @@ def bf16_normal(rng, shape):
     return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
 
 
+def activations(cfg_id, layer, rows, k, step=0, tensor=T_X):
+    """bf16 activation rows [rows, k] ~ N(0,1) (bit patterns)."""
+    return bf16_normal(_rng(cfg_id, tensor, layer, step), (rows, k))
+
+
 def moe_layer_inputs(cfg_id, layer, rows, hidden, experts, step=0):
     """x (bf16 bits [rows, hidden]), router logits (fp32 [rows, E]) and the
     shared-expert gate logit z (fp32 [rows]) of one MoE layer."""

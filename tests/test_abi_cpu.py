@@ -1,0 +1,174 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any launch (no GPU is touched: every call
+here fails host validation, which runs before any HIP call)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_decode_verification_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdv.h")
+
+P = 0x10000  # fake, 16-byte aligned "device" addresses; validation fails before any use
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SDV_API\s+[\w\s\*]+?\b(sdv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libsdv.so is not built (run `python __graft_entry__.py build`)")
+    return L.lib()
+
+
+def test_exports_match_header(lib):
+    names = declared()
+    assert len(names) == 10
+    assert tuple(sorted(L.EXPORTS)) == tuple(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (sdv_\w+)", nm)))
+    assert exported == names
+
+
+def test_status_strings(lib):
+    for code, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported row width"),
+                       (-3, "unsupported layout"), (-4, "value out of range"), (-5, "output aliases"),
+                       (-6, "HIP runtime error")]:
+        assert lib.sdv_status_string(code).decode().startswith(text)
+    assert b"gfx950" in lib.sdv_build_info()
+
+
+def q4(E=1, N=64, K=128, group=64, codes=P, scales=P + 0x100000, biases=P + 0x200000):
+    return L.SdvQ4(codes, scales, biases, E, N, K, group)
+
+
+def qmv(lib, W, act=P + 0x400000, dtype=L.ACT_BF16, k=2, mode=L.MODE_PLAIN, y=P + 0x800000):
+    return lib.sdv_qmv_k(ctypes.byref(W), act, dtype, k, mode, y, None)
+
+
+def test_qmv_validation(lib):
+    assert qmv(lib, q4(), k=0) == L.SDV_EWIDTH
+    assert qmv(lib, q4(), k=10) == L.SDV_EWIDTH
+    assert qmv(lib, q4(group=32)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4(K=100)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4(K=0)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4(E=2)) == L.SDV_EINVAL
+    assert qmv(lib, q4(N=0)) == L.SDV_EINVAL
+    assert qmv(lib, q4(codes=0)) == L.SDV_EINVAL
+    assert qmv(lib, q4(scales=P + 2)) == L.SDV_EINVAL
+    assert qmv(lib, q4(), act=0) == L.SDV_EINVAL
+    assert qmv(lib, q4(), y=P + 0x800008) == L.SDV_EINVAL
+    assert qmv(lib, q4(N=63), mode=L.MODE_GATEUP_SWIGLU) == L.SDV_ELAYOUT
+    assert qmv(lib, q4(), mode=7) == L.SDV_EINVAL
+    assert qmv(lib, q4(), dtype=5) == L.SDV_EINVAL
+    # output inside the codes array
+    assert qmv(lib, q4(), y=P + 64) == L.SDV_EALIAS
+    # output overlapping the activations
+    assert qmv(lib, q4(), y=P + 0x400000 + 16) == L.SDV_EALIAS
+    # fp32 activation rows that cannot be staged in LDS
+    assert qmv(lib, q4(K=8192), dtype=L.ACT_F32, k=9) == L.SDV_ELAYOUT
+    assert "LDS" in lib.sdv_last_error().decode()
+
+
+def route(lib, k=2, E=64, topk=4, mode=L.ROUTE_SOFTMAX, logits=P, outs=None):
+    outs = outs or [P + 0x100000 * (i + 1) for i in range(7)]
+    return lib.sdv_moe_route_k(logits, k, E, topk, mode, 0, *outs, None)
+
+
+def test_route_validation(lib):
+    assert route(lib, k=0) == L.SDV_EWIDTH
+    assert route(lib, topk=0) == L.SDV_ERANGE
+    assert route(lib, topk=17, E=64) == L.SDV_ERANGE
+    assert route(lib, topk=8, E=4) == L.SDV_ERANGE
+    assert route(lib, E=1025) == L.SDV_ERANGE
+    assert route(lib, mode=3) == L.SDV_EINVAL
+    assert route(lib, logits=0) == L.SDV_EINVAL
+    outs = [P + 0x100000 * (i + 1) for i in range(7)]
+    outs[1] = P  # weights written over the logits
+    assert route(lib, outs=outs) == L.SDV_EALIAS
+    outs = [P + 0x100000 * (i + 1) for i in range(7)]
+    outs[6] = outs[5] + 16  # pair_slot overlapping pair_row
+    assert route(lib, outs=outs) == L.SDV_EALIAS
+
+
+def gather(lib, bank, k=2, topk=4, mode=L.MODE_GATEUP_SWIGLU, dtype=L.ACT_BF16, out=P + 0x2000000):
+    ptrs = [P + 0x800000 + 0x10000 * i for i in range(6)]
+    return lib.sdv_gather_qmv_k(ctypes.byref(bank), mode, ptrs[0], dtype, ptrs[1], ptrs[2], ptrs[3], ptrs[4],
+                                ptrs[5], k, topk, out, None)
+
+
+def test_gather_validation(lib):
+    bank = q4(E=8, N=128, K=128)
+    assert gather(lib, bank, k=10) == L.SDV_EWIDTH
+    assert gather(lib, bank, topk=9) == L.SDV_ERANGE
+    assert gather(lib, q4(E=8, N=127, K=128)) == L.SDV_ELAYOUT
+    assert gather(lib, q4(E=8, N=128, K=96)) == L.SDV_ELAYOUT
+    assert gather(lib, bank, out=0) == L.SDV_EINVAL
+    assert gather(lib, bank, out=P + 0x800000) == L.SDV_EALIAS
+
+
+def test_combine_validation(lib):
+    f = lib.sdv_moe_combine_k
+    assert f(P, P + 0x10000, None, None, 0, 4, 64, P + 0x20000, None) == L.SDV_EWIDTH
+    assert f(P, P + 0x10000, None, None, 2, 0, 64, P + 0x20000, None) == L.SDV_ERANGE
+    assert f(P, P + 0x10000, None, None, 2, 4, 62, P + 0x20000, None) == L.SDV_EINVAL
+    assert f(P, P + 0x10000, None, P + 0x30000, 2, 4, 64, P + 0x20000, None) == L.SDV_EINVAL
+    assert f(P, P + 0x10000, None, None, 2, 4, 64, P + 0x100, None) == L.SDV_EALIAS
+
+
+def gdn(lib, k=2, Hv=4, Hk=4, Dk=64, Dv=64, snaps=None, S_in=P, y=P + 0x700000):
+    base = [P + 0x100000 * (i + 1) for i in range(5)]
+    snaps = snaps if snaps is not None else [P + 0x1000000 * (t + 1) for t in range(k)]
+    arr = (ctypes.c_void_p * max(1, len(snaps)))(*snaps)
+    return lib.sdv_gdn_verify_k(S_in, base[0], base[1], base[2], base[3], base[4], k, Hv, Hk, Dk, Dv, y, arr, None)
+
+
+def test_gdn_validation(lib):
+    assert gdn(lib, k=0) == L.SDV_EWIDTH
+    assert gdn(lib, k=10) == L.SDV_EWIDTH
+    assert gdn(lib, Dk=96) == L.SDV_ELAYOUT
+    assert gdn(lib, Dk=256) == L.SDV_ELAYOUT
+    assert gdn(lib, Hv=6, Hk=4) == L.SDV_ELAYOUT
+    assert gdn(lib, Hv=0) == L.SDV_EINVAL
+    assert gdn(lib, S_in=0) == L.SDV_EINVAL
+    s = P + 0x1000000
+    assert gdn(lib, snaps=[s, s]) == L.SDV_EALIAS                   # two rows, one snapshot buffer
+    assert "snaps" in lib.sdv_last_error().decode()
+    assert gdn(lib, snaps=[s, P + 8 * 1024]) == L.SDV_EALIAS        # snapshot over S_in
+    assert gdn(lib, snaps=[s, 0]) == L.SDV_EINVAL
+    assert gdn(lib, y=P + 0x100000) == L.SDV_EALIAS                 # y over q
+    assert lib.sdv_last_error().decode() == "output y overlaps input q"
+
+
+def test_rollback_selection(lib):
+    slot = ctypes.c_int(-7)
+    for k in range(1, 10):
+        for j in range(0, k + 1):
+            assert lib.sdv_gdn_rollback(k, j, ctypes.byref(slot)) == 0
+            assert slot.value == j
+        assert lib.sdv_gdn_rollback(k, k + 1, ctypes.byref(slot)) == L.SDV_ERANGE
+        assert lib.sdv_gdn_rollback(k, -1, ctypes.byref(slot)) == L.SDV_ERANGE
+    assert lib.sdv_gdn_rollback(10, 1, ctypes.byref(slot)) == L.SDV_EWIDTH
+    assert lib.sdv_gdn_rollback(2, 1, None) == L.SDV_EINVAL
+
+
+def test_rollback_copy_validation(lib):
+    snaps = (ctypes.c_void_p * 2)(P + 0x100000, P + 0x200000)
+    f = lib.sdv_gdn_rollback_copy
+    # selecting the state the destination already is: nothing to copy, no HIP call
+    assert f(P, P, snaps, 2, 0, 1024, None) == 0
+    assert f(P + 0x200000, P, snaps, 2, 2, 1024, None) == 0
+    assert f(P + 16, P, snaps, 2, 0, 1024, None) == L.SDV_EALIAS
+    assert f(P + 0x900000, P, snaps, 2, 3, 1024, None) == L.SDV_ERANGE
+    assert f(P + 0x900000, P, snaps, 2, 1, 0, None) == L.SDV_EINVAL
+    assert f(0, P, snaps, 2, 1, 1024, None) == L.SDV_EINVAL

@@ -1,0 +1,128 @@
+"""GPU parity of the dense multi-row affine-Q4 product (sdv_qmv_k) against
+the CPU oracle, plus bitwise width-k == width-1 and integer-exact cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import device as sdev
+from synth.inputs import DENSE_W, SHARED_GATEUP
+from tests.gpu_helpers import DEV, assert_close, banner, q4_device_from_host, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    from speculative_decode_verification_amd import ops
+    return ops
+
+
+def dense_case(cfg, layer, N, K, rows, kind=DENSE_W):
+    codes, scales, biases = synth.dense_weight(cfg, kind, layer, N, K)
+    x = synth.activations(cfg, layer, rows, K)
+    return codes, scales, biases, x
+
+
+def test_tiny_projection_matches_oracle():
+    banner("qmv tiny N=K=1024 k=2")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(0, 0, 1024, 1024, 2)
+    W = q4_device_from_host(codes, scales, biases)
+    y = ops.qmv_k(W, sdev.upload_bf16(x, DEV))
+    ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x))
+    assert_close(to_np(y), ref, "tiny projection")
+
+
+def test_integer_exact_is_bit_exact():
+    banner("qmv integer-exact N=256 K=1024 k=9")
+    ops = _ops()
+    codes, scales, biases, x = synth.integer_exact_weight(3, 256, 1024, 9)
+    W = q4_device_from_host(codes, scales, biases)
+    y = to_np(ops.qmv_k(W, sdev.upload_bf16(x, DEV)))
+    ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x)).astype(np.float32)
+    assert np.array_equal(y, ref)
+
+
+def test_dense_5120_widths_bitwise_and_parity():
+    banner("qmv 5120x5120 widths 1,4,8,9")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(1, 0, 5120, 5120, 9)
+    W = q4_device_from_host(codes, scales, biases)
+    xd = sdev.upload_bf16(x, DEV)
+    singles = [to_np(ops.qmv_k(W, xd[r:r + 1].contiguous()))[0] for r in range(9)]
+    for k in (1, 4, 8, 9):
+        y = to_np(ops.qmv_k(W, xd[:k].contiguous()))
+        for r in range(k):
+            assert np.array_equal(y[r], singles[r]), f"width {k} row {r} differs from width 1"
+    ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x))
+    assert_close(np.stack(singles), ref, "5120x5120 projection")
+
+
+@pytest.mark.parametrize("N,K", [(1000, 576), (33, 64), (1, 64), (4097, 192), (96, 5120)])
+def test_ragged_shapes(N, K):
+    banner(f"qmv ragged N={N} K={K}")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(0, 7, N, K, 9)
+    W = q4_device_from_host(codes, scales, biases)
+    xd = sdev.upload_bf16(x, DEV)
+    ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x))
+    for k in (1, 3, 9):
+        y = to_np(ops.qmv_k(W, xd[:k].contiguous()))
+        assert_close(y, ref[:k], f"N={N} K={K} k={k}")
+
+
+@pytest.mark.parametrize("I,H", [(640, 2560), (40, 128), (17, 192)])
+def test_gate_up_swiglu(I, H):
+    banner(f"qmv gate/up I={I} H={H}")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(4, 3, 2 * I, H, 9, kind=SHARED_GATEUP)
+    W = q4_device_from_host(codes, scales, biases)
+    xd = sdev.upload_bf16(x, DEV)
+    ref = oracle.swiglu(oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x)))
+    y9 = to_np(ops.qmv_k(W, xd, mode=ops.MODE_GATEUP_SWIGLU))
+    assert_close(y9, ref, "gate/up swiglu")
+    for r in range(9):
+        y1 = to_np(ops.qmv_k(W, xd[r:r + 1].contiguous(), mode=ops.MODE_GATEUP_SWIGLU))[0]
+        assert np.array_equal(y9[r], y1)
+
+
+@pytest.mark.parametrize("N,K", [(2560, 640), (300, 512), (64, 2048)])
+def test_fp32_activations(N, K):
+    banner(f"qmv fp32 act N={N} K={K}")
+    ops = _ops()
+    codes, scales, biases = synth.dense_weight(4, 4, 5, N, K)
+    h = np.random.default_rng(N + K).standard_normal((9, K)).astype(np.float32) * np.float32(0.3)
+    W = q4_device_from_host(codes, scales, biases)
+    hd = sdev.upload_f32(h, DEV)
+    ref = oracle.qmv(codes, scales, biases, h.astype(np.float64))
+    y9 = to_np(ops.qmv_k(W, hd))
+    assert_close(y9, ref, "fp32 activations")
+    for r in (0, 4, 8):
+        y1 = to_np(ops.qmv_k(W, hd[r:r + 1].contiguous()))[0]
+        assert np.array_equal(y9[r], y1)
+
+
+def test_mfma_row_position_independence():
+    """A row's result must not depend on where it sits among the activation
+    rows: permuting the rows permutes the outputs bit for bit."""
+    banner("qmv row permutation")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(1, 3, 512, 1024, 9)
+    W = q4_device_from_host(codes, scales, biases)
+    y = to_np(ops.qmv_k(W, sdev.upload_bf16(x, DEV)))
+    perm = np.array([8, 3, 0, 5, 1, 7, 2, 6, 4])
+    yp = to_np(ops.qmv_k(W, sdev.upload_bf16(np.ascontiguousarray(x[perm]), DEV)))
+    assert np.array_equal(yp, y[perm])
+
+
+def test_repeat_is_deterministic():
+    banner("qmv determinism")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(1, 4, 2048, 2048, 9)
+    W = q4_device_from_host(codes, scales, biases)
+    xd = sdev.upload_bf16(x, DEV)
+    a = to_np(ops.qmv_k(W, xd))
+    b = to_np(ops.qmv_k(W, xd))
+    assert np.array_equal(a, b)
