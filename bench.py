@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of one exact k-row verification step on one MI355X.
+
+Workload (default ``flashnext_k9``): the Flash-Next-shaped hybrid at k = 9
+draft rows.  One step runs, for each of the 48 layers, the Gated DeltaNet
+verify with per-row snapshots (on the 36 layers with l % 4 != 3) and the MoE
+verify (router dispatch and union over 512 experts, top-10 sigmoid scores
+renormalised; gathered fused gate/up + SwiGLU and down projection over the
+union's affine-Q4/g64 experts [512, 1280, 2560] / [512, 2560, 640]; the
+sigmoid-gated shared expert; the fixed-order combine), then rolls every GDN
+layer back to an accepted prefix j ~ U{0..9} by slot selection.  All inputs
+are synthetic (synth/), generated before timing and resident in HBM: 67.9 GB
+of expert weights, 48 shared experts and 36 fp32 GDN state pools.
+
+Prints one JSON line: verified rows/s (k rows per step), the roofline of the
+dominant kernel (the gathered gate/up product, timed with HIP events on its
+stream inside the timed region), a per-kernel breakdown from a separate
+instrumented pass, and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified rows/s and achieved HBM GB/s (% of peak) for k-row Q4 verify + GDN"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+DOMINANT = "gate_up"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="flashnext_k9", choices=["flashnext_k9"])
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel instrumented pass")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain device copy of known size (PMC counter calibration)")
+    return p.parse_args()
+
+
+def q4_bytes(n, k):
+    return n * k // 2 + n * (k // 64) * 4
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("q4_matvec.hip", "common.h"):
+        with open(os.path.join(ROOT, "speculative_decode_verification_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+class Workload:
+    """Device-resident inputs and bound launches of the flashnext_k9 step."""
+
+    def __init__(self, dev, k=9):
+        import torch
+        import synth
+        from synth import configs
+        from synth import device as sdev
+        from synth.inputs import DOWN, GATEUP, SHARED_DOWN, SHARED_GATEUP
+        from speculative_decode_verification_amd import ops, pipeline
+
+        cfg = configs.C4
+        m, gs = cfg.moe, cfg.gdn
+        self.k, self.cfg = k, cfg
+        self.E, self.H, self.I, self.topk = m.experts, m.hidden, m.inter, m.topk
+        self.layers = cfg.layers
+        self.gdn_ids = list(cfg.gdn_layers)
+        self.gs = gs
+        self.moe, self.calls, self.gdn = [], [], {}
+        t0 = time.time()
+        for l in range(self.layers):
+            gu = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, GATEUP, l), self.E, 2 * self.I, self.H, dev))
+            dn = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, DOWN, l), self.E, self.H, self.I, dev))
+            sgu = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, SHARED_GATEUP, l), 1, 2 * self.I, self.H, dev))
+            sdn = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, SHARED_DOWN, l), 1, self.H, self.I, dev))
+            inp = synth.moe_layer_inputs(cfg.cid, l, k, self.H, self.E)
+            x, lg, z = (sdev.upload_bf16(inp["x"], dev), sdev.upload_f32(inp["logits"], dev),
+                        sdev.upload_f32(inp["z"], dev))
+            layer = pipeline.MoeLayer(gu, dn, k, self.topk, ops.ROUTE_SIGMOID, m.renorm, sgu, sdn)
+            self.moe.append((layer, x, lg, z))
+            self.calls.append(layer.bind(x, lg, z))
+        for l in self.gdn_ids:
+            S0 = sdev.upload_f32(synth.gdn_state(cfg.cid, l, gs.hv, gs.dv, gs.dk), dev)
+            gi = synth.gdn_layer_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
+            d = {n: sdev.upload_f32(v, dev) for n, v in gi.items()}
+            gl = pipeline.GdnLayer(S0, k).bind(d["q"], d["k"], d["v"], d["g"], d["beta"])
+            self.gdn[l] = (gl, d)
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+        self.bank_bytes = self.layers * (self.E + 1) * (q4_bytes(2 * self.I, self.H) + q4_bytes(self.H, self.I))
+
+    def step(self, s, js, events=None, per_kernel=None):
+        import torch
+        for l in range(self.layers):
+            g = self.gdn.get(l)
+            if g is not None:
+                if per_kernel is not None:
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    g[0].run_bound()
+                    b.record()
+                    per_kernel.append(("gdn", l, a, b))
+                else:
+                    g[0].run_bound()
+            for name, call in self.calls[l]:
+                if per_kernel is not None:
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    call()
+                    b.record()
+                    per_kernel.append((name, l, a, b))
+                elif events is not None and name == DOMINANT:
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    call()
+                    b.record()
+                    events.append((l, a, b))
+                else:
+                    call()
+        j = js[s % len(js)]
+        for gl, _ in self.gdn.values():
+            gl.rollback(j)
+
+    def unions(self):
+        return [int(layer.route.n_union.item()) for layer, *_ in self.moe]
+
+    def kernel_bytes(self, name, l, unions):
+        k, H, I, topk, E = self.k, self.H, self.I, self.topk, self.E
+        U = unions[l]
+        if name == "route":
+            return k * E * 4 + k * topk * 4 * 5 + 8
+        if name == "gate_up":
+            return U * q4_bytes(2 * I, H) + k * H * 2 + k * topk * I * 4
+        if name == "down":
+            return U * q4_bytes(H, I) + k * topk * I * 4 + k * topk * H * 4
+        if name == "shared_gate_up":
+            return q4_bytes(2 * I, H) + k * H * 2 + k * I * 4
+        if name == "shared_down":
+            return q4_bytes(H, I) + k * I * 4 + k * H * 4
+        if name == "combine":
+            return k * topk * H * 4 + k * topk * 4 + k * H * 4 + k * 4 + k * H * 4
+        if name == "gdn":
+            g = self.gs
+            return ((k + 1) * g.hv * g.dv * g.dk * 4 + 2 * k * g.hk * g.dk * 4 + 2 * k * g.hv * g.dv * 4
+                    + 2 * k * g.hv * 4)
+        raise KeyError(name)
+
+    def step_bytes(self, unions):
+        total = 0
+        for l in range(self.layers):
+            for name, _ in self.calls[l]:
+                total += self.kernel_bytes(name, l, unions)
+            if l in self.gdn:
+                total += self.kernel_bytes("gdn", l, unions)
+        return total
+
+
+def traffic_for(kernel_hash):
+    """Counter-measured HBM bytes per launch of the dominant kernel, if the
+    committed counter summary was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, "traffic_gather_gate_up_flashnext_k9.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(k=9):
+    """The CPU oracle on a bounded sample of the same workload: one MoE layer
+    (route, union, gate/up, down, shared expert, combine; its union experts
+    regenerated on the host before timing) and one GDN layer, scaled to the
+    48 MoE + 36 GDN layers of a step."""
+    import numpy as np
+    import oracle
+    import synth
+    from synth import configs
+    from synth.inputs import DOWN, GATEUP, SHARED_DOWN, SHARED_GATEUP
+
+    cfg = configs.C4
+    m, gs = cfg.moe, cfg.gdn
+    E, H, I, topk = m.experts, m.hidden, m.inter, m.topk
+    l = 0
+    inp = synth.moe_layer_inputs(cfg.cid, l, k, H, E)
+    idx, _ = oracle.route(inp["logits"], topk, m.mode, m.renorm)
+    used = sorted(set(idx.ravel().tolist()))
+    gk, dk = synth.bank_keys(cfg.cid, GATEUP, l), synth.bank_keys(cfg.cid, DOWN, l)
+    packed_g = {e: synth.q4_rows(gk, E, 2 * I, H, expert=e) for e in used}
+    packed_d = {e: synth.q4_rows(dk, E, H, I, expert=e) for e in used}
+    sgu = synth.dense_weight(cfg.cid, SHARED_GATEUP, l, 2 * I, H)
+    sdn = synth.dense_weight(cfg.cid, SHARED_DOWN, l, H, I)
+    S = synth.gdn_state(cfg.cid, cfg.gdn_layers[0], gs.hv, gs.dv, gs.dk)
+    gi = synth.gdn_layer_inputs(cfg.cid, cfg.gdn_layers[0], k, gs.hv, gs.hk, gs.dk, gs.dv)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], lambda e: oracle.dequant(*packed_g[e]),
+                      lambda e: oracle.dequant(*packed_d[e]), topk, m.mode, m.renorm, z=inp["z"],
+                      shared_gate_up=oracle.dequant(*sgu), shared_down=oracle.dequant(*sdn))
+    t_moe = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gdn_verify(S, gi["q"], gi["k"], gi["v"], gi["g"], gi["beta"])
+    t_gdn = time.perf_counter() - t0
+    step = cfg.layers * t_moe + len(cfg.gdn_layers) * t_gdn
+    return {"value": k / step, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": (f"flashnext_k9 layer 0: one MoE layer ({len(used)} union experts, {t_moe:.2f} s) and "
+                       f"one GDN layer ({t_gdn:.3f} s) of the oracle (numpy fp64), scaled to 48 MoE + 36 GDN "
+                       f"layers per step ({step:.1f} s per 9-row step)"),
+            "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
+
+
+def copy_probe():
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies of {a.numel() * 4} bytes")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        log(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+            "the per-GPU shard of the verify step is the single-GPU workload.")
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
+    from speculative_decode_verification_amd import _lib
+    _lib.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    k = 9
+    log("building workload (device-filled banks) ...")
+    wl = Workload(dev, k)
+    log(f"workload ready in {wl.setup_s:.1f} s: {wl.bank_bytes / 1e9:.1f} GB of Q4 banks, "
+        f"{len(wl.gdn)} GDN layers")
+    import synth
+    js = [synth.accepted_prefix(wl.cfg.cid, s, k) for s in range(max(64, args.steps + args.warmup))]
+
+    for s in range(args.warmup):
+        wl.step(s, js)
+    torch.cuda.synchronize()
+    unions = wl.unions()
+
+    events = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        wl.step(args.warmup + s, js, events=events)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    rows_per_s = k * args.steps / (ms_total / 1e3)
+    step_bytes = wl.step_bytes(unions)
+
+    dom_us = [a.elapsed_time(b) * 1e3 for (_, a, b) in events]
+    dom_bytes = [wl.kernel_bytes(DOMINANT, l, unions) for (l, _, _) in events]
+    dom_avg_us = sum(dom_us) / len(dom_us)
+    dom_gbs = sum(dom_bytes) / (sum(dom_us) * 1e-6) / 1e9
+    khash = kernel_source_hash()
+    traffic = traffic_for(khash)
+
+    breakdown = None
+    if not args.no_breakdown:
+        per = []
+        wl.step(args.warmup + args.steps, js, per_kernel=per)
+        torch.cuda.synchronize()
+        agg = {}
+        for name, l, a, b in per:
+            us = a.elapsed_time(b) * 1e3
+            d = agg.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0})
+            d["launches"] += 1
+            d["us"] += us
+            d["bytes"] += wl.kernel_bytes(name, l, unions)
+        breakdown = {n: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 2),
+                         "share_of_step": round(d["us"] / 1e3 / ms_step, 3),
+                         "gbs": round(d["bytes"] / (d["us"] * 1e-6) / 1e9, 1),
+                         "frac_hbm": round(d["bytes"] / (d["us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+                     for n, d in agg.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(k)
+
+    out = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "flashnext_k9", "rows": k, "layers": wl.layers, "gdn_layers": len(wl.gdn),
+                   "experts": wl.E, "topk": wl.topk, "hidden": wl.H, "inter": wl.I, "shared_expert": True,
+                   "gdn_heads": [wl.gs.hv, wl.gs.hk, wl.gs.dk], "mean_union": round(sum(unions) / len(unions), 2),
+                   "bytes_per_step": step_bytes},
+        "hbm_gbs_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac_step": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 3), "traffic": traffic,
+                     "kernel": "q4_matvec_kernel<GATEUP_SWIGLU, BF16, gathered> (sdv_gather_qmv_k gate/up)",
+                     "avg_launch_us": round(dom_avg_us, 2),
+                     "bytes_per_launch": round(sum(dom_bytes) / len(dom_bytes)),
+                     "kernel_source_hash": khash},
+        "kernels": breakdown,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+        "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "host_cpu": cpu_model()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -204,3 +204,83 @@ def gdn_rollback_copy(dst, S_in, snaps, j):
     check(lib().sdv_gdn_rollback_copy(_need(dst, "dst", torch.float32, n, dev), _need(S_in, "S_in", torch.float32, n, dev),
                                       arr, k, j, n, _stream(dst)))
     return dst
+
+
+class BoundCall:
+    """A library call with its arguments marshalled once (fixed buffers).
+
+    Calling it re-issues the same launch on the stream captured at bind time;
+    used where the same buffers are reused every step, so the per-launch host
+    cost is one ctypes call."""
+
+    def __init__(self, fn_name, args):
+        self._fn = getattr(lib(), fn_name)
+        self._args = tuple(args)
+        self.name = fn_name
+
+    def __call__(self):
+        check(self._fn(*self._args))
+
+
+def bind_qmv_k(W, act, mode, out):
+    k = act.shape[0]
+    n_out = W.N if mode == MODE_PLAIN else W.N // 2
+    if act.dim() != 2 or act.shape[1] != W.K:
+        raise ValueError(f"act must be [k, {W.K}]")
+    return BoundCall("sdv_qmv_k", [W.desc, _need(act, "act", act.dtype, device=W.device), _act_kind(act), k, mode,
+                                   _need(out, "out", torch.float32, k * n_out, W.device), _stream(out)])
+
+
+def bind_moe_route_k(logits, topk, score_mode, renorm, out):
+    k, E = logits.shape
+    kt = k * topk
+    dev = logits.device
+    return BoundCall("sdv_moe_route_k", [
+        _need(logits, "logits", torch.float32), k, E, topk, score_mode, int(bool(renorm)),
+        _need(out.idx, "idx", torch.int32, kt, dev), _need(out.w, "w", torch.float32, kt, dev),
+        _need(out.union_ids, "union_ids", torch.int32, kt, dev), _need(out.n_union, "n_union", torch.int32, 1, dev),
+        _need(out.pair_off, "pair_off", torch.int32, kt + 1, dev),
+        _need(out.pair_row, "pair_row", torch.int32, kt, dev),
+        _need(out.pair_slot, "pair_slot", torch.int32, kt, dev), _stream(logits)])
+
+
+def bind_gather_qmv_k(bank, mode, act, route, k, topk, out):
+    kind = _act_kind(act)
+    kt = k * topk
+    need_act = kt * bank.K if kind == ACT_F32 else k * bank.K
+    n_out = bank.N if mode == MODE_PLAIN else bank.N // 2
+    dev = bank.device
+    return BoundCall("sdv_gather_qmv_k", [
+        bank.desc, mode, _need(act, "act", act.dtype, need_act, dev), kind,
+        _need(route.union_ids, "union_ids", torch.int32, kt, dev), _need(route.n_union, "n_union", torch.int32, 1, dev),
+        _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
+        _need(route.pair_row, "pair_row", torch.int32, kt, dev),
+        _need(route.pair_slot, "pair_slot", torch.int32, kt, dev), k, topk,
+        _need(out, "out", torch.float32, kt * n_out, dev), _stream(out)])
+
+
+def bind_moe_combine_k(partial, w, shared_out, shared_logit, out):
+    k, topk, H = partial.shape
+    dev = partial.device
+    ps = _need(shared_out, "shared_out", torch.float32, k * H, dev) if shared_out is not None else None
+    pz = _need(shared_logit, "shared_logit", torch.float32, k, dev) if shared_logit is not None else None
+    return BoundCall("sdv_moe_combine_k", [
+        _need(partial, "partial", torch.float32, k * topk * H, dev), _need(w, "w", torch.float32, k * topk, dev),
+        ps, pz, k, topk, H, _need(out, "out", torch.float32, k * H, dev), _stream(out)])
+
+
+def bind_gdn_verify_k(S_in, q, kk, v, g, beta, snaps, y):
+    Hv, Dv, Dk = S_in.shape
+    k, Hk, _ = q.shape
+    dev = S_in.device
+    if len(snaps) != k or tuple(kk.shape) != (k, Hk, Dk) or tuple(v.shape) != (k, Hv, Dv):
+        raise ValueError("gdn shapes do not match")
+    if tuple(g.shape) != (k, Hv) or tuple(beta.shape) != (k, Hv):
+        raise ValueError("g/beta must be [k, Hv]")
+    st = Hv * Dv * Dk
+    arr = (ctypes.c_void_p * k)(*[_need(sn, f"snaps[{t}]", torch.float32, st, dev).value for t, sn in enumerate(snaps)])
+    return BoundCall("sdv_gdn_verify_k", [
+        _need(S_in, "S_in", torch.float32, st, dev), _need(q, "q", torch.float32, device=dev),
+        _need(kk, "kk", torch.float32, device=dev), _need(v, "v", torch.float32, device=dev),
+        _need(g, "g", torch.float32, device=dev), _need(beta, "beta", torch.float32, device=dev),
+        k, Hv, Hk, Dk, Dv, _need(y, "y", torch.float32, k * Hv * Dv, dev), arr, _stream(y)])

@@ -37,6 +37,21 @@ class MoeLayer:
         else:
             self.sh_h = self.sh_out = None
 
+    def bind(self, x, logits, z=None):
+        """Marshal the layer's launches once for fixed input buffers; returns a
+        list of (name, call) pairs to run in order."""
+        calls = [("route", ops.bind_moe_route_k(logits, self.topk, self.score_mode, self.renorm, self.route)),
+                 ("gate_up", ops.bind_gather_qmv_k(self.gate_up, MODE_GATEUP_SWIGLU, x, self.route, self.k,
+                                                   self.topk, self.h)),
+                 ("down", ops.bind_gather_qmv_k(self.down, MODE_PLAIN, self.h, self.route, self.k, self.topk,
+                                                self.partial))]
+        if self.shared_gate_up is not None:
+            calls.append(("shared_gate_up", ops.bind_qmv_k(self.shared_gate_up, x, MODE_GATEUP_SWIGLU, self.sh_h)))
+            calls.append(("shared_down", ops.bind_qmv_k(self.shared_down, self.sh_h, MODE_PLAIN, self.sh_out)))
+        calls.append(("combine", ops.bind_moe_combine_k(self.partial, self.route.w, self.sh_out,
+                                                        z if self.sh_out is not None else None, self.y)))
+        return calls
+
     def __call__(self, x, logits, z=None):
         """x: bf16 bits [k, H] (int16); logits fp32 [k, E]; z fp32 [k] or None."""
         ops.moe_route_k(logits, self.topk, self.score_mode, self.renorm, out=self.route)
@@ -72,6 +87,24 @@ class GdnLayer:
         y = self.y[:rows]
         ops.gdn_verify_k(self.state, q, kk, v, g, beta, [self.slots[i] for i in self.snap_ids], y=y)
         return y
+
+    def bind(self, q, kk, v, g, beta):
+        """Marshal the verify launch once per possible live slot for fixed
+        input buffers; ``run_bound`` then issues the one matching the live slot."""
+        rows = q.shape[0]
+        self._bound = []
+        for live in range(len(self.slots)):
+            ids = [i for i in range(len(self.slots)) if i != live][:rows]
+            call = ops.bind_gdn_verify_k(self.slots[live], q, kk, v, g, beta, [self.slots[i] for i in ids],
+                                         self.y[:rows])
+            self._bound.append((ids, call))
+        return self
+
+    def run_bound(self):
+        ids, call = self._bound[self.live]
+        self.snap_ids = ids
+        call()
+        return self.y
 
     def rollback(self, j):
         """Make the state after the accepted prefix of j rows live (no copy)."""
