@@ -96,11 +96,16 @@ class Workload:
         self.gs = gs
         self.moe, self.calls, self.gdn = [], [], {}
         t0 = time.time()
+        def bank(kind, l, E, N, K, fused):
+            # generated row-major in a scratch bank, then rewritten in the tiled layout
+            rm = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, kind, l), E, N, K, dev))
+            return rm.tiled(fused_gateup=fused)
+
         for l in range(self.layers):
-            gu = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, GATEUP, l), self.E, 2 * self.I, self.H, dev))
-            dn = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, DOWN, l), self.E, self.H, self.I, dev))
-            sgu = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, SHARED_GATEUP, l), 1, 2 * self.I, self.H, dev))
-            sdn = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, SHARED_DOWN, l), 1, self.H, self.I, dev))
+            gu = bank(GATEUP, l, self.E, 2 * self.I, self.H, True)
+            dn = bank(DOWN, l, self.E, self.H, self.I, False)
+            sgu = bank(SHARED_GATEUP, l, 1, 2 * self.I, self.H, True)
+            sdn = bank(SHARED_DOWN, l, 1, self.H, self.I, False)
             inp = synth.moe_layer_inputs(cfg.cid, l, k, self.H, self.E)
             x, lg, z = (sdev.upload_bf16(inp["x"], dev), sdev.upload_f32(inp["logits"], dev),
                         sdev.upload_f32(inp["z"], dev))
@@ -157,10 +162,13 @@ class Workload:
         U = unions[l]
         if name == "route":
             return k * E * 4 + k * topk * 4 * 5 + 8
+        # with the shared expert in the gathered launches, each reads one more
+        # weight (its activations: the same x for gate/up, its own h for down)
+        sh = 1 if self.moe[l][0].fused_shared else 0
         if name == "gate_up":
-            return U * q4_bytes(2 * I, H) + k * H * 2 + k * topk * I * 4
+            return (U + sh) * q4_bytes(2 * I, H) + k * H * 2 + (k * topk + sh * k) * I * 4
         if name == "down":
-            return U * q4_bytes(H, I) + k * topk * I * 4 + k * topk * H * 4
+            return (U + sh) * q4_bytes(H, I) + (k * topk + sh * k) * (I + H) * 4
         if name == "shared_gate_up":
             return q4_bytes(2 * I, H) + k * H * 2 + k * I * 4
         if name == "shared_down":

@@ -79,7 +79,8 @@ typedef void *sdv_stream_t; /* hipStream_t */
 #define SDV_ROUTE_SIGMOID 1 /* independent sigmoid per logit */
 
 /*
- * An affine-Q4, group-64 weight: E matrices of N rows by K inputs.
+ * An affine-Q4, group-64 weight in row-major interchange layout: E matrices of
+ * N rows by K inputs.
  *   codes  [E][N][K/8] uint32: element 8w+i of a row in bits [4i, 4i+4) of word w,
  *          an unsigned code q in 0..15
  *   scales [E][N][K/64] bf16, biases [E][N][K/64] bf16
@@ -87,7 +88,8 @@ typedef void *sdv_stream_t; /* hipStream_t */
  * E = 1 is a dense matrix.  group must be 64 and K a positive multiple of 64.
  * (mere.run transfer report, "Shared architecture and implemented paths":
  * affine Q4, group size 64, compatible bf16 tensors; the nibble order is this
- * library's definition.)
+ * library's definition.)  The products read the tiled layout below, written
+ * once per weight by sdv_q4_repack.
  */
 typedef struct sdv_q4 {
   const uint32_t *codes;
@@ -97,21 +99,55 @@ typedef struct sdv_q4 {
 } sdv_q4;
 
 /*
+ * The same weight in the tiled layout the kernels stream (written by
+ * sdv_q4_repack).  Columns are grouped into T tiles of 32 weight rows:
+ *   fused_gateup = 0: tile t holds rows 32t .. 32t+31 (T = ceil(N/32));
+ *   fused_gateup = 1: the rows are [gate; up] halves of N/2 each, and tile t
+ *     holds gate rows 16t .. 16t+15 then up rows N/2+16t .. (T = ceil(N/32)).
+ *   codes  [E][T][K/64][64][16 bytes]: for tile t and group g, 16-byte chunk
+ *          l = 32h + c holds words 4h .. 4h+3 of group g of the tile's row c;
+ *   sb     [E][T][K/64][32] uint32: scale bits | bias bits << 16 of row c.
+ * Padding rows (past N) are zero.  Sizes: sdv_q4t_codes_bytes / sdv_q4t_sb_bytes.
+ */
+typedef struct sdv_q4t {
+  const void *codes;
+  const uint32_t *sb;
+  int32_t E, N, K, group;
+  int32_t fused_gateup;
+} sdv_q4t;
+
+/* Bytes of the tiled codes / scale-bias arrays of an E x N x K weight. */
+SDV_API size_t sdv_q4t_codes_bytes(int E, int N, int K, int fused_gateup);
+SDV_API size_t sdv_q4t_sb_bytes(int E, int N, int K, int fused_gateup);
+
+/*
+ * sdv_q4_repack -- rewrite a row-major weight into the tiled layout (device to
+ * device, on `stream`).  fused_gateup = 1 pairs row i of the first half with
+ * row N/2 + i in one tile (N must be even) for SDV_MODE_GATEUP_SWIGLU.
+ *   src        row-major descriptor (device arrays)
+ *   codes_out  device, sdv_q4t_codes_bytes(...) bytes; sb_out device, sdv_q4t_sb_bytes(...)
+ * Errors: EINVAL, ELAYOUT, EALIAS, EHIP.
+ */
+SDV_API int sdv_q4_repack(const sdv_q4 *src, int fused_gateup, void *codes_out, uint32_t *sb_out,
+                          sdv_stream_t stream);
+
+/*
  * sdv_qmv_k -- dense multi-row affine-Q4 matvec (E must be 1).
  * The width-k product decodes each weight once for all k rows; each row
  * equals the width-1 result bit for bit (mere.run report, "Exact verification
  * kernels and benchmark admission": small-batch Q4 kernel against serial QMV
  * with exact agreement at widths 4, 8, 9; Red Lite dev45 "What it is": decode
  * each weight once and compute each row in the 1-row kernel's order).
- *   W         weight descriptor (host struct, device arrays)
+ *   W         tiled weight descriptor (host struct, device arrays)
  *   act       device, [k][K]: bf16 bits (act_dtype SDV_ACT_BF16) or fp32 (SDV_ACT_F32)
  *   k         rows, 1..9
- *   mode      SDV_MODE_PLAIN: y [k][N];  SDV_MODE_GATEUP_SWIGLU: N even, y [k][N/2]
+ *   mode      SDV_MODE_PLAIN: y [k][N], needs fused_gateup = 0;
+ *             SDV_MODE_GATEUP_SWIGLU: y [k][N/2], needs fused_gateup = 1
  *   y         device fp32 output
- * Errors: EINVAL, EWIDTH, ELAYOUT, EALIAS, EHIP.
+ * Errors: EINVAL, EWIDTH, ELAYOUT (also a mode that does not match the layout), EALIAS, EHIP.
  */
-SDV_API int sdv_qmv_k(const sdv_q4 *W, const void *act, int act_dtype, int k, int mode, float *y,
-              sdv_stream_t stream);
+SDV_API int sdv_qmv_k(const sdv_q4t *W, const void *act, int act_dtype, int k, int mode, float *y,
+                      sdv_stream_t stream);
 
 /*
  * sdv_moe_route_k -- one router dispatch for all k rows: per-row top-k, the
@@ -128,7 +164,10 @@ SDV_API int sdv_qmv_k(const sdv_q4 *W, const void *act, int act_dtype, int k, in
  *   n_union    device int32 [1]
  *   pair_off   device int32 [k*topk + 1]: pairs of union entry u are [pair_off[u], pair_off[u+1])
  *   pair_row, pair_slot  device int32 [k*topk]: ordered by (expert, row) ascending
- * E in topk..1024, topk in 1..16.  Errors: EINVAL, EWIDTH, ERANGE, EALIAS, EHIP.
+ * E in topk..1024, topk in 1..16.  NaN logits are never preferred to a number;
+ * a slot left with no candidate (all remaining logits NaN) gets idx -1 and no
+ * pair, so every written index and pair stays in range.
+ * Errors: EINVAL, EWIDTH, ERANGE, EALIAS, EHIP.
  */
 SDV_API int sdv_moe_route_k(const float *logits, int k, int E, int topk, int score_mode, int renorm,
                     int32_t *idx, float *w, int32_t *union_ids, int32_t *n_union,
@@ -142,20 +181,29 @@ SDV_API int sdv_moe_route_k(const float *logits, int k, int E, int topk, int sco
  * admission": gathered expert kernel, affine Q4/group 64, widths 2..9, fused
  * gate/up weights, unsupported layouts rejected; Red Lite dev45: the (expert,
  * row) pairs share one pool encode with a two-input gate/up pipeline).
- *   bank       weight descriptor, E experts of [N][K]
- *   mode       SDV_MODE_GATEUP_SWIGLU (fused [gate; up] rows, output N/2) or SDV_MODE_PLAIN
+ *   bank       tiled weight descriptor, E experts of [N][K]
+ *   mode       SDV_MODE_GATEUP_SWIGLU (fused [gate; up] rows, output N/2; needs
+ *              fused_gateup = 1) or SDV_MODE_PLAIN (needs fused_gateup = 0)
  *   act        device: SDV_ACT_BF16 shared rows [k][K] (row r's input for every slot),
  *              or SDV_ACT_F32 per pair [k][topk][K] (e.g. the SwiGLU output)
  *   union_ids, n_union, pair_off, pair_row, pair_slot  device, as written by sdv_moe_route_k
  *   out        device fp32 [k][topk][N or N/2]; entry (r, s) holds expert idx[r][s]'s output
- * The grid covers k*topk union entries and entries past n_union exit; expert
- * ids, rows and slots outside their ranges are skipped on the device.
+ *   shared     optional always-on expert (Flash-Next plan "2.3 MoE": one shared
+ *              expert beside the routed ones): a tiled descriptor with E = 1 and
+ *              the bank's N, K and fused_gateup, applied to all k rows in the same
+ *              launch; NULL for none (then shared_act and shared_out must be NULL)
+ *   shared_act device, the shared expert's rows [k][K] in act_dtype
+ *   shared_out device fp32 [k][N or N/2]
+ * The grid covers k*topk union entries (plus one for the shared expert) and
+ * entries past n_union exit; expert ids, rows and slots outside their ranges
+ * are skipped on the device.
  * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE, EALIAS, EHIP.
  */
-SDV_API int sdv_gather_qmv_k(const sdv_q4 *bank, int mode, const void *act, int act_dtype,
+SDV_API int sdv_gather_qmv_k(const sdv_q4t *bank, int mode, const void *act, int act_dtype,
                      const int32_t *union_ids, const int32_t *n_union, const int32_t *pair_off,
                      const int32_t *pair_row, const int32_t *pair_slot, int k, int topk,
-                     float *out, sdv_stream_t stream);
+                     float *out, const sdv_q4t *shared, const void *shared_act,
+                     float *shared_out, sdv_stream_t stream);
 
 /*
  * sdv_moe_combine_k -- one MoE tail for all rows (Red Lite dev45, "What it

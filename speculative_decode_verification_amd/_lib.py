@@ -11,15 +11,21 @@ MODE_PLAIN, MODE_GATEUP_SWIGLU = 0, 1
 ACT_BF16, ACT_F32 = 0, 1
 ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1
 
-EXPORTS = ("sdv_qmv_k", "sdv_moe_route_k", "sdv_gather_qmv_k", "sdv_moe_combine_k", "sdv_gdn_verify_k",
-           "sdv_gdn_rollback", "sdv_gdn_rollback_copy", "sdv_status_string", "sdv_last_error",
-           "sdv_build_info")
+EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_qmv_k", "sdv_moe_route_k",
+           "sdv_gather_qmv_k", "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
+           "sdv_gdn_rollback_copy", "sdv_status_string", "sdv_last_error", "sdv_build_info")
 
 
 class SdvQ4(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("group", ctypes.c_int32)]
+
+
+class SdvQ4T(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("sb", ctypes.c_void_p), ("E", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("fused_gateup", ctypes.c_int32)]
 
 
 class SdvError(RuntimeError):
@@ -33,9 +39,13 @@ _LIB = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SIGS = {
-    "sdv_qmv_k": [ctypes.POINTER(SdvQ4), _P, _I, _I, _I, _P, _P],
+    "sdv_q4t_codes_bytes": [_I, _I, _I, _I],
+    "sdv_q4t_sb_bytes": [_I, _I, _I, _I],
+    "sdv_q4_repack": [ctypes.POINTER(SdvQ4), _I, _P, _P, _P],
+    "sdv_qmv_k": [ctypes.POINTER(SdvQ4T), _P, _I, _I, _I, _P, _P],
     "sdv_moe_route_k": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
-    "sdv_gather_qmv_k": [ctypes.POINTER(SdvQ4), _I, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P],
+    "sdv_gather_qmv_k": [ctypes.POINTER(SdvQ4T), _I, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P,
+                         ctypes.POINTER(SdvQ4T), _P, _P, _P],
     "sdv_moe_combine_k": [_P, _P, _P, _P, _I, _I, _I, _P, _P],
     "sdv_gdn_verify_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_P), _P],
     "sdv_gdn_rollback": [_I, _I, ctypes.POINTER(_I)],
@@ -57,8 +67,12 @@ def lib():
         for name, args in _SIGS.items():
             fn = getattr(L, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name in ("sdv_status_string", "sdv_last_error",
-                                                     "sdv_build_info") else ctypes.c_int
+            if name in ("sdv_status_string", "sdv_last_error", "sdv_build_info"):
+                fn.restype = ctypes.c_char_p
+            elif name in ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes"):
+                fn.restype = ctypes.c_size_t
+            else:
+                fn.restype = ctypes.c_int
         _LIB = L
     return _LIB
 

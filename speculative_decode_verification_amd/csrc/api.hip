@@ -8,12 +8,15 @@
 #include "common.h"
 
 namespace sdv {
-hipError_t q4_launch(const sdv_q4& W, int mode, const void* act, int act_dtype, bool gather,
+hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, bool gather,
                      const int32_t* union_ids, const int32_t* n_union, const int32_t* pair_off,
                      const int32_t* pair_row, const int32_t* pair_slot, int k, int topk, float* out,
-                     hipStream_t st);
+                     const sdv_q4t* shared, const void* shared_act, float* shared_out, hipStream_t st);
 int q4_waves_for(int K);
-size_t q4_lds_bytes(int K, int vrow_cap, int nw);
+size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather);
+size_t q4t_codes_bytes(int E, int N, int K, int fused);
+size_t q4t_sb_bytes(int E, int N, int K, int fused);
+hipError_t q4_repack_launch(const sdv_q4& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st);
 hipError_t route_launch(const float* logits, int k, int E, int topk, int mode, int renorm,
                         int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
                         int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot, hipStream_t st);
@@ -97,6 +100,29 @@ int check_q4(const sdv_q4* W, const char* what) {
 size_t q4_codes_bytes(const sdv_q4& W) { return (size_t)W.E * W.N * (W.K / 8) * 4; }
 size_t q4_sb_bytes(const sdv_q4& W) { return (size_t)W.E * W.N * (W.K / 64) * 2; }
 
+int check_q4t(const sdv_q4t* W, const char* what) {
+  if (!W) return fail(SDV_EINVAL, "%s descriptor is NULL", what);
+  if (W->group != SDV_GROUP) return fail(SDV_ELAYOUT, "%s group=%d, only 64 is supported", what, W->group);
+  if (W->K <= 0 || W->K % SDV_GROUP) return fail(SDV_ELAYOUT, "%s K=%d is not a positive multiple of 64", what, W->K);
+  if (W->N <= 0 || W->E <= 0) return fail(SDV_EINVAL, "%s E=%d N=%d must be positive", what, W->E, W->N);
+  if (W->fused_gateup != 0 && W->fused_gateup != 1)
+    return fail(SDV_ELAYOUT, "%s fused_gateup=%d must be 0 or 1", what, W->fused_gateup);
+  if (W->fused_gateup && (W->N % 2)) return fail(SDV_ELAYOUT, "%s fused gate/up needs an even N", what);
+  int st;
+  if ((st = check_ptr(W->codes, "codes"))) return st;
+  if ((st = check_ptr(W->sb, "sb"))) return st;
+  return SDV_OK;
+}
+
+// The product mode must match the tile layout ("rejects unsupported layouts").
+int check_mode_layout(int mode, const sdv_q4t& W) {
+  if (mode == SDV_MODE_GATEUP_SWIGLU && !W.fused_gateup)
+    return fail(SDV_ELAYOUT, "gate/up SwiGLU needs a weight repacked with fused_gateup=1");
+  if (mode == SDV_MODE_PLAIN && W.fused_gateup)
+    return fail(SDV_ELAYOUT, "a plain product needs a weight repacked with fused_gateup=0");
+  return SDV_OK;
+}
+
 int check_mode(int mode, int act_dtype, int N) {
   if (mode != SDV_MODE_PLAIN && mode != SDV_MODE_GATEUP_SWIGLU)
     return fail(SDV_EINVAL, "unknown mode %d", mode);
@@ -107,9 +133,9 @@ int check_mode(int mode, int act_dtype, int N) {
   return SDV_OK;
 }
 
-int check_lds(const sdv_q4& W, int act_dtype, int k) {
+int check_lds(const sdv_q4t& W, int act_dtype, int k, bool gather) {
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
-  const size_t lds = sdv::q4_lds_bytes(W.K, cap, sdv::q4_waves_for(W.K));
+  const size_t lds = sdv::q4_lds_bytes_for(W.K, act_dtype, k, gather);
   if (lds > kMaxLds)
     return fail(SDV_ELAYOUT, "K=%d with %d activation rows needs %zu bytes of LDS (max %zu)", W.K, cap,
                 lds, kMaxLds);
@@ -142,26 +168,54 @@ const char* sdv_last_error(void) { return g_err; }
 
 const char* sdv_build_info(void) { return "sdv 0.1 gfx950"; }
 
-int sdv_qmv_k(const sdv_q4* W, const void* act, int act_dtype, int k, int mode, float* y,
+size_t sdv_q4t_codes_bytes(int E, int N, int K, int fused_gateup) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % SDV_GROUP) return 0;
+  return sdv::q4t_codes_bytes(E, N, K, fused_gateup ? 1 : 0);
+}
+
+size_t sdv_q4t_sb_bytes(int E, int N, int K, int fused_gateup) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % SDV_GROUP) return 0;
+  return sdv::q4t_sb_bytes(E, N, K, fused_gateup ? 1 : 0);
+}
+
+int sdv_q4_repack(const sdv_q4* src, int fused_gateup, void* codes_out, uint32_t* sb_out, sdv_stream_t stream) {
+  int st;
+  if ((st = check_q4(src, "src"))) return st;
+  if (fused_gateup != 0 && fused_gateup != 1) return fail(SDV_ELAYOUT, "fused_gateup=%d must be 0 or 1", fused_gateup);
+  if (fused_gateup && (src->N % 2)) return fail(SDV_ELAYOUT, "fused gate/up needs an even N (got %d)", src->N);
+  if ((st = check_ptr(codes_out, "codes_out"))) return st;
+  if ((st = check_ptr(sb_out, "sb_out"))) return st;
+  Range outs[] = {{codes_out, sdv::q4t_codes_bytes(src->E, src->N, src->K, fused_gateup), "codes_out"},
+                  {sb_out, sdv::q4t_sb_bytes(src->E, src->N, src->K, fused_gateup), "sb_out"}};
+  Range ins[] = {{src->codes, q4_codes_bytes(*src), "codes"},
+                 {src->scales, q4_sb_bytes(*src), "scales"},
+                 {src->biases, q4_sb_bytes(*src), "biases"}};
+  if ((st = check_alias(outs, 2, ins, 3))) return st;
+  return hip_status(sdv::q4_repack_launch(*src, fused_gateup, codes_out, sb_out, (hipStream_t)stream),
+                    "sdv_q4_repack launch");
+}
+
+int sdv_qmv_k(const sdv_q4t* W, const void* act, int act_dtype, int k, int mode, float* y,
               sdv_stream_t stream) {
   int st;
-  if ((st = check_q4(W, "W"))) return st;
+  if ((st = check_q4t(W, "W"))) return st;
   if (W->E != 1) return fail(SDV_EINVAL, "dense product needs E=1 (got %d)", W->E);
   if ((st = check_width(k))) return st;
   if ((st = check_mode(mode, act_dtype, W->N))) return st;
+  if ((st = check_mode_layout(mode, *W))) return st;
   if ((st = check_ptr(act, "act"))) return st;
   if ((st = check_ptr(y, "y"))) return st;
-  if ((st = check_lds(*W, act_dtype, k))) return st;
+  if ((st = check_lds(*W, act_dtype, k, false))) return st;
   const size_t act_bytes = (size_t)k * W->K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
   const size_t n_out = mode == SDV_MODE_PLAIN ? W->N : W->N / 2;
   Range outs[] = {{y, (size_t)k * n_out * 4, "y"}};
-  Range ins[] = {{W->codes, q4_codes_bytes(*W), "codes"},
-                 {W->scales, q4_sb_bytes(*W), "scales"},
-                 {W->biases, q4_sb_bytes(*W), "biases"},
+  Range ins[] = {{W->codes, sdv::q4t_codes_bytes(W->E, W->N, W->K, W->fused_gateup), "codes"},
+                 {W->sb, sdv::q4t_sb_bytes(W->E, W->N, W->K, W->fused_gateup), "sb"},
                  {act, act_bytes, "act"}};
-  if ((st = check_alias(outs, 1, ins, 4))) return st;
+  if ((st = check_alias(outs, 1, ins, 3))) return st;
   return hip_status(sdv::q4_launch(*W, mode, act, act_dtype, false, nullptr, nullptr, nullptr,
-                                   nullptr, nullptr, k, 1, y, (hipStream_t)stream),
+                                   nullptr, nullptr, k, 1, y, nullptr, nullptr, nullptr,
+                                   (hipStream_t)stream),
                     "sdv_qmv_k launch");
 }
 
@@ -192,37 +246,56 @@ int sdv_moe_route_k(const float* logits, int k, int E, int topk, int score_mode,
                     "sdv_moe_route_k launch");
 }
 
-int sdv_gather_qmv_k(const sdv_q4* bank, int mode, const void* act, int act_dtype,
+int sdv_gather_qmv_k(const sdv_q4t* bank, int mode, const void* act, int act_dtype,
                      const int32_t* union_ids, const int32_t* n_union, const int32_t* pair_off,
                      const int32_t* pair_row, const int32_t* pair_slot, int k, int topk,
-                     float* out, sdv_stream_t stream) {
+                     float* out, const sdv_q4t* shared, const void* shared_act, float* shared_out,
+                     sdv_stream_t stream) {
   int st;
-  if ((st = check_q4(bank, "bank"))) return st;
+  if ((st = check_q4t(bank, "bank"))) return st;
   if ((st = check_width(k))) return st;
   if (topk < 1 || topk > SDV_MAX_TOPK || topk > bank->E)
     return fail(SDV_ERANGE, "topk=%d outside 1..min(E,%d)", topk, SDV_MAX_TOPK);
   if ((st = check_mode(mode, act_dtype, bank->N))) return st;
-  if ((st = check_lds(*bank, act_dtype, k))) return st;
+  if ((st = check_mode_layout(mode, *bank))) return st;
+  if ((st = check_lds(*bank, act_dtype, k, true))) return st;
   const void* ptrs[] = {act, union_ids, n_union, pair_off, pair_row, pair_slot, out};
   const char* names[] = {"act", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot", "out"};
   for (int i = 0; i < 7; ++i)
     if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  if (shared) {
+    if ((st = check_q4t(shared, "shared"))) return st;
+    if (shared->E != 1) return fail(SDV_EINVAL, "shared expert needs E=1 (got %d)", shared->E);
+    if (shared->N != bank->N || shared->K != bank->K || shared->fused_gateup != bank->fused_gateup)
+      return fail(SDV_ELAYOUT, "shared expert geometry (N=%d K=%d fused=%d) differs from the bank's (N=%d K=%d fused=%d)",
+                  shared->N, shared->K, shared->fused_gateup, bank->N, bank->K, bank->fused_gateup);
+    if ((st = check_ptr(shared_act, "shared_act"))) return st;
+    if ((st = check_ptr(shared_out, "shared_out"))) return st;
+  } else if (shared_act || shared_out) {
+    return fail(SDV_EINVAL, "shared_act/shared_out given without a shared expert");
+  }
   const size_t kt = (size_t)k * topk;
   const size_t act_bytes = act_dtype == SDV_ACT_F32 ? kt * bank->K * 4 : (size_t)k * bank->K * 2;
   const size_t n_out = mode == SDV_MODE_PLAIN ? bank->N : bank->N / 2;
-  Range outs[] = {{out, kt * n_out * 4, "out"}};
-  Range ins[] = {{bank->codes, q4_codes_bytes(*bank), "codes"},
-                 {bank->scales, q4_sb_bytes(*bank), "scales"},
-                 {bank->biases, q4_sb_bytes(*bank), "biases"},
+  const size_t sh_act_bytes = shared ? (size_t)k * bank->K * (act_dtype == SDV_ACT_F32 ? 4 : 2) : 0;
+  Range outs[] = {{out, kt * n_out * 4, "out"}, {shared_out, shared ? (size_t)k * n_out * 4 : 0, "shared_out"}};
+  Range ins[] = {{bank->codes, sdv::q4t_codes_bytes(bank->E, bank->N, bank->K, bank->fused_gateup), "codes"},
+                 {bank->sb, sdv::q4t_sb_bytes(bank->E, bank->N, bank->K, bank->fused_gateup), "sb"},
                  {act, act_bytes, "act"},
                  {union_ids, kt * 4, "union_ids"},
                  {n_union, 4, "n_union"},
                  {pair_off, (kt + 1) * 4, "pair_off"},
                  {pair_row, kt * 4, "pair_row"},
-                 {pair_slot, kt * 4, "pair_slot"}};
-  if ((st = check_alias(outs, 1, ins, 9))) return st;
+                 {pair_slot, kt * 4, "pair_slot"},
+                 {shared ? shared->codes : nullptr, shared ? sdv::q4t_codes_bytes(1, bank->N, bank->K, bank->fused_gateup) : 0,
+                  "shared codes"},
+                 {shared ? shared->sb : nullptr, shared ? sdv::q4t_sb_bytes(1, bank->N, bank->K, bank->fused_gateup) : 0,
+                  "shared sb"},
+                 {shared_act, sh_act_bytes, "shared_act"}};
+  if ((st = check_alias(outs, 2, ins, 11))) return st;
   return hip_status(sdv::q4_launch(*bank, mode, act, act_dtype, true, union_ids, n_union, pair_off,
-                                   pair_row, pair_slot, k, topk, out, (hipStream_t)stream),
+                                   pair_row, pair_slot, k, topk, out, shared, shared_act, shared_out,
+                                   (hipStream_t)stream),
                     "sdv_gather_qmv_k launch");
 }
 

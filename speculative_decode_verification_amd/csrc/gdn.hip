@@ -35,33 +35,83 @@ struct GdnArgs {
   float* snaps[SDV_MAX_ROWS];
 };
 
-template <int DK>
+constexpr int kRowsPerBlock = 16;  // 16 value rows x 16 lanes = 256 threads
+
+// LDS_KQ: the block's 16 value rows belong to one v head (Dv % 16 == 0), so
+// the per-row vectors k_t, q_t (for that head's qk head), v_t, g_t, beta_t of
+// all k rows are staged in LDS once and the serial t loop reads only LDS and
+// registers.  Otherwise they are read from global memory inside the loop.
+template <int DK, bool LDS_KQ>
 __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   constexpr int NV4 = DK / 64;  // float4 per lane
+  __shared__ float4 s_k[LDS_KQ ? SDV_MAX_ROWS * DK / 4 : 1];
+  __shared__ float4 s_q[LDS_KQ ? SDV_MAX_ROWS * DK / 4 : 1];
+  __shared__ float s_v[LDS_KQ ? SDV_MAX_ROWS * kRowsPerBlock : 1];
+  __shared__ float s_g[SDV_MAX_ROWS], s_b[SDV_MAX_ROWS];
+
   const int sub = threadIdx.x & 15;
-  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 4;  // h * Dv + i
+  const int lrow = threadIdx.x >> 4;
+  const long row = (long)blockIdx.x * kRowsPerBlock + lrow;  // h * Dv + i
   const long nrows = (long)a.Hv * a.Dv;
-  if (row >= nrows) return;  // whole 16-lane groups leave together
-  const int h = (int)(row / a.Dv);
-  const int i = (int)(row - (long)h * a.Dv);
+  const bool active = row < nrows;
+  const int h = active ? (int)(row / a.Dv) : 0;
+  const int i = active ? (int)(row - (long)h * a.Dv) : 0;
   const int c = h / (a.Hv / a.Hk);
 
   float4 S[NV4];
-  const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + row * DK);
+  if (active) {
+    const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + row * DK);
 #pragma unroll
-  for (int j = 0; j < NV4; ++j) S[j] = sin4[sub + 16 * j];
+    for (int j = 0; j < NV4; ++j) S[j] = sin4[sub + 16 * j];
+  }
+
+  if (LDS_KQ) {
+    // every row of the block is in head h0 (and qk head c0)
+    const long row0 = (long)blockIdx.x * kRowsPerBlock;
+    const int h0 = (int)(row0 / a.Dv);
+    const int i0 = (int)(row0 - (long)h0 * a.Dv);
+    const int c0 = h0 / (a.Hv / a.Hk);
+    const int n4 = a.k * DK / 4;
+    for (int t = threadIdx.x; t < n4; t += blockDim.x) {
+      const int tt = t / (DK / 4), jj = t - tt * (DK / 4);
+      s_k[t] = reinterpret_cast<const float4*>(a.kk + ((long)tt * a.Hk + c0) * DK)[jj];
+      s_q[t] = reinterpret_cast<const float4*>(a.q + ((long)tt * a.Hk + c0) * DK)[jj];
+    }
+    for (int t = threadIdx.x; t < a.k * kRowsPerBlock; t += blockDim.x) {
+      const int tt = t / kRowsPerBlock, r = t - tt * kRowsPerBlock;
+      s_v[t] = (row0 + r < nrows) ? a.v[((long)tt * a.Hv + h0) * a.Dv + i0 + r] : 0.0f;
+    }
+    if (threadIdx.x < a.k) {
+      s_g[threadIdx.x] = a.g[threadIdx.x * a.Hv + h0];
+      s_b[threadIdx.x] = a.beta[threadIdx.x * a.Hv + h0];
+    }
+    __syncthreads();
+  }
+  if (!active) return;  // whole 16-lane groups leave together
 
   for (int t = 0; t < a.k; ++t) {
-    const float gt = a.g[t * a.Hv + h];
-    const float bt = a.beta[t * a.Hv + h];
-    const float vt = a.v[((long)t * a.Hv + h) * a.Dv + i];
-    const float4* k4 = reinterpret_cast<const float4*>(a.kk + ((long)t * a.Hk + c) * DK);
-    const float4* q4 = reinterpret_cast<const float4*>(a.q + ((long)t * a.Hk + c) * DK);
+    float gt, bt, vt;
     float4 kt[NV4], qt[NV4];
+    if (LDS_KQ) {
+      gt = s_g[t];
+      bt = s_b[t];
+      vt = s_v[t * kRowsPerBlock + lrow];
 #pragma unroll
-    for (int j = 0; j < NV4; ++j) {
-      kt[j] = k4[sub + 16 * j];
-      qt[j] = q4[sub + 16 * j];
+      for (int j = 0; j < NV4; ++j) {
+        kt[j] = s_k[t * (DK / 4) + sub + 16 * j];
+        qt[j] = s_q[t * (DK / 4) + sub + 16 * j];
+      }
+    } else {
+      gt = a.g[t * a.Hv + h];
+      bt = a.beta[t * a.Hv + h];
+      vt = a.v[((long)t * a.Hv + h) * a.Dv + i];
+      const float4* k4 = reinterpret_cast<const float4*>(a.kk + ((long)t * a.Hk + c) * DK);
+      const float4* q4 = reinterpret_cast<const float4*>(a.q + ((long)t * a.Hk + c) * DK);
+#pragma unroll
+      for (int j = 0; j < NV4; ++j) {
+        kt[j] = k4[sub + 16 * j];
+        qt[j] = q4[sub + 16 * j];
+      }
     }
     // decay, then kv_mem on the decayed state
     float m = 0.0f;
@@ -117,13 +167,17 @@ hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const 
   a.Dv = Dv;
   a.y = y;
   for (int t = 0; t < SDV_MAX_ROWS; ++t) a.snaps[t] = t < k ? snaps[t] : nullptr;
-  const long threads_total = (long)Hv * Dv * 16;
-  const int block = 256;
-  const long blocks = (threads_total + block - 1) / block;
-  if (Dk == 64)
-    hipLaunchKernelGGL(gdn_verify_kernel<64>, dim3((unsigned)blocks), dim3(block), 0, st, a);
+  const long blocks = ((long)Hv * Dv + kRowsPerBlock - 1) / kRowsPerBlock;
+  const bool lds = (Dv % kRowsPerBlock) == 0;
+  const dim3 grid((unsigned)blocks), block(kRowsPerBlock * 16);
+  if (Dk == 64 && lds)
+    hipLaunchKernelGGL((gdn_verify_kernel<64, true>), grid, block, 0, st, a);
+  else if (Dk == 64)
+    hipLaunchKernelGGL((gdn_verify_kernel<64, false>), grid, block, 0, st, a);
+  else if (Dk == 128 && lds)
+    hipLaunchKernelGGL((gdn_verify_kernel<128, true>), grid, block, 0, st, a);
   else if (Dk == 128)
-    hipLaunchKernelGGL(gdn_verify_kernel<128>, dim3((unsigned)blocks), dim3(block), 0, st, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<128, false>), grid, block, 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -16,20 +16,42 @@
 //     s * P + (b - 128 s) * X to the output, X being the group sum of the
 //     activation row (computed once, in a fixed order, while staging).
 //   * Every output row's arithmetic depends only on its own activation row
-//     and the weights: the K partition (contiguous group ranges per wave,
-//     fixed by K), the per-group epilogue order and the cross-wave sum order
-//     do not depend on k or on which other rows share the expert, so a
-//     width-k row is bit-identical to the width-1 row.
+//     and the weights: the K partition (fixed by K), the per-group epilogue
+//     order and the cross-wave sum order do not depend on k or on which other
+//     rows share the expert, so a width-k row is bit-identical to the width-1
+//     row.
+//
+// Weight layout.  The kernels read the tiled layout written by
+// sdv_q4_repack: for expert e, tile t (32 weight rows) and group g, a 1 KB
+// block of codes in lane order (lane l = 32*half + col holds words
+// 4*half .. 4*half+3 of the group in row col) and a 128-byte block of 32
+// packed (scale | bias << 16) words.  A wave-step therefore reads 1 KB of
+// contiguous codes and one 128-byte line of scales and biases, instead of 32
+// scattered rows.  With fused gate/up weights, tile t holds gate rows
+// 16t .. 16t+15 in columns 0-15 and the matching up rows in columns 16-31.
+//
+// Work decomposition.  Gathered units (union experts) run one wave per weight
+// tile over the whole K: a workgroup of 8 waves takes 8 tiles of one expert,
+// stages that expert's activation rows once, and each wave streams its tile
+// through a ring of prefetched loads (8 groups deep).  The first loads are
+// issued before staging, and finished tiles go through LDS so no global store
+// sits among the stream's loads (on gfx9 loads and stores share one counter,
+// and a pending store forces full waits).  Dense matrices (few tiles, long K)
+// split K over the waves of a workgroup instead and add the partial results
+// in wave order through LDS.
 //
 // Lane layout of v_mfma_f32_32x32x16_bf16 (64 lanes, l = lane):
 //   A: lane l holds row l%32, K slots 8*(l/32) .. +7 (8 bf16)
 //   B: lane l holds col l%32, the same K slots
 //   D: lane l, register v holds row 8*(v/4) + 4*(l/32) + v%4, col l%32
-// A lane (col, half) loads 16 bytes of codes = words 4*half .. 4*half+3 of its
-// group; MFMA step j consumes word j.  Decoding word j gives bf16 pairs
-// (n0,n4) (n1,n5) (n2,n6) (n3,n7), i.e. K slot i <-> nibble NU[i] with
-// NU = {0,4,1,5,2,6,3,7}; activations are stored in LDS in that order within
-// each 8-element block so the A slots match.
+// MFMA step j of a group consumes word j of the lane's 16 bytes.  Decoding a
+// word gives bf16 pairs (n0,n4) (n1,n5) (n2,n6) (n3,n7), i.e. K slot i <->
+// nibble NU[i] with NU = {0,4,1,5,2,6,3,7}; activations are stored in LDS in
+// that order within each 8-element block so the A slots match.
+//
+// Virtual rows (MFMA rows).  bf16 activations: row i is MFMA row i.  fp32
+// activations: part p of row i is MFMA row i + 8p for i < 8 and 24 + p for
+// i = 8, so the three parts of a row land in one lane's registers.
 
 #include "common.h"
 
@@ -38,15 +60,14 @@ namespace sdv {
 namespace {
 
 constexpr int kTileCols = 32;
-constexpr int kMaxVRows = 32;
 constexpr int kMaxWaves = 8;
-constexpr int kPF = 4;  // groups of codes in flight per lane
+constexpr int kGatherWaves = 8;
+constexpr int kPF = 8;  // groups in flight per lane
 
 struct Q4Args {
-  const uint32_t* codes;
-  const uint16_t* scales;
-  const uint16_t* biases;
-  int E, N, K;
+  const uint4* codes;    // tiled: [E][T][G][64] uint4
+  const uint32_t* sb;    // tiled: [E][T][G][32] (scale | bias << 16)
+  int E, N, K, T;
   const void* act;
   // gathered
   const int32_t* union_ids;
@@ -56,8 +77,15 @@ struct Q4Args {
   const int32_t* pair_slot;
   int k, topk;
   float* out;
-  int n_out;      // outputs per row: N (plain) or N/2 (gate/up)
-  int vrow_cap;   // LDS rows reserved (k or 3k)
+  // optional extra unit (the shared expert): a dense weight with the same
+  // geometry, applied to all k rows of xact ([k][K]), written to xout [k][n_out]
+  const uint4* xcodes;
+  const uint32_t* xsb;
+  const void* xact;
+  float* xout;
+  int n_out;       // outputs per row: N (plain) or N/2 (gate/up)
+  int slot_cap;    // activation rows staged in LDS (k or 3k)
+  int tiles_per_block;
 };
 
 __device__ __forceinline__ uint32_t dec_pair(uint32_t w, int sh) {
@@ -79,242 +107,499 @@ __device__ __forceinline__ uint4 nu_pack(const uint32_t e[8]) {
   return r;
 }
 
-template <int MODE, int ACT, bool GATHER>
-__global__ __launch_bounds__(512) void q4_matvec_kernel(Q4Args a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int K = a.K;
-  const int G = K >> 6;
-  const int rs = K + 8;  // LDS row stride in bf16 (16-byte pad against bank conflicts)
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* xsum = reinterpret_cast<float*>(smem + (size_t)a.vrow_cap * rs * 2);
-  float* red = xsum + (size_t)a.vrow_cap * G;  // [nw][vrow_cap][33]
+// MFMA row of part p of activation row i.
+template <int ACT>
+__device__ __forceinline__ int vrow_of(int i, int p) {
+  if (ACT == SDV_ACT_BF16) return i;
+  return i < 8 ? i + 8 * p : 24 + p;
+}
 
-  const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
-  const int nw = nthreads >> 6;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+// Register of the D layout holding MFMA row vr (for the lane half (vr/4)%2).
+__device__ __forceinline__ int reg_of(int vr) { return 4 * (vr >> 3) + (vr & 3); }
 
-  // ---- resolve the unit (union expert or the dense matrix) and its rows
-  int e = 0, p0 = 0, nrows = a.k;
-  if (GATHER) {
-    const int u = blockIdx.y;
-    int nu = *a.n_union;
-    if (u >= nu) return;
-    e = a.union_ids[u];
-    if (e < 0 || e >= a.E) return;
-    p0 = a.pair_off[u];
-    const int p1 = a.pair_off[u + 1];
-    nrows = p1 - p0;
-    if (p0 < 0 || nrows <= 0 || p1 > a.k * a.topk) return;
-    if (nrows > a.k) nrows = a.k;
-  }
-  const int nparts = (ACT == SDV_ACT_F32) ? 3 : 1;
-  const int vrows = nrows * nparts;
+// Sum over the 8 lanes l .. l+7 (l a multiple of 8); every lane of the group
+// ends with the same total (xor pairing adds the same two operands in both
+// lanes of a pair).
+__device__ __forceinline__ float sum8(float x) {
+  x = x + __shfl_xor(x, 1);
+  x = x + __shfl_xor(x, 2);
+  x = x + __shfl_xor(x, 4);
+  return x;
+}
 
-  // ---- stage activation rows (bf16, NU order) and per-group sums into LDS.
-  // One task = (real row, group): 64 consecutive inputs summed in order.
-  for (int task = tid; task < nrows * G; task += nthreads) {
-    const int i = task / G, g = task - i * G;
-    bool ok = true;
-    size_t src_row = (size_t)i;
-    if (GATHER) {
-      const int r = a.pair_row[p0 + i], s = a.pair_slot[p0 + i];
-      ok = (r >= 0 && r < a.k && s >= 0 && s < a.topk);
-      src_row = (ACT == SDV_ACT_F32) ? (size_t)(ok ? r : 0) * a.topk + (ok ? s : 0)
-                                     : (size_t)(ok ? r : 0);
-    }
+// Stage the unit's activation rows into LDS (NU order, bf16 parts) and their
+// per-group sums (indexed by MFMA row).  One task = (row, 8-element block):
+// the block's elements are summed in order, then the 8 blocks of a group are
+// summed by the fixed 8-lane pairing above.
+template <int ACT>
+__device__ void stage_rows(const Q4Args& a, const void* act, int nrows, uint16_t* xs, float* xsum, int rs,
+                           const int* s_src) {
+  const int K = a.K, G = K >> 6, nb = K >> 3;
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+  for (int t = tid; t < 32 * G; t += nthreads) xsum[t] = 0.0f;
+  uint32_t* zrow = reinterpret_cast<uint32_t*>(xs + (size_t)a.slot_cap * rs);
+  for (int t = tid; t < rs / 2; t += nthreads) zrow[t] = 0u;
+  __syncthreads();
+  // nthreads is a multiple of 64, so the 8 tasks of a group share one 8-lane set
+  for (int task = tid; task < nrows * nb; task += nthreads) {
+    const int i = task / nb, b8 = task - i * nb;
+    const int src = s_src[i];
+    const bool ok = src >= 0;
+    const size_t src_row = ok ? (size_t)src : 0;
     if (ACT == SDV_ACT_BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          static_cast<const uint16_t*>(a.act) + src_row * K + (size_t)g * 64);
+      const uint4 v = ok ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(act) + src_row * K)[b8]
+                         : make_uint4(0, 0, 0, 0);
+      const uint32_t e8[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                              v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
       float acc = 0.0f;
-      uint16_t* dst = xs + (size_t)i * rs + g * 64;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        uint4 v = ok ? src[b] : make_uint4(0, 0, 0, 0);
-        uint32_t e8[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                          v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc = acc + bf16_bits_to_f32(e8[c]);
-        *reinterpret_cast<uint4*>(dst + b * 8) = nu_pack(e8);
-      }
-      xsum[(size_t)i * G + g] = acc;
+      for (int c = 0; c < 8; ++c) acc = acc + bf16_bits_to_f32(e8[c]);
+      *reinterpret_cast<uint4*>(xs + (size_t)i * rs + b8 * 8) = nu_pack(e8);
+      acc = sum8(acc);
+      if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, 0) * G + (b8 >> 3)] = acc;
     } else {
-      const float4* src = reinterpret_cast<const float4*>(
-          static_cast<const float*>(a.act) + src_row * K + (size_t)g * 64);
+      const float4* sp = reinterpret_cast<const float4*>(static_cast<const float*>(act) + src_row * K) + 2 * b8;
+      const float4 v0 = ok ? sp[0] : make_float4(0, 0, 0, 0);
+      const float4 v1 = ok ? sp[1] : make_float4(0, 0, 0, 0);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t hi[8], mi[8], lo[8];
       float acc[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        float4 v0 = ok ? src[2 * b] : make_float4(0, 0, 0, 0);
-        float4 v1 = ok ? src[2 * b + 1] : make_float4(0, 0, 0, 0);
-        float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        uint32_t hi[8], mi[8], lo[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          hi[c] = f32_to_bf16_rne(f[c]);
-          float r1 = f[c] - bf16_bits_to_f32(hi[c]);
-          mi[c] = f32_to_bf16_rne(r1);
-          float r2 = r1 - bf16_bits_to_f32(mi[c]);
-          lo[c] = f32_to_bf16_rne(r2);
-          acc[0] = acc[0] + bf16_bits_to_f32(hi[c]);
-          acc[1] = acc[1] + bf16_bits_to_f32(mi[c]);
-          acc[2] = acc[2] + bf16_bits_to_f32(lo[c]);
-        }
-        *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 0) * rs + g * 64 + b * 8) = nu_pack(hi);
-        *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 1) * rs + g * 64 + b * 8) = nu_pack(mi);
-        *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 2) * rs + g * 64 + b * 8) = nu_pack(lo);
+      for (int c = 0; c < 8; ++c) {
+        hi[c] = f32_to_bf16_rne(f[c]);
+        const float r1 = f[c] - bf16_bits_to_f32(hi[c]);
+        mi[c] = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_bits_to_f32(mi[c]);
+        lo[c] = f32_to_bf16_rne(r2);
+        acc[0] = acc[0] + bf16_bits_to_f32(hi[c]);
+        acc[1] = acc[1] + bf16_bits_to_f32(mi[c]);
+        acc[2] = acc[2] + bf16_bits_to_f32(lo[c]);
       }
+      *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 0) * rs + b8 * 8) = nu_pack(hi);
+      *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 1) * rs + b8 * 8) = nu_pack(mi);
+      *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 2) * rs + b8 * 8) = nu_pack(lo);
 #pragma unroll
-      for (int p = 0; p < 3; ++p) xsum[(size_t)(3 * i + p) * G + g] = acc[p];
-    }
-  }
-  __syncthreads();
-
-  // ---- this lane's weight column
-  const int col = lane & 31, half = lane >> 5;
-  int n;
-  bool col_ok;
-  if (MODE == SDV_MODE_PLAIN) {
-    n = blockIdx.x * kTileCols + col;
-    col_ok = n < a.N;
-  } else {
-    const int ihalf = a.N >> 1;
-    const int i = blockIdx.x * 16 + (col & 15);
-    col_ok = i < ihalf;
-    n = (col < 16) ? i : ihalf + i;
-  }
-  if (!col_ok) n = 0;  // in-bounds dummy column; its results are never stored
-  const size_t wrow = (size_t)e * a.N + n;
-  const uint4* crow = reinterpret_cast<const uint4*>(a.codes + wrow * (size_t)(K >> 3)) + half;
-  const uint16_t* srow = a.scales + wrow * (size_t)G;
-  const uint16_t* brow = a.biases + wrow * (size_t)G;
-
-  // contiguous group range of this wave (depends on K and the wave count only)
-  const int gb = (G * wave) / nw;
-  const int ge = (G * (wave + 1)) / nw;
-
-  const int nquads = (vrows + 7) >> 3;
-  const int arow = col;  // A operand row of this lane
-  const bool a_ok = arow < vrows;
-  const uint16_t* arow_ptr = xs + (size_t)(a_ok ? arow : 0) * rs + half * 32;
-
-  float yacc[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) yacc[v] = 0.0f;
-
-  uint4 cbuf[kPF];
-  uint32_t sbuf[kPF], bbuf[kPF];
-#pragma unroll
-  for (int i = 0; i < kPF; ++i) {
-    if (gb + i < ge) {
-      cbuf[i] = crow[(size_t)(gb + i) * 2];
-      sbuf[i] = srow[gb + i];
-      bbuf[i] = brow[gb + i];
-    }
-  }
-
-  for (int g0 = gb; g0 < ge; g0 += kPF) {
-#pragma unroll
-    for (int i = 0; i < kPF; ++i) {
-      const int g = g0 + i;
-      if (g < ge) {
-        const uint4 cw = cbuf[i];
-        const float s = bf16_bits_to_f32(sbuf[i]);
-        const float b = bf16_bits_to_f32(bbuf[i]);
-        if (g + kPF < ge) {
-          cbuf[i] = crow[(size_t)(g + kPF) * 2];
-          sbuf[i] = srow[g + kPF];
-          bbuf[i] = brow[g + kPF];
-        }
-        const float c = fmaf(-128.0f, s, b);
-        const uint16_t* ap = arow_ptr + g * 64;
-        f32x16 acc = {};
-        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4 av = a_ok ? *reinterpret_cast<const uint4*>(ap + j * 8) : make_uint4(0, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                        decode_word(cws[j]), acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q < nquads) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int v = 4 * q + r;
-              const int vr = 8 * q + 4 * half + r;
-              const float xg = (vr < vrows) ? xsum[(size_t)vr * G + g] : 0.0f;
-              yacc[v] = fmaf(s, acc[v], yacc[v]);
-              yacc[v] = fmaf(c, xg, yacc[v]);
-            }
-          }
-        }
+      for (int p = 0; p < 3; ++p) {
+        const float t = sum8(acc[p]);
+        if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, p) * G + (b8 >> 3)] = t;
       }
     }
   }
+}
 
-  // ---- cross-wave reduction in wave order, then the epilogue
-  float* myred = red + (size_t)wave * a.vrow_cap * 33;
+// LDS slot of the activation data for MFMA row `arow` (or -1 if unused).
+template <int ACT>
+__device__ __forceinline__ int slot_of_arow(int arow, int nrows) {
+  if (ACT == SDV_ACT_BF16) return arow < nrows ? arow : -1;
+  if (arow < 24) {
+    const int i = arow & 7, p = arow >> 3;
+    return i < nrows ? 3 * i + p : -1;
+  }
+  const int p = arow - 24;
+  return (nrows == 9 && p < 3) ? 24 + p : -1;
+}
+
+// One 64-element group: 4 MFMA steps, then the group's scale/bias epilogue
+// into yacc for the first `nquads` register quads.  `ap` points at this
+// lane's activation row (or at an all-zero LDS row), so the four A reads are
+// issued together, unconditionally, before the decode.
+__device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xs_g,
+                                          int G, int half, int nquads, float yacc[16]) {
+  uint4 av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 8);
+  const float s = __uint_as_float(sbw << 16);
+  const float b = __uint_as_float(sbw & 0xFFFF0000u);
+  const float c = fmaf(-128.0f, s, b);
+  f32x16 acc = {};
+  const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j]), acc,
+                                                  0, 0, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (q < nquads) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int vr = 8 * q + 4 * half + r;
-        if (vr < vrows) myred[(size_t)vr * 33 + col] = yacc[4 * q + r];
+        const int v = 4 * q + r;
+        const float xg = xs_g[(8 * q + 4 * half + r) * G];
+        yacc[v] = fmaf(s, acc[v], yacc[v]);
+        yacc[v] = fmaf(c, xg, yacc[v]);
       }
     }
   }
-  __syncthreads();
+}
 
-  const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
-  for (int t = tid; t < nrows * cols_out; t += nthreads) {
-    const int i = t / cols_out, cc = t - i * cols_out;
-    size_t orow = (size_t)i;
-    if (GATHER) {
-      const int r = a.pair_row[p0 + i], s = a.pair_slot[p0 + i];
-      if (r < 0 || r >= a.k || s < 0 || s >= a.topk) continue;
-      orow = (size_t)r * a.topk + s;
+// Final value of activation row i from the wave's accumulators (valid in the
+// lanes of half (vrow/4)%2).
+template <int ACT>
+__device__ __forceinline__ float row_value(const float yacc[16], int i) {
+  if (ACT == SDV_ACT_BF16) {
+    const int v = reg_of(i);
+    float r = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t == v) r = yacc[t];
+    return r;
+  }
+  float p[3];
+#pragma unroll
+  for (int pp = 0; pp < 3; ++pp) {
+    const int v = reg_of(vrow_of<ACT>(i, pp));
+    float r = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t == v) r = yacc[t];
+    p[pp] = r;
+  }
+  return (p[0] + p[1]) + p[2];
+}
+
+template <int ACT>
+__device__ __forceinline__ int half_of_row(int i) {
+  return (vrow_of<ACT>(i, 0) >> 2) & 1;
+}
+
+template <int MODE, int ACT, bool GATHER, bool KSPLIT>
+__device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* smem, int* s_src, int* s_dst) {
+  const int K = a.K;
+  const int G = K >> 6;
+  const int rs = K + 8;  // LDS row stride in bf16 (16-byte pad against bank conflicts)
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* xsum = reinterpret_cast<float*>(smem + (size_t)(a.slot_cap + 1) * rs * 2);  // [32][G]
+  float* red = xsum + 32 * G;  // split-K: [nw][32][33]; gathered: per-wave tile outputs
+
+  const int tid = threadIdx.x;
+  const int nw = blockDim.x >> 6;
+  // wave-uniform values live in scalar registers, so the stream loop below
+  // branches on scalars and keeps its loads in flight
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- the unit (union expert, the shared expert, or the dense matrix) and its rows
+  int e = 0, p0 = 0, nrows = a.k;
+  const uint4* codes = a.codes;
+  const uint32_t* sbp = a.sb;
+  const void* act = a.act;
+  float* out = a.out;
+  bool pairs = GATHER;  // rows come from the pair lists
+  if (GATHER) {
+    const int u = blockIdx.y;
+    if (u == a.k * a.topk) {
+      // the shared expert: all k rows, its own weight, input and output
+      codes = a.xcodes;
+      sbp = a.xsb;
+      act = a.xact;
+      out = a.xout;
+      pairs = false;
+    } else {
+      const int nu = *a.n_union;
+      if (u >= nu) return;
+      e = a.union_ids[u];
+      if (e < 0 || e >= a.E) return;
+      p0 = a.pair_off[u];
+      const int p1 = a.pair_off[u + 1];
+      nrows = p1 - p0;
+      if (p0 < 0 || nrows <= 0 || p1 > a.k * a.topk) return;
+      if (nrows > a.k) nrows = a.k;
+      e = __builtin_amdgcn_readfirstlane(e);
+      p0 = __builtin_amdgcn_readfirstlane(p0);
+      nrows = __builtin_amdgcn_readfirstlane(nrows);
     }
+  }
+
+  // ---- this wave's tiles and K range, and its load stream
+  int t_first, t_step, t_count, gb, ge;
+  if (KSPLIT) {
+    t_first = blockIdx.x;
+    t_step = 1;
+    t_count = 1;
+    gb = (G * wave) / nw;
+    ge = (G * (wave + 1)) / nw;
+  } else {
+    const int tb0 = blockIdx.x * a.tiles_per_block;
+    const int tb1 = min(tb0 + a.tiles_per_block, a.T);
+    t_first = tb0 + wave;
+    t_step = nw;
+    t_count = t_first < tb1 ? (tb1 - t_first + nw - 1) / nw : 0;
+    gb = 0;
+    ge = G;
+  }
+  const int gn = ge - gb;
+  const int total = __builtin_amdgcn_readfirstlane(t_count * gn);
+
+  // (tile, group) steps in order; block (t, g) of expert e starts at
+  // ((e * T + t) * G + g) in units of 64 uint4 (codes) or 32 words (sb)
+  size_t ld_blk = ((size_t)e * a.T + t_first) * G + gb;
+  int ld_g = gb;
+  const size_t tile_jump = (size_t)t_step * G - gn;  // from the end of one tile's range to the next
+  uint4 cbuf[kPF];
+  uint32_t sbuf[kPF];
+  auto issue = [&](int slot) {
+    cbuf[slot] = codes[ld_blk * 64 + lane];
+    sbuf[slot] = sbp[ld_blk * 32 + col];
+    ++ld_blk;
+    if (++ld_g == ge) {
+      ld_g = gb;
+      ld_blk += tile_jump;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kPF; ++i)
+    if (i < total) issue(i);
+
+  // ---- rows, then staging (the loads above are already in flight)
+  if (tid < SDV_MAX_ROWS) {
+    int src = -1, dst = -1;
+    if (tid < nrows) {
+      if (pairs) {
+        const int r = a.pair_row[p0 + tid], s = a.pair_slot[p0 + tid];
+        if (r >= 0 && r < a.k && s >= 0 && s < a.topk) {
+          src = (ACT == SDV_ACT_F32) ? r * a.topk + s : r;
+          dst = r * a.topk + s;
+        }
+      } else {
+        src = dst = tid;
+      }
+    }
+    s_src[tid] = src;
+    s_dst[tid] = dst;
+  }
+  __syncthreads();
+  stage_rows<ACT>(a, act, nrows, xs, xsum, rs, s_src);
+  __syncthreads();
+  // The first ring loads were issued before staging and have had the staging
+  // time to land; wait for them here so the stream loop is entered with no
+  // load outstanding and its waits only count the loop's own refills.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (gfx9 encoding: expcnt 7, lgkmcnt 15)
+
+  const int max_vrow = (ACT == SDV_ACT_F32) ? (nrows == 9 ? 27 : 16 + nrows) : nrows;
+  const int nquads = (max_vrow + 7) >> 3;
+  const int slot = slot_of_arow<ACT>(col, nrows);
+  // rows without data read the zero row (LDS row slot_cap)
+  const uint16_t* arow_ptr = xs + (size_t)(slot >= 0 ? slot : a.slot_cap) * rs + half * 32;
+
+  float yacc[16];
+  int cur_g = gb, cur_tl = 0;
+  const int tiles_per_wave = KSPLIT ? 1 : (a.tiles_per_block + nw - 1) / nw;
+  // One (tile, group) step: consume ring slot i, refill it (if asked) after
+  // the slot's data has been decoded, and finish the tile after its last group.
+  auto step = [&](int i, bool refill) {
+    if (cur_g == gb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) yacc[v] = 0.0f;
+    }
+    group_mac(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc);
+    if (refill) issue(i);
+    if (++cur_g == ge) {
+      if (!KSPLIT) {
+        // finished tile values go to this wave's LDS area; the global stores
+        // happen after the stream loop
+        float* o = red + ((size_t)wave * tiles_per_wave + cur_tl) * SDV_MAX_ROWS * 32;
+#pragma unroll
+        for (int r = 0; r < SDV_MAX_ROWS; ++r) {
+          if (r < nrows) {
+            const float val = row_value<ACT>(yacc, r);
+            const bool mine = half == half_of_row<ACT>(r);
+            if (MODE == SDV_MODE_PLAIN) {
+              if (mine) o[r * 32 + col] = val;
+            } else {
+              const float up = __shfl_xor(val, 16);
+              if (mine && col < 16) o[r * 32 + col] = siluf_(val) * up;
+            }
+          }
+        }
+      }
+      cur_g = gb;
+      ++cur_tl;
+    }
+  };
+  int st0 = 0;
+  // steady state: every slot is refilled right after it is consumed
+  for (; st0 + 2 * kPF <= total; st0 += kPF) {
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) step(i, true);
+  }
+  // drain: the last (< 2 kPF) steps
+  for (; st0 < total; st0 += kPF) {
+#pragma unroll
+    for (int i = 0; i < kPF; ++i)
+      if (st0 + i < total) step(i, st0 + i + kPF < total);
+  }
+
+  if (!KSPLIT) {
+    __syncthreads();
+    const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
+    const float* o = red + (size_t)wave * tiles_per_wave * SDV_MAX_ROWS * 32;
+    for (int tl = 0; tl < t_count; ++tl) {
+      const int t = t_first + tl * t_step;
+      const int on = t * cols_out + col;
+      if (col < cols_out && on < a.n_out) {
+        for (int r = 0; r < nrows; ++r) {
+          const int orow = s_dst[r];
+          if (orow >= 0) out[(size_t)orow * a.n_out + on] = o[(tl * SDV_MAX_ROWS + r) * 32 + col];
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- split-K: cross-wave reduction in wave order, then the epilogue
+  float* myred = red + (size_t)wave * 32 * 33;
+  if (total == 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) yacc[v] = 0.0f;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int vr = 8 * (v >> 2) + 4 * half + (v & 3);
+    myred[vr * 33 + col] = yacc[v];
+  }
+  __syncthreads();
+  const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
+  for (int t = tid; t < nrows * cols_out; t += blockDim.x) {
+    const int i = t / cols_out, cc = t - i * cols_out;
     float val[2];
     const int ncol = (MODE == SDV_MODE_PLAIN) ? 1 : 2;
     for (int h2 = 0; h2 < ncol; ++h2) {
       const int cidx = cc + 16 * h2;
       float part[3];
-      for (int p = 0; p < nparts; ++p) {
-        const int vr = nparts * i + p;
+      const int np = (ACT == SDV_ACT_F32) ? 3 : 1;
+      for (int p = 0; p < np; ++p) {
+        const int vr = vrow_of<ACT>(i, p);
         float sum = 0.0f;
-        for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * a.vrow_cap + vr) * 33 + cidx];
+        for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * 32 + vr) * 33 + cidx];
         part[p] = sum;
       }
-      val[h2] = (nparts == 3) ? (part[0] + part[1]) + part[2] : part[0];
+      val[h2] = (np == 3) ? (part[0] + part[1]) + part[2] : part[0];
     }
+    const int orow = s_dst[i];
+    if (orow < 0) continue;
     if (MODE == SDV_MODE_PLAIN) {
       const int on = blockIdx.x * kTileCols + cc;
-      if (on < a.N) a.out[orow * a.n_out + on] = val[0];
+      if (on < a.N) out[(size_t)orow * a.n_out + on] = val[0];
     } else {
       const int on = blockIdx.x * 16 + cc;
-      if (on < a.n_out) a.out[orow * a.n_out + on] = siluf_(val[0]) * val[1];
+      if (on < a.n_out) out[(size_t)orow * a.n_out + on] = siluf_(val[0]) * val[1];
     }
   }
 }
 
+// Split-K (dense): up to 8 waves per workgroup.
+template <int MODE, int ACT>
+__global__ __launch_bounds__(512, 2) void q4_dense_kernel(Q4Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
+  q4_matvec_body<MODE, ACT, false, true>(a, smem, s_src, s_dst);
+}
+
+// Gathered units: 8 waves per workgroup (one weight tile each), at most 128
+// VGPRs so 4 waves fit per SIMD.
+template <int MODE, int ACT>
+__global__ __launch_bounds__(512, 4) void q4_gather_kernel(Q4Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
+  q4_matvec_body<MODE, ACT, true, false>(a, smem, s_src, s_dst);
+}
+
 template <int MODE, int ACT, bool GATHER>
-hipError_t launch_one(const Q4Args& a, int tiles, int units, int nw, size_t lds, hipStream_t st) {
-  auto kern = q4_matvec_kernel<MODE, ACT, GATHER>;
+hipError_t launch_one(const Q4Args& a, int blocks_x, int units, int nw, size_t lds, hipStream_t st) {
+  void (*kern)(Q4Args) = GATHER ? q4_gather_kernel<MODE, ACT> : q4_dense_kernel<MODE, ACT>;
   if (lds > 65536) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(tiles, units), dim3(64 * nw), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(blocks_x, units), dim3(64 * nw), lds, st, a);
   return hipGetLastError();
+}
+
+// ---- repack: row-major affine Q4 -> tiled layout ---------------------------
+
+struct RepackArgs {
+  const uint32_t* codes;   // [E][N][K/8]
+  const uint16_t* scales;  // [E][N][K/64]
+  const uint16_t* biases;
+  int E, N, K, T, fused;
+  uint4* tcodes;           // [E][T][G][64]
+  uint32_t* tsb;           // [E][T][G][32]
+};
+
+// Source row of column c of tile t (or -1 for a padding column).
+__device__ __forceinline__ int repack_row(const RepackArgs& r, int t, int c) {
+  if (!r.fused) {
+    const int n = t * kTileCols + c;
+    return n < r.N ? n : -1;
+  }
+  const int ihalf = r.N >> 1;
+  const int i = t * 16 + (c & 15);
+  if (i >= ihalf) return -1;
+  return c < 16 ? i : ihalf + i;
+}
+
+__global__ __launch_bounds__(256) void q4_repack_kernel(RepackArgs r) {
+  const int G = r.K >> 6;
+  const size_t nblk = (size_t)r.E * r.T * G;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  // codes: one thread per 16-byte lane chunk
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * 64; idx += stride) {
+    const int lane = (int)(idx & 63);
+    const size_t blk = idx >> 6;
+    const int g = (int)(blk % G);
+    const size_t et = blk / G;
+    const int t = (int)(et % r.T);
+    const int e = (int)(et / r.T);
+    const int n = repack_row(r, t, lane & 31);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n >= 0) {
+      const uint4* src = reinterpret_cast<const uint4*>(r.codes + ((size_t)e * r.N + n) * (r.K >> 3));
+      v = src[2 * g + (lane >> 5)];
+    }
+    r.tcodes[idx] = v;
+  }
+  // scales and biases: one thread per (block, column)
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * 32; idx += stride) {
+    const int c = (int)(idx & 31);
+    const size_t blk = idx >> 5;
+    const int g = (int)(blk % G);
+    const size_t et = blk / G;
+    const int t = (int)(et % r.T);
+    const int e = (int)(et / r.T);
+    const int n = repack_row(r, t, c);
+    uint32_t w = 0;
+    if (n >= 0) {
+      const size_t o = ((size_t)e * r.N + n) * G + g;
+      w = (uint32_t)r.scales[o] | ((uint32_t)r.biases[o] << 16);
+    }
+    r.tsb[idx] = w;
+  }
 }
 
 }  // namespace
 
-// Waves per workgroup (split of the K groups): a function of K only, so the
-// summation order never depends on the row count.
+// Tiles of a weight: 32 rows each, or 16 gate + 16 up rows when fused.
+int q4_tiles(int N, int fused) { return fused ? (N / 2 + 15) / 16 : (N + kTileCols - 1) / kTileCols; }
+
+size_t q4t_codes_bytes(int E, int N, int K, int fused) {
+  return (size_t)E * q4_tiles(N, fused) * (K / 64) * 1024;
+}
+
+size_t q4t_sb_bytes(int E, int N, int K, int fused) { return (size_t)E * q4_tiles(N, fused) * (K / 64) * 128; }
+
+hipError_t q4_repack_launch(const sdv_q4& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st) {
+  RepackArgs r{src.codes, src.scales, src.biases, src.E, src.N, src.K, q4_tiles(src.N, fused), fused,
+               static_cast<uint4*>(tcodes), tsb};
+  const size_t n = (size_t)src.E * r.T * (src.K / 64) * 64;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(q4_repack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, r);
+  return hipGetLastError();
+}
+
+// Waves per workgroup for a split-K (dense) product: a function of K only, so
+// the summation order never depends on the row count.
 int q4_waves_for(int K) {
   const int G = K / 64;
   int nw = G / 5;
@@ -323,22 +608,30 @@ int q4_waves_for(int K) {
   return nw;
 }
 
-size_t q4_lds_bytes(int K, int vrow_cap, int nw) {
+size_t q4_lds_bytes(int K, int slot_cap, int nw) {
   const int G = K / 64;
-  return (size_t)vrow_cap * (K + 8) * 2 + (size_t)vrow_cap * G * 4 + (size_t)nw * vrow_cap * 33 * 4;
+  return (size_t)(slot_cap + 1) * (K + 8) * 2 + (size_t)32 * G * 4 + (size_t)nw * 32 * 33 * 4;
 }
 
-hipError_t q4_launch(const sdv_q4& W, int mode, const void* act, int act_dtype, bool gather,
+size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather) {
+  const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
+  // gathered: per-wave output staging for one tile of up to 9 rows x 32 columns
+  return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * 4 +
+                      (size_t)kGatherWaves * SDV_MAX_ROWS * 32 * 4
+                : q4_lds_bytes(K, cap, q4_waves_for(K));
+}
+
+hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, bool gather,
                      const int32_t* union_ids, const int32_t* n_union, const int32_t* pair_off,
                      const int32_t* pair_row, const int32_t* pair_slot, int k, int topk, float* out,
-                     hipStream_t st) {
+                     const sdv_q4t* shared, const void* shared_act, float* shared_out, hipStream_t st) {
   Q4Args a;
-  a.codes = W.codes;
-  a.scales = W.scales;
-  a.biases = W.biases;
+  a.codes = static_cast<const uint4*>(W.codes);
+  a.sb = W.sb;
   a.E = W.E;
   a.N = W.N;
   a.K = W.K;
+  a.T = q4_tiles(W.N, W.fused_gateup);
   a.act = act;
   a.union_ids = union_ids;
   a.n_union = n_union;
@@ -348,24 +641,37 @@ hipError_t q4_launch(const sdv_q4& W, int mode, const void* act, int act_dtype, 
   a.k = k;
   a.topk = topk;
   a.out = out;
+  a.xcodes = shared ? static_cast<const uint4*>(shared->codes) : nullptr;
+  a.xsb = shared ? shared->sb : nullptr;
+  a.xact = shared_act;
+  a.xout = shared_out;
   a.n_out = (mode == SDV_MODE_PLAIN) ? W.N : W.N / 2;
-  a.vrow_cap = (act_dtype == SDV_ACT_F32) ? 3 * k : k;
-  const int nw = q4_waves_for(W.K);
-  const size_t lds = q4_lds_bytes(W.K, a.vrow_cap, nw);
-  const int tiles = (mode == SDV_MODE_PLAIN) ? (W.N + kTileCols - 1) / kTileCols : (W.N / 2 + 15) / 16;
-  const int units = gather ? k * topk : 1;
-#define SDV_Q4_CASE(M, A, GA)                                                  \
-  if (mode == M && act_dtype == A && gather == GA)                             \
-    return launch_one<M, A, GA>(a, tiles, units, nw, lds, st);
-  SDV_Q4_CASE(SDV_MODE_PLAIN, SDV_ACT_BF16, false)
-  SDV_Q4_CASE(SDV_MODE_PLAIN, SDV_ACT_F32, false)
-  SDV_Q4_CASE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16, false)
-  SDV_Q4_CASE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32, false)
-  SDV_Q4_CASE(SDV_MODE_PLAIN, SDV_ACT_BF16, true)
-  SDV_Q4_CASE(SDV_MODE_PLAIN, SDV_ACT_F32, true)
-  SDV_Q4_CASE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16, true)
-  SDV_Q4_CASE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32, true)
-#undef SDV_Q4_CASE
+  a.slot_cap = (act_dtype == SDV_ACT_F32) ? 3 * k : k;
+  if (gather) {
+    const int nw = kGatherWaves;
+    a.tiles_per_block = nw;
+    const int bx = (a.T + a.tiles_per_block - 1) / a.tiles_per_block;
+    const int units = k * topk + (shared ? 1 : 0);
+    const size_t lds = q4_lds_bytes_for(W.K, act_dtype, k, true);
+#define SDV_Q4_G(M, A) \
+  if (mode == M && act_dtype == A) return launch_one<M, A, true>(a, bx, units, nw, lds, st);
+    SDV_Q4_G(SDV_MODE_PLAIN, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_MODE_PLAIN, SDV_ACT_F32)
+    SDV_Q4_G(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+#undef SDV_Q4_G
+  } else {
+    const int nw = q4_waves_for(W.K);
+    a.tiles_per_block = 1;
+    const size_t lds = q4_lds_bytes(W.K, a.slot_cap, nw);
+#define SDV_Q4_D(M, A) \
+  if (mode == M && act_dtype == A) return launch_one<M, A, false>(a, a.T, 1, nw, lds, st);
+    SDV_Q4_D(SDV_MODE_PLAIN, SDV_ACT_BF16)
+    SDV_Q4_D(SDV_MODE_PLAIN, SDV_ACT_F32)
+    SDV_Q4_D(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+    SDV_Q4_D(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+#undef SDV_Q4_D
+  }
   return hipErrorInvalidValue;
 }
 

@@ -12,9 +12,9 @@ from collections import namedtuple
 import torch
 
 from ._lib import (ACT_BF16, ACT_F32, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX,
-                   SdvError, SdvQ4, check, lib)
+                   SdvError, SdvQ4, SdvQ4T, check, lib)
 
-__all__ = ["Q4Weight", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
+__all__ = ["Q4Weight", "TiledQ4", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
            "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
 
@@ -69,6 +69,51 @@ class Q4Weight:
     def nbytes(self):
         return self.E * self.N * (self.K // 2 + (self.K // 64) * 4)
 
+    def tiled(self, fused_gateup=False):
+        """The weight rewritten on the device into the tiled layout the
+        products read (sdv_q4_repack)."""
+        return TiledQ4.from_rowmajor(self, fused_gateup)
+
+
+class TiledQ4:
+    """Affine-Q4/g64 weights in the tiled layout of ``sdv_q4t`` (device
+    tensors ``codes`` uint8 and ``sb`` int32)."""
+
+    def __init__(self, codes, sb, E, N, K, fused_gateup):
+        self.E, self.N, self.K, self.fused = E, N, K, bool(fused_gateup)
+        L = lib()
+        need_c = L.sdv_q4t_codes_bytes(E, N, K, int(self.fused))
+        need_s = L.sdv_q4t_sb_bytes(E, N, K, int(self.fused))
+        if codes.numel() * codes.element_size() < need_c or sb.numel() * 4 < need_s:
+            raise ValueError("tiled buffers are smaller than the layout needs")
+        self.codes, self.sb = codes, sb
+        self.device = codes.device
+        self._desc = SdvQ4T(_need(codes, "codes", codes.dtype).value,
+                            _need(sb, "sb", torch.int32, device=self.device).value, E, N, K, 64, int(self.fused))
+
+    @staticmethod
+    def empty(E, N, K, fused_gateup, device):
+        L = lib()
+        nc = L.sdv_q4t_codes_bytes(E, N, K, int(bool(fused_gateup)))
+        ns = L.sdv_q4t_sb_bytes(E, N, K, int(bool(fused_gateup)))
+        codes = torch.empty((nc,), dtype=torch.uint8, device=device)
+        sb = torch.empty((ns // 4,), dtype=torch.int32, device=device)
+        return codes, sb
+
+    @classmethod
+    def from_rowmajor(cls, W, fused_gateup=False, out=None):
+        codes, sb = out if out is not None else cls.empty(W.E, W.N, W.K, fused_gateup, W.device)
+        check(lib().sdv_q4_repack(W.desc, int(bool(fused_gateup)), _need(codes, "codes_out", codes.dtype),
+                                  _need(sb, "sb_out", torch.int32), _stream(codes)))
+        return cls(codes, sb, W.E, W.N, W.K, fused_gateup)
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def nbytes(self):
+        return self.codes.numel() * self.codes.element_size() + self.sb.numel() * 4
+
 
 def _act_kind(act):
     if act.dtype == torch.int16:
@@ -79,8 +124,9 @@ def _act_kind(act):
 
 
 def qmv_k(W, act, mode=MODE_PLAIN, out=None):
-    """Dense k-row product: act [k, K] (bf16 bits as int16, or fp32) -> fp32
-    [k, N] (plain) or [k, N/2] (fused gate/up with SwiGLU)."""
+    """Dense k-row product with a tiled weight: act [k, K] (bf16 bits as
+    int16, or fp32) -> fp32 [k, N] (plain) or [k, N/2] (fused gate/up with
+    SwiGLU; the weight must be tiled with fused_gateup=True)."""
     k = act.shape[0]
     kind = _act_kind(act)
     if act.dim() != 2 or act.shape[1] != W.K:
@@ -126,25 +172,43 @@ def moe_route_k(logits, topk, score_mode, renorm, out=None):
     return out
 
 
-def gather_qmv_k(bank, mode, act, route, k, topk, out=None):
-    """Gathered-expert product over the union in ``route``.  act: bf16 bits
-    [k, K] shared by a row's slots, or fp32 [k, topk, K] per pair.  Returns
-    fp32 [k, topk, N or N/2]; entry (r, s) is expert idx[r, s]'s output."""
+def _gather_args(bank, mode, act, route, k, topk, out, shared, shared_act, shared_out):
     kind = _act_kind(act)
     kt = k * topk
     need_act = kt * bank.K if kind == ACT_F32 else k * bank.K
     n_out = bank.N if mode == MODE_PLAIN else bank.N // 2
+    dev = bank.device
+    if shared is not None:
+        sh = (shared.desc, _need(shared_act, "shared_act", act.dtype, k * bank.K, dev),
+              _need(shared_out, "shared_out", torch.float32, k * n_out, dev))
+    else:
+        sh = (None, None, None)
+    return [bank.desc, mode, _need(act, "act", act.dtype, need_act, dev), kind,
+            _need(route.union_ids, "union_ids", torch.int32, kt, dev),
+            _need(route.n_union, "n_union", torch.int32, 1, dev),
+            _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
+            _need(route.pair_row, "pair_row", torch.int32, kt, dev),
+            _need(route.pair_slot, "pair_slot", torch.int32, kt, dev), k, topk,
+            _need(out, "out", torch.float32, kt * n_out, dev), *sh, _stream(out)]
+
+
+def gather_qmv_k(bank, mode, act, route, k, topk, out=None, shared=None, shared_act=None, shared_out=None):
+    """Gathered-expert product over the union in ``route``.  act: bf16 bits
+    [k, K] shared by a row's slots, or fp32 [k, topk, K] per pair.  Returns
+    fp32 [k, topk, N or N/2]; entry (r, s) is expert idx[r, s]'s output.
+
+    ``shared`` (a TiledQ4 with E = 1 and the bank's geometry) adds the
+    always-on expert to the same launch: it reads ``shared_act`` [k, K] (same
+    dtype as act) and writes ``shared_out`` [k, N or N/2] (allocated if None).
+    Returns ``out`` or ``(out, shared_out)``."""
+    n_out = bank.N if mode == MODE_PLAIN else bank.N // 2
     if out is None:
         out = torch.empty((k, topk, n_out), dtype=torch.float32, device=bank.device)
-    dev = bank.device
-    check(lib().sdv_gather_qmv_k(bank.desc, mode, _need(act, "act", act.dtype, need_act, dev), kind,
-                                 _need(route.union_ids, "union_ids", torch.int32, kt, dev),
-                                 _need(route.n_union, "n_union", torch.int32, 1, dev),
-                                 _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
-                                 _need(route.pair_row, "pair_row", torch.int32, kt, dev),
-                                 _need(route.pair_slot, "pair_slot", torch.int32, kt, dev),
-                                 k, topk, _need(out, "out", torch.float32, kt * n_out, dev), _stream(out)))
-    return out
+    if shared is not None and shared_out is None:
+        shared_out = torch.empty((k, n_out), dtype=torch.float32, device=bank.device)
+    check(lib().sdv_gather_qmv_k(*_gather_args(bank, mode, act, route, k, topk, out, shared, shared_act,
+                                               shared_out)))
+    return out if shared is None else (out, shared_out)
 
 
 def moe_combine_k(partial, w, shared_out=None, shared_logit=None, out=None):
@@ -244,19 +308,9 @@ def bind_moe_route_k(logits, topk, score_mode, renorm, out):
         _need(out.pair_slot, "pair_slot", torch.int32, kt, dev), _stream(logits)])
 
 
-def bind_gather_qmv_k(bank, mode, act, route, k, topk, out):
-    kind = _act_kind(act)
-    kt = k * topk
-    need_act = kt * bank.K if kind == ACT_F32 else k * bank.K
-    n_out = bank.N if mode == MODE_PLAIN else bank.N // 2
-    dev = bank.device
-    return BoundCall("sdv_gather_qmv_k", [
-        bank.desc, mode, _need(act, "act", act.dtype, need_act, dev), kind,
-        _need(route.union_ids, "union_ids", torch.int32, kt, dev), _need(route.n_union, "n_union", torch.int32, 1, dev),
-        _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
-        _need(route.pair_row, "pair_row", torch.int32, kt, dev),
-        _need(route.pair_slot, "pair_slot", torch.int32, kt, dev), k, topk,
-        _need(out, "out", torch.float32, kt * n_out, dev), _stream(out)])
+def bind_gather_qmv_k(bank, mode, act, route, k, topk, out, shared=None, shared_act=None, shared_out=None):
+    return BoundCall("sdv_gather_qmv_k",
+                     _gather_args(bank, mode, act, route, k, topk, out, shared, shared_act, shared_out))
 
 
 def bind_moe_combine_k(partial, w, shared_out, shared_logit, out):

@@ -2,8 +2,10 @@
 
 ``MoeLayer`` runs the MoE half of a layer for k rows: router dispatch and
 union, gathered fused gate/up with SwiGLU, gathered down projection, the
-optional shared expert (dense gate/up + down) and the fixed-order combine,
-all on the device with no host synchronisation.  ``GdnLayer`` keeps a pool of
+optional shared expert and the fixed-order combine, all on the device with no
+host synchronisation.  When the shared expert has the routed experts'
+geometry it rides in the two gathered launches as one more unit; otherwise
+it runs as two dense products.  ``GdnLayer`` keeps a pool of
 k+1 state buffers per layer: the live state and k snapshot slots.  A verify
 call writes the snapshots; rollback to an accepted prefix j only swaps which
 buffer is live (Red Lite dev45, "What it is": pointer swap with the
@@ -17,9 +19,13 @@ from ._lib import MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX
 
 
 class MoeLayer:
-    def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None):
+    def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None,
+                 fuse_shared=True):
         self.gate_up, self.down = gate_up, down
         self.shared_gate_up, self.shared_down = shared_gate_up, shared_down
+        self.fused_shared = (fuse_shared and shared_gate_up is not None and
+                             (shared_gate_up.N, shared_gate_up.K) == (gate_up.N, gate_up.K) and
+                             (shared_down.N, shared_down.K) == (down.N, down.K))
         self.k, self.topk = k, topk
         self.score_mode, self.renorm = score_mode, renorm
         dev = gate_up.device
@@ -40,12 +46,15 @@ class MoeLayer:
     def bind(self, x, logits, z=None):
         """Marshal the layer's launches once for fixed input buffers; returns a
         list of (name, call) pairs to run in order."""
+        fs = self.fused_shared
+        sg = dict(shared=self.shared_gate_up, shared_act=x, shared_out=self.sh_h) if fs else {}
+        sd = dict(shared=self.shared_down, shared_act=self.sh_h, shared_out=self.sh_out) if fs else {}
         calls = [("route", ops.bind_moe_route_k(logits, self.topk, self.score_mode, self.renorm, self.route)),
                  ("gate_up", ops.bind_gather_qmv_k(self.gate_up, MODE_GATEUP_SWIGLU, x, self.route, self.k,
-                                                   self.topk, self.h)),
+                                                   self.topk, self.h, **sg)),
                  ("down", ops.bind_gather_qmv_k(self.down, MODE_PLAIN, self.h, self.route, self.k, self.topk,
-                                                self.partial))]
-        if self.shared_gate_up is not None:
+                                                self.partial, **sd))]
+        if self.shared_gate_up is not None and not fs:
             calls.append(("shared_gate_up", ops.bind_qmv_k(self.shared_gate_up, x, MODE_GATEUP_SWIGLU, self.sh_h)))
             calls.append(("shared_down", ops.bind_qmv_k(self.shared_down, self.sh_h, MODE_PLAIN, self.sh_out)))
         calls.append(("combine", ops.bind_moe_combine_k(self.partial, self.route.w, self.sh_out,
@@ -55,9 +64,12 @@ class MoeLayer:
     def __call__(self, x, logits, z=None):
         """x: bf16 bits [k, H] (int16); logits fp32 [k, E]; z fp32 [k] or None."""
         ops.moe_route_k(logits, self.topk, self.score_mode, self.renorm, out=self.route)
-        ops.gather_qmv_k(self.gate_up, MODE_GATEUP_SWIGLU, x, self.route, self.k, self.topk, out=self.h)
-        ops.gather_qmv_k(self.down, MODE_PLAIN, self.h, self.route, self.k, self.topk, out=self.partial)
-        if self.shared_gate_up is not None:
+        fs = self.fused_shared
+        sg = dict(shared=self.shared_gate_up, shared_act=x, shared_out=self.sh_h) if fs else {}
+        sd = dict(shared=self.shared_down, shared_act=self.sh_h, shared_out=self.sh_out) if fs else {}
+        ops.gather_qmv_k(self.gate_up, MODE_GATEUP_SWIGLU, x, self.route, self.k, self.topk, out=self.h, **sg)
+        ops.gather_qmv_k(self.down, MODE_PLAIN, self.h, self.route, self.k, self.topk, out=self.partial, **sd)
+        if self.shared_gate_up is not None and not fs:
             ops.qmv_k(self.shared_gate_up, x, MODE_GATEUP_SWIGLU, out=self.sh_h)
             ops.qmv_k(self.shared_down, self.sh_h, MODE_PLAIN, out=self.sh_out)
         ops.moe_combine_k(self.partial, self.route.w, self.sh_out, z if self.sh_out is not None else None,

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 10
+    assert len(names) == 13
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,31 +52,59 @@ def q4(E=1, N=64, K=128, group=64, codes=P, scales=P + 0x100000, biases=P + 0x20
     return L.SdvQ4(codes, scales, biases, E, N, K, group)
 
 
+def q4t(E=1, N=64, K=128, group=64, codes=P, sb=P + 0x100000, fused=0):
+    return L.SdvQ4T(codes, sb, E, N, K, group, fused)
+
+
 def qmv(lib, W, act=P + 0x400000, dtype=L.ACT_BF16, k=2, mode=L.MODE_PLAIN, y=P + 0x800000):
     return lib.sdv_qmv_k(ctypes.byref(W), act, dtype, k, mode, y, None)
 
 
+def test_tiled_sizes(lib):
+    # T tiles x G groups x (1 KB of codes, 128 B of scale/bias words)
+    assert lib.sdv_q4t_codes_bytes(512, 1280, 2560, 1) == 512 * 40 * 40 * 1024
+    assert lib.sdv_q4t_sb_bytes(512, 1280, 2560, 1) == 512 * 40 * 40 * 128
+    assert lib.sdv_q4t_codes_bytes(1, 1000, 576, 0) == 32 * 9 * 1024
+    assert lib.sdv_q4t_codes_bytes(1, 34, 64, 1) == 2 * 1 * 1024
+    assert lib.sdv_q4t_codes_bytes(1, 64, 100, 0) == 0
+
+
+def test_repack_validation(lib):
+    f = lib.sdv_q4_repack
+    out_c, out_s = P + 0x4000000, P + 0x8000000
+    assert f(ctypes.byref(q4(group=32)), 0, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(ctypes.byref(q4(N=63)), 1, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(ctypes.byref(q4()), 2, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(ctypes.byref(q4()), 0, 0, out_s, None) == L.SDV_EINVAL
+    assert f(ctypes.byref(q4()), 0, P + 16, out_s, None) == L.SDV_EALIAS      # over the source codes
+    assert f(ctypes.byref(q4()), 0, out_c, out_c + 64, None) == L.SDV_EALIAS  # outputs overlap
+
+
 def test_qmv_validation(lib):
-    assert qmv(lib, q4(), k=0) == L.SDV_EWIDTH
-    assert qmv(lib, q4(), k=10) == L.SDV_EWIDTH
-    assert qmv(lib, q4(group=32)) == L.SDV_ELAYOUT
-    assert qmv(lib, q4(K=100)) == L.SDV_ELAYOUT
-    assert qmv(lib, q4(K=0)) == L.SDV_ELAYOUT
-    assert qmv(lib, q4(E=2)) == L.SDV_EINVAL
-    assert qmv(lib, q4(N=0)) == L.SDV_EINVAL
-    assert qmv(lib, q4(codes=0)) == L.SDV_EINVAL
-    assert qmv(lib, q4(scales=P + 2)) == L.SDV_EINVAL
-    assert qmv(lib, q4(), act=0) == L.SDV_EINVAL
-    assert qmv(lib, q4(), y=P + 0x800008) == L.SDV_EINVAL
-    assert qmv(lib, q4(N=63), mode=L.MODE_GATEUP_SWIGLU) == L.SDV_ELAYOUT
-    assert qmv(lib, q4(), mode=7) == L.SDV_EINVAL
-    assert qmv(lib, q4(), dtype=5) == L.SDV_EINVAL
+    assert qmv(lib, q4t(), k=0) == L.SDV_EWIDTH
+    assert qmv(lib, q4t(), k=10) == L.SDV_EWIDTH
+    assert qmv(lib, q4t(group=32)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(K=100)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(K=0)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(E=2)) == L.SDV_EINVAL
+    assert qmv(lib, q4t(N=0)) == L.SDV_EINVAL
+    assert qmv(lib, q4t(codes=0)) == L.SDV_EINVAL
+    assert qmv(lib, q4t(sb=P + 4)) == L.SDV_EINVAL
+    assert qmv(lib, q4t(), act=0) == L.SDV_EINVAL
+    assert qmv(lib, q4t(), y=P + 0x800008) == L.SDV_EINVAL
+    assert qmv(lib, q4t(N=63, fused=1), mode=L.MODE_GATEUP_SWIGLU) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(fused=3)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(), mode=7) == L.SDV_EINVAL
+    assert qmv(lib, q4t(), dtype=5) == L.SDV_EINVAL
+    # the product mode must match the tile layout
+    assert qmv(lib, q4t(fused=0), mode=L.MODE_GATEUP_SWIGLU) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(fused=1), mode=L.MODE_PLAIN) == L.SDV_ELAYOUT
     # output inside the codes array
-    assert qmv(lib, q4(), y=P + 64) == L.SDV_EALIAS
+    assert qmv(lib, q4t(), y=P + 64) == L.SDV_EALIAS
     # output overlapping the activations
-    assert qmv(lib, q4(), y=P + 0x400000 + 16) == L.SDV_EALIAS
+    assert qmv(lib, q4t(), y=P + 0x400000 + 16) == L.SDV_EALIAS
     # fp32 activation rows that cannot be staged in LDS
-    assert qmv(lib, q4(K=8192), dtype=L.ACT_F32, k=9) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(K=8192), dtype=L.ACT_F32, k=9) == L.SDV_ELAYOUT
     assert "LDS" in lib.sdv_last_error().decode()
 
 
@@ -101,20 +129,43 @@ def test_route_validation(lib):
     assert route(lib, outs=outs) == L.SDV_EALIAS
 
 
-def gather(lib, bank, k=2, topk=4, mode=L.MODE_GATEUP_SWIGLU, dtype=L.ACT_BF16, out=P + 0x2000000):
+def gather(lib, bank, k=2, topk=4, mode=L.MODE_GATEUP_SWIGLU, dtype=L.ACT_BF16, out=P + 0x2000000,
+           shared=None, shared_act=None, shared_out=None):
     ptrs = [P + 0x800000 + 0x10000 * i for i in range(6)]
     return lib.sdv_gather_qmv_k(ctypes.byref(bank), mode, ptrs[0], dtype, ptrs[1], ptrs[2], ptrs[3], ptrs[4],
-                                ptrs[5], k, topk, out, None)
+                                ptrs[5], k, topk, out, ctypes.byref(shared) if shared is not None else None,
+                                shared_act, shared_out, None)
 
 
 def test_gather_validation(lib):
-    bank = q4(E=8, N=128, K=128)
+    bank = q4t(E=8, N=128, K=128, fused=1)
     assert gather(lib, bank, k=10) == L.SDV_EWIDTH
     assert gather(lib, bank, topk=9) == L.SDV_ERANGE
-    assert gather(lib, q4(E=8, N=127, K=128)) == L.SDV_ELAYOUT
-    assert gather(lib, q4(E=8, N=128, K=96)) == L.SDV_ELAYOUT
+    assert gather(lib, q4t(E=8, N=127, K=128, fused=1)) == L.SDV_ELAYOUT
+    assert gather(lib, q4t(E=8, N=128, K=96, fused=1)) == L.SDV_ELAYOUT
+    assert gather(lib, q4t(E=8, N=128, K=128, fused=0)) == L.SDV_ELAYOUT
     assert gather(lib, bank, out=0) == L.SDV_EINVAL
     assert gather(lib, bank, out=P + 0x800000) == L.SDV_EALIAS
+
+
+def test_gather_shared_validation(lib):
+    bank = q4t(E=8, N=128, K=128, fused=1)
+    sh = q4t(E=1, N=128, K=128, fused=1)
+    sh.codes, sh.sb = P + 0x4000000, P + 0x5000000
+    ok = dict(shared=sh, shared_act=P + 0x6000000, shared_out=P + 0x7000000)
+    assert gather(lib, bank, shared_act=P + 0x6000000) == L.SDV_EINVAL      # no shared weight
+    assert gather(lib, bank, shared_out=P + 0x7000000) == L.SDV_EINVAL
+    assert gather(lib, bank, **{**ok, "shared_out": None}) == L.SDV_EINVAL
+    assert gather(lib, bank, **{**ok, "shared_act": None}) == L.SDV_EINVAL
+    bad = q4t(E=2, N=128, K=128, fused=1)
+    assert gather(lib, bank, **{**ok, "shared": bad}) == L.SDV_EINVAL       # E must be 1
+    for geo in (dict(N=256, K=128, fused=1), dict(N=128, K=192, fused=1), dict(N=128, K=128, fused=0)):
+        other = q4t(E=1, **geo)
+        other.codes, other.sb = sh.codes, sh.sb
+        assert gather(lib, bank, **{**ok, "shared": other}) == L.SDV_ELAYOUT
+    assert gather(lib, bank, **{**ok, "shared_out": P + 0x2000000 + 64}) == L.SDV_EALIAS  # over out
+    assert gather(lib, bank, **{**ok, "shared_out": sh.codes}) == L.SDV_EALIAS
+    assert "shared" in lib.sdv_last_error().decode()
 
 
 def test_combine_validation(lib):

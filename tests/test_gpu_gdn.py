@@ -21,9 +21,10 @@ def _ops():
     return ops
 
 
-def layer_inputs(cfg, layer, k, hv, hk, d, step=0):
-    S = synth.gdn_state(cfg, layer, hv, d, d)
-    inp = synth.gdn_layer_inputs(cfg, layer, k, hv, hk, d, d, step=step)
+def layer_inputs(cfg, layer, k, hv, hk, d, step=0, dv=None):
+    dv = d if dv is None else dv
+    S = synth.gdn_state(cfg, layer, hv, dv, d)
+    inp = synth.gdn_layer_inputs(cfg, layer, k, hv, hk, d, dv, step=step)
     return S, inp
 
 
@@ -65,11 +66,12 @@ def test_tiny_layer_and_rollback_to_prefix_1():
     assert_close(to_np(st), oracle.rollback(S, ref_s, 1), "rollback to prefix 1")
 
 
-@pytest.mark.parametrize("hv,hk,d", [(48, 16, 128), (4, 1, 64), (6, 2, 128), (5, 5, 64)])
-def test_layer_matches_oracle(hv, hk, d):
-    banner(f"gdn layer Hv={hv} Hk={hk} D={d} k=9")
+@pytest.mark.parametrize("hv,hk,d,dv", [(48, 16, 128, 128), (4, 1, 64, 64), (6, 2, 128, 128), (5, 5, 64, 64),
+                                        (3, 1, 64, 40), (2, 2, 128, 7)])
+def test_layer_matches_oracle(hv, hk, d, dv):
+    banner(f"gdn layer Hv={hv} Hk={hk} Dk={d} Dv={dv} k=9")
     ops = _ops()
-    S, inp = layer_inputs(3, 1, 9, hv, hk, d)
+    S, inp = layer_inputs(3, 1, 9, hv, hk, d, dv=dv)
     S_d, dd = sdev.upload_f32(S, DEV), upload(inp)
     y, snaps = run(ops, S_d, dd)
     ref_y, ref_s = oracle_run(S, inp)

@@ -83,33 +83,37 @@ def oracle_moe(gu, dn, inp, topk, mode, renorm, sgu=None, sdn=None):
                              shared_down=oracle.dequant(*sdn) if sdn is not None else None)
 
 
-def run_layer(ops, pipeline, gu, dn, inp, k, topk, mode, renorm, sgu=None, sdn=None):
-    layer = pipeline.MoeLayer(q4_device_from_host(*gu), q4_device_from_host(*dn), k, topk,
+def run_layer(ops, pipeline, gu, dn, inp, k, topk, mode, renorm, sgu=None, sdn=None, fuse_shared=True):
+    layer = pipeline.MoeLayer(q4_device_from_host(*gu).tiled(True), q4_device_from_host(*dn).tiled(), k, topk,
                               ops.ROUTE_SOFTMAX if mode == "softmax" else ops.ROUTE_SIGMOID, renorm,
-                              q4_device_from_host(*sgu) if sgu is not None else None,
-                              q4_device_from_host(*sdn) if sdn is not None else None)
+                              q4_device_from_host(*sgu).tiled(True) if sgu is not None else None,
+                              q4_device_from_host(*sdn).tiled() if sdn is not None else None,
+                              fuse_shared=fuse_shared)
+    assert layer.fused_shared == (fuse_shared and sgu is not None)
     y = layer(sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV),
               sdev.upload_f32(inp["z"], DEV))
     torch.cuda.synchronize()
     return layer, to_np(y)
 
 
-@pytest.mark.parametrize("shared", [False, True])
-def test_small_moe_matches_oracle_and_width1(shared):
+@pytest.mark.parametrize("shared,fuse", [(False, True), (True, True), (True, False)])
+def test_small_moe_matches_oracle_and_width1(shared, fuse):
     ops, pipeline = _mods()
     k, topk = 9, 4
     gu, dn, inp, sgu, sdn = small_moe(k, shared=shared)
-    banner(f"small moe shared={shared}")
-    layer, y = run_layer(ops, pipeline, gu, dn, inp, k, topk, "softmax", False, sgu, sdn)
+    banner(f"small moe shared={shared} fused={fuse}")
+    layer, y = run_layer(ops, pipeline, gu, dn, inp, k, topk, "softmax", False, sgu, sdn, fuse)
     ref = oracle_moe(gu, dn, inp, topk, "softmax", False, sgu, sdn)
     assert int(to_np(layer.route.n_union)[0]) == ref["n_union"]
     assert_close(to_np(layer.h), ref["h"], "h")
     assert_close(to_np(layer.partial), ref["partial"], "partial")
+    if shared:
+        assert_close(to_np(layer.sh_out), ref["shared"], "shared expert")
     assert_close(y, ref["y"], "y")
     h9, p9 = to_np(layer.h), to_np(layer.partial)
     for r in range(k):
         one = {n: (v[r:r + 1] if n != "z" else v[r:r + 1]) for n, v in inp.items()}
-        l1, y1 = run_layer(ops, pipeline, gu, dn, one, 1, topk, "softmax", False, sgu, sdn)
+        l1, y1 = run_layer(ops, pipeline, gu, dn, one, 1, topk, "softmax", False, sgu, sdn, fuse)
         assert np.array_equal(to_np(l1.h)[0], h9[r]), f"h row {r}"
         assert np.array_equal(to_np(l1.partial)[0], p9[r]), f"partial row {r}"
         assert np.array_equal(y1[0], y[r]), f"y row {r}"
@@ -133,7 +137,7 @@ def test_ornith_shaped_layer():
             dev_rows = to_np(b[e, 1000:1024])
             assert np.array_equal(dev_rows.view(a.dtype), a), f"bank fill mismatch expert {e}"
     from speculative_decode_verification_amd.ops import Q4Weight
-    gu_w, dn_w = Q4Weight(*gu_d), Q4Weight(*dn_d)
+    gu_w, dn_w = Q4Weight(*gu_d).tiled(True), Q4Weight(*dn_d).tiled()
     for k in (2, 5, 9):
         banner(f"ornith layer k={k}")
         inp = synth.moe_layer_inputs(cfg, layer_id, k, H, E)
@@ -160,16 +164,26 @@ def test_flash_next_shaped_layer():
     gkeys = synth.bank_keys(cfg, GATEUP, layer_id)
     dkeys = synth.bank_keys(cfg, DOWN, layer_id)
     from speculative_decode_verification_amd.ops import Q4Weight
-    gu_w = Q4Weight(*sdev.q4_bank(gkeys, E, 2 * I, H, DEV))
-    dn_w = Q4Weight(*sdev.q4_bank(dkeys, E, H, I, DEV))
+    gu_w = Q4Weight(*sdev.q4_bank(gkeys, E, 2 * I, H, DEV)).tiled(True)
+    dn_w = Q4Weight(*sdev.q4_bank(dkeys, E, H, I, DEV)).tiled()
     sgu = synth.dense_weight(cfg, SHARED_GATEUP, layer_id, 2 * I, H)
     sdn = synth.dense_weight(cfg, SHARED_DOWN, layer_id, H, I)
-    layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, q4_device_from_host(*sgu),
-                              q4_device_from_host(*sdn))
+    sgu_w, sdn_w = q4_device_from_host(*sgu).tiled(True), q4_device_from_host(*sdn).tiled()
+    layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w)
+    assert layer.fused_shared
     inp = synth.moe_layer_inputs(cfg, layer_id, k, H, E)
     banner("flash-next layer k=9")
-    y = to_np(layer(sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV),
-                    sdev.upload_f32(inp["z"], DEV)))
+    args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV), sdev.upload_f32(inp["z"], DEV))
+    y = to_np(layer(*args))
+    # the same layer with the shared expert as two dense launches
+    split = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w, fuse_shared=False)
+    y_split = to_np(split(*args))
+    # the bound (marshalled-once) launches give the fused layer's result bit for bit
+    layer.y.zero_()
+    for _, call in layer.bind(*args):
+        call()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(layer.y), y)
     idx, _ = oracle.route(inp["logits"], topk, "sigmoid", True)
     used = sorted(set(idx.ravel().tolist()))
     gmat = {e: oracle.dequant(*synth.q4_rows(gkeys, E, 2 * I, H, expert=e)) for e in used}
@@ -182,7 +196,9 @@ def test_flash_next_shaped_layer():
     assert_close(to_np(layer.h), ref["h"], "h")
     assert_close(to_np(layer.partial), ref["partial"], "partial")
     assert_close(to_np(layer.sh_out), ref["shared"], "shared expert")
+    assert_close(to_np(split.sh_out), ref["shared"], "shared expert (dense launches)")
     assert_close(y, ref["y"], "y")
+    assert_close(y_split, ref["y"], "y (dense shared launches)")
 
 
 def test_combine_matches_oracle_order():

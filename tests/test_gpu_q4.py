@@ -29,7 +29,7 @@ def test_tiny_projection_matches_oracle():
     banner("qmv tiny N=K=1024 k=2")
     ops = _ops()
     codes, scales, biases, x = dense_case(0, 0, 1024, 1024, 2)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     y = ops.qmv_k(W, sdev.upload_bf16(x, DEV))
     ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x))
     assert_close(to_np(y), ref, "tiny projection")
@@ -39,7 +39,7 @@ def test_integer_exact_is_bit_exact():
     banner("qmv integer-exact N=256 K=1024 k=9")
     ops = _ops()
     codes, scales, biases, x = synth.integer_exact_weight(3, 256, 1024, 9)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     y = to_np(ops.qmv_k(W, sdev.upload_bf16(x, DEV)))
     ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x)).astype(np.float32)
     assert np.array_equal(y, ref)
@@ -49,7 +49,7 @@ def test_dense_5120_widths_bitwise_and_parity():
     banner("qmv 5120x5120 widths 1,4,8,9")
     ops = _ops()
     codes, scales, biases, x = dense_case(1, 0, 5120, 5120, 9)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     xd = sdev.upload_bf16(x, DEV)
     singles = [to_np(ops.qmv_k(W, xd[r:r + 1].contiguous()))[0] for r in range(9)]
     for k in (1, 4, 8, 9):
@@ -65,7 +65,7 @@ def test_ragged_shapes(N, K):
     banner(f"qmv ragged N={N} K={K}")
     ops = _ops()
     codes, scales, biases, x = dense_case(0, 7, N, K, 9)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     xd = sdev.upload_bf16(x, DEV)
     ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x))
     for k in (1, 3, 9):
@@ -78,7 +78,7 @@ def test_gate_up_swiglu(I, H):
     banner(f"qmv gate/up I={I} H={H}")
     ops = _ops()
     codes, scales, biases, x = dense_case(4, 3, 2 * I, H, 9, kind=SHARED_GATEUP)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled(fused_gateup=True)
     xd = sdev.upload_bf16(x, DEV)
     ref = oracle.swiglu(oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x)))
     y9 = to_np(ops.qmv_k(W, xd, mode=ops.MODE_GATEUP_SWIGLU))
@@ -94,7 +94,7 @@ def test_fp32_activations(N, K):
     ops = _ops()
     codes, scales, biases = synth.dense_weight(4, 4, 5, N, K)
     h = np.random.default_rng(N + K).standard_normal((9, K)).astype(np.float32) * np.float32(0.3)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     hd = sdev.upload_f32(h, DEV)
     ref = oracle.qmv(codes, scales, biases, h.astype(np.float64))
     y9 = to_np(ops.qmv_k(W, hd))
@@ -110,7 +110,7 @@ def test_mfma_row_position_independence():
     banner("qmv row permutation")
     ops = _ops()
     codes, scales, biases, x = dense_case(1, 3, 512, 1024, 9)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     y = to_np(ops.qmv_k(W, sdev.upload_bf16(x, DEV)))
     perm = np.array([8, 3, 0, 5, 1, 7, 2, 6, 4])
     yp = to_np(ops.qmv_k(W, sdev.upload_bf16(np.ascontiguousarray(x[perm]), DEV)))
@@ -121,8 +121,59 @@ def test_repeat_is_deterministic():
     banner("qmv determinism")
     ops = _ops()
     codes, scales, biases, x = dense_case(1, 4, 2048, 2048, 9)
-    W = q4_device_from_host(codes, scales, biases)
+    W = q4_device_from_host(codes, scales, biases).tiled()
     xd = sdev.upload_bf16(x, DEV)
     a = to_np(ops.qmv_k(W, xd))
     b = to_np(ops.qmv_k(W, xd))
     assert np.array_equal(a, b)
+
+
+def tile_host(codes, scales, biases, fused):
+    """The tiled layout written out from its definition in numpy (layout only)."""
+    n, kw = codes.shape
+    k = kw * 8
+    g = k // 64
+    T = (n // 2 + 15) // 16 if fused else (n + 31) // 32
+    tc = np.zeros((T, g, 64, 4), dtype=np.uint32)
+    tsb = np.zeros((T, g, 32), dtype=np.uint32)
+    for t in range(T):
+        for c in range(32):
+            if fused:
+                i = 16 * t + (c % 16)
+                if i >= n // 2:
+                    continue
+                row = i if c < 16 else n // 2 + i
+            else:
+                row = 32 * t + c
+                if row >= n:
+                    continue
+            for gg in range(g):
+                for h in range(2):
+                    tc[t, gg, 32 * h + c] = codes[row, 8 * gg + 4 * h: 8 * gg + 4 * h + 4]
+                tsb[t, gg, c] = int(scales[row, gg]) | (int(biases[row, gg]) << 16)
+    return tc, tsb
+
+
+@pytest.mark.parametrize("N,K,fused", [(64, 128, False), (70, 192, False), (2 * 40, 128, True), (2 * 17, 64, True)])
+def test_repack_layout(N, K, fused):
+    banner(f"repack N={N} K={K} fused={fused}")
+    codes, scales, biases = synth.dense_weight(0, 9, 1, N, K)
+    W = q4_device_from_host(codes, scales, biases)
+    Wt = W.tiled(fused_gateup=fused)
+    tc, tsb = tile_host(codes, scales, biases, fused)
+    got_c = to_np(Wt.codes).view(np.uint32).reshape(tc.shape)
+    got_s = to_np(Wt.sb).view(np.uint32).reshape(tsb.shape)
+    assert np.array_equal(got_c, tc)
+    assert np.array_equal(got_s, tsb)
+
+
+def test_mode_must_match_layout():
+    banner("qmv layout/mode mismatch")
+    ops = _ops()
+    codes, scales, biases, x = dense_case(0, 8, 64, 128, 2)
+    W = q4_device_from_host(codes, scales, biases)
+    xd = sdev.upload_bf16(x, DEV)
+    with pytest.raises(ops.SdvError, match="fused_gateup=1"):
+        ops.qmv_k(W.tiled(False), xd, mode=ops.MODE_GATEUP_SWIGLU)
+    with pytest.raises(ops.SdvError, match="fused_gateup=0"):
+        ops.qmv_k(W.tiled(True), xd)
