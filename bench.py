@@ -33,6 +33,10 @@ if ROOT not in sys.path:
 METRIC = "verified rows/s and achieved HBM GB/s (% of peak) for k-row Q4 verify + GDN"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 DOMINANT = "gate_up"
+# the dominant kernel is bracketed by timing events in every SAMPLE_EVERY-th
+# layer of each timed step: each event pair adds a few microseconds of idle
+# time to the stream, so sampling keeps the step time close to untimed runs
+SAMPLE_EVERY = 4
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -63,6 +67,69 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "speculative_decode_verification_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _hip_runtime():
+    """The HIP runtime already mapped into this process (the one torch and
+    libsdv use), so events and streams are the same objects."""
+    import ctypes
+    paths = []
+    with open("/proc/self/maps") as f:
+        for line in f:
+            part = line.split()
+            if len(part) >= 6 and "libamdhip64" in part[-1] and part[-1] not in paths:
+                paths.append(part[-1])
+    if len(paths) != 1:
+        raise RuntimeError(f"expected one HIP runtime in the process, found {paths}")
+    return ctypes.CDLL(paths[0]), paths[0]
+
+
+class HipTimer:
+    """Timing events recorded on the launch stream without the system-scope
+    fence default events carry (hipEventDisableSystemFence): recording them
+    between kernels then costs no cache write-back and invalidation, so the
+    timed sequence runs as it would untimed.  Events are created up front."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, pairs):
+        import ctypes
+        import torch
+        self.ct = ctypes
+        self.rt, self.path = _hip_runtime()
+        self.rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.pool = []
+        for _ in range(2 * pairs):
+            ev = ctypes.c_void_p()
+            rc = self.rt.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.pool.append(ev)
+        self.next = 0
+
+    def start(self):
+        ev = self.pool[self.next]
+        self.next += 1
+        self.rt.hipEventRecord(ev, self.stream)
+        return ev
+
+    stop = start
+
+    def elapsed_us(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.rt.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value * 1e3
+
+    def close(self):
+        for ev in self.pool:
+            self.rt.hipEventDestroy(ev)
+        self.pool = []
 
 
 def cpu_model():
@@ -122,34 +189,25 @@ class Workload:
         self.setup_s = time.time() - t0
         self.bank_bytes = self.layers * (self.E + 1) * (q4_bytes(2 * self.I, self.H) + q4_bytes(self.H, self.I))
 
-    def step(self, s, js, events=None, per_kernel=None):
-        import torch
+    def step(self, s, js, timer=None, events=None, per_kernel=None):
+        """One verify step over all layers, then rollback of every GDN layer.
+        With ``events``, the dominant kernel of every layer is bracketed by
+        timer events; with ``per_kernel``, every launch is."""
+        def run(name, l, call):
+            if per_kernel is not None or (events is not None and name == DOMINANT and l % SAMPLE_EVERY == 0):
+                a = timer.start()
+                call()
+                b = timer.stop()
+                (per_kernel if per_kernel is not None else events).append((name, l, a, b))
+            else:
+                call()
+
         for l in range(self.layers):
             g = self.gdn.get(l)
             if g is not None:
-                if per_kernel is not None:
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    g[0].run_bound()
-                    b.record()
-                    per_kernel.append(("gdn", l, a, b))
-                else:
-                    g[0].run_bound()
+                run("gdn", l, g[0].run_bound)
             for name, call in self.calls[l]:
-                if per_kernel is not None:
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    call()
-                    b.record()
-                    per_kernel.append((name, l, a, b))
-                elif events is not None and name == DOMINANT:
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    call()
-                    b.record()
-                    events.append((l, a, b))
-                else:
-                    call()
+                run(name, l, call)
         j = js[s % len(js)]
         for gl, _ in self.gdn.values():
             gl.rollback(j)
@@ -292,23 +350,25 @@ def main():
     torch.cuda.synchronize()
     unions = wl.unions()
 
+    per_step = len(wl.calls[0]) * wl.layers + len(wl.gdn)
+    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1)
+    log(f"timing events on the launch stream (HIP runtime {timer.path})")
     events = []
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    t_start = timer.start()
     for s in range(args.steps):
-        wl.step(args.warmup + s, js, events=events)
-    t_end.record()
+        wl.step(args.warmup + s, js, timer=timer, events=events)
+    t_end = timer.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
+    ms_total = timer.elapsed_us(t_start, t_end) / 1e3
     ms_step = ms_total / args.steps
     rows_per_s = k * args.steps / (ms_total / 1e3)
     step_bytes = wl.step_bytes(unions)
 
-    dom_us = [a.elapsed_time(b) * 1e3 for (_, a, b) in events]
-    dom_bytes = [wl.kernel_bytes(DOMINANT, l, unions) for (l, _, _) in events]
+    dom_us = [timer.elapsed_us(a, b) for (_, _, a, b) in events]
+    dom_bytes = [wl.kernel_bytes(DOMINANT, l, unions) for (_, l, _, _) in events]
     dom_avg_us = sum(dom_us) / len(dom_us)
     dom_gbs = sum(dom_bytes) / (sum(dom_us) * 1e-6) / 1e9
     khash = kernel_source_hash()
@@ -317,11 +377,11 @@ def main():
     breakdown = None
     if not args.no_breakdown:
         per = []
-        wl.step(args.warmup + args.steps, js, per_kernel=per)
+        wl.step(args.warmup + args.steps, js, timer=timer, per_kernel=per)
         torch.cuda.synchronize()
         agg = {}
         for name, l, a, b in per:
-            us = a.elapsed_time(b) * 1e3
+            us = timer.elapsed_us(a, b)
             d = agg.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0})
             d["launches"] += 1
             d["us"] += us
@@ -367,6 +427,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "host_cpu": cpu_model()},
     }
+    timer.close()
     print(json.dumps(out), flush=True)
 
 

@@ -53,6 +53,8 @@
 // activations: part p of row i is MFMA row i + 8p for i < 8 and 24 + p for
 // i = 8, so the three parts of a row land in one lane's registers.
 
+#include <atomic>
+
 #include "common.h"
 
 namespace sdv {
@@ -62,6 +64,7 @@ namespace {
 constexpr int kTileCols = 32;
 constexpr int kMaxWaves = 8;
 constexpr int kGatherWaves = 8;
+constexpr int kGatherTilesPerWave = 1;  // tiles one wave streams back to back
 constexpr int kPF = 8;  // groups in flight per lane
 
 struct Q4Args {
@@ -507,10 +510,16 @@ __global__ __launch_bounds__(512, 4) void q4_gather_kernel(Q4Args a) {
 template <int MODE, int ACT, bool GATHER>
 hipError_t launch_one(const Q4Args& a, int blocks_x, int units, int nw, size_t lds, hipStream_t st) {
   void (*kern)(Q4Args) = GATHER ? q4_gather_kernel<MODE, ACT> : q4_dense_kernel<MODE, ACT>;
-  if (lds > 65536) {
+  // raise the kernel's dynamic LDS limit once per process (the largest size
+  // asked for so far; the attribute is per function, not per device)
+  static std::atomic<size_t> lds_limit{65536};
+  size_t cur = lds_limit.load(std::memory_order_relaxed);
+  if (lds > cur) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
+    while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
+    }
   }
   hipLaunchKernelGGL(kern, dim3(blocks_x, units), dim3(64 * nw), lds, st, a);
   return hipGetLastError();
@@ -617,7 +626,7 @@ size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather) {
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   // gathered: per-wave output staging for one tile of up to 9 rows x 32 columns
   return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * 4 +
-                      (size_t)kGatherWaves * SDV_MAX_ROWS * 32 * 4
+                      (size_t)kGatherWaves * kGatherTilesPerWave * SDV_MAX_ROWS * 32 * 4
                 : q4_lds_bytes(K, cap, q4_waves_for(K));
 }
 
@@ -649,7 +658,7 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
   a.slot_cap = (act_dtype == SDV_ACT_F32) ? 3 * k : k;
   if (gather) {
     const int nw = kGatherWaves;
-    a.tiles_per_block = nw;
+    a.tiles_per_block = nw * kGatherTilesPerWave;
     const int bx = (a.T + a.tiles_per_block - 1) / a.tiles_per_block;
     const int units = k * topk + (shared ? 1 : 0);
     const size_t lds = q4_lds_bytes_for(W.K, act_dtype, k, true);

@@ -4,10 +4,12 @@
 // (expert, row) pairs of their union; Flash-Next plan "2.3 MoE").
 //
 // One workgroup of 16 waves.  Wave r selects row r's top-k by repeated
-// argmax: each lane scans its own logits, the 16 lanes of a DPP row reduce
-// with DPP moves, and the four row winners are read into scalar registers.
-// Selection compares the raw fp32 logits (higher first, ties to the lower
-// index), so it is exact and independent of how the scores are rounded.
+// argmax over 64-bit (value, index) keys: each lane takes the largest of its
+// own candidates, the 16 lanes of a DPP row reduce with DPP moves, and the
+// four row winners are compared in scalar registers; the code has no
+// data-dependent branches.  Selection compares the raw fp32 logits (higher
+// first, ties to the lower index), so it is exact and independent of how the
+// scores are rounded.
 // The union and the pair order come from per-row expert bitmaps, per-expert
 // counts and one prefix scan over the experts, all integer and independent
 // of thread timing.
@@ -34,42 +36,53 @@ struct RouteArgs {
   int32_t* pair_slot;
 };
 
-// (value, index) order: larger value first, then smaller index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return (v > bv) || (v == bv && i < bi);
+// Selection key of (value, index): larger value first, then smaller index.
+// The high word maps the fp32 value onto an unsigned order (-0 taken as +0,
+// so the two zeros tie); the low word is the complement of the index.  NaN
+// and empty candidates get key 0, which never wins.
+__device__ __forceinline__ uint64_t sel_key(float v, int e) {
+  const float c = v + 0.0f;  // -0 + +0 = +0 under round-to-nearest
+  const uint32_t b = __float_as_uint(c);
+  const uint32_t hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint64_t key = ((uint64_t)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+  return (c != c) ? 0ull : key;
 }
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
 template <int CTRL>
-__device__ __forceinline__ void dpp_best(float& bv, int& bi) {
-  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, false);
-  if (better(ov, oi, bv, bi)) {
-    bv = ov;
-    bi = oi;
-  }
+__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
 }
 
-// Best (value, index) of the wave, returned in every lane (scalar registers).
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-  dpp_best<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
-  dpp_best<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
-  dpp_best<0x124>(bv, bi);  // row_ror:4
-  dpp_best<0x128>(bv, bi);  // row_ror:8   (every lane now holds its row's best)
-  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-  int i = __builtin_amdgcn_readlane(bi, 0);
+// Largest key of the wave, in every lane (via scalar registers).
+__device__ __forceinline__ uint64_t wave_max(uint64_t k) {
+  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max<0x124>(k);  // row_ror:4
+  k = dpp_max<0x128>(k);  // row_ror:8   (every lane now holds its row's largest)
+  uint64_t best = 0;
 #pragma unroll
-  for (int row = 1; row < 4; ++row) {
-    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * row));
-    const int ri = __builtin_amdgcn_readlane(bi, 16 * row);
-    if (better(rv, ri, v, i)) {
-      v = rv;
-      i = ri;
-    }
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
+    const uint64_t rk = ((uint64_t)hi << 32) | lo;
+    best = rk > best ? rk : best;
   }
-  bv = v;
-  bi = i;
+  return best;
 }
 
+// Wave r < k selects row r's top-k: each lane holds PL candidates (expert
+// lane + 64 j); a round takes the wave's largest key and clears it.
+template <int PL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int32_t s_idx[SDV_MAX_ROWS * SDV_MAX_TOPK];
   __shared__ uint32_t s_rowbits[SDV_MAX_ROWS][kWords];
@@ -79,7 +92,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int E = a.E, topk = a.topk;
-  const int per_lane = (E + 63) >> 6;
 
   for (int t = tid; t < SDV_MAX_ROWS * kWords; t += kRouteThreads) (&s_rowbits[0][0])[t] = 0u;
   for (int t = tid; t < SDV_MAX_EXPERTS; t += kRouteThreads) s_cnt[t] = 0;
@@ -87,68 +99,52 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   if (wave < a.k) {
     const int r = wave;
     const float* l = a.logits + (size_t)r * E;
-    float val[kMaxPerLane];
-    bool taken[kMaxPerLane];
+    float val[PL];
+    uint64_t key[PL];
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < PL; ++j) val[j] = l[min(lane + 64 * j, E - 1)];  // unconditional loads
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
       const int e = lane + 64 * j;
-      const bool in = (j < per_lane) && (e < E);
-      val[j] = in ? l[e] : 0.0f;
-      taken[j] = !in;
+      key[j] = e < E ? sel_key(val[j], e) : 0ull;
     }
-    float sel_val[SDV_MAX_TOPK];
-    int sel_idx[SDV_MAX_TOPK];
+    uint64_t mine = 0;  // lane s keeps slot s's key
     for (int s = 0; s < topk; ++s) {
-      float bv = -__builtin_inff();
-      int bi = 0x7FFFFFFF;
+      uint64_t m = key[0];
 #pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
-        const int e = lane + 64 * j;
-        if (!taken[j] && better(val[j], e, bv, bi)) {
-          bv = val[j];
-          bi = e;
-        }
-      }
-      wave_best(bv, bi);
-      sel_val[s] = bv;
-      sel_idx[s] = bi < E ? bi : -1;  // no candidate left (only NaN logits remain)
-      if ((bi & 63) == lane) {
+      for (int j = 1; j < PL; ++j) m = key[j] > m ? key[j] : m;
+      const uint64_t win = wave_max(m);
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j)
-          if (j == (bi >> 6)) taken[j] = true;
-      }
+      for (int j = 0; j < PL; ++j) key[j] = key[j] == win ? 0ull : key[j];
+      mine = lane == s ? win : mine;
     }
-    // scores of the selected slots
-    float p[SDV_MAX_TOPK];
+    const bool has = lane < topk && mine != 0ull;
+    const float v = key_value(mine);
+    // score of this lane's slot
+    float p;
     if (a.mode == SDV_ROUTE_SOFTMAX) {
-      const float m = sel_val[0];  // the largest logit of the row
+      const float mx = __shfl(v, 0);  // slot 0 holds the row's largest logit
       float part = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
-        const int e = lane + 64 * j;
-        if (j < per_lane && e < E) part = part + expf(val[j] - m);
-      }
+      for (int j = 0; j < PL; ++j)
+        if (lane + 64 * j < E) part = part + expf(val[j] - mx);
 #pragma unroll
       for (int off = 1; off <= 32; off <<= 1) part = part + __shfl_xor(part, off);
-      for (int s = 0; s < topk; ++s) p[s] = expf(sel_val[s] - m) / part;
+      p = expf(v - mx) / part;
     } else {
-      for (int s = 0; s < topk; ++s) p[s] = 1.0f / (1.0f + expf(-sel_val[s]));
+      p = 1.0f / (1.0f + expf(-v));
     }
+    p = has ? p : 0.0f;
     if (a.renorm) {
-      float den = 0.0f;
-      for (int s = 0; s < topk; ++s) den = den + p[s];
-      for (int s = 0; s < topk; ++s) p[s] = p[s] / den;
+      // fixed butterfly over the slots (lanes past topk add exact zeros)
+      float den = p;
+#pragma unroll
+      for (int off = 1; off <= 32; off <<= 1) den = den + __shfl_xor(den, off);
+      p = p / den;
     }
-    // every lane holds the same scores; lane s writes slot s
     if (lane < topk) {
-      float pv = 0.0f;
-      int iv = 0;
-      for (int s = 0; s < topk; ++s)
-        if (s == lane) {
-          pv = p[s];
-          iv = sel_idx[s];
-        }
-      a.w[r * topk + lane] = pv;
+      const int iv = has ? key_index(mine) : -1;
+      a.w[r * topk + lane] = has ? p : 0.0f;
       a.idx[r * topk + lane] = iv;
       s_idx[r * topk + lane] = iv;
     }
@@ -221,7 +217,20 @@ hipError_t route_launch(const float* logits, int k, int E, int topk, int mode, i
                         int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
                         int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot, hipStream_t st) {
   RouteArgs a{logits, k, E, topk, mode, renorm, idx, w, union_ids, n_union, pair_off, pair_row, pair_slot};
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, a);
+  // candidates per lane: the smallest power of two covering E / 64
+  const int per_lane = (E + 63) / 64;
+  if (per_lane <= 1)
+    hipLaunchKernelGGL(route_kernel<1>, dim3(1), dim3(kRouteThreads), 0, st, a);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL(route_kernel<2>, dim3(1), dim3(kRouteThreads), 0, st, a);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL(route_kernel<4>, dim3(1), dim3(kRouteThreads), 0, st, a);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL(route_kernel<8>, dim3(1), dim3(kRouteThreads), 0, st, a);
+  else if (per_lane <= kMaxPerLane)
+    hipLaunchKernelGGL(route_kernel<kMaxPerLane>, dim3(1), dim3(kRouteThreads), 0, st, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
