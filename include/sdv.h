@@ -206,6 +206,54 @@ SDV_API int sdv_gather_qmv_k(const sdv_q4t *bank, int mode, const void *act, int
                      float *shared_out, sdv_stream_t stream);
 
 /*
+ * sdv_moe_experts_k -- the union experts' whole MLP in one launch: fused
+ * gate/up with SwiGLU, then the down projection, each union expert's packed
+ * weights read once for all rows routed to it (mere.run report, "Exact
+ * verification kernels and benchmark admission": gathered expert kernel with
+ * fused gate/up weights; Red Lite dev45, "What it is": one pool encode with a
+ * two-input gate/up pipeline for the union's (expert, row) pairs; Flash-Next
+ * plan "2.3 MoE": top-10 of 512 plus one shared expert).  The intermediate
+ * dimension is cut into S = ceil(I / 128) slices; workgroup (expert, slice)
+ * computes h = silu(gate) * up for its slice and multiplies it by the matching
+ * K slice of the down weight, so for slot (r, s) of row r
+ *   sum_{j = 0..S-1, ascending} partial[j][r][s] = down_e(silu(gate_e x_r) * up_e x_r)
+ * with e = idx[r][s]; sdv_moe_combine_sliced_k adds the slices in that order.
+ *   gate_up    tiled bank with fused_gateup = 1: E experts of [2I][H] (gate rows, then up rows)
+ *   down       tiled bank with fused_gateup = 0: E experts of [H][I]
+ *   x          device bf16 bits [k][H], row r's input for all of its slots
+ *   union_ids, n_union, pair_off, pair_row, pair_slot  device, as written by sdv_moe_route_k
+ *   shared_gate_up, shared_down  optional always-on expert (E = 1, same geometry), applied to
+ *              all k rows and written to slot topk; both NULL for none
+ *   partial    device fp32 [S][k][topk + 1][H] (sdv_moe_experts_partial_bytes); entries of
+ *              slots without an expert, and slot topk without a shared expert, are not written
+ * H and I must be multiples of 64, I at most 1024; LDS limits H (about 7000 at k = 9).
+ * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_moe_experts_k(const sdv_q4t *gate_up, const sdv_q4t *down, const void *x,
+                              const int32_t *union_ids, const int32_t *n_union, const int32_t *pair_off,
+                              const int32_t *pair_row, const int32_t *pair_slot, int k, int topk,
+                              const sdv_q4t *shared_gate_up, const sdv_q4t *shared_down, float *partial,
+                              sdv_stream_t stream);
+
+/* Bytes of sdv_moe_experts_k's partial output, or 0 for invalid sizes. */
+SDV_API size_t sdv_moe_experts_partial_bytes(int k, int topk, int H, int I);
+
+/*
+ * sdv_moe_combine_sliced_k -- the MoE tail over sdv_moe_experts_k's output
+ * (Red Lite dev45, "What it is": one tail for all rows; Flash-Next plan "5.3
+ * MoE deltas": fixed-width weighted expert sums):
+ *   P[r][s][n] = sum_{j = 0..S-1, ascending} partial[j][r][s][n]
+ *   y[r][n]    = sum_{s = 0..topk-1, ascending, idx[r][s] >= 0} w[r][s] * P[r][s][n]
+ *                + sigmoid(shared_logit[r]) * P[r][topk][n]     (if has_shared)
+ *   partial device fp32 [S][k][topk + 1][H] with S = ceil(I / 128); idx device int32 [k][topk];
+ *   w device fp32 [k][topk]; shared_logit device fp32 [k] or NULL (gate 1); y device fp32 [k][H].
+ * I at most 1024.  Errors: EINVAL, EWIDTH, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_moe_combine_sliced_k(const float *partial, const int32_t *idx, const float *w,
+                                     const float *shared_logit, int k, int topk, int H, int I, int has_shared,
+                                     float *y, sdv_stream_t stream);
+
+/*
  * sdv_moe_combine_k -- one MoE tail for all rows (Red Lite dev45, "What it
  * is": one tail for both rows; Flash-Next plan "5.3 MoE deltas": fixed-width
  * weighted expert sum):

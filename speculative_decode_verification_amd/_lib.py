@@ -12,7 +12,8 @@ ACT_BF16, ACT_F32 = 0, 1
 ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1
 
 EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_qmv_k", "sdv_moe_route_k",
-           "sdv_gather_qmv_k", "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
+           "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
+           "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
            "sdv_gdn_rollback_copy", "sdv_status_string", "sdv_last_error", "sdv_build_info")
 
 
@@ -46,6 +47,10 @@ _SIGS = {
     "sdv_moe_route_k": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
     "sdv_gather_qmv_k": [ctypes.POINTER(SdvQ4T), _I, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P,
                          ctypes.POINTER(SdvQ4T), _P, _P, _P],
+    "sdv_moe_experts_k": [ctypes.POINTER(SdvQ4T), ctypes.POINTER(SdvQ4T), _P, _P, _P, _P, _P, _P, _I, _I,
+                          ctypes.POINTER(SdvQ4T), ctypes.POINTER(SdvQ4T), _P, _P],
+    "sdv_moe_experts_partial_bytes": [_I, _I, _I, _I],
+    "sdv_moe_combine_sliced_k": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P],
     "sdv_moe_combine_k": [_P, _P, _P, _P, _I, _I, _I, _P, _P],
     "sdv_gdn_verify_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_P), _P],
     "sdv_gdn_rollback": [_I, _I, ctypes.POINTER(_I)],
@@ -69,7 +74,7 @@ def lib():
             fn.argtypes = args
             if name in ("sdv_status_string", "sdv_last_error", "sdv_build_info"):
                 fn.restype = ctypes.c_char_p
-            elif name in ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes"):
+            elif name in ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_moe_experts_partial_bytes"):
                 fn.restype = ctypes.c_size_t
             else:
                 fn.restype = ctypes.c_int

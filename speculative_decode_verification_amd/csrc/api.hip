@@ -23,6 +23,16 @@ hipError_t route_launch(const float* logits, int k, int E, int topk, int mode, i
 hipError_t combine_launch(const float* partial, const float* w, const float* shared_out,
                           const float* shared_logit, int k, int topk, int H, float* y,
                           hipStream_t st);
+hipError_t combine_sliced_launch(const float* partial, const int32_t* idx, const float* w,
+                                 const float* shared_logit, int S, int k, int topk, int H, int has_shared,
+                                 float* y, hipStream_t st);
+int expert_slices(int I);
+size_t expert_lds_bytes(int k, int H);
+size_t expert_partial_bytes(int k, int topk, int H, int I);
+hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn,
+                              const void* x, const int32_t* union_ids, const int32_t* n_union,
+                              const int32_t* pair_off, const int32_t* pair_row, const int32_t* pair_slot, int k,
+                              int topk, float* partial, hipStream_t st);
 hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
                       const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
                       float* y, float* const* snaps, hipStream_t st);
@@ -32,6 +42,7 @@ namespace {
 
 // LDS available to one workgroup on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kMaxExpertInter = 1024;  // fused expert path: at most 8 slices of 128
 
 thread_local char g_err[256] = "";
 
@@ -297,6 +308,103 @@ int sdv_gather_qmv_k(const sdv_q4t* bank, int mode, const void* act, int act_dty
                                    pair_row, pair_slot, k, topk, out, shared, shared_act, shared_out,
                                    (hipStream_t)stream),
                     "sdv_gather_qmv_k launch");
+}
+
+size_t sdv_moe_experts_partial_bytes(int k, int topk, int H, int I) {
+  if (k < 1 || k > SDV_MAX_ROWS || topk < 1 || topk > SDV_MAX_TOPK || H <= 0 || I <= 0 || H % SDV_GROUP ||
+      I % SDV_GROUP)
+    return 0;
+  return sdv::expert_partial_bytes(k, topk, H, I);
+}
+
+int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x, const int32_t* union_ids,
+                      const int32_t* n_union, const int32_t* pair_off, const int32_t* pair_row,
+                      const int32_t* pair_slot, int k, int topk, const sdv_q4t* shared_gate_up,
+                      const sdv_q4t* shared_down, float* partial, sdv_stream_t stream) {
+  int st;
+  if ((st = check_q4t(gate_up, "gate_up"))) return st;
+  if ((st = check_q4t(down, "down"))) return st;
+  if (!gate_up->fused_gateup) return fail(SDV_ELAYOUT, "gate_up must be repacked with fused_gateup=1");
+  if (down->fused_gateup) return fail(SDV_ELAYOUT, "down must be repacked with fused_gateup=0");
+  const int H = gate_up->K, I = gate_up->N / 2;
+  if (down->E != gate_up->E || down->N != H || down->K != I)
+    return fail(SDV_ELAYOUT, "down is E=%d N=%d K=%d, expected E=%d N=%d K=%d (gate_up E=%d N=2I=%d K=H=%d)",
+                down->E, down->N, down->K, gate_up->E, H, I, gate_up->E, gate_up->N, H);
+  if (I % SDV_GROUP) return fail(SDV_ELAYOUT, "intermediate size %d is not a multiple of 64", I);
+  if (I > kMaxExpertInter) return fail(SDV_ERANGE, "intermediate size %d above %d (8 slices)", I, kMaxExpertInter);
+  if ((st = check_width(k))) return st;
+  if (topk < 1 || topk > SDV_MAX_TOPK || topk > gate_up->E)
+    return fail(SDV_ERANGE, "topk=%d outside 1..min(E,%d)", topk, SDV_MAX_TOPK);
+  if ((shared_gate_up == nullptr) != (shared_down == nullptr))
+    return fail(SDV_EINVAL, "give both shared expert weights or neither");
+  if (shared_gate_up) {
+    if ((st = check_q4t(shared_gate_up, "shared_gate_up"))) return st;
+    if ((st = check_q4t(shared_down, "shared_down"))) return st;
+    if (shared_gate_up->E != 1 || shared_down->E != 1)
+      return fail(SDV_EINVAL, "shared expert weights need E=1");
+    if (shared_gate_up->N != gate_up->N || shared_gate_up->K != H || !shared_gate_up->fused_gateup ||
+        shared_down->N != H || shared_down->K != I || shared_down->fused_gateup)
+      return fail(SDV_ELAYOUT, "shared expert geometry differs from the routed experts'");
+  }
+  const size_t lds = sdv::expert_lds_bytes(k, H);
+  if (lds > kMaxLds) return fail(SDV_ELAYOUT, "H=%d with k=%d needs %zu bytes of LDS (max %zu)", H, k, lds, kMaxLds);
+  const size_t pbytes = sdv::expert_partial_bytes(k, topk, H, I);
+  if (pbytes >= 0x7FFFFFF0u) return fail(SDV_ERANGE, "partial output of %zu bytes exceeds 2 GiB", pbytes);
+  const void* ptrs[] = {x, union_ids, n_union, pair_off, pair_row, pair_slot, partial};
+  const char* names[] = {"x", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot", "partial"};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  const size_t kt = (size_t)k * topk;
+  Range outs[] = {{partial, pbytes, "partial"}};
+  Range ins[] = {
+      {gate_up->codes, sdv::q4t_codes_bytes(gate_up->E, gate_up->N, H, 1), "gate_up codes"},
+      {gate_up->sb, sdv::q4t_sb_bytes(gate_up->E, gate_up->N, H, 1), "gate_up sb"},
+      {down->codes, sdv::q4t_codes_bytes(down->E, H, I, 0), "down codes"},
+      {down->sb, sdv::q4t_sb_bytes(down->E, H, I, 0), "down sb"},
+      {shared_gate_up ? shared_gate_up->codes : nullptr, shared_gate_up ? sdv::q4t_codes_bytes(1, 2 * I, H, 1) : 0,
+       "shared_gate_up codes"},
+      {shared_gate_up ? shared_gate_up->sb : nullptr, shared_gate_up ? sdv::q4t_sb_bytes(1, 2 * I, H, 1) : 0,
+       "shared_gate_up sb"},
+      {shared_down ? shared_down->codes : nullptr, shared_down ? sdv::q4t_codes_bytes(1, H, I, 0) : 0,
+       "shared_down codes"},
+      {shared_down ? shared_down->sb : nullptr, shared_down ? sdv::q4t_sb_bytes(1, H, I, 0) : 0, "shared_down sb"},
+      {x, (size_t)k * H * 2, "x"},
+      {union_ids, kt * 4, "union_ids"},
+      {n_union, 4, "n_union"},
+      {pair_off, (kt + 1) * 4, "pair_off"},
+      {pair_row, kt * 4, "pair_row"},
+      {pair_slot, kt * 4, "pair_slot"}};
+  if ((st = check_alias(outs, 1, ins, 14))) return st;
+  return hip_status(sdv::moe_experts_launch(*gate_up, *down, shared_gate_up, shared_down, x, union_ids, n_union,
+                                            pair_off, pair_row, pair_slot, k, topk, partial, (hipStream_t)stream),
+                    "sdv_moe_experts_k launch");
+}
+
+int sdv_moe_combine_sliced_k(const float* partial, const int32_t* idx, const float* w, const float* shared_logit,
+                             int k, int topk, int H, int I, int has_shared, float* y, sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (topk < 1 || topk > SDV_MAX_TOPK) return fail(SDV_ERANGE, "topk=%d outside 1..%d", topk, SDV_MAX_TOPK);
+  if (H <= 0 || H % SDV_GROUP || I <= 0 || I % SDV_GROUP)
+    return fail(SDV_EINVAL, "H=%d and I=%d must be positive multiples of 64", H, I);
+  if (I > kMaxExpertInter) return fail(SDV_ERANGE, "I=%d above %d (8 slices)", I, kMaxExpertInter);
+  if (has_shared != 0 && has_shared != 1) return fail(SDV_EINVAL, "has_shared=%d must be 0 or 1", has_shared);
+  if (shared_logit && !has_shared) return fail(SDV_EINVAL, "shared_logit given without a shared expert");
+  const void* ptrs[] = {partial, idx, w, y};
+  const char* names[] = {"partial", "idx", "w", "y"};
+  for (int i = 0; i < 4; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  if (shared_logit && (st = check_ptr(shared_logit, "shared_logit"))) return st;
+  const size_t kt = (size_t)k * topk;
+  Range outs[] = {{y, (size_t)k * H * 4, "y"}};
+  Range ins[] = {{partial, sdv::expert_partial_bytes(k, topk, H, I), "partial"},
+                 {idx, kt * 4, "idx"},
+                 {w, kt * 4, "w"},
+                 {shared_logit, shared_logit ? (size_t)k * 4 : 0, "shared_logit"}};
+  if ((st = check_alias(outs, 1, ins, 4))) return st;
+  return hip_status(sdv::combine_sliced_launch(partial, idx, w, shared_logit, sdv::expert_slices(I), k, topk, H,
+                                               has_shared, y, (hipStream_t)stream),
+                    "sdv_moe_combine_sliced_k launch");
 }
 
 int sdv_moe_combine_k(const float* partial, const float* w, const float* shared_out,

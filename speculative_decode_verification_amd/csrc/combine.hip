@@ -2,7 +2,9 @@
 // slot order, plus the sigmoid-gated shared expert (Red Lite dev45, "What it
 // is": one tail for both rows; Flash-Next plan "5.3 MoE deltas": fixed-width
 // weighted expert sums).  Each output is summed by one thread in slot order,
-// so a row's result is independent of k.
+// so a row's result is independent of k.  The sliced form reads the fused
+// expert kernel's per-slice partial outputs and adds a slot's slices in slice
+// order before weighting it.
 
 #include "common.h"
 
@@ -44,7 +46,79 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   *reinterpret_cast<float4*>(a.y + (size_t)r * a.H + n4) = acc;
 }
 
+struct SlicedArgs {
+  const float* partial;  // [S][k][topk + 1][H]
+  const int32_t* idx;    // [k][topk]
+  const float* w;        // [k][topk]
+  const float* shared_logit;
+  int S, k, topk, H, has_shared;
+  float* y;
+};
+
+// Slot (r, s) contributes w[r][s] * sum_j partial[j][r][s] (slices in order);
+// slots without an expert (idx < 0) contribute nothing.  One thread per
+// output element; the loads of a chunk of slots (all of their slices) are
+// issued before any of them is added, so a thread waits for memory once per
+// chunk rather than once per slot.
+template <int S>
+__global__ __launch_bounds__(256) void combine_sliced_kernel(SlicedArgs a) {
+  constexpr int kChunk = S <= 4 ? 12 : (S <= 6 ? 8 : 6);  // slots per chunk (about 50 loads in flight)
+  const int r = blockIdx.y;
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= a.H) return;
+  const size_t slice_stride = (size_t)a.k * (a.topk + 1) * a.H;
+  const float* pr = a.partial + (size_t)r * (a.topk + 1) * a.H + n;
+  const int nslots = a.topk + (a.has_shared ? 1 : 0);
+  float acc = 0.0f;
+  for (int s0 = 0; s0 < nslots; s0 += kChunk) {
+    float v[kChunk][S];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int s = min(s0 + c, nslots - 1);  // past the last slot: a harmless re-read
+#pragma unroll
+      for (int j = 0; j < S; ++j) v[c][j] = pr[j * slice_stride + (size_t)s * a.H];
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int s = s0 + c;
+      if (s >= nslots) break;
+      float ws;
+      if (s < a.topk) {
+        if (a.idx[r * a.topk + s] < 0) continue;
+        ws = a.w[r * a.topk + s];
+      } else {
+        ws = a.shared_logit ? sigmoidf_(a.shared_logit[r]) : 1.0f;
+      }
+      float p = v[c][0];
+#pragma unroll
+      for (int j = 1; j < S; ++j) p = p + v[c][j];
+      acc = fmaf(ws, p, acc);
+    }
+  }
+  a.y[(size_t)r * a.H + n] = acc;
+}
+
 }  // namespace
+
+hipError_t combine_sliced_launch(const float* partial, const int32_t* idx, const float* w,
+                                 const float* shared_logit, int S, int k, int topk, int H, int has_shared,
+                                 float* y, hipStream_t st) {
+  SlicedArgs a{partial, idx, w, shared_logit, S, k, topk, H, has_shared, y};
+  const int threads = 256;
+  const dim3 grid((H + threads - 1) / threads, k);
+  switch (S) {
+    case 1: hipLaunchKernelGGL(combine_sliced_kernel<1>, grid, dim3(threads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(combine_sliced_kernel<2>, grid, dim3(threads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(combine_sliced_kernel<3>, grid, dim3(threads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(combine_sliced_kernel<4>, grid, dim3(threads), 0, st, a); break;
+    case 5: hipLaunchKernelGGL(combine_sliced_kernel<5>, grid, dim3(threads), 0, st, a); break;
+    case 6: hipLaunchKernelGGL(combine_sliced_kernel<6>, grid, dim3(threads), 0, st, a); break;
+    case 7: hipLaunchKernelGGL(combine_sliced_kernel<7>, grid, dim3(threads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(combine_sliced_kernel<8>, grid, dim3(threads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t combine_launch(const float* partial, const float* w, const float* shared_out,
                           const float* shared_logit, int k, int topk, int H, float* y,

@@ -1,0 +1,239 @@
+// Device helpers of the affine-Q4 products (gfx950): code decode, the
+// activation staging in MFMA slot order and the per-group MFMA step with its
+// scale/bias epilogue.  Layout conventions of v_mfma_f32_32x32x16_bf16:
+//   A: lane l holds row l%32, K slots 8*(l/32) .. +7 (8 bf16)
+//   B: lane l holds col l%32, the same K slots
+//   D: lane l, register v holds row 8*(v/4) + 4*(l/32) + v%4, col l%32
+// A code q decodes to the bf16 value 128 + q; decoding a 32-bit word gives the
+// bf16 pairs (n0,n4) (n1,n5) (n2,n6) (n3,n7), so K slot i holds nibble NU[i]
+// with NU = {0,4,1,5,2,6,3,7}, and activations are staged in that order.
+// fp32 activations are split into three bf16 parts; part p of row i is MFMA
+// row i + 8p for i < 8 and 24 + p for i = 8.
+#pragma once
+
+#include "common.h"
+
+namespace sdv {
+namespace q4 {
+
+__device__ __forceinline__ uint32_t dec_pair(uint32_t w, int sh) {
+  return ((w >> sh) & 0x000F000Fu) | 0x43004300u;
+}
+
+__device__ __forceinline__ bf16x8 decode_word(uint32_t w) {
+  uint32_t p[4] = {dec_pair(w, 0), dec_pair(w, 4), dec_pair(w, 8), dec_pair(w, 12)};
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(p));
+}
+
+// Permute 8 bf16 values (natural K order in e[0..7]) into slot order NU.
+__device__ __forceinline__ uint4 nu_pack(const uint32_t e[8]) {
+  uint4 r;
+  r.x = e[0] | (e[4] << 16);
+  r.y = e[1] | (e[5] << 16);
+  r.z = e[2] | (e[6] << 16);
+  r.w = e[3] | (e[7] << 16);
+  return r;
+}
+
+// MFMA row of part p of activation row i.
+template <int ACT>
+__device__ __forceinline__ int vrow_of(int i, int p) {
+  if (ACT == SDV_ACT_BF16) return i;
+  return i < 8 ? i + 8 * p : 24 + p;
+}
+
+// Register of the D layout holding MFMA row vr (for the lane half (vr/4)%2).
+__device__ __forceinline__ int reg_of(int vr) { return 4 * (vr >> 3) + (vr & 3); }
+
+// Sum over the 8 lanes l .. l+7 (l a multiple of 8); every lane of the group
+// ends with the same total (xor pairing adds the same two operands in both
+// lanes of a pair).
+__device__ __forceinline__ float sum8(float x) {
+  x = x + __shfl_xor(x, 1);
+  x = x + __shfl_xor(x, 2);
+  x = x + __shfl_xor(x, 4);
+  return x;
+}
+
+// Stage the unit's activation rows into LDS (NU order, bf16 parts) and their
+// per-group sums (indexed by MFMA row).  One task = (row, 8-element block):
+// the block's elements are summed in order, then the 8 blocks of a group are
+// summed by the fixed 8-lane pairing above.
+//   act       rows of K elements (bf16 bits or fp32), row s_src[i] feeds row i
+//   slot_cap  LDS row of the all-zero row (rows past the data read it)
+template <int ACT>
+__device__ __forceinline__ void stage_rows(const void* act, int K, int slot_cap, int nrows, uint16_t* xs,
+                                           float* xsum, int rs, const int* s_src) {
+  const int G = K >> 6, nb = K >> 3;
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+  for (int t = tid; t < 32 * G; t += nthreads) xsum[t] = 0.0f;
+  uint32_t* zrow = reinterpret_cast<uint32_t*>(xs + (size_t)slot_cap * rs);
+  for (int t = tid; t < rs / 2; t += nthreads) zrow[t] = 0u;
+  __syncthreads();
+  // nthreads is a multiple of 64, so the 8 tasks of a group share one 8-lane set
+  for (int task = tid; task < nrows * nb; task += nthreads) {
+    const int i = task / nb, b8 = task - i * nb;
+    const int src = s_src[i];
+    const bool ok = src >= 0;
+    const size_t src_row = ok ? (size_t)src : 0;
+    if (ACT == SDV_ACT_BF16) {
+      const uint4 v = ok ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(act) + src_row * K)[b8]
+                         : make_uint4(0, 0, 0, 0);
+      const uint32_t e8[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                              v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc = acc + bf16_bits_to_f32(e8[c]);
+      *reinterpret_cast<uint4*>(xs + (size_t)i * rs + b8 * 8) = nu_pack(e8);
+      acc = sum8(acc);
+      if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, 0) * G + (b8 >> 3)] = acc;
+    } else {
+      const float4* sp = reinterpret_cast<const float4*>(static_cast<const float*>(act) + src_row * K) + 2 * b8;
+      const float4 v0 = ok ? sp[0] : make_float4(0, 0, 0, 0);
+      const float4 v1 = ok ? sp[1] : make_float4(0, 0, 0, 0);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t hi[8], mi[8], lo[8];
+      float acc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        hi[c] = f32_to_bf16_rne(f[c]);
+        const float r1 = f[c] - bf16_bits_to_f32(hi[c]);
+        mi[c] = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_bits_to_f32(mi[c]);
+        lo[c] = f32_to_bf16_rne(r2);
+        acc[0] = acc[0] + bf16_bits_to_f32(hi[c]);
+        acc[1] = acc[1] + bf16_bits_to_f32(mi[c]);
+        acc[2] = acc[2] + bf16_bits_to_f32(lo[c]);
+      }
+      *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 0) * rs + b8 * 8) = nu_pack(hi);
+      *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 1) * rs + b8 * 8) = nu_pack(mi);
+      *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 2) * rs + b8 * 8) = nu_pack(lo);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const float t = sum8(acc[p]);
+        if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, p) * G + (b8 >> 3)] = t;
+      }
+    }
+  }
+}
+
+// LDS slot of the activation data for MFMA row `arow` (or -1 if unused).
+template <int ACT>
+__device__ __forceinline__ int slot_of_arow(int arow, int nrows) {
+  if (ACT == SDV_ACT_BF16) return arow < nrows ? arow : -1;
+  if (arow < 24) {
+    const int i = arow & 7, p = arow >> 3;
+    return i < nrows ? 3 * i + p : -1;
+  }
+  const int p = arow - 24;
+  return (nrows == 9 && p < 3) ? 24 + p : -1;
+}
+
+// One 64-element group: 4 MFMA steps, then the group's scale/bias epilogue
+// into yacc for the first `nquads` register quads.  `ap` points at this
+// lane's activation row (or at an all-zero LDS row), so the four A reads are
+// issued together, unconditionally, before the decode.
+__device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xs_g,
+                                          int G, int half, int nquads, float yacc[16]) {
+  uint4 av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 8);
+  const float s = __uint_as_float(sbw << 16);
+  const float b = __uint_as_float(sbw & 0xFFFF0000u);
+  const float c = fmaf(-128.0f, s, b);
+  f32x16 acc = {};
+  const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j]), acc,
+                                                  0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < nquads) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * q + r;
+        const float xg = xs_g[(8 * q + 4 * half + r) * G];
+        yacc[v] = fmaf(s, acc[v], yacc[v]);
+        yacc[v] = fmaf(c, xg, yacc[v]);
+      }
+    }
+  }
+}
+
+// The same group step with the parts of each activation row summed right after
+// the matrix product, so a lane keeps five accumulators: y[i] for row
+// 4*half + i (i < 4) and y[4] for row 8 (meaningful in half 0).  xr_g[row * G]
+// is the row's group sum (for fp32 rows, of all three parts).  Per group,
+//   y += s * P + (b - 128 s) * X,   P = the row's parts' products summed in part order.
+template <int ACT>
+__device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xr_g,
+                                               int G, int half, float y[5]) {
+  uint4 av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 8);
+  const float s = __uint_as_float(sbw << 16);
+  const float b = __uint_as_float(sbw & 0xFFFF0000u);
+  const float c = fmaf(-128.0f, s, b);
+  f32x16 acc = {};
+  const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j]), acc,
+                                                  0, 0, 0);
+  float t[5];
+  if (ACT == SDV_ACT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[i] = acc[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = (acc[i] + acc[4 + i]) + acc[8 + i];
+    t[4] = (acc[12] + acc[13]) + acc[14];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[i] = fmaf(s, t[i], y[i]);
+    y[i] = fmaf(c, xr_g[(4 * half + i) * G], y[i]);
+  }
+  y[4] = fmaf(s, t[4], y[4]);
+  y[4] = fmaf(c, xr_g[8 * G], y[4]);
+}
+
+// Row r's value from group_mac_rows accumulators (valid in half (r / 4) % 2
+// for r < 8, in half 0 for r = 8).
+__device__ __forceinline__ float rows_value(const float y[5], int r) { return r < 8 ? y[r & 3] : y[4]; }
+
+__device__ __forceinline__ int rows_half(int r) { return r < 8 ? (r >> 2) & 1 : 0; }
+
+// Final value of activation row i from the wave's accumulators (valid in the
+// lanes of half (vrow/4)%2).
+template <int ACT>
+__device__ __forceinline__ float row_value(const float yacc[16], int i) {
+  if (ACT == SDV_ACT_BF16) {
+    const int v = reg_of(i);
+    float r = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t == v) r = yacc[t];
+    return r;
+  }
+  float p[3];
+#pragma unroll
+  for (int pp = 0; pp < 3; ++pp) {
+    const int v = reg_of(vrow_of<ACT>(i, pp));
+    float r = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t == v) r = yacc[t];
+    p[pp] = r;
+  }
+  return (p[0] + p[1]) + p[2];
+}
+
+template <int ACT>
+__device__ __forceinline__ int half_of_row(int i) {
+  return (vrow_of<ACT>(i, 0) >> 2) & 1;
+}
+
+}  // namespace q4
+}  // namespace sdv

@@ -211,6 +211,63 @@ def gather_qmv_k(bank, mode, act, route, k, topk, out=None, shared=None, shared_
     return out if shared is None else (out, shared_out)
 
 
+def expert_slices(I):
+    """Intermediate slices of the fused expert product (128 columns each)."""
+    return (I + 127) // 128
+
+
+def _experts_args(gate_up, down, x, route, k, topk, shared_gate_up, shared_down, partial):
+    kt = k * topk
+    dev = gate_up.device
+    H, I = gate_up.K, gate_up.N // 2
+    need = lib().sdv_moe_experts_partial_bytes(k, topk, H, I) // 4
+    return [gate_up.desc, down.desc, _need(x, "x", x.dtype, k * H, dev),
+            _need(route.union_ids, "union_ids", torch.int32, kt, dev),
+            _need(route.n_union, "n_union", torch.int32, 1, dev),
+            _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
+            _need(route.pair_row, "pair_row", torch.int32, kt, dev),
+            _need(route.pair_slot, "pair_slot", torch.int32, kt, dev), k, topk,
+            shared_gate_up.desc if shared_gate_up is not None else None,
+            shared_down.desc if shared_down is not None else None,
+            _need(partial, "partial", torch.float32, need, dev), _stream(partial)]
+
+
+def experts_partial(k, topk, H, I, device):
+    return torch.empty((expert_slices(I), k, topk + 1, H), dtype=torch.float32, device=device)
+
+
+def moe_experts_k(gate_up, down, x, route, k, topk, shared_gate_up=None, shared_down=None, partial=None):
+    """Fused gate/up + SwiGLU + down over the union in ``route`` (and the
+    shared expert, slot ``topk``).  Returns the per-slice partial outputs
+    fp32 [S, k, topk + 1, H]; their sum over S is each slot's expert output."""
+    H, I = gate_up.K, gate_up.N // 2
+    if partial is None:
+        partial = experts_partial(k, topk, H, I, gate_up.device)
+    check(lib().sdv_moe_experts_k(*_experts_args(gate_up, down, x, route, k, topk, shared_gate_up, shared_down,
+                                                 partial)))
+    return partial
+
+
+def _combine_sliced_args(partial, route, shared_logit, has_shared, I, out):
+    S, k, tp1, H = partial.shape
+    topk = tp1 - 1
+    dev = partial.device
+    pz = _need(shared_logit, "shared_logit", torch.float32, k, dev) if shared_logit is not None else None
+    return [_need(partial, "partial", torch.float32, S * k * tp1 * H, dev),
+            _need(route.idx, "idx", torch.int32, k * topk, dev), _need(route.w, "w", torch.float32, k * topk, dev),
+            pz, k, topk, H, I, int(bool(has_shared)), _need(out, "out", torch.float32, k * H, dev), _stream(out)]
+
+
+def moe_combine_sliced_k(partial, route, I, has_shared=False, shared_logit=None, out=None):
+    """y[r] = sum_s w[r, s] (sum_j partial[j, r, s]) over slots with an expert,
+    plus sigmoid(z_r) times the shared slot's sum when ``has_shared``."""
+    S, k, tp1, H = partial.shape
+    if out is None:
+        out = torch.empty((k, H), dtype=torch.float32, device=partial.device)
+    check(lib().sdv_moe_combine_sliced_k(*_combine_sliced_args(partial, route, shared_logit, has_shared, I, out)))
+    return out
+
+
 def moe_combine_k(partial, w, shared_out=None, shared_logit=None, out=None):
     """y[r] = sum_s w[r, s] partial[r, s] (slot order) + sigmoid(z_r) shared[r]."""
     k, topk, H = partial.shape
@@ -311,6 +368,15 @@ def bind_moe_route_k(logits, topk, score_mode, renorm, out):
 def bind_gather_qmv_k(bank, mode, act, route, k, topk, out, shared=None, shared_act=None, shared_out=None):
     return BoundCall("sdv_gather_qmv_k",
                      _gather_args(bank, mode, act, route, k, topk, out, shared, shared_act, shared_out))
+
+
+def bind_moe_experts_k(gate_up, down, x, route, k, topk, shared_gate_up, shared_down, partial):
+    return BoundCall("sdv_moe_experts_k",
+                     _experts_args(gate_up, down, x, route, k, topk, shared_gate_up, shared_down, partial))
+
+
+def bind_moe_combine_sliced_k(partial, route, I, has_shared, shared_logit, out):
+    return BoundCall("sdv_moe_combine_sliced_k", _combine_sliced_args(partial, route, shared_logit, has_shared, I, out))
 
 
 def bind_moe_combine_k(partial, w, shared_out, shared_logit, out):

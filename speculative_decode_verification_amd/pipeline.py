@@ -20,8 +20,9 @@ from ._lib import MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX
 
 class MoeLayer:
     def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None,
-                 fuse_shared=True):
+                 fuse_shared=True, fused_experts=True):
         self.gate_up, self.down = gate_up, down
+        self.fused_experts = fused_experts
         self.shared_gate_up, self.shared_down = shared_gate_up, shared_down
         self.fused_shared = (fuse_shared and shared_gate_up is not None and
                              (shared_gate_up.N, shared_gate_up.K) == (gate_up.N, gate_up.K) and
@@ -42,10 +43,21 @@ class MoeLayer:
             self.sh_out = torch.empty((k, self.H), dtype=torch.float32, device=dev)
         else:
             self.sh_h = self.sh_out = None
+        if fused_experts:
+            if shared_gate_up is not None and not self.fused_shared:
+                raise ValueError("the fused expert path needs the shared expert in the routed experts' geometry")
+            self.xpartial = ops.experts_partial(k, topk, self.H, self.I, dev)
 
     def bind(self, x, logits, z=None):
         """Marshal the layer's launches once for fixed input buffers; returns a
         list of (name, call) pairs to run in order."""
+        if self.fused_experts:
+            has = self.shared_gate_up is not None
+            return [("route", ops.bind_moe_route_k(logits, self.topk, self.score_mode, self.renorm, self.route)),
+                    ("experts", ops.bind_moe_experts_k(self.gate_up, self.down, x, self.route, self.k, self.topk,
+                                                       self.shared_gate_up, self.shared_down, self.xpartial)),
+                    ("combine", ops.bind_moe_combine_sliced_k(self.xpartial, self.route, self.I, has,
+                                                              z if has else None, self.y))]
         fs = self.fused_shared
         sg = dict(shared=self.shared_gate_up, shared_act=x, shared_out=self.sh_h) if fs else {}
         sd = dict(shared=self.shared_down, shared_act=self.sh_h, shared_out=self.sh_out) if fs else {}
@@ -64,6 +76,11 @@ class MoeLayer:
     def __call__(self, x, logits, z=None):
         """x: bf16 bits [k, H] (int16); logits fp32 [k, E]; z fp32 [k] or None."""
         ops.moe_route_k(logits, self.topk, self.score_mode, self.renorm, out=self.route)
+        if self.fused_experts:
+            has = self.shared_gate_up is not None
+            ops.moe_experts_k(self.gate_up, self.down, x, self.route, self.k, self.topk, self.shared_gate_up,
+                              self.shared_down, partial=self.xpartial)
+            return ops.moe_combine_sliced_k(self.xpartial, self.route, self.I, has, z if has else None, out=self.y)
         fs = self.fused_shared
         sg = dict(shared=self.shared_gate_up, shared_act=x, shared_out=self.sh_h) if fs else {}
         sd = dict(shared=self.shared_down, shared_act=self.sh_h, shared_out=self.sh_out) if fs else {}

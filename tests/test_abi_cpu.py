@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 16
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -166,6 +166,66 @@ def test_gather_shared_validation(lib):
     assert gather(lib, bank, **{**ok, "shared_out": P + 0x2000000 + 64}) == L.SDV_EALIAS  # over out
     assert gather(lib, bank, **{**ok, "shared_out": sh.codes}) == L.SDV_EALIAS
     assert "shared" in lib.sdv_last_error().decode()
+
+
+def experts(lib, gu, dn, k=2, topk=4, x=P + 0x3000000, partial=P + 0x4000000, sgu=None, sdn=None):
+    ptrs = [P + 0x800000 + 0x10000 * i for i in range(5)]
+    return lib.sdv_moe_experts_k(ctypes.byref(gu), ctypes.byref(dn), x, *ptrs, k, topk,
+                                 ctypes.byref(sgu) if sgu is not None else None,
+                                 ctypes.byref(sdn) if sdn is not None else None, partial, None)
+
+
+def test_experts_partial_bytes(lib):
+    # S = ceil(I / 128) slices of [k][topk + 1][H] fp32
+    assert lib.sdv_moe_experts_partial_bytes(9, 10, 2560, 640) == 5 * 9 * 11 * 2560 * 4
+    assert lib.sdv_moe_experts_partial_bytes(2, 4, 256, 192) == 2 * 2 * 5 * 256 * 4
+    assert lib.sdv_moe_experts_partial_bytes(10, 4, 256, 128) == 0
+    assert lib.sdv_moe_experts_partial_bytes(2, 4, 250, 128) == 0
+    assert lib.sdv_moe_experts_partial_bytes(2, 4, 256, 96) == 0
+
+
+def test_experts_validation(lib):
+    E, H, I = 8, 256, 128
+    gu = q4t(E=E, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000)
+    dn = q4t(E=E, N=H, K=I, fused=0, codes=P + 0x200000, sb=P + 0x300000)
+    assert experts(lib, gu, dn, k=10) == L.SDV_EWIDTH
+    assert experts(lib, gu, dn, topk=9) == L.SDV_ERANGE
+    assert experts(lib, q4t(E=E, N=2 * I, K=H, fused=0), dn) == L.SDV_ELAYOUT            # gate/up not fused
+    assert experts(lib, gu, q4t(E=E, N=H, K=I, fused=1, codes=P + 0x200000)) == L.SDV_ELAYOUT
+    assert experts(lib, gu, q4t(E=E, N=H + 32, K=I, codes=P + 0x200000, sb=P + 0x300000)) == L.SDV_ELAYOUT
+    assert experts(lib, gu, q4t(E=E - 1, N=H, K=I, codes=P + 0x200000, sb=P + 0x300000)) == L.SDV_ELAYOUT
+    gu96 = q4t(E=E, N=2 * 96, K=H, fused=1)
+    dn96 = q4t(E=E, N=H, K=96, codes=P + 0x200000, sb=P + 0x300000)
+    assert experts(lib, gu96, dn96) == L.SDV_ELAYOUT                                     # K=96 not a group multiple
+    assert experts(lib, gu, dn, x=0) == L.SDV_EINVAL
+    assert experts(lib, gu, dn, partial=P + 0x80) == L.SDV_EALIAS                        # over the gate/up codes
+    assert experts(lib, gu, dn, partial=P + 0x800000) == L.SDV_EALIAS                    # over union_ids
+    sgu = q4t(E=1, N=2 * I, K=H, fused=1, codes=P + 0x5000000, sb=P + 0x5100000)
+    sdn = q4t(E=1, N=H, K=I, codes=P + 0x5200000, sb=P + 0x5300000)
+    assert experts(lib, gu, dn, sgu=sgu) == L.SDV_EINVAL                                 # one of the pair
+    assert experts(lib, gu, dn, sgu=q4t(E=2, N=2 * I, K=H, fused=1), sdn=sdn) == L.SDV_EINVAL
+    assert experts(lib, gu, dn, sgu=q4t(E=1, N=2 * I, K=H, fused=0), sdn=sdn) == L.SDV_ELAYOUT
+    assert experts(lib, gu, dn, sgu=sgu, sdn=sdn, partial=P + 0x5000000 + 64) == L.SDV_EALIAS
+    # too much LDS: k = 9 rows of a very wide hidden size
+    wide = q4t(E=E, N=2 * I, K=16384, fused=1)
+    assert experts(lib, wide, q4t(E=E, N=16384, K=I, codes=P + 0x200000, sb=P + 0x300000), k=9) == L.SDV_ELAYOUT
+    assert "LDS" in lib.sdv_last_error().decode()
+    gu9 = q4t(E=E, N=2 * 1088, K=H, fused=1)
+    assert experts(lib, gu9, q4t(E=E, N=H, K=1088, codes=P + 0x2000000, sb=P + 0x3000000)) == L.SDV_ERANGE
+
+
+def test_combine_sliced_validation(lib):
+    f = lib.sdv_moe_combine_sliced_k
+    part, idx, w, y = P, P + 0x1000000, P + 0x1100000, P + 0x1200000
+    assert f(part, idx, w, None, 0, 4, 256, 128, 0, y, None) == L.SDV_EWIDTH
+    assert f(part, idx, w, None, 2, 17, 256, 128, 0, y, None) == L.SDV_ERANGE
+    assert f(part, idx, w, None, 2, 4, 250, 128, 0, y, None) == L.SDV_EINVAL
+    assert f(part, idx, w, None, 2, 4, 256, 100, 0, y, None) == L.SDV_EINVAL
+    assert f(part, idx, w, None, 2, 4, 256, 128, 2, y, None) == L.SDV_EINVAL
+    assert f(part, idx, w, None, 2, 4, 256, 1088, 0, y, None) == L.SDV_ERANGE              # 9 slices
+    assert f(part, idx, w, P + 0x1300000, 2, 4, 256, 128, 0, y, None) == L.SDV_EINVAL    # logit without shared slot
+    assert f(part, idx, w, None, 2, 4, 256, 128, 0, P + 0x100, None) == L.SDV_EALIAS
+    assert f(part, idx, w, None, 2, 4, 256, 128, 0, idx + 16, None) == L.SDV_EALIAS
 
 
 def test_combine_validation(lib):

@@ -83,12 +83,13 @@ def oracle_moe(gu, dn, inp, topk, mode, renorm, sgu=None, sdn=None):
                              shared_down=oracle.dequant(*sdn) if sdn is not None else None)
 
 
-def run_layer(ops, pipeline, gu, dn, inp, k, topk, mode, renorm, sgu=None, sdn=None, fuse_shared=True):
+def run_layer(ops, pipeline, gu, dn, inp, k, topk, mode, renorm, sgu=None, sdn=None, fuse_shared=True,
+              fused_experts=False):
     layer = pipeline.MoeLayer(q4_device_from_host(*gu).tiled(True), q4_device_from_host(*dn).tiled(), k, topk,
                               ops.ROUTE_SOFTMAX if mode == "softmax" else ops.ROUTE_SIGMOID, renorm,
                               q4_device_from_host(*sgu).tiled(True) if sgu is not None else None,
                               q4_device_from_host(*sdn).tiled() if sdn is not None else None,
-                              fuse_shared=fuse_shared)
+                              fuse_shared=fuse_shared, fused_experts=fused_experts)
     assert layer.fused_shared == (fuse_shared and sgu is not None)
     y = layer(sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV),
               sdev.upload_f32(inp["z"], DEV))
@@ -96,27 +97,103 @@ def run_layer(ops, pipeline, gu, dn, inp, k, topk, mode, renorm, sgu=None, sdn=N
     return layer, to_np(y)
 
 
-@pytest.mark.parametrize("shared,fuse", [(False, True), (True, True), (True, False)])
-def test_small_moe_matches_oracle_and_width1(shared, fuse):
+def slot_outputs(layer):
+    """Per-slot expert outputs of a fused-path layer: the slices of
+    sdv_moe_experts_k summed in slice order (fp32), [k, topk (+ 1), H]; the
+    shared slot only when the layer has a shared expert (else it is never
+    written)."""
+    xp = to_np(layer.xpartial)
+    if layer.shared_gate_up is None:
+        xp = xp[:, :, :layer.topk]
+    acc = xp[0].copy()
+    for j in range(1, xp.shape[0]):
+        acc = acc + xp[j]
+    return acc
+
+
+def check_layer_vs_oracle(layer, y, ref, k, topk, shared, label):
+    if layer.fused_experts:
+        P = slot_outputs(layer)
+        idx = to_np(layer.route.idx)
+        assert (idx >= 0).all()
+        assert_close(P[:, :topk], ref["partial"], f"{label} slot outputs")
+        if shared:
+            assert_close(P[:, topk], ref["shared"], f"{label} shared expert")
+    else:
+        assert_close(to_np(layer.h), ref["h"], f"{label} h")
+        assert_close(to_np(layer.partial), ref["partial"], f"{label} partial")
+        if shared:
+            assert_close(to_np(layer.sh_out), ref["shared"], f"{label} shared expert")
+    assert_close(y, ref["y"], f"{label} y")
+
+
+PATHS = [(False, True, False), (True, True, False), (True, False, False), (False, True, True), (True, True, True)]
+
+
+@pytest.mark.parametrize("shared,fuse,fused_experts", PATHS)
+def test_small_moe_matches_oracle_and_width1(shared, fuse, fused_experts):
     ops, pipeline = _mods()
     k, topk = 9, 4
     gu, dn, inp, sgu, sdn = small_moe(k, shared=shared)
-    banner(f"small moe shared={shared} fused={fuse}")
-    layer, y = run_layer(ops, pipeline, gu, dn, inp, k, topk, "softmax", False, sgu, sdn, fuse)
+    banner(f"small moe shared={shared} fused_shared={fuse} fused_experts={fused_experts}")
+    layer, y = run_layer(ops, pipeline, gu, dn, inp, k, topk, "softmax", False, sgu, sdn, fuse, fused_experts)
     ref = oracle_moe(gu, dn, inp, topk, "softmax", False, sgu, sdn)
     assert int(to_np(layer.route.n_union)[0]) == ref["n_union"]
-    assert_close(to_np(layer.h), ref["h"], "h")
-    assert_close(to_np(layer.partial), ref["partial"], "partial")
-    if shared:
-        assert_close(to_np(layer.sh_out), ref["shared"], "shared expert")
-    assert_close(y, ref["y"], "y")
-    h9, p9 = to_np(layer.h), to_np(layer.partial)
+    check_layer_vs_oracle(layer, y, ref, k, topk, shared, "small moe")
+    if fused_experts:
+        P9 = slot_outputs(layer)
+    else:
+        h9, p9 = to_np(layer.h), to_np(layer.partial)
     for r in range(k):
-        one = {n: (v[r:r + 1] if n != "z" else v[r:r + 1]) for n, v in inp.items()}
-        l1, y1 = run_layer(ops, pipeline, gu, dn, one, 1, topk, "softmax", False, sgu, sdn, fuse)
-        assert np.array_equal(to_np(l1.h)[0], h9[r]), f"h row {r}"
-        assert np.array_equal(to_np(l1.partial)[0], p9[r]), f"partial row {r}"
+        one = {n: v[r:r + 1] for n, v in inp.items()}
+        l1, y1 = run_layer(ops, pipeline, gu, dn, one, 1, topk, "softmax", False, sgu, sdn, fuse, fused_experts)
+        if fused_experts:
+            assert np.array_equal(slot_outputs(l1)[0], P9[r]), f"slot outputs row {r}"
+        else:
+            assert np.array_equal(to_np(l1.h)[0], h9[r]), f"h row {r}"
+            assert np.array_equal(to_np(l1.partial)[0], p9[r]), f"partial row {r}"
         assert np.array_equal(y1[0], y[r]), f"y row {r}"
+
+
+@pytest.mark.parametrize("E,H,I,topk,k,shared", [(16, 256, 192, 4, 9, True), (8, 192, 64, 2, 5, True),
+                                                 (32, 320, 384, 6, 7, False), (4, 128, 128, 4, 9, True),
+                                                 (64, 1024, 256, 8, 3, True), (16, 256, 128, 1, 1, False)])
+def test_fused_experts_shapes(E, H, I, topk, k, shared):
+    """Ragged geometry of the fused expert path: a 64-wide last slice, fewer
+    down tiles than waves, a hidden size that is not a multiple of 256, top-1
+    and one row, every expert in the union (topk = E)."""
+    ops, pipeline = _mods()
+    banner(f"fused experts E={E} H={H} I={I} topk={topk} k={k} shared={shared}")
+    cfg = 9
+    gu = q4_host(cfg, GATEUP, 1, E, 2 * I, H)
+    dn = q4_host(cfg, DOWN, 1, E, H, I)
+    inp = synth.moe_layer_inputs(cfg, 1, k, H, E)
+    sgu = synth.dense_weight(cfg, SHARED_GATEUP, 1, 2 * I, H) if shared else None
+    sdn = synth.dense_weight(cfg, SHARED_DOWN, 1, H, I) if shared else None
+    layer, y = run_layer(ops, pipeline, gu, dn, inp, k, topk, "sigmoid", True, sgu, sdn, True, True)
+    ref = oracle_moe(gu, dn, inp, topk, "sigmoid", True, sgu, sdn)
+    assert np.array_equal(to_np(layer.route.idx), ref["idx"])
+    check_layer_vs_oracle(layer, y, ref, k, topk, shared, "fused experts")
+    # the gathered path computes the same layer
+    _, y_g = run_layer(ops, pipeline, gu, dn, inp, k, topk, "sigmoid", True, sgu, sdn, True, False)
+    assert_close(y_g, ref["y"], "gathered path y")
+
+
+def test_fused_experts_unused_slots_untouched():
+    """Slices and slots the layer does not use are not written: a sentinel
+    in the shared slot survives a layer without a shared expert."""
+    ops, pipeline = _mods()
+    banner("fused experts sentinel")
+    k, topk = 3, 2
+    gu, dn, inp, _, _ = small_moe(k)
+    layer = pipeline.MoeLayer(q4_device_from_host(*gu).tiled(True), q4_device_from_host(*dn).tiled(), k, topk,
+                              ops.ROUTE_SOFTMAX, False, fused_experts=True)
+    layer.xpartial.fill_(12345.0)
+    layer(sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV))
+    torch.cuda.synchronize()
+    xp = to_np(layer.xpartial)
+    assert (xp[:, :, topk] == 12345.0).all()
+    assert not (xp[:, :, :topk] == 12345.0).any()
 
 
 def test_ornith_shaped_layer():
@@ -141,8 +218,11 @@ def test_ornith_shaped_layer():
     for k in (2, 5, 9):
         banner(f"ornith layer k={k}")
         inp = synth.moe_layer_inputs(cfg, layer_id, k, H, E)
-        layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SOFTMAX, False)
-        y = to_np(layer(sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV)))
+        layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SOFTMAX, False, fused_experts=False)
+        fused = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SOFTMAX, False, fused_experts=True)
+        args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV))
+        y = to_np(layer(*args))
+        y_f = to_np(fused(*args))
         idx, _ = oracle.route(inp["logits"], topk, "softmax", False)
         used = sorted(set(idx.ravel().tolist()))
         gmat = {e: oracle.dequant(*synth.q4_rows(gkeys, E, 2 * I, H, expert=e)) for e in used}
@@ -152,6 +232,8 @@ def test_ornith_shaped_layer():
         assert np.array_equal(to_np(layer.route.idx), ref["idx"])
         assert_close(to_np(layer.h), ref["h"], "h")
         assert_close(y, ref["y"], "y")
+        assert_close(slot_outputs(fused)[:, :topk], ref["partial"], "fused slot outputs")
+        assert_close(y_f, ref["y"], "fused y")
 
 
 def test_flash_next_shaped_layer():
@@ -169,15 +251,25 @@ def test_flash_next_shaped_layer():
     sgu = synth.dense_weight(cfg, SHARED_GATEUP, layer_id, 2 * I, H)
     sdn = synth.dense_weight(cfg, SHARED_DOWN, layer_id, H, I)
     sgu_w, sdn_w = q4_device_from_host(*sgu).tiled(True), q4_device_from_host(*sdn).tiled()
-    layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w)
+    layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w, fused_experts=False)
     assert layer.fused_shared
     inp = synth.moe_layer_inputs(cfg, layer_id, k, H, E)
     banner("flash-next layer k=9")
     args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV), sdev.upload_f32(inp["z"], DEV))
     y = to_np(layer(*args))
     # the same layer with the shared expert as two dense launches
-    split = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w, fuse_shared=False)
+    split = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w, fuse_shared=False,
+                              fused_experts=False)
     y_split = to_np(split(*args))
+    # the fused expert path (the step's hot path), marshalled once like the bench
+    fused = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SIGMOID, True, sgu_w, sdn_w)
+    assert fused.fused_experts
+    y_f = to_np(fused(*args))
+    fused.y.zero_()
+    for _, call in fused.bind(*args):
+        call()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(fused.y), y_f)
     # the bound (marshalled-once) launches give the fused layer's result bit for bit
     layer.y.zero_()
     for _, call in layer.bind(*args):
@@ -199,6 +291,10 @@ def test_flash_next_shaped_layer():
     assert_close(to_np(split.sh_out), ref["shared"], "shared expert (dense launches)")
     assert_close(y, ref["y"], "y")
     assert_close(y_split, ref["y"], "y (dense shared launches)")
+    P = slot_outputs(fused)
+    assert_close(P[:, :topk], ref["partial"], "fused slot outputs")
+    assert_close(P[:, topk], ref["shared"], "fused shared expert")
+    assert_close(y_f, ref["y"], "fused y")
 
 
 def test_combine_matches_oracle_order():
