@@ -23,6 +23,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -62,8 +63,10 @@ def q4_bytes(n, k):
 
 
 def kernel_source_hash():
+    """Hash of the dominant kernel's sources: a counter summary taken on other
+    sources no longer describes it."""
     h = hashlib.sha256()
-    for f in ("q4_matvec.hip", "common.h"):
+    for f in ("moe_experts.hip", "q4_core.h", "common.h"):
         with open(os.path.join(ROOT, "speculative_decode_verification_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -260,18 +263,27 @@ class Workload:
         return total
 
 
+TRAFFIC_SUMMARY = "traffic_moe_experts_flashnext_k9.md"
+
+
 def traffic_for(kernel_hash):
-    """Counter-measured HBM bytes per launch of the dominant kernel, if the
-    committed counter summary was taken on the current kernel source."""
-    path = os.path.join(PROFILE_DIR, "traffic_gather_gate_up_flashnext_k9.json")
+    """Counter-measured HBM bytes per launch of the dominant kernel, read from
+    the committed counter summary (lines ``kernel_source_hash: H`` and
+    ``hbm_bytes_per_launch: N``), or None if that summary was taken on other
+    kernel sources."""
+    path = os.path.join(PROFILE_DIR, TRAFFIC_SUMMARY)
+    rec = {}
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                m = re.match(r"^\s*[-*]?\s*`?(kernel_source_hash|hbm_bytes_per_launch)`?:\s*`?([0-9a-f]+)`?", line)
+                if m:
+                    rec[m.group(1)] = m.group(2)
+    except OSError:
         return None
-    if rec.get("kernel_source_hash") != kernel_hash:
+    if rec.get("kernel_source_hash") != kernel_hash or "hbm_bytes_per_launch" not in rec:
         return None
-    return rec.get("bytes_per_launch")
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(k=9):
