@@ -105,7 +105,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t by
 template <typename Issue>
 __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)[kRing], const uint32_t (&sbuf)[kRing],
                                         Issue& issue, const uint16_t* hs, const float* hrow, const int* s_dst,
-                                        int nrows, int j, int wave, int lane, int s_begin, int s_end) {
+                                        int nrows, int j, int wave, int lane, int s_begin, int s_end, DecodeK dk) {
   const int k = a.k, H = a.H;
   const int col = lane & 31, half = lane >> 5;
   const int rsB = kSlice + 8;
@@ -136,7 +136,7 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
 #pragma unroll
         for (int v = 0; v < 5; ++v) y[v] = 0.0f;
       }
-      group_mac_rows<SDV_ACT_F32>(cbuf[i], sbuf[i], ap + z + g * 64, hrow + z + g, 2, half, y);
+      group_mac_rows<SDV_ACT_F32>(cbuf[i], sbuf[i], ap + z + g * 64, hrow + z + g, 2, half, y, dk);
       issue(i, s0 + i + kRing);
       if (g == 1) {
         const int n = t * 32 + col;
@@ -263,6 +263,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): enter the stream with no load outstanding
 
+  const DecodeK dk = decode_k();
   // ---- phase A: one fused gate/up tile over all GA groups
   {
     const int slot = slot_of_arow<SDV_ACT_BF16>(col, nrows);
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = s0 + i;
-        if (s < nA) group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xsum + s, GA, half, y);
+        if (s < nA) group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xsum + s, GA, half, y, dk);
         issue(i, s + kRing);
       }
     }
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   __syncthreads();
 
   // ---- phase B: down tiles over the slice's groups
-  phase_b(a, cbuf, sbuf, issue, hs, hrow, s_dst, nrows, j, wave, lane, nA8, total);
+  phase_b(a, cbuf, sbuf, issue, hs, hrow, s_dst, nrows, j, wave, lane, nA8, total, dk);
 }
 
 }  // namespace

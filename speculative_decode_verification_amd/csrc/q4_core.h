@@ -16,12 +16,24 @@
 namespace sdv {
 namespace q4 {
 
-__device__ __forceinline__ uint32_t dec_pair(uint32_t w, int sh) {
-  return ((w >> sh) & 0x000F000Fu) | 0x43004300u;
+// The decode's mask and bf16 bias pattern, held in registers.  A gfx9 VOP3
+// instruction takes at most one literal, so with both constants as literals
+// the and-or of a pair becomes two instructions; from registers it is one
+// v_and_or_b32.  The empty asm makes the values opaque so they stay in VGPRs.
+struct DecodeK {
+  uint32_t mask, bias;
+};
+
+__device__ __forceinline__ DecodeK decode_k() {
+  DecodeK d{0x000F000Fu, 0x43004300u};
+  asm volatile("" : "+v"(d.mask), "+v"(d.bias));
+  return d;
 }
 
-__device__ __forceinline__ bf16x8 decode_word(uint32_t w) {
-  uint32_t p[4] = {dec_pair(w, 0), dec_pair(w, 4), dec_pair(w, 8), dec_pair(w, 12)};
+__device__ __forceinline__ uint32_t dec_pair(uint32_t w, int sh, DecodeK d) { return ((w >> sh) & d.mask) | d.bias; }
+
+__device__ __forceinline__ bf16x8 decode_word(uint32_t w, DecodeK d) {
+  uint32_t p[4] = {dec_pair(w, 0, d), dec_pair(w, 4, d), dec_pair(w, 8, d), dec_pair(w, 12, d)};
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(p));
 }
 
@@ -134,7 +146,7 @@ __device__ __forceinline__ int slot_of_arow(int arow, int nrows) {
 // lane's activation row (or at an all-zero LDS row), so the four A reads are
 // issued together, unconditionally, before the decode.
 __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xs_g,
-                                          int G, int half, int nquads, float yacc[16]) {
+                                          int G, int half, int nquads, float yacc[16], DecodeK dk) {
   uint4 av[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 8);
@@ -145,7 +157,7 @@ __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const ui
   const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j]), acc,
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j], dk), acc,
                                                   0, 0, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -168,7 +180,7 @@ __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const ui
 //   y += s * P + (b - 128 s) * X,   P = the row's parts' products summed in part order.
 template <int ACT>
 __device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xr_g,
-                                               int G, int half, float y[5]) {
+                                               int G, int half, float y[5], DecodeK dk) {
   uint4 av[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 8);
@@ -179,7 +191,7 @@ __device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, con
   const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j]), acc,
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j], dk), acc,
                                                   0, 0, 0);
   float t[5];
   if (ACT == SDV_ACT_BF16) {

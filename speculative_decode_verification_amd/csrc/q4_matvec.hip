@@ -214,6 +214,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   const uint16_t* arow_ptr = xs + (size_t)(slot >= 0 ? slot : a.slot_cap) * rs + half * 32;
 
   float yacc[16];
+  const DecodeK dk = decode_k();
   int cur_g = gb, cur_tl = 0;
   const int tiles_per_wave = KSPLIT ? 1 : (a.tiles_per_block + nw - 1) / nw;
   // One (tile, group) step: consume ring slot i, refill it (if asked) after
@@ -223,7 +224,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
 #pragma unroll
       for (int v = 0; v < 16; ++v) yacc[v] = 0.0f;
     }
-    group_mac(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc);
+    group_mac(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc, dk);
     if (refill) issue(i);
     if (++cur_g == ge) {
       if (!KSPLIT) {
