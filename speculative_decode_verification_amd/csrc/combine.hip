@@ -56,44 +56,54 @@ struct SlicedArgs {
 };
 
 // Slot (r, s) contributes w[r][s] * sum_j partial[j][r][s] (slices in order);
-// slots without an expert (idx < 0) contribute nothing.  One thread per
-// output element; the loads of a chunk of slots (all of their slices) are
-// issued before any of them is added, so a thread waits for memory once per
-// chunk rather than once per slot.
+// slots without an expert (idx < 0) contribute nothing.  A workgroup takes 64
+// output columns of one row in two stages: its four waves first add the
+// slices of every slot (wave q takes slots q, q + 4, ...; all of a thread's
+// loads are issued before any is added) into LDS, then one wave runs the
+// slot-ordered fused multiply-add chain for each column.  The chain is the
+// same for every row count, so a row's result does not depend on k.
+constexpr int kSlotsMax = SDV_MAX_TOPK + 1;
+constexpr int kSlotGroups = 4;
+constexpr int kSlotsPerThread = (kSlotsMax + kSlotGroups - 1) / kSlotGroups;
+
 template <int S>
 __global__ __launch_bounds__(256) void combine_sliced_kernel(SlicedArgs a) {
-  constexpr int kChunk = S <= 4 ? 12 : (S <= 6 ? 8 : 6);  // slots per chunk (about 50 loads in flight)
+  __shared__ float s_p[kSlotsMax][64];
   const int r = blockIdx.y;
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= a.H) return;
+  const int col = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int n = min(blockIdx.x * 64 + col, a.H - 1);  // columns past H re-read the last one
   const size_t slice_stride = (size_t)a.k * (a.topk + 1) * a.H;
   const float* pr = a.partial + (size_t)r * (a.topk + 1) * a.H + n;
   const int nslots = a.topk + (a.has_shared ? 1 : 0);
-  float acc = 0.0f;
-  for (int s0 = 0; s0 < nslots; s0 += kChunk) {
-    float v[kChunk][S];
+  float v[kSlotsPerThread][S];
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int s = min(s0 + c, nslots - 1);  // past the last slot: a harmless re-read
+  for (int c = 0; c < kSlotsPerThread; ++c) {
+    const int s = min(q + kSlotGroups * c, nslots - 1);  // past the last slot: a harmless re-read
 #pragma unroll
-      for (int j = 0; j < S; ++j) v[c][j] = pr[j * slice_stride + (size_t)s * a.H];
-    }
+    for (int j = 0; j < S; ++j) v[c][j] = pr[j * slice_stride + (size_t)s * a.H];
+  }
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int s = s0 + c;
-      if (s >= nslots) break;
-      float ws;
-      if (s < a.topk) {
-        if (a.idx[r * a.topk + s] < 0) continue;
-        ws = a.w[r * a.topk + s];
-      } else {
-        ws = a.shared_logit ? sigmoidf_(a.shared_logit[r]) : 1.0f;
-      }
+  for (int c = 0; c < kSlotsPerThread; ++c) {
+    const int s = q + kSlotGroups * c;
+    if (s < nslots) {
       float p = v[c][0];
 #pragma unroll
       for (int j = 1; j < S; ++j) p = p + v[c][j];
-      acc = fmaf(ws, p, acc);
+      s_p[s][col] = p;
     }
+  }
+  __syncthreads();
+  if (q != 0 || blockIdx.x * 64 + col >= a.H) return;
+  float acc = 0.0f;
+  for (int s = 0; s < nslots; ++s) {
+    float ws;
+    if (s < a.topk) {
+      if (a.idx[r * a.topk + s] < 0) continue;
+      ws = a.w[r * a.topk + s];
+    } else {
+      ws = a.shared_logit ? sigmoidf_(a.shared_logit[r]) : 1.0f;
+    }
+    acc = fmaf(ws, s_p[s][col], acc);
   }
   a.y[(size_t)r * a.H + n] = acc;
 }
@@ -105,7 +115,7 @@ hipError_t combine_sliced_launch(const float* partial, const int32_t* idx, const
                                  float* y, hipStream_t st) {
   SlicedArgs a{partial, idx, w, shared_logit, S, k, topk, H, has_shared, y};
   const int threads = 256;
-  const dim3 grid((H + threads - 1) / threads, k);
+  const dim3 grid((H + 63) / 64, k);
   switch (S) {
     case 1: hipLaunchKernelGGL(combine_sliced_kernel<1>, grid, dim3(threads), 0, st, a); break;
     case 2: hipLaunchKernelGGL(combine_sliced_kernel<2>, grid, dim3(threads), 0, st, a); break;

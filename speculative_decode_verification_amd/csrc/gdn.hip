@@ -58,32 +58,60 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   const int i = active ? (int)(row - (long)h * a.Dv) : 0;
   const int c = h / (a.Hv / a.Hk);
 
+  // Every load is issued before any is used: first the per-row vectors of
+  // the staging (at most two float4 of k and of q, one v and one g, beta per
+  // thread), then the state.  Loads complete in issue order, so the LDS
+  // writes wait only for the staging loads and overlap the state's arrival.
+  static_assert(kRowsPerBlock * 16 == 256, "staging assumes 256 threads");
   float4 S[NV4];
-  if (active) {
-    const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + row * DK);
+  constexpr int KQ_PER_THREAD = (SDV_MAX_ROWS * DK / 4 + 255) / 256;
+  float4 ck[KQ_PER_THREAD], cq[KQ_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < KQ_PER_THREAD; ++u) ck[u] = cq[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float cv = 0.0f, cg = 0.0f, cb = 0.0f;
+  const long row0 = (long)blockIdx.x * kRowsPerBlock;
+  const int h0 = (int)(row0 / a.Dv);
+  const int i0 = (int)(row0 - (long)h0 * a.Dv);
+  const int c0 = h0 / (a.Hv / a.Hk);
+  const int n4 = a.k * DK / 4;
+  if (LDS_KQ) {
+    // every row of the block is in head h0 (and qk head c0).  The loads are
+    // unconditional (indices past the data are clamped and the values
+    // discarded), so the compiler can count them exactly in its waits.
+#pragma unroll
+    for (int u = 0; u < KQ_PER_THREAD; ++u) {
+      const int t = min((int)threadIdx.x + 256 * u, n4 - 1);
+      const int tt = t / (DK / 4), jj = t - tt * (DK / 4);
+      ck[u] = reinterpret_cast<const float4*>(a.kk + ((long)tt * a.Hk + c0) * DK)[jj];
+      cq[u] = reinterpret_cast<const float4*>(a.q + ((long)tt * a.Hk + c0) * DK)[jj];
+    }
+    const int tv = min((int)threadIdx.x, a.k * kRowsPerBlock - 1);
+    const int tt = tv / kRowsPerBlock, r = min(tv - tt * kRowsPerBlock, (int)(nrows - 1 - row0));
+    cv = a.v[((long)tt * a.Hv + h0) * a.Dv + i0 + r];
+    const int tg = min((int)threadIdx.x, a.k - 1);
+    cg = a.g[tg * a.Hv + h0];
+    cb = a.beta[tg * a.Hv + h0];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the staging loads ahead of the state loads
+  {
+    const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + (active ? row : nrows - 1) * DK);
 #pragma unroll
     for (int j = 0; j < NV4; ++j) S[j] = sin4[sub + 16 * j];
   }
-
+  __builtin_amdgcn_sched_barrier(0);
   if (LDS_KQ) {
-    // every row of the block is in head h0 (and qk head c0)
-    const long row0 = (long)blockIdx.x * kRowsPerBlock;
-    const int h0 = (int)(row0 / a.Dv);
-    const int i0 = (int)(row0 - (long)h0 * a.Dv);
-    const int c0 = h0 / (a.Hv / a.Hk);
-    const int n4 = a.k * DK / 4;
-    for (int t = threadIdx.x; t < n4; t += blockDim.x) {
-      const int tt = t / (DK / 4), jj = t - tt * (DK / 4);
-      s_k[t] = reinterpret_cast<const float4*>(a.kk + ((long)tt * a.Hk + c0) * DK)[jj];
-      s_q[t] = reinterpret_cast<const float4*>(a.q + ((long)tt * a.Hk + c0) * DK)[jj];
+#pragma unroll
+    for (int u = 0; u < KQ_PER_THREAD; ++u) {
+      const int t = threadIdx.x + 256 * u;
+      if (t < n4) {
+        s_k[t] = ck[u];
+        s_q[t] = cq[u];
+      }
     }
-    for (int t = threadIdx.x; t < a.k * kRowsPerBlock; t += blockDim.x) {
-      const int tt = t / kRowsPerBlock, r = t - tt * kRowsPerBlock;
-      s_v[t] = (row0 + r < nrows) ? a.v[((long)tt * a.Hv + h0) * a.Dv + i0 + r] : 0.0f;
-    }
+    if (threadIdx.x < a.k * kRowsPerBlock) s_v[threadIdx.x] = (row0 + threadIdx.x % kRowsPerBlock < nrows) ? cv : 0.0f;
     if (threadIdx.x < a.k) {
-      s_g[threadIdx.x] = a.g[threadIdx.x * a.Hv + h0];
-      s_b[threadIdx.x] = a.beta[threadIdx.x * a.Hv + h0];
+      s_g[threadIdx.x] = cg;
+      s_b[threadIdx.x] = cb;
     }
     __syncthreads();
   }

@@ -80,6 +80,27 @@ __device__ __forceinline__ uint64_t wave_max(uint64_t k) {
   return best;
 }
 
+// DPP move with zero fill: lanes whose source is outside the row (or whose
+// row is masked off) read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int32_t dpp_or_zero(int32_t x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 within each 16-lane row, then row 0's total into row 1 and row
+// 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2-3
+// (row_bcast:31).  Integer adds, so the order does not matter.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Wave r < k selects row r's top-k: each lane holds PL candidates (expert
 // lane + 64 j); a round takes the wave's largest key and clears it.
 template <int PL>
@@ -110,10 +131,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     uint64_t mine = 0;  // lane s keeps slot s's key
     for (int s = 0; s < topk; ++s) {
-      uint64_t m = key[0];
+      // the lane's largest key by a pairwise tree (depth log2 PL)
+      uint64_t t[PL];
 #pragma unroll
-      for (int j = 1; j < PL; ++j) m = key[j] > m ? key[j] : m;
-      const uint64_t win = wave_max(m);
+      for (int j = 0; j < PL; ++j) t[j] = key[j];
+#pragma unroll
+      for (int w = PL / 2; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int j = 0; j < w; ++j) t[j] = t[j + w] > t[j] ? t[j + w] : t[j];
+      }
+      const uint64_t win = wave_max(t[0]);
 #pragma unroll
       for (int j = 0; j < PL; ++j) key[j] = key[j] == win ? 0ull : key[j];
       mine = lane == s ? win : mine;
@@ -165,12 +192,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   // counts the distinct experts below e, the low half the pairs below e
   int32_t packed = 0;
   if (tid < E) packed = (s_cnt[tid] > 0 ? (1 << 16) : 0) | s_cnt[tid];
-  int32_t incl = packed;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int32_t incl = wave_incl_scan(packed);
   if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
   int32_t base = 0;
