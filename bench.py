@@ -286,12 +286,13 @@ def traffic_for(kernel_hash):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(k=9):
-    """The CPU oracle on a bounded sample of the same workload: one MoE layer
-    (route, union, gate/up, down, shared expert, combine; its union experts
-    regenerated on the host before timing) and one GDN layer, scaled to the
-    48 MoE + 36 GDN layers of a step."""
-    import numpy as np
+def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
+    """The CPU oracle on a bounded sample of the same workload: whole layers
+    (MoE: route, union, gate/up, down, shared expert, combine, with the layer's
+    union experts regenerated on the host before timing; GDN: the k-row
+    recurrence with snapshots), layer by layer until at least ``min_seconds``
+    of oracle time or ``max_layers`` layers, then scaled to the 48 MoE + 36 GDN
+    layers of a step."""
     import oracle
     import synth
     from synth import configs
@@ -300,36 +301,81 @@ def cpu_baseline(k=9):
     cfg = configs.C4
     m, gs = cfg.moe, cfg.gdn
     E, H, I, topk = m.experts, m.hidden, m.inter, m.topk
-    l = 0
-    inp = synth.moe_layer_inputs(cfg.cid, l, k, H, E)
-    idx, _ = oracle.route(inp["logits"], topk, m.mode, m.renorm)
-    used = sorted(set(idx.ravel().tolist()))
-    gk, dk = synth.bank_keys(cfg.cid, GATEUP, l), synth.bank_keys(cfg.cid, DOWN, l)
-    packed_g = {e: synth.q4_rows(gk, E, 2 * I, H, expert=e) for e in used}
-    packed_d = {e: synth.q4_rows(dk, E, H, I, expert=e) for e in used}
-    sgu = synth.dense_weight(cfg.cid, SHARED_GATEUP, l, 2 * I, H)
-    sdn = synth.dense_weight(cfg.cid, SHARED_DOWN, l, H, I)
-    S = synth.gdn_state(cfg.cid, cfg.gdn_layers[0], gs.hv, gs.dv, gs.dk)
-    gi = synth.gdn_layer_inputs(cfg.cid, cfg.gdn_layers[0], k, gs.hv, gs.hk, gs.dk, gs.dv)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], lambda e: oracle.dequant(*packed_g[e]),
-                      lambda e: oracle.dequant(*packed_d[e]), topk, m.mode, m.renorm, z=inp["z"],
-                      shared_gate_up=oracle.dequant(*sgu), shared_down=oracle.dequant(*sdn))
-    t_moe = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.gdn_verify(S, gi["q"], gi["k"], gi["v"], gi["g"], gi["beta"])
-    t_gdn = time.perf_counter() - t0
-    step = cfg.layers * t_moe + len(cfg.gdn_layers) * t_gdn
+    t_moe, t_gdn, n_moe, n_gdn, unions = 0.0, 0.0, 0, 0, []
+    for l in range(min(max_layers, cfg.layers)):
+        inp = synth.moe_layer_inputs(cfg.cid, l, k, H, E)
+        idx, _ = oracle.route(inp["logits"], topk, m.mode, m.renorm)
+        used = sorted(set(idx.ravel().tolist()))
+        gk, dk = synth.bank_keys(cfg.cid, GATEUP, l), synth.bank_keys(cfg.cid, DOWN, l)
+        packed_g = {e: synth.q4_rows(gk, E, 2 * I, H, expert=e) for e in used}
+        packed_d = {e: synth.q4_rows(dk, E, H, I, expert=e) for e in used}
+        sgu = synth.dense_weight(cfg.cid, SHARED_GATEUP, l, 2 * I, H)
+        sdn = synth.dense_weight(cfg.cid, SHARED_DOWN, l, H, I)
+        t0 = time.perf_counter()
+        oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], lambda e: oracle.dequant(*packed_g[e]),
+                          lambda e: oracle.dequant(*packed_d[e]), topk, m.mode, m.renorm, z=inp["z"],
+                          shared_gate_up=oracle.dequant(*sgu), shared_down=oracle.dequant(*sdn))
+        t_moe += time.perf_counter() - t0
+        n_moe += 1
+        unions.append(len(used))
+        if l in cfg.gdn_layers:
+            S = synth.gdn_state(cfg.cid, l, gs.hv, gs.dv, gs.dk)
+            gi = synth.gdn_layer_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
+            t0 = time.perf_counter()
+            oracle.gdn_verify(S, gi["q"], gi["k"], gi["v"], gi["g"], gi["beta"])
+            t_gdn += time.perf_counter() - t0
+            n_gdn += 1
+        if t_moe + t_gdn >= min_seconds:
+            break
+    step = cfg.layers * t_moe / n_moe + len(cfg.gdn_layers) * t_gdn / n_gdn
     return {"value": k / step, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": (f"flashnext_k9 layer 0: one MoE layer ({len(used)} union experts, {t_moe:.2f} s) and "
-                       f"one GDN layer ({t_gdn:.3f} s) of the oracle (numpy fp64), scaled to 48 MoE + 36 GDN "
-                       f"layers per step ({step:.1f} s per 9-row step)"),
+            "sample": (f"flashnext_k9 layers 0..{n_moe - 1}: {n_moe} MoE layers (union experts {unions}, "
+                       f"{t_moe:.1f} s) and {n_gdn} GDN layers ({t_gdn:.2f} s) of the oracle (numpy fp64, "
+                       f"{t_moe + t_gdn:.1f} s in all), scaled to 48 MoE + 36 GDN layers per step "
+                       f"({step:.1f} s per 9-row step)"),
             "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
+
+
+def dense_projection(dev, timer, n_weights=64, reps=4):
+    """sdv_qmv_k on the dense 5120 x 5120 shape: 64 distinct weights (944 MB,
+    more than the last-level cache) launched back to back at each width, timed
+    with HIP events around each width's launches.  Reported per projection:
+    time and algorithmic GB/s (weights, activations and outputs once)."""
+    import torch
+    import synth
+    from synth import device as sdev
+    from synth.inputs import DENSE_W
+    from speculative_decode_verification_amd import ops
+    N = K = 5120
+    Ws = [ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(1, DENSE_W, l), 1, N, K, dev)).tiled()
+          for l in range(n_weights)]
+    x = sdev.upload_bf16(synth.activations(1, 0, 9, K), dev)
+    out = {}
+    for k in (1, 4, 8, 9):
+        xs = x[:k].contiguous()
+        ys = torch.empty((k, N), dtype=torch.float32, device=dev)
+        calls = [ops.bind_qmv_k(W, xs, ops.MODE_PLAIN, ys) for W in Ws]
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        a = timer.start()
+        for _ in range(reps):
+            for c in calls:
+                c()
+        b = timer.stop()
+        torch.cuda.synchronize()
+        us = timer.elapsed_us(a, b) / (reps * n_weights)
+        nbytes = q4_bytes(N, K) + k * (2 * K + 4 * N)
+        out[f"k{k}"] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                        "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3)}
+    del Ws
+    torch.cuda.empty_cache()
+    return {"shape": [N, K], "weights": n_weights, "widths": out}
 
 
 def copy_probe():
@@ -374,7 +420,7 @@ def main():
     unions = wl.unions()
 
     per_step = len(wl.calls[0]) * wl.layers + len(wl.gdn)
-    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1)
+    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1 + 4)
     log(f"timing events on the launch stream (HIP runtime {timer.path})")
     events = []
     torch.cuda.synchronize()
@@ -415,6 +461,11 @@ def main():
                          "frac_hbm": round(d["bytes"] / (d["us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
                      for n, d in agg.items()}
 
+    dense = None
+    if not args.no_breakdown:
+        log("timing the dense 5120 x 5120 projection ...")
+        dense = dense_projection(dev, timer)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -446,6 +497,7 @@ def main():
                      "bytes_per_launch": round(sum(dom_bytes) / len(dom_bytes)),
                      "kernel_source_hash": khash},
         "kernels": breakdown,
+        "dense_qmv_k": dense,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
         "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "host_cpu": cpu_model()},

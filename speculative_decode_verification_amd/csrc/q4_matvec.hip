@@ -67,7 +67,8 @@ constexpr int kTileCols = 32;
 constexpr int kMaxWaves = 8;
 constexpr int kGatherWaves = 8;
 constexpr int kGatherTilesPerWave = 1;  // tiles one wave streams back to back
-constexpr int kPF = 8;  // groups in flight per lane
+constexpr int kPF = 8;        // groups in flight per lane (gathered units)
+constexpr int kPFDense = 10;  // split-K waves: K = 5120 gives each of 8 waves 10 groups, all issued at once
 
 struct Q4Args {
   const uint4* codes;    // tiled: [E][T][G][64] uint4
@@ -93,7 +94,7 @@ struct Q4Args {
   int tiles_per_block;
 };
 
-template <int MODE, int ACT, bool GATHER, bool KSPLIT>
+template <int MODE, int ACT, bool GATHER, bool KSPLIT, int PF>
 __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* smem, int* s_src, int* s_dst) {
   const int K = a.K;
   const int G = K >> 6;
@@ -167,8 +168,8 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   size_t ld_blk = ((size_t)e * a.T + t_first) * G + gb;
   int ld_g = gb;
   const size_t tile_jump = (size_t)t_step * G - gn;  // from the end of one tile's range to the next
-  uint4 cbuf[kPF];
-  uint32_t sbuf[kPF];
+  uint4 cbuf[PF];
+  uint32_t sbuf[PF];
   auto issue = [&](int slot) {
     cbuf[slot] = codes[ld_blk * 64 + lane];
     sbuf[slot] = sbp[ld_blk * 32 + col];
@@ -179,7 +180,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
     }
   };
 #pragma unroll
-  for (int i = 0; i < kPF; ++i)
+  for (int i = 0; i < PF; ++i)
     if (i < total) issue(i);
 
   // ---- rows, then staging (the loads above are already in flight)
@@ -251,15 +252,15 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   };
   int st0 = 0;
   // steady state: every slot is refilled right after it is consumed
-  for (; st0 + 2 * kPF <= total; st0 += kPF) {
+  for (; st0 + 2 * PF <= total; st0 += PF) {
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) step(i, true);
+    for (int i = 0; i < PF; ++i) step(i, true);
   }
-  // drain: the last (< 2 kPF) steps
-  for (; st0 < total; st0 += kPF) {
+  // drain: the last (< 2 PF) steps
+  for (; st0 < total; st0 += PF) {
 #pragma unroll
-    for (int i = 0; i < kPF; ++i)
-      if (st0 + i < total) step(i, st0 + i + kPF < total);
+    for (int i = 0; i < PF; ++i)
+      if (st0 + i < total) step(i, st0 + i + PF < total);
   }
 
   if (!KSPLIT) {
@@ -325,7 +326,7 @@ template <int MODE, int ACT>
 __global__ __launch_bounds__(512, 2) void q4_dense_kernel(Q4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
-  q4_matvec_body<MODE, ACT, false, true>(a, smem, s_src, s_dst);
+  q4_matvec_body<MODE, ACT, false, true, kPFDense>(a, smem, s_src, s_dst);
 }
 
 // Gathered units: 8 waves per workgroup (one weight tile each), at most 128
@@ -334,7 +335,7 @@ template <int MODE, int ACT>
 __global__ __launch_bounds__(512, 4) void q4_gather_kernel(Q4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
-  q4_matvec_body<MODE, ACT, true, false>(a, smem, s_src, s_dst);
+  q4_matvec_body<MODE, ACT, true, false, kPF>(a, smem, s_src, s_dst);
 }
 
 template <int MODE, int ACT, bool GATHER>

@@ -3,13 +3,14 @@
 // (Red Lite dev45, "What it is": one router dispatch for both rows and the
 // (expert, row) pairs of their union; Flash-Next plan "2.3 MoE").
 //
-// One workgroup of 16 waves.  Wave r selects row r's top-k by repeated
-// argmax over 64-bit (value, index) keys: each lane takes the largest of its
-// own candidates, the 16 lanes of a DPP row reduce with DPP moves, and the
-// four row winners are compared in scalar registers; the code has no
-// data-dependent branches.  Selection compares the raw fp32 logits (higher
-// first, ties to the lower index), so it is exact and independent of how the
-// scores are rounded.
+// One workgroup of 16 waves.  Wave r selects row r's top-k on an order word
+// of each fp32 logit (monotone in the value, -0 equal to +0, NaN lowest):
+// the topk-th largest word T is found bit by bit from the top, each bit one
+// round of wave ballots counting the candidates at or above the trial value;
+// the candidates above T and the lowest-index ones equal to T are compacted,
+// and each takes its slot by counting the selected keys (word, then lower
+// index) that beat it.  Selection compares the raw logits, so it is exact and
+// independent of how the scores are rounded.
 // The union and the pair order come from per-row expert bitmaps, per-expert
 // counts and one prefix scan over the experts, all integer and independent
 // of thread timing.
@@ -48,6 +49,17 @@ __device__ __forceinline__ uint64_t sel_key(float v, int e) {
   return (c != c) ? 0ull : key;
 }
 
+// The order word alone (0 for NaN, never selected), and its value.
+__device__ __forceinline__ uint32_t sel_ord(float v) { return (uint32_t)(sel_key(v, 0) >> 32); }
+
+__device__ __forceinline__ uint64_t key_of(uint32_t ord, int e) {
+  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float ord_value(uint32_t hi) {
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
 __device__ __forceinline__ float key_value(uint64_t key) {
   const uint32_t hi = (uint32_t)(key >> 32);
   return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
@@ -56,28 +68,22 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 __device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
-  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)k, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  return o > k ? o : k;
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t x) {
+  const uint32_t o = __builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+  return o > x ? o : x;
 }
 
-// Largest key of the wave, in every lane (via scalar registers).
-__device__ __forceinline__ uint64_t wave_max(uint64_t k) {
-  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
-  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
-  k = dpp_max<0x124>(k);  // row_ror:4
-  k = dpp_max<0x128>(k);  // row_ror:8   (every lane now holds its row's largest)
-  uint64_t best = 0;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
-    const uint64_t rk = ((uint64_t)hi << 32) | lo;
-    best = rk > best ? rk : best;
-  }
-  return best;
+// Largest 32-bit value of the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = dpp_max_u32<0xB1>(x);
+  x = dpp_max_u32<0x4E>(x);
+  x = dpp_max_u32<0x124>(x);
+  x = dpp_max_u32<0x128>(x);
+  uint32_t m = __builtin_amdgcn_readlane((int)x, 0);
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)x, 32));
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return m;
 }
 
 // DPP move with zero fill: lanes whose source is outside the row (or whose
@@ -110,6 +116,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int32_t s_cnt[SDV_MAX_EXPERTS];
   __shared__ int32_t s_wave[kRouteThreads / 64];
   __shared__ int32_t s_total;
+  __shared__ uint64_t s_cand[SDV_MAX_ROWS][SDV_MAX_TOPK];
+  __shared__ int32_t s_nsel[SDV_MAX_ROWS];
+  __shared__ float s_mx[SDV_MAX_ROWS], s_part[SDV_MAX_ROWS];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int E = a.E, topk = a.topk;
@@ -121,59 +130,95 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int r = wave;
     const float* l = a.logits + (size_t)r * E;
     float val[PL];
-    uint64_t key[PL];
+    uint32_t ord[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) val[j] = l[min(lane + 64 * j, E - 1)];  // unconditional loads
 #pragma unroll
+    for (int j = 0; j < PL; ++j) ord[j] = lane + 64 * j < E ? sel_ord(val[j]) : 0u;
+    // T = the topk-th largest order value: the largest T with at least topk
+    // candidates >= T, found bit by bit from the top (counts by ballots)
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < PL; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
+      if (cnt >= topk) T = cand;
+    }
+    // selected: every candidate above T, then the lowest indices among those
+    // equal to T (T = 0 means fewer than topk candidates: take them all)
+    int above = 0;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) above += __popcll(__ballot(ord[j] > T));
+    const int need = T > 0 ? topk - above : 0;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
     for (int j = 0; j < PL; ++j) {
-      const int e = lane + 64 * j;
-      key[j] = e < E ? sel_key(val[j], e) : 0ull;
+      const bool eq = T > 0 && ord[j] == T;
+      const uint64_t eqb = __ballot(eq);
+      const bool sel = ord[j] > T || (eq && eq_before + __popcll(eqb & lt_mask) < need);
+      const uint64_t selb = __ballot(sel);
+      if (sel) s_cand[r][sel_before + __popcll(selb & lt_mask)] = key_of(ord[j], lane + 64 * j);
+      eq_before += __popcll(eqb);
+      sel_before += __popcll(selb);
     }
-    uint64_t mine = 0;  // lane s keeps slot s's key
-    for (int s = 0; s < topk; ++s) {
-      // the lane's largest key by a pairwise tree (depth log2 PL)
-      uint64_t t[PL];
+    if (lane == 0) s_nsel[r] = sel_before;
+    // the row's largest logit (softmax shift) and the softmax denominator
+    uint32_t omax = 0;
 #pragma unroll
-      for (int j = 0; j < PL; ++j) t[j] = key[j];
-#pragma unroll
-      for (int w = PL / 2; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int j = 0; j < w; ++j) t[j] = t[j + w] > t[j] ? t[j + w] : t[j];
-      }
-      const uint64_t win = wave_max(t[0]);
-#pragma unroll
-      for (int j = 0; j < PL; ++j) key[j] = key[j] == win ? 0ull : key[j];
-      mine = lane == s ? win : mine;
-    }
-    const bool has = lane < topk && mine != 0ull;
-    const float v = key_value(mine);
-    // score of this lane's slot
-    float p;
+    for (int j = 0; j < PL; ++j) omax = max(omax, ord[j]);
+    omax = wave_max_u32(omax);
     if (a.mode == SDV_ROUTE_SOFTMAX) {
-      const float mx = __shfl(v, 0);  // slot 0 holds the row's largest logit
+      const float mx = ord_value(omax);
       float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < PL; ++j)
         if (lane + 64 * j < E) part = part + expf(val[j] - mx);
 #pragma unroll
       for (int off = 1; off <= 32; off <<= 1) part = part + __shfl_xor(part, off);
-      p = expf(v - mx) / part;
+      if (lane == 0) {
+        s_mx[r] = mx;
+        s_part[r] = part;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < a.k) {
+    // lane c takes the c-th selected candidate (index order) and places it by
+    // its rank among the row's selected keys: slot order is larger logit
+    // first, ties to the lower index
+    const int r = wave;
+    const int nsel = s_nsel[r];
+    const bool has = lane < nsel;
+    int slot = lane;
+    uint64_t key = 0;
+    if (has) {
+      key = s_cand[r][lane];
+      int rank = 0;
+      for (int c = 0; c < nsel; ++c) rank += s_cand[r][c] > key;
+      slot = rank;
+    }
+    const float v = key_value(key);
+    float p;
+    if (a.mode == SDV_ROUTE_SOFTMAX) {
+      p = expf(v - s_mx[r]) / s_part[r];
     } else {
       p = 1.0f / (1.0f + expf(-v));
     }
     p = has ? p : 0.0f;
     if (a.renorm) {
-      // fixed butterfly over the slots (lanes past topk add exact zeros)
+      // fixed butterfly over the lanes (lanes without a candidate add zeros)
       float den = p;
 #pragma unroll
       for (int off = 1; off <= 32; off <<= 1) den = den + __shfl_xor(den, off);
       p = p / den;
     }
     if (lane < topk) {
-      const int iv = has ? key_index(mine) : -1;
-      a.w[r * topk + lane] = has ? p : 0.0f;
-      a.idx[r * topk + lane] = iv;
-      s_idx[r * topk + lane] = iv;
+      const int iv = has ? key_index(key) : -1;
+      a.w[r * topk + slot] = has ? p : 0.0f;
+      a.idx[r * topk + slot] = iv;
+      s_idx[r * topk + slot] = iv;
     }
   }
   __syncthreads();
