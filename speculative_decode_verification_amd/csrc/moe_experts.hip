@@ -17,9 +17,9 @@
 //
 // Workgroup (unit u, slice j), 8 waves:
 //   phase A  wave w streams fused gate/up tile 8j + w (16 gate + 16 up
-//            weight rows) over all H / 64 groups; the SwiGLU outputs of the
-//            unit's rows go to LDS (fp32 [rows][slice width]).
-//   phase B  the slice's activations are split into bf16 parts; wave w streams
+//            weight rows) over all H / 64 groups; its SwiGLU outputs go to
+//            LDS already split into phase B's bf16 parts, with their sums.
+//   phase B  wave w streams
 //            down tiles w, w + 8, ... over the slice's two K groups and stores
 //            each finished tile (32 outputs per row).  A 64-wide last slice
 //            is padded with zero activations; its second group re-reads the
@@ -73,24 +73,22 @@ struct ExpertArgs {
 };
 
 struct Lds {
-  size_t xs, xsum, hf, hs, hsum, hrow, total;
+  size_t xs, xsum, hs, hpart, hrow, total;
 };
 
-// LDS layout: phase A's bf16 rows and group sums, and phase B's bf16 parts
-// and group sums share region 0; the fp32 SwiGLU outputs follow it.
+// LDS layout: phase A's bf16 x rows and their group sums; phase B's bf16
+// parts of h (written by phase A's epilogue, so they cannot share space with
+// x rows that slower waves may still read), the per-wave partial group sums
+// of h and the rows' group sums.
 __host__ __device__ inline Lds expert_lds(int k, int H) {
   Lds l;
   const size_t rsA = (size_t)H + 8, rsB = kSlice + 8;
-  const size_t a = (size_t)(k + 1) * rsA * 2 + (size_t)32 * (H / 64) * 4;
-  const size_t b = (size_t)(3 * k + 1) * rsB * 2 + (size_t)32 * (kSlice / 64) * 4 +
-                   (size_t)SDV_MAX_ROWS * (kSlice / 64) * 4;
   l.xs = 0;
   l.xsum = (size_t)(k + 1) * rsA * 2;
-  l.hs = 0;
-  l.hsum = (size_t)(3 * k + 1) * rsB * 2;
-  l.hrow = l.hsum + (size_t)32 * (kSlice / 64) * 4;
-  l.hf = ((a > b ? a : b) + 15) & ~(size_t)15;
-  l.total = l.hf + (size_t)k * kSlice * 4;
+  l.hs = (l.xsum + (size_t)32 * (H / 64) * 4 + 15) & ~(size_t)15;
+  l.hpart = l.hs + (size_t)(3 * k + 1) * rsB * 2;
+  l.hrow = l.hpart + (size_t)SDV_MAX_ROWS * kSliceTiles * 4;
+  l.total = l.hrow + (size_t)SDV_MAX_ROWS * (kSlice / 64) * 4;
   return l;
 }
 
@@ -163,9 +161,8 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   float* xsum = reinterpret_cast<float*>(smem + L.xsum);
   uint16_t* hs = reinterpret_cast<uint16_t*>(smem + L.hs);
-  float* hsum = reinterpret_cast<float*>(smem + L.hsum);
+  float* hpart = reinterpret_cast<float*>(smem + L.hpart);
   float* hrow = reinterpret_cast<float*>(smem + L.hrow);
-  float* hf = reinterpret_cast<float*>(smem + L.hf);
   const int rsA = H + 8, rsB = kSlice + 8;
 
   const int tid = threadIdx.x;
@@ -258,6 +255,8 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     s_src[tid] = src;
     s_dst[tid] = dst;
   }
+  // phase B's all-zero activation row (MFMA rows without data read it)
+  for (int t = tid; t < rsB / 2; t += blockDim.x) reinterpret_cast<uint32_t*>(hs + (size_t)3 * k * rsB)[t] = 0u;
   __syncthreads();
   stage_rows<SDV_ACT_BF16>(a.x, H, k, nrows, xs, xsum, rsA, s_src);
   __syncthreads();
@@ -277,33 +276,44 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
         issue(i, s + kRing);
       }
     }
-    if (nA > 0) {
-      // SwiGLU of this wave's 16 intermediate columns (gate in columns 0-15,
-      // the matching up rows in columns 16-31)
+    // SwiGLU of this wave's 16 intermediate columns (gate in columns 0-15,
+    // the matching up rows in columns 16-31), written straight into phase
+    // B's activation rows: the three bf16 parts of each value at its slot in
+    // the NU order of its 8-column block, and the 16 columns' sum per row.
+    // Columns past a 64-wide slice's end are zero.
+    const int c16 = col & 15;
+    const int n = wave * 16 + c16;                              // column in the slice
+    const int hpos = (n & ~7) + ((n & 7) < 4 ? 2 * (n & 7) : 2 * (n & 7) - 7);
 #pragma unroll
-      for (int r = 0; r < SDV_MAX_ROWS; ++r) {
-        if (r < nrows) {
+    for (int r = 0; r < SDV_MAX_ROWS; ++r) {
+      if (r < nrows && wave < kSliceTiles) {
+        float h = 0.0f;
+        if (nA > 0) {
           const float g = rows_value(y, r);
           const float up = __shfl_xor(g, 16);
-          if (half == rows_half(r) && col < 16) hf[r * kSlice + wave * 16 + col] = siluf_(g) * up;
+          h = siluf_(g) * up;
+        }
+        const float sum16 = row16_sum(h);                        // lanes 0-15 and 32-47 hold columns
+        if (half == rows_half(r) && col < 16) {
+          const uint32_t hi = f32_to_bf16_rne(h);
+          const float r1 = h - bf16_bits_to_f32(hi);
+          const uint32_t mi = f32_to_bf16_rne(r1);
+          const float r2 = r1 - bf16_bits_to_f32(mi);
+          const uint32_t lo = f32_to_bf16_rne(r2);
+          hs[(size_t)(3 * r + 0) * rsB + hpos] = (uint16_t)hi;
+          hs[(size_t)(3 * r + 1) * rsB + hpos] = (uint16_t)mi;
+          hs[(size_t)(3 * r + 2) * rsB + hpos] = (uint16_t)lo;
+          if (col == 0) hpart[r * kSliceTiles + wave] = sum16;
         }
       }
-    } else if (wave < kSliceTiles) {
-      // columns past a 64-wide slice's end are zero
-      for (int e2 = lane; e2 < nrows * 16; e2 += 64) hf[(e2 >> 4) * kSlice + wave * 16 + (e2 & 15)] = 0.0f;
     }
   }
-  __syncthreads();  // every wave's SwiGLU outputs are in hf; xs is free
-  if (tid < SDV_MAX_ROWS) s_src[tid] = tid < nrows ? tid : -1;
-  __syncthreads();
-  stage_rows<SDV_ACT_F32>(hf, kSlice, 3 * k, nrows, hs, hsum, rsB, s_src);
-  __syncthreads();
-  // each row's group sums over its three parts, in part order
+  __syncthreads();  // every wave's part of h is in LDS
+  // each row's group sums: the four 16-column partial sums of the group, in order
   if (tid < SDV_MAX_ROWS * 2) {
     const int r = tid >> 1, g = tid & 1;
-    const int v0 = r < 8 ? r : 24;
-    const int d = r < 8 ? 8 : 1;
-    hrow[r * 2 + g] = (hsum[v0 * 2 + g] + hsum[(v0 + d) * 2 + g]) + hsum[(v0 + 2 * d) * 2 + g];
+    const float* hp = hpart + r * kSliceTiles + 4 * g;
+    hrow[r * 2 + g] = r < nrows ? (hp[0] + hp[1]) + (hp[2] + hp[3]) : 0.0f;
   }
   __syncthreads();
 
