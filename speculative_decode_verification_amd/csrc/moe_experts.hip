@@ -24,8 +24,8 @@
 //            each finished tile (32 outputs per row).  A 64-wide last slice
 //            is padded with zero activations; its second group re-reads the
 //            first group's weights, which then add exactly zero.
-// Each wave's ring of 6 prefetched (codes, scale/bias) blocks runs across the
-// phase boundary.  Phase A is padded to a multiple of 6 steps (the padding
+// Each wave's ring of 4 prefetched (codes, scale/bias) blocks runs across the
+// phase boundary.  Phase A is padded to a multiple of 4 steps (the padding
 // steps re-read the tile's last block and compute nothing), so phase B starts
 // at ring slot 0; every refill is unconditional (past the end of the stream it
 // re-reads the last block), which keeps the load counter waits static.
@@ -45,7 +45,7 @@ namespace {
 using namespace q4;
 
 constexpr int kWaves = 8;
-constexpr int kRing = 6;         // blocks in flight per wave (a multiple of the slice's groups)
+constexpr int kRing = 4;         // blocks in flight per wave (a multiple of the slice's groups)
 constexpr int kSlice = 128;      // intermediate columns per workgroup
 constexpr int kSliceTiles = kSlice / 16;
 constexpr uint32_t kBufferDword3 = 0x00020000u;  // raw buffer resource word 3 (gfx9 family)
@@ -109,6 +109,9 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
   const int rsB = kSlice + 8;
   const int slot = slot_of_arow<SDV_ACT_F32>(col, nrows);
   const uint16_t* ap = hs + (size_t)(slot >= 0 ? slot : 3 * k) * rsB + half * 32;
+  const float* xr[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) xr[i] = hrow + (i < 4 ? 4 * half + i : 8) * 2;
   const __amdgpu_buffer_rsrc_t rsrc = out_rsrc(a.partial, a.partial_bytes);
   // byte offset of the output row behind each of this lane's five
   // accumulators (rows 4 * half + i, and row 8), or -1
@@ -125,16 +128,19 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       // The slice's activations are the same for every tile; an opaque zero
-      // offset keeps their LDS reads in each step instead of holding them in
-      // registers across steps (which would not fit beside the load ring).
-      int z = 0;
-      asm volatile("" : "+v"(z));
+      // offset (distinct per step, so never merged or hoisted, and free of
+      // side effects, so the scheduler may still move it) keeps their LDS
+      // reads in each step instead of holding them in registers across steps
+      // (which would not fit beside the load ring).
+      int z = __builtin_amdgcn_readfirstlane(s0 + i);
+      asm("" : "+s"(z));
+      z -= s0 + i;
       const int g = i & 1;  // ring rounds start at slot 0 and kRing is even
       if (g == 0) {
 #pragma unroll
         for (int v = 0; v < 5; ++v) y[v] = 0.0f;
       }
-      group_mac_rows<SDV_ACT_F32>(cbuf[i], sbuf[i], ap + z + g * 64, hrow + z + g, 2, half, y, dk);
+      group_mac_rows<SDV_ACT_F32>(cbuf[i], sbuf[i], ap + z + g * 64, xr, z + g, y, dk);
       issue(i, s0 + i + kRing);
       if (g == 1) {
         const int n = t * 32 + col;
@@ -170,7 +176,21 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   const int lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
 
-  // ---- unit: a union expert's rows, or the shared expert's k rows
+  // ---- x rows: thread t stages group t % G of row t / G (its 64 elements are
+  // contiguous, at element 64 t); the loads of the first k * G tasks go out
+  // before anything else, since x does not depend on the routing.  All k rows
+  // are staged, in x-row order; the unit's rows pick theirs through s_src.
+  const int G = H >> 6, nxt = k * G;
+  constexpr int kThreads = 64 * kWaves;
+  uint4 xv[8];
+  {
+    const uint4* xp = reinterpret_cast<const uint4*>(a.x) + (size_t)min(tid, nxt - 1) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xv[q] = xp[q];
+  }
+
+  // ---- unit: a union expert's rows, or the shared expert's k rows.  The
+  // routing words are loaded together before any is tested.
   const int u = blockIdx.y, j = blockIdx.x;
   const bool shared = u == k * a.topk;
   int e = 0, p0 = 0, nrows = k;
@@ -185,17 +205,17 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     dnc = a.sdn_codes;
     dns = a.sdn_sb;
   } else {
-    const int nu = *a.n_union;
-    if (u >= nu) return;
-    e = a.union_ids[u];
-    if (e < 0 || e >= a.E) return;
-    p0 = a.pair_off[u];
-    const int p1 = a.pair_off[u + 1];
-    nrows = p1 - p0;
-    if (p0 < 0 || nrows <= 0 || p1 > k * a.topk) return;
+    int nu = __builtin_amdgcn_readfirstlane(*a.n_union);
+    int e0 = __builtin_amdgcn_readfirstlane(a.union_ids[u]);
+    int q0 = __builtin_amdgcn_readfirstlane(a.pair_off[u]);
+    int q1 = __builtin_amdgcn_readfirstlane(a.pair_off[u + 1]);
+    asm volatile("" : "+s"(nu), "+s"(e0), "+s"(q0), "+s"(q1));  // all four in flight together
+    if (u >= nu || e0 < 0 || e0 >= a.E) return;
+    nrows = q1 - q0;
+    if (q0 < 0 || nrows <= 0 || q1 > k * a.topk) return;
     if (nrows > k) nrows = k;
-    e = __builtin_amdgcn_readfirstlane(e);
-    p0 = __builtin_amdgcn_readfirstlane(p0);
+    e = __builtin_amdgcn_readfirstlane(e0);
+    p0 = __builtin_amdgcn_readfirstlane(q0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
   }
 
@@ -212,37 +232,40 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   const int nB8 = (nB + kRing - 1) / kRing * kRing;
   const int total = __builtin_amdgcn_readfirstlane(nA8 + nB8);
   const size_t baseA = ((size_t)e * a.TA + (size_t)j * kSliceTiles + wave) * GA;  // block of step 0
-  const size_t baseB = ((size_t)e * a.TB + wave) * GB;
+  const size_t baseB = ((size_t)e * a.TB + min(wave, a.TB - 1)) * GB;
 
   uint4 cbuf[kRing];
   uint32_t sbuf[kRing];
   // Load the (codes, scale/bias) block of stream step s into ring slot `slot`.
+  // Steps past the end re-read the last block; a wave without blocks reads
+  // the first block of its last down tile, so every wave issues the same
+  // loads in the same order.
+  // The block is selected without branches, so a ring round is one
+  // straight-line block the compiler can schedule across steps.
   auto issue = [&](int slot, int s) {
-    if (s >= total) s = total - 1;
-    if (s < nA8) {
-      const size_t blk = baseA + (size_t)min(s, nA - 1);
-      cbuf[slot] = guc[blk * 64 + lane];
-      sbuf[slot] = gus[blk * 32 + col];
-    } else {
-      const int q = min(s - nA8, nB - 1);
-      const int t = q >> 1;
-      const int g = min(gB0 + (q & 1), gBlast);  // a 64-wide slice re-reads its only group
-      const size_t blk = baseB + (size_t)t * kWaves * GB + g;
-      cbuf[slot] = dnc[blk * 64 + lane];
-      sbuf[slot] = dns[blk * 32 + col];
-    }
+    s = max(min(s, total - 1), 0);
+    const bool inA = s < nA8;                               // then nA > 0
+    const int q = max(min(s - nA8, nB - 1), 0);
+    const int g = min(gB0 + (q & 1), gBlast);               // a 64-wide slice re-reads its only group
+    const long blk = inA ? (long)baseA + min(s, nA - 1) : (long)baseB + (long)(q >> 1) * kWaves * GB + g;
+    cbuf[slot] = (inA ? guc : dnc)[blk * 64 + lane];
+    sbuf[slot] = (inA ? gus : dns)[blk * 32 + col];
   };
-  if (total > 0) {
+  // the unit's (row, slot) pairs go out before the ring, so waiting for them
+  // does not wait for the ring (loads complete in issue order)
+  // (every lane loads, at a clamped index in [p0, p0 + nrows); the shared
+  // unit's are not used).
+  const int pq = p0 + min(tid, nrows - 1);
+  const int pr = a.pair_row[pq], ps = a.pair_slot[pq];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) issue(i, i);
-  }
+  for (int i = 0; i < kRing; ++i) issue(i, i);
 
   // ---- rows, then phase A staging (the ring loads are already in flight)
   if (tid < SDV_MAX_ROWS) {
     int src = -1, dst = -1;
     if (tid < nrows) {
       if (!shared) {
-        const int r = a.pair_row[p0 + tid], s = a.pair_slot[p0 + tid];
+        const int r = pr, s = ps;
         if (r >= 0 && r < k && s >= 0 && s < a.topk) {
           src = r;
           dst = r * (a.topk + 1) + s;
@@ -255,24 +278,68 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     s_src[tid] = src;
     s_dst[tid] = dst;
   }
-  // phase B's all-zero activation row (MFMA rows without data read it)
-  for (int t = tid; t < rsB / 2; t += blockDim.x) reinterpret_cast<uint32_t*>(hs + (size_t)3 * k * rsB)[t] = 0u;
-  __syncthreads();
-  stage_rows<SDV_ACT_BF16>(a.x, H, k, nrows, xs, xsum, rsA, s_src);
+  // the all-zero rows (MFMA rows without data read them)
+  for (int t = tid; t < rsA / 2; t += kThreads) reinterpret_cast<uint32_t*>(xs + (size_t)k * rsA)[t] = 0u;
+  for (int t = tid; t < rsB / 2; t += kThreads) reinterpret_cast<uint32_t*>(hs + (size_t)3 * k * rsB)[t] = 0u;
+  for (int t = tid; t < G; t += kThreads) xsum[k * G + t] = 0.0f;
+  // One task = (x row i, group g): its 8 blocks of 8 elements are stored in NU
+  // order and summed in order, and the group sum adds the 8 block sums
+  // pairwise ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7)).
+  auto put = [&](int t, const uint4 (&v)[8]) {
+    const int i = t / G, g = t - i * G;
+    float bsum[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t e8[8] = {v[q].x & 0xFFFFu, v[q].x >> 16, v[q].y & 0xFFFFu, v[q].y >> 16,
+                              v[q].z & 0xFFFFu, v[q].z >> 16, v[q].w & 0xFFFFu, v[q].w >> 16};
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc = acc + bf16_bits_to_f32(e8[c]);
+      bsum[q] = acc;
+      *reinterpret_cast<uint4*>(xs + (size_t)i * rsA + g * 64 + q * 8) = nu_pack(e8);
+    }
+    xsum[i * G + g] = ((bsum[0] + bsum[1]) + (bsum[2] + bsum[3])) + ((bsum[4] + bsum[5]) + (bsum[6] + bsum[7]));
+  };
+  if (tid < nxt) put(tid, xv);
+  for (int t = tid + kThreads; t < nxt; t += kThreads) {
+    const uint4* xp = reinterpret_cast<const uint4*>(a.x) + (size_t)t * 8;
+    uint4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = xp[q];
+    put(t, v);
+  }
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): enter the stream with no load outstanding
 
   const DecodeK dk = decode_k();
   // ---- phase A: one fused gate/up tile over all GA groups
   {
-    const int slot = slot_of_arow<SDV_ACT_BF16>(col, nrows);
-    const uint16_t* ap = xs + (size_t)(slot >= 0 ? slot : k) * rsA + half * 32;
+    const int src = col < nrows ? s_src[col] : -1;
+    const uint16_t* ap = xs + (size_t)(src >= 0 ? src : k) * rsA + half * 32;
+    // group sums of the x row behind each accumulator (row k is all zero)
+    const float* xr[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int r = i < 4 ? 4 * half + i : 8;
+      const int sr = r < nrows ? s_src[r] : -1;
+      xr[i] = xsum + (sr >= 0 ? sr : k) * G;
+    }
     float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < nA8; s0 += kRing) {
+    // whole rounds, then a last round whose steps past nA compute nothing
+    const int nAfull = nA / kRing * kRing;
+    for (int s0 = 0; s0 < nAfull; s0 += kRing) {
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = s0 + i;
-        if (s < nA) group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xsum + s, GA, half, y, dk);
+        group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+        issue(i, s + kRing);
+      }
+    }
+    if (nAfull < nA8) {
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        const int s = nAfull + i;
+        if (s < nA) group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
         issue(i, s + kRing);
       }
     }

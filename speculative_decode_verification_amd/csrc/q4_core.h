@@ -202,12 +202,13 @@ __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const ui
 
 // The same group step with the parts of each activation row summed right after
 // the matrix product, so a lane keeps five accumulators: y[i] for row
-// 4*half + i (i < 4) and y[4] for row 8 (meaningful in half 0).  xr_g[row * G]
-// is the row's group sum (for fp32 rows, of all three parts).  Per group,
+// 4*half + i (i < 4) and y[4] for row 8 (meaningful in half 0).  xr[i] points
+// at the group sums of the row behind y[i] (for fp32 rows, of all three parts)
+// and s_idx is the group.  Per group,
 //   y += s * P + (b - 128 s) * X,   P = the row's parts' products summed in part order.
 template <int ACT>
-__device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xr_g,
-                                               int G, int half, float y[5], DecodeK dk) {
+__device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, const uint16_t* ap,
+                                               const float* const (&xr)[5], int s_idx, float y[5], DecodeK dk) {
   uint4 av[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 8);
@@ -230,12 +231,10 @@ __device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, con
     t[4] = (acc[12] + acc[13]) + acc[14];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     y[i] = fmaf(s, t[i], y[i]);
-    y[i] = fmaf(c, xr_g[(4 * half + i) * G], y[i]);
+    y[i] = fmaf(c, xr[i][s_idx], y[i]);
   }
-  y[4] = fmaf(s, t[4], y[4]);
-  y[4] = fmaf(c, xr_g[8 * G], y[4]);
 }
 
 // Row r's value from group_mac_rows accumulators (valid in half (r / 4) % 2
