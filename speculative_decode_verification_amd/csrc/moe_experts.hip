@@ -260,25 +260,8 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 #pragma unroll
   for (int i = 0; i < kRing; ++i) issue(i, i);
 
-  // ---- rows, then phase A staging (the ring loads are already in flight)
-  if (tid < SDV_MAX_ROWS) {
-    int src = -1, dst = -1;
-    if (tid < nrows) {
-      if (!shared) {
-        const int r = pr, s = ps;
-        if (r >= 0 && r < k && s >= 0 && s < a.topk) {
-          src = r;
-          dst = r * (a.topk + 1) + s;
-        }
-      } else {
-        src = tid;
-        dst = tid * (a.topk + 1) + a.topk;
-      }
-    }
-    s_src[tid] = src;
-    s_dst[tid] = dst;
-  }
-  // the all-zero rows (MFMA rows without data read them)
+  // ---- phase A staging (the ring loads are already in flight): the all-zero
+  // rows (MFMA rows without data read them)
   for (int t = tid; t < rsA / 2; t += kThreads) reinterpret_cast<uint32_t*>(xs + (size_t)k * rsA)[t] = 0u;
   for (int t = tid; t < rsB / 2; t += kThreads) reinterpret_cast<uint32_t*>(hs + (size_t)3 * k * rsB)[t] = 0u;
   for (int t = tid; t < G; t += kThreads) xsum[k * G + t] = 0.0f;
@@ -307,6 +290,25 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = xp[q];
     put(t, v);
+  }
+  // the unit's rows, after the x tasks (whose loads went out first), so the
+  // wait for the (row, slot) pairs overlaps that work
+  if (tid < SDV_MAX_ROWS) {
+    int src = -1, dst = -1;
+    if (tid < nrows) {
+      if (!shared) {
+        const int r = pr, s = ps;
+        if (r >= 0 && r < k && s >= 0 && s < a.topk) {
+          src = r;
+          dst = r * (a.topk + 1) + s;
+        }
+      } else {
+        src = tid;
+        dst = tid * (a.topk + 1) + a.topk;
+      }
+    }
+    s_src[tid] = src;
+    s_dst[tid] = dst;
   }
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): enter the stream with no load outstanding
