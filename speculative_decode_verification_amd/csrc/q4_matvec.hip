@@ -453,12 +453,16 @@ size_t q4_lds_bytes(int K, int slot_cap, int nw) {
   return (size_t)(slot_cap + 1) * (K + 8) * 2 + (size_t)32 * G * 4 + (size_t)nw * 32 * 33 * 4;
 }
 
+size_t dense_lds_bytes(int K, int act_dtype, int k);
+hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
+                        hipStream_t st);
+
 size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather) {
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   // gathered: per-wave output staging for one tile of up to 9 rows x 32 columns
   return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * 4 +
                       (size_t)kGatherWaves * kGatherTilesPerWave * SDV_MAX_ROWS * 32 * 4
-                : q4_lds_bytes(K, cap, q4_waves_for(K));
+                : dense_lds_bytes(K, act_dtype, k);
 }
 
 hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, bool gather,
@@ -501,16 +505,7 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
     SDV_Q4_G(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
 #undef SDV_Q4_G
   } else {
-    const int nw = q4_waves_for(W.K);
-    a.tiles_per_block = 1;
-    const size_t lds = q4_lds_bytes(W.K, a.slot_cap, nw);
-#define SDV_Q4_D(M, A) \
-  if (mode == M && act_dtype == A) return launch_one<M, A, false>(a, a.T, 1, nw, lds, st);
-    SDV_Q4_D(SDV_MODE_PLAIN, SDV_ACT_BF16)
-    SDV_Q4_D(SDV_MODE_PLAIN, SDV_ACT_F32)
-    SDV_Q4_D(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
-    SDV_Q4_D(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
-#undef SDV_Q4_D
+    return dense_launch(W, mode, act, act_dtype, k, out, st);
   }
   return hipErrorInvalidValue;
 }
