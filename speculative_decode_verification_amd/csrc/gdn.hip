@@ -171,9 +171,11 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     }
     o = row16_sum(o);
     if (sub == 0) a.y[((long)t * a.Hv + h) * a.Dv + i] = o;
-    float4* dst = reinterpret_cast<float4*>(a.snaps[t] + row * DK);
+    // snapshots are written once and read back at most once, after the call:
+    // streaming (nontemporal) stores keep them from displacing cached data
+    f32x4* dst = reinterpret_cast<f32x4*>(a.snaps[t] + row * DK);
 #pragma unroll
-    for (int j = 0; j < NV4; ++j) dst[sub + 16 * j] = S[j];
+    for (int j = 0; j < NV4; ++j) __builtin_nontemporal_store(f32x4{S[j].x, S[j].y, S[j].z, S[j].w}, dst + sub + 16 * j);
   }
 }
 
