@@ -12,6 +12,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming loads for data read once per call (weights, the input state):
+// nontemporal, so they do not displace data that is read again.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v w = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(w.x, w.y, w.z, w.w);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   {
     const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + (active ? row : nrows - 1) * DK);
 #pragma unroll
-    for (int j = 0; j < NV4; ++j) S[j] = sin4[sub + 16 * j];
+    for (int j = 0; j < NV4; ++j) S[j] = load_nt(sin4 + sub + 16 * j);  // the state: read once per call
   }
   __builtin_amdgcn_sched_barrier(0);
   if (LDS_KQ) {

@@ -248,8 +248,8 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     const int q = max(min(s - nA8, nB - 1), 0);
     const int g = min(gB0 + (q & 1), gBlast);               // a 64-wide slice re-reads its only group
     const long blk = inA ? (long)baseA + min(s, nA - 1) : (long)baseB + (long)(q >> 1) * kWaves * GB + g;
-    cbuf[slot] = (inA ? guc : dnc)[blk * 64 + lane];
-    sbuf[slot] = (inA ? gus : dns)[blk * 32 + col];
+    cbuf[slot] = load_nt((inA ? guc : dnc) + blk * 64 + lane);  // weights: read once per call
+    sbuf[slot] = load_nt((inA ? gus : dns) + blk * 32 + col);
   };
   // the unit's (row, slot) pairs go out before the ring, so waiting for them
   // does not wait for the ring (loads complete in issue order)

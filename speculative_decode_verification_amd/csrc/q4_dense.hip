@@ -115,8 +115,8 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   uint32_t sbuf[PF];
   auto issue = [&](int slot, int s) {
     const size_t blk = blk0 + min(s, gw - 1);
-    cbuf[slot] = a.codes[blk * 64 + lane];
-    sbuf[slot] = a.sb[blk * 32 + col];
+    cbuf[slot] = load_nt(a.codes + blk * 64 + lane);  // weights: read once per call
+    sbuf[slot] = load_nt(a.sb + blk * 32 + col);
   };
 #pragma unroll
   for (int i = 0; i < PF; ++i) issue(i, i);

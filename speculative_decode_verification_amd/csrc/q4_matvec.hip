@@ -171,8 +171,8 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   uint4 cbuf[PF];
   uint32_t sbuf[PF];
   auto issue = [&](int slot) {
-    cbuf[slot] = codes[ld_blk * 64 + lane];
-    sbuf[slot] = sbp[ld_blk * 32 + col];
+    cbuf[slot] = load_nt(codes + ld_blk * 64 + lane);  // weights: read once per call
+    sbuf[slot] = load_nt(sbp + ld_blk * 32 + col);
     ++ld_blk;
     if (++ld_g == ge) {
       ld_g = gb;
