@@ -11,7 +11,7 @@
 // and each takes its slot by counting the selected keys (word, then lower
 // index) that beat it.  Selection compares the raw logits, so it is exact and
 // independent of how the scores are rounded.
-// The union and the pair order come from per-row expert bitmaps, per-expert
+// The union and the pair order come from per-expert row masks, per-expert
 // counts and one prefix scan over the experts, all integer and independent
 // of thread timing.
 
@@ -23,7 +23,6 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxPerLane = SDV_MAX_EXPERTS / 64;
-constexpr int kWords = SDV_MAX_EXPERTS / 32;
 
 struct RouteArgs {
   const float* logits;
@@ -112,7 +111,7 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
 template <int PL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int32_t s_idx[SDV_MAX_ROWS * SDV_MAX_TOPK];
-  __shared__ uint32_t s_rowbits[SDV_MAX_ROWS][kWords];
+  __shared__ uint32_t s_rowmask[SDV_MAX_EXPERTS];  // rows choosing each expert (bit r)
   __shared__ int32_t s_cnt[SDV_MAX_EXPERTS];
   __shared__ int32_t s_wave[kRouteThreads / 64];
   __shared__ int32_t s_total;
@@ -123,7 +122,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int E = a.E, topk = a.topk;
 
-  for (int t = tid; t < SDV_MAX_ROWS * kWords; t += kRouteThreads) (&s_rowbits[0][0])[t] = 0u;
+  for (int t = tid; t < SDV_MAX_EXPERTS; t += kRouteThreads) s_rowmask[t] = 0u;
   for (int t = tid; t < SDV_MAX_EXPERTS; t += kRouteThreads) s_cnt[t] = 0;
 
   if (wave < a.k) {
@@ -137,6 +136,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     for (int j = 0; j < PL; ++j) ord[j] = lane + 64 * j < E ? sel_ord(val[j]) : 0u;
     // T = the topk-th largest order value: the largest T with at least topk
     // candidates >= T, found bit by bit from the top (counts by ballots)
+    // The search stops early once exactly topk candidates are >= the trial
+    // value: T is then a lower bound of the topk-th value that selects the
+    // same set (every candidate >= T, no tie to break).
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 #pragma unroll
       for (int j = 0; j < PL; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
       if (cnt >= topk) T = cand;
+      if (cnt == topk) break;
     }
     // selected: every candidate above T, then the lowest indices among those
     // equal to T (T = 0 means fewer than topk candidates: take them all)
@@ -195,8 +198,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     uint64_t key = 0;
     if (has) {
       key = s_cand[r][lane];
+      // all the row's candidate reads are issued together (at most
+      // SDV_MAX_TOPK, the unused ones predicated off)
       int rank = 0;
-      for (int c = 0; c < nsel; ++c) rank += s_cand[r][c] > key;
+#pragma unroll
+      for (int c = 0; c < SDV_MAX_TOPK; ++c) rank += (c < nsel && s_cand[r][c] > key) ? 1 : 0;
       slot = rank;
     }
     const float v = key_value(key);
@@ -208,10 +214,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     p = has ? p : 0.0f;
     if (a.renorm) {
-      // fixed butterfly over the lanes (lanes without a candidate add zeros)
-      float den = p;
-#pragma unroll
-      for (int off = 1; off <= 32; off <<= 1) den = den + __shfl_xor(den, off);
+      // the row's sum in a fixed order: each 16-lane DPP row, then the four
+      // row totals in row order (lanes without a candidate add zeros)
+      const float part = row16_sum(p);
+      const float den = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), 0)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), 16))) +
+                        (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), 32)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), 48)));
       p = p / den;
     }
     if (lane < topk) {
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   if (tid < total) {
     const int e = s_idx[tid];
     if (e >= 0 && e < E) {
-      atomicOr(&s_rowbits[tid / topk][e >> 5], 1u << (e & 31));
+      atomicOr(&s_rowmask[e], 1u << (tid / topk));
       atomicAdd(&s_cnt[e], 1);
     }
   }
@@ -252,13 +261,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     if (e >= 0 && e < E) {
       const int32_t pre = s_cnt[e];
       const int less = pre & 0xFFFF, distinct_less = pre >> 16;
-      int same_before = 0;
-      bool first = true;
-      for (int r2 = 0; r2 < r; ++r2) {
-        const bool has = (s_rowbits[r2][e >> 5] >> (e & 31)) & 1u;
-        same_before += has;
-        first = first && !has;
-      }
+      const uint32_t before = s_rowmask[e] & ((1u << r) - 1u);  // earlier rows with expert e
+      const int same_before = __popc(before);
+      const bool first = before == 0u;
       const int pos = less + same_before;  // pairs ordered by (expert, row)
       a.pair_row[pos] = r;
       a.pair_slot[pos] = s;
