@@ -249,8 +249,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int32_t incl = wave_incl_scan(packed);
   if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
-  int32_t base = 0;
-  for (int w2 = 0; w2 < wave; ++w2) base += s_wave[w2];
+  int32_t base = 0;  // totals of the earlier waves (reads issued together)
+#pragma unroll
+  for (int w2 = 0; w2 < kRouteThreads / 64; ++w2) base += w2 < wave ? s_wave[w2] : 0;
   if (tid == kRouteThreads - 1) s_total = base + incl;
   __syncthreads();
   if (tid < E) s_cnt[tid] = base + incl - packed;  // exclusive prefix of expert tid
@@ -273,13 +274,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       }
     }
   }
-  if (tid == 0) {
+  {
     const int nu = s_total >> 16, npairs = s_total & 0xFFFF;
-    *a.n_union = nu;
+    if (tid == 0) *a.n_union = nu;
     // entries past n_union are unused; keep them defined (the last union
     // entry's pair range ends at the number of pairs written)
-    for (int u = nu; u <= total; ++u) a.pair_off[u] = npairs;
-    for (int u = nu; u < total; ++u) a.union_ids[u] = -1;
+    for (int u = nu + tid; u <= total; u += kRouteThreads) {
+      a.pair_off[u] = npairs;
+      if (u < total) a.union_ids[u] = -1;
+    }
   }
 }
 
