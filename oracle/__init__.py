@@ -23,6 +23,9 @@ definition written out.  Sources, by page and section:
   t of the DeltaNet runs from the state after row t-1 and that state is
   snapshotted; one router dispatch and the union of the rows' experts; a
   rejected draft is undone by selecting the snapshot.
+* Red Lite dev45, "Acceptance": a draft is accepted when the token sampled
+  from the previous row's logits equals it (exact with any sampler); dev45b:
+  a draft whose sampled token is the end-of-answer token is rejected.
 * Flash-Next plan (QWEN38FLASH.md): "2.1 Gated DeltaNet" (decay, kv_mem,
   delta, rank-1 update, readout on fp32 [Hv, Dv, Dk]), "2.3 MoE" (routed +
   shared experts, SwiGLU, gate+up concatenated), "3.1 Overlap" (per-head
@@ -38,7 +41,8 @@ in the function's docstring.
 """
 
 from .ref import (bf16_to_f64, unpack_q4, dequant, qmv, route, union_pairs, silu, swiglu,
-                  combine, moe_verify, gdn_verify, rollback)
+                  combine, moe_verify, gdn_verify, rollback, sample_tokens, accept, verify_cycle)
 
 __all__ = ["bf16_to_f64", "unpack_q4", "dequant", "qmv", "route", "union_pairs", "silu",
-           "swiglu", "combine", "moe_verify", "gdn_verify", "rollback"]
+           "swiglu", "combine", "moe_verify", "gdn_verify", "rollback", "sample_tokens", "accept",
+           "verify_cycle"]

@@ -278,3 +278,63 @@ def rollback(S_in, snaps, j):
     if not (0 <= j <= rows):
         raise ValueError(f"accepted prefix {j} outside 0..{rows}")
     return np.array(S_in, copy=True) if j == 0 else np.array(snaps[j - 1], copy=True)
+
+
+# ---------------------------------------------------------------------------
+# acceptance (Red Lite dev45, "Acceptance": a draft is accepted when the token
+# sampled from the previous row's logits equals it, which keeps the output that
+# of ordinary decoding with any sampler; dev45b: a draft row whose sampled
+# token is the end-of-answer token is rejected, so that token never enters the
+# state)
+# ---------------------------------------------------------------------------
+
+def sample_tokens(logits, noise=None, inv_temp=1.0):
+    """The token sampled from each row of ``logits`` [rows, V]: the index of
+    the largest z, the lowest such index on ties, a NaN z never chosen (-1 for
+    a row with no number).  Greedy: z = logits.  With Gumbel noise g (one
+    value per logit, passed in): z = fl32(fl32(logits * inv_temp) + g), each
+    operation rounded to fp32, so the decision is taken in the precision of
+    the kernel; Gumbel-max of z samples the softmax at temperature 1 /
+    inv_temp.  -0 and +0 compare equal.  (The sampler is our reading: the
+    pages allow any sampler and measure greedy.)"""
+    l = np.asarray(logits, dtype=np.float32)
+    if noise is None:
+        z = l
+    else:
+        z = (l * np.float32(inv_temp)).astype(np.float32) + np.asarray(noise, dtype=np.float32)
+        z = z.astype(np.float32)
+    out = np.full(z.shape[0], -1, dtype=np.int32)
+    for r in range(z.shape[0]):
+        valid = np.flatnonzero(~np.isnan(z[r]))
+        if valid.size == 0:
+            continue
+        best = z[r][valid].max()
+        out[r] = valid[z[r][valid] == best][0]
+    return out
+
+
+def accept(tokens, drafts, eos=-1):
+    """Number of leading drafts accepted.  ``drafts[t]`` is the token of row
+    t + 1; it is accepted when every earlier draft was, it equals the token
+    sampled from row t, and it is not the end-of-answer token ``eos`` (-1:
+    none).  With n accepted, rows 0..n stay in the state (rollback to the
+    prefix of n + 1 rows) and tokens[0..n] are emitted, tokens[n] becoming the
+    next pending token."""
+    n = 0
+    for t in range(len(drafts)):
+        if drafts[t] == tokens[t] and (eos < 0 or drafts[t] != eos):
+            n += 1
+        else:
+            break
+    return n
+
+
+def verify_cycle(logits, drafts, eos=-1, noise=None, inv_temp=1.0):
+    """Acceptance of one verified block: the sampled tokens, the accepted
+    draft count n, the accepted prefix length n + 1 (rows kept in the state)
+    and the emitted tokens (the n accepted drafts, then the token sampled
+    after them)."""
+    tokens = sample_tokens(logits, noise, inv_temp)
+    n = accept(tokens, drafts, eos)
+    emitted = [int(d) for d in drafts[:n]] + [int(tokens[n])]
+    return {"tokens": tokens, "accepted": n, "prefix": n + 1, "emitted": emitted}

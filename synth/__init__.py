@@ -22,11 +22,11 @@ from .counter import (GAMMA, SEED, derive_key, mix64, rand64, bf16_bits_from_f32
                       q4_code_words, q4_affine_bf16, q4_rows)
 from . import configs
 from .inputs import (BankKeys, bank_keys, activations, dense_weight, moe_layer_inputs, gdn_layer_inputs,
-                     gdn_state, accepted_prefix, integer_exact_weight)
+                     gdn_state, accepted_prefix, integer_exact_weight, verify_block, gumbel_noise)
 
 __all__ = [
     "GAMMA", "SEED", "derive_key", "mix64", "rand64", "bf16_bits_from_f32",
     "q4_code_words", "q4_affine_bf16", "q4_rows", "configs", "BankKeys", "bank_keys", "activations",
-    "dense_weight", "moe_layer_inputs", "gdn_layer_inputs", "gdn_state",
+    "dense_weight", "moe_layer_inputs", "gdn_layer_inputs", "gdn_state", "verify_block", "gumbel_noise",
     "accepted_prefix", "integer_exact_weight",
 ]

@@ -5,7 +5,10 @@ router logits ~ N(0,1) fp32; shared-expert gate logit z ~ N(0,1) fp32;
 codes ~ U{0..15}; scales ~ U(0.005, 0.02) bf16; biases ~ U(-0.1, 0.1) bf16;
 GDN state S ~ N(0, 0.1^2) fp32; q, k ~ N(0,1) then L2-normalised per (row,
 head); v ~ N(0,1); beta = sigmoid(N(0,1)); g = exp(-softplus(N(0,1)));
-accepted prefix j ~ U{0..k}.
+accepted prefix j ~ U{0..k}.  Verify-block next-token logits ~ N(0,1) fp32
+over the vocabulary, with a planted number of accepted drafts ~ U{0..k-1}
+(the planted tokens are raised a fixed margin above their row's maximum);
+Gumbel noise g = -log(-log(u)), u ~ U(0,1), for sampled acceptance.
 """
 
 from collections import namedtuple
@@ -20,6 +23,7 @@ BankKeys = namedtuple("BankKeys", "codes scales biases")
 DENSE_W, GATEUP, DOWN, SHARED_GATEUP, SHARED_DOWN = 0, 1, 2, 3, 4
 # tensor ids (part of the numpy seeds)
 T_X, T_LOGITS, T_Z, T_S, T_Q, T_K, T_V, T_G, T_BETA, T_J = 10, 11, 12, 20, 21, 22, 23, 24, 25, 30
+T_VLOGITS, T_GUMBEL, T_DRAFTS = 40, 41, 42
 
 
 def bank_keys(cfg_id, kind, layer):
@@ -94,3 +98,36 @@ def integer_exact_weight(seed, n, k, rows):
     biases = bf16_bits_from_f32(m * np.float32(2.0 ** -6))
     x = bf16_bits_from_f32(rng.integers(-8, 9, size=(rows, k)).astype(np.float32))
     return codes, scales, biases, x
+
+
+def verify_block(cfg_id, step, rows, vocab, accepted=None, margin=4.0, eos=-1):
+    """Next-token logits [rows, vocab] fp32 ~ N(0,1) and the drafts [rows - 1]
+    of one verify block, with ``accepted`` (default ~ U{0..rows-1}) drafts
+    planted to be accepted under greedy sampling: for t < accepted, row t's
+    logit of drafts[t] is set ``margin`` above the row's maximum; when
+    accepted < rows - 1, row ``accepted`` gets its raised token on a token
+    other than drafts[accepted].  Drafts never equal ``eos`` unless planted
+    by the caller.  Returns (logits, drafts, accepted)."""
+    rng = _rng(cfg_id, T_VLOGITS, step)
+    logits = rng.standard_normal((rows, vocab), dtype=np.float32)
+    drng = _rng(cfg_id, T_DRAFTS, step)
+    drafts = drng.integers(0, vocab, size=max(rows - 1, 0)).astype(np.int32)
+    if eos >= 0:
+        drafts[drafts == eos] = (eos + 1) % vocab
+    if accepted is None:
+        accepted = int(drng.integers(0, rows))
+    for t in range(min(accepted, rows - 1)):
+        logits[t, drafts[t]] = logits[t].max() + np.float32(margin)
+    if accepted < rows - 1:
+        other = (int(drafts[accepted]) + 1 + int(drng.integers(0, vocab - 1))) % vocab
+        if other == drafts[accepted]:
+            other = (other + 1) % vocab
+        logits[accepted, other] = logits[accepted].max() + np.float32(margin)
+    return logits, drafts, accepted
+
+
+def gumbel_noise(cfg_id, step, rows, vocab):
+    """Gumbel(0, 1) noise [rows, vocab] fp32: -log(-log(u)) with u uniform in (0, 1)."""
+    u = _rng(cfg_id, T_GUMBEL, step).random((rows, vocab))
+    u = np.clip(u, 2.0 ** -53, 1.0 - 2.0 ** -53)
+    return (-np.log(-np.log(u))).astype(np.float32)

@@ -475,11 +475,115 @@ def check_gdn_rollback(ref):
             raise AssertionError("rollback accepted an out-of-range prefix")
 
 
+# ---------------------------------------------------------------------------
+# acceptance
+# ---------------------------------------------------------------------------
+
+def _scan_argmax(row):
+    """Independent scan: first index of the largest non-NaN value (-1 if none)."""
+    best, arg = None, -1
+    for i, v in enumerate(row):
+        v = float(v)
+        if math.isnan(v):
+            continue
+        if best is None or v > best:
+            best, arg = v, i
+    return arg
+
+
+def check_sample_greedy(ref):
+    """P13: greedy tokens equal an element-by-element scan: ties (including
+    -0 against +0 and equal infinities) go to the lower index, NaN is never
+    chosen, an all-NaN row gives -1."""
+    nan, inf = float("nan"), float("inf")
+    rows = np.array([[0.5, 2.0, 2.0, -1.0, 1.0],
+                     [nan, -3.0, nan, -3.0, -4.0],
+                     [-0.0, 0.0, -1.0, -2.0, -0.0],
+                     [nan, nan, nan, nan, nan],
+                     [-inf, inf, 3.0, inf, nan],
+                     [-inf, -inf, -inf, -inf, -inf]], dtype=np.float32)
+    got = ref.sample_tokens(rows)
+    assert [int(t) for t in got] == [_scan_argmax(r) for r in rows] == [1, 1, 0, -1, 1, 0]
+    rng = np.random.default_rng(7)
+    rnd = rng.integers(-3, 4, size=(40, 12)).astype(np.float32)  # many ties
+    assert [int(t) for t in ref.sample_tokens(rnd)] == [_scan_argmax(r) for r in rnd]
+
+
+def check_sample_noise_rounding(ref):
+    """P13: with noise, z is fp32(fp32(l * inv_temp) + g) with each operation
+    rounded; near-ties decided in fp32 match a scalar fp32 evaluation."""
+    rng = np.random.default_rng(8)
+    l = rng.standard_normal((30, 16)).astype(np.float32)
+    g = rng.gumbel(size=(30, 16)).astype(np.float32)
+    inv_t = np.float32(0.7)
+    expect = []
+    for r in range(30):
+        z = [np.float32(np.float32(l[r, i] * inv_t) + g[r, i]) for i in range(16)]
+        expect.append(_scan_argmax(z))
+    assert [int(t) for t in ref.sample_tokens(l, g, float(inv_t))] == expect
+
+
+def check_sample_gumbel_is_softmax(ref):
+    """P14: Gumbel-max sampling: over many noise draws the token frequencies
+    match softmax(l * inv_temp) (chi-square with 5 degrees of freedom below
+    40, p ~ 1e-7 for a correct sampler)."""
+    l = np.array([0.0, 1.0, 2.0, 3.0, -1.0, 0.5], dtype=np.float32)
+    inv_t = 0.7
+    n = 40000
+    g = np.random.default_rng(9).gumbel(size=(n, l.size)).astype(np.float32)
+    toks = ref.sample_tokens(np.broadcast_to(l, (n, l.size)), g, inv_t)
+    counts = np.bincount(toks, minlength=l.size).astype(float)
+    w = [math.exp(inv_t * float(x)) for x in l]
+    p = [x / sum(w) for x in w]
+    chi2 = sum((counts[i] - n * p[i]) ** 2 / (n * p[i]) for i in range(l.size))
+    assert chi2 < 40.0, chi2
+
+
+def check_accept_cases(ref):
+    """P15: acceptance stops at the first draft that differs from the token
+    sampled from the previous row, and at a draft equal to the end-of-answer
+    token even when it matches; no drafts (one row) accepts none."""
+    cases = [
+        ([5, 6, 7, 8], [5, 6, 7], -1, 3),
+        ([5, 6, 7, 8], [4, 6, 7], -1, 0),
+        ([5, 6, 7, 8], [5, 9, 7], -1, 1),
+        ([5, 6, 7, 8], [5, 6, 1], -1, 2),
+        ([5, 6, 7, 8], [5, 6, 7], 6, 1),   # row 2's draft is the end-of-answer token
+        ([5, 6, 7, 8], [5, 6, 7], 5, 0),
+        ([5], [], 3, 0),
+        ([-1, 4], [-1], -1, 1),            # an all-NaN row's token still compares by value
+    ]
+    for tokens, drafts, eos, n in cases:
+        assert ref.accept(tokens, drafts, eos) == n, (tokens, drafts, eos)
+
+
+def check_verify_cycle_rollback(ref):
+    """P16: the emitted tokens are the accepted drafts and then the token
+    sampled after them, and rolling the GDN state back to the accepted prefix
+    equals a fresh run over those rows only."""
+    hv, hk, d, rows = 4, 2, 8, 6
+    inp = synth.gdn_layer_inputs(13, 0, rows, hv, hk, d, d)
+    S = synth.gdn_state(13, 0, hv, d, d)
+    y, snaps = ref.gdn_verify(S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    for planted in range(rows):
+        logits, drafts, _ = synth.verify_block(13, planted, rows, 50, accepted=planted)
+        out = ref.verify_cycle(logits, drafts)
+        n = out["accepted"]
+        assert n == planted
+        toks = [_scan_argmax(r) for r in logits]
+        assert out["emitted"] == [int(x) for x in drafts[:n]] + [toks[n]]
+        assert out["prefix"] == n + 1
+        st = ref.rollback(S, snaps, out["prefix"])
+        _, sj = ref.gdn_verify(S, *(inp[m][:n + 1] for m in ("q", "k", "v", "g", "beta")))
+        assert np.array_equal(st, sj[-1])
+
+
 ALL_CHECKS = [
     check_bf16_decode, check_unpack_roundtrip, check_qmv_bruteforce, check_qmv_integer_exact,
     check_qmv_closed_forms, check_qmv_rows_independent, check_route_selection, check_route_weights,
     check_union_pairs, check_swiglu, check_moe_pairs_dense, check_moe_single_expert,
     check_moe_combine_closed_form, check_moe_identical_experts, check_gdn_bruteforce,
     check_gdn_no_write, check_gdn_scalar, check_gdn_basis, check_gdn_retrieval,
-    check_gdn_head_groups, check_gdn_rollback,
+    check_gdn_head_groups, check_gdn_rollback, check_sample_greedy, check_sample_noise_rounding,
+    check_sample_gumbel_is_softmax, check_accept_cases, check_verify_cycle_rollback,
 ]

@@ -35,6 +35,15 @@ MUTANTS = {
     "gdn_readout_before_update": ("y[t, h] = S[h] @ qt", "y[t, h] = (S[h] - np.outer(delta, kt)) @ qt"),
     "gdn_kvmem_uses_q": ("m = S[h] @ kt", "m = S[h] @ qt"),
     "rollback_off_by_one": ("else np.array(snaps[j - 1], copy=True)", "else np.array(snaps[min(j, rows - 1)], copy=True)"),
+    "sample_ties_to_higher": ("out[r] = valid[z[r][valid] == best][0]", "out[r] = valid[z[r][valid] == best][-1]"),
+    "sample_nan_chosen": ("valid = np.flatnonzero(~np.isnan(z[r]))", "valid = np.arange(z.shape[1])"),
+    "sample_temperature_dropped": ("(l * np.float32(inv_temp))", "(l * np.float32(1.0))"),
+    "sample_noise_subtracted": ("+ np.asarray(noise, dtype=np.float32)", "- np.asarray(noise, dtype=np.float32)"),
+    "accept_past_mismatch": ("            n += 1\n        else:\n            break", "            n += 1"),
+    "accept_end_of_answer_ignored": ("if drafts[t] == tokens[t] and (eos < 0 or drafts[t] != eos):", "if drafts[t] == tokens[t]:"),
+    "accept_compares_next_row": ("if drafts[t] == tokens[t] and", "if drafts[t] == tokens[t + 1] and"),
+    "emitted_without_bonus": ("+ [int(tokens[n])]", ""),
+    "prefix_off_by_one": ('"prefix": n + 1', '"prefix": n'),
 }
 
 
