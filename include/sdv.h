@@ -312,6 +312,43 @@ SDV_API int sdv_gdn_rollback(int k, int j, int *selected_slot);
 SDV_API int sdv_gdn_rollback_copy(float *dst, const float *S_in, float *const *snaps, int k, int j,
                           size_t state_elems, sdv_stream_t stream);
 
+/*
+ * sdv_verify_accept_workspace_bytes -- device workspace needed by
+ * sdv_verify_accept_k for k rows of V logits (0 for k outside 1..9 or V < 1).
+ */
+SDV_API size_t sdv_verify_accept_workspace_bytes(int k, int V);
+
+/*
+ * sdv_verify_accept_k -- acceptance of a verified block: the token sampled from
+ * each row and the number of leading drafts accepted (Red Lite dev45,
+ * "Acceptance": a draft is accepted when the token sampled from the previous
+ * row's logits equals it, so the output is that of ordinary decoding with any
+ * sampler; dev45b: a draft whose sampled token is the end-of-answer token is
+ * rejected, so that token never enters the state).
+ *   logits    device fp32 [k][V]: row t's next-token logits (row 0 follows the
+ *             pending token, row t > 0 follows draft t)
+ *   noise     device fp32 [k][V] Gumbel(0, 1) noise, or NULL for greedy
+ *   inv_temp  1 / temperature (used with noise): a row's scores are
+ *             fp32(fp32(logits * inv_temp) + noise), each operation rounded
+ *   drafts    device int32 [k - 1]: the tokens of rows 1..k-1 (NULL allowed for k = 1)
+ *   eos       end-of-answer token id, or -1 for none
+ *   tokens    device int32 [k] out: row t's sample = the index of its largest
+ *             score, ties to the lower index; NaN scores never win; -1 if a row
+ *             has no number
+ *   accepted  device int32 [1] out: n in 0..k-1, the count of leading drafts
+ *             that equal the token sampled from the previous row and are not
+ *             eos.  Rows 0..n stay in the state (sdv_gdn_rollback with j = n + 1)
+ *             and tokens[0..n] are emitted, tokens[n] becoming the next pending token.
+ *   workspace device, at least sdv_verify_accept_workspace_bytes(k, V) bytes,
+ *             overwritten (scratch between the call's two launches)
+ * Results are exact (integer keys), independent of launch shape.
+ * Errors: EINVAL (null, misaligned, workspace too small), EWIDTH, ERANGE (V outside
+ * 1..2^30, or inv_temp not finite and positive when noise is given), EALIAS, EHIP.
+ */
+SDV_API int sdv_verify_accept_k(const float *logits, const float *noise, float inv_temp, const int32_t *drafts,
+                                int k, int V, int eos, int32_t *tokens, int32_t *accepted, void *workspace,
+                                size_t workspace_bytes, sdv_stream_t stream);
+
 /* Static text for a status code. */
 SDV_API const char *sdv_status_string(int status);
 

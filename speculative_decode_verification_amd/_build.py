@@ -20,7 +20,8 @@ HIPCC_FLAGS = [
     # keep the compiler from emitting packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-LIB_SOURCES = ["api.hip", "q4_matvec.hip", "q4_dense.hip", "moe_experts.hip", "route.hip", "combine.hip", "gdn.hip"]
+LIB_SOURCES = ["api.hip", "q4_matvec.hip", "q4_dense.hip", "moe_experts.hip", "route.hip", "combine.hip", "gdn.hip",
+               "accept.hip"]
 
 
 def hipcc():

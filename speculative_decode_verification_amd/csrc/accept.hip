@@ -1,0 +1,153 @@
+// Acceptance of a verified block on the device: the token sampled from each
+// row and the number of leading drafts accepted (Red Lite dev45,
+// "Acceptance": a draft is accepted when the token sampled from the previous
+// row's logits equals it, which keeps the output that of ordinary decoding
+// with any sampler; dev45b: a draft whose sampled token is the end-of-answer
+// token is rejected, so that token never enters the state).
+//
+// A row's sample is its largest score, ties to the lower index.  Greedy
+// scores are the logits; with Gumbel noise g (passed in) a score is
+// fp32(fp32(l * inv_temp) + g), each operation rounded.  A score becomes a
+// 64-bit key whose high word maps fp32 onto an unsigned order (-0 taken as
+// +0; NaN gets key 0 and never wins) and whose low word is the complemented
+// index, so the largest key is the sample.
+//
+// Stage 1, grid (chunks, rows) of 256 threads: each workgroup takes the
+// largest key of a 4096-element chunk of one row (16 coalesced loads per
+// thread, all issued before any is used) and writes it to the workspace.
+// Stage 2, one workgroup: wave r reduces row r's chunk keys to its token,
+// then one thread counts the accepted drafts.  Integer keys make the result
+// independent of the reduction order.
+
+#include "common.h"
+
+namespace sdv {
+
+namespace {
+
+constexpr int kAcceptThreads = 256;
+constexpr int kAcceptPerThread = 16;
+constexpr int kAcceptChunk = kAcceptThreads * kAcceptPerThread;
+
+struct AcceptArgs {
+  const float* logits;  // [k][V]
+  const float* noise;   // [k][V] or null
+  float inv_temp;
+  const int32_t* drafts;  // [k - 1]
+  int k, V, eos, chunks;
+  int32_t* tokens;    // [k]
+  int32_t* accepted;  // [1]
+  uint64_t* keys;     // workspace [k][chunks]
+};
+
+__device__ __forceinline__ uint64_t score_key(float z, int i) {
+  const float c = z + 0.0f;  // -0 + +0 = +0 under round-to-nearest
+  const uint32_t b = __float_as_uint(c);
+  const uint32_t hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (c != c) ? 0ull : (((uint64_t)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(x, off);
+    x = o > x ? o : x;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kAcceptThreads) void accept_partial_kernel(AcceptArgs a) {
+  __shared__ uint64_t s_best[kAcceptThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int V = a.V;
+  const float* lrow = a.logits + (size_t)r * V;
+  const int base = c * kAcceptChunk + tid;
+  float z[kAcceptPerThread];
+#pragma unroll
+  for (int j = 0; j < kAcceptPerThread; ++j) z[j] = lrow[min(base + kAcceptThreads * j, V - 1)];
+  if (a.noise) {
+    const float* nrow = a.noise + (size_t)r * V;
+    float g[kAcceptPerThread];
+#pragma unroll
+    for (int j = 0; j < kAcceptPerThread; ++j) g[j] = nrow[min(base + kAcceptThreads * j, V - 1)];
+#pragma unroll
+    for (int j = 0; j < kAcceptPerThread; ++j) z[j] = __fadd_rn(__fmul_rn(z[j], a.inv_temp), g[j]);
+  }
+  uint64_t best = 0;
+#pragma unroll
+  for (int j = 0; j < kAcceptPerThread; ++j) {
+    const int i = base + kAcceptThreads * j;
+    const uint64_t key = i < V ? score_key(z[j], i) : 0ull;
+    best = key > best ? key : best;
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) s_best[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t m = s_best[0];
+#pragma unroll
+    for (int w = 1; w < kAcceptThreads / 64; ++w) m = s_best[w] > m ? s_best[w] : m;
+    a.keys[(size_t)r * a.chunks + c] = m;
+  }
+}
+
+__global__ __launch_bounds__(64 * SDV_MAX_ROWS) void accept_final_kernel(AcceptArgs a) {
+  __shared__ int32_t s_tok[SDV_MAX_ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave < a.k) {
+    uint64_t best = 0;
+    for (int c = lane; c < a.chunks; c += 64) {
+      const uint64_t key = a.keys[(size_t)wave * a.chunks + c];
+      best = key > best ? key : best;
+    }
+    best = wave_max_u64(best);
+    const int tok = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : -1;
+    if (lane == 0) {
+      a.tokens[wave] = tok;
+      s_tok[wave] = tok;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int t = 0; t + 1 < a.k; ++t) {
+      const int d = a.drafts[t];
+      if (d == s_tok[t] && (a.eos < 0 || d != a.eos)) {
+        ++n;
+      } else {
+        break;
+      }
+    }
+    *a.accepted = n;
+  }
+}
+
+}  // namespace
+
+int accept_chunks(int V) { return (V + kAcceptChunk - 1) / kAcceptChunk; }
+
+size_t accept_workspace_bytes(int k, int V) { return (size_t)k * accept_chunks(V) * 8; }
+
+hipError_t accept_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts, int k,
+                         int V, int eos, int32_t* tokens, int32_t* accepted, void* workspace, hipStream_t st) {
+  AcceptArgs a;
+  a.logits = logits;
+  a.noise = noise;
+  a.inv_temp = inv_temp;
+  a.drafts = drafts;
+  a.k = k;
+  a.V = V;
+  a.eos = eos;
+  a.chunks = accept_chunks(V);
+  a.tokens = tokens;
+  a.accepted = accepted;
+  a.keys = static_cast<uint64_t*>(workspace);
+  hipLaunchKernelGGL(accept_partial_kernel, dim3(a.chunks, k), dim3(kAcceptThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(64 * k), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sdv

@@ -33,6 +33,9 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
                               const void* x, const int32_t* union_ids, const int32_t* n_union,
                               const int32_t* pair_off, const int32_t* pair_row, const int32_t* pair_slot, int k,
                               int topk, float* partial, hipStream_t st);
+size_t accept_workspace_bytes(int k, int V);
+hipError_t accept_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts, int k,
+                         int V, int eos, int32_t* tokens, int32_t* accepted, void* workspace, hipStream_t st);
 hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
                       const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
                       float* y, float* const* snaps, hipStream_t st);
@@ -494,6 +497,41 @@ int sdv_gdn_rollback_copy(float* dst, const float* S_in, float* const* snaps, in
   if (overlap(a, b)) return fail(SDV_EALIAS, "dst partially overlaps the selected state");
   return hip_status(hipMemcpyAsync(dst, src, state_elems * 4, hipMemcpyDeviceToDevice, (hipStream_t)stream),
                     "sdv_gdn_rollback_copy");
+}
+
+size_t sdv_verify_accept_workspace_bytes(int k, int V) {
+  if (k < 1 || k > SDV_MAX_ROWS || V < 1 || V > (1 << 30)) return 0;
+  return sdv::accept_workspace_bytes(k, V);
+}
+
+int sdv_verify_accept_k(const float* logits, const float* noise, float inv_temp, const int32_t* drafts, int k,
+                        int V, int eos, int32_t* tokens, int32_t* accepted, void* workspace,
+                        size_t workspace_bytes, sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (V < 1 || V > (1 << 30)) return fail(SDV_ERANGE, "V=%d outside 1..2^30", V);
+  if ((st = check_ptr(logits, "logits"))) return st;
+  if (noise) {
+    if ((st = check_ptr(noise, "noise"))) return st;
+    if (!(inv_temp > 0.0f && inv_temp <= 3.4e38f))
+      return fail(SDV_ERANGE, "inv_temp=%g must be finite and positive", (double)inv_temp);
+  }
+  if (k > 1 && (st = check_ptr(drafts, "drafts"))) return st;
+  if ((st = check_ptr(tokens, "tokens"))) return st;
+  if ((st = check_ptr(accepted, "accepted"))) return st;
+  if ((st = check_ptr(workspace, "workspace"))) return st;
+  const size_t need = sdv::accept_workspace_bytes(k, V);
+  if (workspace_bytes < need)
+    return fail(SDV_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t lbytes = (size_t)k * V * 4;
+  Range outs[] = {{tokens, (size_t)k * 4, "tokens"}, {accepted, 4, "accepted"}, {workspace, need, "workspace"}};
+  Range ins[] = {{logits, lbytes, "logits"},
+                 {noise, noise ? lbytes : 0, "noise"},
+                 {drafts, k > 1 ? (size_t)(k - 1) * 4 : 0, "drafts"}};
+  if ((st = check_alias(outs, 3, ins, 3))) return st;
+  return hip_status(sdv::accept_launch(logits, noise, inv_temp, k > 1 ? drafts : nullptr, k, V, eos, tokens,
+                                       accepted, workspace, (hipStream_t)stream),
+                    "sdv_verify_accept_k launch");
 }
 
 }  // extern "C"

@@ -327,6 +327,47 @@ def gdn_rollback_copy(dst, S_in, snaps, j):
     return dst
 
 
+def verify_accept_workspace(k, V, device):
+    """Workspace for verify_accept_k (uint8 device buffer)."""
+    n = lib().sdv_verify_accept_workspace_bytes(k, V)
+    if n == 0:
+        raise ValueError(f"no acceptance workspace for k={k}, V={V}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _accept_args(logits, drafts, noise, inv_temp, eos, tokens, accepted, workspace):
+    k, V = logits.shape
+    dev = logits.device
+    pn = _need(noise, "noise", torch.float32, k * V, dev) if noise is not None else None
+    pd = _need(drafts, "drafts", torch.int32, k - 1, dev) if k > 1 else None
+    return [_need(logits, "logits", torch.float32, k * V, dev), pn, ctypes.c_float(inv_temp), pd, k, V, eos,
+            _need(tokens, "tokens", torch.int32, k, dev), _need(accepted, "accepted", torch.int32, 1, dev),
+            _need(workspace, "workspace", torch.uint8, device=dev), workspace.numel(), _stream(tokens)]
+
+
+def verify_accept_k(logits, drafts, noise=None, inv_temp=1.0, eos=-1, tokens=None, accepted=None, workspace=None):
+    """Acceptance of a verified block: logits fp32 [k, V], drafts int32 [k-1]
+    (the tokens of rows 1..k-1), optional Gumbel noise fp32 [k, V].  Returns
+    (tokens int32 [k], accepted int32 [1]) on the device: the token sampled
+    from each row and the number of leading drafts accepted."""
+    k, V = logits.shape
+    dev = logits.device
+    if tokens is None:
+        tokens = torch.empty(k, dtype=torch.int32, device=dev)
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = verify_accept_workspace(k, V, dev)
+    check(lib().sdv_verify_accept_k(*_accept_args(logits, drafts, noise, inv_temp, eos, tokens, accepted,
+                                                  workspace)))
+    return tokens, accepted
+
+
+def bind_verify_accept_k(logits, drafts, tokens, accepted, workspace, noise=None, inv_temp=1.0, eos=-1):
+    return BoundCall("sdv_verify_accept_k",
+                     _accept_args(logits, drafts, noise, inv_temp, eos, tokens, accepted, workspace))
+
+
 class BoundCall:
     """A library call with its arguments marshalled once (fixed buffers).
 

@@ -145,3 +145,41 @@ class GdnLayer:
 
 
 __all__ = ["MoeLayer", "GdnLayer", "MODE_PLAIN", "MODE_GATEUP_SWIGLU", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
+
+
+class VerifyCycle:
+    """Closes a verify step: the acceptance of the block on the device, then
+    every GDN layer rolled back to the accepted prefix by selecting its
+    snapshot (Red Lite dev45, "Acceptance" and "What it is": a rejected draft
+    is undone by swapping the state pointers with the snapshots).
+
+    The accepted count is read back to the host, which holds the slot choice
+    of each layer's state pool."""
+
+    def __init__(self, gdn_layers, k, vocab, device, eos=-1):
+        self.layers = list(gdn_layers)
+        self.k, self.vocab, self.eos = k, vocab, eos
+        self.tokens = torch.empty(k, dtype=torch.int32, device=device)
+        self.accepted = torch.empty(1, dtype=torch.int32, device=device)
+        self.workspace = ops.verify_accept_workspace(k, vocab, device)
+
+    def accept(self, logits, drafts, noise=None, inv_temp=1.0):
+        """Device acceptance only: (tokens, accepted) device tensors."""
+        return ops.verify_accept_k(logits, drafts, noise, inv_temp, self.eos, self.tokens, self.accepted,
+                                   self.workspace)
+
+    def bind(self, logits, drafts, noise=None, inv_temp=1.0):
+        return ops.bind_verify_accept_k(logits, drafts, self.tokens, self.accepted, self.workspace, noise, inv_temp,
+                                        self.eos)
+
+    def __call__(self, logits, drafts, noise=None, inv_temp=1.0):
+        """Accept, roll every layer back to the accepted prefix, and return
+        (n accepted drafts, emitted tokens: the accepted drafts, then the
+        token sampled after them)."""
+        self.accept(logits, drafts, noise, inv_temp)
+        n = int(self.accepted.item())
+        for layer in self.layers:
+            layer.rollback(n + 1)
+        toks = self.tokens.cpu().tolist()
+        accepted_drafts = drafts[:n].cpu().tolist() if n > 0 else []
+        return n, accepted_drafts + [toks[n]]

@@ -105,8 +105,8 @@ def verify_block(cfg_id, step, rows, vocab, accepted=None, margin=4.0, eos=-1):
     of one verify block, with ``accepted`` (default ~ U{0..rows-1}) drafts
     planted to be accepted under greedy sampling: for t < accepted, row t's
     logit of drafts[t] is set ``margin`` above the row's maximum; when
-    accepted < rows - 1, row ``accepted`` gets its raised token on a token
-    other than drafts[accepted].  Drafts never equal ``eos`` unless planted
+    accepted < rows - 1 (and vocab > 1), row ``accepted`` gets its raised
+    token on a token other than drafts[accepted].  Drafts never equal ``eos`` unless planted
     by the caller.  Returns (logits, drafts, accepted)."""
     rng = _rng(cfg_id, T_VLOGITS, step)
     logits = rng.standard_normal((rows, vocab), dtype=np.float32)
@@ -118,7 +118,7 @@ def verify_block(cfg_id, step, rows, vocab, accepted=None, margin=4.0, eos=-1):
         accepted = int(drng.integers(0, rows))
     for t in range(min(accepted, rows - 1)):
         logits[t, drafts[t]] = logits[t].max() + np.float32(margin)
-    if accepted < rows - 1:
+    if accepted < rows - 1 and vocab > 1:
         other = (int(drafts[accepted]) + 1 + int(drng.integers(0, vocab - 1))) % vocab
         if other == drafts[accepted]:
             other = (other + 1) % vocab

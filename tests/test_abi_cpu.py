@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 18
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -283,3 +283,43 @@ def test_rollback_copy_validation(lib):
     assert f(P + 0x900000, P, snaps, 2, 3, 1024, None) == L.SDV_ERANGE
     assert f(P + 0x900000, P, snaps, 2, 1, 0, None) == L.SDV_EINVAL
     assert f(0, P, snaps, 2, 1, 1024, None) == L.SDV_EINVAL
+
+
+def test_accept_workspace_bytes(lib):
+    assert lib.sdv_verify_accept_workspace_bytes(9, 248320) == 9 * 61 * 8
+    assert lib.sdv_verify_accept_workspace_bytes(1, 1) == 8
+    assert lib.sdv_verify_accept_workspace_bytes(2, 4097) == 2 * 2 * 8
+    for k, V in [(0, 10), (10, 10), (2, 0), (2, -5)]:
+        assert lib.sdv_verify_accept_workspace_bytes(k, V) == 0
+
+
+def test_accept_validation(lib):
+    f = lib.sdv_verify_accept_k
+    logits, noise, drafts = P, P + 0x1000000, P + 0x2000000
+    tok, acc, ws = P + 0x2100000, P + 0x2200000, P + 0x2300000
+    ok = dict(logits=logits, noise=None, inv=1.0, drafts=drafts, k=3, V=1000, eos=-1, tok=tok, acc=acc,
+              ws=ws, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["logits"], a["noise"], a["inv"], a["drafts"], a["k"], a["V"], a["eos"], a["tok"], a["acc"],
+                 a["ws"], a["wsb"], None)
+
+    assert call(k=0) == L.SDV_EWIDTH
+    assert call(k=10) == L.SDV_EWIDTH
+    assert call(V=0) == L.SDV_ERANGE
+    assert call(V=(1 << 30) + 1) == L.SDV_ERANGE
+    assert call(logits=None) == L.SDV_EINVAL
+    assert call(logits=P + 4) == L.SDV_EINVAL                       # misaligned
+    assert call(noise=noise, inv=0.0) == L.SDV_ERANGE
+    assert call(noise=noise, inv=float("inf")) == L.SDV_ERANGE
+    assert call(noise=noise, inv=float("nan")) == L.SDV_ERANGE
+    assert call(drafts=None) == L.SDV_EINVAL
+    assert call(tok=None) == L.SDV_EINVAL
+    assert call(acc=None) == L.SDV_EINVAL
+    assert call(ws=None) == L.SDV_EINVAL
+    assert call(wsb=3 * 8 - 1) == L.SDV_EINVAL
+    assert "workspace" in lib.sdv_last_error().decode()
+    assert call(tok=logits + 64) == L.SDV_EALIAS                    # tokens over logits
+    assert call(ws=tok) == L.SDV_EALIAS                             # workspace over tokens
+    assert call(acc=noise + 16, noise=noise) == L.SDV_EALIAS         # accepted over noise
