@@ -38,6 +38,7 @@ DOMINANT = "experts"
 # layer of each timed step: each event pair adds a few microseconds of idle
 # time to the stream, so sampling keeps the step time close to untimed runs
 SAMPLE_EVERY = 4
+ACCEPT_BLOCKS = 8  # distinct verify blocks (logits, drafts) cycled through the steps
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -188,14 +189,26 @@ class Workload:
             d = {n: sdev.upload_f32(v, dev) for n, v in gi.items()}
             gl = pipeline.GdnLayer(S0, k).bind(d["q"], d["k"], d["v"], d["g"], d["beta"])
             self.gdn[l] = (gl, d)
+        # acceptance of the block: next-token logits over the vocabulary with a
+        # planted accepted-draft count per step (greedy), and the accepted
+        # prefix n + 1 the GDN layers roll back to
+        self.vocab = cfg.extra["vocab"]
+        self.cycle = pipeline.VerifyCycle([gl for gl, _ in self.gdn.values()], k, self.vocab, dev)
+        self.blocks = []
+        for s in range(ACCEPT_BLOCKS):
+            lg, dr, n = synth.verify_block(cfg.cid, s, k, self.vocab)
+            lg_d = sdev.upload_f32(lg, dev)
+            dr_d = torch.from_numpy(dr).to(dev)
+            self.blocks.append((self.cycle.bind(lg_d, dr_d), n, lg_d, dr_d))
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
         self.bank_bytes = self.layers * (self.E + 1) * (q4_bytes(2 * self.I, self.H) + q4_bytes(self.H, self.I))
 
-    def step(self, s, js, timer=None, events=None, per_kernel=None):
-        """One verify step over all layers, then rollback of every GDN layer.
-        With ``events``, the dominant kernel of every layer is bracketed by
-        timer events; with ``per_kernel``, every launch is."""
+    def step(self, s, timer=None, events=None, per_kernel=None):
+        """One verify step over all layers, the acceptance of the block, then
+        rollback of every GDN layer to the accepted prefix.  With ``events``,
+        the dominant kernel of every layer is bracketed by timer events; with
+        ``per_kernel``, every launch is."""
         def run(name, l, call):
             if per_kernel is not None or (events is not None and name == DOMINANT and l % SAMPLE_EVERY == 0):
                 a = timer.start()
@@ -211,15 +224,26 @@ class Workload:
                 run("gdn", l, g[0].run_bound)
             for name, call in self.calls[l]:
                 run(name, l, call)
-        j = js[s % len(js)]
+        accept, n, _, _ = self.blocks[s % len(self.blocks)]
+        run("accept", self.layers, accept)
         for gl, _ in self.gdn.values():
-            gl.rollback(j)
+            gl.rollback(n + 1)
+
+    def check_acceptance(self):
+        """Every block's device acceptance equals its planted count (outside timing)."""
+        for call, n, _, _ in self.blocks:
+            call()
+            got = int(self.cycle.accepted.item())
+            if got != n:
+                raise RuntimeError(f"acceptance returned {got} drafts, planted {n}")
 
     def unions(self):
         return [int(layer.route.n_union.item()) for layer, *_ in self.moe]
 
     def kernel_bytes(self, name, l, unions):
         k, H, I, topk, E = self.k, self.H, self.I, self.topk, self.E
+        if name == "accept":  # logits once, drafts, tokens and the count
+            return k * self.vocab * 4 + (k - 1) * 4 + k * 4 + 4
         U = unions[l]
         if name == "route":
             return k * E * 4 + k * topk * 4 * 5 + 8
@@ -260,7 +284,7 @@ class Workload:
                 total += self.kernel_bytes(name, l, unions)
             if l in self.gdn:
                 total += self.kernel_bytes("gdn", l, unions)
-        return total
+        return total + self.kernel_bytes("accept", self.layers, unions)
 
 
 TRAFFIC_SUMMARY = "traffic_moe_experts_flashnext_k9.md"
@@ -332,12 +356,16 @@ def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
             n_gdn += 1
         if t_moe + t_gdn >= min_seconds:
             break
-    step = cfg.layers * t_moe / n_moe + len(cfg.gdn_layers) * t_gdn / n_gdn
+    lg, dr, _ = synth.verify_block(cfg.cid, 0, k, cfg.extra["vocab"])
+    t0 = time.perf_counter()
+    oracle.verify_cycle(lg, dr)
+    t_acc = time.perf_counter() - t0
+    step = cfg.layers * t_moe / n_moe + len(cfg.gdn_layers) * t_gdn / n_gdn + t_acc
     return {"value": k / step, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": (f"flashnext_k9 layers 0..{n_moe - 1}: {n_moe} MoE layers (union experts {unions}, "
                        f"{t_moe:.1f} s) and {n_gdn} GDN layers ({t_gdn:.2f} s) of the oracle (numpy fp64, "
-                       f"{t_moe + t_gdn:.1f} s in all), scaled to 48 MoE + 36 GDN layers per step "
-                       f"({step:.1f} s per 9-row step)"),
+                       f"{t_moe + t_gdn:.1f} s in all), scaled to 48 MoE + 36 GDN layers per step, plus one "
+                       f"acceptance of the block ({t_acc:.2f} s) ({step:.1f} s per 9-row step)"),
             "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
 
 
@@ -411,15 +439,13 @@ def main():
     wl = Workload(dev, k)
     log(f"workload ready in {wl.setup_s:.1f} s: {wl.bank_bytes / 1e9:.1f} GB of Q4 banks, "
         f"{len(wl.gdn)} GDN layers")
-    import synth
-    js = [synth.accepted_prefix(wl.cfg.cid, s, k) for s in range(max(64, args.steps + args.warmup))]
-
+    wl.check_acceptance()
     for s in range(args.warmup):
-        wl.step(s, js)
+        wl.step(s)
     torch.cuda.synchronize()
     unions = wl.unions()
 
-    per_step = len(wl.calls[0]) * wl.layers + len(wl.gdn)
+    per_step = len(wl.calls[0]) * wl.layers + len(wl.gdn) + 1
     timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1 + 4)
     log(f"timing events on the launch stream (HIP runtime {timer.path})")
     events = []
@@ -427,7 +453,7 @@ def main():
     wall0 = time.perf_counter()
     t_start = timer.start()
     for s in range(args.steps):
-        wl.step(args.warmup + s, js, timer=timer, events=events)
+        wl.step(args.warmup + s, timer=timer, events=events)
     t_end = timer.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -446,7 +472,7 @@ def main():
     breakdown = None
     if not args.no_breakdown:
         per = []
-        wl.step(args.warmup + args.steps, js, timer=timer, per_kernel=per)
+        wl.step(args.warmup + args.steps, timer=timer, per_kernel=per)
         torch.cuda.synchronize()
         agg = {}
         for name, l, a, b in per:
@@ -486,7 +512,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "flashnext_k9", "rows": k, "layers": wl.layers, "gdn_layers": len(wl.gdn),
                    "experts": wl.E, "topk": wl.topk, "hidden": wl.H, "inter": wl.I, "shared_expert": True,
-                   "gdn_heads": [wl.gs.hv, wl.gs.hk, wl.gs.dk], "mean_union": round(sum(unions) / len(unions), 2),
+                   "gdn_heads": [wl.gs.hv, wl.gs.hk, wl.gs.dk], "vocab": wl.vocab,
+                   "mean_union": round(sum(unions) / len(unions), 2),
                    "bytes_per_step": step_bytes},
         "hbm_gbs_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac_step": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),

@@ -70,7 +70,9 @@ C4 = Config(FLASH, "flashnext_k9", widths=(9,),
             moe=MoeShape(hidden=2560, experts=512, inter=640, topk=10, mode="sigmoid",
                          renorm=True, shared=True),
             gdn=GdnShape(hv=48, hk=16, dk=128, dv=128), layers=48,
-            gdn_layers=tuple(l for l in range(48) if l % 4 != 3))
+            gdn_layers=tuple(l for l in range(48) if l % 4 != 3),
+            # Flash-Next plan, "1. Target model and identity": vocab 248,320 (padded)
+            extra={"vocab": 248320})
 
 ALL = (C0, C1, C2, C3, C4)
 
