@@ -26,6 +26,10 @@ definition written out.  Sources, by page and section:
 * Red Lite dev45, "Acceptance": a draft is accepted when the token sampled
   from the previous row's logits equals it (exact with any sampler); dev45b:
   a draft whose sampled token is the end-of-answer token is rejected.
+* Flash-Next plan, "2.1 Gated DeltaNet" and "5.1 Gated DeltaNet": the
+  preparation (causal depthwise conv1d of kernel 4 over the q/k/v channels
+  with a carried tail, per-head L2 norm of q and k, g from A_log and dt_bias
+  by softplus and exp, beta = sigmoid(b)) and the gated RMSNorm output.
 * Flash-Next plan (QWEN38FLASH.md): "2.1 Gated DeltaNet" (decay, kv_mem,
   delta, rank-1 update, readout on fp32 [Hv, Dv, Dk]), "2.3 MoE" (routed +
   shared experts, SwiGLU, gate+up concatenated), "3.1 Overlap" (per-head
@@ -41,8 +45,9 @@ in the function's docstring.
 """
 
 from .ref import (bf16_to_f64, unpack_q4, dequant, qmv, route, union_pairs, silu, swiglu,
-                  combine, moe_verify, gdn_verify, rollback, sample_tokens, accept, verify_cycle)
+                  combine, moe_verify, gdn_verify, rollback, sample_tokens, accept, verify_cycle,
+                  softplus, gdn_prepare, gdn_gated_norm, CONV_TAPS)
 
 __all__ = ["bf16_to_f64", "unpack_q4", "dequant", "qmv", "route", "union_pairs", "silu",
            "swiglu", "combine", "moe_verify", "gdn_verify", "rollback", "sample_tokens", "accept",
-           "verify_cycle"]
+           "verify_cycle", "softplus", "gdn_prepare", "gdn_gated_norm", "CONV_TAPS"]

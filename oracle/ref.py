@@ -338,3 +338,76 @@ def verify_cycle(logits, drafts, eos=-1, noise=None, inv_temp=1.0):
     n = accept(tokens, drafts, eos)
     emitted = [int(d) for d in drafts[:n]] + [int(tokens[n])]
     return {"tokens": tokens, "accepted": n, "prefix": n + 1, "emitted": emitted}
+
+
+# ---------------------------------------------------------------------------
+# GDN preparation and tail (Flash-Next plan, "2.1 Gated DeltaNet": a short
+# causal depthwise conv1d over the concatenated q/k/v channels, per-head L2
+# normalisation of q and k, the decay gate from A_log and dt_bias via
+# softplus and exp, beta = sigmoid(b), and the gated RMSNorm output
+# rmsnorm(y) * act(gate); persistent conv tail = the last kernel - 1 input
+# columns; "5.1 Gated DeltaNet": kernel size 4, sigmoid gate for this model)
+# ---------------------------------------------------------------------------
+
+CONV_TAPS = 4
+
+
+def softplus(x):
+    """log(1 + e^x), written stably: max(x, 0) + log1p(e^-|x|)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def gdn_prepare(qkv, hist, conv_w, a, b, A_log, dt_bias, hk, hv, dk, dv, act="none", eps=1e-6):
+    """The k rows' inputs of the recurrence from their projections.
+
+    qkv [k, C] with C = 2 hk dk + hv dv, channels [q | k | v] (q, k head-major);
+    hist [CONV_TAPS - 1, C], the inputs before row 0 (oldest first); conv_w
+    [C, CONV_TAPS], tap i applied to the input CONV_TAPS - 1 - i steps before
+    the current one (tap 3 to the current input): with X = [hist; qkv]
+    (k + 3 columns), conv[t, c] = sum_i conv_w[c, i] * X[t + i, c].  act "silu" applies silu
+    after the conv, "none" nothing (the page names no activation; reading).
+    q and k are divided per (row, head) by sqrt(sum of squares + eps) (eps is
+    our reading).  g[t, h] = exp(-exp(A_log[h]) * softplus(a[t, h] +
+    dt_bias[h])), beta[t, h] = sigmoid(b[t, h]).  Returns q [k, hk, dk], k,
+    v [k, hv, dv], g, beta [k, hv] and the window X [k + 3, C]; the conv
+    history after an accepted prefix of j rows is X[j : j + 3]."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    rows, C = qkv.shape
+    assert C == 2 * hk * dk + hv * dv
+    X = np.concatenate([np.asarray(hist, dtype=np.float64), qkv], axis=0)
+    w = np.asarray(conv_w, dtype=np.float64)
+    conv = np.zeros((rows, C))
+    for t in range(rows):
+        for i in range(CONV_TAPS):
+            conv[t] = conv[t] + w[:, i] * X[t + i]
+    if act == "silu":
+        conv = silu(conv)
+    elif act != "none":
+        raise ValueError(act)
+    q = conv[:, :hk * dk].reshape(rows, hk, dk)
+    k = conv[:, hk * dk:2 * hk * dk].reshape(rows, hk, dk)
+    v = conv[:, 2 * hk * dk:].reshape(rows, hv, dv)
+    q = q / np.sqrt((q * q).sum(axis=-1, keepdims=True) + eps)
+    k = k / np.sqrt((k * k).sum(axis=-1, keepdims=True) + eps)
+    g = np.exp(-np.exp(np.asarray(A_log, dtype=np.float64))[None, :] *
+               softplus(np.asarray(a, dtype=np.float64) + np.asarray(dt_bias, dtype=np.float64)[None, :]))
+    beta = 1.0 / (1.0 + np.exp(-np.asarray(b, dtype=np.float64)))
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "window": X}
+
+
+def gdn_gated_norm(y, z, w, act="sigmoid", eps=1e-6):
+    """The GDN output: per (row, v head), rmsnorm over Dv times the weight w
+    [Dv], times act(z): y / sqrt(mean(y^2) + eps) * w * act(z).  act
+    "sigmoid" (the page's note for this model) or "silu"; eps is our
+    reading."""
+    y = np.asarray(y, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    n = y / np.sqrt((y * y).mean(axis=-1, keepdims=True) + eps)
+    if act == "sigmoid":
+        gate = 1.0 / (1.0 + np.exp(-z))
+    elif act == "silu":
+        gate = silu(z)
+    else:
+        raise ValueError(act)
+    return n * np.asarray(w, dtype=np.float64) * gate

@@ -22,11 +22,13 @@ from .counter import (GAMMA, SEED, derive_key, mix64, rand64, bf16_bits_from_f32
                       q4_code_words, q4_affine_bf16, q4_rows)
 from . import configs
 from .inputs import (BankKeys, bank_keys, activations, dense_weight, moe_layer_inputs, gdn_layer_inputs,
-                     gdn_state, accepted_prefix, integer_exact_weight, verify_block, gumbel_noise)
+                     gdn_state, accepted_prefix, integer_exact_weight, verify_block, gumbel_noise,
+                     gdn_raw_inputs)
 
 __all__ = [
     "GAMMA", "SEED", "derive_key", "mix64", "rand64", "bf16_bits_from_f32",
     "q4_code_words", "q4_affine_bf16", "q4_rows", "configs", "BankKeys", "bank_keys", "activations",
     "dense_weight", "moe_layer_inputs", "gdn_layer_inputs", "gdn_state", "verify_block", "gumbel_noise",
+    "gdn_raw_inputs",
     "accepted_prefix", "integer_exact_weight",
 ]

@@ -8,7 +8,10 @@ head); v ~ N(0,1); beta = sigmoid(N(0,1)); g = exp(-softplus(N(0,1)));
 accepted prefix j ~ U{0..k}.  Verify-block next-token logits ~ N(0,1) fp32
 over the vocabulary, with a planted number of accepted drafts ~ U{0..k-1}
 (the planted tokens are raised a fixed margin above their row's maximum);
-Gumbel noise g = -log(-log(u)), u ~ U(0,1), for sampled acceptance.
+Gumbel noise g = -log(-log(u)), u ~ U(0,1), for sampled acceptance.  GDN
+preparation inputs: projections qkv ~ N(0,1), conv history ~ N(0,1), conv
+weights ~ U(-0.5, 0.5), a, b ~ N(0,1), A_log, dt_bias ~ U(-1, 1); output
+gate z ~ N(0,1) and norm weight ~ U(0.5, 1.5).
 """
 
 from collections import namedtuple
@@ -24,6 +27,7 @@ DENSE_W, GATEUP, DOWN, SHARED_GATEUP, SHARED_DOWN = 0, 1, 2, 3, 4
 # tensor ids (part of the numpy seeds)
 T_X, T_LOGITS, T_Z, T_S, T_Q, T_K, T_V, T_G, T_BETA, T_J = 10, 11, 12, 20, 21, 22, 23, 24, 25, 30
 T_VLOGITS, T_GUMBEL, T_DRAFTS = 40, 41, 42
+T_QKV, T_HIST, T_CONVW, T_A, T_B, T_ALOG, T_DTB, T_GATEZ, T_NORMW = 50, 51, 52, 53, 54, 55, 56, 57, 58
 
 
 def bank_keys(cfg_id, kind, layer):
@@ -131,3 +135,24 @@ def gumbel_noise(cfg_id, step, rows, vocab):
     u = _rng(cfg_id, T_GUMBEL, step).random((rows, vocab))
     u = np.clip(u, 2.0 ** -53, 1.0 - 2.0 ** -53)
     return (-np.log(-np.log(u))).astype(np.float32)
+
+
+def gdn_raw_inputs(cfg_id, layer, rows, hv, hk, dk, dv, step=0):
+    """Projections of one GDN layer before the preparation: qkv [rows, C]
+    (C = 2 hk dk + hv dv, channels q | k | v), the conv history [3, C], the
+    depthwise conv weights [C, 4], a, b [rows, hv], A_log, dt_bias [hv], the
+    output gate z [rows, hv, dv] and the output norm weight [dv] (fp32)."""
+    C = 2 * hk * dk + hv * dv
+    f = np.float32
+    out = {
+        "qkv": _rng(cfg_id, T_QKV, layer, step).standard_normal((rows, C), dtype=f),
+        "hist": _rng(cfg_id, T_HIST, layer).standard_normal((3, C), dtype=f),
+        "conv_w": _rng(cfg_id, T_CONVW, layer).uniform(-0.5, 0.5, (C, 4)).astype(f),
+        "a": _rng(cfg_id, T_A, layer, step).standard_normal((rows, hv), dtype=f),
+        "b": _rng(cfg_id, T_B, layer, step).standard_normal((rows, hv), dtype=f),
+        "A_log": _rng(cfg_id, T_ALOG, layer).uniform(-1.0, 1.0, hv).astype(f),
+        "dt_bias": _rng(cfg_id, T_DTB, layer).uniform(-1.0, 1.0, hv).astype(f),
+        "z": _rng(cfg_id, T_GATEZ, layer, step).standard_normal((rows, hv, dv), dtype=f),
+        "norm_w": _rng(cfg_id, T_NORMW, layer).uniform(0.5, 1.5, dv).astype(f),
+    }
+    return out

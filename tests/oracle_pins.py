@@ -578,6 +578,129 @@ def check_verify_cycle_rollback(ref):
         assert np.array_equal(st, sj[-1])
 
 
+# ---------------------------------------------------------------------------
+# GDN preparation and tail
+# ---------------------------------------------------------------------------
+
+def _prep(ref, raw, hk, hv, dk, dv, **kw):
+    return ref.gdn_prepare(raw["qkv"], raw["hist"], raw["conv_w"], raw["a"], raw["b"], raw["A_log"],
+                           raw["dt_bias"], hk, hv, dk, dv, **kw)
+
+
+def check_conv_is_convolution(ref):
+    """P17: the v channels (no norm) of the preparation are numpy's 'valid'
+    convolution of [history; inputs] with the reversed taps."""
+    hk, hv, dk, dv, rows = 1, 2, 4, 3, 5
+    raw = synth.gdn_raw_inputs(14, 0, rows, hv, hk, dk, dv)
+    out = _prep(ref, raw, hk, hv, dk, dv)
+    X = np.concatenate([raw["hist"], raw["qkv"]]).astype(np.float64)
+    v = out["v"].reshape(rows, hv * dv)
+    for j in range(hv * dv):
+        c = 2 * hk * dk + j
+        expect = np.convolve(X[:, c], raw["conv_w"][c, ::-1].astype(np.float64), mode="valid")
+        assert np.allclose(v[:, j], expect, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(out["window"], X)
+
+
+def check_conv_alignment(ref):
+    """P17: a tap on the current input passes the rows through; a tap three
+    steps back passes the history, then the rows, through; with act silu the
+    pass-through is x / (1 + e^-x)."""
+    hk, hv, dk, dv, rows = 1, 1, 2, 2, 5
+    raw = synth.gdn_raw_inputs(15, 0, rows, hv, hk, dk, dv)
+    C = raw["qkv"].shape[1]
+    for tap, shift in ((3, 0), (0, 3), (2, 1)):
+        w = np.zeros((C, 4), dtype=np.float32)
+        w[:, tap] = 1.0
+        out = ref.gdn_prepare(raw["qkv"], raw["hist"], w, raw["a"], raw["b"], raw["A_log"], raw["dt_bias"],
+                              hk, hv, dk, dv)
+        X = np.concatenate([raw["hist"], raw["qkv"]]).astype(np.float64)
+        assert np.array_equal(out["v"].reshape(rows, -1), X[3 - shift:3 - shift + rows, 2 * hk * dk:])
+        act = ref.gdn_prepare(raw["qkv"], raw["hist"], w, raw["a"], raw["b"], raw["A_log"], raw["dt_bias"],
+                              hk, hv, dk, dv, act="silu")
+        xs = X[3 - shift:3 - shift + rows, 2 * hk * dk:]
+        assert np.allclose(act["v"].reshape(rows, -1), xs / (1.0 + np.exp(-xs)), rtol=1e-14)
+
+
+def check_conv_history_chain(ref):
+    """P18: continuing from the history after an accepted prefix j
+    (window[j:j+3]) gives the later rows exactly as one call over all rows."""
+    hk, hv, dk, dv, rows = 1, 2, 4, 4, 7
+    raw = synth.gdn_raw_inputs(16, 0, rows, hv, hk, dk, dv)
+    full = _prep(ref, raw, hk, hv, dk, dv, act="silu")
+    for j in range(rows + 1):
+        part = dict(raw)
+        part["qkv"] = raw["qkv"][j:]
+        part["hist"] = full["window"][j:j + 3]
+        part["a"], part["b"] = raw["a"][j:], raw["b"][j:]
+        if j == rows:
+            assert np.array_equal(full["window"][rows:rows + 3], np.concatenate([raw["hist"], raw["qkv"]])[-3:])
+            continue
+        out = _prep(ref, part, hk, hv, dk, dv, act="silu")
+        for n in ("q", "k", "v", "g", "beta"):
+            assert np.array_equal(out[n], full[n][j:]), (n, j)
+
+
+def check_qk_l2_norm(ref):
+    """P19: with eps = 0 every (row, head) of q and k has unit norm and the
+    direction of the conv output; eps enters as sqrt(sum + eps)."""
+    hk, hv, dk, dv, rows = 2, 2, 8, 2, 3
+    raw = synth.gdn_raw_inputs(17, 0, rows, hv, hk, dk, dv)
+    w = np.zeros((raw["qkv"].shape[1], 4), dtype=np.float32)
+    w[:, 3] = 1.0
+    raw["conv_w"] = w
+    out = _prep(ref, raw, hk, hv, dk, dv, eps=0.0)
+    for n, off in (("q", 0), ("k", hk * dk)):
+        t = out[n]
+        assert np.allclose((t * t).sum(-1), 1.0, rtol=1e-14)
+        src = raw["qkv"][:, off:off + hk * dk].reshape(rows, hk, dk).astype(np.float64)
+        assert np.allclose(t * np.linalg.norm(src, axis=-1, keepdims=True), src, rtol=1e-13)
+    big = _prep(ref, raw, hk, hv, dk, dv, eps=3.0)
+    src = raw["qkv"][:, :hk * dk].reshape(rows, hk, dk).astype(np.float64)
+    assert np.allclose(big["q"], src / np.sqrt((src * src).sum(-1, keepdims=True) + 3.0), rtol=1e-14)
+
+
+def check_gates(ref):
+    """P20: beta = sigmoid(b); with A_log = 0 the decay is exp(-softplus(a +
+    dt)) = 1 / (1 + e^(a + dt)); with A_log = log 2 it is the square of that;
+    softplus(x) - softplus(-x) = x and softplus(0) = log 2."""
+    hk, hv, dk, dv, rows = 1, 3, 2, 2, 4
+    raw = synth.gdn_raw_inputs(18, 0, rows, hv, hk, dk, dv)
+    for alog, power in ((0.0, 1), (math.log(2.0), 2)):
+        raw["A_log"] = np.full(hv, alog, dtype=np.float64)
+        out = _prep(ref, raw, hk, hv, dk, dv)
+        x = raw["a"].astype(np.float64) + raw["dt_bias"].astype(np.float64)[None, :]
+        assert np.allclose(out["g"], (1.0 / (1.0 + np.exp(x))) ** power, rtol=1e-13)
+        b = raw["b"].astype(np.float64)
+        assert np.allclose(out["beta"], np.exp(b) / (1.0 + np.exp(b)), rtol=1e-14)
+    xs = np.linspace(-30, 30, 61)
+    assert np.allclose(ref.softplus(xs) - ref.softplus(-xs), xs, atol=1e-12)
+    assert abs(float(ref.softplus(0.0)) - math.log(2.0)) < 1e-15
+
+
+def check_gated_norm(ref):
+    """P21: a constant row c normalises to c / sqrt(c^2 + eps); with eps = 0
+    the norm is scale-free and has unit rms; sigmoid(0) halves, silu(0)
+    zeroes, and the weight multiplies elementwise."""
+    rng = np.random.default_rng(19)
+    y = rng.standard_normal((3, 2, 6))
+    z = rng.standard_normal((3, 2, 6))
+    w = rng.uniform(0.5, 1.5, 6)
+    c = np.full((1, 1, 6), -2.5)
+    out = ref.gdn_gated_norm(c, np.zeros_like(c), np.ones(6), eps=0.25)
+    assert np.allclose(out, 0.5 * (-2.5) / math.sqrt(6.25 + 0.25), rtol=1e-14)
+    big = np.full_like(z, 60.0)
+    n1 = ref.gdn_gated_norm(y, big, np.ones(6), eps=0.0)
+    assert np.allclose(np.sqrt((n1 * n1).mean(-1)), 1.0, rtol=1e-12)
+    assert np.allclose(ref.gdn_gated_norm(7.0 * y, big, np.ones(6), eps=0.0), n1, rtol=1e-12)
+    assert np.allclose(ref.gdn_gated_norm(y, big, w, eps=0.0), n1 * w, rtol=1e-12)
+    assert np.array_equal(ref.gdn_gated_norm(y, np.zeros_like(z), w, act="silu"), np.zeros_like(y))
+    half = ref.gdn_gated_norm(y, np.zeros_like(z), w, act="sigmoid")
+    assert np.allclose(half, 0.5 * ref.gdn_gated_norm(y, big, w), rtol=1e-12)
+    sig = ref.gdn_gated_norm(y, z, np.ones(6), act="sigmoid")
+    assert np.allclose(sig, ref.gdn_gated_norm(y, big, np.ones(6)) / (1.0 + np.exp(-z)), rtol=1e-12)
+
+
 ALL_CHECKS = [
     check_bf16_decode, check_unpack_roundtrip, check_qmv_bruteforce, check_qmv_integer_exact,
     check_qmv_closed_forms, check_qmv_rows_independent, check_route_selection, check_route_weights,
@@ -586,4 +709,6 @@ ALL_CHECKS = [
     check_gdn_no_write, check_gdn_scalar, check_gdn_basis, check_gdn_retrieval,
     check_gdn_head_groups, check_gdn_rollback, check_sample_greedy, check_sample_noise_rounding,
     check_sample_gumbel_is_softmax, check_accept_cases, check_verify_cycle_rollback,
+    check_conv_is_convolution, check_conv_alignment, check_conv_history_chain, check_qk_l2_norm, check_gates,
+    check_gated_norm,
 ]

@@ -44,6 +44,18 @@ MUTANTS = {
     "accept_compares_next_row": ("if drafts[t] == tokens[t] and", "if drafts[t] == tokens[t + 1] and"),
     "emitted_without_bonus": ("+ [int(tokens[n])]", ""),
     "prefix_off_by_one": ('"prefix": n + 1', '"prefix": n'),
+    "conv_taps_reversed": ("conv[t] = conv[t] + w[:, i] * X[t + i]", "conv[t] = conv[t] + w[:, 3 - i] * X[t + i]"),
+    "conv_history_misaligned": ("conv[t] = conv[t] + w[:, i] * X[t + i]", "conv[t] = conv[t] + w[:, i] * X[min(t + i + 1, rows + 2)]"),
+    "conv_silu_ignored": ("        conv = silu(conv)", "        conv = conv"),
+    "qk_norm_without_eps": ("q = q / np.sqrt((q * q).sum(axis=-1, keepdims=True) + eps)", "q = q / np.sqrt((q * q).sum(axis=-1, keepdims=True))"),
+    "k_not_normalised": ("k = k / np.sqrt((k * k).sum(axis=-1, keepdims=True) + eps)", "k = k"),
+    "decay_A_not_exponentiated": ("g = np.exp(-np.exp(np.asarray(A_log, dtype=np.float64))[None, :] *", "g = np.exp(-(np.asarray(A_log, dtype=np.float64))[None, :] *"),
+    "decay_dt_bias_dropped": ("softplus(np.asarray(a, dtype=np.float64) + np.asarray(dt_bias, dtype=np.float64)[None, :]))", "softplus(np.asarray(a, dtype=np.float64)))"),
+    "beta_sign": ("beta = 1.0 / (1.0 + np.exp(-np.asarray(b, dtype=np.float64)))", "beta = 1.0 / (1.0 + np.exp(np.asarray(b, dtype=np.float64)))"),
+    "softplus_sign": ("return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))", "return np.maximum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))"),
+    "norm_sum_not_mean": ("n = y / np.sqrt((y * y).mean(axis=-1, keepdims=True) + eps)", "n = y / np.sqrt((y * y).sum(axis=-1, keepdims=True) + eps)"),
+    "norm_weight_dropped": ("return n * np.asarray(w, dtype=np.float64) * gate", "return n * gate"),
+    "gate_silu_for_sigmoid": ("        gate = 1.0 / (1.0 + np.exp(-z))", "        gate = silu(z)"),
 }
 
 
