@@ -78,6 +78,14 @@ typedef void *sdv_stream_t; /* hipStream_t */
 #define SDV_ROUTE_SOFTMAX 0 /* softmax over all E logits */
 #define SDV_ROUTE_SIGMOID 1 /* independent sigmoid per logit */
 
+/* Activation after the GDN input conv (sdv_gdn_prepare_k). */
+#define SDV_CONV_NONE 0
+#define SDV_CONV_SILU 1
+
+/* Gate activation of the GDN output norm (sdv_gdn_gated_norm_k). */
+#define SDV_GATE_SIGMOID 0
+#define SDV_GATE_SILU 1
+
 /*
  * An affine-Q4, group-64 weight in row-major interchange layout: E matrices of
  * N rows by K inputs.
@@ -311,6 +319,46 @@ SDV_API int sdv_gdn_rollback(int k, int j, int *selected_slot);
  */
 SDV_API int sdv_gdn_rollback_copy(float *dst, const float *S_in, float *const *snaps, int k, int j,
                           size_t state_elems, sdv_stream_t stream);
+
+/*
+ * sdv_gdn_prepare_k -- the inputs of the k-row recurrence from their
+ * projections (Flash-Next plan, "2.1 Gated DeltaNet": a short causal depthwise
+ * conv1d over the concatenated q/k/v channels whose last kernel - 1 input
+ * columns are persistent state, per-head L2 normalisation of q and k, the
+ * decay gate from A_log and dt_bias via softplus and exp, beta = sigmoid(b);
+ * "5.1 Gated DeltaNet": 4 taps; Red Lite dev45, "What it is": the per-row
+ * conv shift, q/k norm and beta/decay kernels).
+ *   qkv      device fp32 [k][C], C = 2 Hk Dk + Hv Dv, channels [q heads | k heads | v heads]
+ *   hist     device fp32 [3][C]: the three inputs before row 0, oldest first
+ *   conv_w   device fp32 [C][4]: tap i multiplies the input 3 - i steps before the current one
+ *   a, b     device fp32 [k][Hv];  A_log, dt_bias  device fp32 [Hv]
+ *   conv_act SDV_CONV_NONE or SDV_CONV_SILU (applied to the conv output)
+ *   eps      >= 0: q and k are divided per (row, head) by sqrt(sum of squares + eps)
+ *   q, kk    device fp32 [k][Hk][Dk] out;  v  device fp32 [k][Hv][Dv] out
+ *   g, beta  device fp32 [k][Hv] out: g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+ *   window   device fp32 [k + 3][C] out: [hist; qkv].  The conv history after an
+ *            accepted prefix of j rows (0..k) is window + j C (rollback by
+ *            selection); the next call takes it as `hist` and writes another window.
+ * Dk = Dv in {64, 128}; Hv a multiple of Hk.  Each row is computed in the same order
+ * at every width.  Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE (eps), EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_prepare_k(const float *qkv, const float *hist, const float *conv_w, const float *a,
+                              const float *b, const float *A_log, const float *dt_bias, int k, int Hv, int Hk,
+                              int Dk, int Dv, int conv_act, float eps, float *q, float *kk, float *v, float *g,
+                              float *beta, float *window, sdv_stream_t stream);
+
+/*
+ * sdv_gdn_gated_norm_k -- the GDN output before its projection (Flash-Next plan,
+ * "2.1 Gated DeltaNet": gated RMSNorm rmsnorm(y) * act(gate); "5.1": sigmoid gate
+ * for this model; Red Lite dev45 "What it is": the tail norm).
+ *   y, z     device fp32 [k][Hv][Dv]: the recurrence output and the gate projection
+ *   w        device fp32 [Dv]: the norm weight
+ *   gate_act SDV_GATE_SIGMOID or SDV_GATE_SILU
+ *   out      device fp32 [k][Hv][Dv] = y / sqrt(mean_Dv(y^2) + eps) * w * act(z)
+ * Dv in {64, 128}.  Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE (eps), EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_gated_norm_k(const float *y, const float *z, const float *w, int k, int Hv, int Dv,
+                                 int gate_act, float eps, float *out, sdv_stream_t stream);
 
 /*
  * sdv_verify_accept_workspace_bytes -- device workspace needed by

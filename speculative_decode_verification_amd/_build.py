@@ -21,7 +21,7 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 LIB_SOURCES = ["api.hip", "q4_matvec.hip", "q4_dense.hip", "moe_experts.hip", "route.hip", "combine.hip", "gdn.hip",
-               "accept.hip"]
+               "accept.hip", "gdn_prep.hip"]
 
 
 def hipcc():

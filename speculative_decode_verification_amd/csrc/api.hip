@@ -33,6 +33,12 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
                               const void* x, const int32_t* union_ids, const int32_t* n_union,
                               const int32_t* pair_off, const int32_t* pair_row, const int32_t* pair_slot, int k,
                               int topk, float* partial, hipStream_t st);
+hipError_t gdn_prepare_launch(const float* qkv, const float* hist, const float* conv_w, const float* ga,
+                              const float* gb, const float* A_log, const float* dt_bias, int k, int Hv, int Hk,
+                              int Dk, int Dv, int conv_act, float eps, float* q, float* kk, float* v, float* g,
+                              float* beta, float* window, hipStream_t st);
+hipError_t gdn_gated_norm_launch(const float* y, const float* z, const float* w, int k, int Hv, int Dv,
+                                 int gate_act, float eps, float* out, hipStream_t st);
 size_t accept_workspace_bytes(int k, int V);
 hipError_t accept_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts, int k,
                          int V, int eos, int32_t* tokens, int32_t* accepted, void* workspace, hipStream_t st);
@@ -532,6 +538,58 @@ int sdv_verify_accept_k(const float* logits, const float* noise, float inv_temp,
   return hip_status(sdv::accept_launch(logits, noise, inv_temp, k > 1 ? drafts : nullptr, k, V, eos, tokens,
                                        accepted, workspace, (hipStream_t)stream),
                     "sdv_verify_accept_k launch");
+}
+
+int sdv_gdn_prepare_k(const float* qkv, const float* hist, const float* conv_w, const float* a, const float* b,
+                      const float* A_log, const float* dt_bias, int k, int Hv, int Hk, int Dk, int Dv, int conv_act,
+                      float eps, float* q, float* kk, float* v, float* g, float* beta, float* window,
+                      sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (Hv <= 0 || Hk <= 0) return fail(SDV_EINVAL, "Hv=%d Hk=%d must be positive", Hv, Hk);
+  if (Hv % Hk) return fail(SDV_ELAYOUT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
+  if (Dk != Dv || (Dk != 64 && Dk != 128))
+    return fail(SDV_ELAYOUT, "Dk=%d Dv=%d: the preparation needs Dk = Dv in {64, 128}", Dk, Dv);
+  if (conv_act != SDV_CONV_NONE && conv_act != SDV_CONV_SILU) return fail(SDV_EINVAL, "conv_act=%d", conv_act);
+  if (!(eps >= 0.0f && eps <= 3.4e38f)) return fail(SDV_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+  const struct {
+    const void* p;
+    const char* n;
+  } ptrs[] = {{qkv, "qkv"}, {hist, "hist"}, {conv_w, "conv_w"}, {a, "a"}, {b, "b"}, {A_log, "A_log"},
+              {dt_bias, "dt_bias"}, {q, "q"}, {kk, "kk"}, {v, "v"}, {g, "g"}, {beta, "beta"}, {window, "window"}};
+  for (const auto& pt : ptrs)
+    if ((st = check_ptr(pt.p, pt.n))) return st;
+  const size_t C = 2 * (size_t)Hk * Dk + (size_t)Hv * Dv;
+  Range outs[] = {{q, (size_t)k * Hk * Dk * 4, "q"}, {kk, (size_t)k * Hk * Dk * 4, "kk"},
+                  {v, (size_t)k * Hv * Dv * 4, "v"}, {g, (size_t)k * Hv * 4, "g"}, {beta, (size_t)k * Hv * 4, "beta"},
+                  {window, (size_t)(k + 3) * C * 4, "window"}};
+  Range ins[] = {{qkv, (size_t)k * C * 4, "qkv"}, {hist, 3 * C * 4, "hist"}, {conv_w, C * 16, "conv_w"},
+                 {a, (size_t)k * Hv * 4, "a"}, {b, (size_t)k * Hv * 4, "b"}, {A_log, (size_t)Hv * 4, "A_log"},
+                 {dt_bias, (size_t)Hv * 4, "dt_bias"}};
+  if ((st = check_alias(outs, 6, ins, 7))) return st;
+  return hip_status(sdv::gdn_prepare_launch(qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk, Dv, conv_act,
+                                            eps, q, kk, v, g, beta, window, (hipStream_t)stream),
+                    "sdv_gdn_prepare_k launch");
+}
+
+int sdv_gdn_gated_norm_k(const float* y, const float* z, const float* w, int k, int Hv, int Dv, int gate_act,
+                         float eps, float* out, sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (Hv <= 0) return fail(SDV_EINVAL, "Hv=%d must be positive", Hv);
+  if (Dv != 64 && Dv != 128) return fail(SDV_ELAYOUT, "Dv=%d: the output norm needs Dv in {64, 128}", Dv);
+  if (gate_act != SDV_GATE_SIGMOID && gate_act != SDV_GATE_SILU) return fail(SDV_EINVAL, "gate_act=%d", gate_act);
+  if (!(eps >= 0.0f && eps <= 3.4e38f)) return fail(SDV_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+  if ((st = check_ptr(y, "y"))) return st;
+  if ((st = check_ptr(z, "z"))) return st;
+  if ((st = check_ptr(w, "w"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  const size_t n = (size_t)k * Hv * Dv * 4;
+  Range outs[] = {{out, n, "out"}};
+  Range ins[] = {{y, n, "y"}, {z, n, "z"}, {w, (size_t)Dv * 4, "w"}};
+  if ((st = check_alias(outs, 1, ins, 3))) return st;
+  return hip_status(sdv::gdn_gated_norm_launch(y, z, w, k, Hv, Dv, gate_act, eps, out, (hipStream_t)stream),
+                    "sdv_gdn_gated_norm_k launch");
 }
 
 }  // extern "C"

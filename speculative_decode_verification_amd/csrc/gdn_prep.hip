@@ -1,0 +1,193 @@
+// k-row Gated DeltaNet preparation and output norm (gfx950).
+//
+// Flash-Next plan, "2.1 Gated DeltaNet": before the recurrence, a short
+// causal depthwise conv1d over the concatenated q/k/v channels (the conv
+// keeps the last kernel - 1 input columns as persistent state), L2
+// normalisation of q and k per head, the decay gate from A_log and dt_bias
+// through softplus and exp, and beta = sigmoid(b); after it, the gated
+// RMSNorm rmsnorm(y) * act(gate).  "5.1 Gated DeltaNet": 4 taps, sigmoid gate
+// for this model.  Red Lite dev45, "What it is", runs these per row pair
+// (dn_conv_shift2, dn_qk_l2_2, dn_ba_params2, dn_tail_norm2).
+//
+// Preparation.  The conv of row t reads inputs only (the history and rows
+// 0..t), so all k rows are independent: one workgroup per head block of
+// D channels (q heads, then k heads, then v heads), one thread per channel,
+// all rows.  A thread loads its channel's 3 + k inputs and 4 taps, applies
+// the taps in order (fma chain from the oldest input), and writes the window
+// [history; rows] that rollback selects from.  q and k are divided per (row,
+// head) by sqrt(sum of squares + eps); the sum is a fixed 16-lane DPP sum,
+// the four row totals of a wave in row order, then the waves in order, so
+// every row is computed the same way at every width.  One extra workgroup
+// forms g and beta for every (row, v head).
+//
+// Output norm.  One workgroup per (row, v head) of Dv threads: the mean of
+// squares in the same fixed order, then y / sqrt(mean + eps) * w * act(z).
+
+#include "common.h"
+
+namespace sdv {
+
+namespace {
+
+constexpr int kTaps = 4;
+
+struct PrepArgs {
+  const float* qkv;      // [k][C]
+  const float* hist;     // [3][C]
+  const float* conv_w;   // [C][4]
+  const float* a;        // [k][Hv]
+  const float* b;        // [k][Hv]
+  const float* A_log;    // [Hv]
+  const float* dt_bias;  // [Hv]
+  int k, Hv, Hk, Dk, Dv, C, conv_act;
+  float eps;
+  float* q;       // [k][Hk][Dk]
+  float* kk;      // [k][Hk][Dk]
+  float* v;       // [k][Hv][Dv]
+  float* g;       // [k][Hv]
+  float* beta;    // [k][Hv]
+  float* window;  // [k + 3][C]
+};
+
+// Sum over the 64 lanes of a wave, in every lane: a 16-lane DPP sum, then the
+// four row totals in row order.
+__device__ __forceinline__ float wave_sum(float x) {
+  const float r = row16_sum(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+
+// Block of D (64 or 128) channels, all k rows.
+template <int D>
+__global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
+  __shared__ float s_part[D / 64][SDV_MAX_ROWS];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int nq = a.Hk, nqk = 2 * a.Hk;
+  const int blk = blockIdx.x;
+  if (blk == nqk + a.Hv) {
+    // gates: one thread per (row, v head)
+    for (int e = tid; e < a.k * a.Hv; e += D) {
+      const int h = e % a.Hv;
+      const float x = a.a[e] + a.dt_bias[h];
+      a.g[e] = expf(-expf(a.A_log[h]) * softplusf_(x));
+      a.beta[e] = 1.0f / (1.0f + expf(-a.b[e]));
+    }
+    return;
+  }
+  // channel of this thread
+  const bool is_q = blk < nq, is_k = !is_q && blk < nqk;
+  const int c = is_q ? blk * a.Dk + tid : (is_k ? nq * a.Dk + (blk - nq) * a.Dk + tid
+                                                : nqk * a.Dk + (blk - nqk) * a.Dv + tid);
+  const int C = a.C, k = a.k;
+  // the history and every row's input of the channel, issued together
+  float x[3 + SDV_MAX_ROWS];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) x[j] = a.hist[(size_t)j * C + c];
+#pragma unroll
+  for (int t = 0; t < SDV_MAX_ROWS; ++t) x[3 + t] = a.qkv[(size_t)min(t, k - 1) * C + c];
+  const float4 w = reinterpret_cast<const float4*>(a.conv_w)[c];
+  // the window [history; rows] for rollback by selection
+#pragma unroll
+  for (int j = 0; j < 3 + SDV_MAX_ROWS; ++j)
+    if (j < 3 + k) a.window[(size_t)j * C + c] = x[j];
+  float o[SDV_MAX_ROWS];
+#pragma unroll
+  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
+    float acc = w.x * x[t];
+    acc = fmaf(w.y, x[t + 1], acc);
+    acc = fmaf(w.z, x[t + 2], acc);
+    acc = fmaf(w.w, x[t + 3], acc);
+    if (a.conv_act == SDV_CONV_SILU) acc = siluf_(acc);
+    o[t] = acc;
+  }
+  if (!is_q && !is_k) {
+    const int hv = blk - nqk;
+#pragma unroll
+    for (int t = 0; t < SDV_MAX_ROWS; ++t)
+      if (t < k) a.v[((size_t)t * a.Hv + hv) * a.Dv + tid] = o[t];
+    return;
+  }
+  // per-row L2 norm over the head's D channels
+#pragma unroll
+  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
+    const float ws = wave_sum(o[t] * o[t]);
+    if ((tid & 63) == 0) s_part[wave][t] = ws;
+  }
+  __syncthreads();
+  const int h = is_q ? blk : blk - nq;
+  float* dst = is_q ? a.q : a.kk;
+#pragma unroll
+  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
+    if (t < k) {
+      float ss = s_part[0][t];
+#pragma unroll
+      for (int w2 = 1; w2 < D / 64; ++w2) ss = ss + s_part[w2][t];
+      dst[((size_t)t * a.Hk + h) * a.Dk + tid] = o[t] / sqrtf(ss + a.eps);
+    }
+  }
+}
+
+struct NormArgs {
+  const float* y;  // [k][Hv][Dv]
+  const float* z;  // [k][Hv][Dv]
+  const float* w;  // [Dv]
+  int Dv, gate_act;
+  float eps;
+  float* out;
+};
+
+template <int D>
+__global__ __launch_bounds__(D) void gdn_gated_norm_kernel(NormArgs a) {
+  __shared__ float s_part[D / 64];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const size_t base = (size_t)blockIdx.x * D;  // (row, v head)
+  const float y = a.y[base + tid];
+  const float z = a.z[base + tid];
+  const float ws = wave_sum(y * y);
+  if ((tid & 63) == 0) s_part[wave] = ws;
+  __syncthreads();
+  float ss = s_part[0];
+#pragma unroll
+  for (int w2 = 1; w2 < D / 64; ++w2) ss = ss + s_part[w2];
+  const float n = y / sqrtf(ss / (float)D + a.eps);
+  const float gate = a.gate_act == SDV_GATE_SILU ? siluf_(z) : sigmoidf_(z);
+  a.out[base + tid] = n * a.w[tid] * gate;
+}
+
+}  // namespace
+
+hipError_t gdn_prepare_launch(const float* qkv, const float* hist, const float* conv_w, const float* ga,
+                              const float* gb, const float* A_log, const float* dt_bias, int k, int Hv, int Hk,
+                              int Dk, int Dv, int conv_act, float eps, float* q, float* kk, float* v, float* g,
+                              float* beta, float* window, hipStream_t st) {
+  PrepArgs a{qkv, hist, conv_w, ga, gb, A_log, dt_bias, k, Hv, Hk, Dk, Dv, 2 * Hk * Dk + Hv * Dv, conv_act,
+             eps, q, kk, v, g, beta, window};
+  const dim3 grid((unsigned)(2 * Hk + Hv + 1));
+  if (Dk == 64)
+    hipLaunchKernelGGL(gdn_prepare_kernel<64>, grid, dim3(64), 0, st, a);
+  else if (Dk == 128)
+    hipLaunchKernelGGL(gdn_prepare_kernel<128>, grid, dim3(128), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t gdn_gated_norm_launch(const float* y, const float* z, const float* w, int k, int Hv, int Dv,
+                                 int gate_act, float eps, float* out, hipStream_t st) {
+  NormArgs a{y, z, w, Dv, gate_act, eps, out};
+  const dim3 grid((unsigned)(k * Hv));
+  if (Dv == 64)
+    hipLaunchKernelGGL(gdn_gated_norm_kernel<64>, grid, dim3(64), 0, st, a);
+  else if (Dv == 128)
+    hipLaunchKernelGGL(gdn_gated_norm_kernel<128>, grid, dim3(128), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sdv

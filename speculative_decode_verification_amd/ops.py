@@ -11,11 +11,12 @@ from collections import namedtuple
 
 import torch
 
-from ._lib import (ACT_BF16, ACT_F32, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX,
-                   SdvError, SdvQ4, SdvQ4T, check, lib)
+from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, GATE_SIGMOID, GATE_SILU, MODE_GATEUP_SWIGLU,
+                   MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ4, SdvQ4T, check, lib)
 
 __all__ = ["Q4Weight", "TiledQ4", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
-           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "SdvError", "MODE_PLAIN",
+           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_gated_norm_k",
+           "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
 
 RouteResult = namedtuple("RouteResult", "idx w union_ids n_union pair_off pair_row pair_slot")
@@ -325,6 +326,72 @@ def gdn_rollback_copy(dst, S_in, snaps, j):
     check(lib().sdv_gdn_rollback_copy(_need(dst, "dst", torch.float32, n, dev), _need(S_in, "S_in", torch.float32, n, dev),
                                       arr, k, j, n, _stream(dst)))
     return dst
+
+
+def _prepare_args(qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, Dk, conv_act, eps, out):
+    k, C = qkv.shape
+    Hv = A_log.shape[0]
+    Dv = Dk
+    dev = qkv.device
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError(f"qkv has {C} channels, expected 2*{Hk}*{Dk} + {Hv}*{Dv}")
+    f = torch.float32
+    return [_need(qkv, "qkv", f, k * C, dev), _need(hist, "hist", f, 3 * C, dev),
+            _need(conv_w, "conv_w", f, 4 * C, dev), _need(a, "a", f, k * Hv, dev), _need(b, "b", f, k * Hv, dev),
+            _need(A_log, "A_log", f, Hv, dev), _need(dt_bias, "dt_bias", f, Hv, dev), k, Hv, Hk, Dk, Dv, conv_act,
+            ctypes.c_float(eps), _need(out["q"], "q", f, k * Hk * Dk, dev), _need(out["k"], "k", f, k * Hk * Dk, dev),
+            _need(out["v"], "v", f, k * Hv * Dv, dev), _need(out["g"], "g", f, k * Hv, dev),
+            _need(out["beta"], "beta", f, k * Hv, dev), _need(out["window"], "window", f, (k + 3) * C, dev),
+            _stream(qkv)]
+
+
+def gdn_prepare_outputs(k, Hv, Hk, Dk, device):
+    f = torch.float32
+    C = 2 * Hk * Dk + Hv * Dk
+    return {"q": torch.empty((k, Hk, Dk), dtype=f, device=device), "k": torch.empty((k, Hk, Dk), dtype=f, device=device),
+            "v": torch.empty((k, Hv, Dk), dtype=f, device=device), "g": torch.empty((k, Hv), dtype=f, device=device),
+            "beta": torch.empty((k, Hv), dtype=f, device=device),
+            "window": torch.empty((k + 3, C), dtype=f, device=device)}
+
+
+def gdn_prepare_k(qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, Dk, conv_act=CONV_NONE, eps=1e-6, out=None):
+    """The recurrence inputs from the GDN projections: qkv fp32 [k, C] (channels
+    q | k | v), hist [3, C], conv_w [C, 4], a, b [k, Hv], A_log, dt_bias [Hv].
+    Returns {q, k, v, g, beta, window}; window [k+3, C] rows j..j+3 are the
+    conv history after an accepted prefix of j rows."""
+    k = qkv.shape[0]
+    Hv = A_log.shape[0]
+    if out is None:
+        out = gdn_prepare_outputs(k, Hv, Hk, Dk, qkv.device)
+    check(lib().sdv_gdn_prepare_k(*_prepare_args(qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, Dk, conv_act, eps,
+                                                 out)))
+    return out
+
+
+def _norm_args(y, z, w, gate_act, eps, out):
+    k, Hv, Dv = y.shape
+    dev = y.device
+    f = torch.float32
+    n = k * Hv * Dv
+    return [_need(y, "y", f, n, dev), _need(z, "z", f, n, dev), _need(w, "w", f, Dv, dev), k, Hv, Dv, gate_act,
+            ctypes.c_float(eps), _need(out, "out", f, n, dev), _stream(y)]
+
+
+def gdn_gated_norm_k(y, z, w, gate_act=GATE_SIGMOID, eps=1e-6, out=None):
+    """y / sqrt(mean(y^2) + eps) * w * act(z) per (row, v head); y, z fp32 [k, Hv, Dv], w [Dv]."""
+    if out is None:
+        out = torch.empty_like(y)
+    check(lib().sdv_gdn_gated_norm_k(*_norm_args(y, z, w, gate_act, eps, out)))
+    return out
+
+
+def bind_gdn_prepare_k(qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, Dk, out, conv_act=CONV_NONE, eps=1e-6):
+    return BoundCall("sdv_gdn_prepare_k", _prepare_args(qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, Dk, conv_act,
+                                                        eps, out))
+
+
+def bind_gdn_gated_norm_k(y, z, w, out, gate_act=GATE_SIGMOID, eps=1e-6):
+    return BoundCall("sdv_gdn_gated_norm_k", _norm_args(y, z, w, gate_act, eps, out))
 
 
 def verify_accept_workspace(k, V, device):

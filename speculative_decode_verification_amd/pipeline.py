@@ -135,12 +135,65 @@ class GdnLayer:
         call()
         return self.y
 
+    def attach_prep(self, hist, conv_w, A_log, dt_bias, Hk, conv_act=ops.CONV_NONE, eps=1e-6):
+        """Run the layer from its projections: the conv history hist [3, C]
+        (copied), depthwise taps conv_w [C, 4], A_log and dt_bias [Hv], Hk
+        q/k heads.  Two windows [k + 3, C] alternate: rollback makes rows j..j+2
+        of the last window the history (no copy), and the next preparation
+        writes the other window."""
+        C = hist.shape[1]
+        dev = hist.device
+        self.prep_params = (conv_w.contiguous(), A_log.contiguous(), dt_bias.contiguous(), Hk, conv_act, eps)
+        self.hist = hist.contiguous().clone()
+        self.windows = [torch.empty((self.k + 3, C), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.win = 0
+        self.prepped = False
+        self.prep_out = [{n: t for n, t in ops.gdn_prepare_outputs(self.k, self.Hv, Hk, self.Dk, dev).items()
+                          if n != "window"} for _ in range(2)]
+        self._bound_prep = {}
+        return self
+
+    def _prep_out(self, rows):
+        o = self.prep_out[self.win]
+        out = {n: t[:rows] for n, t in o.items()}
+        out["window"] = self.windows[self.win][:rows + 3]
+        return out
+
+    def prepare(self, qkv, a, b):
+        """The recurrence inputs of rows qkv [rows, C], a, b [rows, Hv];
+        returns {q, k, v, g, beta, window}."""
+        conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+        out = ops.gdn_prepare_k(qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk, self.Dk, act, eps,
+                                self._prep_out(qkv.shape[0]))
+        self.prepped = True
+        return out
+
+    def run_prepare_bound(self, qkv, a, b):
+        """``prepare`` for fixed qkv, a, b buffers, marshalled once per
+        (window, history source) pair."""
+        key = (self.win, self.hist.data_ptr(), qkv.data_ptr(), a.data_ptr(), b.data_ptr())
+        call = self._bound_prep.get(key)
+        out = self._prep_out(qkv.shape[0])
+        if call is None:
+            conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+            call = ops.bind_gdn_prepare_k(qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk, self.Dk, out, act, eps)
+            self._bound_prep[key] = call
+        call()
+        self.prepped = True
+        return out
+
     def rollback(self, j):
-        """Make the state after the accepted prefix of j rows live (no copy)."""
+        """Make the state after the accepted prefix of j rows live (no copy);
+        with a preparation stage, rows j..j+2 of its window become the conv
+        history."""
         slot = ops.gdn_rollback(len(self.snap_ids), j)
         if slot > 0:
             self.live = self.snap_ids[slot - 1]
         self.snap_ids = None
+        if getattr(self, "prepped", False):
+            self.hist = self.windows[self.win][j:j + 3]
+            self.win ^= 1
+            self.prepped = False
         return self.state
 
 

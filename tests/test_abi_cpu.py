@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 18
+    assert len(names) == 20
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -323,3 +323,53 @@ def test_accept_validation(lib):
     assert call(tok=logits + 64) == L.SDV_EALIAS                    # tokens over logits
     assert call(ws=tok) == L.SDV_EALIAS                             # workspace over tokens
     assert call(acc=noise + 16, noise=noise) == L.SDV_EALIAS         # accepted over noise
+
+
+def prep(lib, k=2, Hv=4, Hk=2, Dk=64, Dv=64, act=0, eps=1e-6, **over):
+    C = 2 * Hk * Dk + Hv * Dv
+    ptr = dict(qkv=P, hist=P + 0x100000, conv_w=P + 0x200000, a=P + 0x300000, b=P + 0x310000,
+               A_log=P + 0x320000, dt_bias=P + 0x330000, q=P + 0x400000, kk=P + 0x500000, v=P + 0x600000,
+               g=P + 0x700000, beta=P + 0x710000, window=P + 0x800000)
+    ptr.update(over)
+    assert C * 4 * 12 < 0x100000
+    return lib.sdv_gdn_prepare_k(ptr["qkv"], ptr["hist"], ptr["conv_w"], ptr["a"], ptr["b"], ptr["A_log"],
+                                 ptr["dt_bias"], k, Hv, Hk, Dk, Dv, act, eps, ptr["q"], ptr["kk"], ptr["v"],
+                                 ptr["g"], ptr["beta"], ptr["window"], None)
+
+
+def test_prepare_validation(lib):
+    assert prep(lib, k=0) == L.SDV_EWIDTH
+    assert prep(lib, k=10) == L.SDV_EWIDTH
+    assert prep(lib, Hv=0) == L.SDV_EINVAL
+    assert prep(lib, Hv=5, Hk=2) == L.SDV_ELAYOUT
+    assert prep(lib, Dk=128, Dv=64) == L.SDV_ELAYOUT
+    assert prep(lib, Dk=96, Dv=96) == L.SDV_ELAYOUT
+    assert prep(lib, act=2) == L.SDV_EINVAL
+    assert prep(lib, eps=-1.0) == L.SDV_ERANGE
+    assert prep(lib, eps=float("nan")) == L.SDV_ERANGE
+    assert prep(lib, eps=float("inf")) == L.SDV_ERANGE
+    assert prep(lib, hist=0) == L.SDV_EINVAL
+    assert lib.sdv_last_error().decode() == "hist is NULL"
+    assert prep(lib, conv_w=P + 0x200004) == L.SDV_EINVAL            # taps are read as float4
+    # the window (k + 3 rows) over the conv history: the next step reads it
+    assert prep(lib, window=P + 0x100000 + 64) == L.SDV_EALIAS
+    assert lib.sdv_last_error().decode() == "output window overlaps input hist"
+    assert prep(lib, q=P + 0x500000) == L.SDV_EALIAS                 # q over kk
+    assert prep(lib, beta=P + 0x700000 + 16) == L.SDV_EALIAS         # beta over g
+    assert prep(lib, g=P + 0x300000) == L.SDV_EALIAS                 # g over a
+
+
+def norm(lib, k=2, Hv=4, Dv=64, act=0, eps=1e-6, y=P, z=P + 0x100000, w=P + 0x200000, out=P + 0x300000):
+    return lib.sdv_gdn_gated_norm_k(y, z, w, k, Hv, Dv, act, eps, out, None)
+
+
+def test_gated_norm_validation(lib):
+    assert norm(lib, k=0) == L.SDV_EWIDTH
+    assert norm(lib, Hv=0) == L.SDV_EINVAL
+    assert norm(lib, Dv=32) == L.SDV_ELAYOUT
+    assert norm(lib, act=5) == L.SDV_EINVAL
+    assert norm(lib, eps=-0.5) == L.SDV_ERANGE
+    assert norm(lib, w=0) == L.SDV_EINVAL
+    assert norm(lib, out=P + 16) == L.SDV_EALIAS                     # in place over y
+    assert lib.sdv_last_error().decode() == "output out overlaps input y"
+    assert norm(lib, out=P + 0x200000) == L.SDV_EALIAS
