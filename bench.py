@@ -184,10 +184,15 @@ class Workload:
             self.moe.append((layer, x, lg, z))
             self.calls.append(layer.bind(x, lg, z))
         for l in self.gdn_ids:
+            # from the layer's projections: preparation (conv, q/k norm, gates),
+            # the recurrence with snapshots, the gated output norm
             S0 = sdev.upload_f32(synth.gdn_state(cfg.cid, l, gs.hv, gs.dv, gs.dk), dev)
-            gi = synth.gdn_layer_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
-            d = {n: sdev.upload_f32(v, dev) for n, v in gi.items()}
-            gl = pipeline.GdnLayer(S0, k).bind(d["q"], d["k"], d["v"], d["g"], d["beta"])
+            raw = synth.gdn_raw_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
+            d = {n: sdev.upload_f32(v, dev) for n, v in raw.items()}
+            gl = pipeline.GdnLayer(S0, k).attach_prep(d["hist"], d["conv_w"], d["A_log"], d["dt_bias"], gs.hk)
+            gl.bind_from_proj(d["qkv"], d["a"], d["b"])
+            d["out"] = torch.empty((k, gs.hv, gs.dv), dtype=torch.float32, device=dev)
+            gl.bind_tail(d["z"], d["norm_w"], d["out"])
             self.gdn[l] = (gl, d)
         # acceptance of the block: next-token logits over the vocabulary with a
         # planted accepted-draft count per step (greedy), and the accepted
@@ -221,7 +226,8 @@ class Workload:
         for l in range(self.layers):
             g = self.gdn.get(l)
             if g is not None:
-                run("gdn", l, g[0].run_bound)
+                run("gdn", l, g[0].run_from_proj_bound)
+                run("gdn_norm", l, g[0].run_tail_bound)
             for name, call in self.calls[l]:
                 run(name, l, call)
         accept, n, _, _ = self.blocks[s % len(self.blocks)]
@@ -272,9 +278,16 @@ class Workload:
         if name == "combine":
             return k * topk * H * 4 + k * topk * 4 + k * H * 4 + k * 4 + k * H * 4
         if name == "gdn":
+            # preparation and recurrence in one launch: the state in, k
+            # snapshots and y out; qkv rows, history, taps, a, b, A_log and
+            # dt_bias in, the window [history; rows] out
             g = self.gs
-            return ((k + 1) * g.hv * g.dv * g.dk * 4 + 2 * k * g.hk * g.dk * 4 + 2 * k * g.hv * g.dv * 4
-                    + 2 * k * g.hv * 4)
+            C = 2 * g.hk * g.dk + g.hv * g.dv
+            return ((k + 1) * g.hv * g.dv * g.dk * 4 + k * g.hv * g.dv * 4
+                    + (k * C + 3 * C + 4 * C + 2 * k * g.hv + 2 * g.hv + (k + 3) * C) * 4)
+        if name == "gdn_norm":
+            g = self.gs
+            return (3 * k * g.hv * g.dv + g.dv) * 4
         raise KeyError(name)
 
     def step_bytes(self, unions):
@@ -283,7 +296,8 @@ class Workload:
             for name, _ in self.calls[l]:
                 total += self.kernel_bytes(name, l, unions)
             if l in self.gdn:
-                total += self.kernel_bytes("gdn", l, unions)
+                for name in ("gdn", "gdn_norm"):
+                    total += self.kernel_bytes(name, l, unions)
         return total + self.kernel_bytes("accept", self.layers, unions)
 
 
@@ -313,10 +327,10 @@ def traffic_for(kernel_hash):
 def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
     """The CPU oracle on a bounded sample of the same workload: whole layers
     (MoE: route, union, gate/up, down, shared expert, combine, with the layer's
-    union experts regenerated on the host before timing; GDN: the k-row
-    recurrence with snapshots), layer by layer until at least ``min_seconds``
-    of oracle time or ``max_layers`` layers, then scaled to the 48 MoE + 36 GDN
-    layers of a step."""
+    union experts regenerated on the host before timing; GDN: preparation,
+    the k-row recurrence with snapshots, the gated output norm), layer by
+    layer until at least ``min_seconds`` of oracle time or ``max_layers``
+    layers, then scaled to the 48 MoE + 36 GDN layers of a step."""
     import oracle
     import synth
     from synth import configs
@@ -349,9 +363,12 @@ def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
         unions.append(len(used))
         if l in cfg.gdn_layers:
             S = synth.gdn_state(cfg.cid, l, gs.hv, gs.dv, gs.dk)
-            gi = synth.gdn_layer_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
+            raw = synth.gdn_raw_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
             t0 = time.perf_counter()
-            oracle.gdn_verify(S, gi["q"], gi["k"], gi["v"], gi["g"], gi["beta"])
+            p = oracle.gdn_prepare(raw["qkv"], raw["hist"], raw["conv_w"], raw["a"], raw["b"], raw["A_log"],
+                                   raw["dt_bias"], gs.hk, gs.hv, gs.dk, gs.dv)
+            y, _ = oracle.gdn_verify(S, p["q"], p["k"], p["v"], p["g"], p["beta"])
+            oracle.gdn_gated_norm(y, raw["z"], raw["norm_w"])
             t_gdn += time.perf_counter() - t0
             n_gdn += 1
         if t_moe + t_gdn >= min_seconds:
@@ -445,7 +462,7 @@ def main():
     torch.cuda.synchronize()
     unions = wl.unions()
 
-    per_step = len(wl.calls[0]) * wl.layers + len(wl.gdn) + 1
+    per_step = len(wl.calls[0]) * wl.layers + 2 * len(wl.gdn) + 1
     timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1 + 4)
     log(f"timing events on the launch stream (HIP runtime {timer.path})")
     events = []

@@ -333,7 +333,8 @@ SDV_API int sdv_gdn_rollback_copy(float *dst, const float *S_in, float *const *s
  *   conv_w   device fp32 [C][4]: tap i multiplies the input 3 - i steps before the current one
  *   a, b     device fp32 [k][Hv];  A_log, dt_bias  device fp32 [Hv]
  *   conv_act SDV_CONV_NONE or SDV_CONV_SILU (applied to the conv output)
- *   eps      >= 0: q and k are divided per (row, head) by sqrt(sum of squares + eps)
+ *   eps      >= 0: q and k are multiplied per (row, head) by rsqrt(sum of squares + eps)
+ *            (the device reciprocal square root, within 2 ulp of 1 / sqrt)
  *   q, kk    device fp32 [k][Hk][Dk] out;  v  device fp32 [k][Hv][Dv] out
  *   g, beta  device fp32 [k][Hv] out: g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
  *   window   device fp32 [k + 3][C] out: [hist; qkv].  The conv history after an
@@ -346,6 +347,23 @@ SDV_API int sdv_gdn_prepare_k(const float *qkv, const float *hist, const float *
                               const float *b, const float *A_log, const float *dt_bias, int k, int Hv, int Hk,
                               int Dk, int Dv, int conv_act, float eps, float *q, float *kk, float *v, float *g,
                               float *beta, float *window, sdv_stream_t stream);
+
+/*
+ * sdv_gdn_verify_prep_k -- sdv_gdn_prepare_k and sdv_gdn_verify_k in one
+ * launch (Flash-Next plan, "2.1 Gated DeltaNet": the conv, q/k norm and gates
+ * feed the recurrence; Red Lite dev45, "What it is": the per-row preparation
+ * kernels ahead of the state kernel).  Each workgroup prepares the inputs of
+ * its own value rows; y, the snapshots and the window equal those of the two
+ * separate calls bit for bit.  The prepared q, k, v, g, beta are not written.
+ *   S_in, snaps, y  as sdv_gdn_verify_k;  qkv, hist, conv_w, a, b, A_log, dt_bias,
+ *   conv_act, eps, window  as sdv_gdn_prepare_k.
+ * Dk = Dv in {64, 128}; Hv a multiple of Hk.  No output may overlap an input or
+ * another output.  Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE (eps), EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_verify_prep_k(const float *S_in, const float *qkv, const float *hist, const float *conv_w,
+                                  const float *a, const float *b, const float *A_log, const float *dt_bias, int k,
+                                  int Hv, int Hk, int Dk, int Dv, int conv_act, float eps, float *window, float *y,
+                                  float *const *snaps, sdv_stream_t stream);
 
 /*
  * sdv_gdn_gated_norm_k -- the GDN output before its projection (Flash-Next plan,

@@ -45,6 +45,10 @@ hipError_t accept_launch(const float* logits, const float* noise, float inv_temp
 hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
                       const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
                       float* y, float* const* snaps, hipStream_t st);
+hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
+                                  const float* ga, const float* gb, const float* A_log, const float* dt_bias, int k,
+                                  int Hv, int Hk, int D, int conv_act, float eps, float* window, float* y,
+                                  float* const* snaps, hipStream_t st);
 }  // namespace sdv
 
 namespace {
@@ -570,6 +574,52 @@ int sdv_gdn_prepare_k(const float* qkv, const float* hist, const float* conv_w, 
   return hip_status(sdv::gdn_prepare_launch(qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk, Dv, conv_act,
                                             eps, q, kk, v, g, beta, window, (hipStream_t)stream),
                     "sdv_gdn_prepare_k launch");
+}
+
+int sdv_gdn_verify_prep_k(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
+                          const float* a, const float* b, const float* A_log, const float* dt_bias, int k, int Hv,
+                          int Hk, int Dk, int Dv, int conv_act, float eps, float* window, float* y,
+                          float* const* snaps, sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (Hv <= 0 || Hk <= 0) return fail(SDV_EINVAL, "Hv=%d Hk=%d must be positive", Hv, Hk);
+  if (Hv % Hk) return fail(SDV_ELAYOUT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
+  if (Dk != Dv || (Dk != 64 && Dk != 128))
+    return fail(SDV_ELAYOUT, "Dk=%d Dv=%d: the preparation needs Dk = Dv in {64, 128}", Dk, Dv);
+  if ((long)Hv * Dv > (1L << 26)) return fail(SDV_EINVAL, "Hv*Dv=%ld too large", (long)Hv * Dv);
+  if (conv_act != SDV_CONV_NONE && conv_act != SDV_CONV_SILU) return fail(SDV_EINVAL, "conv_act=%d", conv_act);
+  if (!(eps >= 0.0f && eps <= 3.4e38f)) return fail(SDV_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+  const struct {
+    const void* p;
+    const char* n;
+  } ptrs[] = {{S_in, "S_in"}, {qkv, "qkv"}, {hist, "hist"}, {conv_w, "conv_w"}, {a, "a"}, {b, "b"},
+              {A_log, "A_log"}, {dt_bias, "dt_bias"}, {window, "window"}, {y, "y"}};
+  for (const auto& pt : ptrs)
+    if ((st = check_ptr(pt.p, pt.n))) return st;
+  if (!snaps) return fail(SDV_EINVAL, "snaps is NULL");
+  const size_t C = 2 * (size_t)Hk * Dk + (size_t)Hv * Dv;
+  const size_t state = (size_t)Hv * Dv * Dk * 4;
+  Range ins[] = {{S_in, state, "S_in"},
+                 {qkv, (size_t)k * C * 4, "qkv"},
+                 {hist, 3 * C * 4, "hist"},
+                 {conv_w, C * 16, "conv_w"},
+                 {a, (size_t)k * Hv * 4, "a"},
+                 {b, (size_t)k * Hv * 4, "b"},
+                 {A_log, (size_t)Hv * 4, "A_log"},
+                 {dt_bias, (size_t)Hv * 4, "dt_bias"}};
+  Range outs[SDV_MAX_ROWS + 2];
+  outs[0] = {y, (size_t)k * Hv * Dv * 4, "y"};
+  outs[1] = {window, (size_t)(k + 3) * C * 4, "window"};
+  static const char* snap_names[SDV_MAX_ROWS] = {"snaps[0]", "snaps[1]", "snaps[2]", "snaps[3]", "snaps[4]",
+                                                  "snaps[5]", "snaps[6]", "snaps[7]", "snaps[8]"};
+  for (int t = 0; t < k; ++t) {
+    if ((st = check_ptr(snaps[t], snap_names[t]))) return st;
+    outs[t + 2] = {snaps[t], state, snap_names[t]};
+  }
+  if ((st = check_alias(outs, k + 2, ins, 8))) return st;
+  return hip_status(sdv::gdn_verify_prep_launch(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk,
+                                                conv_act, eps, window, y, snaps, (hipStream_t)stream),
+                    "sdv_gdn_verify_prep_k launch");
 }
 
 int sdv_gdn_gated_norm_k(const float* y, const float* z, const float* w, int k, int Hv, int Dv, int gate_act,

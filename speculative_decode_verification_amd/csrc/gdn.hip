@@ -17,7 +17,9 @@
 // row t-1, bit for bit.  HBM traffic per layer: the state once in, k
 // snapshots out, plus the small per-row vectors.
 
-#include "common.h"
+#include <utility>
+
+#include "gdn_prep_core.h"
 
 namespace sdv {
 
@@ -33,29 +35,66 @@ struct GdnArgs {
   int k, Hv, Hk, Dv;
   float* y;
   float* snaps[SDV_MAX_ROWS];
+  // with the preparation in the kernel: the projections instead of q, kk, v,
+  // g, beta, and the conv window out
+  const float* qkv;      // [k][C]
+  const float* hist;     // [3][C]
+  const float* conv_w;   // [C][4]
+  const float* ga;       // [k][Hv]
+  const float* gb;       // [k][Hv]
+  const float* A_log;    // [Hv]
+  const float* dt_bias;  // [Hv]
+  int C, conv_act;
+  float eps;
+  float* window;  // [k + 3][C]
 };
 
 constexpr int kRowsPerBlock = 16;  // 16 value rows x 16 lanes = 256 threads
+
+// f(integral_constant<int, t>) for t = 0, 1, ... while t < k, in order.
+template <int... T, class F>
+__device__ __forceinline__ void for_rows(std::integer_sequence<int, T...>, int k, F&& f) {
+  (void)((T < k ? (f(std::integral_constant<int, T>{}), true) : false) && ...);
+}
 
 // LDS_KQ: the block's 16 value rows belong to one v head (Dv % 16 == 0), so
 // the per-row vectors k_t, q_t (for that head's qk head), v_t, g_t, beta_t of
 // all k rows are staged in LDS once and the serial t loop reads only LDS and
 // registers.  Otherwise they are read from global memory inside the loop.
-template <int DK, bool LDS_KQ>
+//
+// PREP (Dk = Dv, LDS_KQ): the block prepares its own inputs from the
+// projections with the instructions of the stand-alone preparation, so its
+// rows equal preparation followed by the recurrence, bit for bit.  Threads
+// 0..2Dk-1 take the q then k channels of the block's qk head (conv, per-wave
+// sums of squares; the factor rsqrt(sum of the waves in order + eps) is
+// applied as row t is read), 16 threads the block's 16 v channels, k threads
+// the gates of its v head; one barrier.  The qk columns of the window
+// are written by the first block of each qk head, the v columns by their
+// block.  Blocks of one qk head are placed on one XCD when the block count
+// allows, so its repeated q/k inputs are L2 hits.
+template <int DK, bool LDS_KQ, bool PREP>
 __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
+  static_assert(!PREP || LDS_KQ, "the in-kernel preparation stages through LDS");
   constexpr int NV4 = DK / 64;  // float4 per lane
   __shared__ float4 s_k[LDS_KQ ? SDV_MAX_ROWS * DK / 4 : 1];
   __shared__ float4 s_q[LDS_KQ ? SDV_MAX_ROWS * DK / 4 : 1];
   __shared__ float s_v[LDS_KQ ? SDV_MAX_ROWS * kRowsPerBlock : 1];
   __shared__ float s_g[SDV_MAX_ROWS], s_b[SDV_MAX_ROWS];
+  __shared__ float s_part[PREP ? 4 : 1][SDV_MAX_ROWS];
 
+  // blocks dealt round-robin over the 8 XCDs; with PREP and a multiple of 8
+  // blocks, XCD x takes the consecutive logical blocks x*n/8 .. (x+1)*n/8-1
+  int lblk = blockIdx.x;
+  if (PREP && (gridDim.x & 7) == 0) lblk = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int sub = threadIdx.x & 15;
   const int lrow = threadIdx.x >> 4;
-  const long row = (long)blockIdx.x * kRowsPerBlock + lrow;  // h * Dv + i
-  const long nrows = (long)a.Hv * a.Dv;
+  // value rows fit in int (Hv * Dv <= 2^26); with PREP, Dv = DK is known
+  const int Dv = PREP ? DK : a.Dv;
+  const int row = lblk * kRowsPerBlock + lrow;  // h * Dv + i
+  const int nrows = a.Hv * Dv;
   const bool active = row < nrows;
-  const int h = active ? (int)(row / a.Dv) : 0;
-  const int i = active ? (int)(row - (long)h * a.Dv) : 0;
+  const int h = active ? row / Dv : 0;
+  const int i = active ? row - h * Dv : 0;
   const int c = h / (a.Hv / a.Hk);
 
   // Every load is issued before any is used: first the per-row vectors of
@@ -69,12 +108,37 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
 #pragma unroll
   for (int u = 0; u < KQ_PER_THREAD; ++u) ck[u] = cq[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float cv = 0.0f, cg = 0.0f, cb = 0.0f;
-  const long row0 = (long)blockIdx.x * kRowsPerBlock;
-  const int h0 = (int)(row0 / a.Dv);
-  const int i0 = (int)(row0 - (long)h0 * a.Dv);
+  const int row0 = lblk * kRowsPerBlock;
+  const int h0 = row0 / Dv;
+  const int i0 = row0 - h0 * Dv;
   const int c0 = h0 / (a.Hv / a.Hk);
   const int n4 = a.k * DK / 4;
-  if (LDS_KQ) {
+  // PREP: the inputs of the block's q/k channel (threads 0..2Dk-1), of its v
+  // channel (threads VB..VB+15) and of its gates (threads GB..GB+k-1); every
+  // thread issues all of them, clamped, so the waits are static
+  constexpr int VB = DK == 128 ? 0 : 128, GB = 192;
+  float xq[PREP ? kConvWin : 1], xv[PREP ? kConvWin : 1];
+  float4 wq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), wv = wq;
+  float pa = 0.0f, pb = 0.0f, pal = 0.0f, pdb = 0.0f;
+  const int ratio = a.Hv / a.Hk;
+  const int cq_ch = min((int)threadIdx.x, 2 * DK - 1);
+  const int c_qk = cq_ch < DK ? c0 * DK + cq_ch : (a.Hk + c0) * DK + cq_ch - DK;
+  const int rv = min(max((int)threadIdx.x - VB, 0), kRowsPerBlock - 1);
+  const int c_v = 2 * a.Hk * DK + h0 * DK + i0 + rv;
+  if constexpr (PREP) {
+    // gate inputs first: their wave forms the gates while the rest arrives
+    const int tg = min(max((int)threadIdx.x - GB, 0), a.k - 1);
+    pa = a.ga[tg * a.Hv + h0];
+    pb = a.gb[tg * a.Hv + h0];
+    pal = a.A_log[h0];
+    pdb = a.dt_bias[h0];
+    __builtin_amdgcn_sched_barrier(0);
+    gdn_conv_load(a.qkv, a.hist, a.C, c_qk, a.k, xq);
+    gdn_conv_load(a.qkv, a.hist, a.C, c_v, a.k, xv);
+    wq = reinterpret_cast<const float4*>(a.conv_w)[c_qk];
+    wv = reinterpret_cast<const float4*>(a.conv_w)[c_v];
+  }
+  if (LDS_KQ && !PREP) {
     // every row of the block is in head h0 (and qk head c0).  The loads are
     // unconditional (indices past the data are clamped and the values
     // discarded), so the compiler can count them exactly in its waits.
@@ -87,19 +151,51 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     }
     const int tv = min((int)threadIdx.x, a.k * kRowsPerBlock - 1);
     const int tt = tv / kRowsPerBlock, r = min(tv - tt * kRowsPerBlock, (int)(nrows - 1 - row0));
-    cv = a.v[((long)tt * a.Hv + h0) * a.Dv + i0 + r];
+    cv = a.v[((long)tt * a.Hv + h0) * Dv + i0 + r];
     const int tg = min((int)threadIdx.x, a.k - 1);
     cg = a.g[tg * a.Hv + h0];
     cb = a.beta[tg * a.Hv + h0];
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the staging loads ahead of the state loads
   {
-    const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + (active ? row : nrows - 1) * DK);
+    const float4* sin4 = reinterpret_cast<const float4*>(a.S_in + (size_t)(active ? row : nrows - 1) * DK);
 #pragma unroll
     for (int j = 0; j < NV4; ++j) S[j] = load_nt(sin4 + sub + 16 * j);  // the state: read once per call
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (LDS_KQ) {
+  if constexpr (PREP) {
+    // conv of the q/k channel and the per-wave sums of squares; the conv
+    // outputs go to LDS unnormalised, each row's factor is applied as it is
+    // read in the row loop
+    const int tid = threadIdx.x, wave = tid >> 6, k = a.k;
+    if (tid >= GB && tid < GB + k) {
+      s_g[tid - GB] = gdn_decay(pa, pal, pdb);
+      s_b[tid - GB] = gdn_beta(pb);
+    }
+    float o[SDV_MAX_ROWS];
+    gdn_conv_rows(wq, xq, a.conv_act, o);
+    if (tid < 2 * DK) {  // whole waves: q, then k
+      float ws[SDV_MAX_ROWS];
+      gdn_wave_sq_sums(o, ws);
+      if ((tid & 63) == 0) {
+#pragma unroll
+        for (int t = 0; t < SDV_MAX_ROWS; ++t) s_part[wave][t] = ws[t];
+      }
+      float* dst = reinterpret_cast<float*>(tid < DK ? s_q : s_k);
+      const int ch = tid < DK ? tid : tid - DK;
+#pragma unroll
+      for (int t = 0; t < SDV_MAX_ROWS; ++t)
+        if (t < k) dst[t * DK + ch] = o[t];
+    }
+    if (tid >= VB && tid < VB + kRowsPerBlock) {
+      float ov[SDV_MAX_ROWS];
+      gdn_conv_rows(wv, xv, a.conv_act, ov);
+#pragma unroll
+      for (int t = 0; t < SDV_MAX_ROWS; ++t)
+        if (t < k) s_v[t * kRowsPerBlock + rv] = ov[t];
+    }
+    __syncthreads();
+  } else if (LDS_KQ) {
 #pragma unroll
     for (int u = 0; u < KQ_PER_THREAD; ++u) {
       const int t = threadIdx.x + 256 * u;
@@ -117,66 +213,114 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   }
   if (!active) return;  // whole 16-lane groups leave together
 
-  for (int t = 0; t < a.k; ++t) {
-    float gt, bt, vt;
-    float4 kt[NV4], qt[NV4];
-    if (LDS_KQ) {
-      gt = s_g[t];
-      bt = s_b[t];
-      vt = s_v[t * kRowsPerBlock + lrow];
+  // PREP: the window [history; rows] of the block's channels, stored once
+  // the state has arrived (stores issued earlier would be counted in the
+  // waits for it): the v columns by their block, the q/k columns by the first
+  // block of the qk head
+  auto window_out = [&]() {
+    const int tid = threadIdx.x, k = a.k;
+    if (tid >= VB && tid < VB + kRowsPerBlock) {
 #pragma unroll
-      for (int j = 0; j < NV4; ++j) {
-        kt[j] = s_k[t * (DK / 4) + sub + 16 * j];
-        qt[j] = s_q[t * (DK / 4) + sub + 16 * j];
+      for (int j = 0; j < kConvWin; ++j)
+        if (j < kConvHist + k) a.window[(size_t)j * a.C + c_v] = xv[j];
+    }
+    if (tid < 2 * DK && h0 % ratio == 0 && i0 == 0) {
+#pragma unroll
+      for (int j = 0; j < kConvWin; ++j)
+        if (j < kConvHist + k) a.window[(size_t)j * a.C + c_qk] = xq[j];
+    }
+  };
+  // one row of the recurrence; the rows are expanded with t a constant, so
+  // the LDS reads of a row, which need nothing of the previous row, can be
+  // issued ahead of it
+  auto row_step = [&](auto tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc)::value;
+    {
+      float gt, bt, vt;
+      float4 kt[NV4], qt[NV4];
+      if (LDS_KQ) {
+        gt = s_g[t];
+        bt = s_b[t];
+        vt = s_v[t * kRowsPerBlock + lrow];
+  #pragma unroll
+        for (int j = 0; j < NV4; ++j) {
+          kt[j] = s_k[t * (DK / 4) + sub + 16 * j];
+          qt[j] = s_q[t * (DK / 4) + sub + 16 * j];
+        }
+        if constexpr (PREP) {
+          // the L2 norm of row t: the q waves' sums in wave order, then the k waves'
+          float sq = s_part[0][t], sk = s_part[DK / 64][t];
+  #pragma unroll
+          for (int w2 = 1; w2 < DK / 64; ++w2) {
+            sq = sq + s_part[w2][t];
+            sk = sk + s_part[DK / 64 + w2][t];
+          }
+          const float iq = gdn_inv_norm(sq, a.eps), ik = gdn_inv_norm(sk, a.eps);
+  #pragma unroll
+          for (int j = 0; j < NV4; ++j) {
+            kt[j].x = kt[j].x * ik;
+            kt[j].y = kt[j].y * ik;
+            kt[j].z = kt[j].z * ik;
+            kt[j].w = kt[j].w * ik;
+            qt[j].x = qt[j].x * iq;
+            qt[j].y = qt[j].y * iq;
+            qt[j].z = qt[j].z * iq;
+            qt[j].w = qt[j].w * iq;
+          }
+        }
+      } else {
+        gt = a.g[t * a.Hv + h];
+        bt = a.beta[t * a.Hv + h];
+        vt = a.v[((long)t * a.Hv + h) * Dv + i];
+        const float4* k4 = reinterpret_cast<const float4*>(a.kk + ((long)t * a.Hk + c) * DK);
+        const float4* q4 = reinterpret_cast<const float4*>(a.q + ((long)t * a.Hk + c) * DK);
+  #pragma unroll
+        for (int j = 0; j < NV4; ++j) {
+          kt[j] = k4[sub + 16 * j];
+          qt[j] = q4[sub + 16 * j];
+        }
       }
-    } else {
-      gt = a.g[t * a.Hv + h];
-      bt = a.beta[t * a.Hv + h];
-      vt = a.v[((long)t * a.Hv + h) * a.Dv + i];
-      const float4* k4 = reinterpret_cast<const float4*>(a.kk + ((long)t * a.Hk + c) * DK);
-      const float4* q4 = reinterpret_cast<const float4*>(a.q + ((long)t * a.Hk + c) * DK);
-#pragma unroll
+      // decay, then kv_mem on the decayed state
+      float m = 0.0f;
+  #pragma unroll
       for (int j = 0; j < NV4; ++j) {
-        kt[j] = k4[sub + 16 * j];
-        qt[j] = q4[sub + 16 * j];
+        S[j].x = gt * S[j].x;
+        S[j].y = gt * S[j].y;
+        S[j].z = gt * S[j].z;
+        S[j].w = gt * S[j].w;
+        m = fmaf(S[j].x, kt[j].x, m);
+        m = fmaf(S[j].y, kt[j].y, m);
+        m = fmaf(S[j].z, kt[j].z, m);
+        m = fmaf(S[j].w, kt[j].w, m);
+      }
+      m = row16_sum(m);
+      const float d = bt * (vt - m);
+      // rank-1 update and readout
+      float o = 0.0f;
+  #pragma unroll
+      for (int j = 0; j < NV4; ++j) {
+        S[j].x = fmaf(d, kt[j].x, S[j].x);
+        S[j].y = fmaf(d, kt[j].y, S[j].y);
+        S[j].z = fmaf(d, kt[j].z, S[j].z);
+        S[j].w = fmaf(d, kt[j].w, S[j].w);
+        o = fmaf(S[j].x, qt[j].x, o);
+        o = fmaf(S[j].y, qt[j].y, o);
+        o = fmaf(S[j].z, qt[j].z, o);
+        o = fmaf(S[j].w, qt[j].w, o);
+      }
+      o = row16_sum(o);
+      if (sub == 0) a.y[((long)t * a.Hv + h) * Dv + i] = o;
+      // snapshots are written once and read back at most once, after the call:
+      // streaming (nontemporal) stores keep them from displacing cached data
+      f32x4* dst = reinterpret_cast<f32x4*>(a.snaps[t] + (size_t)row * DK);
+  #pragma unroll
+      for (int j = 0; j < NV4; ++j) __builtin_nontemporal_store(f32x4{S[j].x, S[j].y, S[j].z, S[j].w}, dst + sub + 16 * j);
+      if constexpr (PREP) {
+        if (t == 0) window_out();
       }
     }
-    // decay, then kv_mem on the decayed state
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NV4; ++j) {
-      S[j].x = gt * S[j].x;
-      S[j].y = gt * S[j].y;
-      S[j].z = gt * S[j].z;
-      S[j].w = gt * S[j].w;
-      m = fmaf(S[j].x, kt[j].x, m);
-      m = fmaf(S[j].y, kt[j].y, m);
-      m = fmaf(S[j].z, kt[j].z, m);
-      m = fmaf(S[j].w, kt[j].w, m);
-    }
-    m = row16_sum(m);
-    const float d = bt * (vt - m);
-    // rank-1 update and readout
-    float o = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NV4; ++j) {
-      S[j].x = fmaf(d, kt[j].x, S[j].x);
-      S[j].y = fmaf(d, kt[j].y, S[j].y);
-      S[j].z = fmaf(d, kt[j].z, S[j].z);
-      S[j].w = fmaf(d, kt[j].w, S[j].w);
-      o = fmaf(S[j].x, qt[j].x, o);
-      o = fmaf(S[j].y, qt[j].y, o);
-      o = fmaf(S[j].z, qt[j].z, o);
-      o = fmaf(S[j].w, qt[j].w, o);
-    }
-    o = row16_sum(o);
-    if (sub == 0) a.y[((long)t * a.Hv + h) * a.Dv + i] = o;
-    // snapshots are written once and read back at most once, after the call:
-    // streaming (nontemporal) stores keep them from displacing cached data
-    f32x4* dst = reinterpret_cast<f32x4*>(a.snaps[t] + row * DK);
-#pragma unroll
-    for (int j = 0; j < NV4; ++j) __builtin_nontemporal_store(f32x4{S[j].x, S[j].y, S[j].z, S[j].w}, dst + sub + 16 * j);
-  }
+  };
+  for_rows(std::make_integer_sequence<int, SDV_MAX_ROWS>{}, a.k, row_step);
 }
 
 }  // namespace
@@ -184,7 +328,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
 hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
                       const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
                       float* y, float* const* snaps, hipStream_t st) {
-  GdnArgs a;
+  GdnArgs a{};
   a.S_in = S_in;
   a.q = q;
   a.kk = kk;
@@ -201,13 +345,46 @@ hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const 
   const bool lds = (Dv % kRowsPerBlock) == 0;
   const dim3 grid((unsigned)blocks), block(kRowsPerBlock * 16);
   if (Dk == 64 && lds)
-    hipLaunchKernelGGL((gdn_verify_kernel<64, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<64, true, false>), grid, block, 0, st, a);
   else if (Dk == 64)
-    hipLaunchKernelGGL((gdn_verify_kernel<64, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<64, false, false>), grid, block, 0, st, a);
   else if (Dk == 128 && lds)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<128, true, false>), grid, block, 0, st, a);
   else if (Dk == 128)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<128, false, false>), grid, block, 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
+                                  const float* ga, const float* gb, const float* A_log, const float* dt_bias, int k,
+                                  int Hv, int Hk, int D, int conv_act, float eps, float* window, float* y,
+                                  float* const* snaps, hipStream_t st) {
+  GdnArgs a{};
+  a.S_in = S_in;
+  a.k = k;
+  a.Hv = Hv;
+  a.Hk = Hk;
+  a.Dv = D;
+  a.y = y;
+  for (int t = 0; t < SDV_MAX_ROWS; ++t) a.snaps[t] = t < k ? snaps[t] : nullptr;
+  a.qkv = qkv;
+  a.hist = hist;
+  a.conv_w = conv_w;
+  a.ga = ga;
+  a.gb = gb;
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.C = 2 * Hk * D + Hv * D;
+  a.conv_act = conv_act;
+  a.eps = eps;
+  a.window = window;
+  const dim3 grid((unsigned)((long)Hv * D / kRowsPerBlock)), block(kRowsPerBlock * 16);
+  if (D == 64)
+    hipLaunchKernelGGL((gdn_verify_kernel<64, true, true>), grid, block, 0, st, a);
+  else if (D == 128)
+    hipLaunchKernelGGL((gdn_verify_kernel<128, true, true>), grid, block, 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

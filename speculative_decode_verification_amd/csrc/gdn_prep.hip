@@ -14,22 +14,20 @@
 // D channels (q heads, then k heads, then v heads), one thread per channel,
 // all rows.  A thread loads its channel's 3 + k inputs and 4 taps, applies
 // the taps in order (fma chain from the oldest input), and writes the window
-// [history; rows] that rollback selects from.  q and k are divided per (row,
-// head) by sqrt(sum of squares + eps); the sum is a fixed 16-lane DPP sum,
+// [history; rows] that rollback selects from.  q and k are multiplied per
+// (row, head) by rsqrt(sum of squares + eps); the sum is a fixed 16-lane DPP sum,
 // the four row totals of a wave in row order, then the waves in order, so
-// every row is computed the same way at every width.  One extra workgroup
-// forms g and beta for every (row, v head).
+// every row is computed the same way at every width.  The workgroup of v
+// head h also forms g and beta of head h for every row (thread t, row t).
 //
 // Output norm.  One workgroup per (row, v head) of Dv threads: the mean of
 // squares in the same fixed order, then y / sqrt(mean + eps) * w * act(z).
 
-#include "common.h"
+#include "gdn_prep_core.h"
 
 namespace sdv {
 
 namespace {
-
-constexpr int kTaps = 4;
 
 struct PrepArgs {
   const float* qkv;      // [k][C]
@@ -49,19 +47,6 @@ struct PrepArgs {
   float* window;  // [k + 3][C]
 };
 
-// Sum over the 64 lanes of a wave, in every lane: a 16-lane DPP sum, then the
-// four row totals in row order.
-__device__ __forceinline__ float wave_sum(float x) {
-  const float r = row16_sum(x);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
-
 // Block of D (64 or 128) channels, all k rows.
 template <int D>
 __global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
@@ -69,54 +54,43 @@ __global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const int nq = a.Hk, nqk = 2 * a.Hk;
   const int blk = blockIdx.x;
-  if (blk == nqk + a.Hv) {
-    // gates: one thread per (row, v head)
-    for (int e = tid; e < a.k * a.Hv; e += D) {
-      const int h = e % a.Hv;
-      const float x = a.a[e] + a.dt_bias[h];
-      a.g[e] = expf(-expf(a.A_log[h]) * softplusf_(x));
-      a.beta[e] = 1.0f / (1.0f + expf(-a.b[e]));
-    }
-    return;
-  }
-  // channel of this thread
   const bool is_q = blk < nq, is_k = !is_q && blk < nqk;
+  const int hv = max(blk - nqk, 0);
   const int c = is_q ? blk * a.Dk + tid : (is_k ? nq * a.Dk + (blk - nq) * a.Dk + tid
-                                                : nqk * a.Dk + (blk - nqk) * a.Dv + tid);
+                                                : nqk * a.Dk + hv * a.Dv + tid);
   const int C = a.C, k = a.k;
-  // the history and every row's input of the channel, issued together
-  float x[3 + SDV_MAX_ROWS];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) x[j] = a.hist[(size_t)j * C + c];
-#pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) x[3 + t] = a.qkv[(size_t)min(t, k - 1) * C + c];
+  // every load first: the channel's history and rows, its taps, and the gate
+  // inputs of (row tid, head hv) (clamped; used by the v blocks only)
+  float x[kConvWin];
+  gdn_conv_load(a.qkv, a.hist, C, c, k, x);
   const float4 w = reinterpret_cast<const float4*>(a.conv_w)[c];
+  const int tg = min(tid, k - 1);
+  const float ga = a.a[tg * a.Hv + hv], gb = a.b[tg * a.Hv + hv];
+  const float al = a.A_log[hv], db = a.dt_bias[hv];
   // the window [history; rows] for rollback by selection
 #pragma unroll
-  for (int j = 0; j < 3 + SDV_MAX_ROWS; ++j)
-    if (j < 3 + k) a.window[(size_t)j * C + c] = x[j];
+  for (int j = 0; j < kConvWin; ++j)
+    if (j < kConvHist + k) a.window[(size_t)j * C + c] = x[j];
   float o[SDV_MAX_ROWS];
-#pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
-    float acc = w.x * x[t];
-    acc = fmaf(w.y, x[t + 1], acc);
-    acc = fmaf(w.z, x[t + 2], acc);
-    acc = fmaf(w.w, x[t + 3], acc);
-    if (a.conv_act == SDV_CONV_SILU) acc = siluf_(acc);
-    o[t] = acc;
-  }
+  gdn_conv_rows(w, x, a.conv_act, o);
   if (!is_q && !is_k) {
-    const int hv = blk - nqk;
 #pragma unroll
     for (int t = 0; t < SDV_MAX_ROWS; ++t)
       if (t < k) a.v[((size_t)t * a.Hv + hv) * a.Dv + tid] = o[t];
+    if (tid < k) {
+      a.g[tid * a.Hv + hv] = gdn_decay(ga, al, db);
+      a.beta[tid * a.Hv + hv] = gdn_beta(gb);
+    }
     return;
   }
   // per-row L2 norm over the head's D channels
+  {
+    float ws[SDV_MAX_ROWS];
+    gdn_wave_sq_sums(o, ws);
+    if ((tid & 63) == 0) {
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
-    const float ws = wave_sum(o[t] * o[t]);
-    if ((tid & 63) == 0) s_part[wave][t] = ws;
+      for (int t = 0; t < SDV_MAX_ROWS; ++t) s_part[wave][t] = ws[t];
+    }
   }
   __syncthreads();
   const int h = is_q ? blk : blk - nq;
@@ -127,7 +101,7 @@ __global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
       float ss = s_part[0][t];
 #pragma unroll
       for (int w2 = 1; w2 < D / 64; ++w2) ss = ss + s_part[w2][t];
-      dst[((size_t)t * a.Hk + h) * a.Dk + tid] = o[t] / sqrtf(ss + a.eps);
+      dst[((size_t)t * a.Hk + h) * a.Dk + tid] = o[t] * gdn_inv_norm(ss, a.eps);
     }
   }
 }
@@ -148,7 +122,7 @@ __global__ __launch_bounds__(D) void gdn_gated_norm_kernel(NormArgs a) {
   const size_t base = (size_t)blockIdx.x * D;  // (row, v head)
   const float y = a.y[base + tid];
   const float z = a.z[base + tid];
-  const float ws = wave_sum(y * y);
+  const float ws = gdn_wave_sum(y * y);
   if ((tid & 63) == 0) s_part[wave] = ws;
   __syncthreads();
   float ss = s_part[0];
@@ -167,7 +141,7 @@ hipError_t gdn_prepare_launch(const float* qkv, const float* hist, const float* 
                               float* beta, float* window, hipStream_t st) {
   PrepArgs a{qkv, hist, conv_w, ga, gb, A_log, dt_bias, k, Hv, Hk, Dk, Dv, 2 * Hk * Dk + Hv * Dv, conv_act,
              eps, q, kk, v, g, beta, window};
-  const dim3 grid((unsigned)(2 * Hk + Hv + 1));
+  const dim3 grid((unsigned)(2 * Hk + Hv));
   if (Dk == 64)
     hipLaunchKernelGGL(gdn_prepare_kernel<64>, grid, dim3(64), 0, st, a);
   else if (Dk == 128)

@@ -15,7 +15,7 @@ from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, GATE_SIGMOID, GATE_S
                    MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ4, SdvQ4T, check, lib)
 
 __all__ = ["Q4Weight", "TiledQ4", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
-           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_gated_norm_k",
+           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_gated_norm_k",
            "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
 
@@ -377,6 +377,44 @@ def _norm_args(y, z, w, gate_act, eps, out):
             ctypes.c_float(eps), _need(out, "out", f, n, dev), _stream(y)]
 
 
+def _verify_prep_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y, conv_act, eps):
+    Hv, Dv, Dk = S_in.shape
+    k, C = qkv.shape
+    dev = S_in.device
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError(f"qkv has {C} channels, expected 2*{Hk}*{Dk} + {Hv}*{Dv}")
+    if len(snaps) != k:
+        raise ValueError(f"{len(snaps)} snapshot buffers for k={k} rows")
+    f = torch.float32
+    st = Hv * Dv * Dk
+    arr = (ctypes.c_void_p * k)(*[_need(s, f"snaps[{t}]", f, st, dev).value for t, s in enumerate(snaps)])
+    return [_need(S_in, "S_in", f, st, dev), _need(qkv, "qkv", f, k * C, dev), _need(hist, "hist", f, 3 * C, dev),
+            _need(conv_w, "conv_w", f, 4 * C, dev), _need(a, "a", f, k * Hv, dev), _need(b, "b", f, k * Hv, dev),
+            _need(A_log, "A_log", f, Hv, dev), _need(dt_bias, "dt_bias", f, Hv, dev), k, Hv, Hk, Dk, Dv, conv_act,
+            ctypes.c_float(eps), _need(window, "window", f, (k + 3) * C, dev), _need(y, "y", f, k * Hv * Dv, dev),
+            arr, _stream(y)]
+
+
+def gdn_verify_prep_k(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y=None,
+                      conv_act=CONV_NONE, eps=1e-6):
+    """gdn_prepare_k followed by gdn_verify_k in one launch: from the
+    projections (qkv [k, C], hist [3, C], conv_w [C, 4], a, b [k, Hv], A_log,
+    dt_bias [Hv]) and S_in [Hv, Dv, Dk], writes the snapshots, the window
+    [k + 3, C] and returns y [k, Hv, Dv]."""
+    Hv, Dv, _ = S_in.shape
+    if y is None:
+        y = torch.empty((qkv.shape[0], Hv, Dv), dtype=torch.float32, device=S_in.device)
+    check(lib().sdv_gdn_verify_prep_k(*_verify_prep_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps,
+                                                         window, y, conv_act, eps)))
+    return y
+
+
+def bind_gdn_verify_prep_k(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y, conv_act=CONV_NONE,
+                           eps=1e-6):
+    return BoundCall("sdv_gdn_verify_prep_k", _verify_prep_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk,
+                                                                snaps, window, y, conv_act, eps))
+
+
 def gdn_gated_norm_k(y, z, w, gate_act=GATE_SIGMOID, eps=1e-6, out=None):
     """y / sqrt(mean(y^2) + eps) * w * act(z) per (row, v head); y, z fp32 [k, Hv, Dv], w [Dv]."""
     if out is None:
@@ -449,6 +487,16 @@ class BoundCall:
 
     def __call__(self):
         check(self._fn(*self._args))
+
+    def replaced(self, changes):
+        """The same call with the arguments at the given positions replaced
+        (already marshalled values, e.g. ctypes.c_void_p of a device pointer)."""
+        args = list(self._args)
+        for i, v in changes.items():
+            args[i] = v
+        out = BoundCall.__new__(BoundCall)
+        out._fn, out._args, out.name = self._fn, tuple(args), self.name
+        return out
 
 
 def bind_qmv_k(W, act, mode, out):

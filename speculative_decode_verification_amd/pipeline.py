@@ -12,6 +12,8 @@ buffer is live (Red Lite dev45, "What it is": pointer swap with the
 snapshots), so no state is copied.
 """
 
+import ctypes
+
 import torch
 
 from . import ops
@@ -148,14 +150,13 @@ class GdnLayer:
         self.windows = [torch.empty((self.k + 3, C), dtype=torch.float32, device=dev) for _ in range(2)]
         self.win = 0
         self.prepped = False
-        self.prep_out = [{n: t for n, t in ops.gdn_prepare_outputs(self.k, self.Hv, Hk, self.Dk, dev).items()
-                          if n != "window"} for _ in range(2)]
+        self.prep_out = {n: t for n, t in ops.gdn_prepare_outputs(self.k, self.Hv, Hk, self.Dk, dev).items()
+                         if n != "window"}
         self._bound_prep = {}
         return self
 
     def _prep_out(self, rows):
-        o = self.prep_out[self.win]
-        out = {n: t[:rows] for n, t in o.items()}
+        out = {n: t[:rows] for n, t in self.prep_out.items()}
         out["window"] = self.windows[self.win][:rows + 3]
         return out
 
@@ -168,19 +169,91 @@ class GdnLayer:
         self.prepped = True
         return out
 
+    def bind_tail(self, z, norm_w, out, gate_act=ops.GATE_SIGMOID, eps=1e-6):
+        """The output norm of all k rows for fixed z [k, Hv, Dv] and out."""
+        self._bound_tail = ops.bind_gdn_gated_norm_k(self.y, z, norm_w, out, gate_act, eps)
+        return self
+
+    def run_tail_bound(self):
+        self._bound_tail()
+
+    def _prep_call(self, qkv, a, b, win, hist):
+        key = (win, hist.data_ptr(), qkv.data_ptr(), a.data_ptr(), b.data_ptr())
+        call = self._bound_prep.get(key)
+        if call is None:
+            conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+            rows = qkv.shape[0]
+            out = {n: t[:rows] for n, t in self.prep_out.items()}
+            out["window"] = self.windows[win][:rows + 3]
+            call = ops.bind_gdn_prepare_k(qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, self.Dk, out, act, eps)
+            self._bound_prep[key] = call
+        return call
+
+    def prebind_prepare(self, qkv, a, b):
+        """Marshal ``run_prepare_bound`` for every (window, history source)
+        pair it can meet, so later steps only look the call up."""
+        for win in (0, 1):
+            self._prep_call(qkv, a, b, win, self.hist)
+            for j in range(self.k + 1):
+                self._prep_call(qkv, a, b, win, self.windows[win ^ 1][j:j + 3])
+        return self
+
     def run_prepare_bound(self, qkv, a, b):
         """``prepare`` for fixed qkv, a, b buffers, marshalled once per
         (window, history source) pair."""
-        key = (self.win, self.hist.data_ptr(), qkv.data_ptr(), a.data_ptr(), b.data_ptr())
-        call = self._bound_prep.get(key)
-        out = self._prep_out(qkv.shape[0])
+        self._prep_call(qkv, a, b, self.win, self.hist)()
+        self.prepped = True
+        return self._prep_out(qkv.shape[0])
+
+    def verify_from_proj(self, qkv, a, b):
+        """Preparation and recurrence in one launch from the projections qkv
+        [rows, C], a, b [rows, Hv]; returns y [rows, Hv, Dv]."""
+        conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+        rows = qkv.shape[0]
+        self.snap_ids = [i for i in range(len(self.slots)) if i != self.live][:rows]
+        y = self.y[:rows]
+        ops.gdn_verify_prep_k(self.state, qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk,
+                              [self.slots[i] for i in self.snap_ids], self.windows[self.win][:rows + 3], y, act, eps)
+        self.prepped = True
+        return y
+
+    # argument positions of sdv_gdn_verify_prep_k that change between steps
+    _FP_S_IN, _FP_HIST, _FP_WINDOW, _FP_SNAPS = 0, 2, 15, 17
+
+    def bind_from_proj(self, qkv, a, b):
+        """Marshal ``verify_from_proj`` for fixed qkv, a, b buffers; the state,
+        history, window and snapshot pointers are patched per step from
+        prebuilt values (no argument checks on the host path after this)."""
+        conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+        rows = qkv.shape[0]
+        self._fp_rows = rows
+        self._fp_snaps = {}
+        for live in range(len(self.slots)):
+            ids = [i for i in range(len(self.slots)) if i != live][:rows]
+            arr = (ctypes.c_void_p * rows)(*[self.slots[i].data_ptr() for i in ids])
+            self._fp_snaps[live] = (ids, arr)
+        ids0 = self._fp_snaps[self.live][0]
+        self._fp_template = ops.bind_gdn_verify_prep_k(self.state, qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk,
+                                                       [self.slots[i] for i in ids0],
+                                                       self.windows[self.win][:rows + 3], self.y[:rows], act, eps)
+        self._fp_cache = {}
+        return self
+
+    def run_from_proj_bound(self):
+        key = (self.live, self.win, self.hist.data_ptr())
+        call = self._fp_cache.get(key)
+        ids, arr = self._fp_snaps[self.live]
         if call is None:
-            conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
-            call = ops.bind_gdn_prepare_k(qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk, self.Dk, out, act, eps)
-            self._bound_prep[key] = call
+            call = self._fp_template.replaced({
+                self._FP_S_IN: ctypes.c_void_p(self.state.data_ptr()),
+                self._FP_HIST: ctypes.c_void_p(self.hist.data_ptr()),
+                self._FP_WINDOW: ctypes.c_void_p(self.windows[self.win].data_ptr()),
+                self._FP_SNAPS: arr})
+            self._fp_cache[key] = call
+        self.snap_ids = ids
         call()
         self.prepped = True
-        return out
+        return self.y[:self._fp_rows]
 
     def rollback(self, j):
         """Make the state after the accepted prefix of j rows live (no copy);

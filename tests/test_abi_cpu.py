@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 20
+    assert len(names) == 21
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -373,3 +373,33 @@ def test_gated_norm_validation(lib):
     assert norm(lib, out=P + 16) == L.SDV_EALIAS                     # in place over y
     assert lib.sdv_last_error().decode() == "output out overlaps input y"
     assert norm(lib, out=P + 0x200000) == L.SDV_EALIAS
+
+
+def verify_prep(lib, k=2, Hv=4, Hk=2, D=64, Dv=None, act=0, eps=1e-6, snaps=None, **over):
+    ptr = dict(S_in=P + 0x4000000, qkv=P, hist=P + 0x100000, conv_w=P + 0x200000, a=P + 0x300000, b=P + 0x310000,
+               A_log=P + 0x320000, dt_bias=P + 0x330000, window=P + 0x800000, y=P + 0x900000)
+    ptr.update(over)
+    snaps = snaps if snaps is not None else [P + 0x5000000 + 0x1000000 * t for t in range(k)]
+    arr = (ctypes.c_void_p * max(1, len(snaps)))(*snaps)
+    return lib.sdv_gdn_verify_prep_k(ptr["S_in"], ptr["qkv"], ptr["hist"], ptr["conv_w"], ptr["a"], ptr["b"],
+                                     ptr["A_log"], ptr["dt_bias"], k, Hv, Hk, D, D if Dv is None else Dv, act, eps,
+                                     ptr["window"], ptr["y"], arr, None)
+
+
+def test_verify_prep_validation(lib):
+    assert verify_prep(lib, k=0) == L.SDV_EWIDTH
+    assert verify_prep(lib, k=10) == L.SDV_EWIDTH
+    assert verify_prep(lib, Hv=5) == L.SDV_ELAYOUT
+    assert verify_prep(lib, D=128, Dv=64) == L.SDV_ELAYOUT
+    assert verify_prep(lib, D=32) == L.SDV_ELAYOUT
+    assert verify_prep(lib, act=7) == L.SDV_EINVAL
+    assert verify_prep(lib, eps=float("nan")) == L.SDV_ERANGE
+    assert verify_prep(lib, S_in=0) == L.SDV_EINVAL
+    assert verify_prep(lib, snaps=[P + 0x5000000, 0]) == L.SDV_EINVAL
+    s = P + 0x5000000
+    assert verify_prep(lib, snaps=[s, s]) == L.SDV_EALIAS
+    assert verify_prep(lib, snaps=[s, P + 0x4000000 + 64]) == L.SDV_EALIAS      # snapshot over S_in
+    assert verify_prep(lib, window=P + 0x100000) == L.SDV_EALIAS                # window over hist
+    assert lib.sdv_last_error().decode() == "output window overlaps input hist"
+    assert verify_prep(lib, y=P + 0x800000 + 4096) == L.SDV_EALIAS              # y over window
+    assert verify_prep(lib, y=P + 0x5000000 + 64) == L.SDV_EALIAS               # y over a snapshot

@@ -195,3 +195,77 @@ def test_layer_steps_with_rollback():
         hist_ref = ref["window"][j:j + 3]
         assert_close(to_np(live)[None], S_ref[None], f"step {step} state after {j} rows")
         assert np.array_equal(to_np(layer.hist), hist_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("hv,hk,d", SHAPES + [(3, 1, 64), (6, 2, 128)])
+@pytest.mark.parametrize("act", ["none", "silu"])
+@pytest.mark.parametrize("k", [1, 4, 9])
+def test_fused_prep_equals_separate_calls(hv, hk, d, act, k):
+    """sdv_gdn_verify_prep_k: y, every snapshot and the window equal the
+    preparation followed by the recurrence, bit for bit, and the oracle
+    within tolerance (head counts whose block count is and is not a multiple
+    of 8, so both block placements run)."""
+    ops = _ops()
+    banner(f"gdn verify+prep hv={hv} hk={hk} d={d} act={act} k={k}")
+    raw = synth.gdn_raw_inputs(46, hv, k, hv, hk, d, d)
+    S = synth.gdn_state(46, hv, hv, d, d)
+    dd = upload(raw)
+    S_d = sdev.upload_f32(S, DEV)
+    p = ops.gdn_prepare_k(dd["qkv"], dd["hist"], dd["conv_w"], dd["a"], dd["b"], dd["A_log"], dd["dt_bias"], hk, d,
+                          ACTS[act])
+    snaps_a = [torch.empty_like(S_d) for _ in range(k)]
+    y_a = ops.gdn_verify_k(S_d, p["q"], p["k"], p["v"], p["g"], p["beta"], snaps_a)
+    snaps_b = [torch.full_like(S_d, float("nan")) for _ in range(k)]
+    win_b = torch.full_like(p["window"], float("nan"))
+    y_b = ops.gdn_verify_prep_k(S_d, dd["qkv"], dd["hist"], dd["conv_w"], dd["a"], dd["b"], dd["A_log"],
+                                dd["dt_bias"], hk, snaps_b, win_b, conv_act=ACTS[act])
+    torch.cuda.synchronize()
+    assert torch.equal(y_a, y_b)
+    assert torch.equal(p["window"], win_b)
+    for t in range(k):
+        assert torch.equal(snaps_a[t], snaps_b[t]), t
+    ref = oracle.gdn_prepare(raw["qkv"], raw["hist"], raw["conv_w"], raw["a"], raw["b"], raw["A_log"],
+                             raw["dt_bias"], hk, hv, d, d, act)
+    y_ref, s_ref = oracle.gdn_verify(S, ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"])
+    assert_close(to_np(y_b), y_ref, "y")
+    assert_close(np.stack([to_np(s) for s in snaps_b]), np.stack(s_ref), "snapshots")
+
+
+def test_fused_layer_steps_with_rollback():
+    """The layer's one-launch path over four steps (bound calls), against the
+    oracle run on the accepted stream, and against the two-launch path bit
+    for bit."""
+    from speculative_decode_verification_amd import pipeline
+    banner("gdn fused layer steps with rollback")
+    hv, hk, d, k = 48, 16, 128, 9
+    S = synth.gdn_state(47, 0, hv, d, d)
+    raw0 = synth.gdn_raw_inputs(47, 0, k, hv, hk, d, d)
+    mk = lambda: pipeline.GdnLayer(sdev.upload_f32(S, DEV), k).attach_prep(
+        sdev.upload_f32(raw0["hist"], DEV), sdev.upload_f32(raw0["conv_w"], DEV), sdev.upload_f32(raw0["A_log"], DEV),
+        sdev.upload_f32(raw0["dt_bias"], DEV), hk)
+    fused, split = mk(), mk()
+    S_ref = S.astype(np.float64)
+    hist_ref = raw0["hist"].astype(np.float64)
+    bufs = {n: torch.empty_like(t) for n, t in upload(raw0).items()}
+    fused.bind_from_proj(bufs["qkv"], bufs["a"], bufs["b"])
+    for step, j in enumerate([3, 9, 0, 6, 1]):
+        raw = synth.gdn_raw_inputs(47, 0, k, hv, hk, d, d, step=step + 1)
+        for n, t in upload(raw).items():
+            bufs[n].copy_(t)
+        y = fused.run_from_proj_bound()
+        p = split.prepare(bufs["qkv"], bufs["a"], bufs["b"])
+        y2 = split.verify(p["q"], p["k"], p["v"], p["g"], p["beta"])
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), step
+        ref = oracle.gdn_prepare(raw["qkv"], hist_ref, raw["conv_w"], raw["a"], raw["b"], raw["A_log"],
+                                 raw["dt_bias"], hk, hv, d, d)
+        y_ref, snaps = oracle.gdn_verify(S_ref, ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"])
+        assert_close(to_np(y), y_ref, f"step {step} y")
+        live, live2 = fused.rollback(j), split.rollback(j)
+        assert torch.equal(live, live2)
+        assert torch.equal(fused.hist, split.hist)
+        if j > 0:
+            S_ref = snaps[j - 1]
+        hist_ref = ref["window"][j:j + 3]
+        assert_close(to_np(live)[None], S_ref[None], f"step {step} state after {j} rows")
+        assert np.array_equal(to_np(fused.hist), hist_ref.astype(np.float32))
