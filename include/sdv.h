@@ -30,7 +30,8 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *     the default stream).  Results are visible after the stream reaches the
  *     call.  Calls are reentrant; two calls whose outputs overlap race.
- *   - Row width k must be 1..SDV_MAX_ROWS (9), the widths the pages verify.
+ *   - Row width k must be 1..SDV_MAX_ROWS (32): the widths 1-9 of the dense and
+ *     MoE checkpoints and the widths 1, 4, 8, 16, 32 of the Flash-Next verifier.
  *   - Every row of a width-k call is bit-identical to the same row computed
  *     by a width-1 call (fixed per-output reduction order, independent of k
  *     and of which other rows share an expert).
@@ -61,7 +62,7 @@ typedef void *sdv_stream_t; /* hipStream_t */
 #define SDV_EALIAS (-5)  /* an output overlaps an input or another output */
 #define SDV_EHIP (-6)    /* the HIP runtime reported an error at launch */
 
-#define SDV_MAX_ROWS 9
+#define SDV_MAX_ROWS 32
 #define SDV_GROUP 64
 #define SDV_MAX_EXPERTS 1024
 #define SDV_MAX_TOPK 16

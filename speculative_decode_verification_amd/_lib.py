@@ -6,7 +6,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdv.so")
 
 SDV_OK, SDV_EINVAL, SDV_EWIDTH, SDV_ELAYOUT, SDV_ERANGE, SDV_EALIAS, SDV_EHIP = 0, -1, -2, -3, -4, -5, -6
-MAX_ROWS, GROUP, MAX_EXPERTS, MAX_TOPK = 9, 64, 1024, 16
+MAX_ROWS, GROUP, MAX_EXPERTS, MAX_TOPK = 32, 64, 1024, 16
 MODE_PLAIN, MODE_GATEUP_SWIGLU = 0, 1
 ACT_BF16, ACT_F32 = 0, 1
 ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1

@@ -15,9 +15,9 @@
 // Stage 1, grid (chunks, rows) of 256 threads: each workgroup takes the
 // largest key of a 4096-element chunk of one row (16 coalesced loads per
 // thread, all issued before any is used) and writes it to the workspace.
-// Stage 2, one workgroup: wave r reduces row r's chunk keys to its token,
-// then one thread counts the accepted drafts.  Integer keys make the result
-// independent of the reduction order.
+// Stage 2, one workgroup of up to 16 waves: wave w reduces the chunk keys of
+// rows w, w + 16 to their tokens, then one thread counts the accepted
+// drafts.  Integer keys make the result independent of the reduction order.
 
 #include "common.h"
 
@@ -92,20 +92,23 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_partial_kernel(AcceptAr
   }
 }
 
-__global__ __launch_bounds__(64 * SDV_MAX_ROWS) void accept_final_kernel(AcceptArgs a) {
+constexpr int kFinalWaves = 16;
+
+__global__ __launch_bounds__(64 * kFinalWaves) void accept_final_kernel(AcceptArgs a) {
   __shared__ int32_t s_tok[SDV_MAX_ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (wave < a.k) {
+  const int nw = blockDim.x >> 6;
+  for (int r = wave; r < a.k; r += nw) {
     uint64_t best = 0;
     for (int c = lane; c < a.chunks; c += 64) {
-      const uint64_t key = a.keys[(size_t)wave * a.chunks + c];
+      const uint64_t key = a.keys[(size_t)r * a.chunks + c];
       best = key > best ? key : best;
     }
     best = wave_max_u64(best);
     const int tok = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : -1;
     if (lane == 0) {
-      a.tokens[wave] = tok;
-      s_tok[wave] = tok;
+      a.tokens[r] = tok;
+      s_tok[r] = tok;
     }
   }
   __syncthreads();
@@ -146,7 +149,7 @@ hipError_t accept_launch(const float* logits, const float* noise, float inv_temp
   hipLaunchKernelGGL(accept_partial_kernel, dim3(a.chunks, k), dim3(kAcceptThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(64 * k), 0, st, a);
+  hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(64 * (k < kFinalWaves ? k : kFinalWaves)), 0, st, a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,14 @@ int check_ptr(const void* p, const char* name) {
   return SDV_OK;
 }
 
+// names of the snapshot arguments, for error messages
+const char* const kSnapNames[SDV_MAX_ROWS] = {
+    "snaps[0]", "snaps[1]", "snaps[2]", "snaps[3]", "snaps[4]", "snaps[5]", "snaps[6]", "snaps[7]", "snaps[8]",
+    "snaps[9]", "snaps[10]", "snaps[11]", "snaps[12]", "snaps[13]", "snaps[14]", "snaps[15]", "snaps[16]",
+    "snaps[17]", "snaps[18]", "snaps[19]", "snaps[20]", "snaps[21]", "snaps[22]", "snaps[23]", "snaps[24]",
+    "snaps[25]", "snaps[26]", "snaps[27]", "snaps[28]", "snaps[29]", "snaps[30]", "snaps[31]"};
+static_assert(SDV_MAX_ROWS == 32, "one snapshot name per row");
+
 int check_width(int k) {
   if (k < 1 || k > SDV_MAX_ROWS) return fail(SDV_EWIDTH, "k=%d outside 1..%d", k, SDV_MAX_ROWS);
   return SDV_OK;
@@ -467,11 +475,9 @@ int sdv_gdn_verify_k(const float* S_in, const float* q, const float* kk, const f
                  {beta, (size_t)k * Hv * 4, "beta"}};
   Range outs[SDV_MAX_ROWS + 1];
   outs[0] = {y, (size_t)k * Hv * Dv * 4, "y"};
-  static const char* snap_names[SDV_MAX_ROWS] = {"snaps[0]", "snaps[1]", "snaps[2]", "snaps[3]", "snaps[4]",
-                                                  "snaps[5]", "snaps[6]", "snaps[7]", "snaps[8]"};
   for (int t = 0; t < k; ++t) {
-    if ((st = check_ptr(snaps[t], snap_names[t]))) return st;
-    outs[t + 1] = {snaps[t], state, snap_names[t]};
+    if ((st = check_ptr(snaps[t], kSnapNames[t]))) return st;
+    outs[t + 1] = {snaps[t], state, kSnapNames[t]};
   }
   if ((st = check_alias(outs, k + 1, ins, 6))) return st;
   return hip_status(sdv::gdn_launch(S_in, q, kk, v, g, beta, k, Hv, Hk, Dk, Dv, y, snaps,
@@ -610,11 +616,9 @@ int sdv_gdn_verify_prep_k(const float* S_in, const float* qkv, const float* hist
   Range outs[SDV_MAX_ROWS + 2];
   outs[0] = {y, (size_t)k * Hv * Dv * 4, "y"};
   outs[1] = {window, (size_t)(k + 3) * C * 4, "window"};
-  static const char* snap_names[SDV_MAX_ROWS] = {"snaps[0]", "snaps[1]", "snaps[2]", "snaps[3]", "snaps[4]",
-                                                  "snaps[5]", "snaps[6]", "snaps[7]", "snaps[8]"};
   for (int t = 0; t < k; ++t) {
-    if ((st = check_ptr(snaps[t], snap_names[t]))) return st;
-    outs[t + 2] = {snaps[t], state, snap_names[t]};
+    if ((st = check_ptr(snaps[t], kSnapNames[t]))) return st;
+    outs[t + 2] = {snaps[t], state, kSnapNames[t]};
   }
   if ((st = check_alias(outs, k + 2, ins, 8))) return st;
   return hip_status(sdv::gdn_verify_prep_launch(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk,

@@ -8,6 +8,13 @@
 
 namespace sdv {
 
+// Rows of one pass of the Q4 kernels: a 32-row MFMA operand holds 9
+// activation rows (as three bf16 parts each for fp32 activations).  Wider
+// calls run a unit or launch per pass of at most kPassRows rows.
+constexpr int kPassRows = 9;
+// Row capacity of the wide instantiations of the row-indexed kernels.
+constexpr int kWideRows = SDV_MAX_ROWS;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

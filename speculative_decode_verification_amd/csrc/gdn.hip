@@ -72,15 +72,15 @@ __device__ __forceinline__ void for_rows(std::integer_sequence<int, T...>, int k
 // are written by the first block of each qk head, the v columns by their
 // block.  Blocks of one qk head are placed on one XCD when the block count
 // allows, so its repeated q/k inputs are L2 hits.
-template <int DK, bool LDS_KQ, bool PREP>
+template <int DK, bool LDS_KQ, bool PREP, int R>
 __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   static_assert(!PREP || LDS_KQ, "the in-kernel preparation stages through LDS");
   constexpr int NV4 = DK / 64;  // float4 per lane
-  __shared__ float4 s_k[LDS_KQ ? SDV_MAX_ROWS * DK / 4 : 1];
-  __shared__ float4 s_q[LDS_KQ ? SDV_MAX_ROWS * DK / 4 : 1];
-  __shared__ float s_v[LDS_KQ ? SDV_MAX_ROWS * kRowsPerBlock : 1];
-  __shared__ float s_g[SDV_MAX_ROWS], s_b[SDV_MAX_ROWS];
-  __shared__ float s_part[PREP ? 4 : 1][SDV_MAX_ROWS];
+  __shared__ float4 s_k[LDS_KQ ? R * DK / 4 : 1];
+  __shared__ float4 s_q[LDS_KQ ? R * DK / 4 : 1];
+  __shared__ float s_v[LDS_KQ ? R * kRowsPerBlock : 1];
+  __shared__ float s_g[R], s_b[R];
+  __shared__ float s_part[PREP ? 4 : 1][R];
 
   // blocks dealt round-robin over the 8 XCDs; with PREP and a multiple of 8
   // blocks, XCD x takes the consecutive logical blocks x*n/8 .. (x+1)*n/8-1
@@ -98,16 +98,19 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   const int c = h / (a.Hv / a.Hk);
 
   // Every load is issued before any is used: first the per-row vectors of
-  // the staging (at most two float4 of k and of q, one v and one g, beta per
-  // thread), then the state.  Loads complete in issue order, so the LDS
+  // the staging (KQ_PER_THREAD float4 of k and of q, V_PER_THREAD values of
+  // v, one g and beta per thread), then the state.  Loads complete in issue order, so the LDS
   // writes wait only for the staging loads and overlap the state's arrival.
   static_assert(kRowsPerBlock * 16 == 256, "staging assumes 256 threads");
   float4 S[NV4];
-  constexpr int KQ_PER_THREAD = (SDV_MAX_ROWS * DK / 4 + 255) / 256;
+  constexpr int KQ_PER_THREAD = (R * DK / 4 + 255) / 256;
   float4 ck[KQ_PER_THREAD], cq[KQ_PER_THREAD];
 #pragma unroll
   for (int u = 0; u < KQ_PER_THREAD; ++u) ck[u] = cq[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  float cv = 0.0f, cg = 0.0f, cb = 0.0f;
+  constexpr int V_PER_THREAD = (R * kRowsPerBlock + 255) / 256;  // v values staged per thread
+  float cv[V_PER_THREAD], cg = 0.0f, cb = 0.0f;
+#pragma unroll
+  for (int u = 0; u < V_PER_THREAD; ++u) cv[u] = 0.0f;
   const int row0 = lblk * kRowsPerBlock;
   const int h0 = row0 / Dv;
   const int i0 = row0 - h0 * Dv;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   // channel (threads VB..VB+15) and of its gates (threads GB..GB+k-1); every
   // thread issues all of them, clamped, so the waits are static
   constexpr int VB = DK == 128 ? 0 : 128, GB = 192;
-  float xq[PREP ? kConvWin : 1], xv[PREP ? kConvWin : 1];
+  float xq[PREP ? kConvWin<R> : 1], xv[PREP ? kConvWin<R> : 1];
   float4 wq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), wv = wq;
   float pa = 0.0f, pb = 0.0f, pal = 0.0f, pdb = 0.0f;
   const int ratio = a.Hv / a.Hk;
@@ -133,8 +136,8 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     pal = a.A_log[h0];
     pdb = a.dt_bias[h0];
     __builtin_amdgcn_sched_barrier(0);
-    gdn_conv_load(a.qkv, a.hist, a.C, c_qk, a.k, xq);
-    gdn_conv_load(a.qkv, a.hist, a.C, c_v, a.k, xv);
+    gdn_conv_load<R>(a.qkv, a.hist, a.C, c_qk, a.k, xq);
+    gdn_conv_load<R>(a.qkv, a.hist, a.C, c_v, a.k, xv);
     wq = reinterpret_cast<const float4*>(a.conv_w)[c_qk];
     wv = reinterpret_cast<const float4*>(a.conv_w)[c_v];
   }
@@ -149,9 +152,12 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
       ck[u] = reinterpret_cast<const float4*>(a.kk + ((long)tt * a.Hk + c0) * DK)[jj];
       cq[u] = reinterpret_cast<const float4*>(a.q + ((long)tt * a.Hk + c0) * DK)[jj];
     }
-    const int tv = min((int)threadIdx.x, a.k * kRowsPerBlock - 1);
-    const int tt = tv / kRowsPerBlock, r = min(tv - tt * kRowsPerBlock, (int)(nrows - 1 - row0));
-    cv = a.v[((long)tt * a.Hv + h0) * Dv + i0 + r];
+#pragma unroll
+    for (int u = 0; u < V_PER_THREAD; ++u) {
+      const int tv = min((int)threadIdx.x + 256 * u, a.k * kRowsPerBlock - 1);
+      const int tt = tv / kRowsPerBlock, r = min(tv - tt * kRowsPerBlock, (int)(nrows - 1 - row0));
+      cv[u] = a.v[((long)tt * a.Hv + h0) * Dv + i0 + r];
+    }
     const int tg = min((int)threadIdx.x, a.k - 1);
     cg = a.g[tg * a.Hv + h0];
     cb = a.beta[tg * a.Hv + h0];
@@ -172,26 +178,26 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
       s_g[tid - GB] = gdn_decay(pa, pal, pdb);
       s_b[tid - GB] = gdn_beta(pb);
     }
-    float o[SDV_MAX_ROWS];
-    gdn_conv_rows(wq, xq, a.conv_act, o);
+    float o[R];
+    gdn_conv_rows<R>(wq, xq, a.conv_act, o);
     if (tid < 2 * DK) {  // whole waves: q, then k
-      float ws[SDV_MAX_ROWS];
-      gdn_wave_sq_sums(o, ws);
+      float ws[R];
+      gdn_wave_sq_sums<R>(o, ws);
       if ((tid & 63) == 0) {
 #pragma unroll
-        for (int t = 0; t < SDV_MAX_ROWS; ++t) s_part[wave][t] = ws[t];
+        for (int t = 0; t < R; ++t) s_part[wave][t] = ws[t];
       }
       float* dst = reinterpret_cast<float*>(tid < DK ? s_q : s_k);
       const int ch = tid < DK ? tid : tid - DK;
 #pragma unroll
-      for (int t = 0; t < SDV_MAX_ROWS; ++t)
+      for (int t = 0; t < R; ++t)
         if (t < k) dst[t * DK + ch] = o[t];
     }
     if (tid >= VB && tid < VB + kRowsPerBlock) {
-      float ov[SDV_MAX_ROWS];
-      gdn_conv_rows(wv, xv, a.conv_act, ov);
+      float ov[R];
+      gdn_conv_rows<R>(wv, xv, a.conv_act, ov);
 #pragma unroll
-      for (int t = 0; t < SDV_MAX_ROWS; ++t)
+      for (int t = 0; t < R; ++t)
         if (t < k) s_v[t * kRowsPerBlock + rv] = ov[t];
     }
     __syncthreads();
@@ -204,7 +210,11 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
         s_q[t] = cq[u];
       }
     }
-    if (threadIdx.x < a.k * kRowsPerBlock) s_v[threadIdx.x] = (row0 + threadIdx.x % kRowsPerBlock < nrows) ? cv : 0.0f;
+#pragma unroll
+    for (int u = 0; u < V_PER_THREAD; ++u) {
+      const int tv = threadIdx.x + 256 * u;
+      if (tv < a.k * kRowsPerBlock) s_v[tv] = (row0 + tv % kRowsPerBlock < nrows) ? cv[u] : 0.0f;
+    }
     if (threadIdx.x < a.k) {
       s_g[threadIdx.x] = cg;
       s_b[threadIdx.x] = cb;
@@ -221,12 +231,12 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     const int tid = threadIdx.x, k = a.k;
     if (tid >= VB && tid < VB + kRowsPerBlock) {
 #pragma unroll
-      for (int j = 0; j < kConvWin; ++j)
+      for (int j = 0; j < kConvWin<R>; ++j)
         if (j < kConvHist + k) a.window[(size_t)j * a.C + c_v] = xv[j];
     }
     if (tid < 2 * DK && h0 % ratio == 0 && i0 == 0) {
 #pragma unroll
-      for (int j = 0; j < kConvWin; ++j)
+      for (int j = 0; j < kConvWin<R>; ++j)
         if (j < kConvHist + k) a.window[(size_t)j * a.C + c_qk] = xq[j];
     }
   };
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
       }
     }
   };
-  for_rows(std::make_integer_sequence<int, SDV_MAX_ROWS>{}, a.k, row_step);
+  for_rows(std::make_integer_sequence<int, R>{}, a.k, row_step);
 }
 
 }  // namespace
@@ -344,16 +354,17 @@ hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const 
   const long blocks = ((long)Hv * Dv + kRowsPerBlock - 1) / kRowsPerBlock;
   const bool lds = (Dv % kRowsPerBlock) == 0;
   const dim3 grid((unsigned)blocks), block(kRowsPerBlock * 16);
-  if (Dk == 64 && lds)
-    hipLaunchKernelGGL((gdn_verify_kernel<64, true, false>), grid, block, 0, st, a);
-  else if (Dk == 64)
-    hipLaunchKernelGGL((gdn_verify_kernel<64, false, false>), grid, block, 0, st, a);
-  else if (Dk == 128 && lds)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, true, false>), grid, block, 0, st, a);
-  else if (Dk == 128)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, false, false>), grid, block, 0, st, a);
-  else
-    return hipErrorInvalidValue;
+  if (Dk != 64 && Dk != 128) return hipErrorInvalidValue;
+  const bool wide = k > kPassRows;
+  auto kern = Dk == 64 ? (lds ? (wide ? gdn_verify_kernel<64, true, false, kWideRows>
+                                      : gdn_verify_kernel<64, true, false, kPassRows>)
+                              : (wide ? gdn_verify_kernel<64, false, false, kWideRows>
+                                      : gdn_verify_kernel<64, false, false, kPassRows>))
+                       : (lds ? (wide ? gdn_verify_kernel<128, true, false, kWideRows>
+                                      : gdn_verify_kernel<128, true, false, kPassRows>)
+                              : (wide ? gdn_verify_kernel<128, false, false, kWideRows>
+                                      : gdn_verify_kernel<128, false, false, kPassRows>));
+  hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -381,12 +392,12 @@ hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const flo
   a.eps = eps;
   a.window = window;
   const dim3 grid((unsigned)((long)Hv * D / kRowsPerBlock)), block(kRowsPerBlock * 16);
-  if (D == 64)
-    hipLaunchKernelGGL((gdn_verify_kernel<64, true, true>), grid, block, 0, st, a);
-  else if (D == 128)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, true, true>), grid, block, 0, st, a);
-  else
-    return hipErrorInvalidValue;
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  const bool wide = k > kPassRows;
+  auto kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows> : gdn_verify_kernel<64, true, true, kPassRows>)
+                      : (wide ? gdn_verify_kernel<128, true, true, kWideRows>
+                              : gdn_verify_kernel<128, true, true, kPassRows>);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

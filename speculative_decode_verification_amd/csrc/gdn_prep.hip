@@ -47,10 +47,10 @@ struct PrepArgs {
   float* window;  // [k + 3][C]
 };
 
-// Block of D (64 or 128) channels, all k rows.
-template <int D>
+// Block of D (64 or 128) channels, all k rows (k <= R).
+template <int D, int R>
 __global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
-  __shared__ float s_part[D / 64][SDV_MAX_ROWS];
+  __shared__ float s_part[D / 64][R];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int nq = a.Hk, nqk = 2 * a.Hk;
   const int blk = blockIdx.x;
@@ -61,21 +61,21 @@ __global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
   const int C = a.C, k = a.k;
   // every load first: the channel's history and rows, its taps, and the gate
   // inputs of (row tid, head hv) (clamped; used by the v blocks only)
-  float x[kConvWin];
-  gdn_conv_load(a.qkv, a.hist, C, c, k, x);
+  float x[kConvWin<R>];
+  gdn_conv_load<R>(a.qkv, a.hist, C, c, k, x);
   const float4 w = reinterpret_cast<const float4*>(a.conv_w)[c];
   const int tg = min(tid, k - 1);
   const float ga = a.a[tg * a.Hv + hv], gb = a.b[tg * a.Hv + hv];
   const float al = a.A_log[hv], db = a.dt_bias[hv];
   // the window [history; rows] for rollback by selection
 #pragma unroll
-  for (int j = 0; j < kConvWin; ++j)
+  for (int j = 0; j < kConvWin<R>; ++j)
     if (j < kConvHist + k) a.window[(size_t)j * C + c] = x[j];
-  float o[SDV_MAX_ROWS];
-  gdn_conv_rows(w, x, a.conv_act, o);
+  float o[R];
+  gdn_conv_rows<R>(w, x, a.conv_act, o);
   if (!is_q && !is_k) {
 #pragma unroll
-    for (int t = 0; t < SDV_MAX_ROWS; ++t)
+    for (int t = 0; t < R; ++t)
       if (t < k) a.v[((size_t)t * a.Hv + hv) * a.Dv + tid] = o[t];
     if (tid < k) {
       a.g[tid * a.Hv + hv] = gdn_decay(ga, al, db);
@@ -85,18 +85,18 @@ __global__ __launch_bounds__(D) void gdn_prepare_kernel(PrepArgs a) {
   }
   // per-row L2 norm over the head's D channels
   {
-    float ws[SDV_MAX_ROWS];
-    gdn_wave_sq_sums(o, ws);
+    float ws[R];
+    gdn_wave_sq_sums<R>(o, ws);
     if ((tid & 63) == 0) {
 #pragma unroll
-      for (int t = 0; t < SDV_MAX_ROWS; ++t) s_part[wave][t] = ws[t];
+      for (int t = 0; t < R; ++t) s_part[wave][t] = ws[t];
     }
   }
   __syncthreads();
   const int h = is_q ? blk : blk - nq;
   float* dst = is_q ? a.q : a.kk;
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
+  for (int t = 0; t < R; ++t) {
     if (t < k) {
       float ss = s_part[0][t];
 #pragma unroll
@@ -142,10 +142,15 @@ hipError_t gdn_prepare_launch(const float* qkv, const float* hist, const float* 
   PrepArgs a{qkv, hist, conv_w, ga, gb, A_log, dt_bias, k, Hv, Hk, Dk, Dv, 2 * Hk * Dk + Hv * Dv, conv_act,
              eps, q, kk, v, g, beta, window};
   const dim3 grid((unsigned)(2 * Hk + Hv));
-  if (Dk == 64)
-    hipLaunchKernelGGL(gdn_prepare_kernel<64>, grid, dim3(64), 0, st, a);
+  const bool wide = k > kPassRows;
+  if (Dk == 64 && !wide)
+    hipLaunchKernelGGL((gdn_prepare_kernel<64, kPassRows>), grid, dim3(64), 0, st, a);
+  else if (Dk == 64)
+    hipLaunchKernelGGL((gdn_prepare_kernel<64, kWideRows>), grid, dim3(64), 0, st, a);
+  else if (Dk == 128 && !wide)
+    hipLaunchKernelGGL((gdn_prepare_kernel<128, kPassRows>), grid, dim3(128), 0, st, a);
   else if (Dk == 128)
-    hipLaunchKernelGGL(gdn_prepare_kernel<128>, grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((gdn_prepare_kernel<128, kWideRows>), grid, dim3(128), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -14,7 +14,9 @@ namespace sdv {
 
 constexpr int kConvTaps = 4;
 constexpr int kConvHist = kConvTaps - 1;
-constexpr int kConvWin = kConvHist + SDV_MAX_ROWS;  // history plus the rows of one call
+// history plus the rows of one call, for a kernel of row capacity R
+template <int R>
+constexpr int kConvWin = kConvHist + R;
 
 // Sum over the 64 lanes of a wave, in every lane: a 16-lane DPP sum, then the
 // four row totals in row order.
@@ -39,20 +41,22 @@ __device__ __forceinline__ float gdn_beta(float b) { return 1.0f / (1.0f + expf(
 // Channel c's history (3 inputs) and the inputs of rows 0..k-1 into x, in
 // time order; slots past row k-1 repeat row k-1 (loads always issued, values
 // unused).
+template <int R>
 __device__ __forceinline__ void gdn_conv_load(const float* qkv, const float* hist, int C, int c, int k,
-                                              float (&x)[kConvWin]) {
+                                              float (&x)[kConvWin<R>]) {
 #pragma unroll
   for (int j = 0; j < kConvHist; ++j) x[j] = hist[(size_t)j * C + c];
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) x[kConvHist + t] = qkv[(size_t)min(t, k - 1) * C + c];
+  for (int t = 0; t < R; ++t) x[kConvHist + t] = qkv[(size_t)min(t, k - 1) * C + c];
 }
 
 // The conv outputs of every row slot t: taps applied oldest input first (tap
 // 3 multiplies the current input), then the optional silu.
-__device__ __forceinline__ void gdn_conv_rows(const float4 w, const float (&x)[kConvWin], int act,
-                                              float (&o)[SDV_MAX_ROWS]) {
+template <int R>
+__device__ __forceinline__ void gdn_conv_rows(const float4 w, const float (&x)[kConvWin<R>], int act,
+                                              float (&o)[R]) {
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
+  for (int t = 0; t < R; ++t) {
     float acc = w.x * x[t];
     acc = fmaf(w.y, x[t + 1], acc);
     acc = fmaf(w.z, x[t + 2], acc);
@@ -60,26 +64,27 @@ __device__ __forceinline__ void gdn_conv_rows(const float4 w, const float (&x)[k
   }
   if (act == SDV_CONV_SILU) {
 #pragma unroll
-    for (int t = 0; t < SDV_MAX_ROWS; ++t) o[t] = siluf_(o[t]);
+    for (int t = 0; t < R; ++t) o[t] = siluf_(o[t]);
   }
 }
 
 // gdn_wave_sum(o[t] * o[t]) for every row slot, the rows' DPP stages
 // interleaved (each row's sum has the same order as gdn_wave_sum).
-__device__ __forceinline__ void gdn_wave_sq_sums(const float (&o)[SDV_MAX_ROWS], float (&s)[SDV_MAX_ROWS]) {
-  float r[SDV_MAX_ROWS];
+template <int R>
+__device__ __forceinline__ void gdn_wave_sq_sums(const float (&o)[R], float (&s)[R]) {
+  float r[R];
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) r[t] = o[t] * o[t];
+  for (int t = 0; t < R; ++t) r[t] = o[t] * o[t];
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) r[t] = r[t] + dpp_f32<0xB1>(r[t]);
+  for (int t = 0; t < R; ++t) r[t] = r[t] + dpp_f32<0xB1>(r[t]);
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) r[t] = r[t] + dpp_f32<0x4E>(r[t]);
+  for (int t = 0; t < R; ++t) r[t] = r[t] + dpp_f32<0x4E>(r[t]);
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) r[t] = r[t] + dpp_f32<0x128>(r[t]);
+  for (int t = 0; t < R; ++t) r[t] = r[t] + dpp_f32<0x128>(r[t]);
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) r[t] = r[t] + dpp_f32<0x124>(r[t]);
+  for (int t = 0; t < R; ++t) r[t] = r[t] + dpp_f32<0x124>(r[t]);
 #pragma unroll
-  for (int t = 0; t < SDV_MAX_ROWS; ++t) {
+  for (int t = 0; t < R; ++t) {
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r[t]), 0));
     const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r[t]), 16));
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r[t]), 32));

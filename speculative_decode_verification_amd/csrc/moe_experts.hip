@@ -87,8 +87,8 @@ __host__ __device__ inline Lds expert_lds(int k, int H) {
   l.xsum = (size_t)(k + 1) * rsA * 2;
   l.hs = (l.xsum + (size_t)32 * (H / 64) * 4 + 15) & ~(size_t)15;
   l.hpart = l.hs + (size_t)(3 * k + 1) * rsB * 2;
-  l.hrow = l.hpart + (size_t)SDV_MAX_ROWS * kSliceTiles * 4;
-  l.total = l.hrow + (size_t)SDV_MAX_ROWS * (kSlice / 64) * 4;
+  l.hrow = l.hpart + (size_t)kPassRows * kSliceTiles * 4;
+  l.total = l.hrow + (size_t)kPassRows * (kSlice / 64) * 4;
   return l;
 }
 
@@ -103,12 +103,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t by
 template <typename Issue>
 __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)[kRing], const uint32_t (&sbuf)[kRing],
                                         Issue& issue, const uint16_t* hs, const float* hrow, const int* s_dst,
-                                        int nrows, int j, int wave, int lane, int s_begin, int s_end, DecodeK dk) {
+                                        int nrows, int kr, int j, int wave, int lane, int s_begin, int s_end,
+                                        DecodeK dk) {
   const int k = a.k, H = a.H;
   const int col = lane & 31, half = lane >> 5;
   const int rsB = kSlice + 8;
   const int slot = slot_of_arow<SDV_ACT_F32>(col, nrows);
-  const uint16_t* ap = hs + (size_t)(slot >= 0 ? slot : 3 * k) * rsB + half * 32;
+  const uint16_t* ap = hs + (size_t)(slot >= 0 ? slot : 3 * kr) * rsB + half * 32;
   const float* xr[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) xr[i] = hrow + (i < 4 ? 4 * half + i : 8) * 2;
@@ -159,11 +160,15 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
   for (int s0 = s_begin + kRing; s0 < s_end; s0 += kRing) round(s0);
 }
 
+// WIDE (k > kPassRows): a unit is one pass of at most kPassRows of an
+// expert's rows (pass blockIdx.z), and only those rows are staged.
+template <bool WIDE>
 __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
+  __shared__ int s_src[kPassRows], s_dst[kPassRows];
   const int H = a.H, GA = a.GA, GB = a.GB, k = a.k;
-  const Lds L = expert_lds(k, H);
+  const int kr = WIDE ? kPassRows : k;  // rows of the LDS staging; row kr is all zero
+  const Lds L = expert_lds(kr, H);
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   float* xsum = reinterpret_cast<float*>(smem + L.xsum);
   uint16_t* hs = reinterpret_cast<uint16_t*>(smem + L.hs);
@@ -180,10 +185,11 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // contiguous, at element 64 t); the loads of the first k * G tasks go out
   // before anything else, since x does not depend on the routing.  All k rows
   // are staged, in x-row order; the unit's rows pick theirs through s_src.
-  const int G = H >> 6, nxt = k * G;
+  const int G = H >> 6;
+  int nxt = k * G;
   constexpr int kThreads = 64 * kWaves;
   uint4 xv[8];
-  {
+  if constexpr (!WIDE) {
     const uint4* xp = reinterpret_cast<const uint4*>(a.x) + (size_t)min(tid, nxt - 1) * 8;
 #pragma unroll
     for (int q = 0; q < 8; ++q) xv[q] = xp[q];
@@ -192,6 +198,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // ---- unit: a union expert's rows, or the shared expert's k rows.  The
   // routing words are loaded together before any is tested.
   const int u = blockIdx.y, j = blockIdx.x;
+  const int pass0 = WIDE ? (int)blockIdx.z * kPassRows : 0;
   const bool shared = u == k * a.topk;
   int e = 0, p0 = 0, nrows = k;
   const uint4* guc = a.gu_codes;
@@ -204,6 +211,10 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     gus = a.sgu_sb;
     dnc = a.sdn_codes;
     dns = a.sdn_sb;
+    if constexpr (WIDE) {
+      nrows = min(k - pass0, kPassRows);
+      if (nrows <= 0) return;
+    }
   } else {
     int nu = __builtin_amdgcn_readfirstlane(*a.n_union);
     int e0 = __builtin_amdgcn_readfirstlane(a.union_ids[u]);
@@ -211,9 +222,10 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     int q1 = __builtin_amdgcn_readfirstlane(a.pair_off[u + 1]);
     asm volatile("" : "+s"(nu), "+s"(e0), "+s"(q0), "+s"(q1));  // all four in flight together
     if (u >= nu || e0 < 0 || e0 >= a.E) return;
-    nrows = q1 - q0;
-    if (q0 < 0 || nrows <= 0 || q1 > k * a.topk) return;
-    if (nrows > k) nrows = k;
+    if (q0 < 0 || q1 <= q0 || q1 > k * a.topk) return;
+    q0 += pass0;
+    nrows = min(q1 - q0, WIDE ? kPassRows : k);
+    if (nrows <= 0) return;
     e = __builtin_amdgcn_readfirstlane(e0);
     p0 = __builtin_amdgcn_readfirstlane(q0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
@@ -257,14 +269,28 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // unit's are not used).
   const int pq = p0 + min(tid, nrows - 1);
   const int pr = a.pair_row[pq], ps = a.pair_slot[pq];
+  // WIDE: the x rows of this pass's rows only, staged in pass order (the
+  // pair rows are loaded first: the x addresses depend on them)
+  auto x_src = [&](int i) {  // x row of staged row i
+    if (shared) return pass0 + i;
+    const int r = a.pair_row[p0 + i];
+    return min(max(r, 0), k - 1);
+  };
+  if constexpr (WIDE) {
+    nxt = nrows * G;
+    const int t = min(tid, nxt - 1), i = t / G;
+    const uint4* xp = reinterpret_cast<const uint4*>(a.x) + ((size_t)x_src(i) * G + (t - i * G)) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xv[q] = xp[q];
+  }
 #pragma unroll
   for (int i = 0; i < kRing; ++i) issue(i, i);
 
   // ---- phase A staging (the ring loads are already in flight): the all-zero
   // rows (MFMA rows without data read them)
-  for (int t = tid; t < rsA / 2; t += kThreads) reinterpret_cast<uint32_t*>(xs + (size_t)k * rsA)[t] = 0u;
-  for (int t = tid; t < rsB / 2; t += kThreads) reinterpret_cast<uint32_t*>(hs + (size_t)3 * k * rsB)[t] = 0u;
-  for (int t = tid; t < G; t += kThreads) xsum[k * G + t] = 0.0f;
+  for (int t = tid; t < rsA / 2; t += kThreads) reinterpret_cast<uint32_t*>(xs + (size_t)kr * rsA)[t] = 0u;
+  for (int t = tid; t < rsB / 2; t += kThreads) reinterpret_cast<uint32_t*>(hs + (size_t)3 * kr * rsB)[t] = 0u;
+  for (int t = tid; t < G; t += kThreads) xsum[kr * G + t] = 0.0f;
   // One task = (x row i, group g): its 8 blocks of 8 elements are stored in NU
   // order and summed in order, and the group sum adds the 8 block sums
   // pairwise ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7)).
@@ -285,7 +311,8 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   };
   if (tid < nxt) put(tid, xv);
   for (int t = tid + kThreads; t < nxt; t += kThreads) {
-    const uint4* xp = reinterpret_cast<const uint4*>(a.x) + (size_t)t * 8;
+    const int i = t / G;
+    const uint4* xp = reinterpret_cast<const uint4*>(a.x) + (WIDE ? ((size_t)x_src(i) * G + (t - i * G)) : (size_t)t) * 8;
     uint4 v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = xp[q];
@@ -293,18 +320,18 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   }
   // the unit's rows, after the x tasks (whose loads went out first), so the
   // wait for the (row, slot) pairs overlaps that work
-  if (tid < SDV_MAX_ROWS) {
+  if (tid < kPassRows) {
     int src = -1, dst = -1;
     if (tid < nrows) {
       if (!shared) {
         const int r = pr, s = ps;
         if (r >= 0 && r < k && s >= 0 && s < a.topk) {
-          src = r;
+          src = WIDE ? tid : r;
           dst = r * (a.topk + 1) + s;
         }
       } else {
         src = tid;
-        dst = tid * (a.topk + 1) + a.topk;
+        dst = (pass0 + tid) * (a.topk + 1) + a.topk;
       }
     }
     s_src[tid] = src;
@@ -317,14 +344,14 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // ---- phase A: one fused gate/up tile over all GA groups
   {
     const int src = col < nrows ? s_src[col] : -1;
-    const uint16_t* ap = xs + (size_t)(src >= 0 ? src : k) * rsA + half * 32;
+    const uint16_t* ap = xs + (size_t)(src >= 0 ? src : kr) * rsA + half * 32;
     // group sums of the x row behind each accumulator (row k is all zero)
     const float* xr[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int r = i < 4 ? 4 * half + i : 8;
       const int sr = r < nrows ? s_src[r] : -1;
-      xr[i] = xsum + (sr >= 0 ? sr : k) * G;
+      xr[i] = xsum + (sr >= 0 ? sr : kr) * G;
     }
     float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     // whole rounds, then a last round whose steps past nA compute nothing
@@ -354,7 +381,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     const int n = wave * 16 + c16;                              // column in the slice
     const int hpos = (n & ~7) + ((n & 7) < 4 ? 2 * (n & 7) : 2 * (n & 7) - 7);
 #pragma unroll
-    for (int r = 0; r < SDV_MAX_ROWS; ++r) {
+    for (int r = 0; r < kPassRows; ++r) {
       if (r < nrows && wave < kSliceTiles) {
         float h = 0.0f;
         if (nA > 0) {
@@ -379,7 +406,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   }
   __syncthreads();  // every wave's part of h is in LDS
   // each row's group sums: the four 16-column partial sums of the group, in order
-  if (tid < SDV_MAX_ROWS * 2) {
+  if (tid < kPassRows * 2) {
     const int r = tid >> 1, g = tid & 1;
     const float* hp = hpart + r * kSliceTiles + 4 * g;
     hrow[r * 2 + g] = r < nrows ? (hp[0] + hp[1]) + (hp[2] + hp[3]) : 0.0f;
@@ -387,14 +414,34 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   __syncthreads();
 
   // ---- phase B: down tiles over the slice's groups
-  phase_b(a, cbuf, sbuf, issue, hs, hrow, s_dst, nrows, j, wave, lane, nA8, total, dk);
+  phase_b(a, cbuf, sbuf, issue, hs, hrow, s_dst, nrows, kr, j, wave, lane, nA8, total, dk);
 }
 
 }  // namespace
 
 int expert_slices(int I) { return (I + kSlice - 1) / kSlice; }
 
-size_t expert_lds_bytes(int k, int H) { return expert_lds(k, H).total; }
+size_t expert_lds_bytes(int k, int H) { return expert_lds(k < kPassRows ? k : kPassRows, H).total; }
+
+namespace {
+
+// Raise the kernel's dynamic LDS limit once per process (the largest size
+// asked for so far; the attribute is per function, not per device).
+template <bool WIDE>
+hipError_t raise_lds_limit(size_t lds) {
+  static std::atomic<size_t> lds_limit{65536};
+  size_t cur = lds_limit.load(std::memory_order_relaxed);
+  if (lds > cur) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_experts_kernel<WIDE>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
 
 size_t expert_partial_bytes(int k, int topk, int H, int I) {
   return (size_t)expert_slices(I) * k * (topk + 1) * H * 4;
@@ -432,17 +479,17 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
   a.partial = partial;
   a.partial_bytes = (uint32_t)expert_partial_bytes(k, topk, a.H, a.I);
   const size_t lds = expert_lds_bytes(k, a.H);
-  static std::atomic<size_t> lds_limit{65536};
-  size_t cur = lds_limit.load(std::memory_order_relaxed);
-  if (lds > cur) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_experts_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
-    }
-  }
   const int units = k * topk + (sgu ? 1 : 0);
-  hipLaunchKernelGGL(moe_experts_kernel, dim3(a.S, units), dim3(64 * kWaves), lds, st, a);
+  if (k > kPassRows) {
+    const hipError_t err = raise_lds_limit<true>(lds);
+    if (err != hipSuccess) return err;
+    const int passes = (k + kPassRows - 1) / kPassRows;
+    hipLaunchKernelGGL(moe_experts_kernel<true>, dim3(a.S, units, passes), dim3(64 * kWaves), lds, st, a);
+  } else {
+    const hipError_t err = raise_lds_limit<false>(lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(moe_experts_kernel<false>, dim3(a.S, units), dim3(64 * kWaves), lds, st, a);
+  }
   return hipGetLastError();
 }
 

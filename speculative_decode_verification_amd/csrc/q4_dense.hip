@@ -52,14 +52,14 @@ struct DenseArgs {
 __host__ __device__ inline int dense_row_stride(int gwmax) { return gwmax * 64 + 8; }
 
 // One wave's region: (cap + 1) staged rows of the wave's K slice, then the
-// rows' group sums [SDV_MAX_ROWS + 1][gwmax] (row k all zero).
+// rows' group sums [kPassRows + 1][gwmax] (row k all zero).
 __host__ __device__ inline size_t dense_region_bytes(int cap, int gwmax) {
-  return ((size_t)(cap + 1) * dense_row_stride(gwmax) * 2 + (size_t)(SDV_MAX_ROWS + 1) * gwmax * 4 + 15) &
+  return ((size_t)(cap + 1) * dense_row_stride(gwmax) * 2 + (size_t)(kPassRows + 1) * gwmax * 4 + 15) &
          ~(size_t)15;
 }
 
-// The cross-wave sums reuse the regions: [nw][SDV_MAX_ROWS][33].
-__host__ __device__ inline size_t dense_red_bytes(int nw) { return (size_t)nw * SDV_MAX_ROWS * 33 * 4; }
+// The cross-wave sums reuse the regions: [nw][kPassRows][33].
+__host__ __device__ inline size_t dense_red_bytes(int nw) { return (size_t)nw * kPassRows * 33 * 4; }
 
 // Sum of 8 consecutive bf16 values (natural order), and their NU packing.
 __device__ __forceinline__ float block8(const uint4 v, uint4& packed) {
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   // ---- cross-wave sum in wave order, then the epilogue
   __syncthreads();  // every wave is done with its region
   float* red = reinterpret_cast<float*>(smem);
-  float* myred = red + (size_t)wave * SDV_MAX_ROWS * 33;
+  float* myred = red + (size_t)wave * kPassRows * 33;
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const int r = i < 4 ? 4 * half + i : 8;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
     for (int h2 = 0; h2 < ncol; ++h2) {
       const int cidx = cc + 16 * h2;
       float sum = 0.0f;
-      for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * SDV_MAX_ROWS + i) * 33 + cidx];
+      for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * kPassRows + i) * 33 + cidx];
       val[h2] = sum;
     }
     if (MODE == SDV_MODE_PLAIN) {
@@ -297,6 +297,7 @@ int dense_waves_for(int K) {
 }
 
 size_t dense_lds_bytes(int K, int act_dtype, int k) {
+  if (k > kPassRows) k = kPassRows;  // one launch per pass
   const int G = K / 64, nw = dense_waves_for(K);
   const int gwmax = (G + nw - 1) / nw;
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
@@ -305,8 +306,10 @@ size_t dense_lds_bytes(int K, int act_dtype, int k) {
   return regions > red ? regions : red;
 }
 
-hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
-                        hipStream_t st) {
+namespace {
+
+hipError_t dense_launch_pass(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
+                             hipStream_t st) {
   DenseArgs a;
   a.codes = static_cast<const uint4*>(W.codes);
   a.sb = W.sb;
@@ -331,6 +334,24 @@ hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dty
   SDV_DENSE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
 #undef SDV_DENSE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Widths above one pass run one launch per pass of at most kPassRows rows
+// (rows 9c .. 9c + 8 of the activations and outputs); each launch reads the
+// weights again.
+hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
+                        hipStream_t st) {
+  const size_t act_row = (size_t)W.K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
+  const int n_out = (mode == SDV_MODE_PLAIN) ? W.N : W.N / 2;
+  for (int r0 = 0; r0 < k; r0 += kPassRows) {
+    const int kc = k - r0 < kPassRows ? k - r0 : kPassRows;
+    const hipError_t e = dense_launch_pass(W, mode, static_cast<const unsigned char*>(act) + r0 * act_row, act_dtype,
+                                           kc, out + (size_t)r0 * n_out, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace sdv

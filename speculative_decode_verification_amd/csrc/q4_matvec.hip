@@ -112,14 +112,16 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   const int col = lane & 31, half = lane >> 5;
 
   // ---- the unit (union expert, the shared expert, or the dense matrix) and its rows
-  int e = 0, p0 = 0, nrows = a.k;
+  // A unit's rows are taken kPassRows at a time: pass c = blockIdx.z takes
+  // its rows 9c .. 9c + 8 (one pass unless k > kPassRows).
+  int e = 0, p0 = 0, nrows = a.k, r0 = 0;
   const uint4* codes = a.codes;
   const uint32_t* sbp = a.sb;
   const void* act = a.act;
   float* out = a.out;
   bool pairs = GATHER;  // rows come from the pair lists
   if (GATHER) {
-    const int u = blockIdx.y;
+    const int u = blockIdx.y, pass0 = blockIdx.z * kPassRows;
     if (u == a.k * a.topk) {
       // the shared expert: all k rows, its own weight, input and output
       codes = a.xcodes;
@@ -127,6 +129,9 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
       act = a.xact;
       out = a.xout;
       pairs = false;
+      r0 = pass0;
+      nrows = min(a.k - pass0, kPassRows);
+      if (nrows <= 0) return;
     } else {
       const int nu = *a.n_union;
       if (u >= nu) return;
@@ -134,9 +139,10 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
       if (e < 0 || e >= a.E) return;
       p0 = a.pair_off[u];
       const int p1 = a.pair_off[u + 1];
-      nrows = p1 - p0;
-      if (p0 < 0 || nrows <= 0 || p1 > a.k * a.topk) return;
-      if (nrows > a.k) nrows = a.k;
+      if (p0 < 0 || p1 <= p0 || p1 > a.k * a.topk) return;
+      p0 += pass0;
+      nrows = min(p1 - p0, kPassRows);
+      if (nrows <= 0) return;
       e = __builtin_amdgcn_readfirstlane(e);
       p0 = __builtin_amdgcn_readfirstlane(p0);
       nrows = __builtin_amdgcn_readfirstlane(nrows);
@@ -184,7 +190,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
     if (i < total) issue(i);
 
   // ---- rows, then staging (the loads above are already in flight)
-  if (tid < SDV_MAX_ROWS) {
+  if (tid < kPassRows) {
     int src = -1, dst = -1;
     if (tid < nrows) {
       if (pairs) {
@@ -194,7 +200,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
           dst = r * a.topk + s;
         }
       } else {
-        src = dst = tid;
+        src = dst = r0 + tid;
       }
     }
     s_src[tid] = src;
@@ -231,9 +237,9 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
       if (!KSPLIT) {
         // finished tile values go to this wave's LDS area; the global stores
         // happen after the stream loop
-        float* o = red + ((size_t)wave * tiles_per_wave + cur_tl) * SDV_MAX_ROWS * 32;
+        float* o = red + ((size_t)wave * tiles_per_wave + cur_tl) * kPassRows * 32;
 #pragma unroll
-        for (int r = 0; r < SDV_MAX_ROWS; ++r) {
+        for (int r = 0; r < kPassRows; ++r) {
           if (r < nrows) {
             const float val = row_value<ACT>(yacc, r);
             const bool mine = half == half_of_row<ACT>(r);
@@ -266,14 +272,14 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   if (!KSPLIT) {
     __syncthreads();
     const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
-    const float* o = red + (size_t)wave * tiles_per_wave * SDV_MAX_ROWS * 32;
+    const float* o = red + (size_t)wave * tiles_per_wave * kPassRows * 32;
     for (int tl = 0; tl < t_count; ++tl) {
       const int t = t_first + tl * t_step;
       const int on = t * cols_out + col;
       if (col < cols_out && on < a.n_out) {
         for (int r = 0; r < nrows; ++r) {
           const int orow = s_dst[r];
-          if (orow >= 0) out[(size_t)orow * a.n_out + on] = o[(tl * SDV_MAX_ROWS + r) * 32 + col];
+          if (orow >= 0) out[(size_t)orow * a.n_out + on] = o[(tl * kPassRows + r) * 32 + col];
         }
       }
     }
@@ -325,7 +331,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
 template <int MODE, int ACT>
 __global__ __launch_bounds__(512, 2) void q4_dense_kernel(Q4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
+  __shared__ int s_src[kPassRows], s_dst[kPassRows];
   q4_matvec_body<MODE, ACT, false, true, kPFDense>(a, smem, s_src, s_dst);
 }
 
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(512, 2) void q4_dense_kernel(Q4Args a) {
 template <int MODE, int ACT>
 __global__ __launch_bounds__(512, 4) void q4_gather_kernel(Q4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_src[SDV_MAX_ROWS], s_dst[SDV_MAX_ROWS];
+  __shared__ int s_src[kPassRows], s_dst[kPassRows];
   q4_matvec_body<MODE, ACT, true, false, kPF>(a, smem, s_src, s_dst);
 }
 
@@ -352,7 +358,8 @@ hipError_t launch_one(const Q4Args& a, int blocks_x, int units, int nw, size_t l
     while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
     }
   }
-  hipLaunchKernelGGL(kern, dim3(blocks_x, units), dim3(64 * nw), lds, st, a);
+  const int passes = (a.k + kPassRows - 1) / kPassRows;
+  hipLaunchKernelGGL(kern, dim3(blocks_x, units, passes), dim3(64 * nw), lds, st, a);
   return hipGetLastError();
 }
 
@@ -458,10 +465,11 @@ hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dty
                         hipStream_t st);
 
 size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather) {
+  if (k > kPassRows) k = kPassRows;  // rows are staged one pass at a time
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   // gathered: per-wave output staging for one tile of up to 9 rows x 32 columns
   return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * 4 +
-                      (size_t)kGatherWaves * kGatherTilesPerWave * SDV_MAX_ROWS * 32 * 4
+                      (size_t)kGatherWaves * kGatherTilesPerWave * kPassRows * 32 * 4
                 : dense_lds_bytes(K, act_dtype, k);
 }
 
@@ -490,7 +498,8 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
   a.xact = shared_act;
   a.xout = shared_out;
   a.n_out = (mode == SDV_MODE_PLAIN) ? W.N : W.N / 2;
-  a.slot_cap = (act_dtype == SDV_ACT_F32) ? 3 * k : k;
+  const int kp = k < kPassRows ? k : kPassRows;  // rows staged per pass
+  a.slot_cap = (act_dtype == SDV_ACT_F32) ? 3 * kp : kp;
   if (gather) {
     const int nw = kGatherWaves;
     a.tiles_per_block = nw * kGatherTilesPerWave;

@@ -3,8 +3,9 @@
 // (Red Lite dev45, "What it is": one router dispatch for both rows and the
 // (expert, row) pairs of their union; Flash-Next plan "2.3 MoE").
 //
-// One workgroup of 16 waves.  Wave r selects row r's top-k on an order word
-// of each fp32 logit (monotone in the value, -0 equal to +0, NaN lowest):
+// One workgroup of 16 waves.  Wave w selects the top-k of rows w and w + 16
+// on an order word of each fp32 logit (monotone in the value, -0 equal to
+// +0, NaN lowest):
 // the topk-th largest word T is found bit by bit from the top, each bit one
 // round of wave ballots counting the candidates at or above the trial value;
 // the candidates above T and the lowest-index ones equal to T are compacted,
@@ -125,8 +126,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   for (int t = tid; t < SDV_MAX_EXPERTS; t += kRouteThreads) s_rowmask[t] = 0u;
   for (int t = tid; t < SDV_MAX_EXPERTS; t += kRouteThreads) s_cnt[t] = 0;
 
-  if (wave < a.k) {
-    const int r = wave;
+  for (int r = wave; r < a.k; r += kRouteThreads / 64) {
     const float* l = a.logits + (size_t)r * E;
     float val[PL];
     uint32_t ord[PL];
@@ -187,11 +187,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  if (wave < a.k) {
+  for (int r = wave; r < a.k; r += kRouteThreads / 64) {
     // lane c takes the c-th selected candidate (index order) and places it by
     // its rank among the row's selected keys: slot order is larger logit
     // first, ties to the lower index
-    const int r = wave;
     const int nsel = s_nsel[r];
     const bool has = lane < nsel;
     int slot = lane;

@@ -82,7 +82,7 @@ def test_repack_validation(lib):
 
 def test_qmv_validation(lib):
     assert qmv(lib, q4t(), k=0) == L.SDV_EWIDTH
-    assert qmv(lib, q4t(), k=10) == L.SDV_EWIDTH
+    assert qmv(lib, q4t(), k=33) == L.SDV_EWIDTH
     assert qmv(lib, q4t(group=32)) == L.SDV_ELAYOUT
     assert qmv(lib, q4t(K=100)) == L.SDV_ELAYOUT
     assert qmv(lib, q4t(K=0)) == L.SDV_ELAYOUT
@@ -139,7 +139,7 @@ def gather(lib, bank, k=2, topk=4, mode=L.MODE_GATEUP_SWIGLU, dtype=L.ACT_BF16, 
 
 def test_gather_validation(lib):
     bank = q4t(E=8, N=128, K=128, fused=1)
-    assert gather(lib, bank, k=10) == L.SDV_EWIDTH
+    assert gather(lib, bank, k=33) == L.SDV_EWIDTH
     assert gather(lib, bank, topk=9) == L.SDV_ERANGE
     assert gather(lib, q4t(E=8, N=127, K=128, fused=1)) == L.SDV_ELAYOUT
     assert gather(lib, q4t(E=8, N=128, K=96, fused=1)) == L.SDV_ELAYOUT
@@ -179,7 +179,8 @@ def test_experts_partial_bytes(lib):
     # S = ceil(I / 128) slices of [k][topk + 1][H] fp32
     assert lib.sdv_moe_experts_partial_bytes(9, 10, 2560, 640) == 5 * 9 * 11 * 2560 * 4
     assert lib.sdv_moe_experts_partial_bytes(2, 4, 256, 192) == 2 * 2 * 5 * 256 * 4
-    assert lib.sdv_moe_experts_partial_bytes(10, 4, 256, 128) == 0
+    assert lib.sdv_moe_experts_partial_bytes(32, 10, 2560, 640) == 5 * 32 * 11 * 2560 * 4
+    assert lib.sdv_moe_experts_partial_bytes(33, 4, 256, 128) == 0
     assert lib.sdv_moe_experts_partial_bytes(2, 4, 250, 128) == 0
     assert lib.sdv_moe_experts_partial_bytes(2, 4, 256, 96) == 0
 
@@ -188,7 +189,7 @@ def test_experts_validation(lib):
     E, H, I = 8, 256, 128
     gu = q4t(E=E, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000)
     dn = q4t(E=E, N=H, K=I, fused=0, codes=P + 0x200000, sb=P + 0x300000)
-    assert experts(lib, gu, dn, k=10) == L.SDV_EWIDTH
+    assert experts(lib, gu, dn, k=33) == L.SDV_EWIDTH
     assert experts(lib, gu, dn, topk=9) == L.SDV_ERANGE
     assert experts(lib, q4t(E=E, N=2 * I, K=H, fused=0), dn) == L.SDV_ELAYOUT            # gate/up not fused
     assert experts(lib, gu, q4t(E=E, N=H, K=I, fused=1, codes=P + 0x200000)) == L.SDV_ELAYOUT
@@ -246,7 +247,7 @@ def gdn(lib, k=2, Hv=4, Hk=4, Dk=64, Dv=64, snaps=None, S_in=P, y=P + 0x700000):
 
 def test_gdn_validation(lib):
     assert gdn(lib, k=0) == L.SDV_EWIDTH
-    assert gdn(lib, k=10) == L.SDV_EWIDTH
+    assert gdn(lib, k=33) == L.SDV_EWIDTH
     assert gdn(lib, Dk=96) == L.SDV_ELAYOUT
     assert gdn(lib, Dk=256) == L.SDV_ELAYOUT
     assert gdn(lib, Hv=6, Hk=4) == L.SDV_ELAYOUT
@@ -263,13 +264,13 @@ def test_gdn_validation(lib):
 
 def test_rollback_selection(lib):
     slot = ctypes.c_int(-7)
-    for k in range(1, 10):
+    for k in range(1, 33):
         for j in range(0, k + 1):
             assert lib.sdv_gdn_rollback(k, j, ctypes.byref(slot)) == 0
             assert slot.value == j
         assert lib.sdv_gdn_rollback(k, k + 1, ctypes.byref(slot)) == L.SDV_ERANGE
         assert lib.sdv_gdn_rollback(k, -1, ctypes.byref(slot)) == L.SDV_ERANGE
-    assert lib.sdv_gdn_rollback(10, 1, ctypes.byref(slot)) == L.SDV_EWIDTH
+    assert lib.sdv_gdn_rollback(33, 1, ctypes.byref(slot)) == L.SDV_EWIDTH
     assert lib.sdv_gdn_rollback(2, 1, None) == L.SDV_EINVAL
 
 
@@ -289,7 +290,8 @@ def test_accept_workspace_bytes(lib):
     assert lib.sdv_verify_accept_workspace_bytes(9, 248320) == 9 * 61 * 8
     assert lib.sdv_verify_accept_workspace_bytes(1, 1) == 8
     assert lib.sdv_verify_accept_workspace_bytes(2, 4097) == 2 * 2 * 8
-    for k, V in [(0, 10), (10, 10), (2, 0), (2, -5)]:
+    assert lib.sdv_verify_accept_workspace_bytes(32, 248320) == 32 * 61 * 8
+    for k, V in [(0, 10), (33, 10), (2, 0), (2, -5)]:
         assert lib.sdv_verify_accept_workspace_bytes(k, V) == 0
 
 
@@ -306,7 +308,7 @@ def test_accept_validation(lib):
                  a["ws"], a["wsb"], None)
 
     assert call(k=0) == L.SDV_EWIDTH
-    assert call(k=10) == L.SDV_EWIDTH
+    assert call(k=33) == L.SDV_EWIDTH
     assert call(V=0) == L.SDV_ERANGE
     assert call(V=(1 << 30) + 1) == L.SDV_ERANGE
     assert call(logits=None) == L.SDV_EINVAL
@@ -339,7 +341,7 @@ def prep(lib, k=2, Hv=4, Hk=2, Dk=64, Dv=64, act=0, eps=1e-6, **over):
 
 def test_prepare_validation(lib):
     assert prep(lib, k=0) == L.SDV_EWIDTH
-    assert prep(lib, k=10) == L.SDV_EWIDTH
+    assert prep(lib, k=33) == L.SDV_EWIDTH
     assert prep(lib, Hv=0) == L.SDV_EINVAL
     assert prep(lib, Hv=5, Hk=2) == L.SDV_ELAYOUT
     assert prep(lib, Dk=128, Dv=64) == L.SDV_ELAYOUT
@@ -388,7 +390,7 @@ def verify_prep(lib, k=2, Hv=4, Hk=2, D=64, Dv=None, act=0, eps=1e-6, snaps=None
 
 def test_verify_prep_validation(lib):
     assert verify_prep(lib, k=0) == L.SDV_EWIDTH
-    assert verify_prep(lib, k=10) == L.SDV_EWIDTH
+    assert verify_prep(lib, k=33) == L.SDV_EWIDTH
     assert verify_prep(lib, Hv=5) == L.SDV_ELAYOUT
     assert verify_prep(lib, D=128, Dv=64) == L.SDV_ELAYOUT
     assert verify_prep(lib, D=32) == L.SDV_ELAYOUT
