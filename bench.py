@@ -2,15 +2,20 @@
 """Benchmark of one exact k-row verification step on one MI355X.
 
 Workload (default ``flashnext_k9``): the Flash-Next-shaped hybrid at k = 9
-draft rows.  One step runs, for each of the 48 layers, the Gated DeltaNet
-verify with per-row snapshots (on the 36 layers with l % 4 != 3) and the MoE
-verify (router dispatch and union over 512 experts, top-10 sigmoid scores
-renormalised; the fused expert kernel: gate/up + SwiGLU + down over the
-union's affine-Q4/g64 experts [512, 1280, 2560] / [512, 2560, 640] and the
-sigmoid-gated shared expert; the fixed-order combine), then rolls every GDN
-layer back to an accepted prefix j ~ U{0..9} by slot selection.  All inputs
-are synthetic (synth/), generated before timing and resident in HBM: 67.9 GB
-of expert weights, 48 shared experts and 36 fp32 GDN state pools.
+draft rows (``flashnext_k16`` and ``flashnext_k32``: the same step at the
+verifier's wide widths).  One step runs, for each of the 48 layers, the Gated
+DeltaNet verify from the layer's projections on the 36 layers with l % 4 != 3
+(one launch: causal conv over q/k/v with the carried conv history, q/k L2
+norm, decay and beta gates, the recurrence with per-row snapshots; then the
+gated output norm) and the MoE verify (router dispatch and union over 512
+experts, top-10 sigmoid scores renormalised; the fused expert kernel:
+gate/up + SwiGLU + down over the union's affine-Q4/g64 experts
+[512, 1280, 2560] / [512, 2560, 640] and the sigmoid-gated shared expert;
+the fixed-order combine); then the acceptance of the block over a
+248,320-token vocabulary, and every GDN layer rolls back (state and conv
+history) to the accepted prefix by selection.  All inputs are synthetic
+(synth/), generated before timing and resident in HBM: 67.9 GB of expert
+weights, 48 shared experts and 36 fp32 GDN state pools.
 
 Prints one JSON line: verified rows/s (k rows per step), the roofline of the
 dominant kernel (the fused expert kernel, timed with HIP events on its
@@ -51,7 +56,8 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="flashnext_k9", choices=["flashnext_k9"])
+    p.add_argument("--workload", default="flashnext_k9",
+                   choices=["flashnext_k9", "flashnext_k16", "flashnext_k32"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel instrumented pass")
     p.add_argument("--copy-probe", action="store_true",
@@ -148,7 +154,7 @@ def cpu_model():
 
 
 class Workload:
-    """Device-resident inputs and bound launches of the flashnext_k9 step."""
+    """Device-resident inputs and bound launches of the flashnext step at k rows."""
 
     def __init__(self, dev, k=9):
         import torch
@@ -379,10 +385,10 @@ def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
     t_acc = time.perf_counter() - t0
     step = cfg.layers * t_moe / n_moe + len(cfg.gdn_layers) * t_gdn / n_gdn + t_acc
     return {"value": k / step, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": (f"flashnext_k9 layers 0..{n_moe - 1}: {n_moe} MoE layers (union experts {unions}, "
+            "sample": (f"flashnext_k{k} layers 0..{n_moe - 1}: {n_moe} MoE layers (union experts {unions}, "
                        f"{t_moe:.1f} s) and {n_gdn} GDN layers ({t_gdn:.2f} s) of the oracle (numpy fp64, "
                        f"{t_moe + t_gdn:.1f} s in all), scaled to 48 MoE + 36 GDN layers per step, plus one "
-                       f"acceptance of the block ({t_acc:.2f} s) ({step:.1f} s per 9-row step)"),
+                       f"acceptance of the block ({t_acc:.2f} s) ({step:.1f} s per {k}-row step)"),
             "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
 
 
@@ -451,8 +457,8 @@ def main():
     from speculative_decode_verification_amd import _lib
     _lib.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    k = 9
-    log("building workload (device-filled banks) ...")
+    k = int(args.workload.rsplit("_k", 1)[1])
+    log(f"building workload {args.workload} (device-filled banks) ...")
     wl = Workload(dev, k)
     log(f"workload ready in {wl.setup_s:.1f} s: {wl.bank_bytes / 1e9:.1f} GB of Q4 banks, "
         f"{len(wl.gdn)} GDN layers")
@@ -484,7 +490,7 @@ def main():
     dom_avg_us = sum(dom_us) / len(dom_us)
     dom_gbs = sum(dom_bytes) / (sum(dom_us) * 1e-6) / 1e9
     khash = kernel_source_hash()
-    traffic = traffic_for(khash)
+    traffic = traffic_for(khash) if args.workload == "flashnext_k9" else None
 
     breakdown = None
     if not args.no_breakdown:
@@ -527,7 +533,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "flashnext_k9", "rows": k, "layers": wl.layers, "gdn_layers": len(wl.gdn),
+        "config": {"workload": args.workload, "rows": k, "layers": wl.layers, "gdn_layers": len(wl.gdn),
                    "experts": wl.E, "topk": wl.topk, "hidden": wl.H, "inter": wl.I, "shared_expert": True,
                    "gdn_heads": [wl.gs.hv, wl.gs.hk, wl.gs.dk], "vocab": wl.vocab,
                    "mean_union": round(sum(unions) / len(unions), 2),
