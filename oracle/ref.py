@@ -71,6 +71,48 @@ def qmv(codes, scales, biases, x):
 # + 1 shared)
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# Q8_0 (Red Lite dev45, "What it is": the MTP block's 512 experts are Q8_0 and
+# decode bit-identically to the dense Q8_0 dequantizer; mere.run transfer
+# report, "Shared architecture and implemented paths": the checkpoint's Q8
+# router and shared-gate weights).  The GGUF Q8_0 block: 32 signed 8-bit codes
+# sharing one IEEE half scale.
+# ---------------------------------------------------------------------------
+
+Q8_BLOCK = 32
+
+
+def fp16_to_f64(bits):
+    """IEEE binary16 bit patterns (uint16) to fp64, from the fields: sign,
+    5-bit exponent with bias 15, 10-bit fraction; exponent 0 is subnormal
+    (f * 2^-24), exponent 31 is infinity (f = 0) or NaN."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 31
+    f = (b & 1023).astype(np.float64)
+    normal = (1.0 + f / 1024.0) * np.exp2((e - 15).astype(np.float64))
+    val = np.where(e == 0, f * 2.0 ** -24, normal)
+    val = np.where(e == 31, np.where(f == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def dequant_q8_0(qs, d):
+    """Dense fp64 weights: ``W[n, c] = d[n, c // 32] * q[n, c]`` with q the
+    signed 8-bit code ``qs[n, c]`` and d the half scale of its 32-element
+    block.  Exact in fp64."""
+    q = np.asarray(qs, dtype=np.int8).astype(np.float64)
+    s = np.repeat(fp16_to_f64(d), Q8_BLOCK, axis=-1)
+    return s * q
+
+
+def qmv_q8_0(qs, d, x):
+    """Multi-row Q8_0 matvec, each row on its own: ``y[r] = W @ x[r]`` (the
+    same per-row definition as ``qmv``)."""
+    w = dequant_q8_0(qs, d)
+    x = np.asarray(x, dtype=np.float64)
+    return np.stack([w @ x[r] for r in range(x.shape[0])])
+
+
 def route(logits, topk, mode, renorm):
     """Per-row top-k experts and their weights.
 

@@ -28,6 +28,7 @@ DENSE_W, GATEUP, DOWN, SHARED_GATEUP, SHARED_DOWN = 0, 1, 2, 3, 4
 T_X, T_LOGITS, T_Z, T_S, T_Q, T_K, T_V, T_G, T_BETA, T_J = 10, 11, 12, 20, 21, 22, 23, 24, 25, 30
 T_VLOGITS, T_GUMBEL, T_DRAFTS = 40, 41, 42
 T_QKV, T_HIST, T_CONVW, T_A, T_B, T_ALOG, T_DTB, T_GATEZ, T_NORMW = 50, 51, 52, 53, 54, 55, 56, 57, 58
+T_Q8 = 60
 
 
 def bank_keys(cfg_id, kind, layer):
@@ -86,6 +87,16 @@ def gdn_layer_inputs(cfg_id, layer, rows, hv, hk, dk, dv, step=0):
 def accepted_prefix(cfg_id, step, rows):
     """Accepted-prefix length j ~ U{0..rows} for one verify step."""
     return int(_rng(cfg_id, T_J, step).integers(0, rows + 1))
+
+
+def q8_0_weight(cfg_id, kind, layer, E, N, K):
+    """A Q8_0 weight in the GGUF interchange form: signed codes int8
+    [E, N, K] ~ U{-127..127} (a Q8_0 quantiser never emits -128) and half
+    scales [E, N, K/32] ~ U(2e-4, 8e-4) as IEEE binary16 bit patterns."""
+    rng = _rng(cfg_id, T_Q8, kind, layer)
+    qs = rng.integers(-127, 128, size=(E, N, K), dtype=np.int64).astype(np.int8)
+    d = rng.uniform(2e-4, 8e-4, size=(E, N, K // 32)).astype(np.float16).view(np.uint16)
+    return qs, d
 
 
 def integer_exact_weight(seed, n, k, rows):

@@ -9,6 +9,7 @@ can run them against copies of the oracle with planted mistakes.
 
 from fractions import Fraction
 import math
+import struct
 
 import numpy as np
 
@@ -701,6 +702,57 @@ def check_gated_norm(ref):
     assert np.allclose(sig, ref.gdn_gated_norm(y, big, np.ones(6)) / (1.0 + np.exp(-z)), rtol=1e-12)
 
 
+def half_exact(bits):
+    """Exact value of an IEEE binary16 bit pattern, decoded by Python's struct
+    module (format 'e')."""
+    return Fraction(struct.unpack("<e", struct.pack("<H", int(bits)))[0])
+
+
+def check_fp16_decode(ref):
+    """Q8_0 scales: every 97th finite half pattern against struct's decoder,
+    and the special values."""
+    pats = [p for p in range(0, 65536, 97) if (p >> 10) & 31 != 31]
+    got = ref.fp16_to_f64(np.array(pats, dtype=np.uint16))
+    for p, g in zip(pats, got):
+        assert Fraction(float(g)) == half_exact(p), hex(p)
+    sp = ref.fp16_to_f64(np.array([0x7C00, 0xFC00, 0x7E00, 0x0001, 0x8000, 0x3C00, 0x03FF, 0x7BFF], dtype=np.uint16))
+    assert sp[0] == np.inf and sp[1] == -np.inf and np.isnan(sp[2])
+    assert sp[3] == 2.0 ** -24 and sp[4] == 0.0 and np.signbit(sp[4]) and sp[5] == 1.0
+    assert sp[6] == 1023 * 2.0 ** -24 and sp[7] == 65504.0
+
+
+def check_q8_0_bruteforce(ref):
+    """Q8_0 product: exact rational brute force on tiny inputs (codes over the
+    whole int8 range, one scale per 32 inputs)."""
+    for (n, k, rows) in [(3, 64, 1), (4, 96, 2), (2, 32, 3)]:
+        qs, d = synth.q8_0_weight(0, 9, n + k, 1, n, k)
+        qs, d = qs[0], d[0]
+        qs[0, :3] = np.array([-128, 127, 0], dtype=np.int8)
+        xb = synth.bf16_bits_from_f32(np.random.default_rng(n * k).standard_normal((rows, k), dtype=np.float32))
+        y = ref.qmv_q8_0(qs, d, ref.bf16_to_f64(xb))
+        for r in range(rows):
+            ex = [sum(half_exact(d[o, c // 32]) * int(qs[o, c]) * bf16_exact(xb[r, c]) for c in range(k))
+                  for o in range(n)]
+            scale = max(abs(float(v)) for v in ex)
+            for o in range(n):
+                assert abs(float(Fraction(float(y[r, o])) - ex[o])) <= 1e-13 * scale, (n, k, r, o)
+
+
+def check_q8_0_blocks(ref):
+    """Unit activations read single weights: with x = e_c, y[n] = d[n, c // 32]
+    * q[n, c] exactly, so every block boundary and the sign of every code are
+    checked."""
+    n, k = 3, 128
+    qs, d = synth.q8_0_weight(0, 10, 0, 1, n, k)
+    qs, d = qs[0], d[0]
+    for c in (0, 31, 32, 63, 64, 127):
+        x = np.zeros((1, k))
+        x[0, c] = 1.0
+        y = ref.qmv_q8_0(qs, d, x)[0]
+        for o in range(n):
+            assert Fraction(float(y[o])) == half_exact(d[o, c // 32]) * int(qs[o, c]), (c, o)
+
+
 ALL_CHECKS = [
     check_bf16_decode, check_unpack_roundtrip, check_qmv_bruteforce, check_qmv_integer_exact,
     check_qmv_closed_forms, check_qmv_rows_independent, check_route_selection, check_route_weights,
@@ -710,5 +762,5 @@ ALL_CHECKS = [
     check_gdn_head_groups, check_gdn_rollback, check_sample_greedy, check_sample_noise_rounding,
     check_sample_gumbel_is_softmax, check_accept_cases, check_verify_cycle_rollback,
     check_conv_is_convolution, check_conv_alignment, check_conv_history_chain, check_qk_l2_norm, check_gates,
-    check_gated_norm,
+    check_gated_norm, check_fp16_decode, check_q8_0_bruteforce, check_q8_0_blocks,
 ]

@@ -56,6 +56,13 @@ MUTANTS = {
     "norm_sum_not_mean": ("n = y / np.sqrt((y * y).mean(axis=-1, keepdims=True) + eps)", "n = y / np.sqrt((y * y).sum(axis=-1, keepdims=True) + eps)"),
     "norm_weight_dropped": ("return n * np.asarray(w, dtype=np.float64) * gate", "return n * gate"),
     "gate_silu_for_sigmoid": ("        gate = 1.0 / (1.0 + np.exp(-z))", "        gate = silu(z)"),
+    "q8_block_64": ("Q8_BLOCK = 32", "Q8_BLOCK = 64"),
+    "fp16_exponent_bias": ("np.exp2((e - 15)", "np.exp2((e - 16)"),
+    "fp16_subnormal_scale": ("f * 2.0 ** -24", "f * 2.0 ** -25"),
+    "q8_codes_unsigned": ("q = np.asarray(qs, dtype=np.int8).astype(np.float64)",
+                          "q = np.asarray(qs, dtype=np.int8).view(np.uint8).astype(np.float64)"),
+    "q8_scale_block_shift": ("s = np.repeat(fp16_to_f64(d), Q8_BLOCK, axis=-1)",
+                             "s = np.roll(np.repeat(fp16_to_f64(d), Q8_BLOCK, axis=-1), 1, axis=-1)"),
 }
 
 
