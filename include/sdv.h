@@ -123,7 +123,48 @@ typedef struct sdv_q4t {
   const uint32_t *sb;
   int32_t E, N, K, group;
   int32_t fused_gateup;
+  int32_t format; /* SDV_FMT_AFFINE_Q4 (0, the layout above) or SDV_FMT_Q8_0 (below) */
 } sdv_q4t;
+
+/* Formats of a tiled weight (sdv_q4t.format). */
+#define SDV_FMT_AFFINE_Q4 0
+#define SDV_FMT_Q8_0 1
+
+/*
+ * A Q8_0 weight in row-major interchange layout (the GGUF Q8_0 block: 32
+ * signed 8-bit codes sharing one IEEE half scale; Red Lite dev45, "What it
+ * is": the MTP block's Q8_0 experts; mere.run transfer report, "Shared
+ * architecture and implemented paths": Q8 router and shared-gate weights).
+ *   qs  [E][N][K] int8 codes q;  d  [E][N][K/32] binary16 scale bits
+ *   value  W[e][n][c] = d[e][n][c/32] * q[e][n][c]
+ * K must be a positive multiple of 64 (the tiled group).
+ */
+typedef struct sdv_q8_0 {
+  const int8_t *qs;
+  const uint16_t *d;
+  int32_t E, N, K;
+} sdv_q8_0;
+
+/*
+ * The tiled Q8_0 layout (format = SDV_FMT_Q8_0, written by sdv_q8_0_repack),
+ * tiles as above:
+ *   codes  [E][T][K/64][2][64][16 bytes]: for tile t, group g and half p,
+ *          chunk l = 32h + c holds the bytes u = q + 128 of elements
+ *          32p + 8h + i (words 0, 1: i = 0..3, 4..7) and 32p + 16 + 8h + i
+ *          (words 2, 3) of the group, of the tile's row c;
+ *   sb     [E][T][K/64][32] uint32: half scale bits of block 2g | block 2g + 1 << 16.
+ * Sizes: sdv_q8_0t_codes_bytes; sdv_q4t_sb_bytes.
+ */
+SDV_API size_t sdv_q8_0t_codes_bytes(int E, int N, int K, int fused_gateup);
+
+/*
+ * sdv_q8_0_repack -- rewrite a row-major Q8_0 weight into the tiled layout
+ * (device to device, on `stream`); fused_gateup as for sdv_q4_repack.
+ *   codes_out  device, sdv_q8_0t_codes_bytes(...) bytes; sb_out device, sdv_q4t_sb_bytes(...)
+ * Errors: EINVAL, ELAYOUT, EALIAS, EHIP.
+ */
+SDV_API int sdv_q8_0_repack(const sdv_q8_0 *src, int fused_gateup, void *codes_out, uint32_t *sb_out,
+                            sdv_stream_t stream);
 
 /* Bytes of the tiled codes / scale-bias arrays of an E x N x K weight. */
 SDV_API size_t sdv_q4t_codes_bytes(int E, int N, int K, int fused_gateup);

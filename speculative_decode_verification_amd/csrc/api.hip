@@ -12,9 +12,10 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
                      const int32_t* union_ids, const int32_t* n_union, const int32_t* pair_off,
                      const int32_t* pair_row, const int32_t* pair_slot, int k, int topk, float* out,
                      const sdv_q4t* shared, const void* shared_act, float* shared_out, hipStream_t st);
-int q4_waves_for(int K);
-size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather);
+size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather, int fmt);
 size_t q4t_codes_bytes(int E, int N, int K, int fused);
+size_t q8_0t_codes_bytes(int E, int N, int K, int fused);
+hipError_t q8_0_repack_launch(const sdv_q8_0& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st);
 size_t q4t_sb_bytes(int E, int N, int K, int fused);
 hipError_t q4_repack_launch(const sdv_q4& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st);
 hipError_t route_launch(const float* logits, int k, int E, int topk, int mode, int renorm,
@@ -140,6 +141,8 @@ int check_q4t(const sdv_q4t* W, const char* what) {
   if (W->fused_gateup != 0 && W->fused_gateup != 1)
     return fail(SDV_ELAYOUT, "%s fused_gateup=%d must be 0 or 1", what, W->fused_gateup);
   if (W->fused_gateup && (W->N % 2)) return fail(SDV_ELAYOUT, "%s fused gate/up needs an even N", what);
+  if (W->format != SDV_FMT_AFFINE_Q4 && W->format != SDV_FMT_Q8_0)
+    return fail(SDV_ELAYOUT, "%s format=%d is not a known weight format", what, W->format);
   int st;
   if ((st = check_ptr(W->codes, "codes"))) return st;
   if ((st = check_ptr(W->sb, "sb"))) return st;
@@ -165,9 +168,15 @@ int check_mode(int mode, int act_dtype, int N) {
   return SDV_OK;
 }
 
+// Tiled code bytes of a weight in its format.
+size_t tiled_codes_bytes(const sdv_q4t& W) {
+  return W.format == SDV_FMT_Q8_0 ? sdv::q8_0t_codes_bytes(W.E, W.N, W.K, W.fused_gateup)
+                                  : sdv::q4t_codes_bytes(W.E, W.N, W.K, W.fused_gateup);
+}
+
 int check_lds(const sdv_q4t& W, int act_dtype, int k, bool gather) {
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
-  const size_t lds = sdv::q4_lds_bytes_for(W.K, act_dtype, k, gather);
+  const size_t lds = sdv::q4_lds_bytes_for(W.K, act_dtype, k, gather, W.format);
   if (lds > kMaxLds)
     return fail(SDV_ELAYOUT, "K=%d with %d activation rows needs %zu bytes of LDS (max %zu)", W.K, cap,
                 lds, kMaxLds);
@@ -227,6 +236,31 @@ int sdv_q4_repack(const sdv_q4* src, int fused_gateup, void* codes_out, uint32_t
                     "sdv_q4_repack launch");
 }
 
+size_t sdv_q8_0t_codes_bytes(int E, int N, int K, int fused_gateup) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % SDV_GROUP) return 0;
+  return sdv::q8_0t_codes_bytes(E, N, K, fused_gateup ? 1 : 0);
+}
+
+int sdv_q8_0_repack(const sdv_q8_0* src, int fused_gateup, void* codes_out, uint32_t* sb_out, sdv_stream_t stream) {
+  int st;
+  if (!src) return fail(SDV_EINVAL, "src descriptor is NULL");
+  if (src->K <= 0 || src->K % SDV_GROUP) return fail(SDV_ELAYOUT, "src K=%d is not a positive multiple of 64", src->K);
+  if (src->N <= 0 || src->E <= 0) return fail(SDV_EINVAL, "src E=%d N=%d must be positive", src->E, src->N);
+  if (fused_gateup != 0 && fused_gateup != 1) return fail(SDV_ELAYOUT, "fused_gateup=%d must be 0 or 1", fused_gateup);
+  if (fused_gateup && (src->N % 2)) return fail(SDV_ELAYOUT, "fused gate/up needs an even N (got %d)", src->N);
+  if ((st = check_ptr(src->qs, "qs"))) return st;
+  if ((st = check_ptr(src->d, "d"))) return st;
+  if ((st = check_ptr(codes_out, "codes_out"))) return st;
+  if ((st = check_ptr(sb_out, "sb_out"))) return st;
+  const size_t elems = (size_t)src->E * src->N * src->K;
+  Range outs[] = {{codes_out, sdv::q8_0t_codes_bytes(src->E, src->N, src->K, fused_gateup), "codes_out"},
+                  {sb_out, sdv::q4t_sb_bytes(src->E, src->N, src->K, fused_gateup), "sb_out"}};
+  Range ins[] = {{src->qs, elems, "qs"}, {src->d, elems / 32 * 2, "d"}};
+  if ((st = check_alias(outs, 2, ins, 2))) return st;
+  return hip_status(sdv::q8_0_repack_launch(*src, fused_gateup, codes_out, sb_out, (hipStream_t)stream),
+                    "sdv_q8_0_repack launch");
+}
+
 int sdv_qmv_k(const sdv_q4t* W, const void* act, int act_dtype, int k, int mode, float* y,
               sdv_stream_t stream) {
   int st;
@@ -241,7 +275,7 @@ int sdv_qmv_k(const sdv_q4t* W, const void* act, int act_dtype, int k, int mode,
   const size_t act_bytes = (size_t)k * W->K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
   const size_t n_out = mode == SDV_MODE_PLAIN ? W->N : W->N / 2;
   Range outs[] = {{y, (size_t)k * n_out * 4, "y"}};
-  Range ins[] = {{W->codes, sdv::q4t_codes_bytes(W->E, W->N, W->K, W->fused_gateup), "codes"},
+  Range ins[] = {{W->codes, tiled_codes_bytes(*W), "codes"},
                  {W->sb, sdv::q4t_sb_bytes(W->E, W->N, W->K, W->fused_gateup), "sb"},
                  {act, act_bytes, "act"}};
   if ((st = check_alias(outs, 1, ins, 3))) return st;
@@ -298,9 +332,12 @@ int sdv_gather_qmv_k(const sdv_q4t* bank, int mode, const void* act, int act_dty
   if (shared) {
     if ((st = check_q4t(shared, "shared"))) return st;
     if (shared->E != 1) return fail(SDV_EINVAL, "shared expert needs E=1 (got %d)", shared->E);
-    if (shared->N != bank->N || shared->K != bank->K || shared->fused_gateup != bank->fused_gateup)
-      return fail(SDV_ELAYOUT, "shared expert geometry (N=%d K=%d fused=%d) differs from the bank's (N=%d K=%d fused=%d)",
-                  shared->N, shared->K, shared->fused_gateup, bank->N, bank->K, bank->fused_gateup);
+    if (shared->N != bank->N || shared->K != bank->K || shared->fused_gateup != bank->fused_gateup ||
+        shared->format != bank->format)
+      return fail(SDV_ELAYOUT,
+                  "shared expert geometry (N=%d K=%d fused=%d format=%d) differs from the bank's (N=%d K=%d fused=%d format=%d)",
+                  shared->N, shared->K, shared->fused_gateup, shared->format, bank->N, bank->K, bank->fused_gateup,
+                  bank->format);
     if ((st = check_ptr(shared_act, "shared_act"))) return st;
     if ((st = check_ptr(shared_out, "shared_out"))) return st;
   } else if (shared_act || shared_out) {
@@ -311,7 +348,7 @@ int sdv_gather_qmv_k(const sdv_q4t* bank, int mode, const void* act, int act_dty
   const size_t n_out = mode == SDV_MODE_PLAIN ? bank->N : bank->N / 2;
   const size_t sh_act_bytes = shared ? (size_t)k * bank->K * (act_dtype == SDV_ACT_F32 ? 4 : 2) : 0;
   Range outs[] = {{out, kt * n_out * 4, "out"}, {shared_out, shared ? (size_t)k * n_out * 4 : 0, "shared_out"}};
-  Range ins[] = {{bank->codes, sdv::q4t_codes_bytes(bank->E, bank->N, bank->K, bank->fused_gateup), "codes"},
+  Range ins[] = {{bank->codes, tiled_codes_bytes(*bank), "codes"},
                  {bank->sb, sdv::q4t_sb_bytes(bank->E, bank->N, bank->K, bank->fused_gateup), "sb"},
                  {act, act_bytes, "act"},
                  {union_ids, kt * 4, "union_ids"},
@@ -319,8 +356,7 @@ int sdv_gather_qmv_k(const sdv_q4t* bank, int mode, const void* act, int act_dty
                  {pair_off, (kt + 1) * 4, "pair_off"},
                  {pair_row, kt * 4, "pair_row"},
                  {pair_slot, kt * 4, "pair_slot"},
-                 {shared ? shared->codes : nullptr, shared ? sdv::q4t_codes_bytes(1, bank->N, bank->K, bank->fused_gateup) : 0,
-                  "shared codes"},
+                 {shared ? shared->codes : nullptr, shared ? tiled_codes_bytes(*shared) : 0, "shared codes"},
                  {shared ? shared->sb : nullptr, shared ? sdv::q4t_sb_bytes(1, bank->N, bank->K, bank->fused_gateup) : 0,
                   "shared sb"},
                  {shared_act, sh_act_bytes, "shared_act"}};
@@ -346,6 +382,10 @@ int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x
   if ((st = check_q4t(gate_up, "gate_up"))) return st;
   if ((st = check_q4t(down, "down"))) return st;
   if (!gate_up->fused_gateup) return fail(SDV_ELAYOUT, "gate_up must be repacked with fused_gateup=1");
+  if (gate_up->format != SDV_FMT_AFFINE_Q4 || down->format != SDV_FMT_AFFINE_Q4 ||
+      (shared_gate_up && shared_gate_up->format != SDV_FMT_AFFINE_Q4) ||
+      (shared_down && shared_down->format != SDV_FMT_AFFINE_Q4))
+    return fail(SDV_ELAYOUT, "the fused expert kernel takes affine Q4 weights; use sdv_gather_qmv_k for Q8_0");
   if (down->fused_gateup) return fail(SDV_ELAYOUT, "down must be repacked with fused_gateup=0");
   const int H = gate_up->K, I = gate_up->N / 2;
   if (down->E != gate_up->E || down->N != H || down->K != I)

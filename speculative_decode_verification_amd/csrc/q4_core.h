@@ -67,18 +67,29 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+// The same over the 4 lanes l .. l+3 (l a multiple of 4).
+__device__ __forceinline__ float sum4(float x) {
+  x = x + __shfl_xor(x, 1);
+  x = x + __shfl_xor(x, 2);
+  return x;
+}
+
 // Stage the unit's activation rows into LDS (NU order, bf16 parts) and their
 // per-group sums (indexed by MFMA row).  One task = (row, 8-element block):
 // the block's elements are summed in order, then the 8 blocks of a group are
 // summed by the fixed 8-lane pairing above.
 //   act       rows of K elements (bf16 bits or fp32), row s_src[i] feeds row i
 //   slot_cap  LDS row of the all-zero row (rows past the data read it)
-template <int ACT>
+//   FMT       SDV_FMT_AFFINE_Q4: one sum per 64-element group (xsum [32][G]);
+//             SDV_FMT_Q8_0: one per 32-element block (xsum [32][2G]), the
+//             first four 8-blocks then the last four, each added pairwise
+template <int ACT, int FMT = SDV_FMT_AFFINE_Q4>
 __device__ __forceinline__ void stage_rows(const void* act, int K, int slot_cap, int nrows, uint16_t* xs,
                                            float* xsum, int rs, const int* s_src) {
   const int G = K >> 6, nb = K >> 3;
+  constexpr int SPG = FMT == SDV_FMT_Q8_0 ? 2 : 1;  // sums per group
   const int tid = threadIdx.x, nthreads = blockDim.x;
-  for (int t = tid; t < 32 * G; t += nthreads) xsum[t] = 0.0f;
+  for (int t = tid; t < 32 * G * SPG; t += nthreads) xsum[t] = 0.0f;
   uint32_t* zrow = reinterpret_cast<uint32_t*>(xs + (size_t)slot_cap * rs);
   for (int t = tid; t < rs / 2; t += nthreads) zrow[t] = 0u;
   __syncthreads();
@@ -110,8 +121,13 @@ __device__ __forceinline__ void stage_rows(const void* act, int K, int slot_cap,
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc = acc + bf16_bits_to_f32(e8[c]);
         *reinterpret_cast<uint4*>(xs + (size_t)i * rs + b8 * 8) = nu_pack(e8);
-        acc = sum8(acc);
-        if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, 0) * G + (b8 >> 3)] = acc;
+        if constexpr (FMT == SDV_FMT_Q8_0) {
+          acc = sum4(acc);
+          if ((b8 & 3) == 0) xsum[vrow_of<ACT>(i, 0) * 2 * G + (b8 >> 2)] = acc;
+        } else {
+          acc = sum8(acc);
+          if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, 0) * G + (b8 >> 3)] = acc;
+        }
       }
     } else {
       float4 v0[B], v1[B];
@@ -148,8 +164,13 @@ __device__ __forceinline__ void stage_rows(const void* act, int K, int slot_cap,
         *reinterpret_cast<uint4*>(xs + (size_t)(3 * i + 2) * rs + b8 * 8) = nu_pack(lo);
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-          const float t = sum8(acc[p]);
-          if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, p) * G + (b8 >> 3)] = t;
+          if constexpr (FMT == SDV_FMT_Q8_0) {
+            const float t = sum4(acc[p]);
+            if ((b8 & 3) == 0) xsum[vrow_of<ACT>(i, p) * 2 * G + (b8 >> 2)] = t;
+          } else {
+            const float t = sum8(acc[p]);
+            if ((b8 & 7) == 0) xsum[vrow_of<ACT>(i, p) * G + (b8 >> 3)] = t;
+          }
         }
       }
     }
@@ -234,6 +255,103 @@ __device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, con
   for (int i = 0; i < 5; ++i) {
     y[i] = fmaf(s, t[i], y[i]);
     y[i] = fmaf(c, xr[i][s_idx], y[i]);
+  }
+}
+
+// ---- Q8_0 ---------------------------------------------------------------
+// The tiled code byte is u = q + 128 (0..255): it converts exactly to fp32,
+// and with at most 8 significant bits its bf16 is the fp32's high half.  The
+// matrix core returns P = sum u x = sum q x + 128 X per 32-element block, so
+// a block adds d P - 128 d X.  MFMA step j of lane half h takes elements
+// 16 j + 8 h .. + 7 of the group (steps 0-1: block 0, steps 2-3: block 1);
+// its two code words hold elements 0-3 and 4-7, and the pairs (byte i of
+// word 0, byte i of word 1) give K slots in the Q4 decode's NU order.
+__device__ __forceinline__ uint32_t q8_pair(uint32_t w0, uint32_t w1, int i) {
+  const float lo = (float)((w0 >> (8 * i)) & 0xFFu);
+  const float hi = (float)((w1 >> (8 * i)) & 0xFFu);
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);  // hi.h16 : lo.h16
+}
+
+__device__ __forceinline__ bf16x8 decode_q8(uint32_t w0, uint32_t w1) {
+  uint32_t p[4] = {q8_pair(w0, w1, 0), q8_pair(w0, w1, 1), q8_pair(w0, w1, 2), q8_pair(w0, w1, 3)};
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(p));
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// The two blocks' matrix products of one Q8_0 group: acc[0] over block 0,
+// acc[1] over block 1.  `ap` points at the lane's row at element 8 h of the
+// group (steps at + 16 j); c0 holds code words 0-3 (steps 0, 1), c1 words
+// 4-7 (steps 2, 3).
+__device__ __forceinline__ void q8_products(const uint4 c0, const uint4 c1, const uint16_t* ap, f32x16 (&acc)[2]) {
+  uint4 av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(ap + j * 16);
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+  acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[0]), decode_q8(c0.x, c0.y), acc[0],
+                                                   0, 0, 0);
+  acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[1]), decode_q8(c0.z, c0.w), acc[0],
+                                                   0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[2]), decode_q8(c1.x, c1.y), acc[1],
+                                                   0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[3]), decode_q8(c1.z, c1.w), acc[1],
+                                                   0, 0, 0);
+}
+
+// group_mac for a Q8_0 group: xs_g points at the group's two block sums of
+// MFMA row 0 (row vr at xs_g[vr * G2], G2 = 2 G); sbw holds the blocks' half
+// scales (block 0 low, block 1 high).  Per block b: yacc += d_b P_b - 128 d_b X_b.
+__device__ __forceinline__ void group_mac_q8(const uint4 c0, const uint4 c1, uint32_t sbw, const uint16_t* ap,
+                                             const float* xs_g, int G2, int half, int nquads, float yacc[16]) {
+  f32x16 acc[2];
+  q8_products(c0, c1, ap, acc);
+  const float d[2] = {half_bits_to_f32(sbw & 0xFFFFu), half_bits_to_f32(sbw >> 16)};
+  const float c[2] = {-128.0f * d[0], -128.0f * d[1]};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < nquads) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * q + r;
+        const float* xg = xs_g + (8 * q + 4 * half + r) * G2;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          yacc[v] = fmaf(d[b], acc[b][v], yacc[v]);
+          yacc[v] = fmaf(c[b], xg[b], yacc[v]);
+        }
+      }
+    }
+  }
+}
+
+// group_mac_rows for a Q8_0 group: xr[i] points at the block sums of the row
+// behind y[i] (two per group: xr[i][2 s_idx + b]).
+template <int ACT>
+__device__ __forceinline__ void group_mac_rows_q8(const uint4 c0, const uint4 c1, uint32_t sbw, const uint16_t* ap,
+                                                  const float* const (&xr)[5], int s_idx, float y[5]) {
+  f32x16 acc[2];
+  q8_products(c0, c1, ap, acc);
+  const float d[2] = {half_bits_to_f32(sbw & 0xFFFFu), half_bits_to_f32(sbw >> 16)};
+  const float c[2] = {-128.0f * d[0], -128.0f * d[1]};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float t[5];
+    if (ACT == SDV_ACT_BF16) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) t[i] = acc[b][i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = (acc[b][i] + acc[b][4 + i]) + acc[b][8 + i];
+      t[4] = (acc[b][12] + acc[b][13]) + acc[b][14];
+    }
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      y[i] = fmaf(d[b], t[i], y[i]);
+      y[i] = fmaf(c[b], xr[i][2 * s_idx + b], y[i]);
+    }
   }
 }
 

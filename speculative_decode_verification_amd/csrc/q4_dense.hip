@@ -52,9 +52,10 @@ struct DenseArgs {
 __host__ __device__ inline int dense_row_stride(int gwmax) { return gwmax * 64 + 8; }
 
 // One wave's region: (cap + 1) staged rows of the wave's K slice, then the
-// rows' group sums [kPassRows + 1][gwmax] (row k all zero).
-__host__ __device__ inline size_t dense_region_bytes(int cap, int gwmax) {
-  return ((size_t)(cap + 1) * dense_row_stride(gwmax) * 2 + (size_t)(kPassRows + 1) * gwmax * 4 + 15) &
+// rows' activation sums [kPassRows + 1][gwmax][spg] (row k all zero; spg = 1
+// sum per group for Q4, 2 per group (one per 32-element block) for Q8_0).
+__host__ __device__ inline size_t dense_region_bytes(int cap, int gwmax, int spg) {
+  return ((size_t)(cap + 1) * dense_row_stride(gwmax) * 2 + (size_t)(kPassRows + 1) * gwmax * spg * 4 + 15) &
          ~(size_t)15;
 }
 
@@ -72,13 +73,19 @@ __device__ __forceinline__ float block8(const uint4 v, uint4& packed) {
   return acc;
 }
 
-// Pairwise total of a group's 8 block sums.
-__device__ __forceinline__ float group_total(const float (&b)[8]) {
-  return ((b[0] + b[1]) + (b[2] + b[3])) + ((b[4] + b[5]) + (b[6] + b[7]));
+// Pairwise totals of a group's 8 block sums: the first four (elements
+// 0-31), the last four, and the whole group.
+__device__ __forceinline__ float half_total(const float (&b)[8], int h) {
+  return (b[4 * h] + b[4 * h + 1]) + (b[4 * h + 2] + b[4 * h + 3]);
 }
+__device__ __forceinline__ float group_total(const float (&b)[8]) { return half_total(b, 0) + half_total(b, 1); }
 
-template <int MODE, int ACT, int PF>
+// FMT = SDV_FMT_Q8_0: two 1 KB code chunks per group step, activation sums
+// per 32-element block, and the Q8_0 group step.
+template <int FMT, int MODE, int ACT, int PF>
 __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
+  constexpr bool Q8 = FMT == SDV_FMT_Q8_0;
+  constexpr int SPG = Q8 ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,11 +118,16 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
 
   // ---- the wave's weight blocks: step s reads block (t, gb + min(s, gw - 1))
   const size_t blk0 = (size_t)t * G + gb;
-  uint4 cbuf[PF];
+  uint4 cbuf[PF], cbuf2[Q8 ? PF : 1];
   uint32_t sbuf[PF];
   auto issue = [&](int slot, int s) {
     const size_t blk = blk0 + min(s, gw - 1);
-    cbuf[slot] = load_nt(a.codes + blk * 64 + lane);  // weights: read once per call
+    if constexpr (Q8) {
+      cbuf[slot] = load_nt(a.codes + blk * 128 + lane);  // weights: read once per call
+      cbuf2[slot] = load_nt(a.codes + blk * 128 + 64 + lane);
+    } else {
+      cbuf[slot] = load_nt(a.codes + blk * 64 + lane);
+    }
     sbuf[slot] = load_nt(a.sb + blk * 32 + col);
   };
 #pragma unroll
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
 
   // ---- staging into the wave's own region (no workgroup barrier)
   for (int tq = lane; tq < rs / 2; tq += 64) reinterpret_cast<uint32_t*>(xs + (size_t)a.cap * rs)[tq] = 0u;
-  for (int tq = lane; tq < gw; tq += 64) xsum[k * gw + tq] = 0.0f;
+  for (int tq = lane; tq < gw * SPG; tq += 64) xsum[k * gw * SPG + tq] = 0.0f;
   auto put_bf16 = [&](int task, const uint4 (&v)[8]) {
     const int i = task / gw, g = task - i * gw;
     float bsum[8];
@@ -133,7 +145,12 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
       bsum[q] = block8(v[q], pk);
       *reinterpret_cast<uint4*>(xs + (size_t)i * rs + g * 64 + q * 8) = pk;
     }
-    xsum[i * gw + g] = group_total(bsum);
+    if constexpr (Q8) {
+      xsum[(i * gw + g) * 2] = half_total(bsum, 0);
+      xsum[(i * gw + g) * 2 + 1] = half_total(bsum, 1);
+    } else {
+      xsum[i * gw + g] = group_total(bsum);
+    }
   };
   // fp32 task: 64 values in two halves of 8 loads; each 8-value block is split
   // into three bf16 parts (hi, mid, lo), each part row summed as bf16 rows are,
@@ -173,7 +190,13 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
 #pragma unroll
       for (int p = 0; p < 3; ++p) bs[p][blk] = acc[p];
     }
-    xsum[i * gw + g] = (group_total(bs[0]) + group_total(bs[1])) + group_total(bs[2]);
+    if constexpr (Q8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        xsum[(i * gw + g) * 2 + h] = (half_total(bs[0], h) + half_total(bs[1], h)) + half_total(bs[2], h);
+    } else {
+      xsum[i * gw + g] = (group_total(bs[0]) + group_total(bs[1])) + group_total(bs[2]);
+    }
   };
   for (int task = lane; task < ntask; task += 64) {
     if (task != lane) {
@@ -198,12 +221,13 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   // ---- the wave's group steps: five accumulators per lane, y[i] for row
   // 4 half + i (i < 4) and y[4] for row 8 (in half 0)
   const int slot = slot_of_arow<ACT>(col, k);
-  const uint16_t* ap = xs + (size_t)(slot >= 0 ? slot : a.cap) * rs + half * 32;
+  // a lane half reads elements 32 h .. of a Q4 group, 8 h .. (every 16) of a Q8_0 group
+  const uint16_t* ap = xs + (size_t)(slot >= 0 ? slot : a.cap) * rs + half * (Q8 ? 8 : 32);
   const float* xr[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const int r = i < 4 ? 4 * half + i : 8;
-    xr[i] = xsum + (r < k ? r : k) * gw;
+    xr[i] = xsum + (r < k ? r : k) * gw * SPG;
   }
   const DecodeK dk = decode_k();
   float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -213,7 +237,11 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int s = r * PF + i;
-      group_mac_rows<ACT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+      if constexpr (Q8) {
+        group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + s * 64, xr, s, y);
+      } else {
+        group_mac_rows<ACT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+      }
       issue(i, s + PF);
     }
   }
@@ -222,7 +250,13 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int s = s0 + i;
-      if (s < gw) group_mac_rows<ACT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+      if (s < gw) {
+        if constexpr (Q8) {
+          group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + s * 64, xr, s, y);
+        } else {
+          group_mac_rows<ACT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+        }
+      }
     }
   }
 
@@ -257,9 +291,9 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   }
 }
 
-template <int MODE, int ACT, int PF>
+template <int FMT, int MODE, int ACT, int PF>
 hipError_t dense_launch_one(const DenseArgs& a, size_t lds, hipStream_t st) {
-  void (*kern)(DenseArgs) = q4_dense_k_kernel<MODE, ACT, PF>;
+  void (*kern)(DenseArgs) = q4_dense_k_kernel<FMT, MODE, ACT, PF>;
   static std::atomic<size_t> lds_limit{65536};
   size_t cur = lds_limit.load(std::memory_order_relaxed);
   if (lds > cur) {
@@ -273,17 +307,21 @@ hipError_t dense_launch_one(const DenseArgs& a, size_t lds, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int MODE, int ACT>
+template <int FMT, int MODE, int ACT>
 hipError_t dense_launch_pf(const DenseArgs& a, size_t lds, hipStream_t st) {
   // ring depth: the wave's whole range when it is short, else 8 with refills
-  // (fp32 rows: 2, since staging the parts takes the registers)
+  // (fp32 rows: 2, since staging the parts takes the registers; Q8_0 blocks
+  // take two chunks, so at most 4)
   if constexpr (ACT == SDV_ACT_F32) {
-    return dense_launch_one<MODE, ACT, 2>(a, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 2>(a, lds, st);
+  } else if constexpr (FMT == SDV_FMT_Q8_0) {
+    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 4>(a, lds, st);
   } else {
-    if (a.gwmax <= 2) return dense_launch_one<MODE, ACT, 2>(a, lds, st);
-    if (a.gwmax <= 4) return dense_launch_one<MODE, ACT, 4>(a, lds, st);
-    if (a.gwmax <= 5) return dense_launch_one<MODE, ACT, 5>(a, lds, st);
-    return dense_launch_one<MODE, ACT, 8>(a, lds, st);
+    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, lds, st);
+    if (a.gwmax <= 4) return dense_launch_one<FMT, MODE, ACT, 4>(a, lds, st);
+    if (a.gwmax <= 5) return dense_launch_one<FMT, MODE, ACT, 5>(a, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 8>(a, lds, st);
   }
 }
 
@@ -296,12 +334,12 @@ int dense_waves_for(int K) {
   return G < kDenseMaxWaves ? (G > 0 ? G : 1) : kDenseMaxWaves;
 }
 
-size_t dense_lds_bytes(int K, int act_dtype, int k) {
+size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt) {
   if (k > kPassRows) k = kPassRows;  // one launch per pass
   const int G = K / 64, nw = dense_waves_for(K);
   const int gwmax = (G + nw - 1) / nw;
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
-  const size_t regions = (size_t)nw * dense_region_bytes(cap, gwmax);
+  const size_t regions = (size_t)nw * dense_region_bytes(cap, gwmax, fmt == SDV_FMT_Q8_0 ? 2 : 1);
   const size_t red = dense_red_bytes(nw);
   return regions > red ? regions : red;
 }
@@ -324,14 +362,18 @@ hipError_t dense_launch_pass(const sdv_q4t& W, int mode, const void* act, int ac
   a.nw = dense_waves_for(W.K);
   a.gwmax = (a.G + a.nw - 1) / a.nw;
   a.cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
-  a.region = (int)dense_region_bytes(a.cap, a.gwmax);
-  const size_t lds = dense_lds_bytes(W.K, act_dtype, k);
-#define SDV_DENSE(M, A) \
-  if (mode == M && act_dtype == A) return dense_launch_pf<M, A>(a, lds, st);
-  SDV_DENSE(SDV_MODE_PLAIN, SDV_ACT_BF16)
-  SDV_DENSE(SDV_MODE_PLAIN, SDV_ACT_F32)
-  SDV_DENSE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
-  SDV_DENSE(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+  a.region = (int)dense_region_bytes(a.cap, a.gwmax, W.format == SDV_FMT_Q8_0 ? 2 : 1);
+  const size_t lds = dense_lds_bytes(W.K, act_dtype, k, W.format);
+#define SDV_DENSE(F, M, A) \
+  if (W.format == F && mode == M && act_dtype == A) return dense_launch_pf<F, M, A>(a, lds, st);
+  SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_BF16)
+  SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_F32)
+  SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+  SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+  SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_PLAIN, SDV_ACT_BF16)
+  SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_PLAIN, SDV_ACT_F32)
+  SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+  SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
 #undef SDV_DENSE
   return hipErrorInvalidValue;
 }

@@ -64,11 +64,9 @@ namespace {
 using namespace q4;
 
 constexpr int kTileCols = 32;
-constexpr int kMaxWaves = 8;
 constexpr int kGatherWaves = 8;
 constexpr int kGatherTilesPerWave = 1;  // tiles one wave streams back to back
 constexpr int kPF = 8;        // groups in flight per lane (gathered units)
-constexpr int kPFDense = 10;  // split-K waves: K = 5120 gives each of 8 waves 10 groups, all issued at once
 
 struct Q4Args {
   const uint4* codes;    // tiled: [E][T][G][64] uint4
@@ -94,14 +92,18 @@ struct Q4Args {
   int tiles_per_block;
 };
 
-template <int MODE, int ACT, bool GATHER, bool KSPLIT, int PF>
+// FMT: SDV_FMT_AFFINE_Q4 or SDV_FMT_Q8_0 (two 1 KB code halves per group
+// step, activation sums per 32-element block).
+template <int FMT, int MODE, int ACT, int PF>
 __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* smem, int* s_src, int* s_dst) {
+  constexpr bool Q8 = FMT == SDV_FMT_Q8_0;
+  constexpr int SPG = Q8 ? 2 : 1;  // activation sums per group
   const int K = a.K;
   const int G = K >> 6;
   const int rs = K + 8;  // LDS row stride in bf16 (16-byte pad against bank conflicts)
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* xsum = reinterpret_cast<float*>(smem + (size_t)(a.slot_cap + 1) * rs * 2);  // [32][G]
-  float* red = xsum + 32 * G;  // split-K: [nw][32][33]; gathered: per-wave tile outputs
+  float* xsum = reinterpret_cast<float*>(smem + (size_t)(a.slot_cap + 1) * rs * 2);  // [32][G * SPG]
+  float* red = xsum + 32 * G * SPG;  // per-wave tile outputs
 
   const int tid = threadIdx.x;
   const int nw = blockDim.x >> 6;
@@ -119,8 +121,8 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   const uint32_t* sbp = a.sb;
   const void* act = a.act;
   float* out = a.out;
-  bool pairs = GATHER;  // rows come from the pair lists
-  if (GATHER) {
+  bool pairs = true;  // rows come from the pair lists
+  {
     const int u = blockIdx.y, pass0 = blockIdx.z * kPassRows;
     if (u == a.k * a.topk) {
       // the shared expert: all k rows, its own weight, input and output
@@ -149,35 +151,30 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
     }
   }
 
-  // ---- this wave's tiles and K range, and its load stream
-  int t_first, t_step, t_count, gb, ge;
-  if (KSPLIT) {
-    t_first = blockIdx.x;
-    t_step = 1;
-    t_count = 1;
-    gb = (G * wave) / nw;
-    ge = (G * (wave + 1)) / nw;
-  } else {
-    const int tb0 = blockIdx.x * a.tiles_per_block;
-    const int tb1 = min(tb0 + a.tiles_per_block, a.T);
-    t_first = tb0 + wave;
-    t_step = nw;
-    t_count = t_first < tb1 ? (tb1 - t_first + nw - 1) / nw : 0;
-    gb = 0;
-    ge = G;
-  }
+  // ---- this wave's tiles (all groups of each), and its load stream
+  const int tb0 = blockIdx.x * a.tiles_per_block;
+  const int tb1 = min(tb0 + a.tiles_per_block, a.T);
+  const int t_first = tb0 + wave, t_step = nw;
+  const int t_count = t_first < tb1 ? (tb1 - t_first + nw - 1) / nw : 0;
+  const int gb = 0, ge = G;
   const int gn = ge - gb;
   const int total = __builtin_amdgcn_readfirstlane(t_count * gn);
 
   // (tile, group) steps in order; block (t, g) of expert e starts at
-  // ((e * T + t) * G + g) in units of 64 uint4 (codes) or 32 words (sb)
+  // ((e * T + t) * G + g) in units of 64 uint4 (Q4 codes), 128 uint4 (Q8_0
+  // codes) or 32 words (sb)
   size_t ld_blk = ((size_t)e * a.T + t_first) * G + gb;
   int ld_g = gb;
   const size_t tile_jump = (size_t)t_step * G - gn;  // from the end of one tile's range to the next
-  uint4 cbuf[PF];
+  uint4 cbuf[PF], cbuf2[Q8 ? PF : 1];
   uint32_t sbuf[PF];
   auto issue = [&](int slot) {
-    cbuf[slot] = load_nt(codes + ld_blk * 64 + lane);  // weights: read once per call
+    if constexpr (Q8) {
+      cbuf[slot] = load_nt(codes + ld_blk * 128 + lane);  // weights: read once per call
+      cbuf2[slot] = load_nt(codes + ld_blk * 128 + 64 + lane);
+    } else {
+      cbuf[slot] = load_nt(codes + ld_blk * 64 + lane);
+    }
     sbuf[slot] = load_nt(sbp + ld_blk * 32 + col);
     ++ld_blk;
     if (++ld_g == ge) {
@@ -207,7 +204,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
     s_dst[tid] = dst;
   }
   __syncthreads();
-  stage_rows<ACT>(act, a.K, a.slot_cap, nrows, xs, xsum, rs, s_src);
+  stage_rows<ACT, FMT>(act, a.K, a.slot_cap, nrows, xs, xsum, rs, s_src);
   __syncthreads();
   // The first ring loads were issued before staging and have had the staging
   // time to land; wait for them here so the stream loop is entered with no
@@ -217,13 +214,14 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
   const int max_vrow = (ACT == SDV_ACT_F32) ? (nrows == 9 ? 27 : 16 + nrows) : nrows;
   const int nquads = (max_vrow + 7) >> 3;
   const int slot = slot_of_arow<ACT>(col, nrows);
-  // rows without data read the zero row (LDS row slot_cap)
-  const uint16_t* arow_ptr = xs + (size_t)(slot >= 0 ? slot : a.slot_cap) * rs + half * 32;
+  // rows without data read the zero row (LDS row slot_cap); a lane half
+  // reads elements 32 h .. of a Q4 group, 8 h .. (every 16) of a Q8_0 group
+  const uint16_t* arow_ptr = xs + (size_t)(slot >= 0 ? slot : a.slot_cap) * rs + half * (Q8 ? 8 : 32);
 
   float yacc[16];
   const DecodeK dk = decode_k();
   int cur_g = gb, cur_tl = 0;
-  const int tiles_per_wave = KSPLIT ? 1 : (a.tiles_per_block + nw - 1) / nw;
+  const int tiles_per_wave = (a.tiles_per_block + nw - 1) / nw;
   // One (tile, group) step: consume ring slot i, refill it (if asked) after
   // the slot's data has been decoded, and finish the tile after its last group.
   auto step = [&](int i, bool refill) {
@@ -231,10 +229,14 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
 #pragma unroll
       for (int v = 0; v < 16; ++v) yacc[v] = 0.0f;
     }
-    group_mac(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc, dk);
+    if constexpr (Q8) {
+      group_mac_q8(cbuf[i], cbuf2[i], sbuf[i], arow_ptr + cur_g * 64, xsum + 2 * cur_g, 2 * G, half, nquads, yacc);
+    } else {
+      group_mac(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc, dk);
+    }
     if (refill) issue(i);
     if (++cur_g == ge) {
-      if (!KSPLIT) {
+      {
         // finished tile values go to this wave's LDS area; the global stores
         // happen after the stream loop
         float* o = red + ((size_t)wave * tiles_per_wave + cur_tl) * kPassRows * 32;
@@ -269,7 +271,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
       if (st0 + i < total) step(i, st0 + i + PF < total);
   }
 
-  if (!KSPLIT) {
+  {
     __syncthreads();
     const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
     const float* o = red + (size_t)wave * tiles_per_wave * kPassRows * 32;
@@ -283,70 +285,22 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
         }
       }
     }
-    return;
   }
-
-  // ---- split-K: cross-wave reduction in wave order, then the epilogue
-  float* myred = red + (size_t)wave * 32 * 33;
-  if (total == 0) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) yacc[v] = 0.0f;
-  }
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int vr = 8 * (v >> 2) + 4 * half + (v & 3);
-    myred[vr * 33 + col] = yacc[v];
-  }
-  __syncthreads();
-  const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
-  for (int t = tid; t < nrows * cols_out; t += blockDim.x) {
-    const int i = t / cols_out, cc = t - i * cols_out;
-    float val[2];
-    const int ncol = (MODE == SDV_MODE_PLAIN) ? 1 : 2;
-    for (int h2 = 0; h2 < ncol; ++h2) {
-      const int cidx = cc + 16 * h2;
-      float part[3];
-      const int np = (ACT == SDV_ACT_F32) ? 3 : 1;
-      for (int p = 0; p < np; ++p) {
-        const int vr = vrow_of<ACT>(i, p);
-        float sum = 0.0f;
-        for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * 32 + vr) * 33 + cidx];
-        part[p] = sum;
-      }
-      val[h2] = (np == 3) ? (part[0] + part[1]) + part[2] : part[0];
-    }
-    const int orow = s_dst[i];
-    if (orow < 0) continue;
-    if (MODE == SDV_MODE_PLAIN) {
-      const int on = blockIdx.x * kTileCols + cc;
-      if (on < a.N) out[(size_t)orow * a.n_out + on] = val[0];
-    } else {
-      const int on = blockIdx.x * 16 + cc;
-      if (on < a.n_out) out[(size_t)orow * a.n_out + on] = siluf_(val[0]) * val[1];
-    }
-  }
-}
-
-// Split-K (dense): up to 8 waves per workgroup.
-template <int MODE, int ACT>
-__global__ __launch_bounds__(512, 2) void q4_dense_kernel(Q4Args a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_src[kPassRows], s_dst[kPassRows];
-  q4_matvec_body<MODE, ACT, false, true, kPFDense>(a, smem, s_src, s_dst);
 }
 
 // Gathered units: 8 waves per workgroup (one weight tile each), at most 128
 // VGPRs so 4 waves fit per SIMD.
-template <int MODE, int ACT>
+// (Q8_0: a ring of 4 two-chunk blocks keeps the same register budget.)
+template <int FMT, int MODE, int ACT>
 __global__ __launch_bounds__(512, 4) void q4_gather_kernel(Q4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_src[kPassRows], s_dst[kPassRows];
-  q4_matvec_body<MODE, ACT, true, false, kPF>(a, smem, s_src, s_dst);
+  q4_matvec_body<FMT, MODE, ACT, FMT == SDV_FMT_Q8_0 ? kPF / 2 : kPF>(a, smem, s_src, s_dst);
 }
 
-template <int MODE, int ACT, bool GATHER>
+template <int FMT, int MODE, int ACT>
 hipError_t launch_one(const Q4Args& a, int blocks_x, int units, int nw, size_t lds, hipStream_t st) {
-  void (*kern)(Q4Args) = GATHER ? q4_gather_kernel<MODE, ACT> : q4_dense_kernel<MODE, ACT>;
+  void (*kern)(Q4Args) = q4_gather_kernel<FMT, MODE, ACT>;
   // raise the kernel's dynamic LDS limit once per process (the largest size
   // asked for so far; the attribute is per function, not per device)
   static std::atomic<size_t> lds_limit{65536};
@@ -424,7 +378,74 @@ __global__ __launch_bounds__(256) void q4_repack_kernel(RepackArgs r) {
   }
 }
 
+// ---- repack: row-major Q8_0 -> tiled layout --------------------------------
+
+struct Q8RepackArgs {
+  const int8_t* qs;   // [E][N][K]
+  const uint16_t* d;  // [E][N][K/32]
+  int E, N, K, T, fused;
+  uint4* tcodes;      // [E][T][G][2][64]
+  uint32_t* tsb;      // [E][T][G][32]
+};
+
+__global__ __launch_bounds__(256) void q8_0_repack_kernel(Q8RepackArgs r) {
+  const int G = r.K >> 6;
+  const size_t nblk = (size_t)r.E * r.T * G;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const RepackArgs rows{nullptr, nullptr, nullptr, r.E, r.N, r.K, r.T, r.fused, nullptr, nullptr};
+  // codes: one thread per 16-byte chunk (half p, lane l = 32 h + c): the
+  // bytes of elements 32p + 8h + 0..7 and 32p + 16 + 8h + 0..7, as u = q + 128
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * 128; idx += stride) {
+    const int lane = (int)(idx & 63), p = (int)((idx >> 6) & 1);
+    const size_t blk = idx >> 7;
+    const int g = (int)(blk % G);
+    const size_t et = blk / G;
+    const int t = (int)(et % r.T);
+    const int e = (int)(et / r.T);
+    const int n = repack_row(rows, t, lane & 31);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n >= 0) {
+      const int8_t* src = r.qs + ((size_t)e * r.N + n) * r.K + (size_t)g * 64 + 32 * p + 8 * (lane >> 5);
+      const uint2 a = *reinterpret_cast<const uint2*>(src);
+      const uint2 b = *reinterpret_cast<const uint2*>(src + 16);
+      v = make_uint4(a.x ^ 0x80808080u, a.y ^ 0x80808080u, b.x ^ 0x80808080u, b.y ^ 0x80808080u);
+    }
+    r.tcodes[idx] = v;
+  }
+  // the two blocks' half scales: one thread per (block, column)
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * 32; idx += stride) {
+    const int c = (int)(idx & 31);
+    const size_t blk = idx >> 5;
+    const int g = (int)(blk % G);
+    const size_t et = blk / G;
+    const int t = (int)(et % r.T);
+    const int e = (int)(et / r.T);
+    const int n = repack_row(rows, t, c);
+    uint32_t w = 0;
+    if (n >= 0) {
+      const size_t o = ((size_t)e * r.N + n) * (2 * G) + 2 * g;
+      w = (uint32_t)r.d[o] | ((uint32_t)r.d[o + 1] << 16);
+    }
+    r.tsb[idx] = w;
+  }
+}
+
 }  // namespace
+
+int q4_tiles(int N, int fused);
+
+size_t q8_0t_codes_bytes(int E, int N, int K, int fused) {
+  return (size_t)E * q4_tiles(N, fused) * (K / 64) * 2048;
+}
+
+hipError_t q8_0_repack_launch(const sdv_q8_0& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st) {
+  Q8RepackArgs r{src.qs, src.d, src.E, src.N, src.K, q4_tiles(src.N, fused), fused, static_cast<uint4*>(tcodes), tsb};
+  const size_t n = (size_t)src.E * r.T * (src.K / 64) * 128;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(q8_0_repack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, r);
+  return hipGetLastError();
+}
 
 // Tiles of a weight: 32 rows each, or 16 gate + 16 up rows when fused.
 int q4_tiles(int N, int fused) { return fused ? (N / 2 + 15) / 16 : (N + kTileCols - 1) / kTileCols; }
@@ -445,32 +466,18 @@ hipError_t q4_repack_launch(const sdv_q4& src, int fused, void* tcodes, uint32_t
   return hipGetLastError();
 }
 
-// Waves per workgroup for a split-K (dense) product: a function of K only, so
-// the summation order never depends on the row count.
-int q4_waves_for(int K) {
-  const int G = K / 64;
-  int nw = G / 5;
-  if (nw < 1) nw = 1;
-  if (nw > kMaxWaves) nw = kMaxWaves;
-  return nw;
-}
-
-size_t q4_lds_bytes(int K, int slot_cap, int nw) {
-  const int G = K / 64;
-  return (size_t)(slot_cap + 1) * (K + 8) * 2 + (size_t)32 * G * 4 + (size_t)nw * 32 * 33 * 4;
-}
-
-size_t dense_lds_bytes(int K, int act_dtype, int k);
+size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt);
 hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
                         hipStream_t st);
 
-size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather) {
+size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather, int fmt) {
   if (k > kPassRows) k = kPassRows;  // rows are staged one pass at a time
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
+  const int spg = fmt == SDV_FMT_Q8_0 ? 2 : 1;  // activation sums per group
   // gathered: per-wave output staging for one tile of up to 9 rows x 32 columns
-  return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * 4 +
+  return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * spg * 4 +
                       (size_t)kGatherWaves * kGatherTilesPerWave * kPassRows * 32 * 4
-                : dense_lds_bytes(K, act_dtype, k);
+                : dense_lds_bytes(K, act_dtype, k, fmt);
 }
 
 hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, bool gather,
@@ -505,13 +512,17 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
     a.tiles_per_block = nw * kGatherTilesPerWave;
     const int bx = (a.T + a.tiles_per_block - 1) / a.tiles_per_block;
     const int units = k * topk + (shared ? 1 : 0);
-    const size_t lds = q4_lds_bytes_for(W.K, act_dtype, k, true);
-#define SDV_Q4_G(M, A) \
-  if (mode == M && act_dtype == A) return launch_one<M, A, true>(a, bx, units, nw, lds, st);
-    SDV_Q4_G(SDV_MODE_PLAIN, SDV_ACT_BF16)
-    SDV_Q4_G(SDV_MODE_PLAIN, SDV_ACT_F32)
-    SDV_Q4_G(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
-    SDV_Q4_G(SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+    const size_t lds = q4_lds_bytes_for(W.K, act_dtype, k, true, W.format);
+#define SDV_Q4_G(F, M, A) \
+  if (W.format == F && mode == M && act_dtype == A) return launch_one<F, M, A>(a, bx, units, nw, lds, st);
+    SDV_Q4_G(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_F32)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q4, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q4, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+    SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_PLAIN, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_PLAIN, SDV_ACT_F32)
+    SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
 #undef SDV_Q4_G
   } else {
     return dense_launch(W, mode, act, act_dtype, k, out, st);

@@ -11,10 +11,11 @@ from collections import namedtuple
 
 import torch
 
-from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, GATE_SIGMOID, GATE_SILU, MODE_GATEUP_SWIGLU,
-                   MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ4, SdvQ4T, check, lib)
+from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, FMT_AFFINE_Q4, FMT_Q8_0, GATE_SIGMOID, GATE_SILU,
+                   MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ4, SdvQ4T, SdvQ8_0,
+                   check, lib)
 
-__all__ = ["Q4Weight", "TiledQ4", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
+__all__ = ["Q4Weight", "Q8Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
            "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_gated_norm_k",
            "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
@@ -76,26 +77,58 @@ class Q4Weight:
         return TiledQ4.from_rowmajor(self, fused_gateup)
 
 
-class TiledQ4:
-    """Affine-Q4/g64 weights in the tiled layout of ``sdv_q4t`` (device
-    tensors ``codes`` uint8 and ``sb`` int32)."""
+class Q8Weight:
+    """Q8_0 weights on the device in the GGUF interchange form: codes int8
+    [E, N, K], half scales int16 (binary16 bits) [E, N, K/32].  A 2-D layout
+    [N, K] is a dense matrix (E = 1)."""
 
-    def __init__(self, codes, sb, E, N, K, fused_gateup):
-        self.E, self.N, self.K, self.fused = E, N, K, bool(fused_gateup)
+    def __init__(self, qs, d):
+        if qs.dim() == 2:
+            qs, d = qs[None], d[None]
+        if qs.dim() != 3 or d.dim() != 3:
+            raise ValueError("qs [E,N,K], d [E,N,K/32] expected")
+        self.E, self.N, self.K = qs.shape
+        if d.shape != (self.E, self.N, self.K // 32):
+            raise ValueError(f"d shape {tuple(d.shape)} does not match qs {tuple(qs.shape)}")
+        self.qs, self.d = qs, d
+        self.device = qs.device
+        self._desc = SdvQ8_0(_need(qs, "qs", torch.int8).value, _need(d, "d", torch.int16, device=self.device).value,
+                             self.E, self.N, self.K)
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def nbytes(self):
+        return self.E * self.N * (self.K + (self.K // 32) * 2)
+
+    def tiled(self, fused_gateup=False):
+        """The weight rewritten on the device into the tiled Q8_0 layout
+        (sdv_q8_0_repack)."""
+        return TiledQ4.from_rowmajor(self, fused_gateup)
+
+
+class TiledQ4:
+    """A tiled weight of ``sdv_q4t`` (device tensors ``codes`` uint8 and ``sb``
+    int32): affine Q4/g64 (``fmt`` FMT_AFFINE_Q4) or Q8_0 (FMT_Q8_0)."""
+
+    def __init__(self, codes, sb, E, N, K, fused_gateup, fmt=FMT_AFFINE_Q4):
+        self.E, self.N, self.K, self.fused, self.fmt = E, N, K, bool(fused_gateup), fmt
         L = lib()
-        need_c = L.sdv_q4t_codes_bytes(E, N, K, int(self.fused))
+        need_c = (L.sdv_q8_0t_codes_bytes if fmt == FMT_Q8_0 else L.sdv_q4t_codes_bytes)(E, N, K, int(self.fused))
         need_s = L.sdv_q4t_sb_bytes(E, N, K, int(self.fused))
         if codes.numel() * codes.element_size() < need_c or sb.numel() * 4 < need_s:
             raise ValueError("tiled buffers are smaller than the layout needs")
         self.codes, self.sb = codes, sb
         self.device = codes.device
         self._desc = SdvQ4T(_need(codes, "codes", codes.dtype).value,
-                            _need(sb, "sb", torch.int32, device=self.device).value, E, N, K, 64, int(self.fused))
+                            _need(sb, "sb", torch.int32, device=self.device).value, E, N, K, 64, int(self.fused),
+                            int(fmt))
 
     @staticmethod
-    def empty(E, N, K, fused_gateup, device):
+    def empty(E, N, K, fused_gateup, device, fmt=FMT_AFFINE_Q4):
         L = lib()
-        nc = L.sdv_q4t_codes_bytes(E, N, K, int(bool(fused_gateup)))
+        nc = (L.sdv_q8_0t_codes_bytes if fmt == FMT_Q8_0 else L.sdv_q4t_codes_bytes)(E, N, K, int(bool(fused_gateup)))
         ns = L.sdv_q4t_sb_bytes(E, N, K, int(bool(fused_gateup)))
         codes = torch.empty((nc,), dtype=torch.uint8, device=device)
         sb = torch.empty((ns // 4,), dtype=torch.int32, device=device)
@@ -103,10 +136,12 @@ class TiledQ4:
 
     @classmethod
     def from_rowmajor(cls, W, fused_gateup=False, out=None):
-        codes, sb = out if out is not None else cls.empty(W.E, W.N, W.K, fused_gateup, W.device)
-        check(lib().sdv_q4_repack(W.desc, int(bool(fused_gateup)), _need(codes, "codes_out", codes.dtype),
-                                  _need(sb, "sb_out", torch.int32), _stream(codes)))
-        return cls(codes, sb, W.E, W.N, W.K, fused_gateup)
+        fmt = FMT_Q8_0 if isinstance(W, Q8Weight) else FMT_AFFINE_Q4
+        codes, sb = out if out is not None else cls.empty(W.E, W.N, W.K, fused_gateup, W.device, fmt)
+        repack = lib().sdv_q8_0_repack if fmt == FMT_Q8_0 else lib().sdv_q4_repack
+        check(repack(W.desc, int(bool(fused_gateup)), _need(codes, "codes_out", codes.dtype),
+                     _need(sb, "sb_out", torch.int32), _stream(codes)))
+        return cls(codes, sb, W.E, W.N, W.K, fused_gateup, fmt)
 
     @property
     def desc(self):

@@ -22,13 +22,20 @@ from ._lib import MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX
 
 class MoeLayer:
     def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None,
-                 fuse_shared=True, fused_experts=True):
+                 fuse_shared=True, fused_experts=None):
+        """fused_experts: the one-launch expert kernel (affine Q4 weights);
+        None picks it for affine-Q4 weights and the two gathered launches
+        otherwise (Q8_0)."""
         self.gate_up, self.down = gate_up, down
+        weights = [w for w in (gate_up, down, shared_gate_up, shared_down) if w is not None]
+        if fused_experts is None:
+            fused_experts = all(w.fmt == ops.FMT_AFFINE_Q4 for w in weights)
         self.fused_experts = fused_experts
         self.shared_gate_up, self.shared_down = shared_gate_up, shared_down
         self.fused_shared = (fuse_shared and shared_gate_up is not None and
-                             (shared_gate_up.N, shared_gate_up.K) == (gate_up.N, gate_up.K) and
-                             (shared_down.N, shared_down.K) == (down.N, down.K))
+                             (shared_gate_up.N, shared_gate_up.K, shared_gate_up.fmt) ==
+                             (gate_up.N, gate_up.K, gate_up.fmt) and
+                             (shared_down.N, shared_down.K, shared_down.fmt) == (down.N, down.K, down.fmt))
         self.k, self.topk = k, topk
         self.score_mode, self.renorm = score_mode, renorm
         dev = gate_up.device

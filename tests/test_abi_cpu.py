@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 21
+    assert len(names) == 23
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,8 +52,8 @@ def q4(E=1, N=64, K=128, group=64, codes=P, scales=P + 0x100000, biases=P + 0x20
     return L.SdvQ4(codes, scales, biases, E, N, K, group)
 
 
-def q4t(E=1, N=64, K=128, group=64, codes=P, sb=P + 0x100000, fused=0):
-    return L.SdvQ4T(codes, sb, E, N, K, group, fused)
+def q4t(E=1, N=64, K=128, group=64, codes=P, sb=P + 0x100000, fused=0, fmt=0):
+    return L.SdvQ4T(codes, sb, E, N, K, group, fused, fmt)
 
 
 def qmv(lib, W, act=P + 0x400000, dtype=L.ACT_BF16, k=2, mode=L.MODE_PLAIN, y=P + 0x800000):
@@ -78,6 +78,33 @@ def test_repack_validation(lib):
     assert f(ctypes.byref(q4()), 0, 0, out_s, None) == L.SDV_EINVAL
     assert f(ctypes.byref(q4()), 0, P + 16, out_s, None) == L.SDV_EALIAS      # over the source codes
     assert f(ctypes.byref(q4()), 0, out_c, out_c + 64, None) == L.SDV_EALIAS  # outputs overlap
+
+
+def test_q8_0_sizes_and_repack_validation(lib):
+    # T tiles x G groups x (2 KB of codes, 128 B of half-scale words)
+    assert lib.sdv_q8_0t_codes_bytes(512, 1280, 2560, 1) == 512 * 40 * 40 * 2048
+    assert lib.sdv_q8_0t_codes_bytes(1, 1000, 576, 0) == 32 * 9 * 2048
+    assert lib.sdv_q8_0t_codes_bytes(1, 64, 96, 0) == 0                         # K not a multiple of 64
+    f = lib.sdv_q8_0_repack
+    src = lambda **kw: ctypes.byref(L.SdvQ8_0(kw.get("qs", P), kw.get("d", P + 0x100000), kw.get("E", 1),
+                                               kw.get("N", 64), kw.get("K", 128)))
+    out_c, out_s = P + 0x4000000, P + 0x8000000
+    assert f(None, 0, out_c, out_s, None) == L.SDV_EINVAL
+    assert f(src(K=96), 0, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(src(N=63), 1, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(src(E=0), 0, out_c, out_s, None) == L.SDV_EINVAL
+    assert f(src(qs=0), 0, out_c, out_s, None) == L.SDV_EINVAL
+    assert f(src(), 0, P + 64, out_s, None) == L.SDV_EALIAS                     # over the source codes
+    assert f(src(), 0, out_c, P + 0x100000 + 16, None) == L.SDV_EALIAS          # sb over the scales
+    assert f(src(), 0, out_c, out_c + 64, None) == L.SDV_EALIAS
+
+
+def test_format_validation(lib):
+    assert qmv(lib, q4t(fmt=2)) == L.SDV_ELAYOUT
+    assert "format" in lib.sdv_last_error().decode()
+    # a Q8_0 weight's codes are twice a Q4 weight's: an output right after
+    # the Q4-sized codes still overlaps them
+    assert qmv(lib, q4t(fmt=1), y=P + 64 * 128 // 2 + 64) == L.SDV_EALIAS
 
 
 def test_qmv_validation(lib):
@@ -211,6 +238,9 @@ def test_experts_validation(lib):
     wide = q4t(E=E, N=2 * I, K=16384, fused=1)
     assert experts(lib, wide, q4t(E=E, N=16384, K=I, codes=P + 0x200000, sb=P + 0x300000), k=9) == L.SDV_ELAYOUT
     assert "LDS" in lib.sdv_last_error().decode()
+    # the fused expert kernel takes affine Q4 only
+    assert experts(lib, q4t(E=E, N=2 * I, K=H, fused=1, fmt=1), dn) == L.SDV_ELAYOUT
+    assert "Q8_0" in lib.sdv_last_error().decode()
     gu9 = q4t(E=E, N=2 * 1088, K=H, fused=1)
     assert experts(lib, gu9, q4t(E=E, N=H, K=1088, codes=P + 0x2000000, sb=P + 0x3000000)) == L.SDV_ERANGE
 
