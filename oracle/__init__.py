@@ -30,6 +30,9 @@ definition written out.  Sources, by page and section:
   preparation (causal depthwise conv1d of kernel 4 over the q/k/v channels
   with a carried tail, per-head L2 norm of q and k, g from A_log and dt_bias
   by softplus and exp, beta = sigmoid(b)) and the gated RMSNorm output.
+* mere.run transfer report, "Shared architecture and implemented paths": the
+  gathered expert kernel's Flash-Next Q3 specialization (affine, group 64,
+  3-bit codes; the bit packing is our definition).
 * Red Lite dev45, "What it is": the MTP block's experts are Q8_0 (GGUF
   blocks of 32 signed 8-bit codes and one half-precision scale), decoded as
   the dense Q8_0 dequantizer does.
@@ -50,9 +53,9 @@ in the function's docstring.
 from .ref import (bf16_to_f64, unpack_q4, dequant, qmv, route, union_pairs, silu, swiglu,
                   combine, moe_verify, gdn_verify, rollback, sample_tokens, accept, verify_cycle,
                   softplus, gdn_prepare, gdn_gated_norm, CONV_TAPS, fp16_to_f64, dequant_q8_0,
-                  qmv_q8_0, Q8_BLOCK)
+                  qmv_q8_0, Q8_BLOCK, unpack_q3, dequant_q3, qmv_q3)
 
 __all__ = ["bf16_to_f64", "unpack_q4", "dequant", "qmv", "route", "union_pairs", "silu",
            "swiglu", "combine", "moe_verify", "gdn_verify", "rollback", "sample_tokens", "accept",
            "verify_cycle", "softplus", "gdn_prepare", "gdn_gated_norm", "CONV_TAPS", "fp16_to_f64",
-           "dequant_q8_0", "qmv_q8_0", "Q8_BLOCK"]
+           "dequant_q8_0", "qmv_q8_0", "Q8_BLOCK", "unpack_q3", "dequant_q3", "qmv_q3"]

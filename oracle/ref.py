@@ -72,6 +72,41 @@ def qmv(codes, scales, biases, x):
 # ---------------------------------------------------------------------------
 
 # ---------------------------------------------------------------------------
+# affine Q3 (mere.run transfer report, "Shared architecture and implemented
+# paths": the gathered expert kernel's Flash-Next Q3 specialization beside
+# affine Q4/g64).  Same affine form and group as Q4, 3-bit codes.
+# ---------------------------------------------------------------------------
+
+def unpack_q3(codes):
+    """Unsigned 3-bit codes from packed bytes ``[..., 3K/8]``: element c of a
+    row is bits ``[3c, 3c+3)`` of the row's little-endian bit stream (eight
+    codes in every three bytes).  The pages do not fix the packing; this is
+    our definition (pinned against an independently written packer)."""
+    b = np.asarray(codes, dtype=np.uint8)
+    nbytes = b.shape[-1]
+    n = nbytes * 8 // 3
+    bits = np.unpackbits(b, axis=-1, bitorder="little")            # [..., 8 * nbytes], bit i of the stream
+    trip = bits[..., :3 * n].reshape(*b.shape[:-1], n, 3).astype(np.uint8)
+    return (trip[..., 0] | (trip[..., 1] << 1) | (trip[..., 2] << 2)).astype(np.uint8)
+
+
+def dequant_q3(codes, scales, biases):
+    """Dense fp64 weights: ``W[n, c] = s[n, c // 64] * q[n, c] + b[n, c // 64]``
+    with 3-bit codes q (0..7).  Exact in fp64."""
+    q = unpack_q3(codes).astype(np.float64)
+    s = np.repeat(bf16_to_f64(scales), GROUP, axis=-1)
+    b = np.repeat(bf16_to_f64(biases), GROUP, axis=-1)
+    return s * q + b
+
+
+def qmv_q3(codes, scales, biases, x):
+    """Multi-row affine-Q3 matvec, each row on its own (as ``qmv``)."""
+    w = dequant_q3(codes, scales, biases)
+    x = np.asarray(x, dtype=np.float64)
+    return np.stack([w @ x[r] for r in range(x.shape[0])])
+
+
+# ---------------------------------------------------------------------------
 # Q8_0 (Red Lite dev45, "What it is": the MTP block's 512 experts are Q8_0 and
 # decode bit-identically to the dense Q8_0 dequantizer; mere.run transfer
 # report, "Shared architecture and implemented paths": the checkpoint's Q8

@@ -23,12 +23,12 @@ from .counter import (GAMMA, SEED, derive_key, mix64, rand64, bf16_bits_from_f32
 from . import configs
 from .inputs import (BankKeys, bank_keys, activations, dense_weight, moe_layer_inputs, gdn_layer_inputs,
                      gdn_state, accepted_prefix, integer_exact_weight, verify_block, gumbel_noise,
-                     gdn_raw_inputs, q8_0_weight)
+                     gdn_raw_inputs, q8_0_weight, q3_weight)
 
 __all__ = [
     "GAMMA", "SEED", "derive_key", "mix64", "rand64", "bf16_bits_from_f32",
     "q4_code_words", "q4_affine_bf16", "q4_rows", "configs", "BankKeys", "bank_keys", "activations",
     "dense_weight", "moe_layer_inputs", "gdn_layer_inputs", "gdn_state", "verify_block", "gumbel_noise",
-    "gdn_raw_inputs", "q8_0_weight",
+    "gdn_raw_inputs", "q8_0_weight", "q3_weight",
     "accepted_prefix", "integer_exact_weight",
 ]

@@ -28,7 +28,7 @@ DENSE_W, GATEUP, DOWN, SHARED_GATEUP, SHARED_DOWN = 0, 1, 2, 3, 4
 T_X, T_LOGITS, T_Z, T_S, T_Q, T_K, T_V, T_G, T_BETA, T_J = 10, 11, 12, 20, 21, 22, 23, 24, 25, 30
 T_VLOGITS, T_GUMBEL, T_DRAFTS = 40, 41, 42
 T_QKV, T_HIST, T_CONVW, T_A, T_B, T_ALOG, T_DTB, T_GATEZ, T_NORMW = 50, 51, 52, 53, 54, 55, 56, 57, 58
-T_Q8 = 60
+T_Q8, T_Q3 = 60, 61
 
 
 def bank_keys(cfg_id, kind, layer):
@@ -87,6 +87,21 @@ def gdn_layer_inputs(cfg_id, layer, rows, hv, hk, dk, dv, step=0):
 def accepted_prefix(cfg_id, step, rows):
     """Accepted-prefix length j ~ U{0..rows} for one verify step."""
     return int(_rng(cfg_id, T_J, step).integers(0, rows + 1))
+
+
+def q3_weight(cfg_id, kind, layer, E, N, K):
+    """An affine-Q3/g64 weight in its interchange form: codes uint8
+    [E, N, 3K/8] (a little-endian bit stream of 3-bit codes ~ U{0..7}),
+    scales ~ U(0.01, 0.04) and biases ~ U(-0.1, 0.1) as bf16 bits
+    [E, N, K/64].  Returns (codes, scales, biases, q) with q the codes
+    unpacked, for generators' own checks."""
+    rng = _rng(cfg_id, T_Q3, kind, layer)
+    q = rng.integers(0, 8, size=(E, N, K), dtype=np.int64)
+    bits = np.stack([(q >> i) & 1 for i in range(3)], axis=-1).reshape(E, N, 3 * K).astype(np.uint8)
+    codes = np.packbits(bits, axis=-1, bitorder="little")
+    sc = bf16_bits_from_f32(rng.uniform(0.01, 0.04, size=(E, N, K // 64)).astype(np.float32))
+    bi = bf16_bits_from_f32(rng.uniform(-0.1, 0.1, size=(E, N, K // 64)).astype(np.float32))
+    return codes, sc, bi, q.astype(np.uint8)
 
 
 def q8_0_weight(cfg_id, kind, layer, E, N, K):

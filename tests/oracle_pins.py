@@ -753,6 +753,62 @@ def check_q8_0_blocks(ref):
             assert Fraction(float(y[o])) == half_exact(d[o, c // 32]) * int(qs[o, c]), (c, o)
 
 
+def pack_q3_ints(q):
+    """Independent packer: codes of one row summed into a Python integer at
+    bit 3c, written out little-endian."""
+    v = 0
+    for c, code in enumerate(q):
+        v |= int(code) << (3 * c)
+    return np.frombuffer(v.to_bytes(3 * len(q) // 8, "little"), dtype=np.uint8)
+
+
+def check_q3_unpack_roundtrip(ref):
+    """Affine Q3: packed rows from the independent packer unpack to the codes,
+    and every byte boundary (codes straddling bytes) is covered."""
+    rng = np.random.default_rng(30)
+    for k in (8, 64, 192):
+        rows = rng.integers(0, 8, size=(3, k))
+        packed = np.stack([pack_q3_ints(r) for r in rows])
+        assert np.array_equal(ref.unpack_q3(packed), rows.astype(np.uint8)), k
+    # all eight codes in one three-byte triplet, in order
+    assert np.array_equal(ref.unpack_q3(pack_q3_ints(list(range(8)))[None])[0], np.arange(8))
+
+
+def check_q3_bruteforce(ref):
+    """Affine Q3 product: exact rational brute force (codes from the
+    independent packer)."""
+    rng = np.random.default_rng(31)
+    for (n, k, rows) in [(3, 64, 1), (4, 128, 2)]:
+        q = rng.integers(0, 8, size=(n, k))
+        codes = np.stack([pack_q3_ints(r) for r in q])
+        sc = synth.bf16_bits_from_f32(rng.uniform(0.01, 0.04, size=(n, k // 64)).astype(np.float32))
+        bi = synth.bf16_bits_from_f32(rng.uniform(-0.1, 0.1, size=(n, k // 64)).astype(np.float32))
+        xb = synth.bf16_bits_from_f32(rng.standard_normal((rows, k), dtype=np.float32))
+        y = ref.qmv_q3(codes, sc, bi, ref.bf16_to_f64(xb))
+        for r in range(rows):
+            ex = [sum((bf16_exact(sc[o, c // 64]) * int(q[o, c]) + bf16_exact(bi[o, c // 64])) * bf16_exact(xb[r, c])
+                      for c in range(k)) for o in range(n)]
+            scale = max(abs(float(v)) for v in ex)
+            for o in range(n):
+                assert abs(float(Fraction(float(y[r, o])) - ex[o])) <= 1e-13 * scale, (n, k, r, o)
+
+
+def check_q3_closed_form(ref):
+    """Constant 3-bit codes c give y = sum_g (s_g c + b_g) X_g."""
+    n, k = 3, 128
+    rng = np.random.default_rng(32)
+    for c in (0, 5, 7):
+        codes = np.stack([pack_q3_ints([c] * k) for _ in range(n)])
+        sc = synth.bf16_bits_from_f32(rng.uniform(0.01, 0.04, size=(n, 2)).astype(np.float32))
+        bi = synth.bf16_bits_from_f32(rng.uniform(-0.1, 0.1, size=(n, 2)).astype(np.float32))
+        xb = synth.bf16_bits_from_f32(rng.standard_normal((1, k), dtype=np.float32))
+        y = ref.qmv_q3(codes, sc, bi, ref.bf16_to_f64(xb))[0]
+        xs = [sum(bf16_exact(v) for v in xb[0, 64 * g:64 * (g + 1)]) for g in range(2)]
+        for o in range(n):
+            ex = sum((bf16_exact(sc[o, g]) * c + bf16_exact(bi[o, g])) * xs[g] for g in range(2))
+            assert abs(float(Fraction(float(y[o])) - ex)) <= 1e-13 * max(1.0, abs(float(ex))), (c, o)
+
+
 ALL_CHECKS = [
     check_bf16_decode, check_unpack_roundtrip, check_qmv_bruteforce, check_qmv_integer_exact,
     check_qmv_closed_forms, check_qmv_rows_independent, check_route_selection, check_route_weights,
@@ -762,5 +818,6 @@ ALL_CHECKS = [
     check_gdn_head_groups, check_gdn_rollback, check_sample_greedy, check_sample_noise_rounding,
     check_sample_gumbel_is_softmax, check_accept_cases, check_verify_cycle_rollback,
     check_conv_is_convolution, check_conv_alignment, check_conv_history_chain, check_qk_l2_norm, check_gates,
-    check_gated_norm, check_fp16_decode, check_q8_0_bruteforce, check_q8_0_blocks,
+    check_gated_norm, check_fp16_decode, check_q8_0_bruteforce, check_q8_0_blocks, check_q3_unpack_roundtrip,
+    check_q3_bruteforce, check_q3_closed_form,
 ]

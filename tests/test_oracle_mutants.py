@@ -63,6 +63,17 @@ MUTANTS = {
                           "q = np.asarray(qs, dtype=np.int8).view(np.uint8).astype(np.float64)"),
     "q8_scale_block_shift": ("s = np.repeat(fp16_to_f64(d), Q8_BLOCK, axis=-1)",
                              "s = np.roll(np.repeat(fp16_to_f64(d), Q8_BLOCK, axis=-1), 1, axis=-1)"),
+    "q3_big_endian_bits": ('bits = np.unpackbits(b, axis=-1, bitorder="little")',
+                           'bits = np.unpackbits(b, axis=-1, bitorder="big")'),
+    "q3_bit_weights_swapped": ("(trip[..., 0] | (trip[..., 1] << 1) | (trip[..., 2] << 2))",
+                               "(trip[..., 1] | (trip[..., 0] << 1) | (trip[..., 2] << 2))"),
+    "q3_bias_dropped": ('''    q = unpack_q3(codes).astype(np.float64)
+    s = np.repeat(bf16_to_f64(scales), GROUP, axis=-1)
+    b = np.repeat(bf16_to_f64(biases), GROUP, axis=-1)
+    return s * q + b''', '''    q = unpack_q3(codes).astype(np.float64)
+    s = np.repeat(bf16_to_f64(scales), GROUP, axis=-1)
+    b = np.repeat(bf16_to_f64(biases), GROUP, axis=-1)
+    return s * q'''),
 }
 
 
