@@ -123,12 +123,42 @@ typedef struct sdv_q4t {
   const uint32_t *sb;
   int32_t E, N, K, group;
   int32_t fused_gateup;
-  int32_t format; /* SDV_FMT_AFFINE_Q4 (0, the layout above) or SDV_FMT_Q8_0 (below) */
+  int32_t format; /* SDV_FMT_AFFINE_Q4 (0, the layout above), SDV_FMT_Q8_0 or SDV_FMT_AFFINE_Q3 (below) */
 } sdv_q4t;
 
 /* Formats of a tiled weight (sdv_q4t.format). */
 #define SDV_FMT_AFFINE_Q4 0
 #define SDV_FMT_Q8_0 1
+#define SDV_FMT_AFFINE_Q3 2
+
+/*
+ * An affine-Q3, group-64 weight in row-major interchange layout (mere.run
+ * transfer report, "Shared architecture and implemented paths": the gathered
+ * expert kernel's Q3 specialization beside affine Q4/g64; the bit packing is
+ * this library's definition):
+ *   codes  [E][N][3K/8] bytes: element c of a row is bits [3c, 3c+3) of the
+ *          row's little-endian bit stream, an unsigned code q in 0..7
+ *   scales, biases  [E][N][K/64] bf16;  value = scales * q + biases per group
+ * The tiled form (sdv_q3_repack; format = SDV_FMT_AFFINE_Q3) keeps the Q4
+ * tiles and sb words; codes [E][T][K/64][3][64] uint32: for tile t and group
+ * g, word w of chunk l = 32h + c holds, of the tile's row c and elements
+ * 32h + 8j + i (step j, i < 8): w = 0, 1: the low two bits of steps 2w, 2w+1
+ * (element i < 4 at bit 8 (j & 1) + 2i, element i + 4 sixteen bits higher);
+ * w = 2: bit 2 of step j's element i < 4 at bit 4j + i, of i + 4 sixteen
+ * bits higher.  Sizes: sdv_q3t_codes_bytes; sdv_q4t_sb_bytes.
+ */
+typedef struct sdv_q3 {
+  const uint8_t *codes;
+  const uint16_t *scales;
+  const uint16_t *biases;
+  int32_t E, N, K;
+} sdv_q3;
+
+SDV_API size_t sdv_q3t_codes_bytes(int E, int N, int K, int fused_gateup);
+
+/* sdv_q3_repack -- as sdv_q4_repack for an affine-Q3 weight.  Errors: EINVAL, ELAYOUT, EALIAS, EHIP. */
+SDV_API int sdv_q3_repack(const sdv_q3 *src, int fused_gateup, void *codes_out, uint32_t *sb_out,
+                          sdv_stream_t stream);
 
 /*
  * A Q8_0 weight in row-major interchange layout (the GGUF Q8_0 block: 32

@@ -11,10 +11,11 @@ MODE_PLAIN, MODE_GATEUP_SWIGLU = 0, 1
 ACT_BF16, ACT_F32 = 0, 1
 ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1
 CONV_NONE, CONV_SILU = 0, 1
-FMT_AFFINE_Q4, FMT_Q8_0 = 0, 1
+FMT_AFFINE_Q4, FMT_Q8_0, FMT_AFFINE_Q3 = 0, 1, 2
 GATE_SIGMOID, GATE_SILU = 0, 1
 
 EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_q8_0t_codes_bytes", "sdv_q8_0_repack",
+           "sdv_q3t_codes_bytes", "sdv_q3_repack",
            "sdv_qmv_k", "sdv_moe_route_k",
            "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
            "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
@@ -34,6 +35,11 @@ class SdvQ4T(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("sb", ctypes.c_void_p), ("E", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("fused_gateup", ctypes.c_int32), ("format", ctypes.c_int32)]
+
+
+class SdvQ3(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
 
 
 class SdvQ8_0(ctypes.Structure):
@@ -57,6 +63,8 @@ _SIGS = {
     "sdv_q4_repack": [ctypes.POINTER(SdvQ4), _I, _P, _P, _P],
     "sdv_q8_0t_codes_bytes": [_I, _I, _I, _I],
     "sdv_q8_0_repack": [ctypes.POINTER(SdvQ8_0), _I, _P, _P, _P],
+    "sdv_q3t_codes_bytes": [_I, _I, _I, _I],
+    "sdv_q3_repack": [ctypes.POINTER(SdvQ3), _I, _P, _P, _P],
     "sdv_qmv_k": [ctypes.POINTER(SdvQ4T), _P, _I, _I, _I, _P, _P],
     "sdv_moe_route_k": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
     "sdv_gather_qmv_k": [ctypes.POINTER(SdvQ4T), _I, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P,
@@ -95,7 +103,7 @@ def lib():
             fn.argtypes = args
             if name in ("sdv_status_string", "sdv_last_error", "sdv_build_info"):
                 fn.restype = ctypes.c_char_p
-            elif name in ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q8_0t_codes_bytes",
+            elif name in ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q8_0t_codes_bytes", "sdv_q3t_codes_bytes",
                           "sdv_moe_experts_partial_bytes", "sdv_verify_accept_workspace_bytes"):
                 fn.restype = ctypes.c_size_t
             else:

@@ -15,6 +15,8 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
 size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather, int fmt);
 size_t q4t_codes_bytes(int E, int N, int K, int fused);
 size_t q8_0t_codes_bytes(int E, int N, int K, int fused);
+size_t q3t_codes_bytes(int E, int N, int K, int fused);
+hipError_t q3_repack_launch(const sdv_q3& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st);
 hipError_t q8_0_repack_launch(const sdv_q8_0& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st);
 size_t q4t_sb_bytes(int E, int N, int K, int fused);
 hipError_t q4_repack_launch(const sdv_q4& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st);
@@ -141,7 +143,7 @@ int check_q4t(const sdv_q4t* W, const char* what) {
   if (W->fused_gateup != 0 && W->fused_gateup != 1)
     return fail(SDV_ELAYOUT, "%s fused_gateup=%d must be 0 or 1", what, W->fused_gateup);
   if (W->fused_gateup && (W->N % 2)) return fail(SDV_ELAYOUT, "%s fused gate/up needs an even N", what);
-  if (W->format != SDV_FMT_AFFINE_Q4 && W->format != SDV_FMT_Q8_0)
+  if (W->format != SDV_FMT_AFFINE_Q4 && W->format != SDV_FMT_Q8_0 && W->format != SDV_FMT_AFFINE_Q3)
     return fail(SDV_ELAYOUT, "%s format=%d is not a known weight format", what, W->format);
   int st;
   if ((st = check_ptr(W->codes, "codes"))) return st;
@@ -170,8 +172,9 @@ int check_mode(int mode, int act_dtype, int N) {
 
 // Tiled code bytes of a weight in its format.
 size_t tiled_codes_bytes(const sdv_q4t& W) {
-  return W.format == SDV_FMT_Q8_0 ? sdv::q8_0t_codes_bytes(W.E, W.N, W.K, W.fused_gateup)
-                                  : sdv::q4t_codes_bytes(W.E, W.N, W.K, W.fused_gateup);
+  if (W.format == SDV_FMT_Q8_0) return sdv::q8_0t_codes_bytes(W.E, W.N, W.K, W.fused_gateup);
+  if (W.format == SDV_FMT_AFFINE_Q3) return sdv::q3t_codes_bytes(W.E, W.N, W.K, W.fused_gateup);
+  return sdv::q4t_codes_bytes(W.E, W.N, W.K, W.fused_gateup);
 }
 
 int check_lds(const sdv_q4t& W, int act_dtype, int k, bool gather) {
@@ -259,6 +262,33 @@ int sdv_q8_0_repack(const sdv_q8_0* src, int fused_gateup, void* codes_out, uint
   if ((st = check_alias(outs, 2, ins, 2))) return st;
   return hip_status(sdv::q8_0_repack_launch(*src, fused_gateup, codes_out, sb_out, (hipStream_t)stream),
                     "sdv_q8_0_repack launch");
+}
+
+size_t sdv_q3t_codes_bytes(int E, int N, int K, int fused_gateup) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % SDV_GROUP) return 0;
+  return sdv::q3t_codes_bytes(E, N, K, fused_gateup ? 1 : 0);
+}
+
+int sdv_q3_repack(const sdv_q3* src, int fused_gateup, void* codes_out, uint32_t* sb_out, sdv_stream_t stream) {
+  int st;
+  if (!src) return fail(SDV_EINVAL, "src descriptor is NULL");
+  if (src->K <= 0 || src->K % SDV_GROUP) return fail(SDV_ELAYOUT, "src K=%d is not a positive multiple of 64", src->K);
+  if (src->N <= 0 || src->E <= 0) return fail(SDV_EINVAL, "src E=%d N=%d must be positive", src->E, src->N);
+  if (fused_gateup != 0 && fused_gateup != 1) return fail(SDV_ELAYOUT, "fused_gateup=%d must be 0 or 1", fused_gateup);
+  if (fused_gateup && (src->N % 2)) return fail(SDV_ELAYOUT, "fused gate/up needs an even N (got %d)", src->N);
+  const void* ptrs[] = {src->codes, src->scales, src->biases, codes_out, sb_out};
+  const char* names[] = {"codes", "scales", "biases", "codes_out", "sb_out"};
+  for (int i = 0; i < 5; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  const size_t rows = (size_t)src->E * src->N;
+  Range outs[] = {{codes_out, sdv::q3t_codes_bytes(src->E, src->N, src->K, fused_gateup), "codes_out"},
+                  {sb_out, sdv::q4t_sb_bytes(src->E, src->N, src->K, fused_gateup), "sb_out"}};
+  Range ins[] = {{src->codes, rows * 3 * src->K / 8, "codes"},
+                 {src->scales, rows * (src->K / 64) * 2, "scales"},
+                 {src->biases, rows * (src->K / 64) * 2, "biases"}};
+  if ((st = check_alias(outs, 2, ins, 3))) return st;
+  return hip_status(sdv::q3_repack_launch(*src, fused_gateup, codes_out, sb_out, (hipStream_t)stream),
+                    "sdv_q3_repack launch");
 }
 
 int sdv_qmv_k(const sdv_q4t* W, const void* act, int act_dtype, int k, int mode, float* y,
@@ -385,7 +415,7 @@ int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x
   if (gate_up->format != SDV_FMT_AFFINE_Q4 || down->format != SDV_FMT_AFFINE_Q4 ||
       (shared_gate_up && shared_gate_up->format != SDV_FMT_AFFINE_Q4) ||
       (shared_down && shared_down->format != SDV_FMT_AFFINE_Q4))
-    return fail(SDV_ELAYOUT, "the fused expert kernel takes affine Q4 weights; use sdv_gather_qmv_k for Q8_0");
+    return fail(SDV_ELAYOUT, "the fused expert kernel takes affine Q4 weights; use sdv_gather_qmv_k for Q8_0 and Q3");
   if (down->fused_gateup) return fail(SDV_ELAYOUT, "down must be repacked with fused_gateup=0");
   const int H = gate_up->K, I = gate_up->N / 2;
   if (down->E != gate_up->E || down->N != H || down->K != I)

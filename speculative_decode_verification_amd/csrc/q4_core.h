@@ -37,6 +37,35 @@ __device__ __forceinline__ bf16x8 decode_word(uint32_t w, DecodeK d) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(p));
 }
 
+// Affine Q3: a lane's 32 codes of a group in three words (the tiled layout
+// of SDV_FMT_AFFINE_Q3).  Words 0 and 1 hold the low two bits of steps 0-1
+// and 2-3: step j's element i (i < 4) at bit 8 (j & 1) + 2 i and element
+// i + 4 sixteen bits higher; word 2 holds bit 2 of every code: step j's
+// element i at bit 4 j + i, element i + 4 sixteen bits higher.  A pair
+// decodes, like Q4, to the bf16 values 128 + q of elements (i, i + 4).
+__device__ __forceinline__ bf16x8 decode_q3(const uint4 cw, int j, DecodeK d) {
+  const uint32_t lo = j < 2 ? cw.x : cw.y;
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t l2 = (lo >> (8 * (j & 1) + 2 * i)) & 0x00030003u;
+    const uint32_t b2 = ((cw.z >> (4 * j + i)) & 0x00010001u) << 2;
+    p[i] = l2 | b2 | d.bias;
+  }
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(p));
+}
+
+// The codes of MFMA step j of a Q4 or Q3 block.
+template <int FMT>
+__device__ __forceinline__ bf16x8 decode_step(const uint4 cw, int j, DecodeK d) {
+  if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
+    return decode_q3(cw, j, d);
+  } else {
+    const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+    return decode_word(cws[j], d);
+  }
+}
+
 // Permute 8 bf16 values (natural K order in e[0..7]) into slot order NU.
 __device__ __forceinline__ uint4 nu_pack(const uint32_t e[8]) {
   uint4 r;
@@ -193,6 +222,7 @@ __device__ __forceinline__ int slot_of_arow(int arow, int nrows) {
 // into yacc for the first `nquads` register quads.  `ap` points at this
 // lane's activation row (or at an all-zero LDS row), so the four A reads are
 // issued together, unconditionally, before the decode.
+template <int FMT = SDV_FMT_AFFINE_Q4>
 __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const uint16_t* ap, const float* xs_g,
                                           int G, int half, int nquads, float yacc[16], DecodeK dk) {
   uint4 av[4];
@@ -202,10 +232,9 @@ __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const ui
   const float b = __uint_as_float(sbw & 0xFFFF0000u);
   const float c = fmaf(-128.0f, s, b);
   f32x16 acc = {};
-  const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j], dk), acc,
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_step<FMT>(cw, j, dk), acc,
                                                   0, 0, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -227,7 +256,7 @@ __device__ __forceinline__ void group_mac(const uint4 cw, uint32_t sbw, const ui
 // at the group sums of the row behind y[i] (for fp32 rows, of all three parts)
 // and s_idx is the group.  Per group,
 //   y += s * P + (b - 128 s) * X,   P = the row's parts' products summed in part order.
-template <int ACT>
+template <int ACT, int FMT = SDV_FMT_AFFINE_Q4>
 __device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, const uint16_t* ap,
                                                const float* const (&xr)[5], int s_idx, float y[5], DecodeK dk) {
   uint4 av[4];
@@ -237,10 +266,9 @@ __device__ __forceinline__ void group_mac_rows(const uint4 cw, uint32_t sbw, con
   const float b = __uint_as_float(sbw & 0xFFFF0000u);
   const float c = fmaf(-128.0f, s, b);
   f32x16 acc = {};
-  const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_word(cws[j], dk), acc,
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_step<FMT>(cw, j, dk), acc,
                                                   0, 0, 0);
   float t[5];
   if (ACT == SDV_ACT_BF16) {

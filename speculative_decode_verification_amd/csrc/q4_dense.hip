@@ -125,6 +125,9 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
     if constexpr (Q8) {
       cbuf[slot] = load_nt(a.codes + blk * 128 + lane);  // weights: read once per call
       cbuf2[slot] = load_nt(a.codes + blk * 128 + 64 + lane);
+    } else if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(a.codes) + blk * 192 + lane;
+      cbuf[slot] = make_uint4(load_nt(w), load_nt(w + 64), load_nt(w + 128), 0u);
     } else {
       cbuf[slot] = load_nt(a.codes + blk * 64 + lane);
     }
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
       if constexpr (Q8) {
         group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + s * 64, xr, s, y);
       } else {
-        group_mac_rows<ACT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+        group_mac_rows<ACT, FMT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
       }
       issue(i, s + PF);
     }
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
         if constexpr (Q8) {
           group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + s * 64, xr, s, y);
         } else {
-          group_mac_rows<ACT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+          group_mac_rows<ACT, FMT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
         }
       }
     }
@@ -374,6 +377,10 @@ hipError_t dense_launch_pass(const sdv_q4t& W, int mode, const void* act, int ac
   SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_PLAIN, SDV_ACT_F32)
   SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
   SDV_DENSE(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+  SDV_DENSE(SDV_FMT_AFFINE_Q3, SDV_MODE_PLAIN, SDV_ACT_BF16)
+  SDV_DENSE(SDV_FMT_AFFINE_Q3, SDV_MODE_PLAIN, SDV_ACT_F32)
+  SDV_DENSE(SDV_FMT_AFFINE_Q3, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+  SDV_DENSE(SDV_FMT_AFFINE_Q3, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
 #undef SDV_DENSE
   return hipErrorInvalidValue;
 }

@@ -172,6 +172,9 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
     if constexpr (Q8) {
       cbuf[slot] = load_nt(codes + ld_blk * 128 + lane);  // weights: read once per call
       cbuf2[slot] = load_nt(codes + ld_blk * 128 + 64 + lane);
+    } else if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(codes) + ld_blk * 192 + lane;
+      cbuf[slot] = make_uint4(load_nt(w), load_nt(w + 64), load_nt(w + 128), 0u);
     } else {
       cbuf[slot] = load_nt(codes + ld_blk * 64 + lane);
     }
@@ -232,7 +235,7 @@ __device__ __forceinline__ void q4_matvec_body(const Q4Args& a, unsigned char* s
     if constexpr (Q8) {
       group_mac_q8(cbuf[i], cbuf2[i], sbuf[i], arow_ptr + cur_g * 64, xsum + 2 * cur_g, 2 * G, half, nquads, yacc);
     } else {
-      group_mac(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc, dk);
+      group_mac<FMT>(cbuf[i], sbuf[i], arow_ptr + cur_g * 64, xsum + cur_g, G, half, nquads, yacc, dk);
     }
     if (refill) issue(i);
     if (++cur_g == ge) {
@@ -430,9 +433,89 @@ __global__ __launch_bounds__(256) void q8_0_repack_kernel(Q8RepackArgs r) {
   }
 }
 
+// ---- repack: row-major affine Q3 -> tiled layout ----------------------------
+
+struct Q3RepackArgs {
+  const uint8_t* codes;  // [E][N][3K/8]
+  const uint16_t* scales;
+  const uint16_t* biases;
+  int E, N, K, T, fused;
+  uint32_t* tcodes;  // [E][T][G][3][64]
+  uint32_t* tsb;     // [E][T][G][32]
+};
+
+__global__ __launch_bounds__(256) void q3_repack_kernel(Q3RepackArgs r) {
+  const int G = r.K >> 6;
+  const size_t nblk = (size_t)r.E * r.T * G;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const RepackArgs rows{nullptr, nullptr, nullptr, r.E, r.N, r.K, r.T, r.fused, nullptr, nullptr};
+  // codes: one thread per (block, lane): the lane's 32 codes (12 bytes of the
+  // row's stream, 4-byte aligned) into the three plane words
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * 64; idx += stride) {
+    const int lane = (int)(idx & 63);
+    const size_t blk = idx >> 6;
+    const int g = (int)(blk % G);
+    const size_t et = blk / G;
+    const int t = (int)(et % r.T);
+    const int e = (int)(et / r.T);
+    const int n = repack_row(rows, t, lane & 31);
+    uint32_t w[3] = {0u, 0u, 0u};
+    if (n >= 0) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(r.codes + ((size_t)e * r.N + n) * (3 * (size_t)r.K / 8) +
+                                                              24 * (size_t)g + 12 * (lane >> 5));
+      const uint64_t lo = (uint64_t)src[0] | ((uint64_t)src[1] << 32);
+      const uint32_t hi = src[2];
+      for (int el = 0; el < 32; ++el) {
+        const int b = 3 * el;  // bits b .. b + 2 of the 96-bit value hi:lo
+        uint32_t q;
+        if (b + 3 <= 64)
+          q = (uint32_t)(lo >> b) & 7u;
+        else if (b < 64)
+          q = (uint32_t)((lo >> b) | ((uint64_t)hi << (64 - b))) & 7u;
+        else
+          q = (hi >> (b - 64)) & 7u;
+        const int j = el >> 3, i8 = el & 7, i = i8 & 3, up = (i8 >> 2) * 16;
+        w[j >> 1] |= (q & 3u) << (up + 8 * (j & 1) + 2 * i);
+        w[2] |= (q >> 2) << (up + 4 * j + i);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) r.tcodes[(blk * 3 + p) * 64 + lane] = w[p];
+  }
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * 32; idx += stride) {
+    const int c = (int)(idx & 31);
+    const size_t blk = idx >> 5;
+    const int g = (int)(blk % G);
+    const size_t et = blk / G;
+    const int t = (int)(et % r.T);
+    const int e = (int)(et / r.T);
+    const int n = repack_row(rows, t, c);
+    uint32_t w = 0;
+    if (n >= 0) {
+      const size_t o = ((size_t)e * r.N + n) * G + g;
+      w = (uint32_t)r.scales[o] | ((uint32_t)r.biases[o] << 16);
+    }
+    r.tsb[idx] = w;
+  }
+}
+
 }  // namespace
 
 int q4_tiles(int N, int fused);
+
+size_t q3t_codes_bytes(int E, int N, int K, int fused) {
+  return (size_t)E * q4_tiles(N, fused) * (K / 64) * 768;
+}
+
+hipError_t q3_repack_launch(const sdv_q3& src, int fused, void* tcodes, uint32_t* tsb, hipStream_t st) {
+  Q3RepackArgs r{src.codes, src.scales, src.biases, src.E, src.N, src.K, q4_tiles(src.N, fused), fused,
+                 static_cast<uint32_t*>(tcodes), tsb};
+  const size_t n = (size_t)src.E * r.T * (src.K / 64) * 64;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(q3_repack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, r);
+  return hipGetLastError();
+}
 
 size_t q8_0t_codes_bytes(int E, int N, int K, int fused) {
   return (size_t)E * q4_tiles(N, fused) * (K / 64) * 2048;
@@ -523,6 +606,10 @@ hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype,
     SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_PLAIN, SDV_ACT_F32)
     SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
     SDV_Q4_G(SDV_FMT_Q8_0, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q3, SDV_MODE_PLAIN, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q3, SDV_MODE_PLAIN, SDV_ACT_F32)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q3, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
+    SDV_Q4_G(SDV_FMT_AFFINE_Q3, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_F32)
 #undef SDV_Q4_G
   } else {
     return dense_launch(W, mode, act, act_dtype, k, out, st);

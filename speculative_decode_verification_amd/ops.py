@@ -11,11 +11,11 @@ from collections import namedtuple
 
 import torch
 
-from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, FMT_AFFINE_Q4, FMT_Q8_0, GATE_SIGMOID, GATE_SILU,
-                   MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ4, SdvQ4T, SdvQ8_0,
-                   check, lib)
+from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, FMT_AFFINE_Q3, FMT_AFFINE_Q4, FMT_Q8_0, GATE_SIGMOID,
+                   GATE_SILU, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ3, SdvQ4,
+                   SdvQ4T, SdvQ8_0, check, lib)
 
-__all__ = ["Q4Weight", "Q8Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
+__all__ = ["Q4Weight", "Q8Weight", "Q3Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "FMT_AFFINE_Q3", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
            "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_gated_norm_k",
            "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
@@ -77,6 +77,38 @@ class Q4Weight:
         return TiledQ4.from_rowmajor(self, fused_gateup)
 
 
+class Q3Weight:
+    """Affine-Q3/g64 weights on the device: codes uint8 [E, N, 3K/8] (a
+    little-endian 3-bit stream per row), scales and biases int16 (bf16 bits)
+    [E, N, K/64].  A 2-D layout is a dense matrix (E = 1)."""
+
+    def __init__(self, codes, scales, biases):
+        if codes.dim() == 2:
+            codes, scales, biases = codes[None], scales[None], biases[None]
+        if codes.dim() != 3 or scales.shape != biases.shape or scales.dim() != 3:
+            raise ValueError("codes [E,N,3K/8], scales/biases [E,N,K/64] expected")
+        self.E, self.N, nb = codes.shape
+        self.K = nb * 8 // 3
+        if nb * 8 != self.K * 3 or scales.shape != (self.E, self.N, self.K // 64):
+            raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+        self.codes, self.scales, self.biases = codes, scales, biases
+        self.device = codes.device
+        self._desc = SdvQ3(_need(codes, "codes", torch.uint8).value,
+                           _need(scales, "scales", torch.int16, device=self.device).value,
+                           _need(biases, "biases", torch.int16, device=self.device).value, self.E, self.N, self.K)
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def nbytes(self):
+        return self.E * self.N * (3 * self.K // 8 + (self.K // 64) * 4)
+
+    def tiled(self, fused_gateup=False):
+        """The weight rewritten on the device into the tiled Q3 layout (sdv_q3_repack)."""
+        return TiledQ4.from_rowmajor(self, fused_gateup)
+
+
 class Q8Weight:
     """Q8_0 weights on the device in the GGUF interchange form: codes int8
     [E, N, K], half scales int16 (binary16 bits) [E, N, K/32].  A 2-D layout
@@ -108,14 +140,19 @@ class Q8Weight:
         return TiledQ4.from_rowmajor(self, fused_gateup)
 
 
+_CODES_BYTES = {FMT_AFFINE_Q4: "sdv_q4t_codes_bytes", FMT_Q8_0: "sdv_q8_0t_codes_bytes",
+                FMT_AFFINE_Q3: "sdv_q3t_codes_bytes"}
+
+
 class TiledQ4:
     """A tiled weight of ``sdv_q4t`` (device tensors ``codes`` uint8 and ``sb``
-    int32): affine Q4/g64 (``fmt`` FMT_AFFINE_Q4) or Q8_0 (FMT_Q8_0)."""
+    int32): affine Q4/g64 (``fmt`` FMT_AFFINE_Q4), Q8_0 (FMT_Q8_0) or affine
+    Q3/g64 (FMT_AFFINE_Q3)."""
 
     def __init__(self, codes, sb, E, N, K, fused_gateup, fmt=FMT_AFFINE_Q4):
         self.E, self.N, self.K, self.fused, self.fmt = E, N, K, bool(fused_gateup), fmt
         L = lib()
-        need_c = (L.sdv_q8_0t_codes_bytes if fmt == FMT_Q8_0 else L.sdv_q4t_codes_bytes)(E, N, K, int(self.fused))
+        need_c = getattr(L, _CODES_BYTES[fmt])(E, N, K, int(self.fused))
         need_s = L.sdv_q4t_sb_bytes(E, N, K, int(self.fused))
         if codes.numel() * codes.element_size() < need_c or sb.numel() * 4 < need_s:
             raise ValueError("tiled buffers are smaller than the layout needs")
@@ -128,7 +165,7 @@ class TiledQ4:
     @staticmethod
     def empty(E, N, K, fused_gateup, device, fmt=FMT_AFFINE_Q4):
         L = lib()
-        nc = (L.sdv_q8_0t_codes_bytes if fmt == FMT_Q8_0 else L.sdv_q4t_codes_bytes)(E, N, K, int(bool(fused_gateup)))
+        nc = getattr(L, _CODES_BYTES[fmt])(E, N, K, int(bool(fused_gateup)))
         ns = L.sdv_q4t_sb_bytes(E, N, K, int(bool(fused_gateup)))
         codes = torch.empty((nc,), dtype=torch.uint8, device=device)
         sb = torch.empty((ns // 4,), dtype=torch.int32, device=device)
@@ -136,9 +173,9 @@ class TiledQ4:
 
     @classmethod
     def from_rowmajor(cls, W, fused_gateup=False, out=None):
-        fmt = FMT_Q8_0 if isinstance(W, Q8Weight) else FMT_AFFINE_Q4
+        fmt = FMT_Q8_0 if isinstance(W, Q8Weight) else (FMT_AFFINE_Q3 if isinstance(W, Q3Weight) else FMT_AFFINE_Q4)
         codes, sb = out if out is not None else cls.empty(W.E, W.N, W.K, fused_gateup, W.device, fmt)
-        repack = lib().sdv_q8_0_repack if fmt == FMT_Q8_0 else lib().sdv_q4_repack
+        repack = {FMT_Q8_0: lib().sdv_q8_0_repack, FMT_AFFINE_Q3: lib().sdv_q3_repack}.get(fmt, lib().sdv_q4_repack)
         check(repack(W.desc, int(bool(fused_gateup)), _need(codes, "codes_out", codes.dtype),
                      _need(sb, "sb_out", torch.int32), _stream(codes)))
         return cls(codes, sb, W.E, W.N, W.K, fused_gateup, fmt)

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 23
+    assert len(names) == 25
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -99,8 +99,25 @@ def test_q8_0_sizes_and_repack_validation(lib):
     assert f(src(), 0, out_c, out_c + 64, None) == L.SDV_EALIAS
 
 
+def test_q3_sizes_and_repack_validation(lib):
+    # T tiles x G groups x (768 B of codes: three words per lane)
+    assert lib.sdv_q3t_codes_bytes(512, 1280, 2560, 1) == 512 * 40 * 40 * 768
+    assert lib.sdv_q3t_codes_bytes(1, 64, 96, 0) == 0
+    f = lib.sdv_q3_repack
+    src = lambda **kw: ctypes.byref(L.SdvQ3(kw.get("codes", P), kw.get("scales", P + 0x100000),
+                                             kw.get("biases", P + 0x200000), kw.get("E", 1), kw.get("N", 64),
+                                             kw.get("K", 128)))
+    out_c, out_s = P + 0x4000000, P + 0x8000000
+    assert f(None, 0, out_c, out_s, None) == L.SDV_EINVAL
+    assert f(src(K=100), 0, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(src(N=63), 1, out_c, out_s, None) == L.SDV_ELAYOUT
+    assert f(src(biases=0), 0, out_c, out_s, None) == L.SDV_EINVAL
+    assert f(src(), 0, P + 16, out_s, None) == L.SDV_EALIAS                     # over the source codes
+    assert f(src(), 0, out_c, P + 0x200000 + 16, None) == L.SDV_EALIAS          # sb over the biases
+
+
 def test_format_validation(lib):
-    assert qmv(lib, q4t(fmt=2)) == L.SDV_ELAYOUT
+    assert qmv(lib, q4t(fmt=3)) == L.SDV_ELAYOUT
     assert "format" in lib.sdv_last_error().decode()
     # a Q8_0 weight's codes are twice a Q4 weight's: an output right after
     # the Q4-sized codes still overlaps them
