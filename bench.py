@@ -393,40 +393,68 @@ def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
 
 
 def dense_projection(dev, timer, n_weights=64, reps=4):
-    """sdv_qmv_k on the dense 5120 x 5120 shape: 64 distinct weights (944 MB,
-    more than the last-level cache) launched back to back at each width, timed
-    with HIP events around each width's launches.  Reported per projection:
-    time and algorithmic GB/s (weights, activations and outputs once)."""
+    """sdv_qmv_k on the dense 5120 x 5120 shape: 64 distinct weights (944 MB
+    of affine Q4, more than the last-level cache) launched back to back at
+    each width, timed with HIP events around each width's launches; then the
+    same for the Q8_0 (1.7 GB) and affine-Q3 (0.66 GB) formats, and the
+    32-row width.  Reported per projection: time and algorithmic GB/s
+    (weights, activations and outputs once)."""
     import torch
     import synth
     from synth import device as sdev
     from synth.inputs import DENSE_W
     from speculative_decode_verification_amd import ops
     N = K = 5120
-    Ws = [ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(1, DENSE_W, l), 1, N, K, dev)).tiled()
-          for l in range(n_weights)]
-    x = sdev.upload_bf16(synth.activations(1, 0, 9, K), dev)
-    out = {}
-    for k in (1, 4, 8, 9):
-        xs = x[:k].contiguous()
-        ys = torch.empty((k, N), dtype=torch.float32, device=dev)
-        calls = [ops.bind_qmv_k(W, xs, ops.MODE_PLAIN, ys) for W in Ws]
-        for c in calls:
-            c()
-        torch.cuda.synchronize()
-        a = timer.start()
-        for _ in range(reps):
+    x = sdev.upload_bf16(synth.activations(1, 0, 32, K), dev)
+
+    def time_widths(Ws, wbytes, widths):
+        res = {}
+        for k in widths:
+            xs = x[:k].contiguous()
+            ys = torch.empty((k, N), dtype=torch.float32, device=dev)
+            calls = [ops.bind_qmv_k(W, xs, ops.MODE_PLAIN, ys) for W in Ws]
             for c in calls:
                 c()
-        b = timer.stop()
-        torch.cuda.synchronize()
-        us = timer.elapsed_us(a, b) / (reps * n_weights)
-        nbytes = q4_bytes(N, K) + k * (2 * K + 4 * N)
-        out[f"k{k}"] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
-                        "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3)}
+            torch.cuda.synchronize()
+            a = timer.start()
+            for _ in range(reps):
+                for c in calls:
+                    c()
+            b = timer.stop()
+            torch.cuda.synchronize()
+            us = timer.elapsed_us(a, b) / (reps * len(Ws))
+            nbytes = wbytes + k * (2 * K + 4 * N)
+            res[f"k{k}"] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                            "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3)}
+        return res
+
+    Ws = [ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(1, DENSE_W, l), 1, N, K, dev)).tiled()
+          for l in range(n_weights)]
+    out = time_widths(Ws, q4_bytes(N, K), (1, 4, 8, 9, 32))
+    del Ws
+    # Q8_0 and affine Q3 weights filled on the device (any codes are valid;
+    # parity of these formats is covered by the tests)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5120)
+    Ws = []
+    for _ in range(n_weights):
+        qs = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+        d = (torch.rand((N, K // 32), device=dev, generator=g) * 6e-4 + 2e-4).to(torch.float16).view(torch.int16)
+        Ws.append(ops.Q8Weight(qs, d).tiled())
+        del qs, d
+    q8 = time_widths(Ws, N * K + N * (K // 64) * 4, (1, 9))
+    del Ws
+    Ws = []
+    for _ in range(n_weights):
+        codes = torch.randint(0, 256, (N, 3 * K // 8), dtype=torch.uint8, device=dev, generator=g)
+        sc = (torch.rand((N, K // 64), device=dev, generator=g) * 0.03 + 0.01).to(torch.bfloat16).view(torch.int16)
+        bi = (torch.rand((N, K // 64), device=dev, generator=g) * 0.2 - 0.1).to(torch.bfloat16).view(torch.int16)
+        Ws.append(ops.Q3Weight(codes, sc, bi).tiled())
+        del codes, sc, bi
+    q3 = time_widths(Ws, N * 3 * K // 8 + N * (K // 64) * 4, (1, 9))
     del Ws
     torch.cuda.empty_cache()
-    return {"shape": [N, K], "weights": n_weights, "widths": out}
+    return {"shape": [N, K], "weights": n_weights, "widths": out, "q8_0": q8, "q3": q3}
 
 
 def copy_probe():
@@ -469,7 +497,7 @@ def main():
     unions = wl.unions()
 
     per_step = len(wl.calls[0]) * wl.layers + 2 * len(wl.gdn) + 1
-    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1 + 4)
+    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1 + 9)  # 9: the dense widths
     log(f"timing events on the launch stream (HIP runtime {timer.path})")
     events = []
     torch.cuda.synchronize()
