@@ -275,8 +275,13 @@ class Workload:
             # the per-slice partial outputs of every used slot written once
             S = (I + 127) // 128
             used = k * topk + sh * k
-            return ((U + sh) * (q4_bytes(2 * I, H) + q4_bytes(H, I)) + k * H * 2 + U * 4 * 2
-                    + S * used * H * 4)
+            b = ((U + sh) * (q4_bytes(2 * I, H) + q4_bytes(H, I)) + k * H * 2 + U * 4 * 2
+                 + S * used * H * 4)
+            if self.moe[l][0].route_in_experts:
+                # the router dispatch in the same launch: logits in, its
+                # outputs out (as the "route" launch)
+                b += k * E * 4 + k * topk * 4 * 5 + 8
+            return b
         if name == "combine" and self.moe[l][0].fused_experts:
             S = (I + 127) // 128
             used = k * topk + sh * k

@@ -315,6 +315,25 @@ SDV_API int sdv_moe_experts_k(const sdv_q4t *gate_up, const sdv_q4t *down, const
                               const sdv_q4t *shared_gate_up, const sdv_q4t *shared_down, float *partial,
                               sdv_stream_t stream);
 
+/*
+ * sdv_moe_route_experts_k -- sdv_moe_route_k and sdv_moe_experts_k as one
+ * call (Red Lite dev45, "What it is": one router dispatch, then the union's
+ * (expert, row) pairs in one pool encode).  For k <= 9 and E <= 512 it is one
+ * launch: every expert workgroup runs the router dispatch itself on the
+ * logits (identical results everywhere; workgroup (0, 0) writes them), so the
+ * routing needs no launch of its own.  Otherwise it runs the two launches.
+ * The outputs equal those of the two calls bit for bit.
+ *   logits, score_mode, renorm  as sdv_moe_route_k (E = gate_up->E)
+ *   idx, w, union_ids, n_union, pair_off, pair_row, pair_slot  outputs, as sdv_moe_route_k
+ *   gate_up, down, x, shared_gate_up, shared_down, partial  as sdv_moe_experts_k
+ * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE, EALIAS, EHIP.
+ */
+SDV_API int sdv_moe_route_experts_k(const float *logits, int score_mode, int renorm, const sdv_q4t *gate_up,
+                                    const sdv_q4t *down, const void *x, int k, int topk,
+                                    const sdv_q4t *shared_gate_up, const sdv_q4t *shared_down, int32_t *idx,
+                                    float *w, int32_t *union_ids, int32_t *n_union, int32_t *pair_off,
+                                    int32_t *pair_row, int32_t *pair_slot, float *partial, sdv_stream_t stream);
+
 /* Bytes of sdv_moe_experts_k's partial output, or 0 for invalid sizes. */
 SDV_API size_t sdv_moe_experts_partial_bytes(int k, int topk, int H, int I);
 

@@ -17,7 +17,7 @@ GATE_SIGMOID, GATE_SILU = 0, 1
 EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_q8_0t_codes_bytes", "sdv_q8_0_repack",
            "sdv_q3t_codes_bytes", "sdv_q3_repack",
            "sdv_qmv_k", "sdv_moe_route_k",
-           "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
+           "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_route_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
            "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
            "sdv_gdn_rollback_copy", "sdv_gdn_prepare_k", "sdv_gdn_verify_prep_k",
            "sdv_gdn_gated_norm_k",
@@ -71,6 +71,8 @@ _SIGS = {
                          ctypes.POINTER(SdvQ4T), _P, _P, _P],
     "sdv_moe_experts_k": [ctypes.POINTER(SdvQ4T), ctypes.POINTER(SdvQ4T), _P, _P, _P, _P, _P, _P, _I, _I,
                           ctypes.POINTER(SdvQ4T), ctypes.POINTER(SdvQ4T), _P, _P],
+    "sdv_moe_route_experts_k": [_P, _I, _I, ctypes.POINTER(SdvQ4T), ctypes.POINTER(SdvQ4T), _P, _I, _I,
+                                ctypes.POINTER(SdvQ4T), ctypes.POINTER(SdvQ4T), _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sdv_moe_experts_partial_bytes": [_I, _I, _I, _I],
     "sdv_moe_combine_sliced_k": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P],
     "sdv_moe_combine_k": [_P, _P, _P, _P, _I, _I, _I, _P, _P],

@@ -32,6 +32,13 @@ hipError_t combine_sliced_launch(const float* partial, const int32_t* idx, const
 int expert_slices(int I);
 size_t expert_lds_bytes(int k, int H);
 size_t expert_partial_bytes(int k, int topk, int H, int I);
+bool route_in_experts(int k, int E);
+size_t route_experts_lds_bytes(int k, int E, int H);
+hipError_t moe_route_experts_launch(const float* logits, int mode, int renorm, const sdv_q4t& gu,
+                                    const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn, const void* x, int k,
+                                    int topk, int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
+                                    int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot, float* partial,
+                                    hipStream_t st);
 hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn,
                               const void* x, const int32_t* union_ids, const int32_t* n_union,
                               const int32_t* pair_off, const int32_t* pair_row, const int32_t* pair_slot, int k,
@@ -404,10 +411,14 @@ size_t sdv_moe_experts_partial_bytes(int k, int topk, int H, int I) {
   return sdv::expert_partial_bytes(k, topk, H, I);
 }
 
-int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x, const int32_t* union_ids,
-                      const int32_t* n_union, const int32_t* pair_off, const int32_t* pair_row,
-                      const int32_t* pair_slot, int k, int topk, const sdv_q4t* shared_gate_up,
-                      const sdv_q4t* shared_down, float* partial, sdv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks sdv_moe_experts_k and sdv_moe_route_experts_k share: weights,
+// shapes, widths, LDS and the partial output's size (in *pbytes).
+int check_experts(const sdv_q4t* gate_up, const sdv_q4t* down, const sdv_q4t* shared_gate_up,
+                  const sdv_q4t* shared_down, int k, int topk, size_t lds_extra_for_route, size_t* pbytes_out) {
   int st;
   if ((st = check_q4t(gate_up, "gate_up"))) return st;
   if ((st = check_q4t(down, "down"))) return st;
@@ -437,38 +448,103 @@ int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x
         shared_down->N != H || shared_down->K != I || shared_down->fused_gateup)
       return fail(SDV_ELAYOUT, "shared expert geometry differs from the routed experts'");
   }
-  const size_t lds = sdv::expert_lds_bytes(k, H);
-  if (lds > kMaxLds) return fail(SDV_ELAYOUT, "H=%d with k=%d needs %zu bytes of LDS (max %zu)", H, k, lds, kMaxLds);
+  size_t lds = sdv::expert_lds_bytes(k, H);
+  if (lds_extra_for_route > lds) lds = lds_extra_for_route;
+  // the kernel's static LDS (row maps and the in-kernel routing's outputs)
+  // takes at most kExpertStaticLds of the workgroup's LDS
+  constexpr size_t kExpertStaticLds = 4096;
+  if (lds > kMaxLds - kExpertStaticLds)
+    return fail(SDV_ELAYOUT, "H=%d with k=%d needs %zu bytes of LDS (max %zu)", H, k, lds, kMaxLds - kExpertStaticLds);
   const size_t pbytes = sdv::expert_partial_bytes(k, topk, H, I);
   if (pbytes >= 0x7FFFFFF0u) return fail(SDV_ERANGE, "partial output of %zu bytes exceeds 2 GiB", pbytes);
+  *pbytes_out = pbytes;
+  return SDV_OK;
+}
+
+// Ranges of an expert call's weights (for the alias checks).
+int expert_weight_ranges(const sdv_q4t* gate_up, const sdv_q4t* down, const sdv_q4t* shared_gate_up,
+                         const sdv_q4t* shared_down, Range* r) {
+  const int H = gate_up->K, I = gate_up->N / 2;
+  r[0] = {gate_up->codes, sdv::q4t_codes_bytes(gate_up->E, gate_up->N, H, 1), "gate_up codes"};
+  r[1] = {gate_up->sb, sdv::q4t_sb_bytes(gate_up->E, gate_up->N, H, 1), "gate_up sb"};
+  r[2] = {down->codes, sdv::q4t_codes_bytes(down->E, H, I, 0), "down codes"};
+  r[3] = {down->sb, sdv::q4t_sb_bytes(down->E, H, I, 0), "down sb"};
+  r[4] = {shared_gate_up ? shared_gate_up->codes : nullptr, shared_gate_up ? sdv::q4t_codes_bytes(1, 2 * I, H, 1) : 0,
+          "shared_gate_up codes"};
+  r[5] = {shared_gate_up ? shared_gate_up->sb : nullptr, shared_gate_up ? sdv::q4t_sb_bytes(1, 2 * I, H, 1) : 0,
+          "shared_gate_up sb"};
+  r[6] = {shared_down ? shared_down->codes : nullptr, shared_down ? sdv::q4t_codes_bytes(1, H, I, 0) : 0,
+          "shared_down codes"};
+  r[7] = {shared_down ? shared_down->sb : nullptr, shared_down ? sdv::q4t_sb_bytes(1, H, I, 0) : 0, "shared_down sb"};
+  return 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x, const int32_t* union_ids,
+                      const int32_t* n_union, const int32_t* pair_off, const int32_t* pair_row,
+                      const int32_t* pair_slot, int k, int topk, const sdv_q4t* shared_gate_up,
+                      const sdv_q4t* shared_down, float* partial, sdv_stream_t stream) {
+  int st;
+  size_t pbytes = 0;
+  if ((st = check_experts(gate_up, down, shared_gate_up, shared_down, k, topk, 0, &pbytes))) return st;
+  const int H = gate_up->K;
   const void* ptrs[] = {x, union_ids, n_union, pair_off, pair_row, pair_slot, partial};
   const char* names[] = {"x", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot", "partial"};
   for (int i = 0; i < 7; ++i)
     if ((st = check_ptr(ptrs[i], names[i]))) return st;
   const size_t kt = (size_t)k * topk;
   Range outs[] = {{partial, pbytes, "partial"}};
-  Range ins[] = {
-      {gate_up->codes, sdv::q4t_codes_bytes(gate_up->E, gate_up->N, H, 1), "gate_up codes"},
-      {gate_up->sb, sdv::q4t_sb_bytes(gate_up->E, gate_up->N, H, 1), "gate_up sb"},
-      {down->codes, sdv::q4t_codes_bytes(down->E, H, I, 0), "down codes"},
-      {down->sb, sdv::q4t_sb_bytes(down->E, H, I, 0), "down sb"},
-      {shared_gate_up ? shared_gate_up->codes : nullptr, shared_gate_up ? sdv::q4t_codes_bytes(1, 2 * I, H, 1) : 0,
-       "shared_gate_up codes"},
-      {shared_gate_up ? shared_gate_up->sb : nullptr, shared_gate_up ? sdv::q4t_sb_bytes(1, 2 * I, H, 1) : 0,
-       "shared_gate_up sb"},
-      {shared_down ? shared_down->codes : nullptr, shared_down ? sdv::q4t_codes_bytes(1, H, I, 0) : 0,
-       "shared_down codes"},
-      {shared_down ? shared_down->sb : nullptr, shared_down ? sdv::q4t_sb_bytes(1, H, I, 0) : 0, "shared_down sb"},
-      {x, (size_t)k * H * 2, "x"},
-      {union_ids, kt * 4, "union_ids"},
-      {n_union, 4, "n_union"},
-      {pair_off, (kt + 1) * 4, "pair_off"},
-      {pair_row, kt * 4, "pair_row"},
-      {pair_slot, kt * 4, "pair_slot"}};
+  Range ins[14];
+  expert_weight_ranges(gate_up, down, shared_gate_up, shared_down, ins);
+  ins[8] = {x, (size_t)k * H * 2, "x"};
+  ins[9] = {union_ids, kt * 4, "union_ids"};
+  ins[10] = {n_union, 4, "n_union"};
+  ins[11] = {pair_off, (kt + 1) * 4, "pair_off"};
+  ins[12] = {pair_row, kt * 4, "pair_row"};
+  ins[13] = {pair_slot, kt * 4, "pair_slot"};
   if ((st = check_alias(outs, 1, ins, 14))) return st;
   return hip_status(sdv::moe_experts_launch(*gate_up, *down, shared_gate_up, shared_down, x, union_ids, n_union,
                                             pair_off, pair_row, pair_slot, k, topk, partial, (hipStream_t)stream),
                     "sdv_moe_experts_k launch");
+}
+
+int sdv_moe_route_experts_k(const float* logits, int score_mode, int renorm, const sdv_q4t* gate_up,
+                            const sdv_q4t* down, const void* x, int k, int topk, const sdv_q4t* shared_gate_up,
+                            const sdv_q4t* shared_down, int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
+                            int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot, float* partial,
+                            sdv_stream_t stream) {
+  int st;
+  if ((st = check_q4t(gate_up, "gate_up"))) return st;
+  const int E = gate_up->E;
+  if (E > SDV_MAX_EXPERTS) return fail(SDV_ERANGE, "E=%d above %d", E, SDV_MAX_EXPERTS);
+  if (score_mode != SDV_ROUTE_SOFTMAX && score_mode != SDV_ROUTE_SIGMOID)
+    return fail(SDV_EINVAL, "unknown score mode %d", score_mode);
+  size_t pbytes = 0;
+  const size_t route_lds = sdv::route_in_experts(k, E) ? sdv::route_experts_lds_bytes(k, E, gate_up->K) : 0;
+  if ((st = check_experts(gate_up, down, shared_gate_up, shared_down, k, topk, route_lds, &pbytes))) return st;
+  const int H = gate_up->K;
+  const void* ptrs[] = {logits, x, idx, w, union_ids, n_union, pair_off, pair_row, pair_slot, partial};
+  const char* names[] = {"logits", "x", "idx", "w", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot",
+                         "partial"};
+  for (int i = 0; i < 10; ++i)
+    if ((st = check_ptr(ptrs[i], names[i]))) return st;
+  const size_t kt = (size_t)k * topk;
+  Range outs[] = {{idx, kt * 4, "idx"},           {w, kt * 4, "w"},
+                  {union_ids, kt * 4, "union_ids"}, {n_union, 4, "n_union"},
+                  {pair_off, (kt + 1) * 4, "pair_off"}, {pair_row, kt * 4, "pair_row"},
+                  {pair_slot, kt * 4, "pair_slot"}, {partial, pbytes, "partial"}};
+  Range ins[10];
+  expert_weight_ranges(gate_up, down, shared_gate_up, shared_down, ins);
+  ins[8] = {x, (size_t)k * H * 2, "x"};
+  ins[9] = {logits, (size_t)k * E * 4, "logits"};
+  if ((st = check_alias(outs, 8, ins, 10))) return st;
+  return hip_status(sdv::moe_route_experts_launch(logits, score_mode, renorm, *gate_up, *down, shared_gate_up,
+                                                  shared_down, x, k, topk, idx, w, union_ids, n_union, pair_off,
+                                                  pair_row, pair_slot, partial, (hipStream_t)stream),
+                    "sdv_moe_route_experts_k launch");
 }
 
 int sdv_moe_combine_sliced_k(const float* partial, const int32_t* idx, const float* w, const float* shared_logit,

@@ -37,6 +37,7 @@
 #include <atomic>
 
 #include "q4_core.h"
+#include "route_core.h"
 
 namespace sdv {
 
@@ -70,7 +71,42 @@ struct ExpertArgs {
   int TA, GA, TB, GB, S;
   float* partial;  // [S][k][topk + 1][H]
   uint32_t partial_bytes;
+  // the router dispatch inside the kernel (RPL > 0): its inputs, and the
+  // global copies of its outputs (written by workgroup (0, 0))
+  const float* logits;
+  int mode, renorm;
+  int32_t* r_idx;
+  float* r_w;
+  int32_t* r_union;
+  int32_t* r_nu;
+  int32_t* r_off;
+  int32_t* r_row;
+  int32_t* r_slot;
 };
+
+constexpr int kExpertThreads = 64 * kWaves;
+
+// LDS scratch of the in-kernel router dispatch, at the start of the dynamic
+// LDS (the x staging overwrites it after the dispatch): candidate keys, each
+// wave's pool of 64 keys, row masks and counts over E, wave totals, the
+// total, and per-row counts, softmax shifts and sums.
+struct RouteScratchLayout {
+  size_t cand, pool, rowmask, cnt, wave, total, nsel, mx, part, bytes;
+};
+__host__ __device__ inline RouteScratchLayout route_scratch(int E) {
+  RouteScratchLayout l;
+  l.cand = 0;
+  l.pool = l.cand + (size_t)kPassRows * SDV_MAX_TOPK * 8;
+  l.rowmask = l.pool + (size_t)kExpertThreads * 8;
+  l.cnt = l.rowmask + (size_t)E * 4;
+  l.wave = l.cnt + (size_t)E * 4;
+  l.total = l.wave + (kExpertThreads / 64) * 4;
+  l.nsel = l.total + 4;
+  l.mx = l.nsel + kPassRows * 4;
+  l.part = l.mx + kPassRows * 4;
+  l.bytes = l.part + kPassRows * 4;
+  return l;
+}
 
 struct Lds {
   size_t xs, xsum, hs, hpart, hrow, total;
@@ -162,10 +198,18 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
 
 // WIDE (k > kPassRows): a unit is one pass of at most kPassRows of an
 // expert's rows (pass blockIdx.z), and only those rows are staged.
-template <bool WIDE>
+// RPL > 0 (k <= kPassRows, E <= 512): every workgroup first runs the router
+// dispatch itself (route_block, RPL candidates per lane) on the logits, so
+// the routing needs no launch of its own; the results are identical in every
+// workgroup, and workgroup (0, 0) writes them out for the combine.
+template <bool WIDE, int RPL>
 __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
+  static_assert(!(WIDE && RPL > 0), "the in-kernel dispatch covers one pass of rows");
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_src[kPassRows], s_dst[kPassRows];
+  constexpr int kRS = RPL > 0 ? kPassRows * SDV_MAX_TOPK : 1;
+  __shared__ int32_t s_r_idx[kRS], s_r_union[kRS], s_r_off[kRS + 1], s_r_row[kRS], s_r_slot[kRS], s_r_nu;
+  __shared__ float s_r_w[kRS];
   const int H = a.H, GA = a.GA, GB = a.GB, k = a.k;
   const int kr = WIDE ? kPassRows : k;  // rows of the LDS staging; row kr is all zero
   const Lds L = expert_lds(kr, H);
@@ -187,12 +231,53 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // are staged, in x-row order; the unit's rows pick theirs through s_src.
   const int G = H >> 6;
   int nxt = k * G;
-  constexpr int kThreads = 64 * kWaves;
+  constexpr int kThreads = kExpertThreads;
   uint4 xv[8];
   if constexpr (!WIDE) {
     const uint4* xp = reinterpret_cast<const uint4*>(a.x) + (size_t)min(tid, nxt - 1) * 8;
 #pragma unroll
     for (int q = 0; q < 8; ++q) xv[q] = xp[q];
+  }
+
+  // ---- the router dispatch in the workgroup (RPL > 0)
+  const int32_t* rt_union = a.union_ids;
+  const int32_t* rt_nu = a.n_union;
+  const int32_t* rt_off = a.pair_off;
+  const int32_t* rt_row = a.pair_row;
+  const int32_t* rt_slot = a.pair_slot;
+  if constexpr (RPL > 0) {
+    const RouteScratchLayout rl = route_scratch(a.E);
+    const RouteSmem sm{s_r_idx,
+                       reinterpret_cast<uint32_t*>(smem + rl.rowmask),
+                       reinterpret_cast<int32_t*>(smem + rl.cnt),
+                       reinterpret_cast<int32_t*>(smem + rl.wave),
+                       reinterpret_cast<int32_t*>(smem + rl.total),
+                       reinterpret_cast<uint64_t*>(smem + rl.cand),
+                       reinterpret_cast<int32_t*>(smem + rl.nsel),
+                       reinterpret_cast<float*>(smem + rl.mx),
+                       reinterpret_cast<float*>(smem + rl.part),
+                       reinterpret_cast<uint64_t*>(smem + rl.pool)};
+    const RouteArgs ra{a.logits, k, a.E, a.topk, a.mode, a.renorm, s_r_idx, s_r_w, s_r_union, &s_r_nu,
+                       s_r_off, s_r_row, s_r_slot};
+    route_block<RPL, kExpertThreads>(ra, sm);
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      const int kt = k * a.topk;
+      for (int t = tid; t < kt; t += kExpertThreads) {
+        a.r_idx[t] = s_r_idx[t];
+        a.r_w[t] = s_r_w[t];
+        a.r_union[t] = s_r_union[t];
+        a.r_row[t] = s_r_row[t];
+        a.r_slot[t] = s_r_slot[t];
+      }
+      for (int t = tid; t <= kt; t += kExpertThreads) a.r_off[t] = s_r_off[t];
+      if (tid == 0) *a.r_nu = s_r_nu;
+    }
+    rt_union = s_r_union;
+    rt_nu = &s_r_nu;
+    rt_off = s_r_off;
+    rt_row = s_r_row;
+    rt_slot = s_r_slot;
   }
 
   // ---- unit: a union expert's rows, or the shared expert's k rows.  The
@@ -216,10 +301,10 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
       if (nrows <= 0) return;
     }
   } else {
-    int nu = __builtin_amdgcn_readfirstlane(*a.n_union);
-    int e0 = __builtin_amdgcn_readfirstlane(a.union_ids[u]);
-    int q0 = __builtin_amdgcn_readfirstlane(a.pair_off[u]);
-    int q1 = __builtin_amdgcn_readfirstlane(a.pair_off[u + 1]);
+    int nu = __builtin_amdgcn_readfirstlane(*rt_nu);
+    int e0 = __builtin_amdgcn_readfirstlane(rt_union[u]);
+    int q0 = __builtin_amdgcn_readfirstlane(rt_off[u]);
+    int q1 = __builtin_amdgcn_readfirstlane(rt_off[u + 1]);
     asm volatile("" : "+s"(nu), "+s"(e0), "+s"(q0), "+s"(q1));  // all four in flight together
     if (u >= nu || e0 < 0 || e0 >= a.E) return;
     if (q0 < 0 || q1 <= q0 || q1 > k * a.topk) return;
@@ -268,12 +353,12 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // (every lane loads, at a clamped index in [p0, p0 + nrows); the shared
   // unit's are not used).
   const int pq = p0 + min(tid, nrows - 1);
-  const int pr = a.pair_row[pq], ps = a.pair_slot[pq];
+  const int pr = rt_row[pq], ps = rt_slot[pq];
   // WIDE: the x rows of this pass's rows only, staged in pass order (the
   // pair rows are loaded first: the x addresses depend on them)
   auto x_src = [&](int i) {  // x row of staged row i
     if (shared) return pass0 + i;
-    const int r = a.pair_row[p0 + i];
+    const int r = rt_row[p0 + i];
     return min(max(r, 0), k - 1);
   };
   if constexpr (WIDE) {
@@ -423,16 +508,20 @@ int expert_slices(int I) { return (I + kSlice - 1) / kSlice; }
 
 size_t expert_lds_bytes(int k, int H) { return expert_lds(k < kPassRows ? k : kPassRows, H).total; }
 
+size_t expert_partial_bytes(int k, int topk, int H, int I) {
+  return (size_t)expert_slices(I) * k * (topk + 1) * H * 4;
+}
+
 namespace {
 
 // Raise the kernel's dynamic LDS limit once per process (the largest size
 // asked for so far; the attribute is per function, not per device).
-template <bool WIDE>
+template <bool WIDE, int RPL>
 hipError_t raise_lds_limit(size_t lds) {
   static std::atomic<size_t> lds_limit{65536};
   size_t cur = lds_limit.load(std::memory_order_relaxed);
   if (lds > cur) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_experts_kernel<WIDE>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_experts_kernel<WIDE, RPL>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
@@ -441,17 +530,17 @@ hipError_t raise_lds_limit(size_t lds) {
   return hipSuccess;
 }
 
-}  // namespace
-
-size_t expert_partial_bytes(int k, int topk, int H, int I) {
-  return (size_t)expert_slices(I) * k * (topk + 1) * H * 4;
+template <bool WIDE, int RPL>
+hipError_t launch_experts(const ExpertArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  const hipError_t err = raise_lds_limit<WIDE, RPL>(lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((moe_experts_kernel<WIDE, RPL>), grid, dim3(kExpertThreads), lds, st, a);
+  return hipGetLastError();
 }
 
-hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn,
-                              const void* x, const int32_t* union_ids, const int32_t* n_union,
-                              const int32_t* pair_off, const int32_t* pair_row, const int32_t* pair_slot, int k,
-                              int topk, float* partial, hipStream_t st) {
-  ExpertArgs a;
+ExpertArgs expert_args(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn, const void* x,
+                       int k, int topk, float* partial) {
+  ExpertArgs a{};
   a.gu_codes = static_cast<const uint4*>(gu.codes);
   a.gu_sb = gu.sb;
   a.dn_codes = static_cast<const uint4*>(dn.codes);
@@ -461,11 +550,6 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
   a.sdn_codes = sdn ? static_cast<const uint4*>(sdn->codes) : nullptr;
   a.sdn_sb = sdn ? sdn->sb : nullptr;
   a.x = static_cast<const uint16_t*>(x);
-  a.union_ids = union_ids;
-  a.n_union = n_union;
-  a.pair_off = pair_off;
-  a.pair_row = pair_row;
-  a.pair_slot = pair_slot;
   a.E = gu.E;
   a.H = gu.K;
   a.I = dn.K;
@@ -478,19 +562,75 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
   a.S = expert_slices(a.I);
   a.partial = partial;
   a.partial_bytes = (uint32_t)expert_partial_bytes(k, topk, a.H, a.I);
+  return a;
+}
+
+}  // namespace
+
+hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn,
+                              const void* x, const int32_t* union_ids, const int32_t* n_union,
+                              const int32_t* pair_off, const int32_t* pair_row, const int32_t* pair_slot, int k,
+                              int topk, float* partial, hipStream_t st) {
+  ExpertArgs a = expert_args(gu, dn, sgu, sdn, x, k, topk, partial);
+  a.union_ids = union_ids;
+  a.n_union = n_union;
+  a.pair_off = pair_off;
+  a.pair_row = pair_row;
+  a.pair_slot = pair_slot;
   const size_t lds = expert_lds_bytes(k, a.H);
   const int units = k * topk + (sgu ? 1 : 0);
   if (k > kPassRows) {
-    const hipError_t err = raise_lds_limit<true>(lds);
-    if (err != hipSuccess) return err;
     const int passes = (k + kPassRows - 1) / kPassRows;
-    hipLaunchKernelGGL(moe_experts_kernel<true>, dim3(a.S, units, passes), dim3(64 * kWaves), lds, st, a);
-  } else {
-    const hipError_t err = raise_lds_limit<false>(lds);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(moe_experts_kernel<false>, dim3(a.S, units), dim3(64 * kWaves), lds, st, a);
+    return launch_experts<true, 0>(a, dim3(a.S, units, passes), lds, st);
   }
-  return hipGetLastError();
+  return launch_experts<false, 0>(a, dim3(a.S, units), lds, st);
+}
+
+// Whether the router dispatch runs inside the expert kernel: one pass of
+// rows and at most one expert per thread of its workgroup.
+bool route_in_experts(int k, int E) { return k <= kPassRows && E <= kExpertThreads; }
+
+size_t route_experts_lds_bytes(int k, int E, int H) {
+  const size_t a = expert_lds_bytes(k, H), b = route_scratch(E).bytes;
+  return a > b ? a : b;
+}
+
+hipError_t route_launch(const float* logits, int k, int E, int topk, int mode, int renorm, int32_t* idx, float* w,
+                        int32_t* union_ids, int32_t* n_union, int32_t* pair_off, int32_t* pair_row,
+                        int32_t* pair_slot, hipStream_t st);
+
+hipError_t moe_route_experts_launch(const float* logits, int mode, int renorm, const sdv_q4t& gu,
+                                    const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn, const void* x, int k,
+                                    int topk, int32_t* idx, float* w, int32_t* union_ids, int32_t* n_union,
+                                    int32_t* pair_off, int32_t* pair_row, int32_t* pair_slot, float* partial,
+                                    hipStream_t st) {
+  const int E = gu.E;
+  if (!route_in_experts(k, E)) {
+    // two launches: the router dispatch, then the experts reading its outputs
+    const hipError_t e = route_launch(logits, k, E, topk, mode, renorm, idx, w, union_ids, n_union, pair_off,
+                                      pair_row, pair_slot, st);
+    if (e != hipSuccess) return e;
+    return moe_experts_launch(gu, dn, sgu, sdn, x, union_ids, n_union, pair_off, pair_row, pair_slot, k, topk,
+                              partial, st);
+  }
+  ExpertArgs a = expert_args(gu, dn, sgu, sdn, x, k, topk, partial);
+  a.logits = logits;
+  a.mode = mode;
+  a.renorm = renorm;
+  a.r_idx = idx;
+  a.r_w = w;
+  a.r_union = union_ids;
+  a.r_nu = n_union;
+  a.r_off = pair_off;
+  a.r_row = pair_row;
+  a.r_slot = pair_slot;
+  const size_t lds = route_experts_lds_bytes(k, E, a.H);
+  const dim3 grid(a.S, k * topk + (sgu ? 1 : 0));
+  const int per_lane = (E + 63) / 64;
+  if (per_lane <= 1) return launch_experts<false, 1>(a, grid, lds, st);
+  if (per_lane <= 2) return launch_experts<false, 2>(a, grid, lds, st);
+  if (per_lane <= 4) return launch_experts<false, 4>(a, grid, lds, st);
+  return launch_experts<false, 8>(a, grid, lds, st);
 }
 
 }  // namespace sdv

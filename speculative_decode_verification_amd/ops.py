@@ -15,7 +15,7 @@ from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, FMT_AFFINE_Q3, FMT_A
                    GATE_SILU, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ3, SdvQ4,
                    SdvQ4T, SdvQ8_0, check, lib)
 
-__all__ = ["Q4Weight", "Q8Weight", "Q3Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "FMT_AFFINE_Q3", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_combine_k",
+__all__ = ["Q4Weight", "Q8Weight", "Q3Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "FMT_AFFINE_Q3", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_experts_k", "moe_route_experts_k", "moe_combine_k",
            "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_gated_norm_k",
            "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
@@ -321,6 +321,43 @@ def moe_experts_k(gate_up, down, x, route, k, topk, shared_gate_up=None, shared_
     return partial
 
 
+def _route_experts_args(logits, score_mode, renorm, gate_up, down, x, route, topk, shared_gate_up, shared_down,
+                        partial):
+    k, E = logits.shape
+    if E != gate_up.E:
+        raise ValueError(f"logits have {E} experts, the bank {gate_up.E}")
+    kt = k * topk
+    dev = gate_up.device
+    H, I = gate_up.K, gate_up.N // 2
+    need = lib().sdv_moe_experts_partial_bytes(k, topk, H, I) // 4
+    return [_need(logits, "logits", torch.float32, k * E, dev), score_mode, int(bool(renorm)),
+            gate_up.desc, down.desc, _need(x, "x", x.dtype, k * H, dev), k, topk,
+            shared_gate_up.desc if shared_gate_up is not None else None,
+            shared_down.desc if shared_down is not None else None,
+            _need(route.idx, "idx", torch.int32, kt, dev), _need(route.w, "w", torch.float32, kt, dev),
+            _need(route.union_ids, "union_ids", torch.int32, kt, dev),
+            _need(route.n_union, "n_union", torch.int32, 1, dev),
+            _need(route.pair_off, "pair_off", torch.int32, kt + 1, dev),
+            _need(route.pair_row, "pair_row", torch.int32, kt, dev),
+            _need(route.pair_slot, "pair_slot", torch.int32, kt, dev),
+            _need(partial, "partial", torch.float32, need, dev), _stream(partial)]
+
+
+def moe_route_experts_k(logits, score_mode, renorm, gate_up, down, x, topk, shared_gate_up=None, shared_down=None,
+                        route=None, partial=None):
+    """moe_route_k and moe_experts_k as one call (one launch when k <= 9 and
+    E <= 512).  Returns (route, partial), equal bit for bit to the two calls'."""
+    k = logits.shape[0]
+    H, I = gate_up.K, gate_up.N // 2
+    if route is None:
+        route = route_buffers(k, topk, gate_up.device)
+    if partial is None:
+        partial = experts_partial(k, topk, H, I, gate_up.device)
+    check(lib().sdv_moe_route_experts_k(*_route_experts_args(logits, score_mode, renorm, gate_up, down, x, route,
+                                                             topk, shared_gate_up, shared_down, partial)))
+    return route, partial
+
+
 def _combine_sliced_args(partial, route, shared_logit, has_shared, I, out):
     S, k, tp1, H = partial.shape
     topk = tp1 - 1
@@ -601,6 +638,13 @@ def bind_gather_qmv_k(bank, mode, act, route, k, topk, out, shared=None, shared_
 def bind_moe_experts_k(gate_up, down, x, route, k, topk, shared_gate_up, shared_down, partial):
     return BoundCall("sdv_moe_experts_k",
                      _experts_args(gate_up, down, x, route, k, topk, shared_gate_up, shared_down, partial))
+
+
+def bind_moe_route_experts_k(logits, score_mode, renorm, gate_up, down, x, route, topk, shared_gate_up, shared_down,
+                             partial):
+    return BoundCall("sdv_moe_route_experts_k",
+                     _route_experts_args(logits, score_mode, renorm, gate_up, down, x, route, topk, shared_gate_up,
+                                         shared_down, partial))
 
 
 def bind_moe_combine_sliced_k(partial, route, I, has_shared, shared_logit, out):

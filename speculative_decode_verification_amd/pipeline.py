@@ -22,15 +22,20 @@ from ._lib import MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX
 
 class MoeLayer:
     def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None,
-                 fuse_shared=True, fused_experts=None):
+                 fuse_shared=True, fused_experts=None, route_in_experts=False):
         """fused_experts: the one-launch expert kernel (affine Q4 weights);
         None picks it for affine-Q4 weights and the two gathered launches
-        otherwise (Q8_0)."""
+        otherwise (Q8_0, Q3).  route_in_experts: with the fused expert
+        kernel, the router dispatch runs in one call with it
+        (sdv_moe_route_experts_k) rather than in a launch of its own.  Off by
+        default: every expert workgroup then waits for its own dispatch, which
+        costs more than the separate launch at 512 experts and nine rows."""
         self.gate_up, self.down = gate_up, down
         weights = [w for w in (gate_up, down, shared_gate_up, shared_down) if w is not None]
         if fused_experts is None:
             fused_experts = all(w.fmt == ops.FMT_AFFINE_Q4 for w in weights)
         self.fused_experts = fused_experts
+        self.route_in_experts = bool(fused_experts and route_in_experts)
         self.shared_gate_up, self.shared_down = shared_gate_up, shared_down
         self.fused_shared = (fuse_shared and shared_gate_up is not None and
                              (shared_gate_up.N, shared_gate_up.K, shared_gate_up.fmt) ==
@@ -62,10 +67,16 @@ class MoeLayer:
         list of (name, call) pairs to run in order."""
         if self.fused_experts:
             has = self.shared_gate_up is not None
-            return [("route", ops.bind_moe_route_k(logits, self.topk, self.score_mode, self.renorm, self.route)),
-                    ("experts", ops.bind_moe_experts_k(self.gate_up, self.down, x, self.route, self.k, self.topk,
-                                                       self.shared_gate_up, self.shared_down, self.xpartial)),
-                    ("combine", ops.bind_moe_combine_sliced_k(self.xpartial, self.route, self.I, has,
+            if self.route_in_experts:
+                calls = [("experts", ops.bind_moe_route_experts_k(logits, self.score_mode, self.renorm, self.gate_up,
+                                                                  self.down, x, self.route, self.topk,
+                                                                  self.shared_gate_up, self.shared_down,
+                                                                  self.xpartial))]
+            else:
+                calls = [("route", ops.bind_moe_route_k(logits, self.topk, self.score_mode, self.renorm, self.route)),
+                         ("experts", ops.bind_moe_experts_k(self.gate_up, self.down, x, self.route, self.k, self.topk,
+                                                            self.shared_gate_up, self.shared_down, self.xpartial))]
+            return calls + [("combine", ops.bind_moe_combine_sliced_k(self.xpartial, self.route, self.I, has,
                                                               z if has else None, self.y))]
         fs = self.fused_shared
         sg = dict(shared=self.shared_gate_up, shared_act=x, shared_out=self.sh_h) if fs else {}
@@ -84,6 +95,11 @@ class MoeLayer:
 
     def __call__(self, x, logits, z=None):
         """x: bf16 bits [k, H] (int16); logits fp32 [k, E]; z fp32 [k] or None."""
+        if self.route_in_experts:
+            has = self.shared_gate_up is not None
+            ops.moe_route_experts_k(logits, self.score_mode, self.renorm, self.gate_up, self.down, x, self.topk,
+                                    self.shared_gate_up, self.shared_down, route=self.route, partial=self.xpartial)
+            return ops.moe_combine_sliced_k(self.xpartial, self.route, self.I, has, z if has else None, out=self.y)
         ops.moe_route_k(logits, self.topk, self.score_mode, self.renorm, out=self.route)
         if self.fused_experts:
             has = self.shared_gate_up is not None
