@@ -54,8 +54,8 @@ def log(*a):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="flashnext_k9",
                    choices=["flashnext_k9", "flashnext_k16", "flashnext_k32"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
@@ -502,18 +502,28 @@ def main():
     unions = wl.unions()
 
     per_step = len(wl.calls[0]) * wl.layers + 2 * len(wl.gdn) + 1
-    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + per_step + 1 + 9)  # 9: the dense widths
+    # the dominant kernel's events, one mark per step boundary, the breakdown
+    # pass and the dense widths
+    timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + args.steps + 1 + per_step + 1 + 9)
     log(f"timing events on the launch stream (HIP runtime {timer.path})")
     events = []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start = timer.start()
+    marks = [t_start]
     for s in range(args.steps):
         wl.step(args.warmup + s, timer=timer, events=events)
-    t_end = timer.stop()
+        marks.append(timer.stop())
+    t_end = marks[-1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = timer.elapsed_us(t_start, t_end) / 1e3
+    step_us = sorted(timer.elapsed_us(a, b) for a, b in zip(marks[:-1], marks[1:]))
+    pct = lambda q: step_us[min(len(step_us) - 1, int(q * len(step_us)))]
+    # rows/s of single steps: the median, and p10 / p90 (p10 of rows/s is the
+    # p90 of step time)
+    step_rows = {"median": round(k / (pct(0.5) * 1e-6), 1), "p10": round(k / (pct(0.9) * 1e-6), 1),
+                 "p90": round(k / (pct(0.1) * 1e-6), 1)}
     ms_step = ms_total / args.steps
     rows_per_s = k * args.steps / (ms_total / 1e3)
     step_bytes = wl.step_bytes(unions)
@@ -571,6 +581,7 @@ def main():
                    "gdn_heads": [wl.gs.hv, wl.gs.hk, wl.gs.dk], "vocab": wl.vocab,
                    "mean_union": round(sum(unions) / len(unions), 2),
                    "bytes_per_step": step_bytes},
+        "step_rows_per_s": step_rows,
         "hbm_gbs_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac_step": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

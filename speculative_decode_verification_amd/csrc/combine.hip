@@ -71,10 +71,20 @@ __global__ __launch_bounds__(256) void combine_sliced_kernel(SlicedArgs a) {
   __shared__ float s_p[kSlotsMax][64];
   const int r = blockIdx.y;
   const int col = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int n = min(blockIdx.x * 64 + col, a.H - 1);  // columns past H re-read the last one
+  const int n = min((int)blockIdx.x * 64 + col, a.H - 1);  // columns past H re-read the last one
   const size_t slice_stride = (size_t)a.k * (a.topk + 1) * a.H;
   const float* pr = a.partial + (size_t)r * (a.topk + 1) * a.H + n;
   const int nslots = a.topk + (a.has_shared ? 1 : 0);
+  // the row's expert indices and weights (lane c of wave 0 holds slot c),
+  // loaded before the partial outputs so that the slot chain below waits on
+  // no load of its own
+  int slot_idx = -1;
+  float slot_w = 0.0f;
+  if (q == 0) {
+    const int c = min(col, a.topk - 1);
+    slot_idx = a.idx[r * a.topk + c];
+    slot_w = a.w[r * a.topk + c];
+  }
   float v[kSlotsPerThread][S];
 #pragma unroll
   for (int c = 0; c < kSlotsPerThread; ++c) {
@@ -82,6 +92,7 @@ __global__ __launch_bounds__(256) void combine_sliced_kernel(SlicedArgs a) {
 #pragma unroll
     for (int j = 0; j < S; ++j) v[c][j] = pr[j * slice_stride + (size_t)s * a.H];
   }
+  const float zl = a.shared_logit ? a.shared_logit[r] : 0.0f;  // issued after the partial loads
 #pragma unroll
   for (int c = 0; c < kSlotsPerThread; ++c) {
     const int s = q + kSlotGroups * c;
@@ -93,19 +104,22 @@ __global__ __launch_bounds__(256) void combine_sliced_kernel(SlicedArgs a) {
     }
   }
   __syncthreads();
-  if (q != 0 || blockIdx.x * 64 + col >= a.H) return;
+  if (q != 0) return;
+  const float gate = a.shared_logit ? sigmoidf_(zl) : 1.0f;
   float acc = 0.0f;
-  for (int s = 0; s < nslots; ++s) {
-    float ws;
-    if (s < a.topk) {
-      if (a.idx[r * a.topk + s] < 0) continue;
-      ws = a.w[r * a.topk + s];
-    } else {
-      ws = a.shared_logit ? sigmoidf_(a.shared_logit[r]) : 1.0f;
+#pragma unroll
+  for (int s = 0; s < kSlotsMax; ++s) {
+    if (s < nslots) {
+      if (s < a.topk) {
+        const int e = __builtin_amdgcn_readlane(slot_idx, s);
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(slot_w), s));
+        if (e >= 0) acc = fmaf(ws, s_p[s][col], acc);
+      } else {
+        acc = fmaf(gate, s_p[s][col], acc);
+      }
     }
-    acc = fmaf(ws, s_p[s][col], acc);
   }
-  a.y[(size_t)r * a.H + n] = acc;
+  if ((int)blockIdx.x * 64 + col < a.H) a.y[(size_t)r * a.H + n] = acc;
 }
 
 }  // namespace
