@@ -252,17 +252,16 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, const RouteSmem&
     // first, ties to the lower index
     const int nsel = sm.nsel[r];
     const bool has = lane < nsel;
-    int slot = lane;
-    uint64_t key = 0;
-    if (has) {
-      key = sm.cand[(r) * SDV_MAX_TOPK + (lane)];
-      // all the row's candidate reads are issued together (at most
-      // SDV_MAX_TOPK, the unused ones predicated off)
-      int rank = 0;
+    // all SDV_MAX_TOPK entries of the row are read unconditionally, so the
+    // reads issue back to back; entries at or past nsel are masked out
+    uint64_t ck[SDV_MAX_TOPK];
 #pragma unroll
-      for (int c = 0; c < SDV_MAX_TOPK; ++c) rank += (c < nsel && sm.cand[(r) * SDV_MAX_TOPK + (c)] > key) ? 1 : 0;
-      slot = rank;
-    }
+    for (int c = 0; c < SDV_MAX_TOPK; ++c) ck[c] = sm.cand[(r) * SDV_MAX_TOPK + c];
+    const uint64_t key = has ? sm.cand[(r) * SDV_MAX_TOPK + min(lane, SDV_MAX_TOPK - 1)] : 0ull;
+    int rank = 0;
+#pragma unroll
+    for (int c = 0; c < SDV_MAX_TOPK; ++c) rank += (c < nsel && ck[c] > key) ? 1 : 0;
+    const int slot = has ? rank : lane;
     const float v = key_value(key);
     float p;
     if (a.mode == SDV_ROUTE_SOFTMAX) {
