@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 METRIC = "verified rows/s and achieved HBM GB/s (% of peak) for k-row Q4 verify + GDN"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 DOMINANT = "experts"
 # the dominant kernel is bracketed by timing events in every SAMPLE_EVERY-th
 # layer of each timed step: each event pair adds a few microseconds of idle
@@ -73,7 +74,7 @@ def kernel_source_hash():
     """Hash of the dominant kernel's sources: a counter summary taken on other
     sources no longer describes it."""
     h = hashlib.sha256()
-    for f in ("moe_experts.hip", "q4_core.h", "common.h"):
+    for f in ("moe_experts.hip", "q4_core.h", "common.h", "route_core.h"):
         with open(os.path.join(ROOT, "speculative_decode_verification_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -429,8 +430,12 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
             torch.cuda.synchronize()
             us = timer.elapsed_us(a, b) / (reps * len(Ws))
             nbytes = wbytes + k * (2 * K + 4 * N)
+            # algorithmic flops 2 k N K against the dense bf16 matrix-core
+            # peak (the products run on bf16 MFMA)
+            tflops = 2.0 * k * N * K / us / 1e6
             res[f"k{k}"] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
-                            "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3)}
+                            "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3),
+                            "tflops": round(tflops, 2), "frac_mfma_bf16": round(tflops / PEAK_BF16_TFLOPS, 4)}
         return res
 
     Ws = [ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(1, DENSE_W, l), 1, N, K, dev)).tiled()
