@@ -262,6 +262,40 @@ def test_experts_validation(lib):
     assert experts(lib, gu9, q4t(E=E, N=H, K=1088, codes=P + 0x2000000, sb=P + 0x3000000)) == L.SDV_ERANGE
 
 
+def route_experts(lib, gu, dn, k=2, topk=4, mode=L.ROUTE_SIGMOID, logits=P + 0x6000000, x=P + 0x3000000,
+                  partial=P + 0x4000000, outs=None, sgu=None, sdn=None):
+    outs = outs if outs is not None else [P + 0x800000 + 0x10000 * i for i in range(7)]
+    return lib.sdv_moe_route_experts_k(logits, mode, 1, ctypes.byref(gu), ctypes.byref(dn), x, k, topk,
+                                       ctypes.byref(sgu) if sgu is not None else None,
+                                       ctypes.byref(sdn) if sdn is not None else None, *outs, partial, None)
+
+
+def test_route_experts_validation(lib):
+    """The one-call router dispatch + expert MLP: the router's checks, the
+    expert kernel's checks, and aliasing across both sets of buffers, all
+    before any launch."""
+    E, H, I = 8, 256, 128
+    gu = q4t(E=E, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000)
+    dn = q4t(E=E, N=H, K=I, fused=0, codes=P + 0x200000, sb=P + 0x300000)
+    assert route_experts(lib, gu, dn, mode=7) == L.SDV_EINVAL
+    assert route_experts(lib, gu, dn, k=33) == L.SDV_EWIDTH
+    assert route_experts(lib, gu, dn, topk=9) == L.SDV_ERANGE                            # topk > E
+    big = q4t(E=1025, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000)
+    assert route_experts(lib, big, dn) == L.SDV_ERANGE                                    # E above 1024
+    assert route_experts(lib, q4t(E=E, N=2 * I, K=H, fused=0), dn) == L.SDV_ELAYOUT       # gate/up not fused
+    assert route_experts(lib, gu, dn, logits=0) == L.SDV_EINVAL
+    assert route_experts(lib, gu, dn, x=0) == L.SDV_EINVAL
+    outs = [P + 0x800000 + 0x10000 * i for i in range(7)]
+    assert route_experts(lib, gu, dn, outs=outs[:3] + [0] + outs[4:]) == L.SDV_EINVAL    # n_union NULL
+    assert route_experts(lib, gu, dn, logits=outs[1]) == L.SDV_EALIAS                     # w over the logits
+    assert route_experts(lib, gu, dn, partial=P + 0x80) == L.SDV_EALIAS                   # over the gate/up codes
+    assert route_experts(lib, gu, dn, partial=outs[2]) == L.SDV_EALIAS                    # over union_ids
+    assert route_experts(lib, gu, dn, outs=[outs[0]] * 7) == L.SDV_EALIAS                 # outputs overlap
+    q8 = q4t(E=E, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000)
+    q8.format = L.FMT_Q8_0
+    assert route_experts(lib, q8, dn) == L.SDV_ELAYOUT                                    # affine Q4 only
+
+
 def test_combine_sliced_validation(lib):
     f = lib.sdv_moe_combine_sliced_k
     part, idx, w, y = P, P + 0x1000000, P + 0x1100000, P + 0x1200000
