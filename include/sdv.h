@@ -470,6 +470,29 @@ SDV_API int sdv_gdn_gated_norm_k(const float *y, const float *z, const float *w,
                                  int gate_act, float eps, float *out, sdv_stream_t stream);
 
 /*
+ * sdv_gdn_verify_prep_norm_k -- sdv_gdn_verify_prep_k and sdv_gdn_gated_norm_k
+ * in one launch (Flash-Next plan, "2.1 Gated DeltaNet": preparation,
+ * recurrence and the gated RMSNorm tail of one layer).  The last of each
+ * head's Dv / 16 workgroups to finish applies that head's norm; y, the
+ * snapshots, the window and out equal those of the two separate calls bit
+ * for bit.
+ *   S_in ... snaps  as sdv_gdn_verify_prep_k (y is still written);
+ *   z, norm_w, gate_act, norm_eps, out  as sdv_gdn_gated_norm_k's z, w,
+ *   gate_act, eps, out;
+ *   counters  device int32 [Hv], owned by the caller: all zero before the
+ *             first call, and every completed call leaves them zero.
+ *             Calls that overlap in time must not share counters.
+ * Dk = Dv in {64, 128}.  No output may overlap an input or another output.
+ * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE (eps, norm_eps), EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_verify_prep_norm_k(const float *S_in, const float *qkv, const float *hist, const float *conv_w,
+                                       const float *a, const float *b, const float *A_log, const float *dt_bias,
+                                       int k, int Hv, int Hk, int Dk, int Dv, int conv_act, float eps,
+                                       float *window, float *y, float *const *snaps, const float *z,
+                                       const float *norm_w, int gate_act, float norm_eps, float *out,
+                                       int32_t *counters, sdv_stream_t stream);
+
+/*
  * sdv_verify_accept_workspace_bytes -- device workspace needed by
  * sdv_verify_accept_k for k rows of V logits (0 for k outside 1..9 or V < 1).
  */

@@ -19,7 +19,7 @@ EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_q8_0
            "sdv_qmv_k", "sdv_moe_route_k",
            "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_route_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
            "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
-           "sdv_gdn_rollback_copy", "sdv_gdn_prepare_k", "sdv_gdn_verify_prep_k",
+           "sdv_gdn_rollback_copy", "sdv_gdn_prepare_k", "sdv_gdn_verify_prep_k", "sdv_gdn_verify_prep_norm_k",
            "sdv_gdn_gated_norm_k",
            "sdv_verify_accept_workspace_bytes", "sdv_verify_accept_k",
            "sdv_status_string", "sdv_last_error", "sdv_build_info")
@@ -83,6 +83,8 @@ _SIGS = {
                           _P, _P, _P, _P, _P, _P, _P],
     "sdv_gdn_verify_prep_k": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
                               ctypes.POINTER(_P), _P],
+    "sdv_gdn_verify_prep_norm_k": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                                   ctypes.POINTER(_P), _P, _P, _I, ctypes.c_float, _P, _P, _P],
     "sdv_gdn_gated_norm_k": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P],
     "sdv_verify_accept_workspace_bytes": [_I, _I],
     "sdv_verify_accept_k": [_P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],

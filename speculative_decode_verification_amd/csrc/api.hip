@@ -58,7 +58,9 @@ hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const 
 hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
                                   const float* ga, const float* gb, const float* A_log, const float* dt_bias, int k,
                                   int Hv, int Hk, int D, int conv_act, float eps, float* window, float* y,
-                                  float* const* snaps, hipStream_t st);
+                                  float* const* snaps, hipStream_t st, const float* nz = nullptr,
+                                  const float* nw = nullptr, int gate_act = 0, float neps = 0.0f,
+                                  float* out = nullptr, int32_t* cnt = nullptr);
 }  // namespace sdv
 
 namespace {
@@ -728,10 +730,16 @@ int sdv_gdn_prepare_k(const float* qkv, const float* hist, const float* conv_w, 
                     "sdv_gdn_prepare_k launch");
 }
 
-int sdv_gdn_verify_prep_k(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
-                          const float* a, const float* b, const float* A_log, const float* dt_bias, int k, int Hv,
-                          int Hk, int Dk, int Dv, int conv_act, float eps, float* window, float* y,
-                          float* const* snaps, sdv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks of the preparation + recurrence call; fills the output and
+// input ranges for the alias check (outs: y, window, snapshots; ins: 8).
+int check_verify_prep(const float* S_in, const float* qkv, const float* hist, const float* conv_w, const float* a,
+                      const float* b, const float* A_log, const float* dt_bias, int k, int Hv, int Hk, int Dk,
+                      int Dv, int conv_act, float eps, float* window, float* y, float* const* snaps, Range* outs,
+                      Range* ins) {
   int st;
   if ((st = check_width(k))) return st;
   if (Hv <= 0 || Hk <= 0) return fail(SDV_EINVAL, "Hv=%d Hk=%d must be positive", Hv, Hk);
@@ -751,25 +759,70 @@ int sdv_gdn_verify_prep_k(const float* S_in, const float* qkv, const float* hist
   if (!snaps) return fail(SDV_EINVAL, "snaps is NULL");
   const size_t C = 2 * (size_t)Hk * Dk + (size_t)Hv * Dv;
   const size_t state = (size_t)Hv * Dv * Dk * 4;
-  Range ins[] = {{S_in, state, "S_in"},
-                 {qkv, (size_t)k * C * 4, "qkv"},
-                 {hist, 3 * C * 4, "hist"},
-                 {conv_w, C * 16, "conv_w"},
-                 {a, (size_t)k * Hv * 4, "a"},
-                 {b, (size_t)k * Hv * 4, "b"},
-                 {A_log, (size_t)Hv * 4, "A_log"},
-                 {dt_bias, (size_t)Hv * 4, "dt_bias"}};
-  Range outs[SDV_MAX_ROWS + 2];
+  ins[0] = {S_in, state, "S_in"};
+  ins[1] = {qkv, (size_t)k * C * 4, "qkv"};
+  ins[2] = {hist, 3 * C * 4, "hist"};
+  ins[3] = {conv_w, C * 16, "conv_w"};
+  ins[4] = {a, (size_t)k * Hv * 4, "a"};
+  ins[5] = {b, (size_t)k * Hv * 4, "b"};
+  ins[6] = {A_log, (size_t)Hv * 4, "A_log"};
+  ins[7] = {dt_bias, (size_t)Hv * 4, "dt_bias"};
   outs[0] = {y, (size_t)k * Hv * Dv * 4, "y"};
   outs[1] = {window, (size_t)(k + 3) * C * 4, "window"};
   for (int t = 0; t < k; ++t) {
     if ((st = check_ptr(snaps[t], kSnapNames[t]))) return st;
     outs[t + 2] = {snaps[t], state, kSnapNames[t]};
   }
+  return SDV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdv_gdn_verify_prep_k(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
+                          const float* a, const float* b, const float* A_log, const float* dt_bias, int k, int Hv,
+                          int Hk, int Dk, int Dv, int conv_act, float eps, float* window, float* y,
+                          float* const* snaps, sdv_stream_t stream) {
+  int st;
+  Range outs[SDV_MAX_ROWS + 2], ins[8];
+  if ((st = check_verify_prep(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk, Dv, conv_act, eps,
+                              window, y, snaps, outs, ins)))
+    return st;
   if ((st = check_alias(outs, k + 2, ins, 8))) return st;
   return hip_status(sdv::gdn_verify_prep_launch(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk,
                                                 conv_act, eps, window, y, snaps, (hipStream_t)stream),
                     "sdv_gdn_verify_prep_k launch");
+}
+
+int sdv_gdn_verify_prep_norm_k(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
+                               const float* a, const float* b, const float* A_log, const float* dt_bias, int k,
+                               int Hv, int Hk, int Dk, int Dv, int conv_act, float eps, float* window, float* y,
+                               float* const* snaps, const float* z, const float* norm_w, int gate_act,
+                               float norm_eps, float* out, int32_t* counters, sdv_stream_t stream) {
+  int st;
+  Range outs[SDV_MAX_ROWS + 4], ins[11];
+  if ((st = check_verify_prep(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk, Dv, conv_act, eps,
+                              window, y, snaps, outs, ins)))
+    return st;
+  if (gate_act != SDV_GATE_SIGMOID && gate_act != SDV_GATE_SILU) return fail(SDV_EINVAL, "gate_act=%d", gate_act);
+  if (!(norm_eps >= 0.0f && norm_eps <= 3.4e38f))
+    return fail(SDV_ERANGE, "norm_eps=%g must be finite and >= 0", (double)norm_eps);
+  if ((st = check_ptr(z, "z"))) return st;
+  if ((st = check_ptr(norm_w, "norm_w"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  if (!counters) return fail(SDV_EINVAL, "counters is NULL");
+  if ((uintptr_t)counters % 4) return fail(SDV_EINVAL, "counters is not 4-byte aligned");
+  const size_t n = (size_t)k * Hv * Dv * 4;
+  outs[k + 2] = {out, n, "out"};
+  outs[k + 3] = {counters, (size_t)Hv * 4, "counters"};
+  ins[8] = {z, n, "z"};
+  ins[9] = {norm_w, (size_t)Dv * 4, "norm_w"};
+  if ((st = check_alias(outs, k + 4, ins, 10))) return st;
+  return hip_status(sdv::gdn_verify_prep_launch(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk,
+                                                conv_act, eps, window, y, snaps, (hipStream_t)stream, z, norm_w,
+                                                gate_act, norm_eps, out, counters),
+                    "sdv_gdn_verify_prep_norm_k launch");
 }
 
 int sdv_gdn_gated_norm_k(const float* y, const float* z, const float* w, int k, int Hv, int Dv, int gate_act,

@@ -47,6 +47,13 @@ struct GdnArgs {
   int C, conv_act;
   float eps;
   float* window;  // [k + 3][C]
+  // with the gated output norm in the kernel (NORM)
+  const float* nz;  // gate input [k][Hv][Dv]
+  const float* nw;  // norm weight [Dv]
+  int gate_act;
+  float neps;
+  float* out;       // [k][Hv][Dv]
+  int32_t* cnt;     // [Hv], zero between calls
 };
 
 constexpr int kRowsPerBlock = 16;  // 16 value rows x 16 lanes = 256 threads
@@ -72,9 +79,19 @@ __device__ __forceinline__ void for_rows(std::integer_sequence<int, T...>, int k
 // are written by the first block of each qk head, the v columns by their
 // block.  Blocks of one qk head are placed on one XCD when the block count
 // allows, so its repeated q/k inputs are L2 hits.
-template <int DK, bool LDS_KQ, bool PREP, int R>
+//
+// NORM (with PREP): the gated output norm of each head is applied by the
+// last of the head's Dv / 16 workgroups to finish.  Every workgroup stores
+// its y rows with agent-scope coherent stores and waits for them to
+// complete before it counts itself in on the head's counter; the workgroup
+// that brings the count to Dv / 16 resets it to zero and then reads the
+// head's y rows back (coherent loads) and runs the same arithmetic as
+// gdn_gated_norm_kernel, in the same order, so the output equals the
+// separate launch's bit for bit.  No workgroup waits for another.
+template <int DK, bool LDS_KQ, bool PREP, int R, bool NORM = false>
 __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   static_assert(!PREP || LDS_KQ, "the in-kernel preparation stages through LDS");
+  static_assert(!NORM || PREP, "the output norm needs whole heads per workgroup group (Dv = Dk)");
   constexpr int NV4 = DK / 64;  // float4 per lane
   __shared__ float4 s_k[LDS_KQ ? R * DK / 4 : 1];
   __shared__ float4 s_q[LDS_KQ ? R * DK / 4 : 1];
@@ -319,7 +336,12 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
         o = fmaf(S[j].w, qt[j].w, o);
       }
       o = row16_sum(o);
-      if (sub == 0) a.y[((long)t * a.Hv + h) * Dv + i] = o;
+      if (sub == 0) {
+        if constexpr (NORM)
+          __hip_atomic_store(a.y + ((long)t * a.Hv + h) * Dv + i, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          a.y[((long)t * a.Hv + h) * Dv + i] = o;
+      }
       // snapshots are written once and read back at most once, after the call:
       // streaming (nontemporal) stores keep them from displacing cached data
       f32x4* dst = reinterpret_cast<f32x4*>(a.snaps[t] + (size_t)row * DK);
@@ -331,6 +353,43 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     }
   };
   for_rows(std::make_integer_sequence<int, R>{}, a.k, row_step);
+
+  if constexpr (NORM) {
+    __shared__ int s_last;
+    __shared__ float s_np[256 / 64];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int n = __hip_atomic_fetch_add(a.cnt + h0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = n == DK / kRowsPerBlock - 1;
+      if (last) __hip_atomic_store(a.cnt + h0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last) {
+      // 256 / DK rows of the head at a time, DK threads per row; wave w of
+      // a row sums the squares of elements 64 w .. 64 w + 63
+      constexpr int kRowsAtOnce = 256 / DK, kWavesPerRow = DK / 64;
+      const int d = threadIdx.x % DK, rsub = threadIdx.x / DK, wave = threadIdx.x >> 6;
+      const float wd = a.nw[d];
+      for (int t0 = 0; t0 < a.k; t0 += kRowsAtOnce) {
+        const int t = min(t0 + rsub, a.k - 1);
+        const size_t base = ((size_t)t * a.Hv + h0) * DK;
+        const float yv = __hip_atomic_load(a.y + base + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float z = a.nz[base + d];
+        const float ws = gdn_wave_sum(yv * yv);
+        if ((threadIdx.x & 63) == 0) s_np[wave] = ws;
+        __syncthreads();
+        float ss = s_np[rsub * kWavesPerRow];
+#pragma unroll
+        for (int w2 = 1; w2 < kWavesPerRow; ++w2) ss = ss + s_np[rsub * kWavesPerRow + w2];
+        const float nv = yv / sqrtf(ss / (float)DK + a.neps);
+        const float gate = a.gate_act == SDV_GATE_SILU ? siluf_(z) : sigmoidf_(z);
+        if (t0 + rsub < a.k) a.out[base + d] = nv * wd * gate;
+        __syncthreads();  // s_np is rewritten by the next rows
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -371,8 +430,15 @@ hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const 
 hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
                                   const float* ga, const float* gb, const float* A_log, const float* dt_bias, int k,
                                   int Hv, int Hk, int D, int conv_act, float eps, float* window, float* y,
-                                  float* const* snaps, hipStream_t st) {
+                                  float* const* snaps, hipStream_t st, const float* nz, const float* nw,
+                                  int gate_act, float neps, float* out, int32_t* cnt) {
   GdnArgs a{};
+  a.nz = nz;
+  a.nw = nw;
+  a.gate_act = gate_act;
+  a.neps = neps;
+  a.out = out;
+  a.cnt = cnt;
   a.S_in = S_in;
   a.k = k;
   a.Hv = Hv;
@@ -397,6 +463,11 @@ hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const flo
   auto kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows> : gdn_verify_kernel<64, true, true, kPassRows>)
                       : (wide ? gdn_verify_kernel<128, true, true, kWideRows>
                               : gdn_verify_kernel<128, true, true, kPassRows>);
+  if (out)
+    kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows, true>
+                           : gdn_verify_kernel<64, true, true, kPassRows, true>)
+                   : (wide ? gdn_verify_kernel<128, true, true, kWideRows, true>
+                           : gdn_verify_kernel<128, true, true, kPassRows, true>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
 }

@@ -16,7 +16,7 @@ from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, FMT_AFFINE_Q3, FMT_A
                    SdvQ4T, SdvQ8_0, check, lib)
 
 __all__ = ["Q4Weight", "Q8Weight", "Q3Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "FMT_AFFINE_Q3", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_experts_k", "moe_route_experts_k", "moe_combine_k",
-           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_gated_norm_k",
+           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_verify_prep_norm_k", "gdn_norm_counters", "gdn_gated_norm_k",
            "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
 
@@ -522,6 +522,46 @@ def bind_gdn_verify_prep_k(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, sn
                            eps=1e-6):
     return BoundCall("sdv_gdn_verify_prep_k", _verify_prep_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk,
                                                                 snaps, window, y, conv_act, eps))
+
+
+def _verify_prep_norm_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y, conv_act, eps, z,
+                           norm_w, gate_act, norm_eps, out, counters):
+    args = _verify_prep_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y, conv_act, eps)
+    Hv, Dv, _ = S_in.shape
+    n = qkv.shape[0] * Hv * Dv
+    dev = S_in.device
+    f = torch.float32
+    return args[:-1] + [_need(z, "z", f, n, dev), _need(norm_w, "norm_w", f, Dv, dev), gate_act,
+                        ctypes.c_float(norm_eps), _need(out, "out", f, n, dev),
+                        _need(counters, "counters", torch.int32, Hv, dev), args[-1]]
+
+
+def gdn_norm_counters(Hv, device):
+    """The per-head counters of gdn_verify_prep_norm_k (zero; every call leaves them zero)."""
+    return torch.zeros((Hv,), dtype=torch.int32, device=device)
+
+
+def gdn_verify_prep_norm_k(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, z, norm_w, counters,
+                           y=None, out=None, conv_act=CONV_NONE, eps=1e-6, gate_act=GATE_SIGMOID, norm_eps=1e-6):
+    """gdn_verify_prep_k and gdn_gated_norm_k in one launch: returns (y, out),
+    both [k, Hv, Dv]; ``counters`` int32 [Hv] (gdn_norm_counters)."""
+    Hv, Dv, _ = S_in.shape
+    k = qkv.shape[0]
+    if y is None:
+        y = torch.empty((k, Hv, Dv), dtype=torch.float32, device=S_in.device)
+    if out is None:
+        out = torch.empty((k, Hv, Dv), dtype=torch.float32, device=S_in.device)
+    check(lib().sdv_gdn_verify_prep_norm_k(*_verify_prep_norm_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk,
+                                                                   snaps, window, y, conv_act, eps, z, norm_w,
+                                                                   gate_act, norm_eps, out, counters)))
+    return y, out
+
+
+def bind_gdn_verify_prep_norm_k(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y, z, norm_w, out,
+                                counters, conv_act=CONV_NONE, eps=1e-6, gate_act=GATE_SIGMOID, norm_eps=1e-6):
+    return BoundCall("sdv_gdn_verify_prep_norm_k",
+                     _verify_prep_norm_args(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, Hk, snaps, window, y,
+                                            conv_act, eps, z, norm_w, gate_act, norm_eps, out, counters))
 
 
 def gdn_gated_norm_k(y, z, w, gate_act=GATE_SIGMOID, eps=1e-6, out=None):

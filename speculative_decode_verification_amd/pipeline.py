@@ -262,6 +262,37 @@ class GdnLayer:
         self._fp_cache = {}
         return self
 
+    def verify_from_proj_norm(self, qkv, a, b, z, norm_w, out, gate_act=ops.GATE_SIGMOID, norm_eps=1e-6):
+        """``verify_from_proj`` with the gated output norm in the same launch:
+        out [rows, Hv, Dv] = rmsnorm(y) * norm_w * act(z); returns (y, out)."""
+        conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+        rows = qkv.shape[0]
+        self.snap_ids = [i for i in range(len(self.slots)) if i != self.live][:rows]
+        y = self.y[:rows]
+        ops.gdn_verify_prep_norm_k(self.state, qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk,
+                                   [self.slots[i] for i in self.snap_ids], self.windows[self.win][:rows + 3], z,
+                                   norm_w, self._counters(), y, out, act, eps, gate_act, norm_eps)
+        self.prepped = True
+        return y, out
+
+    def _counters(self):
+        if getattr(self, "norm_counters", None) is None:
+            self.norm_counters = ops.gdn_norm_counters(self.Hv, self.state.device)
+        return self.norm_counters
+
+    def bind_from_proj_norm(self, qkv, a, b, z, norm_w, out, gate_act=ops.GATE_SIGMOID, norm_eps=1e-6):
+        """``bind_from_proj`` with the gated output norm in the same launch
+        (``run_from_proj_bound`` then also writes out)."""
+        self.bind_from_proj(qkv, a, b)
+        conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
+        rows = qkv.shape[0]
+        ids0 = self._fp_snaps[self.live][0]
+        self._fp_template = ops.bind_gdn_verify_prep_norm_k(
+            self.state, qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk, [self.slots[i] for i in ids0],
+            self.windows[self.win][:rows + 3], self.y[:rows], z, norm_w, out, self._counters(), act, eps, gate_act,
+            norm_eps)
+        return self
+
     def run_from_proj_bound(self):
         key = (self.live, self.win, self.hist.data_ptr())
         call = self._fp_cache.get(key)
