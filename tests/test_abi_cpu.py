@@ -486,3 +486,32 @@ def test_verify_prep_validation(lib):
     assert lib.sdv_last_error().decode() == "output window overlaps input hist"
     assert verify_prep(lib, y=P + 0x800000 + 4096) == L.SDV_EALIAS              # y over window
     assert verify_prep(lib, y=P + 0x5000000 + 64) == L.SDV_EALIAS               # y over a snapshot
+
+
+def verify_prep_norm(lib, k=2, Hv=4, Hk=2, D=64, gate=0, neps=1e-6, **over):
+    ptr = dict(S_in=P + 0x4000000, qkv=P, hist=P + 0x100000, conv_w=P + 0x200000, a=P + 0x300000, b=P + 0x310000,
+               A_log=P + 0x320000, dt_bias=P + 0x330000, window=P + 0x800000, y=P + 0x900000, z=P + 0xA00000,
+               norm_w=P + 0xB00000, out=P + 0xC00000, counters=P + 0xD00000)
+    ptr.update(over)
+    snaps = [P + 0x5000000 + 0x1000000 * t for t in range(k)]
+    arr = (ctypes.c_void_p * k)(*snaps)
+    return lib.sdv_gdn_verify_prep_norm_k(ptr["S_in"], ptr["qkv"], ptr["hist"], ptr["conv_w"], ptr["a"], ptr["b"],
+                                          ptr["A_log"], ptr["dt_bias"], k, Hv, Hk, D, D, 0, 1e-6, ptr["window"],
+                                          ptr["y"], arr, ptr["z"], ptr["norm_w"], gate, neps, ptr["out"],
+                                          ptr["counters"], None)
+
+
+def test_verify_prep_norm_validation(lib):
+    """The preparation + recurrence checks, the norm's checks, and aliasing
+    of out and the counters, before any launch."""
+    assert verify_prep_norm(lib, k=33) == L.SDV_EWIDTH
+    assert verify_prep_norm(lib, Hv=5) == L.SDV_ELAYOUT
+    assert verify_prep_norm(lib, gate=5) == L.SDV_EINVAL
+    assert verify_prep_norm(lib, neps=float("inf")) == L.SDV_ERANGE
+    assert verify_prep_norm(lib, z=0) == L.SDV_EINVAL
+    assert verify_prep_norm(lib, counters=0) == L.SDV_EINVAL
+    assert verify_prep_norm(lib, counters=P + 0xD00002) == L.SDV_EINVAL                  # misaligned
+    assert verify_prep_norm(lib, out=P + 0xA00000 + 64) == L.SDV_EALIAS                 # out over z
+    assert verify_prep_norm(lib, out=P + 0x900000) == L.SDV_EALIAS                       # out over y
+    assert verify_prep_norm(lib, counters=P + 0xB00000) == L.SDV_EALIAS                  # counters over norm_w
+    assert verify_prep_norm(lib, counters=P + 0xC00000 + 4) == L.SDV_EALIAS              # counters over out
