@@ -322,7 +322,9 @@ SDV_API int sdv_moe_experts_k(const sdv_q4t *gate_up, const sdv_q4t *down, const
  * launch: every expert workgroup runs the router dispatch itself on the
  * logits (identical results everywhere; workgroup (0, 0) writes them), so the
  * routing needs no launch of its own.  Otherwise it runs the two launches.
- * The outputs equal those of the two calls bit for bit.
+ * The outputs equal those of the two calls bit for bit.  Every expert
+ * workgroup then waits for the whole dispatch before its first weight load:
+ * at 512 experts and nine rows the two separate launches are faster.
  *   logits, score_mode, renorm  as sdv_moe_route_k (E = gate_up->E)
  *   idx, w, union_ids, n_union, pair_off, pair_row, pair_slot  outputs, as sdv_moe_route_k
  *   gate_up, down, x, shared_gate_up, shared_down, partial  as sdv_moe_experts_k
@@ -475,7 +477,9 @@ SDV_API int sdv_gdn_gated_norm_k(const float *y, const float *z, const float *w,
  * recurrence and the gated RMSNorm tail of one layer).  The last of each
  * head's Dv / 16 workgroups to finish applies that head's norm; y, the
  * snapshots, the window and out equal those of the two separate calls bit
- * for bit.
+ * for bit.  A workgroup counts itself in only after all of its stores have
+ * completed, snapshots included, so at the 48-head layer shape the two
+ * separate launches are faster.
  *   S_in ... snaps  as sdv_gdn_verify_prep_k (y is still written);
  *   z, norm_w, gate_act, norm_eps, out  as sdv_gdn_gated_norm_k's z, w,
  *   gate_act, eps, out;
