@@ -303,6 +303,38 @@ def check_moe_combine_closed_form(ref):
         assert np.allclose(out["y"][r], 0.5 * sh, rtol=1e-14, atol=1e-15)
 
 
+def check_shared_gate_closed_form(ref):
+    """The shared expert's scalar gate at z = +-ln 3: sigma(ln 3) = 3 / (3 + 1)
+    = 3/4 and sigma(-ln 3) = 1/4.  With no routed contribution the output is
+    exactly that fraction of the shared expert's output, through the combine
+    alone and through the whole layer; at z = +-40 the gate is 1 and 0 to
+    below 1e-17."""
+    H, I, k = 64, 64, 2
+    ln3 = math.log(3.0)
+    rng = np.random.default_rng(41)
+    sh = rng.standard_normal((k, H))
+    part = np.zeros((k, 3, H))
+    w = rng.uniform(0.1, 1.0, (k, 3))
+    y = ref.combine(part, w, shared=sh, z=np.array([ln3, -ln3]))
+    assert np.allclose(y[0], 0.75 * sh[0], rtol=1e-15, atol=1e-16)
+    assert np.allclose(y[1], 0.25 * sh[1], rtol=1e-15, atol=1e-16)
+    y = ref.combine(part, w, shared=sh, z=np.array([40.0, -40.0]))
+    assert np.allclose(y[0], sh[0], rtol=1e-15, atol=0.0)
+    assert np.max(np.abs(y[1])) <= 1e-17 * np.max(np.abs(sh[1]))
+    gu = _tiny_bank(7, 1, 2, 2 * I, H)
+    dn = _tiny_bank(7, 2, 2, H, I)
+    x = ref.bf16_to_f64(synth.moe_layer_inputs(7, 0, k, H, 2)["x"])
+    l = np.array([[0.0, ln3], [ln3, 0.0]])
+    zero = (np.zeros((2 * I, H // 8), np.uint32), np.zeros((2 * I, 1), np.uint16), np.zeros((2 * I, 1), np.uint16))
+    zdn = (np.zeros((H, I // 8), np.uint32), np.zeros((H, 1), np.uint16), np.zeros((H, 1), np.uint16))
+    sgu, sdn = gu[1], dn[0]
+    out = ref.moe_verify(x, l, lambda e: ref.dequant(*zero), lambda e: ref.dequant(*zdn), 2, "sigmoid", True,
+                         z=np.array([-ln3, ln3]), shared_gate_up=ref.dequant(*sgu), shared_down=ref.dequant(*sdn))
+    for r, frac in ((0, 0.25), (1, 0.75)):
+        s = ref.qmv(*sdn, ref.swiglu(ref.qmv(*sgu, x[r:r + 1])[0])[None, :])[0]
+        assert np.allclose(out["y"][r], frac * s, rtol=1e-14, atol=1e-15)
+
+
 def check_moe_identical_experts(ref):
     """Identical experts: the weights sum to one, so the layer output is the
     single expert's output (softmax over all experts with top-k = E, or any
@@ -698,8 +730,21 @@ def check_gated_norm(ref):
     assert np.array_equal(ref.gdn_gated_norm(y, np.zeros_like(z), w, act="silu"), np.zeros_like(y))
     half = ref.gdn_gated_norm(y, np.zeros_like(z), w, act="sigmoid")
     assert np.allclose(half, 0.5 * ref.gdn_gated_norm(y, big, w), rtol=1e-12)
-    sig = ref.gdn_gated_norm(y, z, np.ones(6), act="sigmoid")
-    assert np.allclose(sig, ref.gdn_gated_norm(y, big, np.ones(6)) / (1.0 + np.exp(-z)), rtol=1e-12)
+    # Both gates at z = +-ln 3 on a constant row: sigmoid gives 3/4 and 1/4,
+    # silu(z) = z * sigmoid(z) gives (3/4) ln 3 and -(1/4) ln 3.
+    ln3 = math.log(3.0)
+    n0 = -2.5 / math.sqrt(6.25 + 0.25)
+    zz = np.array([ln3, -ln3]).reshape(2, 1, 1) * np.ones((2, 1, 6))
+    cc = np.full((2, 1, 6), -2.5)
+    sig = ref.gdn_gated_norm(cc, zz, np.ones(6), act="sigmoid", eps=0.25)
+    assert np.allclose(sig[0], 0.75 * n0, rtol=1e-14) and np.allclose(sig[1], 0.25 * n0, rtol=1e-14)
+    sl = ref.gdn_gated_norm(cc, zz, np.ones(6), act="silu", eps=0.25)
+    assert np.allclose(sl[0], 0.75 * ln3 * n0, rtol=1e-14) and np.allclose(sl[1], -0.25 * ln3 * n0, rtol=1e-14)
+    # silu's limits: silu(z) / z -> 1 for large z, -> 0 for large -z.
+    zl = np.full((2, 1, 6), 40.0)
+    zl[1] = -40.0
+    sl = ref.gdn_gated_norm(cc, zl, np.ones(6), act="silu", eps=0.25)
+    assert np.allclose(sl[0], 40.0 * n0, rtol=1e-15) and np.max(np.abs(sl[1])) < 1e-15
 
 
 def half_exact(bits):
@@ -813,7 +858,7 @@ ALL_CHECKS = [
     check_bf16_decode, check_unpack_roundtrip, check_qmv_bruteforce, check_qmv_integer_exact,
     check_qmv_closed_forms, check_qmv_rows_independent, check_route_selection, check_route_weights,
     check_union_pairs, check_swiglu, check_moe_pairs_dense, check_moe_single_expert,
-    check_moe_combine_closed_form, check_moe_identical_experts, check_gdn_bruteforce,
+    check_moe_combine_closed_form, check_shared_gate_closed_form, check_moe_identical_experts, check_gdn_bruteforce,
     check_gdn_no_write, check_gdn_scalar, check_gdn_basis, check_gdn_retrieval,
     check_gdn_head_groups, check_gdn_rollback, check_sample_greedy, check_sample_noise_rounding,
     check_sample_gumbel_is_softmax, check_accept_cases, check_verify_cycle_rollback,

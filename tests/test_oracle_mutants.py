@@ -56,6 +56,12 @@ MUTANTS = {
     "norm_sum_not_mean": ("n = y / np.sqrt((y * y).mean(axis=-1, keepdims=True) + eps)", "n = y / np.sqrt((y * y).sum(axis=-1, keepdims=True) + eps)"),
     "norm_weight_dropped": ("return n * np.asarray(w, dtype=np.float64) * gate", "return n * gate"),
     "gate_silu_for_sigmoid": ("        gate = 1.0 / (1.0 + np.exp(-z))", "        gate = silu(z)"),
+    "shared_gate_sign": ("return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))",
+                         "return 1.0 / (1.0 + np.exp(np.asarray(z, dtype=np.float64)))"),
+    "shared_gate_squared": ("gate = np.ones(k) if z is None else _sigmoid(z)",
+                            "gate = np.ones(k) if z is None else 2.0 * _sigmoid(z) ** 2"),
+    "norm_silu_sign": ("        gate = silu(z)", "        gate = -silu(z)"),
+    "norm_silu_mirrored": ("        gate = silu(z)", "        gate = silu(-z)"),
     "q8_block_64": ("Q8_BLOCK = 32", "Q8_BLOCK = 64"),
     "fp16_exponent_bias": ("np.exp2((e - 15)", "np.exp2((e - 16)"),
     "fp16_subnormal_scale": ("f * 2.0 ** -24", "f * 2.0 ** -25"),
