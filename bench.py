@@ -61,6 +61,8 @@ def parse_args():
                    choices=["flashnext_k9", "flashnext_k16", "flashnext_k32"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel instrumented pass")
+    p.add_argument("--no-extra-configs", action="store_true",
+                   help="skip the 256-expert MoE and 36-layer GDN lines (the other configurations' widths)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (PMC counter calibration)")
     return p.parse_args()
@@ -218,9 +220,11 @@ class Workload:
 
     def step(self, s, timer=None, events=None, per_kernel=None):
         """One verify step over all layers, the acceptance of the block, then
-        rollback of every GDN layer to the accepted prefix.  With ``events``,
-        the dominant kernel of every layer is bracketed by timer events; with
-        ``per_kernel``, every launch is."""
+        rollback of every GDN layer to the accepted prefix the device
+        returned (its count is read back, one host synchronisation per step,
+        as a decoding loop must).  With ``events``, the dominant kernel of
+        every layer is bracketed by timer events; with ``per_kernel``, every
+        launch is."""
         def run(name, l, call):
             if per_kernel is not None or (events is not None and name == DOMINANT and l % SAMPLE_EVERY == 0):
                 a = timer.start()
@@ -237,10 +241,12 @@ class Workload:
                 run("gdn_norm", l, g[0].run_tail_bound)
             for name, call in self.calls[l]:
                 run(name, l, call)
-        accept, n, _, _ = self.blocks[s % len(self.blocks)]
+        accept, _, _, _ = self.blocks[s % len(self.blocks)]
         run("accept", self.layers, accept)
+        n = int(self.cycle.accepted.item())
         for gl, _ in self.gdn.values():
             gl.rollback(n + 1)
+        return n
 
     def check_acceptance(self):
         """Every block's device acceptance equals its planted count (outside timing)."""
@@ -272,21 +278,22 @@ class Workload:
         if name == "shared_down":
             return q4_bytes(H, I) + k * I * 4 + k * H * 4
         if name == "experts":
-            # union experts (and the shared expert) read once, x read once,
-            # the per-slice partial outputs of every used slot written once
-            S = (I + 127) // 128
+            # algorithmic: the union experts (and the shared expert) read
+            # once, x read once, one output per used (row, slot) written once
+            # (the method's per-slot expert outputs); the kernel's per-slice
+            # partial sums beyond that are design traffic (design_bytes)
             used = k * topk + sh * k
-            b = ((U + sh) * (q4_bytes(2 * I, H) + q4_bytes(H, I)) + k * H * 2 + U * 4 * 2
-                 + S * used * H * 4)
+            b = (U + sh) * (q4_bytes(2 * I, H) + q4_bytes(H, I)) + k * H * 2 + used * H * 4
             if self.moe[l][0].route_in_experts:
                 # the router dispatch in the same launch: logits in, its
                 # outputs out (as the "route" launch)
                 b += k * E * 4 + k * topk * 4 * 5 + 8
             return b
         if name == "combine" and self.moe[l][0].fused_experts:
-            S = (I + 127) // 128
+            # algorithmic: the per-slot outputs in, slot weights and indices,
+            # the shared gate logits, y out
             used = k * topk + sh * k
-            return S * used * H * 4 + k * topk * 8 + k * 4 + k * H * 4
+            return used * H * 4 + k * topk * 8 + k * 4 + k * H * 4
         if name == "combine":
             return k * topk * H * 4 + k * topk * 4 + k * H * 4 + k * 4 + k * H * 4
         if name == "gdn":
@@ -301,6 +308,18 @@ class Workload:
             g = self.gs
             return (3 * k * g.hv * g.dv + g.dv) * 4
         raise KeyError(name)
+
+    def design_bytes(self, name, l):
+        """HBM bytes a launch moves beyond its algorithmic bytes because of
+        this design: the fused expert kernel writes one partial sum per
+        128-wide intermediate slice of each used slot (S of them instead of
+        one), and the combine reads them all back."""
+        if name not in ("experts", "combine") or not self.moe[l][0].fused_experts:
+            return 0
+        S = (self.I + 127) // 128
+        sh = 1 if self.moe[l][0].fused_shared else 0
+        used = self.k * self.topk + sh * self.k
+        return (S - 1) * used * self.H * 4
 
     def step_bytes(self, unions):
         total = 0
@@ -336,7 +355,7 @@ def traffic_for(kernel_hash):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
+def cpu_baseline(k=9, min_seconds=10.0, max_layers=16, threads_limit=None):
     """The CPU oracle on a bounded sample of the same workload: whole layers
     (MoE: route, union, gate/up, down, shared expert, combine, with the layer's
     union experts regenerated on the host before timing; GDN: preparation,
@@ -351,6 +370,10 @@ def cpu_baseline(k=9, min_seconds=10.0, max_layers=16):
     cfg = configs.C4
     m, gs = cfg.moe, cfg.gdn
     E, H, I, topk = m.experts, m.hidden, m.inter, m.topk
+    if threads_limit is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads_limit):
+            return cpu_baseline(k, min_seconds, max_layers)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -467,6 +490,133 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
     return {"shape": [N, K], "weights": n_weights, "widths": out, "q8_0": q8, "q3": q3}
 
 
+def ornith_moe(dev, widths=tuple(range(2, 10)), reps=3):
+    """The 256-expert MoE verify (hidden 2048, intermediate 512, softmax
+    top-8, no shared expert) over 40 distinct layer banks (18.1 GB of affine
+    Q4, rotated so no layer's experts are cache-resident): router dispatch,
+    the fused expert kernel and the combine of every layer, back to back, at
+    each width.  Reported per width: the layer time, verified rows/s of a
+    40-layer step, the mean union, algorithmic bytes per layer (the union
+    experts once, x, logits and y) as GB/s, and the expert kernel alone
+    (events around its launches in a separate pass)."""
+    import torch
+    import synth
+    from synth import configs
+    from synth import device as sdev
+    from synth.inputs import DOWN, GATEUP
+    from speculative_decode_verification_amd import ops, pipeline
+    cfg = configs.C2
+    m = cfg.moe
+    E, H, I, topk = m.experts, m.hidden, m.inter, m.topk
+    banks = []
+    for l in range(cfg.layers):
+        gu = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, GATEUP, l), E, 2 * I, H, dev)).tiled(True)
+        dn = ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg.cid, DOWN, l), E, H, I, dev)).tiled()
+        banks.append((gu, dn))
+    ex_bytes = q4_bytes(2 * I, H) + q4_bytes(H, I)
+    out = {}
+    for k in widths:
+        layers, calls = [], []
+        for l, (gu, dn) in enumerate(banks):
+            inp = synth.moe_layer_inputs(cfg.cid, l, k, H, E)
+            x, lg = sdev.upload_bf16(inp["x"], dev), sdev.upload_f32(inp["logits"], dev)
+            layer = pipeline.MoeLayer(gu, dn, k, topk, ops.ROUTE_SOFTMAX, m.renorm)
+            layers.append((layer, x, lg))
+            calls.append(layer.bind(x, lg))
+        for cl in calls:
+            for _, c in cl:
+                c()
+        torch.cuda.synchronize()
+        timer = HipTimer(1 + cfg.layers)
+        a = timer.start()
+        for _ in range(reps):
+            for cl in calls:
+                for _, c in cl:
+                    c()
+        b = timer.stop()
+        torch.cuda.synchronize()
+        us_layer = timer.elapsed_us(a, b) / (reps * cfg.layers)
+        ev = []
+        for cl in calls:
+            for name, c in cl:
+                if name == "experts":
+                    e0 = timer.start()
+                    c()
+                    ev.append((e0, timer.stop()))
+                else:
+                    c()
+        torch.cuda.synchronize()
+        ex_us = sum(timer.elapsed_us(e0, e1) for e0, e1 in ev) / len(ev)
+        timer.close()
+        unions = [int(layer.route.n_union.item()) for layer, _, _ in layers]
+        mu = sum(unions) / len(unions)
+        lb = mu * ex_bytes + k * H * 2 + k * E * 4 + k * H * 4
+        eb = mu * ex_bytes + k * H * 2 + k * topk * H * 4
+        out[f"k{k}"] = {"us_per_layer": round(us_layer, 2),
+                        "rows_per_s_40_layers": round(k / (us_layer * cfg.layers * 1e-6), 1),
+                        "mean_union": round(mu, 2), "bytes_per_layer": round(lb),
+                        "gbs": round(lb / us_layer / 1e3, 1), "frac_hbm": round(lb / us_layer / 1e3 / PEAK_HBM_GBS, 3),
+                        "experts_us": round(ex_us, 2), "experts_frac_hbm": round(eb / ex_us / 1e3 / PEAK_HBM_GBS, 3)}
+        del layers, calls
+    del banks
+    torch.cuda.empty_cache()
+    return {"workload": "ornith_moe: 40 layers x [256 experts: gate/up 1024x2048 + down 2048x512, affine Q4/g64], "
+                        "softmax top-8", "widths": out}
+
+
+def gdn36_chains(dev, widths=tuple(range(1, 10)), steps=16):
+    """The GDN verify of 36 layers (48 v heads, 16 qk heads, Dk = Dv = 128,
+    3 MB of fp32 state per layer, 113 MB in all) at each width: 16-step
+    chains, each step the k-row recurrence with snapshots on every layer,
+    then rollback of every layer to an accepted prefix j ~ U{0..k} by slot
+    selection.  Reported per width: verified rows/s (k rows per 36-layer
+    step), the per-layer time, and algorithmic bytes per layer (the state in,
+    k snapshots out, q, k, v, g, beta in and y out per row) as GB/s."""
+    import torch
+    import synth
+    from synth import configs
+    from synth import device as sdev
+    from speculative_decode_verification_amd import pipeline
+    cfg = configs.C3
+    g = cfg.gdn
+    S0 = [sdev.upload_f32(synth.gdn_state(cfg.cid, l, g.hv, g.dv, g.dk), dev) for l in range(cfg.layers)]
+    out = {}
+    for k in widths:
+        layers = []
+        for l in range(cfg.layers):
+            d = {n: sdev.upload_f32(v, dev)
+                 for n, v in synth.gdn_layer_inputs(cfg.cid, l, k, g.hv, g.hk, g.dk, g.dv).items()}
+            gl = pipeline.GdnLayer(S0[l], k).bind(d["q"], d["k"], d["v"], d["g"], d["beta"])
+            layers.append((gl, d))
+        js = [synth.accepted_prefix(cfg.cid, s, k) for s in range(steps)]
+        for gl, _ in layers:  # warm-up step
+            gl.run_bound()
+        for gl, _ in layers:
+            gl.rollback(js[0])
+        torch.cuda.synchronize()
+        timer = HipTimer(1)
+        a = timer.start()
+        for s in range(steps):
+            for gl, _ in layers:
+                gl.run_bound()
+            for gl, _ in layers:
+                gl.rollback(js[s])
+        b = timer.stop()
+        torch.cuda.synchronize()
+        us = timer.elapsed_us(a, b)
+        timer.close()
+        per_layer = us / (steps * cfg.layers)
+        lb = (k + 1) * g.hv * g.dv * g.dk * 4 + k * (2 * g.hk * g.dk + 2 * g.hv * g.dv + 2 * g.hv) * 4
+        out[f"k{k}"] = {"rows_per_s": round(k * steps / (us * 1e-6), 1), "us_per_layer": round(per_layer, 2),
+                        "bytes_per_layer": lb, "gbs": round(lb / per_layer / 1e3, 1),
+                        "frac_hbm": round(lb / per_layer / 1e3 / PEAK_HBM_GBS, 3),
+                        "accepted_prefixes": js}
+        del layers
+    del S0
+    torch.cuda.empty_cache()
+    return {"workload": "gdn36: 36 layers x state [48,128,128] fp32, 16-step chains with rollback", "widths": out}
+
+
 def copy_probe():
     """A plain device copy of known size, for scaling HBM counters."""
     import torch
@@ -535,6 +685,7 @@ def main():
 
     dom_us = [timer.elapsed_us(a, b) for (_, _, a, b) in events]
     dom_bytes = [wl.kernel_bytes(DOMINANT, l, unions) for (_, l, _, _) in events]
+    dom_design = [wl.design_bytes(DOMINANT, l) for (_, l, _, _) in events]
     dom_avg_us = sum(dom_us) / len(dom_us)
     dom_gbs = sum(dom_bytes) / (sum(dom_us) * 1e-6) / 1e9
     khash = kernel_source_hash()
@@ -563,10 +714,18 @@ def main():
         log("timing the dense 5120 x 5120 projection ...")
         dense = dense_projection(dev, timer)
 
-    cpu = None
+    extra = {}
+    if not args.no_extra_configs:
+        log("timing the 256-expert MoE layers (k = 2..9) ...")
+        extra["ornith_moe"] = ornith_moe(dev)
+        log("timing the 36-layer GDN chains (k = 1..9) ...")
+        extra["gdn36"] = gdn36_chains(dev)
+
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
+        log("timing the CPU oracle on a bounded sample (all host cores, then one) ...")
         cpu = cpu_baseline(k)
+        cpu1 = cpu_baseline(k, min_seconds=10.0, max_layers=2, threads_limit=1)
 
     out = {
         "metric": METRIC,
@@ -594,10 +753,16 @@ def main():
                      "kernel": "moe_experts_kernel (sdv_moe_experts_k: fused gate/up + SwiGLU + down)",
                      "avg_launch_us": round(dom_avg_us, 2),
                      "bytes_per_launch": round(sum(dom_bytes) / len(dom_bytes)),
+                     "design_traffic": {"bytes_per_launch": round(sum(dom_design) / len(dom_design)),
+                                        "what": "per-slice partial sums written beyond one output per used slot "
+                                                "(read back by the combine); not in achieved"},
                      "kernel_source_hash": khash},
         "kernels": breakdown,
         "dense_qmv_k": dense,
         "cpu_baseline": cpu,
+        "cpu_baseline_1core": cpu1,
+        "accepted_count": "read back from the device every timed step (one host synchronisation per step)",
+        **extra,
         "wall_s_timed": round(wall, 3),
         "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "host_cpu": cpu_model()},
     }

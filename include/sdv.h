@@ -3,7 +3,7 @@
  * AMD Instinct MI355X (gfx950).
  *
  * The library computes one verification step of a Gated-DeltaNet / MoE
- * hybrid layer for k = 1..9 draft rows at once:
+ * hybrid layer for k = 1..SDV_MAX_ROWS (32) draft rows at once:
  *
  *   - affine-Q4 (group 64, bf16 scale and bias) multi-row matvec that decodes
  *     each packed weight once for all k rows, dense and gathered-expert
@@ -17,7 +17,7 @@
  *     [Hv, Dv, Dk] state with a snapshot after every row, and rollback to the
  *     accepted prefix by selecting a snapshot (Flash-Next plan QWEN38FLASH.md,
  *     "2.1 Gated DeltaNet"; Red Lite dev45, "What it is": in-kernel snapshots
- *     and pointer-swap rejection).
+ *     and rejection by choosing which state buffer is live, with no copy).
  *
  * Conventions for every entry point
  *   - Return value: SDV_OK (0) or a negative SDV_E* status.  Arguments are
@@ -36,6 +36,14 @@
  *     by a width-1 call (fixed per-output reduction order, independent of k
  *     and of which other rows share an expert).
  *   - bf16 values are passed as their uint16_t bit patterns.
+ *   - Weights: the products (sdv_qmv_k, sdv_gather_qmv_k, sdv_moe_experts_k and
+ *     the calls built on them) read only the tiled sdv_q4t layout, written once
+ *     per weight by sdv_q4_repack (sdv_q8_0_repack, sdv_q3_repack for the other
+ *     formats).  The row-major sdv_q4 is the interchange form those repacks
+ *     read.  In the tiled layout one matrix-core step of a wave reads one
+ *     contiguous 1 KB block of codes plus one 128-byte line holding the 32
+ *     rows' scales and biases; the row-major form would need 32 scattered rows
+ *     and 64 scattered 2-byte loads per step, which measured 2.4-3.8x slower.
  */
 #ifndef SDV_H
 #define SDV_H
@@ -220,7 +228,7 @@ SDV_API int sdv_q4_repack(const sdv_q4 *src, int fused_gateup, void *codes_out, 
  * each weight once and compute each row in the 1-row kernel's order).
  *   W         tiled weight descriptor (host struct, device arrays)
  *   act       device, [k][K]: bf16 bits (act_dtype SDV_ACT_BF16) or fp32 (SDV_ACT_F32)
- *   k         rows, 1..9
+ *   k         rows, 1..SDV_MAX_ROWS
  *   mode      SDV_MODE_PLAIN: y [k][N], needs fused_gateup = 0;
  *             SDV_MODE_GATEUP_SWIGLU: y [k][N/2], needs fused_gateup = 1
  *   y         device fp32 output
@@ -259,8 +267,9 @@ SDV_API int sdv_moe_route_k(const float *logits, int k, int E, int topk, int sco
  * experts: each union expert's weights are decoded once for all rows routed
  * to it (mere.run report, "Exact verification kernels and benchmark
  * admission": gathered expert kernel, affine Q4/group 64, widths 2..9, fused
- * gate/up weights, unsupported layouts rejected; Red Lite dev45: the (expert,
- * row) pairs share one pool encode with a two-input gate/up pipeline).
+ * gate/up weights, unsupported layouts rejected; Red Lite dev45, "What it is":
+ * all (expert, row) pairs of the union go out in one dispatch, gate and up
+ * read together).
  *   bank       tiled weight descriptor, E experts of [N][K]
  *   mode       SDV_MODE_GATEUP_SWIGLU (fused [gate; up] rows, output N/2; needs
  *              fused_gateup = 1) or SDV_MODE_PLAIN (needs fused_gateup = 0)
@@ -290,8 +299,8 @@ SDV_API int sdv_gather_qmv_k(const sdv_q4t *bank, int mode, const void *act, int
  * gate/up with SwiGLU, then the down projection, each union expert's packed
  * weights read once for all rows routed to it (mere.run report, "Exact
  * verification kernels and benchmark admission": gathered expert kernel with
- * fused gate/up weights; Red Lite dev45, "What it is": one pool encode with a
- * two-input gate/up pipeline for the union's (expert, row) pairs; Flash-Next
+ * fused gate/up weights; Red Lite dev45, "What it is": one dispatch for all
+ * of the union's (expert, row) pairs, gate and up read together; Flash-Next
  * plan "2.3 MoE": top-10 of 512 plus one shared expert).  The intermediate
  * dimension is cut into S = ceil(I / 128) slices; workgroup (expert, slice)
  * computes h = silu(gate) * up for its slice and multiplies it by the matching
@@ -318,7 +327,7 @@ SDV_API int sdv_moe_experts_k(const sdv_q4t *gate_up, const sdv_q4t *down, const
 /*
  * sdv_moe_route_experts_k -- sdv_moe_route_k and sdv_moe_experts_k as one
  * call (Red Lite dev45, "What it is": one router dispatch, then the union's
- * (expert, row) pairs in one pool encode).  For k <= 9 and E <= 512 it is one
+ * (expert, row) pairs in one dispatch).  For k <= 9 and E <= 512 it is one
  * launch: every expert workgroup runs the router dispatch itself on the
  * logits (identical results everywhere; workgroup (0, 0) writes them), so the
  * routing needs no launch of its own.  Otherwise it runs the two launches.
@@ -396,8 +405,8 @@ SDV_API int sdv_gdn_verify_k(const float *S_in, const float *q, const float *kk,
 /*
  * sdv_gdn_rollback -- select the state for an accepted prefix of length j
  * (mere.run report: accepted-prefix rollback, every prefix at widths 4, 8, 9;
- * Red Lite dev45 "What it is": a rejected draft is undone by swapping the
- * state pointers with the snapshots).  Host only, no device work:
+ * Red Lite dev45 "What it is": rejection picks which state buffer is live,
+ * nothing is copied).  Host only, no device work:
  *   *selected_slot = 0 (the verify call's S_in) for j = 0, else j (snaps[j-1]).
  * Errors: EINVAL (null), EWIDTH, ERANGE (j outside 0..k).
  */
@@ -498,7 +507,8 @@ SDV_API int sdv_gdn_verify_prep_norm_k(const float *S_in, const float *qkv, cons
 
 /*
  * sdv_verify_accept_workspace_bytes -- device workspace needed by
- * sdv_verify_accept_k for k rows of V logits (0 for k outside 1..9 or V < 1).
+ * sdv_verify_accept_k for k rows of V logits (0 for k outside 1..SDV_MAX_ROWS
+ * or V < 1).
  */
 SDV_API size_t sdv_verify_accept_workspace_bytes(int k, int V);
 

@@ -82,10 +82,11 @@ __device__ __forceinline__ void for_rows(std::integer_sequence<int, T...>, int k
 //
 // NORM (with PREP): the gated output norm of each head is applied by the
 // last of the head's Dv / 16 workgroups to finish.  Every workgroup stores
-// its y rows with agent-scope coherent stores and waits for them to
-// complete before it counts itself in on the head's counter; the workgroup
-// that brings the count to Dv / 16 resets it to zero and then reads the
-// head's y rows back (coherent loads) and runs the same arithmetic as
+// its y rows with agent-scope coherent stores, and every thread issues an
+// agent-scope release fence before the workgroup counts itself in on the
+// head's counter (an acquire-release add); the workgroup
+// that brings the count to Dv / 16 resets it to zero, issues an acquire
+// fence, reads the head's y rows back (coherent loads) and runs the same arithmetic as
 // gdn_gated_norm_kernel, in the same order, so the output equals the
 // separate launch's bit for bit.  No workgroup waits for another.
 template <int DK, bool LDS_KQ, bool PREP, int R, bool NORM = false>
@@ -357,16 +358,20 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   if constexpr (NORM) {
     __shared__ int s_last;
     __shared__ float s_np[256 / 64];
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are complete
+    // Release: every thread's y stores are visible at agent scope before its
+    // workgroup counts itself in; the counter update is acquire-release, and
+    // the last workgroup acquires before it reads the other workgroups' y.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int n = __hip_atomic_fetch_add(a.cnt + h0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int n = __hip_atomic_fetch_add(a.cnt + h0, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       const int last = n == DK / kRowsPerBlock - 1;
       if (last) __hip_atomic_store(a.cnt + h0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last;
     }
     __syncthreads();
     if (s_last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       // 256 / DK rows of the head at a time, DK threads per row; wave w of
       // a row sums the squares of elements 64 w .. 64 w + 63
       constexpr int kRowsAtOnce = 256 / DK, kWavesPerRow = DK / 64;

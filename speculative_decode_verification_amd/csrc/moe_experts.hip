@@ -4,7 +4,7 @@
 // the same slice of its K dimension, writing one partial output per slice.
 //
 // The method reads each union expert's packed weights once for all rows routed
-// to it, with a two-input (gate, up) pipeline and the gathered down projection
+// to it, gate and up read together, then the gathered down projection
 // (mere.run transfer report, "Exact verification kernels and benchmark
 // admission"; Red Lite dev45, "What it is"; Flash-Next plan "2.3 MoE").
 // Splitting the intermediate dimension into slices keeps SwiGLU's output in
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   __shared__ int32_t s_r_idx[kRS], s_r_union[kRS], s_r_off[kRS + 1], s_r_row[kRS], s_r_slot[kRS], s_r_nu;
   __shared__ float s_r_w[kRS];
   const int H = a.H, GA = a.GA, GB = a.GB, k = a.k;
-  const int kr = WIDE ? kPassRows : k;  // rows of the LDS staging; row kr is all zero
+  const int kr = min(k, kPassRows);  // rows of the LDS staging; row kr is all zero
   const Lds L = expert_lds(kr, H);
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   float* xsum = reinterpret_cast<float*>(smem + L.xsum);
@@ -506,8 +506,8 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 
 int expert_slices(int I) { return (I + kSlice - 1) / kSlice; }
 
-// the pass form stages up to kPassRows rows at any width
-size_t expert_lds_bytes(int k, int H) { return expert_lds(kPassRows, H).total; }
+// a unit stages at most min(k, kPassRows) rows (one pass of its rows)
+size_t expert_lds_bytes(int k, int H) { return expert_lds(k < kPassRows ? k : kPassRows, H).total; }
 
 size_t expert_partial_bytes(int k, int topk, int H, int I) {
   return (size_t)expert_slices(I) * k * (topk + 1) * H * 4;

@@ -8,8 +8,8 @@ geometry it rides in the two gathered launches as one more unit; otherwise
 it runs as two dense products.  ``GdnLayer`` keeps a pool of
 k+1 state buffers per layer: the live state and k snapshot slots.  A verify
 call writes the snapshots; rollback to an accepted prefix j only swaps which
-buffer is live (Red Lite dev45, "What it is": pointer swap with the
-snapshots), so no state is copied.
+buffer is live (Red Lite dev45, "What it is": rejection by choosing the
+live buffer), so no state is copied.
 """
 
 import ctypes
@@ -330,8 +330,8 @@ __all__ = ["MoeLayer", "GdnLayer", "MODE_PLAIN", "MODE_GATEUP_SWIGLU", "ROUTE_SO
 class VerifyCycle:
     """Closes a verify step: the acceptance of the block on the device, then
     every GDN layer rolled back to the accepted prefix by selecting its
-    snapshot (Red Lite dev45, "Acceptance" and "What it is": a rejected draft
-    is undone by swapping the state pointers with the snapshots).
+    snapshot (Red Lite dev45, "Acceptance" and "What it is": rejection
+    picks which state buffer is live, nothing is copied).
 
     The accepted count is read back to the host, which holds the slot choice
     of each layer's state pool."""

@@ -196,44 +196,116 @@ def test_fused_experts_unused_slots_untouched():
     assert not (xp[:, :, :topk] == 12345.0).any()
 
 
-def test_ornith_shaped_layer():
-    """256 experts, hidden 2048, intermediate 512, softmax top-8, k = 2..9;
-    the bank is generated on the device and spot-checked against the host
+class _Bank:
+    """One layer's expert bank: generated on the device, with the host
+    generator's experts dequantised for the oracle on demand (cached, so the
+    widths of one test module share them)."""
+
+    def __init__(self, cfg, layer_id, E, H, I):
+        from speculative_decode_verification_amd.ops import Q4Weight
+        self.cfg, self.E, self.H, self.I = cfg, E, H, I
+        self.gkeys = synth.bank_keys(cfg, GATEUP, layer_id)
+        self.dkeys = synth.bank_keys(cfg, DOWN, layer_id)
+        self.gu_d = sdev.q4_bank(self.gkeys, E, 2 * I, H, DEV)
+        self.dn_d = sdev.q4_bank(self.dkeys, E, H, I, DEV)
+        self.gu_w, self.dn_w = Q4Weight(*self.gu_d).tiled(True), Q4Weight(*self.dn_d).tiled()
+        self._g, self._d = {}, {}
+
+    def gmat(self, e):
+        if e not in self._g:
+            self._g[e] = oracle.dequant(*synth.q4_rows(self.gkeys, self.E, 2 * self.I, self.H, expert=e))
+        return self._g[e]
+
+    def dmat(self, e):
+        if e not in self._d:
+            self._d[e] = oracle.dequant(*synth.q4_rows(self.dkeys, self.E, self.H, self.I, expert=e))
+        return self._d[e]
+
+
+ORNITH = dict(E=256, H=2048, I=512, topk=8, cfg=2, layer=0)
+
+
+@pytest.fixture(scope="module")
+def ornith_bank():
+    banner("ornith layer bank fill")
+    o = ORNITH
+    b = _Bank(o["cfg"], o["layer"], o["E"], o["H"], o["I"])
+    for e in (0, 77, 255):
+        host = synth.q4_rows(b.gkeys, b.E, 2 * b.I, b.H, expert=e, row_start=1000, row_count=24)
+        for a, d in zip(host, b.gu_d):
+            dev_rows = to_np(d[e, 1000:1024])
+            assert np.array_equal(dev_rows.view(a.dtype), a), f"bank fill mismatch expert {e}"
+    return b
+
+
+@pytest.mark.parametrize("k", list(range(2, 10)))
+def test_ornith_shaped_layer(ornith_bank, k):
+    """256 experts, hidden 2048, intermediate 512, softmax top-8, every width
+    k = 2..9, on the gathered launches and on the fused expert kernel; the
+    bank is generated on the device and spot-checked against the host
     generator."""
     ops, pipeline = _mods()
-    E, H, I, topk = 256, 2048, 512, 8
-    cfg, layer_id = 2, 0
-    banner("ornith layer bank fill")
-    gkeys = synth.bank_keys(cfg, GATEUP, layer_id)
-    dkeys = synth.bank_keys(cfg, DOWN, layer_id)
-    gu_d = sdev.q4_bank(gkeys, E, 2 * I, H, DEV)
-    dn_d = sdev.q4_bank(dkeys, E, H, I, DEV)
-    for e in (0, 77, 255):
-        host = synth.q4_rows(gkeys, E, 2 * I, H, expert=e, row_start=1000, row_count=24)
-        for a, b in zip(host, gu_d):
-            dev_rows = to_np(b[e, 1000:1024])
-            assert np.array_equal(dev_rows.view(a.dtype), a), f"bank fill mismatch expert {e}"
-    from speculative_decode_verification_amd.ops import Q4Weight
-    gu_w, dn_w = Q4Weight(*gu_d).tiled(True), Q4Weight(*dn_d).tiled()
-    for k in (2, 5, 9):
-        banner(f"ornith layer k={k}")
-        inp = synth.moe_layer_inputs(cfg, layer_id, k, H, E)
-        layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SOFTMAX, False, fused_experts=False)
-        fused = pipeline.MoeLayer(gu_w, dn_w, k, topk, ops.ROUTE_SOFTMAX, False, fused_experts=True)
-        args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV))
-        y = to_np(layer(*args))
-        y_f = to_np(fused(*args))
-        idx, _ = oracle.route(inp["logits"], topk, "softmax", False)
-        used = sorted(set(idx.ravel().tolist()))
-        gmat = {e: oracle.dequant(*synth.q4_rows(gkeys, E, 2 * I, H, expert=e)) for e in used}
-        dmat = {e: oracle.dequant(*synth.q4_rows(dkeys, E, H, I, expert=e)) for e in used}
-        ref = oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], gmat.__getitem__,
-                                dmat.__getitem__, topk, "softmax", False)
-        assert np.array_equal(to_np(layer.route.idx), ref["idx"])
-        assert_close(to_np(layer.h), ref["h"], "h")
-        assert_close(y, ref["y"], "y")
-        assert_close(slot_outputs(fused)[:, :topk], ref["partial"], "fused slot outputs")
-        assert_close(y_f, ref["y"], "fused y")
+    b, o = ornith_bank, ORNITH
+    topk = o["topk"]
+    banner(f"ornith layer k={k}")
+    inp = synth.moe_layer_inputs(o["cfg"], o["layer"], k, b.H, b.E)
+    layer = pipeline.MoeLayer(b.gu_w, b.dn_w, k, topk, ops.ROUTE_SOFTMAX, False, fused_experts=False)
+    fused = pipeline.MoeLayer(b.gu_w, b.dn_w, k, topk, ops.ROUTE_SOFTMAX, False, fused_experts=True)
+    args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV))
+    y = to_np(layer(*args))
+    y_f = to_np(fused(*args))
+    ref = oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], b.gmat, b.dmat, topk, "softmax", False)
+    assert np.array_equal(to_np(layer.route.idx), ref["idx"])
+    assert np.array_equal(to_np(fused.route.idx), ref["idx"])
+    assert int(to_np(fused.route.n_union)[0]) == ref["n_union"]
+    assert_close(to_np(layer.h), ref["h"], "h")
+    assert_close(to_np(layer.partial), ref["partial"], "partial")
+    assert_close(y, ref["y"], "y")
+    assert_close(slot_outputs(fused)[:, :topk], ref["partial"], "fused slot outputs")
+    assert_close(y_f, ref["y"], "fused y")
+
+
+def _width1_rows(ops, pipeline, gu_w, dn_w, inp, k, topk, mode, renorm, sgu_w=None, sdn_w=None, fused=True):
+    """Each row of a k-row layer against its own one-row layer, bit for bit:
+    y, and the slot outputs (with the shared slot) or h and the partials."""
+    sm = ops.ROUTE_SOFTMAX if mode == "softmax" else ops.ROUTE_SIGMOID
+    has_z = sgu_w is not None
+    layer = pipeline.MoeLayer(gu_w, dn_w, k, topk, sm, renorm, sgu_w, sdn_w, fused_experts=fused)
+    args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV),
+            sdev.upload_f32(inp["z"], DEV) if has_z else None)
+    y = to_np(layer(*args))
+    if fused:
+        P = slot_outputs(layer)
+    else:
+        h, part = to_np(layer.h), to_np(layer.partial)
+        sh = to_np(layer.sh_out) if has_z else None
+    one = pipeline.MoeLayer(gu_w, dn_w, 1, topk, sm, renorm, sgu_w, sdn_w, fused_experts=fused)
+    for r in range(k):
+        a1 = (sdev.upload_bf16(inp["x"][r:r + 1], DEV), sdev.upload_f32(inp["logits"][r:r + 1], DEV),
+              sdev.upload_f32(inp["z"][r:r + 1], DEV) if has_z else None)
+        y1 = to_np(one(*a1))
+        assert np.array_equal(y1[0], y[r]), f"y row {r}"
+        if fused:
+            P1 = slot_outputs(one)
+            assert np.array_equal(P1[0, :topk], P[r, :topk]), f"slot outputs row {r}"
+            if has_z:
+                assert np.array_equal(P1[0, topk], P[r, topk]), f"shared slot row {r}"
+        else:
+            assert np.array_equal(to_np(one.h)[0], h[r]), f"h row {r}"
+            assert np.array_equal(to_np(one.partial)[0], part[r]), f"partial row {r}"
+            if has_z:
+                assert np.array_equal(to_np(one.sh_out)[0], sh[r]), f"shared output row {r}"
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_ornith_width9_equals_width1(ornith_bank, fused):
+    """At the 256-expert, 2048 / 512 geometry every row of a nine-row layer
+    equals the same row run alone, bit for bit."""
+    ops, pipeline = _mods()
+    b, o = ornith_bank, ORNITH
+    banner(f"ornith width 9 vs width 1 fused={fused}")
+    inp = synth.moe_layer_inputs(o["cfg"], o["layer"], 9, b.H, b.E)
+    _width1_rows(ops, pipeline, b.gu_w, b.dn_w, inp, 9, o["topk"], "softmax", False, fused=fused)
 
 
 def test_flash_next_shaped_layer():
@@ -295,6 +367,26 @@ def test_flash_next_shaped_layer():
     assert_close(P[:, :topk], ref["partial"], "fused slot outputs")
     assert_close(P[:, topk], ref["shared"], "fused shared expert")
     assert_close(y_f, ref["y"], "fused y")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_flash_next_width9_equals_width1(fused):
+    """At the 512-expert, 2560 / 640 geometry with the sigmoid-gated shared
+    expert (five 128-wide slices, 40-group gate/up streams) every row of a
+    nine-row layer equals the same row run alone, bit for bit: y, the slot
+    outputs and the shared slot."""
+    ops, pipeline = _mods()
+    E, H, I, topk, k = 512, 2560, 640, 10, 9
+    cfg, layer_id = 4, 7
+    banner(f"flash-next width 9 vs width 1 fused={fused}")
+    from speculative_decode_verification_amd.ops import Q4Weight
+    gu_w = Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg, GATEUP, layer_id), E, 2 * I, H, DEV)).tiled(True)
+    dn_w = Q4Weight(*sdev.q4_bank(synth.bank_keys(cfg, DOWN, layer_id), E, H, I, DEV)).tiled()
+    sgu = synth.dense_weight(cfg, SHARED_GATEUP, layer_id, 2 * I, H)
+    sdn = synth.dense_weight(cfg, SHARED_DOWN, layer_id, H, I)
+    sgu_w, sdn_w = q4_device_from_host(*sgu).tiled(True), q4_device_from_host(*sdn).tiled()
+    inp = synth.moe_layer_inputs(cfg, layer_id, k, H, E)
+    _width1_rows(ops, pipeline, gu_w, dn_w, inp, k, topk, "sigmoid", True, sgu_w, sdn_w, fused=fused)
 
 
 def test_combine_matches_oracle_order():

@@ -1,6 +1,6 @@
 """GPU parity of sdv_moe_route_experts_k, the router dispatch and the fused
 expert kernel as one call (Red Lite dev45, "What it is": one router dispatch,
-then the union's (expert, row) pairs in one pool encode).  Its route outputs
+then all of the union's (expert, row) pairs in one dispatch).  Its route outputs
 equal the oracle's selection and union bit for bit, and every output equals
 that of sdv_moe_route_k followed by sdv_moe_experts_k bit for bit: on the
 one-launch path (k <= 9, E <= 512) and on the two-launch path it takes
