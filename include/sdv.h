@@ -543,6 +543,29 @@ SDV_API int sdv_verify_accept_k(const float *logits, const float *noise, float i
                                 int k, int V, int eos, int32_t *tokens, int32_t *accepted, void *workspace,
                                 size_t workspace_bytes, sdv_stream_t stream);
 
+/*
+ * sdv_verify_accept_k_noalloc -- sdv_verify_accept_k without a caller
+ * workspace and without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a file-scope device
+ * array of sdv_verify_accept_scratch_bytes() bytes (1 MiB), one per GPU,
+ * held until the process ends; its address on a device is looked up once,
+ * on that device's first call.  Arguments, results and errors are those of
+ * sdv_verify_accept_k; in addition, sizes whose workspace
+ * (sdv_verify_accept_workspace_bytes(k, V)) exceeds the scratch are
+ * rejected with SDV_ERANGE before any launch: with 4,096-logit chunks,
+ * k * ceil(V / 4096) <= 131072 (every width at a 16.7M-token vocabulary).
+ * The scratch keeps the last call's contents and needs no clearing (each
+ * call writes every entry it reads).  Calls that overlap in time on one GPU
+ * share the array and race: serialise them (one stream, or events).
+ */
+SDV_API int sdv_verify_accept_k_noalloc(const float *logits, const float *noise, float inv_temp,
+                                        const int32_t *drafts, int k, int V, int eos, int32_t *tokens,
+                                        int32_t *accepted, sdv_stream_t stream);
+
+/* Bytes of the built-in scratch of sdv_verify_accept_k_noalloc. */
+SDV_API size_t sdv_verify_accept_scratch_bytes(void);
+
 /* Static text for a status code. */
 SDV_API const char *sdv_status_string(int status);
 

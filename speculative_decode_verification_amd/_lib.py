@@ -21,7 +21,8 @@ EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_q8_0
            "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
            "sdv_gdn_rollback_copy", "sdv_gdn_prepare_k", "sdv_gdn_verify_prep_k", "sdv_gdn_verify_prep_norm_k",
            "sdv_gdn_gated_norm_k",
-           "sdv_verify_accept_workspace_bytes", "sdv_verify_accept_k",
+           "sdv_verify_accept_workspace_bytes", "sdv_verify_accept_k", "sdv_verify_accept_k_noalloc",
+           "sdv_verify_accept_scratch_bytes",
            "sdv_status_string", "sdv_last_error", "sdv_build_info")
 
 
@@ -88,6 +89,8 @@ _SIGS = {
     "sdv_gdn_gated_norm_k": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P],
     "sdv_verify_accept_workspace_bytes": [_I, _I],
     "sdv_verify_accept_k": [_P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],
+    "sdv_verify_accept_k_noalloc": [_P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P, _P],
+    "sdv_verify_accept_scratch_bytes": [],
     "sdv_status_string": [_I],
     "sdv_last_error": [],
     "sdv_build_info": [],
@@ -108,7 +111,8 @@ def lib():
             if name in ("sdv_status_string", "sdv_last_error", "sdv_build_info"):
                 fn.restype = ctypes.c_char_p
             elif name in ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q8_0t_codes_bytes", "sdv_q3t_codes_bytes",
-                          "sdv_moe_experts_partial_bytes", "sdv_verify_accept_workspace_bytes"):
+                          "sdv_moe_experts_partial_bytes", "sdv_verify_accept_workspace_bytes",
+                          "sdv_verify_accept_scratch_bytes"):
                 fn.restype = ctypes.c_size_t
             else:
                 fn.restype = ctypes.c_int

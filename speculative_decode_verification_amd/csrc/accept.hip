@@ -19,6 +19,8 @@
 // rows w, w + 16 to their tokens, then one thread counts the accepted
 // drafts.  Integer keys make the result independent of the reduction order.
 
+#include <mutex>
+
 #include "common.h"
 
 namespace sdv {
@@ -128,6 +130,13 @@ __global__ __launch_bounds__(64 * kFinalWaves) void accept_final_kernel(AcceptAr
 
 }  // namespace
 
+// The allocation-free form's workspace: file-scope device memory, one copy
+// per GPU the library runs on, held until the process ends.  Host code uses
+// only the address hipGetSymbolAddress returns for the device (kept per
+// device below), never the array's name.
+constexpr size_t kAcceptScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint64_t scratch[kAcceptScratchBytes / 8];
+
 int accept_chunks(int V) { return (V + kAcceptChunk - 1) / kAcceptChunk; }
 
 size_t accept_workspace_bytes(int k, int V) { return (size_t)k * accept_chunks(V) * 8; }
@@ -151,6 +160,55 @@ hipError_t accept_launch(const float* logits, const float* noise, float inv_temp
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(64 * (k < kFinalWaves ? k : kFinalWaves)), 0, st, a);
   return hipGetLastError();
+}
+
+size_t accept_scratch_bytes() { return kAcceptScratchBytes; }
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that runs `st` (the current
+// device for the null stream), looked up once per device with that device
+// current.
+hipError_t scratch_for(hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+// accept_launch with the per-device scratch array as its workspace: no
+// allocation.  The caller has checked accept_workspace_bytes(k, V) against
+// accept_scratch_bytes().  Every (row, chunk) key is written by the first
+// launch before the second reads it, so nothing needs clearing.
+hipError_t accept_noalloc_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts,
+                                 int k, int V, int eos, int32_t* tokens, int32_t* accepted, hipStream_t st) {
+  void* ws = nullptr;
+  const hipError_t e = scratch_for(st, &ws);
+  if (e != hipSuccess) return e;
+  return accept_launch(logits, noise, inv_temp, drafts, k, V, eos, tokens, accepted, ws, st);
 }
 
 }  // namespace sdv

@@ -52,6 +52,9 @@ hipError_t gdn_gated_norm_launch(const float* y, const float* z, const float* w,
 size_t accept_workspace_bytes(int k, int V);
 hipError_t accept_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts, int k,
                          int V, int eos, int32_t* tokens, int32_t* accepted, void* workspace, hipStream_t st);
+size_t accept_scratch_bytes();
+hipError_t accept_noalloc_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts,
+                                 int k, int V, int eos, int32_t* tokens, int32_t* accepted, hipStream_t st);
 hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
                       const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
                       float* y, float* const* snaps, hipStream_t st);
@@ -697,6 +700,38 @@ int sdv_verify_accept_k(const float* logits, const float* noise, float inv_temp,
                                        accepted, workspace, (hipStream_t)stream),
                     "sdv_verify_accept_k launch");
 }
+
+int sdv_verify_accept_k_noalloc(const float* logits, const float* noise, float inv_temp, const int32_t* drafts,
+                                int k, int V, int eos, int32_t* tokens, int32_t* accepted, sdv_stream_t stream) {
+  int st;
+  if ((st = check_width(k))) return st;
+  if (V < 1 || V > (1 << 30)) return fail(SDV_ERANGE, "V=%d outside 1..2^30", V);
+  const size_t need = sdv::accept_workspace_bytes(k, V);
+  if (need > sdv::accept_scratch_bytes())
+    return fail(SDV_ERANGE, "k=%d rows of V=%d logits need %zu bytes of workspace, more than the %zu of the "
+                "built-in scratch (use sdv_verify_accept_k with a caller workspace)",
+                k, V, need, sdv::accept_scratch_bytes());
+  if ((st = check_ptr(logits, "logits"))) return st;
+  if (noise) {
+    if ((st = check_ptr(noise, "noise"))) return st;
+    if (!(inv_temp > 0.0f && inv_temp <= 3.4e38f))
+      return fail(SDV_ERANGE, "inv_temp=%g must be finite and positive", (double)inv_temp);
+  }
+  if (k > 1 && (st = check_ptr(drafts, "drafts"))) return st;
+  if ((st = check_ptr(tokens, "tokens"))) return st;
+  if ((st = check_ptr(accepted, "accepted"))) return st;
+  const size_t lbytes = (size_t)k * V * 4;
+  Range outs[] = {{tokens, (size_t)k * 4, "tokens"}, {accepted, 4, "accepted"}};
+  Range ins[] = {{logits, lbytes, "logits"},
+                 {noise, noise ? lbytes : 0, "noise"},
+                 {drafts, k > 1 ? (size_t)(k - 1) * 4 : 0, "drafts"}};
+  if ((st = check_alias(outs, 2, ins, 3))) return st;
+  return hip_status(sdv::accept_noalloc_launch(logits, noise, inv_temp, k > 1 ? drafts : nullptr, k, V, eos, tokens,
+                                               accepted, (hipStream_t)stream),
+                    "sdv_verify_accept_k_noalloc launch");
+}
+
+size_t sdv_verify_accept_scratch_bytes(void) { return sdv::accept_scratch_bytes(); }
 
 int sdv_gdn_prepare_k(const float* qkv, const float* hist, const float* conv_w, const float* a, const float* b,
                       const float* A_log, const float* dt_bias, int k, int Hv, int Hk, int Dk, int Dv, int conv_act,

@@ -617,6 +617,22 @@ def verify_accept_k(logits, drafts, noise=None, inv_temp=1.0, eos=-1, tokens=Non
     return tokens, accepted
 
 
+def verify_accept_k_noalloc(logits, drafts, tokens, accepted, noise=None, inv_temp=1.0, eos=-1):
+    """``verify_accept_k`` through sdv_verify_accept_k_noalloc: the library's
+    built-in per-device scratch instead of a caller workspace (no allocation
+    in the call).  tokens int32 [k] and accepted int32 [1] are caller
+    buffers."""
+    k, V = logits.shape
+    dev = logits.device
+    pn = _need(noise, "noise", torch.float32, k * V, dev) if noise is not None else None
+    pd = _need(drafts, "drafts", torch.int32, k - 1, dev) if k > 1 else None
+    check(lib().sdv_verify_accept_k_noalloc(
+        _need(logits, "logits", torch.float32, k * V, dev), pn, ctypes.c_float(inv_temp), pd, k, V, eos,
+        _need(tokens, "tokens", torch.int32, k, dev), _need(accepted, "accepted", torch.int32, 1, dev),
+        _stream(tokens)))
+    return tokens, accepted
+
+
 def bind_verify_accept_k(logits, drafts, tokens, accepted, workspace, noise=None, inv_temp=1.0, eos=-1):
     return BoundCall("sdv_verify_accept_k",
                      _accept_args(logits, drafts, noise, inv_temp, eos, tokens, accepted, workspace))

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 27
+    assert len(names) == 29
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -406,6 +406,39 @@ def test_accept_validation(lib):
     assert call(tok=logits + 64) == L.SDV_EALIAS                    # tokens over logits
     assert call(ws=tok) == L.SDV_EALIAS                             # workspace over tokens
     assert call(acc=noise + 16, noise=noise) == L.SDV_EALIAS         # accepted over noise
+
+
+def test_accept_noalloc_validation(lib):
+    """The allocation-free acceptance: the same argument checks as the
+    workspace form, and sizes whose workspace exceeds the built-in 1 MiB
+    scratch are rejected before any launch."""
+    f = lib.sdv_verify_accept_k_noalloc
+    assert lib.sdv_verify_accept_scratch_bytes() == 1 << 20
+    logits, noise, drafts = P, P + 0x1000000, P + 0x2000000
+    tok, acc = P + 0x2100000, P + 0x2200000
+    ok = dict(logits=logits, noise=None, inv=1.0, drafts=drafts, k=3, V=1000, eos=-1, tok=tok, acc=acc)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["logits"], a["noise"], a["inv"], a["drafts"], a["k"], a["V"], a["eos"], a["tok"], a["acc"], None)
+
+    assert call(k=0) == L.SDV_EWIDTH
+    assert call(k=33) == L.SDV_EWIDTH
+    assert call(V=0) == L.SDV_ERANGE
+    # 32 rows x ceil(V / 4096) chunks x 8 bytes: 4096 chunks fit (1 MiB), 4097 do not
+    assert lib.sdv_verify_accept_workspace_bytes(32, 4096 * 4096) == 1 << 20
+    assert call(k=32, V=4096 * 4096 + 1, logits=None) == L.SDV_ERANGE
+    assert "scratch" in lib.sdv_last_error().decode()
+    assert call(k=32, V=1 << 30, logits=None) == L.SDV_ERANGE
+    assert call(k=32, V=4096 * 4096, logits=None) == L.SDV_EINVAL  # fits: the next check fails
+    assert call(logits=None) == L.SDV_EINVAL
+    assert call(logits=P + 4) == L.SDV_EINVAL
+    assert call(noise=noise, inv=0.0) == L.SDV_ERANGE
+    assert call(drafts=None) == L.SDV_EINVAL
+    assert call(tok=None) == L.SDV_EINVAL
+    assert call(acc=None) == L.SDV_EINVAL
+    assert call(tok=logits + 64) == L.SDV_EALIAS
+    assert call(acc=tok) == L.SDV_EALIAS
 
 
 def prep(lib, k=2, Hv=4, Hk=2, Dk=64, Dv=64, act=0, eps=1e-6, **over):
