@@ -61,6 +61,8 @@ def parse_args():
                    choices=["flashnext_k9", "flashnext_k16", "flashnext_k32"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel instrumented pass")
+    p.add_argument("--fused-norm", action="store_true",
+                   help="the GDN gated output norm inside the GDN launch (default: its own launch, faster here)")
     p.add_argument("--no-extra-configs", action="store_true",
                    help="skip the 256-expert MoE and 36-layer GDN lines (the other configurations' widths)")
     p.add_argument("--copy-probe", action="store_true",
@@ -159,7 +161,7 @@ def cpu_model():
 class Workload:
     """Device-resident inputs and bound launches of the flashnext step at k rows."""
 
-    def __init__(self, dev, k=9):
+    def __init__(self, dev, k=9, fused_norm=False):
         import torch
         import synth
         from synth import configs
@@ -199,9 +201,14 @@ class Workload:
             raw = synth.gdn_raw_inputs(cfg.cid, l, k, gs.hv, gs.hk, gs.dk, gs.dv)
             d = {n: sdev.upload_f32(v, dev) for n, v in raw.items()}
             gl = pipeline.GdnLayer(S0, k).attach_prep(d["hist"], d["conv_w"], d["A_log"], d["dt_bias"], gs.hk)
-            gl.bind_from_proj(d["qkv"], d["a"], d["b"])
             d["out"] = torch.empty((k, gs.hv, gs.dv), dtype=torch.float32, device=dev)
-            gl.bind_tail(d["z"], d["norm_w"], d["out"])
+            if fused_norm:
+                # the gated output norm in the same launch (the last workgroup
+                # of each head applies it)
+                gl.bind_from_proj_norm(d["qkv"], d["a"], d["b"], d["z"], d["norm_w"], d["out"])
+            else:
+                gl.bind_from_proj(d["qkv"], d["a"], d["b"])
+                gl.bind_tail(d["z"], d["norm_w"], d["out"])
             self.gdn[l] = (gl, d)
         # acceptance of the block: next-token logits over the vocabulary with a
         # planted accepted-draft count per step (greedy), and the accepted
@@ -215,6 +222,7 @@ class Workload:
             dr_d = torch.from_numpy(dr).to(dev)
             self.blocks.append((self.cycle.bind(lg_d, dr_d), n, lg_d, dr_d))
         torch.cuda.synchronize()
+        self.fused_norm = fused_norm
         self.setup_s = time.time() - t0
         self.bank_bytes = self.layers * (self.E + 1) * (q4_bytes(2 * self.I, self.H) + q4_bytes(self.H, self.I))
 
@@ -238,7 +246,8 @@ class Workload:
             g = self.gdn.get(l)
             if g is not None:
                 run("gdn", l, g[0].run_from_proj_bound)
-                run("gdn_norm", l, g[0].run_tail_bound)
+                if not self.fused_norm:
+                    run("gdn_norm", l, g[0].run_tail_bound)
             for name, call in self.calls[l]:
                 run(name, l, call)
         accept, _, _, _ = self.blocks[s % len(self.blocks)]
@@ -302,8 +311,12 @@ class Workload:
             # dt_bias in, the window [history; rows] out
             g = self.gs
             C = 2 * g.hk * g.dk + g.hv * g.dv
-            return ((k + 1) * g.hv * g.dv * g.dk * 4 + k * g.hv * g.dv * 4
-                    + (k * C + 3 * C + 4 * C + 2 * k * g.hv + 2 * g.hv + (k + 3) * C) * 4)
+            b = ((k + 1) * g.hv * g.dv * g.dk * 4 + k * g.hv * g.dv * 4
+                 + (k * C + 3 * C + 4 * C + 2 * k * g.hv + 2 * g.hv + (k + 3) * C) * 4)
+            if self.fused_norm:
+                # the gated norm in the same launch: z and the weight in, out written
+                b += (2 * k * g.hv * g.dv + g.dv) * 4
+            return b
         if name == "gdn_norm":
             g = self.gs
             return (3 * k * g.hv * g.dv + g.dv) * 4
@@ -327,7 +340,7 @@ class Workload:
             for name, _ in self.calls[l]:
                 total += self.kernel_bytes(name, l, unions)
             if l in self.gdn:
-                for name in ("gdn", "gdn_norm"):
+                for name in (("gdn",) if self.fused_norm else ("gdn", "gdn_norm")):
                     total += self.kernel_bytes(name, l, unions)
         return total + self.kernel_bytes("accept", self.layers, unions)
 
@@ -647,7 +660,7 @@ def main():
     dev = torch.device("cuda:0")
     k = int(args.workload.rsplit("_k", 1)[1])
     log(f"building workload {args.workload} (device-filled banks) ...")
-    wl = Workload(dev, k)
+    wl = Workload(dev, k, fused_norm=args.fused_norm)
     log(f"workload ready in {wl.setup_s:.1f} s: {wl.bank_bytes / 1e9:.1f} GB of Q4 banks, "
         f"{len(wl.gdn)} GDN layers")
     wl.check_acceptance()
@@ -656,7 +669,7 @@ def main():
     torch.cuda.synchronize()
     unions = wl.unions()
 
-    per_step = len(wl.calls[0]) * wl.layers + 2 * len(wl.gdn) + 1
+    per_step = len(wl.calls[0]) * wl.layers + (1 if wl.fused_norm else 2) * len(wl.gdn) + 1
     # the dominant kernel's events, one mark per step boundary, the breakdown
     # pass and the dense widths
     timer = HipTimer((wl.layers // SAMPLE_EVERY + 1) * args.steps + args.steps + 1 + per_step + 1 + 9)
