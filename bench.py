@@ -474,9 +474,34 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
                             "tflops": round(tflops, 2), "frac_mfma_bf16": round(tflops / PEAK_BF16_TFLOPS, 4)}
         return res
 
+    def time_multi(Ws, wbytes, widths, per_call=16):
+        """sdv_qmv_k_multi: the weights in launches of 16 that share the
+        activation rows (one launch ramp per 16 projections)."""
+        res = {}
+        for k in widths:
+            xs = x[:k].contiguous()
+            groups = [Ws[i:i + per_call] for i in range(0, len(Ws), per_call)]
+            outs = [[torch.empty((k, N), dtype=torch.float32, device=dev) for _ in g] for g in groups]
+            calls = [ops.bind_qmv_k_multi(g, xs, ops.MODE_PLAIN, o) for g, o in zip(groups, outs)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            a = timer.start()
+            for _ in range(reps):
+                for c in calls:
+                    c()
+            b = timer.stop()
+            torch.cuda.synchronize()
+            us = timer.elapsed_us(a, b) / (reps * len(Ws))
+            nbytes = wbytes + k * 2 * K + k * 4 * N
+            res[f"k{k}"] = {"us_per_projection": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                            "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3)}
+        return {"weights_per_launch": per_call, "widths": res}
+
     Ws = [ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(1, DENSE_W, l), 1, N, K, dev)).tiled()
           for l in range(n_weights)]
     out = time_widths(Ws, q4_bytes(N, K), (1, 4, 8, 9, 32))
+    multi = time_multi(Ws, q4_bytes(N, K), (1, 9))
     del Ws
     # Q8_0 and affine Q3 weights filled on the device (any codes are valid;
     # parity of these formats is covered by the tests)
@@ -500,7 +525,8 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
     q3 = time_widths(Ws, N * 3 * K // 8 + N * (K // 64) * 4, (1, 9))
     del Ws
     torch.cuda.empty_cache()
-    return {"shape": [N, K], "weights": n_weights, "widths": out, "q8_0": q8, "q3": q3}
+    return {"shape": [N, K], "weights": n_weights, "widths": out, "multi_weight_launch": multi, "q8_0": q8,
+            "q3": q3}
 
 
 def ornith_moe(dev, widths=tuple(range(2, 10)), reps=3):

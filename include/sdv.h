@@ -238,6 +238,20 @@ SDV_API int sdv_qmv_k(const sdv_q4t *W, const void *act, int act_dtype, int k, i
                       sdv_stream_t stream);
 
 /*
+ * sdv_qmv_k_multi -- sdv_qmv_k for nw weights (1..16) of one shape, format
+ * and layout that read the same activation rows, in one launch: for example
+ * the projections of a layer that share their input.  W is a host array of
+ * nw tiled descriptors (E = 1), y a host array of nw device outputs (each
+ * as sdv_qmv_k's y).  Each output equals the separate sdv_qmv_k call's bit
+ * for bit: the launch only places the weights' tiles side by side in one
+ * grid (more workgroups to fill the chip, one launch ramp for all).
+ * Errors: those of sdv_qmv_k; ERANGE for nw outside 1..16; ELAYOUT when a
+ * weight differs from W[0] in shape, format or layout.
+ */
+SDV_API int sdv_qmv_k_multi(const sdv_q4t *W, int nw, const void *act, int act_dtype, int k, int mode,
+                            float *const *y, sdv_stream_t stream);
+
+/*
  * sdv_moe_route_k -- one router dispatch for all k rows: per-row top-k, the
  * routing weights, the union of the rows' experts and the (expert, row, slot)
  * pairs, all on the device with no host synchronisation (Red Lite dev45,

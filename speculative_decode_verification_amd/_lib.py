@@ -16,7 +16,7 @@ GATE_SIGMOID, GATE_SILU = 0, 1
 
 EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_q8_0t_codes_bytes", "sdv_q8_0_repack",
            "sdv_q3t_codes_bytes", "sdv_q3_repack",
-           "sdv_qmv_k", "sdv_moe_route_k",
+           "sdv_qmv_k", "sdv_qmv_k_multi", "sdv_moe_route_k",
            "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_route_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
            "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
            "sdv_gdn_rollback_copy", "sdv_gdn_prepare_k", "sdv_gdn_verify_prep_k", "sdv_gdn_verify_prep_norm_k",
@@ -67,6 +67,7 @@ _SIGS = {
     "sdv_q3t_codes_bytes": [_I, _I, _I, _I],
     "sdv_q3_repack": [ctypes.POINTER(SdvQ3), _I, _P, _P, _P],
     "sdv_qmv_k": [ctypes.POINTER(SdvQ4T), _P, _I, _I, _I, _P, _P],
+    "sdv_qmv_k_multi": [ctypes.POINTER(SdvQ4T), _I, _P, _I, _I, _I, ctypes.POINTER(_P), _P],
     "sdv_moe_route_k": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
     "sdv_gather_qmv_k": [ctypes.POINTER(SdvQ4T), _I, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P,
                          ctypes.POINTER(SdvQ4T), _P, _P, _P],

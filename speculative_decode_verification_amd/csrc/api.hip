@@ -52,6 +52,9 @@ hipError_t gdn_gated_norm_launch(const float* y, const float* z, const float* w,
 size_t accept_workspace_bytes(int k, int V);
 hipError_t accept_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts, int k,
                          int V, int eos, int32_t* tokens, int32_t* accepted, void* workspace, hipStream_t st);
+int dense_multi_max();
+hipError_t dense_multi_launch(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
+                              float* const* outs, hipStream_t st);
 size_t accept_scratch_bytes();
 hipError_t accept_noalloc_launch(const float* logits, const float* noise, float inv_temp, const int32_t* drafts,
                                  int k, int V, int eos, int32_t* tokens, int32_t* accepted, hipStream_t st);
@@ -325,6 +328,40 @@ int sdv_qmv_k(const sdv_q4t* W, const void* act, int act_dtype, int k, int mode,
                                    nullptr, nullptr, k, 1, y, nullptr, nullptr, nullptr,
                                    (hipStream_t)stream),
                     "sdv_qmv_k launch");
+}
+
+int sdv_qmv_k_multi(const sdv_q4t* W, int nw, const void* act, int act_dtype, int k, int mode, float* const* y,
+                    sdv_stream_t stream) {
+  int st;
+  if (!W) return fail(SDV_EINVAL, "W is NULL");
+  if (!y) return fail(SDV_EINVAL, "y is NULL");
+  if (nw < 1 || nw > sdv::dense_multi_max())
+    return fail(SDV_ERANGE, "nw=%d outside 1..%d", nw, sdv::dense_multi_max());
+  if ((st = check_width(k))) return st;
+  if ((st = check_ptr(act, "act"))) return st;
+  const sdv_q4t& W0 = W[0];
+  const size_t act_bytes = (size_t)k * W0.K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
+  const size_t n_out = mode == SDV_MODE_PLAIN ? W0.N : W0.N / 2;
+  // every weight: a valid dense descriptor of W[0]'s shape, format and layout
+  Range ins[2 * 16 + 1];
+  Range outs[16];
+  for (int m = 0; m < nw; ++m) {
+    if ((st = check_q4t(&W[m], "W[m]"))) return st;
+    if (W[m].E != 1) return fail(SDV_EINVAL, "dense product needs E=1 (W[%d] has %d)", m, W[m].E);
+    if (W[m].N != W0.N || W[m].K != W0.K || W[m].format != W0.format || W[m].fused_gateup != W0.fused_gateup)
+      return fail(SDV_ELAYOUT, "W[%d] differs from W[0] in shape, format or layout", m);
+    if ((st = check_ptr(y[m], "y[m]"))) return st;
+    ins[2 * m] = {W[m].codes, tiled_codes_bytes(W[m]), "codes"};
+    ins[2 * m + 1] = {W[m].sb, sdv::q4t_sb_bytes(1, W[m].N, W[m].K, W[m].fused_gateup), "sb"};
+    outs[m] = {y[m], (size_t)k * n_out * 4, "y[m]"};
+  }
+  ins[2 * nw] = {act, act_bytes, "act"};
+  if ((st = check_mode(mode, act_dtype, W0.N))) return st;
+  if ((st = check_mode_layout(mode, W0))) return st;
+  if ((st = check_lds(W0, act_dtype, k, false))) return st;
+  if ((st = check_alias(outs, nw, ins, 2 * nw + 1))) return st;
+  return hip_status(sdv::dense_multi_launch(W, nw, mode, act, act_dtype, k, y, (hipStream_t)stream),
+                    "sdv_qmv_k_multi launch");
 }
 
 int sdv_moe_route_k(const float* logits, int k, int E, int topk, int score_mode, int renorm,

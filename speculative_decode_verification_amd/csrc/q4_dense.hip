@@ -37,12 +37,14 @@ namespace {
 using namespace q4;
 
 constexpr int kDenseMaxWaves = 16;
+constexpr int kDenseMulti = 16;  // weights of one multi-weight launch
 
 struct DenseArgs {
-  const uint4* codes;    // tiled: [T][G][64] uint4
-  const uint32_t* sb;    // tiled: [T][G][32]
-  const void* act;       // [k][K] bf16 bits or fp32
-  float* out;            // [k][n_out]
+  // weight blockIdx.y of the launch (one for sdv_qmv_k)
+  const uint4* codes[kDenseMulti];  // tiled: [T][G][64] uint4
+  const uint32_t* sb[kDenseMulti];  // tiled: [T][G][32]
+  float* out[kDenseMulti];          // [k][n_out]
+  const void* act;       // [k][K] bf16 bits or fp32, shared by the weights
   int N, K, T, G, k, n_out, nw;
   int gwmax;             // groups of the widest wave range
   int cap;               // staged rows per wave (k or 3k); row cap is all zero
@@ -117,21 +119,24 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   }
 
   // ---- the wave's weight blocks: step s reads block (t, gb + min(s, gw - 1))
+  const uint4* const codes = a.codes[blockIdx.y];
+  const uint32_t* const sbp = a.sb[blockIdx.y];
+  float* const out = a.out[blockIdx.y];
   const size_t blk0 = (size_t)t * G + gb;
   uint4 cbuf[PF], cbuf2[Q8 ? PF : 1];
   uint32_t sbuf[PF];
   auto issue = [&](int slot, int s) {
     const size_t blk = blk0 + min(s, gw - 1);
     if constexpr (Q8) {
-      cbuf[slot] = load_nt(a.codes + blk * 128 + lane);  // weights: read once per call
-      cbuf2[slot] = load_nt(a.codes + blk * 128 + 64 + lane);
+      cbuf[slot] = load_nt(codes + blk * 128 + lane);  // weights: read once per call
+      cbuf2[slot] = load_nt(codes + blk * 128 + 64 + lane);
     } else if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(a.codes) + blk * 192 + lane;
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(codes) + blk * 192 + lane;
       cbuf[slot] = make_uint4(load_nt(w), load_nt(w + 64), load_nt(w + 128), 0u);
     } else {
-      cbuf[slot] = load_nt(a.codes + blk * 64 + lane);
+      cbuf[slot] = load_nt(codes + blk * 64 + lane);
     }
-    sbuf[slot] = load_nt(a.sb + blk * 32 + col);
+    sbuf[slot] = load_nt(sbp + blk * 32 + col);
   };
 #pragma unroll
   for (int i = 0; i < PF; ++i) issue(i, i);
@@ -286,16 +291,16 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
     }
     if (MODE == SDV_MODE_PLAIN) {
       const int on = t * 32 + cc;
-      if (on < a.N) a.out[(size_t)i * a.n_out + on] = val[0];
+      if (on < a.N) out[(size_t)i * a.n_out + on] = val[0];
     } else {
       const int on = t * 16 + cc;
-      if (on < a.n_out) a.out[(size_t)i * a.n_out + on] = siluf_(val[0]) * val[1];
+      if (on < a.n_out) out[(size_t)i * a.n_out + on] = siluf_(val[0]) * val[1];
     }
   }
 }
 
 template <int FMT, int MODE, int ACT, int PF>
-hipError_t dense_launch_one(const DenseArgs& a, size_t lds, hipStream_t st) {
+hipError_t dense_launch_one(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
   void (*kern)(DenseArgs) = q4_dense_k_kernel<FMT, MODE, ACT, PF>;
   static std::atomic<size_t> lds_limit{65536};
   size_t cur = lds_limit.load(std::memory_order_relaxed);
@@ -306,25 +311,25 @@ hipError_t dense_launch_one(const DenseArgs& a, size_t lds, hipStream_t st) {
     while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
     }
   }
-  hipLaunchKernelGGL(kern, dim3(a.T), dim3(64 * a.nw), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(a.T, nmulti), dim3(64 * a.nw), lds, st, a);
   return hipGetLastError();
 }
 
 template <int FMT, int MODE, int ACT>
-hipError_t dense_launch_pf(const DenseArgs& a, size_t lds, hipStream_t st) {
+hipError_t dense_launch_pf(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
   // ring depth: the wave's whole range when it is short, else 8 with refills
   // (fp32 rows: 2, since staging the parts takes the registers; Q8_0 blocks
   // take two chunks, so at most 4)
   if constexpr (ACT == SDV_ACT_F32) {
-    return dense_launch_one<FMT, MODE, ACT, 2>(a, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 2>(a, nmulti, lds, st);
   } else if constexpr (FMT == SDV_FMT_Q8_0) {
-    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, lds, st);
-    return dense_launch_one<FMT, MODE, ACT, 4>(a, lds, st);
+    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, nmulti, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 4>(a, nmulti, lds, st);
   } else {
-    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, lds, st);
-    if (a.gwmax <= 4) return dense_launch_one<FMT, MODE, ACT, 4>(a, lds, st);
-    if (a.gwmax <= 5) return dense_launch_one<FMT, MODE, ACT, 5>(a, lds, st);
-    return dense_launch_one<FMT, MODE, ACT, 8>(a, lds, st);
+    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, nmulti, lds, st);
+    if (a.gwmax <= 4) return dense_launch_one<FMT, MODE, ACT, 4>(a, nmulti, lds, st);
+    if (a.gwmax <= 5) return dense_launch_one<FMT, MODE, ACT, 5>(a, nmulti, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 8>(a, nmulti, lds, st);
   }
 }
 
@@ -349,13 +354,18 @@ size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt) {
 
 namespace {
 
-hipError_t dense_launch_pass(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
-                             hipStream_t st) {
-  DenseArgs a;
-  a.codes = static_cast<const uint4*>(W.codes);
-  a.sb = W.sb;
+// One launch over nmulti weights of W's shape and format (Ws[i], outputs
+// outs[i]) that share the activation rows.
+hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
+                             float* const* outs, hipStream_t st) {
+  const sdv_q4t& W = Ws[0];
+  DenseArgs a{};
+  for (int m = 0; m < nmulti; ++m) {
+    a.codes[m] = static_cast<const uint4*>(Ws[m].codes);
+    a.sb[m] = Ws[m].sb;
+    a.out[m] = outs[m];
+  }
   a.act = act;
-  a.out = out;
   a.N = W.N;
   a.K = W.K;
   a.T = (W.N + 31) / 32;
@@ -368,7 +378,7 @@ hipError_t dense_launch_pass(const sdv_q4t& W, int mode, const void* act, int ac
   a.region = (int)dense_region_bytes(a.cap, a.gwmax, W.format == SDV_FMT_Q8_0 ? 2 : 1);
   const size_t lds = dense_lds_bytes(W.K, act_dtype, k, W.format);
 #define SDV_DENSE(F, M, A) \
-  if (W.format == F && mode == M && act_dtype == A) return dense_launch_pf<F, M, A>(a, lds, st);
+  if (W.format == F && mode == M && act_dtype == A) return dense_launch_pf<F, M, A>(a, nmulti, lds, st);
   SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_BF16)
   SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_F32)
   SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_GATEUP_SWIGLU, SDV_ACT_BF16)
@@ -390,17 +400,28 @@ hipError_t dense_launch_pass(const sdv_q4t& W, int mode, const void* act, int ac
 // Widths above one pass run one launch per pass of at most kPassRows rows
 // (rows 9c .. 9c + 8 of the activations and outputs); each launch reads the
 // weights again.
-hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
-                        hipStream_t st) {
+hipError_t dense_multi_launch(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
+                              float* const* outs, hipStream_t st) {
+  const sdv_q4t& W = Ws[0];
+  if (nmulti < 1 || nmulti > kDenseMulti) return hipErrorInvalidValue;
   const size_t act_row = (size_t)W.K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
   const int n_out = (mode == SDV_MODE_PLAIN) ? W.N : W.N / 2;
   for (int r0 = 0; r0 < k; r0 += kPassRows) {
     const int kc = k - r0 < kPassRows ? k - r0 : kPassRows;
-    const hipError_t e = dense_launch_pass(W, mode, static_cast<const unsigned char*>(act) + r0 * act_row, act_dtype,
-                                           kc, out + (size_t)r0 * n_out, st);
+    float* o[kDenseMulti];
+    for (int m = 0; m < nmulti; ++m) o[m] = outs[m] + (size_t)r0 * n_out;
+    const hipError_t e = dense_launch_pass(Ws, nmulti, mode, static_cast<const unsigned char*>(act) + r0 * act_row,
+                                           act_dtype, kc, o, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
+
+hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
+                        hipStream_t st) {
+  return dense_multi_launch(&W, 1, mode, act, act_dtype, k, &out, st);
+}
+
+int dense_multi_max() { return kDenseMulti; }
 
 }  // namespace sdv

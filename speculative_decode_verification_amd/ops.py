@@ -213,6 +213,35 @@ def qmv_k(W, act, mode=MODE_PLAIN, out=None):
     return out
 
 
+def _qmv_multi_args(Ws, act, mode, outs):
+    k = act.shape[0]
+    W0 = Ws[0]
+    n_out = W0.N if mode == MODE_PLAIN else W0.N // 2
+    if act.dim() != 2 or act.shape[1] != W0.K:
+        raise ValueError(f"act must be [k, {W0.K}]")
+    if len(Ws) != len(outs):
+        raise ValueError("one output per weight")
+    descs = (SdvQ4T * len(Ws))(*[W._desc for W in Ws])
+    ys = (ctypes.c_void_p * len(outs))(*[_need(o, "out", torch.float32, k * n_out, W0.device).value for o in outs])
+    return [descs, len(Ws), _need(act, "act", act.dtype, device=W0.device), _act_kind(act), k, mode, ys,
+            _stream(act)]
+
+
+def qmv_k_multi(Ws, act, mode=MODE_PLAIN, outs=None):
+    """``qmv_k`` for several weights of one shape that read the same
+    activation rows, in one launch (sdv_qmv_k_multi); returns the outputs."""
+    k = act.shape[0]
+    n_out = Ws[0].N if mode == MODE_PLAIN else Ws[0].N // 2
+    if outs is None:
+        outs = [torch.empty((k, n_out), dtype=torch.float32, device=Ws[0].device) for _ in Ws]
+    check(lib().sdv_qmv_k_multi(*_qmv_multi_args(Ws, act, mode, outs)))
+    return outs
+
+
+def bind_qmv_k_multi(Ws, act, mode, outs):
+    return BoundCall("sdv_qmv_k_multi", _qmv_multi_args(Ws, act, mode, outs))
+
+
 def route_buffers(k, topk, device):
     kt = k * topk
     return RouteResult(

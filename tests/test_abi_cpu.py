@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 29
+    assert len(names) == 30
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -150,6 +150,33 @@ def test_qmv_validation(lib):
     # fp32 activation rows that cannot be staged in LDS
     assert qmv(lib, q4t(K=8192), dtype=L.ACT_F32, k=9) == L.SDV_ELAYOUT
     assert "LDS" in lib.sdv_last_error().decode()
+
+
+def qmv_multi(lib, Ws, act=P + 0x400000, dtype=L.ACT_BF16, k=2, mode=L.MODE_PLAIN, ys=None, nw=None):
+    arr = (L.SdvQ4T * len(Ws))(*Ws)
+    ys = ys if ys is not None else [P + 0x800000 + 0x10000 * m for m in range(len(Ws))]
+    yarr = (ctypes.c_void_p * len(ys))(*ys)
+    return lib.sdv_qmv_k_multi(arr, len(Ws) if nw is None else nw, act, dtype, k, mode, yarr, None)
+
+
+def test_qmv_multi_validation(lib):
+    """The multi-weight dense call: the single call's checks for every
+    weight, one shape, format and layout for all, 1..16 weights, no output
+    over any weight, the activations or another output."""
+    base = [q4t(codes=P + 0x20000 * m, sb=P + 0x100000 + 0x2000 * m) for m in range(3)]
+    assert qmv_multi(lib, base, nw=0) == L.SDV_ERANGE
+    assert qmv_multi(lib, base, nw=17) == L.SDV_ERANGE
+    assert qmv_multi(lib, base, k=0) == L.SDV_EWIDTH
+    assert qmv_multi(lib, base, act=0) == L.SDV_EINVAL
+    assert qmv_multi(lib, base[:1] + [q4t(N=128, codes=P + 0x20000, sb=P + 0x102000)]) == L.SDV_ELAYOUT
+    assert qmv_multi(lib, base[:1] + [q4t(fmt=1, codes=P + 0x20000, sb=P + 0x102000)]) == L.SDV_ELAYOUT
+    assert qmv_multi(lib, base[:1] + [q4t(E=2, codes=P + 0x20000, sb=P + 0x102000)]) == L.SDV_EINVAL
+    assert qmv_multi(lib, base[:1] + [q4t(codes=0)]) == L.SDV_EINVAL
+    assert qmv_multi(lib, base, ys=[P + 0x800000, 0, P + 0x820000]) == L.SDV_EINVAL
+    assert qmv_multi(lib, base, ys=[P + 0x800000, P + 0x20000 + 64, P + 0x820000]) == L.SDV_EALIAS  # over codes
+    assert qmv_multi(lib, base, ys=[P + 0x800000, P + 0x800000 + 16, P + 0x820000]) == L.SDV_EALIAS  # outputs
+    assert qmv_multi(lib, base, ys=[P + 0x400000 + 16, P + 0x810000, P + 0x820000]) == L.SDV_EALIAS  # over act
+    assert qmv_multi(lib, base, mode=L.MODE_GATEUP_SWIGLU) == L.SDV_ELAYOUT
 
 
 def route(lib, k=2, E=64, topk=4, mode=L.ROUTE_SOFTMAX, logits=P, outs=None):

@@ -177,3 +177,44 @@ def test_mode_must_match_layout():
         ops.qmv_k(W.tiled(False), xd, mode=ops.MODE_GATEUP_SWIGLU)
     with pytest.raises(ops.SdvError, match="fused_gateup=0"):
         ops.qmv_k(W.tiled(True), xd)
+
+
+@pytest.mark.parametrize("fmt_name,mode,act_f32,k", [("q4", 0, False, 9), ("q4", 0, True, 5), ("q4", 1, False, 9),
+                                                    ("q4", 0, False, 32), ("q8", 0, False, 9), ("q3", 0, False, 4)])
+def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k):
+    """sdv_qmv_k_multi over several weights of one shape that share the
+    activation rows: every output equals its own sdv_qmv_k call bit for bit
+    (ragged N, the gate/up mode, fp32 rows, 32 rows in passes, Q8_0, Q3)."""
+    ops = _ops()
+    from speculative_decode_verification_amd.ops import Q3Weight, Q8Weight
+    N, K, nw = (336 if mode == 0 else 320), 1024, 5
+    banner(f"qmv multi {fmt_name} mode={mode} f32={act_f32} k={k} nw={nw}")
+    Ws = []
+    for m in range(nw):
+        if fmt_name == "q8":
+            qs, d = synth.q8_0_weight(40, DENSE_W, m, 1, N, K)
+            W = Q8Weight(torch.from_numpy(np.ascontiguousarray(qs[0])).to(DEV),
+                         torch.from_numpy(np.ascontiguousarray(d[0]).view(np.int16)).to(DEV))
+        elif fmt_name == "q3":
+            c, sc, bi, _ = synth.q3_weight(40, DENSE_W, m, 1, N, K)
+            W = Q3Weight(torch.from_numpy(np.ascontiguousarray(c[0])).to(DEV),
+                         torch.from_numpy(np.ascontiguousarray(sc[0]).view(np.int16)).to(DEV),
+                         torch.from_numpy(np.ascontiguousarray(bi[0]).view(np.int16)).to(DEV))
+        else:
+            W = q4_device_from_host(*synth.dense_weight(40, DENSE_W, m, N, K))
+        Ws.append(W.tiled(fused_gateup=(mode == 1)))
+    x = synth.activations(40, 0, k, K)
+    xd = sdev.upload_bf16(x, DEV)
+    if act_f32:
+        xd = torch.from_numpy(oracle.bf16_to_f64(x).astype(np.float32) * np.float32(1.25)).to(DEV)
+    outs = ops.qmv_k_multi(Ws, xd, mode)
+    for m, W in enumerate(Ws):
+        single = to_np(ops.qmv_k(W, xd, mode))
+        assert np.array_equal(to_np(outs[m]), single), f"weight {m}"
+    # the bound form gives the same
+    for o in outs:
+        o.fill_(0.0)
+    ops.bind_qmv_k_multi(Ws, xd, mode, outs)()
+    torch.cuda.synchronize()
+    for m, W in enumerate(Ws):
+        assert np.array_equal(to_np(outs[m]), to_np(ops.qmv_k(W, xd, mode))), f"bound, weight {m}"
