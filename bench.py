@@ -64,7 +64,7 @@ def parse_args():
     p.add_argument("--fused-norm", action="store_true",
                    help="the GDN gated output norm inside the GDN launch (default: its own launch, faster here)")
     p.add_argument("--no-extra-configs", action="store_true",
-                   help="skip the 256-expert MoE and 36-layer GDN lines (the other configurations' widths)")
+                   help="skip the 256-expert MoE, 36-layer GDN and weight-format MoE lines")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (PMC counter calibration)")
     return p.parse_args()
@@ -603,6 +603,125 @@ def ornith_moe(dev, widths=tuple(range(2, 10)), reps=3):
                         "softmax top-8", "widths": out}
 
 
+def format_bytes(fmt, n, k):
+    """Bytes of one [n, k] matrix in a weight format: affine Q4/g64 (nibbles,
+    bf16 scale and bias per 64), Q8_0 (bytes, a half scale per 32) or affine
+    Q3/g64 (three bits, bf16 scale and bias per 64)."""
+    if fmt == "q4":
+        return q4_bytes(n, k)
+    if fmt == "q8_0":
+        return n * k + n * (k // 32) * 2
+    if fmt == "q3":
+        return n * k * 3 // 8 + n * (k // 64) * 4
+    raise KeyError(fmt)
+
+
+def _format_bank(fmt, E, N, K, fused, dev, gen):
+    """A whole [E, N, K] bank of uniformly random codes in device memory
+    (seeded torch generator; any byte pattern is a valid code), scales and
+    biases in the synthetic inputs' ranges, repacked to the tiled layout."""
+    import torch
+    from speculative_decode_verification_amd import ops
+    bf16 = lambda shape, lo, hi: (torch.empty(shape, dtype=torch.float32, device=dev).uniform_(lo, hi, generator=gen)
+                                  .to(torch.bfloat16).view(torch.int16))
+    if fmt == "q8_0":
+        qs = torch.randint(-127, 128, (E, N, K), dtype=torch.int8, device=dev, generator=gen)
+        d = (torch.empty((E, N, K // 32), dtype=torch.float32, device=dev).uniform_(2e-4, 8e-4, generator=gen)
+             .to(torch.float16).view(torch.int16))
+        W = ops.Q8Weight(qs, d)
+    elif fmt == "q3":
+        codes = torch.randint(0, 256, (E, N, 3 * K // 8), dtype=torch.uint8, device=dev, generator=gen)
+        W = ops.Q3Weight(codes, bf16((E, N, K // 64), 0.01, 0.04), bf16((E, N, K // 64), -0.1, 0.1))
+    else:
+        codes = torch.randint(-2 ** 31, 2 ** 31 - 1, (E, N, K // 8), dtype=torch.int32, device=dev, generator=gen)
+        W = ops.Q4Weight(codes, bf16((E, N, K // 64), 0.01, 0.04), bf16((E, N, K // 64), -0.1, 0.1))
+    T = W.tiled(fused_gateup=fused)
+    del W
+    return T
+
+
+def format_moe(dev, widths=(2, 9), formats=("q4", "q8_0", "q3"), layers=6, reps=3):
+    """The Flash-Next MoE layer geometry (512 experts, hidden 2560,
+    intermediate 640, sigmoid top-10 with renormalisation, the gated shared
+    expert) with the routed and shared experts in affine Q4, Q8_0 or affine
+    Q3, over `layers` distinct banks rotated so no layer's experts are
+    cache-resident.  Per format and width: the fused path (router, expert
+    kernel, sliced combine) and the gathered path (router, gate/up and down
+    gathered launches carrying the shared expert, combine), the layer time
+    each, and the expert kernel alone against its algorithmic bytes (union
+    and shared experts once, x, one output per used slot)."""
+    import torch
+    import synth
+    from synth import configs
+    from synth import device as sdev
+    from speculative_decode_verification_amd import ops, pipeline
+    m = configs.C4.moe
+    E, H, I, topk = m.experts, m.hidden, m.inter, m.topk
+    out = {}
+    for fmt in formats:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4242)
+        banks = []
+        for _ in range(layers):
+            banks.append(tuple(_format_bank(fmt, e, n, kk, f, dev, gen) for e, n, kk, f in
+                               ((E, 2 * I, H, True), (E, H, I, False), (1, 2 * I, H, True), (1, H, I, False))))
+        ex_bytes = format_bytes(fmt, 2 * I, H) + format_bytes(fmt, H, I)
+        res = {}
+        for k in widths:
+            row = {}
+            for path, fused in (("fused", True), ("gathered", False)):
+                layer_objs, calls = [], []
+                for l, (gu, dn, sgu, sdn) in enumerate(banks):
+                    inp = synth.moe_layer_inputs(configs.C4.cid, l, k, H, E)
+                    args = (sdev.upload_bf16(inp["x"], dev), sdev.upload_f32(inp["logits"], dev),
+                            sdev.upload_f32(inp["z"], dev))
+                    layer = pipeline.MoeLayer(gu, dn, k, topk, ops.ROUTE_SIGMOID, m.renorm, sgu, sdn,
+                                              fused_experts=fused)
+                    layer_objs.append((layer, args))
+                    calls.append(layer.bind(*args))
+                for cl in calls:
+                    for _, c in cl:
+                        c()
+                torch.cuda.synchronize()
+                timer = HipTimer(1 + layers)
+                a = timer.start()
+                for _ in range(reps):
+                    for cl in calls:
+                        for _, c in cl:
+                            c()
+                b = timer.stop()
+                torch.cuda.synchronize()
+                us_layer = timer.elapsed_us(a, b) / (reps * layers)
+                ev = []
+                for cl in calls:
+                    for name, c in cl:
+                        if name == "experts":
+                            e0 = timer.start()
+                            c()
+                            ev.append((e0, timer.stop()))
+                        else:
+                            c()
+                torch.cuda.synchronize()
+                r = {"us_per_layer": round(us_layer, 2)}
+                if ev:
+                    ex_us = sum(timer.elapsed_us(e0, e1) for e0, e1 in ev) / len(ev)
+                    unions = [int(lo.route.n_union.item()) for lo, _ in layer_objs]
+                    mu = sum(unions) / len(unions)
+                    eb = (mu + 1) * ex_bytes + k * H * 2 + (k * topk + k) * H * 4
+                    r.update({"mean_union": round(mu, 2), "experts_us": round(ex_us, 2),
+                              "experts_bytes": round(eb),
+                              "experts_frac_hbm": round(eb / ex_us / 1e3 / PEAK_HBM_GBS, 3)})
+                timer.close()
+                row[path] = r
+                del layer_objs, calls
+            res[f"k{k}"] = row
+        out[fmt] = {"bank_bytes_per_layer": E * ex_bytes + ex_bytes, "widths": res}
+        del banks
+        torch.cuda.empty_cache()
+    return {"workload": f"format_moe: {layers} layers x [512 experts + shared: gate/up 1280x2560 + down 2560x640], "
+                        "sigmoid top-10, affine Q4 / Q8_0 / affine Q3", "formats": out}
+
+
 def gdn36_chains(dev, widths=tuple(range(1, 10)), steps=16):
     """The GDN verify of 36 layers (48 v heads, 16 qk heads, Dk = Dv = 128,
     3 MB of fp32 state per layer, 113 MB in all) at each width: 16-step
@@ -759,6 +878,8 @@ def main():
         extra["ornith_moe"] = ornith_moe(dev)
         log("timing the 36-layer GDN chains (k = 1..9) ...")
         extra["gdn36"] = gdn36_chains(dev)
+        log("timing the Flash-Next MoE layer in affine Q4, Q8_0 and affine Q3 (fused and gathered) ...")
+        extra["format_moe"] = format_moe(dev)
 
     cpu = cpu1 = None
     if not args.no_cpu_baseline:

@@ -30,7 +30,7 @@ hipError_t combine_sliced_launch(const float* partial, const int32_t* idx, const
                                  const float* shared_logit, int S, int k, int topk, int H, int has_shared,
                                  float* y, hipStream_t st);
 int expert_slices(int I);
-size_t expert_lds_bytes(int k, int H);
+size_t expert_lds_bytes(int k, int H, int fmt);
 size_t expert_partial_bytes(int k, int topk, int H, int I);
 bool route_in_experts(int k, int E);
 size_t route_experts_lds_bytes(int k, int E, int H);
@@ -460,15 +460,19 @@ namespace {
 // The checks sdv_moe_experts_k and sdv_moe_route_experts_k share: weights,
 // shapes, widths, LDS and the partial output's size (in *pbytes).
 int check_experts(const sdv_q4t* gate_up, const sdv_q4t* down, const sdv_q4t* shared_gate_up,
-                  const sdv_q4t* shared_down, int k, int topk, size_t lds_extra_for_route, size_t* pbytes_out) {
+                  const sdv_q4t* shared_down, int k, int topk, size_t lds_extra_for_route, size_t* pbytes_out,
+                  bool q4_only) {
   int st;
   if ((st = check_q4t(gate_up, "gate_up"))) return st;
   if ((st = check_q4t(down, "down"))) return st;
   if (!gate_up->fused_gateup) return fail(SDV_ELAYOUT, "gate_up must be repacked with fused_gateup=1");
-  if (gate_up->format != SDV_FMT_AFFINE_Q4 || down->format != SDV_FMT_AFFINE_Q4 ||
-      (shared_gate_up && shared_gate_up->format != SDV_FMT_AFFINE_Q4) ||
-      (shared_down && shared_down->format != SDV_FMT_AFFINE_Q4))
-    return fail(SDV_ELAYOUT, "the fused expert kernel takes affine Q4 weights; use sdv_gather_qmv_k for Q8_0 and Q3");
+  const int fmt = gate_up->format;
+  if (down->format != fmt || (shared_gate_up && shared_gate_up->format != fmt) ||
+      (shared_down && shared_down->format != fmt))
+    return fail(SDV_ELAYOUT, "the fused expert kernel needs one weight format for all four weights");
+  if (q4_only && fmt != SDV_FMT_AFFINE_Q4)
+    return fail(SDV_ELAYOUT, "the router dispatch inside the expert kernel takes affine Q4 weights; "
+                "route with sdv_moe_route_k and call sdv_moe_experts_k for Q8_0 and Q3");
   if (down->fused_gateup) return fail(SDV_ELAYOUT, "down must be repacked with fused_gateup=0");
   const int H = gate_up->K, I = gate_up->N / 2;
   if (down->E != gate_up->E || down->N != H || down->K != I)
@@ -490,7 +494,7 @@ int check_experts(const sdv_q4t* gate_up, const sdv_q4t* down, const sdv_q4t* sh
         shared_down->N != H || shared_down->K != I || shared_down->fused_gateup)
       return fail(SDV_ELAYOUT, "shared expert geometry differs from the routed experts'");
   }
-  size_t lds = sdv::expert_lds_bytes(k, H);
+  size_t lds = sdv::expert_lds_bytes(k, H, fmt);
   if (lds_extra_for_route > lds) lds = lds_extra_for_route;
   // the kernel's static LDS (row maps and the in-kernel routing's outputs)
   // takes at most kExpertStaticLds of the workgroup's LDS
@@ -507,15 +511,15 @@ int check_experts(const sdv_q4t* gate_up, const sdv_q4t* down, const sdv_q4t* sh
 int expert_weight_ranges(const sdv_q4t* gate_up, const sdv_q4t* down, const sdv_q4t* shared_gate_up,
                          const sdv_q4t* shared_down, Range* r) {
   const int H = gate_up->K, I = gate_up->N / 2;
-  r[0] = {gate_up->codes, sdv::q4t_codes_bytes(gate_up->E, gate_up->N, H, 1), "gate_up codes"};
+  r[0] = {gate_up->codes, tiled_codes_bytes(*gate_up), "gate_up codes"};
   r[1] = {gate_up->sb, sdv::q4t_sb_bytes(gate_up->E, gate_up->N, H, 1), "gate_up sb"};
-  r[2] = {down->codes, sdv::q4t_codes_bytes(down->E, H, I, 0), "down codes"};
+  r[2] = {down->codes, tiled_codes_bytes(*down), "down codes"};
   r[3] = {down->sb, sdv::q4t_sb_bytes(down->E, H, I, 0), "down sb"};
-  r[4] = {shared_gate_up ? shared_gate_up->codes : nullptr, shared_gate_up ? sdv::q4t_codes_bytes(1, 2 * I, H, 1) : 0,
+  r[4] = {shared_gate_up ? shared_gate_up->codes : nullptr, shared_gate_up ? tiled_codes_bytes(*shared_gate_up) : 0,
           "shared_gate_up codes"};
   r[5] = {shared_gate_up ? shared_gate_up->sb : nullptr, shared_gate_up ? sdv::q4t_sb_bytes(1, 2 * I, H, 1) : 0,
           "shared_gate_up sb"};
-  r[6] = {shared_down ? shared_down->codes : nullptr, shared_down ? sdv::q4t_codes_bytes(1, H, I, 0) : 0,
+  r[6] = {shared_down ? shared_down->codes : nullptr, shared_down ? tiled_codes_bytes(*shared_down) : 0,
           "shared_down codes"};
   r[7] = {shared_down ? shared_down->sb : nullptr, shared_down ? sdv::q4t_sb_bytes(1, H, I, 0) : 0, "shared_down sb"};
   return 8;
@@ -531,7 +535,7 @@ int sdv_moe_experts_k(const sdv_q4t* gate_up, const sdv_q4t* down, const void* x
                       const sdv_q4t* shared_down, float* partial, sdv_stream_t stream) {
   int st;
   size_t pbytes = 0;
-  if ((st = check_experts(gate_up, down, shared_gate_up, shared_down, k, topk, 0, &pbytes))) return st;
+  if ((st = check_experts(gate_up, down, shared_gate_up, shared_down, k, topk, 0, &pbytes, false))) return st;
   const int H = gate_up->K;
   const void* ptrs[] = {x, union_ids, n_union, pair_off, pair_row, pair_slot, partial};
   const char* names[] = {"x", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot", "partial"};
@@ -566,7 +570,7 @@ int sdv_moe_route_experts_k(const float* logits, int score_mode, int renorm, con
     return fail(SDV_EINVAL, "unknown score mode %d", score_mode);
   size_t pbytes = 0;
   const size_t route_lds = sdv::route_in_experts(k, E) ? sdv::route_experts_lds_bytes(k, E, gate_up->K) : 0;
-  if ((st = check_experts(gate_up, down, shared_gate_up, shared_down, k, topk, route_lds, &pbytes))) return st;
+  if ((st = check_experts(gate_up, down, shared_gate_up, shared_down, k, topk, route_lds, &pbytes, true))) return st;
   const int H = gate_up->K;
   const void* ptrs[] = {logits, x, idx, w, union_ids, n_union, pair_off, pair_row, pair_slot, partial};
   const char* names[] = {"logits", "x", "idx", "w", "union_ids", "n_union", "pair_off", "pair_row", "pair_slot",

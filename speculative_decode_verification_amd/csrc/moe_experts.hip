@@ -46,7 +46,13 @@ namespace {
 using namespace q4;
 
 constexpr int kWaves = 8;
-constexpr int kRing = 4;         // blocks in flight per wave (a multiple of the slice's groups)
+// blocks in flight per wave: 4 one-KB blocks, or 2 two-KB Q8_0 blocks (the
+// same bytes and registers); a multiple of the slice's groups
+template <int FMT>
+constexpr int ring_of() { return FMT == SDV_FMT_Q8_0 ? 2 : 4; }
+// activation sums per 64-element group: one, or one per 32-element Q8_0 block
+template <int FMT>
+constexpr int spg_of() { return FMT == SDV_FMT_Q8_0 ? 2 : 1; }
 constexpr int kSlice = 128;      // intermediate columns per workgroup
 constexpr int kSliceTiles = kSlice / 16;
 constexpr uint32_t kBufferDword3 = 0x00020000u;  // raw buffer resource word 3 (gfx9 family)
@@ -112,21 +118,64 @@ struct Lds {
   size_t xs, xsum, hs, hpart, hrow, total;
 };
 
-// LDS layout: phase A's bf16 x rows and their group sums; phase B's bf16
-// parts of h (written by phase A's epilogue, so they cannot share space with
-// x rows that slower waves may still read), the per-wave partial group sums
-// of h and the rows' group sums.
-__host__ __device__ inline Lds expert_lds(int k, int H) {
+// LDS layout: phase A's bf16 x rows and their group sums (spg per group);
+// phase B's bf16 parts of h (written by phase A's epilogue, so they cannot
+// share space with x rows that slower waves may still read), the per-wave
+// partial group sums of h and the rows' group sums (spg per group).
+__host__ __device__ inline Lds expert_lds(int k, int H, int spg) {
   Lds l;
   const size_t rsA = (size_t)H + 8, rsB = kSlice + 8;
   l.xs = 0;
   l.xsum = (size_t)(k + 1) * rsA * 2;
-  l.hs = (l.xsum + (size_t)32 * (H / 64) * 4 + 15) & ~(size_t)15;
+  l.hs = (l.xsum + (size_t)32 * (H / 64) * spg * 4 + 15) & ~(size_t)15;
   l.hpart = l.hs + (size_t)(3 * k + 1) * rsB * 2;
   l.hrow = l.hpart + (size_t)kPassRows * kSliceTiles * 4;
-  l.total = l.hrow + (size_t)kPassRows * (kSlice / 64) * 4;
+  l.total = l.hrow + (size_t)kPassRows * (kSlice / 64) * spg * 4;
   return l;
 }
+
+// One ring entry: the lane's code words of a (tile, group) block.  Q4: one
+// 16-byte chunk of the 1 KB block; Q3: three words of the 768-byte block;
+// Q8_0: two 16-byte chunks, one from each 1 KB half of the 2 KB block.
+template <int FMT>
+struct Blk {
+  uint4 c;
+};
+template <>
+struct Blk<SDV_FMT_Q8_0> {
+  uint4 c, c2;
+};
+
+// Block blk (in block units of the format) of a tiled code array.
+template <int FMT>
+__device__ __forceinline__ void load_block(Blk<FMT>& b, const void* codes, size_t blk, int lane) {
+  if constexpr (FMT == SDV_FMT_Q8_0) {
+    const uint4* p = static_cast<const uint4*>(codes) + blk * 128;
+    b.c = load_nt(p + lane);  // weights: read once per call
+    b.c2 = load_nt(p + 64 + lane);
+  } else if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
+    const uint32_t* w = static_cast<const uint32_t*>(codes) + blk * 192 + lane;
+    b.c = make_uint4(load_nt(w), load_nt(w + 64), load_nt(w + 128), 0u);
+  } else {
+    b.c = load_nt(static_cast<const uint4*>(codes) + blk * 64 + lane);
+  }
+}
+
+// The group step of the format (q4_core.h): activation sums xr[i][s_idx]
+// (Q4, Q3) or xr[i][2 s_idx + b] (Q8_0).
+template <int ACT, int FMT>
+__device__ __forceinline__ void block_mac(const Blk<FMT>& b, uint32_t sbw, const uint16_t* ap,
+                                          const float* const (&xr)[5], int s_idx, float y[5], DecodeK dk) {
+  if constexpr (FMT == SDV_FMT_Q8_0)
+    group_mac_rows_q8<ACT>(b.c, b.c2, sbw, ap, xr, s_idx, y);
+  else
+    group_mac_rows<ACT, FMT>(b.c, sbw, ap, xr, s_idx, y, dk);
+}
+
+// A lane half reads elements 32 h .. of a Q4 or Q3 group, 8 h .. (every 16)
+// of a Q8_0 group.
+template <int FMT>
+constexpr int half_offset() { return FMT == SDV_FMT_Q8_0 ? 8 : 32; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, (int)kBufferDword3);
@@ -136,8 +185,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t by
 // groups.  The stream is padded to whole ring rounds, so every round is the
 // same straight-line code (static load counter waits); padding steps compute
 // tiles past the last one, whose stores are dropped.
-template <typename Issue>
-__device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)[kRing], const uint32_t (&sbuf)[kRing],
+template <int FMT, typename Issue>
+__device__ __forceinline__ void phase_b(const ExpertArgs& a, const Blk<FMT> (&cbuf)[ring_of<FMT>()],
+                                        const uint32_t (&sbuf)[ring_of<FMT>()],
                                         Issue& issue, const uint16_t* hs, const float* hrow, const int* s_dst,
                                         int nrows, int kr, int j, int wave, int lane, int s_begin, int s_end,
                                         DecodeK dk) {
@@ -145,10 +195,11 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
   const int col = lane & 31, half = lane >> 5;
   const int rsB = kSlice + 8;
   const int slot = slot_of_arow<SDV_ACT_F32>(col, nrows);
-  const uint16_t* ap = hs + (size_t)(slot >= 0 ? slot : 3 * kr) * rsB + half * 32;
+  constexpr int kRing = ring_of<FMT>(), SPG = spg_of<FMT>();
+  const uint16_t* ap = hs + (size_t)(slot >= 0 ? slot : 3 * kr) * rsB + half * half_offset<FMT>();
   const float* xr[5];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) xr[i] = hrow + (i < 4 ? 4 * half + i : 8) * 2;
+  for (int i = 0; i < 5; ++i) xr[i] = hrow + (i < 4 ? 4 * half + i : 8) * 2 * SPG;
   const __amdgpu_buffer_rsrc_t rsrc = out_rsrc(a.partial, a.partial_bytes);
   // byte offset of the output row behind each of this lane's five
   // accumulators (rows 4 * half + i, and row 8), or -1
@@ -177,7 +228,7 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
 #pragma unroll
         for (int v = 0; v < 5; ++v) y[v] = 0.0f;
       }
-      group_mac_rows<SDV_ACT_F32>(cbuf[i], sbuf[i], ap + z + g * 64, xr, z + g, y, dk);
+      block_mac<SDV_ACT_F32, FMT>(cbuf[i], sbuf[i], ap + z + g * 64, xr, z + g, y, dk);
       issue(i, s0 + i + kRing);
       if (g == 1) {
         const int n = t * 32 + col;
@@ -202,9 +253,11 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const uint4 (&cbuf)
 // dispatch itself (route_block, RPL candidates per lane) on the logits, so
 // the routing needs no launch of its own; the results are identical in every
 // workgroup, and workgroup (0, 0) writes them out for the combine.
-template <bool WIDE, int RPL>
+template <bool WIDE, int RPL, int FMT>
 __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   static_assert(!(WIDE && RPL > 0), "the in-kernel dispatch covers one pass of rows");
+  static_assert(RPL == 0 || FMT == SDV_FMT_AFFINE_Q4, "the in-kernel dispatch is built for affine Q4 only");
+  constexpr int kRing = ring_of<FMT>(), SPG = spg_of<FMT>();
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_src[kPassRows], s_dst[kPassRows];
   constexpr int kRS = RPL > 0 ? kPassRows * SDV_MAX_TOPK : 1;
@@ -212,7 +265,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   __shared__ float s_r_w[kRS];
   const int H = a.H, GA = a.GA, GB = a.GB, k = a.k;
   const int kr = min(k, kPassRows);  // rows of the LDS staging; row kr is all zero
-  const Lds L = expert_lds(kr, H);
+  const Lds L = expert_lds(kr, H, SPG);
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   float* xsum = reinterpret_cast<float*>(smem + L.xsum);
   uint16_t* hs = reinterpret_cast<uint16_t*>(smem + L.hs);
@@ -331,7 +384,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   const size_t baseA = ((size_t)e * a.TA + (size_t)j * kSliceTiles + wave) * GA;  // block of step 0
   const size_t baseB = ((size_t)e * a.TB + min(wave, a.TB - 1)) * GB;
 
-  uint4 cbuf[kRing];
+  Blk<FMT> cbuf[kRing];
   uint32_t sbuf[kRing];
   // Load the (codes, scale/bias) block of stream step s into ring slot `slot`.
   // Steps past the end re-read the last block; a wave without blocks reads
@@ -345,7 +398,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     const int q = max(min(s - nA8, nB - 1), 0);
     const int g = min(gB0 + (q & 1), gBlast);               // a 64-wide slice re-reads its only group
     const long blk = inA ? (long)baseA + min(s, nA - 1) : (long)baseB + (long)(q >> 1) * kWaves * GB + g;
-    cbuf[slot] = load_nt((inA ? guc : dnc) + blk * 64 + lane);  // weights: read once per call
+    load_block<FMT>(cbuf[slot], inA ? guc : dnc, (size_t)blk, lane);  // weights: read once per call
     sbuf[slot] = load_nt((inA ? gus : dns) + blk * 32 + col);
   };
   // the unit's (row, slot) pairs go out before the ring, so waiting for them
@@ -375,7 +428,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // rows (MFMA rows without data read them)
   for (int t = tid; t < rsA / 2; t += kThreads) reinterpret_cast<uint32_t*>(xs + (size_t)kr * rsA)[t] = 0u;
   for (int t = tid; t < rsB / 2; t += kThreads) reinterpret_cast<uint32_t*>(hs + (size_t)3 * kr * rsB)[t] = 0u;
-  for (int t = tid; t < G; t += kThreads) xsum[kr * G + t] = 0.0f;
+  for (int t = tid; t < G * SPG; t += kThreads) xsum[kr * G * SPG + t] = 0.0f;
   // One task = (x row i, group g): its 8 blocks of 8 elements are stored in NU
   // order and summed in order, and the group sum adds the 8 block sums
   // pairwise ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7)).
@@ -392,7 +445,13 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
       bsum[q] = acc;
       *reinterpret_cast<uint4*>(xs + (size_t)i * rsA + g * 64 + q * 8) = nu_pack(e8);
     }
-    xsum[i * G + g] = ((bsum[0] + bsum[1]) + (bsum[2] + bsum[3])) + ((bsum[4] + bsum[5]) + (bsum[6] + bsum[7]));
+    if constexpr (SPG == 2) {
+      // Q8_0: one sum per 32-element block, each added pairwise
+      xsum[(i * G + g) * 2] = (bsum[0] + bsum[1]) + (bsum[2] + bsum[3]);
+      xsum[(i * G + g) * 2 + 1] = (bsum[4] + bsum[5]) + (bsum[6] + bsum[7]);
+    } else {
+      xsum[i * G + g] = ((bsum[0] + bsum[1]) + (bsum[2] + bsum[3])) + ((bsum[4] + bsum[5]) + (bsum[6] + bsum[7]));
+    }
   };
   if (tid < nxt) put(tid, xv);
   for (int t = tid + kThreads; t < nxt; t += kThreads) {
@@ -429,14 +488,14 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // ---- phase A: one fused gate/up tile over all GA groups
   {
     const int src = col < nrows ? s_src[col] : -1;
-    const uint16_t* ap = xs + (size_t)(src >= 0 ? src : kr) * rsA + half * 32;
+    const uint16_t* ap = xs + (size_t)(src >= 0 ? src : kr) * rsA + half * half_offset<FMT>();
     // group sums of the x row behind each accumulator (row k is all zero)
     const float* xr[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int r = i < 4 ? 4 * half + i : 8;
       const int sr = r < nrows ? s_src[r] : -1;
-      xr[i] = xsum + (sr >= 0 ? sr : kr) * G;
+      xr[i] = xsum + (sr >= 0 ? sr : kr) * G * SPG;
     }
     float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     // whole rounds, then a last round whose steps past nA compute nothing
@@ -445,7 +504,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = s0 + i;
-        group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+        block_mac<SDV_ACT_BF16, FMT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
         issue(i, s + kRing);
       }
     }
@@ -453,7 +512,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = nAfull + i;
-        if (s < nA) group_mac_rows<SDV_ACT_BF16>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
+        if (s < nA) block_mac<SDV_ACT_BF16, FMT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
         issue(i, s + kRing);
       }
     }
@@ -490,16 +549,25 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     }
   }
   __syncthreads();  // every wave's part of h is in LDS
-  // each row's group sums: the four 16-column partial sums of the group, in order
-  if (tid < kPassRows * 2) {
-    const int r = tid >> 1, g = tid & 1;
-    const float* hp = hpart + r * kSliceTiles + 4 * g;
-    hrow[r * 2 + g] = r < nrows ? (hp[0] + hp[1]) + (hp[2] + hp[3]) : 0.0f;
+  // each row's group sums: the four 16-column partial sums of the group, in
+  // order (Q8_0: the two of each 32-element block)
+  if constexpr (SPG == 2) {
+    if (tid < kPassRows * 4) {
+      const int r = tid >> 2, b = tid & 3;
+      const float* hp = hpart + r * kSliceTiles + 2 * b;
+      hrow[r * 4 + b] = r < nrows ? hp[0] + hp[1] : 0.0f;
+    }
+  } else {
+    if (tid < kPassRows * 2) {
+      const int r = tid >> 1, g = tid & 1;
+      const float* hp = hpart + r * kSliceTiles + 4 * g;
+      hrow[r * 2 + g] = r < nrows ? (hp[0] + hp[1]) + (hp[2] + hp[3]) : 0.0f;
+    }
   }
   __syncthreads();
 
   // ---- phase B: down tiles over the slice's groups
-  phase_b(a, cbuf, sbuf, issue, hs, hrow, s_dst, nrows, kr, j, wave, lane, nA8, total, dk);
+  phase_b<FMT>(a, cbuf, sbuf, issue, hs, hrow, s_dst, nrows, kr, j, wave, lane, nA8, total, dk);
 }
 
 }  // namespace
@@ -507,7 +575,9 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 int expert_slices(int I) { return (I + kSlice - 1) / kSlice; }
 
 // a unit stages at most min(k, kPassRows) rows (one pass of its rows)
-size_t expert_lds_bytes(int k, int H) { return expert_lds(k < kPassRows ? k : kPassRows, H).total; }
+size_t expert_lds_bytes(int k, int H, int fmt) {
+  return expert_lds(k < kPassRows ? k : kPassRows, H, fmt == SDV_FMT_Q8_0 ? 2 : 1).total;
+}
 
 size_t expert_partial_bytes(int k, int topk, int H, int I) {
   return (size_t)expert_slices(I) * k * (topk + 1) * H * 4;
@@ -517,12 +587,12 @@ namespace {
 
 // Raise the kernel's dynamic LDS limit once per process (the largest size
 // asked for so far; the attribute is per function, not per device).
-template <bool WIDE, int RPL>
+template <bool WIDE, int RPL, int FMT>
 hipError_t raise_lds_limit(size_t lds) {
   static std::atomic<size_t> lds_limit{65536};
   size_t cur = lds_limit.load(std::memory_order_relaxed);
   if (lds > cur) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_experts_kernel<WIDE, RPL>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_experts_kernel<WIDE, RPL, FMT>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
@@ -531,11 +601,11 @@ hipError_t raise_lds_limit(size_t lds) {
   return hipSuccess;
 }
 
-template <bool WIDE, int RPL>
+template <bool WIDE, int RPL, int FMT = SDV_FMT_AFFINE_Q4>
 hipError_t launch_experts(const ExpertArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  const hipError_t err = raise_lds_limit<WIDE, RPL>(lds);
+  const hipError_t err = raise_lds_limit<WIDE, RPL, FMT>(lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((moe_experts_kernel<WIDE, RPL>), grid, dim3(kExpertThreads), lds, st, a);
+  hipLaunchKernelGGL((moe_experts_kernel<WIDE, RPL, FMT>), grid, dim3(kExpertThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -578,13 +648,19 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
   a.pair_off = pair_off;
   a.pair_row = pair_row;
   a.pair_slot = pair_slot;
-  const size_t lds = expert_lds_bytes(k, a.H);
+  const size_t lds = expert_lds_bytes(k, a.H, gu.format);
   const int units = k * topk + (sgu ? 1 : 0);
   // every width takes the pass form: a unit stages only its own x rows,
   // after its pair loads (about 1.1 rows per routed unit at nine rows,
   // instead of all k)
   const int passes = (k + kPassRows - 1) / kPassRows;
-  return launch_experts<true, 0>(a, dim3(a.S, units, passes), lds, st);
+  const dim3 grid(a.S, units, passes);
+  switch (gu.format) {
+    case SDV_FMT_AFFINE_Q4: return launch_experts<true, 0, SDV_FMT_AFFINE_Q4>(a, grid, lds, st);
+    case SDV_FMT_Q8_0: return launch_experts<true, 0, SDV_FMT_Q8_0>(a, grid, lds, st);
+    case SDV_FMT_AFFINE_Q3: return launch_experts<true, 0, SDV_FMT_AFFINE_Q3>(a, grid, lds, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Whether the router dispatch runs inside the expert kernel: one pass of
@@ -592,7 +668,7 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
 bool route_in_experts(int k, int E) { return k <= kPassRows && E <= kExpertThreads; }
 
 size_t route_experts_lds_bytes(int k, int E, int H) {
-  const size_t a = expert_lds_bytes(k, H), b = route_scratch(E).bytes;
+  const size_t a = expert_lds_bytes(k, H, SDV_FMT_AFFINE_Q4), b = route_scratch(E).bytes;
   return a > b ? a : b;
 }
 

@@ -23,9 +23,9 @@ from ._lib import MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX
 class MoeLayer:
     def __init__(self, gate_up, down, k, topk, score_mode, renorm, shared_gate_up=None, shared_down=None,
                  fuse_shared=True, fused_experts=None, route_in_experts=False):
-        """fused_experts: the one-launch expert kernel (affine Q4 weights);
-        None picks it for affine-Q4 weights and the two gathered launches
-        otherwise (Q8_0, Q3).  route_in_experts: with the fused expert
+        """fused_experts: the one-launch expert kernel; None picks it when the
+        four weights share one format (affine Q4, Q8_0 or affine Q3) and the
+        two gathered launches otherwise.  route_in_experts: with the fused expert
         kernel, the router dispatch runs in one call with it
         (sdv_moe_route_experts_k) rather than in a launch of its own.  Off by
         default: every expert workgroup then waits for its own dispatch, which
@@ -33,8 +33,10 @@ class MoeLayer:
         self.gate_up, self.down = gate_up, down
         weights = [w for w in (gate_up, down, shared_gate_up, shared_down) if w is not None]
         if fused_experts is None:
-            fused_experts = all(w.fmt == ops.FMT_AFFINE_Q4 for w in weights)
+            fused_experts = len({w.fmt for w in weights}) == 1
         self.fused_experts = fused_experts
+        if route_in_experts and gate_up.fmt != ops.FMT_AFFINE_Q4:
+            raise ValueError("the router dispatch inside the expert kernel takes affine-Q4 weights")
         self.route_in_experts = bool(fused_experts and route_in_experts)
         self.shared_gate_up, self.shared_down = shared_gate_up, shared_down
         self.fused_shared = (fuse_shared and shared_gate_up is not None and

@@ -282,9 +282,12 @@ def test_experts_validation(lib):
     wide = q4t(E=E, N=2 * I, K=16384, fused=1)
     assert experts(lib, wide, q4t(E=E, N=16384, K=I, codes=P + 0x200000, sb=P + 0x300000), k=9) == L.SDV_ELAYOUT
     assert "LDS" in lib.sdv_last_error().decode()
-    # the fused expert kernel takes affine Q4 only
-    assert experts(lib, q4t(E=E, N=2 * I, K=H, fused=1, fmt=1), dn) == L.SDV_ELAYOUT
-    assert "Q8_0" in lib.sdv_last_error().decode()
+    # the four weights of the fused expert kernel share one format
+    assert experts(lib, q4t(E=E, N=2 * I, K=H, fused=1, fmt=L.FMT_Q8_0), dn) == L.SDV_ELAYOUT
+    assert "one weight format" in lib.sdv_last_error().decode()
+    q3dn = q4t(E=E, N=H, K=I, codes=P + 0x200000, sb=P + 0x300000, fmt=L.FMT_AFFINE_Q3)
+    assert experts(lib, q4t(E=E, N=2 * I, K=H, fused=1, fmt=L.FMT_AFFINE_Q3), q3dn, sgu=sgu, sdn=sdn) == L.SDV_ELAYOUT
+    assert "one weight format" in lib.sdv_last_error().decode()
     gu9 = q4t(E=E, N=2 * 1088, K=H, fused=1)
     assert experts(lib, gu9, q4t(E=E, N=H, K=1088, codes=P + 0x2000000, sb=P + 0x3000000)) == L.SDV_ERANGE
 
@@ -318,9 +321,10 @@ def test_route_experts_validation(lib):
     assert route_experts(lib, gu, dn, partial=P + 0x80) == L.SDV_EALIAS                   # over the gate/up codes
     assert route_experts(lib, gu, dn, partial=outs[2]) == L.SDV_EALIAS                    # over union_ids
     assert route_experts(lib, gu, dn, outs=[outs[0]] * 7) == L.SDV_EALIAS                 # outputs overlap
-    q8 = q4t(E=E, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000)
-    q8.format = L.FMT_Q8_0
-    assert route_experts(lib, q8, dn) == L.SDV_ELAYOUT                                    # affine Q4 only
+    q8 = q4t(E=E, N=2 * I, K=H, fused=1, codes=P, sb=P + 0x100000, fmt=L.FMT_Q8_0)
+    q8dn = q4t(E=E, N=H, K=I, codes=dn.codes, sb=dn.sb, fmt=L.FMT_Q8_0)
+    assert route_experts(lib, q8, q8dn) == L.SDV_ELAYOUT                                  # affine Q4 only
+    assert "affine Q4" in lib.sdv_last_error().decode()
 
 
 def test_combine_sliced_validation(lib):

@@ -1,6 +1,6 @@
 """GPU parity of the affine-Q3/g64 format (mere.run transfer report, "Shared
 architecture and implemented paths": the gathered expert kernel's Q3
-specialization) in the dense and gathered products: against the oracle
+specialization) in the dense, gathered and fused-expert products: against the oracle
 within tolerance, bit-exact on an integer-exact case, every row
 bit-identical to its width-1 run, at narrow and wide widths."""
 
@@ -85,26 +85,42 @@ def test_dense_q3_gate_up_wide():
         assert np.array_equal(y1, y[k - 1])
 
 
-@pytest.mark.parametrize("k", [9, 32])
-def test_gathered_q3_moe_layer(k):
-    """A Q3 MoE layer (routed and shared experts in Q3) on the gathered
-    launches: against the oracle, rows against width-1 layers bit for bit."""
-    ops, pipeline = _mods()
-    E, H, I, topk = 16, 256, 128, 4
-    banner(f"q3 moe layer k={k}")
+def _slots(layer):
+    """Per-slot outputs of the fused expert kernel: slices added in order."""
+    xp = to_np(layer.xpartial)
+    acc = xp[0].copy()
+    for j in range(1, xp.shape[0]):
+        acc = acc + xp[j]
+    return acc
+
+
+def _q3_bank(seed, E, H, I):
     w = {}
     for name, kind, e, n, kk, fused in (("gu", GATEUP, E, 2 * I, H, True), ("dn", DOWN, E, H, I, False),
                                          ("sgu", SHARED_GATEUP, 1, 2 * I, H, True),
                                          ("sdn", SHARED_DOWN, 1, H, I, False)):
-        codes, sc, bi, _ = synth.q3_weight(27, kind, 0, e, n, kk)
+        codes, sc, bi, _ = synth.q3_weight(seed, kind, 0, e, n, kk)
         w[name] = ((codes, sc, bi), q3_device(codes, sc, bi, fused))
+    return w
+
+
+@pytest.mark.parametrize("k", [9, 32])
+@pytest.mark.parametrize("fused", [False, True])
+def test_q3_moe_layer(k, fused):
+    """A Q3 MoE layer (routed and shared experts in Q3) on the gathered
+    launches and on the fused expert kernel: against the oracle, rows
+    against width-1 layers bit for bit."""
+    ops, pipeline = _mods()
+    E, H, I, topk = 16, 256, 128, 4
+    banner(f"q3 moe layer k={k} fused={fused}")
+    w = _q3_bank(27, E, H, I)
     inp = synth.moe_layer_inputs(27, 0, k, H, E)
     deq = lambda nm, e: oracle.dequant_q3(*(a[e] for a in w[nm][0]))
 
     def run(rows):
         layer = pipeline.MoeLayer(w["gu"][1], w["dn"][1], rows["x"].shape[0], topk, ops.ROUTE_SOFTMAX, False,
-                                  w["sgu"][1], w["sdn"][1])
-        assert not layer.fused_experts and layer.fused_shared
+                                  w["sgu"][1], w["sdn"][1], fused_experts=fused)
+        assert layer.fused_experts == fused and layer.fused_shared
         y = layer(sdev.upload_bf16(rows["x"], DEV), sdev.upload_f32(rows["logits"], DEV),
                   sdev.upload_f32(rows["z"], DEV))
         torch.cuda.synchronize()
@@ -115,9 +131,44 @@ def test_gathered_q3_moe_layer(k):
                             lambda e: deq("dn", e), topk, "softmax", False, z=inp["z"],
                             shared_gate_up=deq("sgu", 0), shared_down=deq("sdn", 0))
     assert np.array_equal(to_np(layer.route.idx), ref["idx"])
-    assert_close(to_np(layer.h), ref["h"], "q3 h")
-    assert_close(to_np(layer.partial), ref["partial"], "q3 partial")
+    if fused:
+        P = _slots(layer)
+        assert_close(P[:, :topk], ref["partial"], "q3 fused slot outputs")
+        assert_close(P[:, topk], ref["shared"], "q3 fused shared expert")
+    else:
+        assert_close(to_np(layer.h), ref["h"], "q3 h")
+        assert_close(to_np(layer.partial), ref["partial"], "q3 partial")
     assert_close(y, ref["y"], "q3 y")
     for r in (0, k - 1):
-        _, y1 = run({n: v[r:r + 1] for n, v in inp.items()})
+        l1, y1 = run({n: v[r:r + 1] for n, v in inp.items()})
         assert np.array_equal(y1[0], y[r]), r
+        if fused:
+            assert np.array_equal(_slots(l1)[0], _slots(layer)[r]), r
+
+
+@pytest.mark.parametrize("k", [9, 2])
+def test_q3_fused_flash_next_geometry(k):
+    """The fused expert kernel on affine-Q3 weights of the Flash-Next expert
+    geometry (hidden 2560, intermediate 640) with 16 experts, top-10 sigmoid
+    and the shared expert: against the oracle and the gathered launches."""
+    ops, pipeline = _mods()
+    E, H, I, topk = 16, 2560, 640, 10
+    banner(f"q3 fused flash-next geometry k={k}")
+    w = _q3_bank(28, E, H, I)
+    inp = synth.moe_layer_inputs(28, k, k, H, E)
+    deq = lambda nm, e: oracle.dequant_q3(*(a[e] for a in w[nm][0]))
+    args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV), sdev.upload_f32(inp["z"], DEV))
+    fused = pipeline.MoeLayer(w["gu"][1], w["dn"][1], k, topk, ops.ROUTE_SIGMOID, True, w["sgu"][1], w["sdn"][1])
+    assert fused.fused_experts
+    y = to_np(fused(*args))
+    gathered = pipeline.MoeLayer(w["gu"][1], w["dn"][1], k, topk, ops.ROUTE_SIGMOID, True, w["sgu"][1],
+                                 w["sdn"][1], fused_experts=False)
+    yg = to_np(gathered(*args))
+    ref = oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], lambda e: deq("gu", e),
+                            lambda e: deq("dn", e), topk, "sigmoid", True, z=inp["z"],
+                            shared_gate_up=deq("sgu", 0), shared_down=deq("sdn", 0))
+    P = _slots(fused)
+    assert_close(P[:, :topk], ref["partial"], "q3 fused slot outputs")
+    assert_close(P[:, topk], ref["shared"], "q3 fused shared expert")
+    assert_close(y, ref["y"], "q3 fused y")
+    assert_close(yg, ref["y"], "q3 gathered y")

@@ -1,9 +1,9 @@
 """GPU parity of the Q8_0 weight format (Red Lite dev45, "What it is": the
 MTP block's Q8_0 experts; mere.run transfer report, "Shared architecture and
 implemented paths": Q8 router and shared-gate weights) in the dense and
-gathered products: against the oracle within tolerance, bit-exact on an
-integer-exact case, every row bit-identical to its width-1 run, at narrow and
-wide widths."""
+gathered products and the fused expert kernel: against the oracle within
+tolerance, bit-exact on an integer-exact case, every row bit-identical to its
+width-1 run, at narrow and wide widths."""
 
 import numpy as np
 import pytest
@@ -95,14 +95,24 @@ def q8_bank(cfg, kind, layer, E, N, K, fused):
     return (qs, d), q8_device(qs, d, fused)
 
 
+def _slots(layer):
+    """Per-slot outputs of the fused expert kernel: slices added in order."""
+    xp = to_np(layer.xpartial)
+    acc = xp[0].copy()
+    for j in range(1, xp.shape[0]):
+        acc = acc + xp[j]
+    return acc
+
+
 @pytest.mark.parametrize("k", [9, 32])
-def test_gathered_q8_moe_layer(k):
-    """A Q8_0 MoE layer (routed experts and the shared expert in Q8_0): the
-    layer takes the gathered launches; against the oracle, and rows against
-    width-1 layers bit for bit."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_q8_moe_layer(k, fused):
+    """A Q8_0 MoE layer (routed experts and the shared expert in Q8_0) on the
+    gathered launches and on the fused expert kernel: against the oracle, and
+    rows against width-1 layers bit for bit."""
     ops, pipeline = _mods()
     E, H, I, topk = 16, 256, 128, 4
-    banner(f"q8 moe layer k={k}")
+    banner(f"q8 moe layer k={k} fused={fused}")
     (gq, gd), gu = q8_bank(22, GATEUP, 0, E, 2 * I, H, True)
     (dq, dd), dn = q8_bank(22, DOWN, 0, E, H, I, False)
     (sgq, sgd), sgu = q8_bank(22, SHARED_GATEUP, 0, 1, 2 * I, H, True)
@@ -110,8 +120,9 @@ def test_gathered_q8_moe_layer(k):
     inp = synth.moe_layer_inputs(22, 0, k, H, E)
 
     def run(rows):
-        layer = pipeline.MoeLayer(gu, dn, rows["x"].shape[0], topk, ops.ROUTE_SIGMOID, True, sgu, sdn)
-        assert not layer.fused_experts and layer.fused_shared
+        layer = pipeline.MoeLayer(gu, dn, rows["x"].shape[0], topk, ops.ROUTE_SIGMOID, True, sgu, sdn,
+                                  fused_experts=fused)
+        assert layer.fused_experts == fused and layer.fused_shared
         y = layer(sdev.upload_bf16(rows["x"], DEV), sdev.upload_f32(rows["logits"], DEV),
                   sdev.upload_f32(rows["z"], DEV))
         torch.cuda.synchronize()
@@ -123,13 +134,51 @@ def test_gathered_q8_moe_layer(k):
                             topk, "sigmoid", True, z=inp["z"], shared_gate_up=oracle.dequant_q8_0(sgq[0], sgd[0]),
                             shared_down=oracle.dequant_q8_0(sdq[0], sdd[0]))
     assert np.array_equal(to_np(layer.route.idx), ref["idx"])
-    assert_close(to_np(layer.h), ref["h"], "q8 h")
-    assert_close(to_np(layer.partial), ref["partial"], "q8 partial")
-    assert_close(to_np(layer.sh_out), ref["shared"], "q8 shared expert")
+    if fused:
+        P = _slots(layer)
+        assert_close(P[:, :topk], ref["partial"], "q8 fused slot outputs")
+        assert_close(P[:, topk], ref["shared"], "q8 fused shared expert")
+    else:
+        assert_close(to_np(layer.h), ref["h"], "q8 h")
+        assert_close(to_np(layer.partial), ref["partial"], "q8 partial")
+        assert_close(to_np(layer.sh_out), ref["shared"], "q8 shared expert")
     assert_close(y, ref["y"], "q8 y")
     for r in (0, k - 1):
-        _, y1 = run({n: v[r:r + 1] for n, v in inp.items()})
+        l1, y1 = run({n: v[r:r + 1] for n, v in inp.items()})
         assert np.array_equal(y1[0], y[r]), r
+        if fused:
+            assert np.array_equal(_slots(l1)[0], _slots(layer)[r]), r
+
+
+@pytest.mark.parametrize("k", [9, 3])
+def test_q8_fused_flash_next_geometry(k):
+    """The fused expert kernel on Q8_0 weights of the Flash-Next expert
+    geometry (hidden 2560, intermediate 640: five slices, 40-group gate/up
+    streams) with 16 experts, top-10 sigmoid and the shared expert: against
+    the oracle and the gathered launches."""
+    ops, pipeline = _mods()
+    E, H, I, topk = 16, 2560, 640, 10
+    banner(f"q8 fused flash-next geometry k={k}")
+    (gq, gd), gu = q8_bank(25, GATEUP, 0, E, 2 * I, H, True)
+    (dq, dd), dn = q8_bank(25, DOWN, 0, E, H, I, False)
+    (sgq, sgd), sgu = q8_bank(25, SHARED_GATEUP, 0, 1, 2 * I, H, True)
+    (sdq, sdd), sdn = q8_bank(25, SHARED_DOWN, 0, 1, H, I, False)
+    inp = synth.moe_layer_inputs(25, k, k, H, E)
+    args = (sdev.upload_bf16(inp["x"], DEV), sdev.upload_f32(inp["logits"], DEV), sdev.upload_f32(inp["z"], DEV))
+    fused = pipeline.MoeLayer(gu, dn, k, topk, ops.ROUTE_SIGMOID, True, sgu, sdn)
+    assert fused.fused_experts
+    y = to_np(fused(*args))
+    gathered = pipeline.MoeLayer(gu, dn, k, topk, ops.ROUTE_SIGMOID, True, sgu, sdn, fused_experts=False)
+    yg = to_np(gathered(*args))
+    ref = oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"],
+                            lambda e: oracle.dequant_q8_0(gq[e], gd[e]), lambda e: oracle.dequant_q8_0(dq[e], dd[e]),
+                            topk, "sigmoid", True, z=inp["z"], shared_gate_up=oracle.dequant_q8_0(sgq[0], sgd[0]),
+                            shared_down=oracle.dequant_q8_0(sdq[0], sdd[0]))
+    P = _slots(fused)
+    assert_close(P[:, :topk], ref["partial"], "q8 fused slot outputs")
+    assert_close(P[:, topk], ref["shared"], "q8 fused shared expert")
+    assert_close(y, ref["y"], "q8 fused y")
+    assert_close(yg, ref["y"], "q8 gathered y")
 
 
 def test_q8_mtp_block_geometry():
@@ -150,14 +199,17 @@ def test_q8_mtp_block_geometry():
         assert_close(y, ref["y"], f"q8 mtp y k={k}")
 
 
-def test_fused_expert_kernel_rejects_q8():
-    ops, _ = _mods()
-    banner("q8 fused experts rejected")
+def test_route_in_experts_rejects_q8():
+    """The router dispatch inside the expert kernel is built for affine Q4
+    only; Q8_0 layers route with their own launch."""
+    ops, pipeline = _mods()
+    banner("q8 route+experts rejected")
     E, H, I = 4, 128, 64
     _, gu = q8_bank(24, GATEUP, 0, E, 2 * I, H, True)
     _, dn = q8_bank(24, DOWN, 0, E, H, I, False)
-    route = ops.route_buffers(2, 2, DEV)
     x = torch.zeros((2, H), dtype=torch.int16, device=DEV)
-    part = ops.experts_partial(2, 2, H, I, DEV)
-    with pytest.raises(ops.SdvError, match="Q8_0"):
-        ops.moe_experts_k(gu, dn, x, route, 2, 2, partial=part)
+    logits = torch.zeros((2, E), dtype=torch.float32, device=DEV)
+    with pytest.raises(ops.SdvError, match="affine Q4"):
+        ops.moe_route_experts_k(logits, ops.ROUTE_SOFTMAX, False, gu, dn, x, 2)
+    with pytest.raises(ValueError, match="affine-Q4"):
+        pipeline.MoeLayer(gu, dn, 2, 2, ops.ROUTE_SOFTMAX, False, route_in_experts=True)
