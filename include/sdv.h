@@ -330,6 +330,8 @@ SDV_API int sdv_gather_qmv_k(const sdv_q4t *bank, int mode, const void *act, int
  *   partial    device fp32 [S][k][topk + 1][H] (sdv_moe_experts_partial_bytes); entries of
  *              slots without an expert, and slot topk without a shared expert, are not written
  * H and I must be multiples of 64, I at most 1024; LDS limits H (about 7000 at k = 9).
+ * The four weights share one format: affine Q4, Q8_0 or affine Q3 (the
+ * descriptors' format field; mixed formats are ELAYOUT).
  * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE, EALIAS, EHIP.
  */
 SDV_API int sdv_moe_experts_k(const sdv_q4t *gate_up, const sdv_q4t *down, const void *x,
@@ -347,7 +349,9 @@ SDV_API int sdv_moe_experts_k(const sdv_q4t *gate_up, const sdv_q4t *down, const
  * routing needs no launch of its own.  Otherwise it runs the two launches.
  * The outputs equal those of the two calls bit for bit.  Every expert
  * workgroup then waits for the whole dispatch before its first weight load:
- * at 512 experts and nine rows the two separate launches are faster.
+ * at 512 experts and nine rows the two separate launches are faster.  The
+ * weights must be affine Q4 (ELAYOUT otherwise: route Q8_0 and Q3 layers
+ * with sdv_moe_route_k, then call sdv_moe_experts_k).
  *   logits, score_mode, renorm  as sdv_moe_route_k (E = gate_up->E)
  *   idx, w, union_ids, n_union, pair_off, pair_row, pair_slot  outputs, as sdv_moe_route_k
  *   gate_up, down, x, shared_gate_up, shared_down, partial  as sdv_moe_experts_k
