@@ -434,6 +434,73 @@ def cpu_baseline(k=9, min_seconds=10.0, max_layers=16, threads_limit=None):
             "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
 
 
+def cpu_configs(threads_limit=None):
+    """The CPU oracle (untuned numpy fp64) on one unit of each other
+    configuration, per width: the dense 5120 x 5120 projection (rows/s of one
+    projection, widths 1/4/8/9), one 256-expert MoE layer (rows/s of a
+    40-layer step, widths 2..9: route, union experts dequantised from the
+    layer's bank, gate/up, down, combine) and one 36-layer GDN step's layer
+    (rows/s of a 36-layer step, widths 1..9: the k-row recurrence with its
+    snapshots).  Each unit runs once per width; generation is outside the
+    timed region; each configuration's first run is an untimed warm-up."""
+    import oracle
+    import synth
+    from synth import configs
+    from synth.inputs import DENSE_W, DOWN, GATEUP
+
+    if threads_limit is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads_limit):
+            r = cpu_configs()
+        r["cores"] = threads_limit
+        return r
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    out = {"cores": threads, "kind": "oracle", "unit": "rows/s"}
+    c1 = configs.C1
+    N, K = c1.dense
+    codes, sc, bi = synth.dense_weight(c1.cid, DENSE_W, 0, N, K)
+    dense = {}
+    oracle.qmv(codes, sc, bi, oracle.bf16_to_f64(synth.activations(c1.cid, 0, 1, K)))  # warm-up, untimed
+    for k in c1.widths:
+        x = oracle.bf16_to_f64(synth.activations(c1.cid, 0, k, K))
+        t0 = time.perf_counter()
+        oracle.qmv(codes, sc, bi, x)
+        dense[f"k{k}"] = round(k / (time.perf_counter() - t0), 2)
+    out["dense5120"] = {"what": "rows/s of one 5120 x 5120 projection", "widths": dense}
+    c2 = configs.C2
+    m = c2.moe
+    E, H, I, topk = m.experts, m.hidden, m.inter, m.topk
+    gk, dk = synth.bank_keys(c2.cid, GATEUP, 0), synth.bank_keys(c2.cid, DOWN, 0)
+    moe, cache_g, cache_d = {}, {}, {}
+    for k in (c2.widths[0],) + tuple(c2.widths):  # the first width twice: its first run is a warm-up
+        inp = synth.moe_layer_inputs(c2.cid, 0, k, H, E)
+        idx, _ = oracle.route(inp["logits"], topk, m.mode, m.renorm)
+        for e in sorted(set(idx.ravel().tolist())):
+            if e not in cache_g:
+                cache_g[e] = synth.q4_rows(gk, E, 2 * I, H, expert=e)
+                cache_d[e] = synth.q4_rows(dk, E, H, I, expert=e)
+        t0 = time.perf_counter()
+        oracle.moe_verify(oracle.bf16_to_f64(inp["x"]), inp["logits"], lambda e: oracle.dequant(*cache_g[e]),
+                          lambda e: oracle.dequant(*cache_d[e]), topk, m.mode, m.renorm)
+        moe[f"k{k}"] = round(k / ((time.perf_counter() - t0) * c2.layers), 3)
+    out["ornith_moe"] = {"what": f"rows/s of a {c2.layers}-layer step, one layer timed", "widths": moe}
+    c3 = configs.C3
+    g = c3.gdn
+    S = synth.gdn_state(c3.cid, 0, g.hv, g.dv, g.dk)
+    gdn = {}
+    for k in (c3.widths[0],) + tuple(c3.widths):  # the first width twice: its first run is a warm-up
+        inp = synth.gdn_layer_inputs(c3.cid, 0, k, g.hv, g.hk, g.dk, g.dv)
+        t0 = time.perf_counter()
+        oracle.gdn_verify(S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+        gdn[f"k{k}"] = round(k / ((time.perf_counter() - t0) * c3.layers), 2)
+    out["gdn36"] = {"what": f"rows/s of a {c3.layers}-layer step, one layer timed", "widths": gdn}
+    return out
+
+
 def dense_projection(dev, timer, n_weights=64, reps=4):
     """sdv_qmv_k on the dense 5120 x 5120 shape: 64 distinct weights (944 MB
     of affine Q4, more than the last-level cache) launched back to back at
@@ -881,11 +948,14 @@ def main():
         log("timing the Flash-Next MoE layer in affine Q4, Q8_0 and affine Q3 (fused and gathered) ...")
         extra["format_moe"] = format_moe(dev)
 
-    cpu = cpu1 = None
+    cpu = cpu1 = cpu_cfg = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample (all host cores, then one) ...")
         cpu = cpu_baseline(k)
         cpu1 = cpu_baseline(k, min_seconds=10.0, max_layers=2, threads_limit=1)
+        if not args.no_extra_configs:
+            log("timing the CPU oracle on the other configurations' units (all host cores, then one) ...")
+            cpu_cfg = {"all_cores": cpu_configs(), "one_core": cpu_configs(threads_limit=1)}
 
     out = {
         "metric": METRIC,
@@ -921,6 +991,7 @@ def main():
         "dense_qmv_k": dense,
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,
+        "cpu_other_configs": cpu_cfg,
         "accepted_count": "read back from the device every timed step (one host synchronisation per step)",
         **extra,
         "wall_s_timed": round(wall, 3),
