@@ -299,6 +299,207 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   }
 }
 
+// Wide form: bf16 activations, more rows than one narrow pass (up to 32),
+// affine Q4 or Q3.  The 32 rows of a tile's activation slices do not fit the
+// LDS (32 rows of K = 5120 are 328 KB), so each wave reads the activation
+// rows of one group at a time (an L2 hit after the first tile) in its load
+// ring: lane l loads 8-element block l % 8 of rows l / 8 + 8 j (four loads,
+// 8 cache lines each), NU-packs and sums it, and passes it through a small
+// per-wave LDS tile to the lane that feeds it to the MFMA (lane (row r, half
+// h) takes blocks 4 h .. 4 h + 3 of row r).  The group sum of a row adds its
+// 8 block sums across the 8 lanes that hold them; the sums meet in a per-wave
+// table, read back in the accumulator layout (lane half h holds rows
+// 8 q + 4 h + 0..3).  A wave of this form takes two
+// consecutive K ranges of the narrow kernel (the registers of 32-row operands
+// allow half as many waves), one after the other, and keeps their results
+// apart.  The K ranges, the group step (the same MFMA chain and epilogue),
+// the order of every sum and the cross-range sum are the narrow kernel's, so
+// each row equals its narrow (and width-1) result bit for bit.
+constexpr int kWideTileRow = 9;  // 16-byte blocks per tile row: 8 and one of padding
+
+// sum8 by DPP moves within each 8-lane half row (pairs, then quads, then the
+// two quads by the half-row mirror): ((b0 + b1) + (b2 + b3)) + ((b4 + b5) +
+// (b6 + b7)) in every lane, the same value as sum8.
+__device__ __forceinline__ float sum8_dpp(float x) {
+  auto dpp = [](float v, int ctrl) -> float {
+    switch (ctrl) {
+      case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    }
+  };
+  x = x + dpp(x, 0xB1);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  x = x + dpp(x, 0x4E);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  return x + dpp(x, 0x141);  // row_half_mirror: lane 7 - lane within 8
+}
+
+template <int FMT, int MODE, int PF>
+__global__ __launch_bounds__(512, 1) void q4_dense_wide_kernel(DenseArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int t = blockIdx.x;
+  const int G = a.G, K = a.K, k = a.k, nw = a.nw;  // nw: the narrow kernel's K ranges
+  // ranges r0 = 2 wave and r0 + 1 (if any): groups [gb, gm) and [gm, ge)
+  const int r0 = 2 * wave, nr = min(2, nw - r0);
+  const int gb = __builtin_amdgcn_readfirstlane((G * r0) / nw);
+  const int gm = __builtin_amdgcn_readfirstlane((G * (r0 + 1)) / nw);
+  const int ge = __builtin_amdgcn_readfirstlane((G * (r0 + nr)) / nw);
+  const int ga = gm - gb, gn = ge - gb;  // steps of the first range, of both
+  float* red = reinterpret_cast<float*>(smem);                          // [nw][32][33]
+  float* xtab = red + (size_t)nw * 32 * 33 + wave * 32;                 // the current group's row sums
+  uint4* xt = reinterpret_cast<uint4*>(red + (size_t)nw * 32 * 33 + (size_t)((nw + 1) / 2) * 32) +
+              (size_t)wave * 32 * kWideTileRow;                         // the group's rows, NU-packed blocks
+
+  const uint4* const codes = a.codes[blockIdx.y];
+  const uint32_t* const sbp = a.sb[blockIdx.y];
+  float* const out = a.out[blockIdx.y];
+  const size_t blk0 = (size_t)t * G + gb;
+  // load j of a group: block lane % 8 of row lane / 8 + 8 j (rows past k: zeros)
+  const int xr0 = lane >> 3, xq = lane & 7;
+  const uint4* const xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.act) + (size_t)gb * 64 + xq * 8);
+  uint4 cbuf[PF], xbuf[PF][4];
+  uint32_t sbuf[PF];
+  auto issue = [&](int slot, int s) {
+    const int g = min(s, gn - 1);
+    const size_t blk = blk0 + g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = xr0 + 8 * j;
+      xbuf[slot][j] = row < k ? xp[(size_t)row * (K / 8) + g * 8] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(codes) + blk * 192 + lane;
+      cbuf[slot] = make_uint4(load_nt(w), load_nt(w + 64), load_nt(w + 128), 0u);
+    } else {
+      cbuf[slot] = load_nt(codes + blk * 64 + lane);  // weights: read once per call
+    }
+    sbuf[slot] = load_nt(sbp + blk * 32 + col);
+  };
+#pragma unroll
+  for (int i = 0; i < PF; ++i) issue(i, i);
+
+  const DecodeK dk = decode_k();
+  float y[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) y[v] = 0.0f;
+  // a range's results go to its row of the cross-range table
+  auto put = [&](int r) {
+    float* myred = red + (size_t)r * 32 * 33;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 8 * (v >> 2) + 4 * half + (v & 3);
+      if (row < k) myred[row * 33 + col] = y[v];
+      y[v] = 0.0f;
+    }
+  };
+  // One group step: the row's operands NU-packed and summed as the narrow
+  // staging sums them (each 8-element block in order from zero, the half's
+  // four blocks pairwise, then half 0 + half 1), the MFMA chain, and the
+  // epilogue y += s P + (b - 128 s) X for each of the lane's 16 rows.
+  auto step = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 pk;
+      const float bs = block8(xbuf[i][j], pk);
+      const int row = xr0 + 8 * j;
+      xt[row * kWideTileRow + xq] = pk;
+      const float X = sum8_dpp(bs);  // ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7)) of the row
+      if (xq == 0) xtab[row] = X;
+    }
+    // The tile and the table are read back by the same wave: LDS operations
+    // of a wave take effect in program order, and the compiler keeps these
+    // accesses (all through smem) in that order.
+    uint4 av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = xt[col * kWideTileRow + 4 * half + j];
+    const float s = __uint_as_float(sbuf[i] << 16);
+    const float b = __uint_as_float(sbuf[i] & 0xFFFF0000u);
+    const float c = fmaf(-128.0f, s, b);
+    f32x16 acc = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), decode_step<FMT>(cbuf[i], j, dk),
+                                                    acc, 0, 0, 0);
+    float xg[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x4 = *reinterpret_cast<const float4*>(xtab + 8 * q + 4 * half);
+      xg[4 * q + 0] = x4.x;
+      xg[4 * q + 1] = x4.y;
+      xg[4 * q + 2] = x4.z;
+      xg[4 * q + 3] = x4.w;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      y[v] = fmaf(s, acc[v], y[v]);
+      y[v] = fmaf(c, xg[v], y[v]);
+    }
+  };
+  const int nround = (gn + PF - 1) / PF;
+  for (int r = 0; r < nround; ++r) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int st = r * PF + i;
+      if (st < gn) {
+        if (st == ga) put(r0);  // the first range is complete
+        step(i);
+      }
+      if (r + 1 < nround) issue(i, st + PF);
+    }
+  }
+  put(nr == 2 ? r0 + 1 : r0);
+
+  // ---- cross-range sum in range order, then the epilogue (as the narrow kernel)
+  __syncthreads();
+  const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
+  for (int q = tid; q < k * cols_out; q += blockDim.x) {
+    const int i = q / cols_out, cc = q - i * cols_out;
+    float val[2];
+    const int ncol = (MODE == SDV_MODE_PLAIN) ? 1 : 2;
+    for (int h2 = 0; h2 < ncol; ++h2) {
+      const int cidx = cc + 16 * h2;
+      float sum = 0.0f;
+      for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * 32 + i) * 33 + cidx];
+      val[h2] = sum;
+    }
+    if (MODE == SDV_MODE_PLAIN) {
+      const int on = t * 32 + cc;
+      if (on < a.N) out[(size_t)i * a.n_out + on] = val[0];
+    } else {
+      const int on = t * 16 + cc;
+      if (on < a.n_out) out[(size_t)i * a.n_out + on] = siluf_(val[0]) * val[1];
+    }
+  }
+}
+
+// the cross-range table [nw][32][33], then per wave a 32-float table and a
+// tile of 32 rows x kWideTileRow blocks of 16 bytes
+__host__ __device__ inline size_t dense_wide_lds_bytes(int nw) {
+  const size_t waves = (size_t)(nw + 1) / 2;
+  return (size_t)nw * 32 * 33 * 4 + waves * 32 * 4 + waves * 32 * kWideTileRow * 16;
+}
+
+template <int FMT, int MODE>
+hipError_t dense_wide_launch_one(const DenseArgs& a, int nmulti, hipStream_t st) {
+  constexpr int PF = 5;
+  void (*kern)(DenseArgs) = q4_dense_wide_kernel<FMT, MODE, PF>;
+  const size_t lds = dense_wide_lds_bytes(a.nw);
+  static std::atomic<size_t> lds_limit{65536};
+  size_t cur = lds_limit.load(std::memory_order_relaxed);
+  if (lds > cur) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(a.T, nmulti), dim3(64 * ((a.nw + 1) / 2)), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int FMT, int MODE, int ACT, int PF>
 hipError_t dense_launch_one(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
   void (*kern)(DenseArgs) = q4_dense_k_kernel<FMT, MODE, ACT, PF>;
@@ -343,6 +544,8 @@ int dense_waves_for(int K) {
 }
 
 size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt) {
+  if (act_dtype == SDV_ACT_BF16 && k > kPassRows && fmt != SDV_FMT_Q8_0)
+    return dense_wide_lds_bytes(dense_waves_for(K));  // the wide form
   if (k > kPassRows) k = kPassRows;  // one launch per pass
   const int G = K / 64, nw = dense_waves_for(K);
   const int gwmax = (G + nw - 1) / nw;
@@ -356,8 +559,8 @@ namespace {
 
 // One launch over nmulti weights of W's shape and format (Ws[i], outputs
 // outs[i]) that share the activation rows.
-hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
-                             float* const* outs, hipStream_t st) {
+DenseArgs dense_args(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
+                     float* const* outs) {
   const sdv_q4t& W = Ws[0];
   DenseArgs a{};
   for (int m = 0; m < nmulti; ++m) {
@@ -376,6 +579,33 @@ hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void
   a.gwmax = (a.G + a.nw - 1) / a.nw;
   a.cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   a.region = (int)dense_region_bytes(a.cap, a.gwmax, W.format == SDV_FMT_Q8_0 ? 2 : 1);
+  return a;
+}
+
+// Whether k rows take the wide form (one pass) instead of narrow passes.
+bool dense_wide(int act_dtype, int k, int fmt) {
+  return act_dtype == SDV_ACT_BF16 && k > kPassRows && fmt != SDV_FMT_Q8_0;
+}
+
+hipError_t dense_launch_wide(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int k, float* const* outs,
+                             hipStream_t st) {
+  const DenseArgs a = dense_args(Ws, nmulti, mode, act, SDV_ACT_BF16, k, outs);
+  const int fmt = Ws[0].format;
+  if (fmt == SDV_FMT_AFFINE_Q4 && mode == SDV_MODE_PLAIN)
+    return dense_wide_launch_one<SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN>(a, nmulti, st);
+  if (fmt == SDV_FMT_AFFINE_Q4 && mode == SDV_MODE_GATEUP_SWIGLU)
+    return dense_wide_launch_one<SDV_FMT_AFFINE_Q4, SDV_MODE_GATEUP_SWIGLU>(a, nmulti, st);
+  if (fmt == SDV_FMT_AFFINE_Q3 && mode == SDV_MODE_PLAIN)
+    return dense_wide_launch_one<SDV_FMT_AFFINE_Q3, SDV_MODE_PLAIN>(a, nmulti, st);
+  if (fmt == SDV_FMT_AFFINE_Q3 && mode == SDV_MODE_GATEUP_SWIGLU)
+    return dense_wide_launch_one<SDV_FMT_AFFINE_Q3, SDV_MODE_GATEUP_SWIGLU>(a, nmulti, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
+                             float* const* outs, hipStream_t st) {
+  const sdv_q4t& W = Ws[0];
+  const DenseArgs a = dense_args(Ws, nmulti, mode, act, act_dtype, k, outs);
   const size_t lds = dense_lds_bytes(W.K, act_dtype, k, W.format);
 #define SDV_DENSE(F, M, A) \
   if (W.format == F && mode == M && act_dtype == A) return dense_launch_pf<F, M, A>(a, nmulti, lds, st);
@@ -397,13 +627,15 @@ hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void
 
 }  // namespace
 
-// Widths above one pass run one launch per pass of at most kPassRows rows
-// (rows 9c .. 9c + 8 of the activations and outputs); each launch reads the
+// Widths above one pass take the wide form (bf16 rows, affine Q4 or Q3: one
+// launch for all rows); otherwise one launch per pass of at most kPassRows
+// rows (rows 9c .. 9c + 8 of the activations and outputs), each reading the
 // weights again.
 hipError_t dense_multi_launch(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
                               float* const* outs, hipStream_t st) {
   const sdv_q4t& W = Ws[0];
   if (nmulti < 1 || nmulti > kDenseMulti) return hipErrorInvalidValue;
+  if (dense_wide(act_dtype, k, W.format)) return dense_launch_wide(Ws, nmulti, mode, act, k, outs, st);
   const size_t act_row = (size_t)W.K * (act_dtype == SDV_ACT_F32 ? 4 : 2);
   const int n_out = (mode == SDV_MODE_PLAIN) ? W.N : W.N / 2;
   for (int r0 = 0; r0 < k; r0 += kPassRows) {

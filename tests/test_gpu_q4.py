@@ -180,7 +180,8 @@ def test_mode_must_match_layout():
 
 
 @pytest.mark.parametrize("fmt_name,mode,act_f32,k", [("q4", 0, False, 9), ("q4", 0, True, 5), ("q4", 1, False, 9),
-                                                    ("q4", 0, False, 32), ("q8", 0, False, 9), ("q3", 0, False, 4)])
+                                                    ("q4", 0, False, 32), ("q8", 0, False, 9), ("q3", 0, False, 4),
+                                                    ("q3", 1, False, 20), ("q8", 0, False, 16)])
 def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k):
     """sdv_qmv_k_multi over several weights of one shape that share the
     activation rows: every output equals its own sdv_qmv_k call bit for bit

@@ -56,6 +56,31 @@ def test_dense_wide_rows_equal_narrow(k):
         assert_close(y, ref, f"qmv k={k} {mode} {dt}")
 
 
+@pytest.mark.parametrize("N,K,mode,k", [(33, 64, "plain", 10), (4097, 192, "plain", 32), (2560, 5120, "plain", 32),
+                                         (96, 5120, "gateup", 19), (2 * 320, 640, "gateup", 32), (1000, 576, "plain", 13)])
+def test_dense_wide_form_shapes(N, K, mode, k):
+    """The one-pass wide form of the dense product (bf16 rows beyond one
+    narrow pass): ragged N, one K range (K = 64), an odd number of K ranges
+    (K = 192, 576), the 5120 shape and the gate/up mode; every row against
+    its width-1 call bit for bit and the oracle within tolerance."""
+    ops, _ = _mods()
+    from synth.inputs import DENSE_W
+    banner(f"qmv wide form N={N} K={K} {mode} k={k}")
+    codes, scales, biases = synth.dense_weight(12, DENSE_W if mode == "plain" else SHARED_GATEUP, 0, N, K)
+    W = q4_device_from_host(codes, scales, biases).tiled(fused_gateup=mode == "gateup")
+    x = synth.activations(12, k, k, K)
+    xd = sdev.upload_bf16(x, DEV)
+    m = ops.MODE_PLAIN if mode == "plain" else ops.MODE_GATEUP_SWIGLU
+    y = to_np(ops.qmv_k(W, xd, m))
+    for r in range(k):
+        y1 = to_np(ops.qmv_k(W, xd[r:r + 1].contiguous(), m))[0]
+        assert np.array_equal(y[r], y1), f"row {r}"
+    ref = oracle.qmv(codes, scales, biases, oracle.bf16_to_f64(x))
+    if mode == "gateup":
+        ref = oracle.swiglu(ref)
+    assert_close(y, ref, f"qmv wide form {N}x{K} {mode} k={k}")
+
+
 @pytest.mark.parametrize("E,topk,mode,renorm", [(512, 10, "sigmoid", True), (256, 8, "softmax", False),
                                                 (64, 16, "sigmoid", False), (4, 2, "softmax", True)])
 def test_route_wide(E, topk, mode, renorm):
