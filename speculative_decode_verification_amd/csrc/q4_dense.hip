@@ -309,13 +309,17 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
 // h) takes blocks 4 h .. 4 h + 3 of row r).  The group sum of a row adds its
 // 8 block sums across the 8 lanes that hold them; the sums meet in a per-wave
 // table, read back in the accumulator layout (lane half h holds rows
-// 8 q + 4 h + 0..3).  A wave of this form takes two
-// consecutive K ranges of the narrow kernel (the registers of 32-row operands
-// allow half as many waves), one after the other, and keeps their results
-// apart.  The K ranges, the group step (the same MFMA chain and epilogue),
+// 8 q + 4 h + 0..3).  A wave takes RPW consecutive K ranges of the narrow
+// kernel, one after the other, and keeps their results apart.  The K
+// ranges, the group step (the same MFMA chain and epilogue),
 // the order of every sum and the cross-range sum are the narrow kernel's, so
 // each row equals its narrow (and width-1) result bit for bit.
 constexpr int kWideTileRow = 9;  // 16-byte blocks per tile row: 8 and one of padding
+// Ring depth and K ranges per wave: one range per wave (16 waves at K >=
+// 1024) with two groups in flight fits 128 VGPRs, so four waves share a SIMD;
+// two ranges per wave with five in flight (2 waves per SIMD) measured 15.4
+// against 12.8 us at 32 rows of 5120 x 5120.
+constexpr int kWidePF = 2, kWideRPW = 1;
 
 // sum8 by DPP moves within each 8-lane half row (pairs, then quads, then the
 // two quads by the half-row mirror): ((b0 + b1) + (b2 + b3)) + ((b4 + b5) +
@@ -333,8 +337,8 @@ __device__ __forceinline__ float sum8_dpp(float x) {
   return x + dpp(x, 0x141);  // row_half_mirror: lane 7 - lane within 8
 }
 
-template <int FMT, int MODE, int PF>
-__global__ __launch_bounds__(512, 1) void q4_dense_wide_kernel(DenseArgs a) {
+template <int FMT, int MODE, int PF, int RPW>
+__global__ __launch_bounds__(1024 / RPW, 1) void q4_dense_wide_kernel(DenseArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,15 +346,15 @@ __global__ __launch_bounds__(512, 1) void q4_dense_wide_kernel(DenseArgs a) {
   const int col = lane & 31, half = lane >> 5;
   const int t = blockIdx.x;
   const int G = a.G, K = a.K, k = a.k, nw = a.nw;  // nw: the narrow kernel's K ranges
-  // ranges r0 = 2 wave and r0 + 1 (if any): groups [gb, gm) and [gm, ge)
-  const int r0 = 2 * wave, nr = min(2, nw - r0);
+  // ranges r0 = RPW wave and (RPW = 2) r0 + 1 if any: groups [gb, gm) and [gm, ge)
+  const int r0 = RPW * wave, nr = min(RPW, nw - r0);
   const int gb = __builtin_amdgcn_readfirstlane((G * r0) / nw);
   const int gm = __builtin_amdgcn_readfirstlane((G * (r0 + 1)) / nw);
   const int ge = __builtin_amdgcn_readfirstlane((G * (r0 + nr)) / nw);
   const int ga = gm - gb, gn = ge - gb;  // steps of the first range, of both
   float* red = reinterpret_cast<float*>(smem);                          // [nw][32][33]
   float* xtab = red + (size_t)nw * 32 * 33 + wave * 32;                 // the current group's row sums
-  uint4* xt = reinterpret_cast<uint4*>(red + (size_t)nw * 32 * 33 + (size_t)((nw + 1) / 2) * 32) +
+  uint4* xt = reinterpret_cast<uint4*>(red + (size_t)nw * 32 * 33 + (size_t)((nw + RPW - 1) / RPW) * 32) +
               (size_t)wave * 32 * kWideTileRow;                         // the group's rows, NU-packed blocks
 
   const uint4* const codes = a.codes[blockIdx.y];
@@ -477,16 +481,16 @@ __global__ __launch_bounds__(512, 1) void q4_dense_wide_kernel(DenseArgs a) {
 
 // the cross-range table [nw][32][33], then per wave a 32-float table and a
 // tile of 32 rows x kWideTileRow blocks of 16 bytes
-__host__ __device__ inline size_t dense_wide_lds_bytes(int nw) {
-  const size_t waves = (size_t)(nw + 1) / 2;
+__host__ __device__ inline size_t dense_wide_lds_bytes(int nw, int rpw) {
+  const size_t waves = (size_t)(nw + rpw - 1) / rpw;
   return (size_t)nw * 32 * 33 * 4 + waves * 32 * 4 + waves * 32 * kWideTileRow * 16;
 }
 
 template <int FMT, int MODE>
 hipError_t dense_wide_launch_one(const DenseArgs& a, int nmulti, hipStream_t st) {
-  constexpr int PF = 5;
-  void (*kern)(DenseArgs) = q4_dense_wide_kernel<FMT, MODE, PF>;
-  const size_t lds = dense_wide_lds_bytes(a.nw);
+  constexpr int PF = kWidePF, RPW = kWideRPW;
+  void (*kern)(DenseArgs) = q4_dense_wide_kernel<FMT, MODE, PF, RPW>;
+  const size_t lds = dense_wide_lds_bytes(a.nw, RPW);
   static std::atomic<size_t> lds_limit{65536};
   size_t cur = lds_limit.load(std::memory_order_relaxed);
   if (lds > cur) {
@@ -496,7 +500,7 @@ hipError_t dense_wide_launch_one(const DenseArgs& a, int nmulti, hipStream_t st)
     while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
     }
   }
-  hipLaunchKernelGGL(kern, dim3(a.T, nmulti), dim3(64 * ((a.nw + 1) / 2)), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(a.T, nmulti), dim3(64 * ((a.nw + RPW - 1) / RPW)), lds, st, a);
   return hipGetLastError();
 }
 
@@ -545,7 +549,7 @@ int dense_waves_for(int K) {
 
 size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt) {
   if (act_dtype == SDV_ACT_BF16 && k > kPassRows && fmt != SDV_FMT_Q8_0)
-    return dense_wide_lds_bytes(dense_waves_for(K));  // the wide form
+    return dense_wide_lds_bytes(dense_waves_for(K), kWideRPW);  // the wide form
   if (k > kPassRows) k = kPassRows;  // one launch per pass
   const int G = K / 64, nw = dense_waves_for(K);
   const int gwmax = (G + nw - 1) / nw;
