@@ -505,9 +505,10 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
     """sdv_qmv_k on the dense 5120 x 5120 shape: 64 distinct weights (944 MB
     of affine Q4, more than the last-level cache) launched back to back at
     each width, timed with HIP events around each width's launches; then the
-    same for the Q8_0 (1.7 GB) and affine-Q3 (0.66 GB) formats, and the
-    32-row width.  Reported per projection: time and algorithmic GB/s
-    (weights, activations and outputs once)."""
+    same for the Q8_0 (1.7 GB) and affine-Q3 (0.66 GB) formats; 16 and 32
+    rows take the one-pass wide form (affine Q4 and Q3).  Reported per
+    projection: time and algorithmic GB/s (weights, activations and outputs
+    once)."""
     import torch
     import synth
     from synth import device as sdev
@@ -567,8 +568,8 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
 
     Ws = [ops.Q4Weight(*sdev.q4_bank(synth.bank_keys(1, DENSE_W, l), 1, N, K, dev)).tiled()
           for l in range(n_weights)]
-    out = time_widths(Ws, q4_bytes(N, K), (1, 4, 8, 9, 32))
-    multi = time_multi(Ws, q4_bytes(N, K), (1, 9))
+    out = time_widths(Ws, q4_bytes(N, K), (1, 4, 8, 9, 16, 32))
+    multi = time_multi(Ws, q4_bytes(N, K), (1, 9, 32))
     del Ws
     # Q8_0 and affine Q3 weights filled on the device (any codes are valid;
     # parity of these formats is covered by the tests)
@@ -589,7 +590,7 @@ def dense_projection(dev, timer, n_weights=64, reps=4):
         bi = (torch.rand((N, K // 64), device=dev, generator=g) * 0.2 - 0.1).to(torch.bfloat16).view(torch.int16)
         Ws.append(ops.Q3Weight(codes, sc, bi).tiled())
         del codes, sc, bi
-    q3 = time_widths(Ws, N * 3 * K // 8 + N * (K // 64) * 4, (1, 9))
+    q3 = time_widths(Ws, N * 3 * K // 8 + N * (K // 64) * 4, (1, 9, 32))
     del Ws
     torch.cuda.empty_cache()
     return {"shape": [N, K], "weights": n_weights, "widths": out, "multi_weight_launch": multi, "q8_0": q8,
