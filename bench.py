@@ -253,8 +253,11 @@ class Workload:
         accept, _, _, _ = self.blocks[s % len(self.blocks)]
         run("accept", self.layers, accept)
         n = int(self.cycle.accepted.item())
+        # each GDN layer applies its rollback just before it runs again, so
+        # between reading the count and the next step's first launch the host
+        # handles one layer only
         for gl, _ in self.gdn.values():
-            gl.rollback(n + 1)
+            gl.rollback_later(n + 1)
         return n
 
     def check_acceptance(self):
@@ -993,7 +996,8 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,
         "cpu_other_configs": cpu_cfg,
-        "accepted_count": "read back from the device every timed step (one host synchronisation per step)",
+        "accepted_count": ("read back from the device every timed step (one host synchronisation per step); "
+                           "each GDN layer's rollback to it is applied before the layer's next launch"),
         **extra,
         "wall_s_timed": round(wall, 3),
         "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "host_cpu": cpu_model()},

@@ -131,13 +131,16 @@ class GdnLayer:
         self.slots = [S0.contiguous()] + [torch.empty_like(S0) for _ in range(k)]
         self.live = 0
         self.snap_ids = None
+        self._pending = None
         self.y = torch.empty((k, self.Hv, self.Dv), dtype=torch.float32, device=S0.device)
 
     @property
     def state(self):
+        self.apply_rollback()
         return self.slots[self.live]
 
     def verify(self, q, kk, v, g, beta):
+        self.apply_rollback()
         rows = q.shape[0]
         self.snap_ids = [i for i in range(len(self.slots)) if i != self.live][:rows]
         y = self.y[:rows]
@@ -147,6 +150,7 @@ class GdnLayer:
     def bind(self, q, kk, v, g, beta):
         """Marshal the verify launch once per possible live slot for fixed
         input buffers; ``run_bound`` then issues the one matching the live slot."""
+        self.apply_rollback()
         rows = q.shape[0]
         self._bound = []
         for live in range(len(self.slots)):
@@ -157,6 +161,7 @@ class GdnLayer:
         return self
 
     def run_bound(self):
+        self.apply_rollback()
         ids, call = self._bound[self.live]
         self.snap_ids = ids
         call()
@@ -188,6 +193,7 @@ class GdnLayer:
     def prepare(self, qkv, a, b):
         """The recurrence inputs of rows qkv [rows, C], a, b [rows, Hv];
         returns {q, k, v, g, beta, window}."""
+        self.apply_rollback()
         conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
         out = ops.gdn_prepare_k(qkv, self.hist, conv_w, a, b, A_log, dt_bias, Hk, self.Dk, act, eps,
                                 self._prep_out(qkv.shape[0]))
@@ -217,6 +223,7 @@ class GdnLayer:
     def prebind_prepare(self, qkv, a, b):
         """Marshal ``run_prepare_bound`` for every (window, history source)
         pair it can meet, so later steps only look the call up."""
+        self.apply_rollback()
         for win in (0, 1):
             self._prep_call(qkv, a, b, win, self.hist)
             for j in range(self.k + 1):
@@ -226,6 +233,7 @@ class GdnLayer:
     def run_prepare_bound(self, qkv, a, b):
         """``prepare`` for fixed qkv, a, b buffers, marshalled once per
         (window, history source) pair."""
+        self.apply_rollback()
         self._prep_call(qkv, a, b, self.win, self.hist)()
         self.prepped = True
         return self._prep_out(qkv.shape[0])
@@ -233,6 +241,7 @@ class GdnLayer:
     def verify_from_proj(self, qkv, a, b):
         """Preparation and recurrence in one launch from the projections qkv
         [rows, C], a, b [rows, Hv]; returns y [rows, Hv, Dv]."""
+        self.apply_rollback()
         conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
         rows = qkv.shape[0]
         self.snap_ids = [i for i in range(len(self.slots)) if i != self.live][:rows]
@@ -249,6 +258,7 @@ class GdnLayer:
         """Marshal ``verify_from_proj`` for fixed qkv, a, b buffers; the state,
         history, window and snapshot pointers are patched per step from
         prebuilt values (no argument checks on the host path after this)."""
+        self.apply_rollback()
         conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
         rows = qkv.shape[0]
         self._fp_rows = rows
@@ -267,6 +277,7 @@ class GdnLayer:
     def verify_from_proj_norm(self, qkv, a, b, z, norm_w, out, gate_act=ops.GATE_SIGMOID, norm_eps=1e-6):
         """``verify_from_proj`` with the gated output norm in the same launch:
         out [rows, Hv, Dv] = rmsnorm(y) * norm_w * act(z); returns (y, out)."""
+        self.apply_rollback()
         conv_w, A_log, dt_bias, Hk, act, eps = self.prep_params
         rows = qkv.shape[0]
         self.snap_ids = [i for i in range(len(self.slots)) if i != self.live][:rows]
@@ -296,6 +307,7 @@ class GdnLayer:
         return self
 
     def run_from_proj_bound(self):
+        self.apply_rollback()
         key = (self.live, self.win, self.hist.data_ptr())
         call = self._fp_cache.get(key)
         ids, arr = self._fp_snaps[self.live]
@@ -311,10 +323,27 @@ class GdnLayer:
         self.prepped = True
         return self.y[:self._fp_rows]
 
+    def rollback_later(self, j):
+        """``rollback(j)``, applied when the layer next runs or its state is
+        read (or by ``apply_rollback``).  A decoding loop that reads the
+        accepted count back then launches the next step's first layer after
+        that layer's rollback alone, instead of after every layer's."""
+        if self._pending is not None:
+            raise RuntimeError("a rollback is already pending")
+        ops.gdn_rollback(len(self.snap_ids), j)  # checks j before it is stored
+        self._pending = j
+
+    def apply_rollback(self):
+        j, self._pending = self._pending, None
+        if j is not None:
+            self.rollback(j)
+
     def rollback(self, j):
         """Make the state after the accepted prefix of j rows live (no copy);
         with a preparation stage, rows j..j+2 of its window become the conv
         history."""
+        if self._pending is not None:
+            raise RuntimeError("a rollback is already pending")
         slot = ops.gdn_rollback(len(self.snap_ids), j)
         if slot > 0:
             self.live = self.snap_ids[slot - 1]
@@ -323,7 +352,7 @@ class GdnLayer:
             self.hist = self.windows[self.win][j:j + 3]
             self.win ^= 1
             self.prepped = False
-        return self.state
+        return self.slots[self.live]
 
 
 __all__ = ["MoeLayer", "GdnLayer", "MODE_PLAIN", "MODE_GATEUP_SWIGLU", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
@@ -354,14 +383,18 @@ class VerifyCycle:
         return ops.bind_verify_accept_k(logits, drafts, self.tokens, self.accepted, self.workspace, noise, inv_temp,
                                         self.eos)
 
-    def __call__(self, logits, drafts, noise=None, inv_temp=1.0):
+    def __call__(self, logits, drafts, noise=None, inv_temp=1.0, defer=False):
         """Accept, roll every layer back to the accepted prefix, and return
         (n accepted drafts, emitted tokens: the accepted drafts, then the
-        token sampled after them)."""
+        token sampled after them).  With ``defer`` each layer's rollback is
+        applied when the layer next runs (``GdnLayer.rollback_later``)."""
         self.accept(logits, drafts, noise, inv_temp)
         n = int(self.accepted.item())
         for layer in self.layers:
-            layer.rollback(n + 1)
+            if defer:
+                layer.rollback_later(n + 1)
+            else:
+                layer.rollback(n + 1)
         toks = self.tokens.cpu().tolist()
         accepted_drafts = drafts[:n].cpu().tolist() if n > 0 else []
         return n, accepted_drafts + [toks[n]]

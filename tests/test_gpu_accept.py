@@ -168,3 +168,43 @@ def test_verify_cycle_rolls_gdn_back():
             _, inp = states[li]
             _, rs = oracle.gdn_verify(starts[li], *(inp[m][:n + 1] for m in ("q", "k", "v", "g", "beta")))
             assert_close(live[None], rs[-1][None], f"layer {li} state after prefix {n + 1}")
+
+
+def test_verify_cycle_deferred_rollback_equals_eager():
+    """``VerifyCycle(..., defer=True)`` leaves each layer's rollback to its
+    next run: over a chain of steps with varied accepted counts, from the
+    projections (conv history rolled back with the state), every output and
+    live state equals the eager cycle's bit for bit."""
+    from speculative_decode_verification_amd import pipeline
+    banner("verify cycle, deferred rollback")
+    k, V, hv, hk, d = 9, 20000, 8, 4, 64
+    C = 2 * hk * d + hv * d
+    rng = np.random.default_rng(77)
+    S0 = synth.gdn_state(36, 0, hv, d, d)
+    hist = rng.standard_normal((3, C)).astype(np.float32)
+    conv_w = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    A_log = rng.standard_normal(hv).astype(np.float32)
+    dt_bias = rng.standard_normal(hv).astype(np.float32)
+    up = lambda a: sdev.upload_f32(a, DEV)
+    runs = {}
+    for defer in (False, True):
+        layers = [pipeline.GdnLayer(up(S0), k).attach_prep(up(hist), up(conv_w), up(A_log), up(dt_bias), hk)
+                  for _ in range(2)]
+        cycle = pipeline.VerifyCycle(layers, k, V, DEV)
+        ys, states = [], []
+        for step, planted in enumerate([3, 0, 8, 5, 1]):
+            srng = np.random.default_rng(100 + step)
+            for layer in layers:
+                qkv = up(srng.standard_normal((k, C)).astype(np.float32))
+                a = up(srng.standard_normal((k, hv)).astype(np.float32))
+                b = up(srng.standard_normal((k, hv)).astype(np.float32))
+                ys.append(to_np(layer.verify_from_proj(qkv, a, b)).copy())
+            logits, drafts, _ = synth.verify_block(36, step, k, V, accepted=planted)
+            n, _ = cycle(sdev.upload_f32(logits, DEV), torch.from_numpy(drafts).to(DEV), defer=defer)
+            assert n == planted
+        states = [to_np(layer.state).copy() for layer in layers]
+        runs[defer] = (ys, states)
+    for a, b in zip(runs[False][0], runs[True][0]):
+        assert np.array_equal(a, b)
+    for a, b in zip(runs[False][1], runs[True][1]):
+        assert np.array_equal(a, b)
