@@ -21,6 +21,12 @@
 // depends on K only, so every row is computed in the same order at every
 // width: a width-k row equals the width-1 row bit for bit.
 //
+// A launch over several weights that share the rows (sdv_qmv_k_multi) gives
+// each workgroup mw of them for its tile when that still leaves about 640
+// workgroups: the rows are staged once, each wave streams its K range of
+// every weight in turn through the same ring, and each weight's sums are
+// taken in a table beside the staging as its last group completes.
+//
 // The arithmetic of a group step is the one of the other Q4 kernels: codes
 // decode exactly to bf16 128 + q, the matrix core returns P = sum (128 + q) x
 // and the group adds s P + (b - 128 s) X, X being the group sum of the
@@ -37,6 +43,7 @@ namespace {
 using namespace q4;
 
 constexpr int kDenseMaxWaves = 16;
+constexpr size_t kDenseMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
 constexpr int kDenseMulti = 16;  // weights of one multi-weight launch
 
 struct DenseArgs {
@@ -46,6 +53,7 @@ struct DenseArgs {
   float* out[kDenseMulti];          // [k][n_out]
   const void* act;       // [k][K] bf16 bits or fp32, shared by the weights
   int N, K, T, G, k, n_out, nw;
+  int nmulti, mw;        // weights of the launch; weights per workgroup (blockIdx.y takes weights mw y ..)
   int gwmax;             // groups of the widest wave range
   int cap;               // staged rows per wave (k or 3k); row cap is all zero
   int region;            // bytes of one wave's LDS region
@@ -61,7 +69,9 @@ __host__ __device__ inline size_t dense_region_bytes(int cap, int gwmax, int spg
          ~(size_t)15;
 }
 
-// The cross-wave sums reuse the regions: [nw][kPassRows][33].
+// The cross-wave sums [nw][kPassRows][33] reuse the regions when a workgroup
+// takes one weight, and follow them when it takes several (the staged rows
+// serve every weight).
 __host__ __device__ inline size_t dense_red_bytes(int nw) { return (size_t)nw * kPassRows * 33 * 4; }
 
 // Sum of 8 consecutive bf16 values (natural order), and their NU packing.
@@ -84,7 +94,7 @@ __device__ __forceinline__ float group_total(const float (&b)[8]) { return half_
 
 // FMT = SDV_FMT_Q8_0: two 1 KB code chunks per group step, activation sums
 // per 32-element block, and the Q8_0 group step.
-template <int FMT, int MODE, int ACT, int PF>
+template <int FMT, int MODE, int ACT, int PF, bool MW>
 __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   constexpr bool Q8 = FMT == SDV_FMT_Q8_0;
   constexpr int SPG = Q8 ? 2 : 1;
@@ -118,15 +128,21 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
                                   : reinterpret_cast<const uint4*>(static_cast<const float*>(a.act) + e0)[q];
   }
 
-  // ---- the wave's weight blocks: step s reads block (t, gb + min(s, gw - 1))
-  const uint4* const codes = a.codes[blockIdx.y];
-  const uint32_t* const sbp = a.sb[blockIdx.y];
-  float* const out = a.out[blockIdx.y];
+  // ---- the wave's weight blocks: the workgroup's weights m0 .. m0 + nm - 1
+  // one after the other, step s reads block (t, gb + s % gw) of weight
+  // m0 + s / gw (steps past the end re-read the last block)
+  const int m0 = MW ? blockIdx.y * a.mw : blockIdx.y;
+  const int nm = MW ? min(a.mw, a.nmulti - m0) : 1;
+  const int ns = nm * gw;
   const size_t blk0 = (size_t)t * G + gb;
   uint4 cbuf[PF], cbuf2[Q8 ? PF : 1];
   uint32_t sbuf[PF];
   auto issue = [&](int slot, int s) {
-    const size_t blk = blk0 + min(s, gw - 1);
+    s = min(s, ns - 1);
+    const int mi = MW ? __builtin_amdgcn_readfirstlane(s / gw) : 0;
+    const uint4* const codes = a.codes[m0 + mi];
+    const uint32_t* const sbp = a.sb[m0 + mi];
+    const size_t blk = blk0 + (s - mi * gw);
     if constexpr (Q8) {
       cbuf[slot] = load_nt(codes + blk * 128 + lane);  // weights: read once per call
       cbuf2[slot] = load_nt(codes + blk * 128 + 64 + lane);
@@ -239,64 +255,66 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   }
   const DecodeK dk = decode_k();
   float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  const int nround = (gw + PF - 1) / PF;
-  // rounds before the last refill their slot after the step; the last does not
+  // ---- cross-wave sum of weight m0 + mi in wave order, then its epilogue
+  float* red = reinterpret_cast<float*>(smem + (MW ? (size_t)nw * a.region : 0));
+  const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
+  auto finish = [&](int mi) {
+    __syncthreads();  // every wave is done with its region (one weight), or with the last weight's sums
+    float* myred = red + (size_t)wave * kPassRows * 33;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int r = i < 4 ? 4 * half + i : 8;
+      if (r < k && (i < 4 || half == 0)) myred[r * 33 + col] = y[i];
+      y[i] = 0.0f;
+    }
+    __syncthreads();
+    float* const out = a.out[m0 + mi];
+    for (int q = tid; q < k * cols_out; q += blockDim.x) {
+      const int i = q / cols_out, cc = q - i * cols_out;
+      float val[2];
+      const int ncol = (MODE == SDV_MODE_PLAIN) ? 1 : 2;
+      for (int h2 = 0; h2 < ncol; ++h2) {
+        const int cidx = cc + 16 * h2;
+        float sum = 0.0f;
+        for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * kPassRows + i) * 33 + cidx];
+        val[h2] = sum;
+      }
+      if (MODE == SDV_MODE_PLAIN) {
+        const int on = t * 32 + cc;
+        if (on < a.N) out[(size_t)i * a.n_out + on] = val[0];
+      } else {
+        const int on = t * 16 + cc;
+        if (on < a.n_out) out[(size_t)i * a.n_out + on] = siluf_(val[0]) * val[1];
+      }
+    }
+  };
+  // group s % gw of weight s / gw; rounds before the last refill their slot
+  // after the step, the last does not
+  auto gstep = [&](int i, int s) {
+    const int g = MW ? s % gw : s;
+    if constexpr (Q8) {
+      group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + g * 64, xr, g, y);
+    } else {
+      group_mac_rows<ACT, FMT>(cbuf[i], sbuf[i], ap + g * 64, xr, g, y, dk);
+    }
+    if (MW && g == gw - 1) finish(s / gw);
+  };
+  const int nround = (ns + PF - 1) / PF;
   for (int r = 0; r + 1 < nround; ++r) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int s = r * PF + i;
-      if constexpr (Q8) {
-        group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + s * 64, xr, s, y);
-      } else {
-        group_mac_rows<ACT, FMT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
-      }
+      gstep(i, s);
       issue(i, s + PF);
     }
   }
   {
     const int s0 = (nround - 1) * PF;
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int s = s0 + i;
-      if (s < gw) {
-        if constexpr (Q8) {
-          group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + s * 64, xr, s, y);
-        } else {
-          group_mac_rows<ACT, FMT>(cbuf[i], sbuf[i], ap + s * 64, xr, s, y, dk);
-        }
-      }
-    }
+    for (int i = 0; i < PF; ++i)
+      if (s0 + i < ns) gstep(i, s0 + i);
   }
-
-  // ---- cross-wave sum in wave order, then the epilogue
-  __syncthreads();  // every wave is done with its region
-  float* red = reinterpret_cast<float*>(smem);
-  float* myred = red + (size_t)wave * kPassRows * 33;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int r = i < 4 ? 4 * half + i : 8;
-    if (r < k && (i < 4 || half == 0)) myred[r * 33 + col] = y[i];
-  }
-  __syncthreads();
-  const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
-  for (int q = tid; q < k * cols_out; q += blockDim.x) {
-    const int i = q / cols_out, cc = q - i * cols_out;
-    float val[2];
-    const int ncol = (MODE == SDV_MODE_PLAIN) ? 1 : 2;
-    for (int h2 = 0; h2 < ncol; ++h2) {
-      const int cidx = cc + 16 * h2;
-      float sum = 0.0f;
-      for (int w = 0; w < nw; ++w) sum = sum + red[((size_t)w * kPassRows + i) * 33 + cidx];
-      val[h2] = sum;
-    }
-    if (MODE == SDV_MODE_PLAIN) {
-      const int on = t * 32 + cc;
-      if (on < a.N) out[(size_t)i * a.n_out + on] = val[0];
-    } else {
-      const int on = t * 16 + cc;
-      if (on < a.n_out) out[(size_t)i * a.n_out + on] = siluf_(val[0]) * val[1];
-    }
-  }
+  if (!MW) finish(0);
 }
 
 // Wide form: bf16 activations, more rows than one narrow pass (up to 32),
@@ -504,19 +522,33 @@ hipError_t dense_wide_launch_one(const DenseArgs& a, int nmulti, hipStream_t st)
   return hipGetLastError();
 }
 
-template <int FMT, int MODE, int ACT, int PF>
-hipError_t dense_launch_one(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
-  void (*kern)(DenseArgs) = q4_dense_k_kernel<FMT, MODE, ACT, PF>;
+// Raise a kernel's dynamic LDS limit once per process (the largest size
+// asked for so far; the attribute is per function).
+template <void (*KERN)(DenseArgs)>
+hipError_t raise_dense_lds(size_t lds) {
   static std::atomic<size_t> lds_limit{65536};
   size_t cur = lds_limit.load(std::memory_order_relaxed);
   if (lds > cur) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     while (cur < lds && !lds_limit.compare_exchange_weak(cur, lds)) {
     }
   }
-  hipLaunchKernelGGL(kern, dim3(a.T, nmulti), dim3(64 * a.nw), lds, st, a);
+  return hipSuccess;
+}
+
+template <int FMT, int MODE, int ACT, int PF>
+hipError_t dense_launch_one(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
+  (void)nmulti;
+  // (a ring of 8 for the several-weight stream measured slower than the
+  // range's own depth: 3.56 against 3.32 us per projection at one row)
+  constexpr auto one = q4_dense_k_kernel<FMT, MODE, ACT, PF, false>;
+  constexpr auto several = q4_dense_k_kernel<FMT, MODE, ACT, PF, true>;
+  const hipError_t err = a.mw > 1 ? raise_dense_lds<several>(lds) : raise_dense_lds<one>(lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(a.mw > 1 ? several : one, dim3(a.T, (a.nmulti + a.mw - 1) / a.mw), dim3(64 * a.nw), lds, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -524,9 +556,13 @@ template <int FMT, int MODE, int ACT>
 hipError_t dense_launch_pf(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
   // ring depth: the wave's whole range when it is short, else 8 with refills
   // (fp32 rows: 2, since staging the parts takes the registers; Q8_0 blocks
-  // take two chunks, so at most 4)
+  // take two chunks, so at most 4; a Q3 ring of 5 spills, so 4)
   if constexpr (ACT == SDV_ACT_F32) {
     return dense_launch_one<FMT, MODE, ACT, 2>(a, nmulti, lds, st);
+  } else if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
+    if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, nmulti, lds, st);
+    if (a.gwmax <= 5) return dense_launch_one<FMT, MODE, ACT, 4>(a, nmulti, lds, st);
+    return dense_launch_one<FMT, MODE, ACT, 8>(a, nmulti, lds, st);
   } else if constexpr (FMT == SDV_FMT_Q8_0) {
     if (a.gwmax <= 2) return dense_launch_one<FMT, MODE, ACT, 2>(a, nmulti, lds, st);
     return dense_launch_one<FMT, MODE, ACT, 4>(a, nmulti, lds, st);
@@ -547,7 +583,7 @@ int dense_waves_for(int K) {
   return G < kDenseMaxWaves ? (G > 0 ? G : 1) : kDenseMaxWaves;
 }
 
-size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt) {
+size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt, int mw) {
   if (act_dtype == SDV_ACT_BF16 && k > kPassRows && fmt != SDV_FMT_Q8_0)
     return dense_wide_lds_bytes(dense_waves_for(K), kWideRPW);  // the wide form
   if (k > kPassRows) k = kPassRows;  // one launch per pass
@@ -556,7 +592,16 @@ size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt) {
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   const size_t regions = (size_t)nw * dense_region_bytes(cap, gwmax, fmt == SDV_FMT_Q8_0 ? 2 : 1);
   const size_t red = dense_red_bytes(nw);
+  if (mw > 1) return regions + red;  // the staged rows serve every weight of the workgroup
   return regions > red ? regions : red;
+}
+
+// Weights per narrow workgroup in a launch over nmulti weights of T tiles:
+// at least about 640 workgroups, and as few stagings of the rows as that allows.
+int dense_weights_per_wg(int T, int nmulti) {
+  const int want_y = (640 + T - 1) / T;
+  const int y = nmulti < want_y ? nmulti : want_y;
+  return (nmulti + y - 1) / y;
 }
 
 namespace {
@@ -583,6 +628,8 @@ DenseArgs dense_args(const sdv_q4t* Ws, int nmulti, int mode, const void* act, i
   a.gwmax = (a.G + a.nw - 1) / a.nw;
   a.cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   a.region = (int)dense_region_bytes(a.cap, a.gwmax, W.format == SDV_FMT_Q8_0 ? 2 : 1);
+  a.nmulti = nmulti;
+  a.mw = 1;  // the wide form takes one weight per workgroup; the narrow pass sets its own
   return a;
 }
 
@@ -609,8 +656,13 @@ hipError_t dense_launch_wide(const sdv_q4t* Ws, int nmulti, int mode, const void
 hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void* act, int act_dtype, int k,
                              float* const* outs, hipStream_t st) {
   const sdv_q4t& W = Ws[0];
-  const DenseArgs a = dense_args(Ws, nmulti, mode, act, act_dtype, k, outs);
-  const size_t lds = dense_lds_bytes(W.K, act_dtype, k, W.format);
+  DenseArgs a = dense_args(Ws, nmulti, mode, act, act_dtype, k, outs);
+  a.mw = dense_weights_per_wg(a.T, nmulti);
+  // several weights per workgroup keep the staged rows and add the sums'
+  // table; past the LDS a workgroup takes one weight (the size checked on
+  // the host before the launch)
+  if (a.mw > 1 && dense_lds_bytes(W.K, act_dtype, k, W.format, a.mw) > kDenseMaxLds) a.mw = 1;
+  const size_t lds = dense_lds_bytes(W.K, act_dtype, k, W.format, a.mw);
 #define SDV_DENSE(F, M, A) \
   if (W.format == F && mode == M && act_dtype == A) return dense_launch_pf<F, M, A>(a, nmulti, lds, st);
   SDV_DENSE(SDV_FMT_AFFINE_Q4, SDV_MODE_PLAIN, SDV_ACT_BF16)

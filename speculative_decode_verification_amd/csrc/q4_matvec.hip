@@ -549,7 +549,7 @@ hipError_t q4_repack_launch(const sdv_q4& src, int fused, void* tcodes, uint32_t
   return hipGetLastError();
 }
 
-size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt);
+size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt, int mw);
 hipError_t dense_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, int k, float* out,
                         hipStream_t st);
 
@@ -560,7 +560,7 @@ size_t q4_lds_bytes_for(int K, int act_dtype, int k, bool gather, int fmt) {
   // gathered: per-wave output staging for one tile of up to 9 rows x 32 columns
   return gather ? (size_t)(cap + 1) * (K + 8) * 2 + (size_t)32 * (K / 64) * spg * 4 +
                       (size_t)kGatherWaves * kGatherTilesPerWave * kPassRows * 32 * 4
-                : dense_lds_bytes(K, act_dtype, k, fmt);
+                : dense_lds_bytes(K, act_dtype, k, fmt, 1);
 }
 
 hipError_t q4_launch(const sdv_q4t& W, int mode, const void* act, int act_dtype, bool gather,

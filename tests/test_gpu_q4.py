@@ -179,39 +179,60 @@ def test_mode_must_match_layout():
         ops.qmv_k(W.tiled(True), xd)
 
 
-@pytest.mark.parametrize("fmt_name,mode,act_f32,k", [("q4", 0, False, 9), ("q4", 0, True, 5), ("q4", 1, False, 9),
-                                                    ("q4", 0, False, 32), ("q8", 0, False, 9), ("q3", 0, False, 4),
-                                                    ("q3", 1, False, 20), ("q8", 0, False, 16)])
-def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k):
+MULTI_CASES = [("q4", 0, False, 9, 336, 1024, 5), ("q4", 0, True, 5, 336, 1024, 5), ("q4", 1, False, 9, 320, 1024, 5),
+               ("q4", 0, False, 32, 336, 1024, 5), ("q8", 0, False, 9, 336, 1024, 5), ("q3", 0, False, 4, 336, 1024, 5),
+               ("q3", 1, False, 20, 320, 1024, 5), ("q8", 0, False, 16, 336, 1024, 5),
+               # several weights per workgroup (one staging of the rows for all of them)
+               ("q4", 0, False, 9, 2560, 5120, 12), ("q4", 1, False, 7, 5120, 1024, 9),
+               ("q4", 0, True, 5, 10240, 512, 5), ("q8", 0, False, 9, 2560, 1024, 12),
+               ("q3", 0, False, 9, 2560, 1024, 12)]
+
+
+@pytest.mark.parametrize("fmt_name,mode,act_f32,k,N,K,nw", MULTI_CASES)
+def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k, N, K, nw):
     """sdv_qmv_k_multi over several weights of one shape that share the
     activation rows: every output equals its own sdv_qmv_k call bit for bit
-    (ragged N, the gate/up mode, fp32 rows, 32 rows in passes, Q8_0, Q3)."""
+    (ragged N, the gate/up mode, fp32 rows, 32 rows, Q8_0, Q3, and launches
+    whose workgroups take several weights: 2560 x 5120 x 12, 5120 x 1024 x 9,
+    10240 x 512 x 5 with an uneven last workgroup), and the first and last
+    weights match the oracle."""
     ops = _ops()
     from speculative_decode_verification_amd.ops import Q3Weight, Q8Weight
-    N, K, nw = (336 if mode == 0 else 320), 1024, 5
-    banner(f"qmv multi {fmt_name} mode={mode} f32={act_f32} k={k} nw={nw}")
-    Ws = []
+    banner(f"qmv multi {fmt_name} mode={mode} f32={act_f32} k={k} N={N} K={K} nw={nw}")
+    Ws, refs = [], {}
+    x = synth.activations(40, 0, k, K)
+    x64 = oracle.bf16_to_f64(x)
+    if act_f32:
+        x64 = (oracle.bf16_to_f64(x).astype(np.float32) * np.float32(1.25)).astype(np.float64)
     for m in range(nw):
         if fmt_name == "q8":
             qs, d = synth.q8_0_weight(40, DENSE_W, m, 1, N, K)
             W = Q8Weight(torch.from_numpy(np.ascontiguousarray(qs[0])).to(DEV),
                          torch.from_numpy(np.ascontiguousarray(d[0]).view(np.int16)).to(DEV))
+            ref = (lambda qs=qs, d=d: oracle.qmv_q8_0(qs[0], d[0], x64))
         elif fmt_name == "q3":
             c, sc, bi, _ = synth.q3_weight(40, DENSE_W, m, 1, N, K)
             W = Q3Weight(torch.from_numpy(np.ascontiguousarray(c[0])).to(DEV),
                          torch.from_numpy(np.ascontiguousarray(sc[0]).view(np.int16)).to(DEV),
                          torch.from_numpy(np.ascontiguousarray(bi[0]).view(np.int16)).to(DEV))
+            ref = (lambda c=c, sc=sc, bi=bi: oracle.qmv_q3(c[0], sc[0], bi[0], x64))
         else:
-            W = q4_device_from_host(*synth.dense_weight(40, DENSE_W, m, N, K))
+            host = synth.dense_weight(40, DENSE_W, m, N, K)
+            W = q4_device_from_host(*host)
+            ref = (lambda host=host: oracle.qmv(*host, x64))
+        if m in (0, nw - 1):
+            refs[m] = ref
         Ws.append(W.tiled(fused_gateup=(mode == 1)))
-    x = synth.activations(40, 0, k, K)
     xd = sdev.upload_bf16(x, DEV)
     if act_f32:
-        xd = torch.from_numpy(oracle.bf16_to_f64(x).astype(np.float32) * np.float32(1.25)).to(DEV)
+        xd = torch.from_numpy(x64.astype(np.float32)).to(DEV)
     outs = ops.qmv_k_multi(Ws, xd, mode)
     for m, W in enumerate(Ws):
         single = to_np(ops.qmv_k(W, xd, mode))
         assert np.array_equal(to_np(outs[m]), single), f"weight {m}"
+    for m, ref in refs.items():
+        r = ref()
+        assert_close(to_np(outs[m]), oracle.swiglu(r) if mode == 1 else r, f"multi weight {m}")
     # the bound form gives the same
     for o in outs:
         o.fill_(0.0)
