@@ -24,11 +24,14 @@
 //            each finished tile (32 outputs per row).  A 64-wide last slice
 //            is padded with zero activations; its second group re-reads the
 //            first group's weights, which then add exactly zero.
-// Each wave's ring of 4 prefetched (codes, scale/bias) blocks runs across the
-// phase boundary.  Phase A is padded to a multiple of 4 steps (the padding
-// steps re-read the tile's last block and compute nothing), so phase B starts
-// at ring slot 0; every refill is unconditional (past the end of the stream it
-// re-reads the last block), which keeps the load counter waits static.
+// Each wave's ring of 4 prefetched (codes, scale/bias) blocks (2 of Q8_0's
+// 2 KB blocks) runs across the phase boundary.  Phase A is padded to a
+// multiple of the ring (the padding steps re-read the tile's last block and
+// compute nothing), so phase B starts at ring slot 0; every refill is
+// unconditional (past the end of the stream it re-reads the last block),
+// which keeps the load counter waits static.  The weights are affine Q4,
+// Q8_0 or affine Q3 (the kernel is instantiated per format; only the block
+// loads, the group step and the Q8_0 activation sums per 32 elements differ).
 // Finished down tiles are written with five buffer stores (store i writes row
 // i from the lanes of half 0 and row 4 + i from half 1; the fifth writes row
 // 8); lanes without a row get an out-of-range offset, so each tile issues the
