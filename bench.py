@@ -846,6 +846,35 @@ def gdn36_chains(dev, widths=tuple(range(1, 10)), steps=16):
     return {"workload": "gdn36: 36 layers x state [48,128,128] fp32, 16-step chains with rollback", "widths": out}
 
 
+def gdn_layers_one_launch(wl, dev, unions, reps=20):
+    """The step's GDN layers (preparation + recurrence with snapshots) as
+    independent layers in one launch (sdv_gdn_verify_prep_k_layers), a
+    measurement form labelled as such: it shows the kernel's bandwidth
+    without the ramp of each launch.  The step itself runs one launch per
+    layer, since each layer's input depends on the layer before."""
+    import torch
+    from speculative_decode_verification_amd import ops
+    layers = sorted(wl.gdn)
+    launch = ops.GdnLayersLaunch([wl.gdn[l][0].prep_call() for l in layers], dev)
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    timer = HipTimer(1)
+    a = timer.start()
+    for _ in range(reps):
+        launch()
+    b = timer.stop()
+    torch.cuda.synchronize()
+    us = timer.elapsed_us(a, b) / reps
+    timer.close()
+    lb = sum(wl.kernel_bytes("gdn", l, unions) for l in layers)
+    return {"what": f"{len(layers)} independent GDN layers (preparation + recurrence, k = {wl.k}) in one launch; "
+                    "a measurement form, not the step's launch sequence",
+            "layers": len(layers), "us_per_launch": round(us, 2), "us_per_layer": round(us / len(layers), 2),
+            "bytes_per_layer": round(lb / len(layers)), "gbs": round(lb / us / 1e3, 1),
+            "frac_hbm": round(lb / us / 1e3 / PEAK_HBM_GBS, 3)}
+
+
 def copy_probe():
     """A plain device copy of known size, for scaling HBM counters."""
     import torch
@@ -938,6 +967,11 @@ def main():
                          "frac_hbm": round(d["bytes"] / (d["us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
                      for n, d in agg.items()}
 
+    gdn_batched = None
+    if not args.no_breakdown and not wl.fused_norm:
+        log("timing the GDN layers in one launch (measurement form) ...")
+        gdn_batched = gdn_layers_one_launch(wl, dev, unions)
+
     dense = None
     if not args.no_breakdown:
         log("timing the dense 5120 x 5120 projection ...")
@@ -992,6 +1026,7 @@ def main():
                                                 "(read back by the combine); not in achieved"},
                      "kernel_source_hash": khash},
         "kernels": breakdown,
+        "gdn_layers_one_launch": gdn_batched,
         "dense_qmv_k": dense,
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,

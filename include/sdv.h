@@ -486,6 +486,47 @@ SDV_API int sdv_gdn_verify_prep_k(const float *S_in, const float *qkv, const flo
                                   float *const *snaps, sdv_stream_t stream);
 
 /*
+ * sdv_gdn_layer -- one layer's buffers for sdv_gdn_verify_prep_k_layers: the
+ * pointer arguments of one sdv_gdn_verify_prep_k call, with the same meaning
+ * and sizes (snaps[0..k-1] are used).
+ */
+typedef struct sdv_gdn_layer {
+  const float *S_in, *qkv, *hist, *conv_w, *a, *b, *A_log, *dt_bias;
+  float *window, *y;
+  float *snaps[SDV_MAX_ROWS];
+} sdv_gdn_layer;
+
+/*
+ * sdv_gdn_layers_table -- check L layers for sdv_gdn_verify_prep_k_layers and
+ * copy them into a caller-owned device table (a blocking copy).
+ *   layers       host array [L], 1 <= L <= 65535: each layer is checked as
+ *                sdv_gdn_verify_prep_k checks its pointers, and no output of any
+ *                layer (y, window, snaps) may overlap an input or output of any
+ *                layer, or the table
+ *   k, Hv, Hk, Dk, Dv  the layers' shape, as sdv_gdn_verify_prep_k
+ *   table        device buffer, 16-byte aligned, of at least
+ *                L * sizeof(sdv_gdn_layer) = table_bytes
+ * Errors: EINVAL, EWIDTH, ELAYOUT, EALIAS, EHIP.
+ */
+SDV_API int sdv_gdn_layers_table(const sdv_gdn_layer *layers, int L, int k, int Hv, int Hk, int Dk, int Dv,
+                                 void *table, size_t table_bytes);
+
+/*
+ * sdv_gdn_verify_prep_k_layers -- sdv_gdn_verify_prep_k over L independent
+ * layers of one shape in one launch: a measurement form, which shows the
+ * recurrence's bandwidth without the ramp of each launch (Flash-Next plan,
+ * "2.1 Gated DeltaNet").  In a model each layer's input depends on the layer
+ * before, so layers run one sdv_gdn_verify_prep_k call each.  Every layer's y,
+ * snapshots and window equal its own sdv_gdn_verify_prep_k call's bit for bit.
+ *   table    device table written by sdv_gdn_layers_table with the same L, k,
+ *            Hv, Hk, Dk, Dv (its pointers are not checked again)
+ *   conv_act, eps  as sdv_gdn_verify_prep_k, for every layer
+ * Errors: EINVAL, EWIDTH, ELAYOUT, ERANGE (eps), EHIP.
+ */
+SDV_API int sdv_gdn_verify_prep_k_layers(const void *table, int L, int k, int Hv, int Hk, int Dk, int Dv,
+                                         int conv_act, float eps, sdv_stream_t stream);
+
+/*
  * sdv_gdn_gated_norm_k -- the GDN output before its projection (Flash-Next plan,
  * "2.1 Gated DeltaNet": gated RMSNorm rmsnorm(y) * act(gate); "5.1": sigmoid gate
  * for this model; Red Lite dev45 "What it is": the tail norm).
@@ -502,7 +543,7 @@ SDV_API int sdv_gdn_gated_norm_k(const float *y, const float *z, const float *w,
  * sdv_gdn_verify_prep_norm_k -- sdv_gdn_verify_prep_k and sdv_gdn_gated_norm_k
  * in one launch (Flash-Next plan, "2.1 Gated DeltaNet": preparation,
  * recurrence and the gated RMSNorm tail of one layer).  The last of each
- * head's Dv / 16 workgroups to finish applies that head's norm; y, the
+ * head's workgroups to finish applies that head's norm; y, the
  * snapshots, the window and out equal those of the two separate calls bit
  * for bit.  A workgroup counts itself in only after all of its stores have
  * completed, snapshots included, so at the 48-head layer shape the two

@@ -20,7 +20,7 @@ EXPORTS = ("sdv_q4t_codes_bytes", "sdv_q4t_sb_bytes", "sdv_q4_repack", "sdv_q8_0
            "sdv_gather_qmv_k", "sdv_moe_experts_k", "sdv_moe_route_experts_k", "sdv_moe_experts_partial_bytes", "sdv_moe_combine_sliced_k",
            "sdv_moe_combine_k", "sdv_gdn_verify_k", "sdv_gdn_rollback",
            "sdv_gdn_rollback_copy", "sdv_gdn_prepare_k", "sdv_gdn_verify_prep_k", "sdv_gdn_verify_prep_norm_k",
-           "sdv_gdn_gated_norm_k",
+           "sdv_gdn_layers_table", "sdv_gdn_verify_prep_k_layers", "sdv_gdn_gated_norm_k",
            "sdv_verify_accept_workspace_bytes", "sdv_verify_accept_k", "sdv_verify_accept_k_noalloc",
            "sdv_verify_accept_scratch_bytes",
            "sdv_status_string", "sdv_last_error", "sdv_build_info")
@@ -30,6 +30,11 @@ class SdvQ4(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("group", ctypes.c_int32)]
+
+
+class SdvGdnLayer(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("S_in", "qkv", "hist", "conv_w", "a", "b", "A_log", "dt_bias",
+                                                 "window", "y")] + [("snaps", ctypes.c_void_p * MAX_ROWS)]
 
 
 class SdvQ4T(ctypes.Structure):
@@ -87,6 +92,8 @@ _SIGS = {
                               ctypes.POINTER(_P), _P],
     "sdv_gdn_verify_prep_norm_k": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(_P), _P, _P, _I, ctypes.c_float, _P, _P, _P],
+    "sdv_gdn_layers_table": [ctypes.c_void_p, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t],
+    "sdv_gdn_verify_prep_k_layers": [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P],
     "sdv_gdn_gated_norm_k": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P],
     "sdv_verify_accept_workspace_bytes": [_I, _I],
     "sdv_verify_accept_k": [_P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],

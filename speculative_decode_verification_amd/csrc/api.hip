@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "common.h"
 
 namespace sdv {
@@ -61,6 +63,8 @@ hipError_t accept_noalloc_launch(const float* logits, const float* noise, float 
 hipError_t gdn_launch(const float* S_in, const float* q, const float* kk, const float* v,
                       const float* g, const float* beta, int k, int Hv, int Hk, int Dk, int Dv,
                       float* y, float* const* snaps, hipStream_t st);
+hipError_t gdn_verify_prep_layers_launch(const sdv_gdn_layer* table, int L, int k, int Hv, int Hk, int D,
+                                         int conv_act, float eps, hipStream_t st);
 hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const float* hist, const float* conv_w,
                                   const float* ga, const float* gb, const float* A_log, const float* dt_bias, int k,
                                   int Hv, int Hk, int D, int conv_act, float eps, float* window, float* y,
@@ -88,6 +92,15 @@ int fail(int status, const char* fmt, ...) {
 int ok() {
   g_err[0] = '\0';
   return SDV_OK;
+}
+
+// Appends to the message of the last failure.
+void fail_note(const char* fmt, ...) {
+  const size_t n = strlen(g_err);
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err + n, sizeof g_err - n, fmt, ap);
+  va_end(ap);
 }
 
 struct Range {
@@ -869,6 +882,48 @@ int sdv_gdn_verify_prep_k(const float* S_in, const float* qkv, const float* hist
   return hip_status(sdv::gdn_verify_prep_launch(S_in, qkv, hist, conv_w, a, b, A_log, dt_bias, k, Hv, Hk, Dk,
                                                 conv_act, eps, window, y, snaps, (hipStream_t)stream),
                     "sdv_gdn_verify_prep_k launch");
+}
+
+int sdv_gdn_layers_table(const sdv_gdn_layer* layers, int L, int k, int Hv, int Hk, int Dk, int Dv, void* table,
+                         size_t table_bytes) {
+  int st;
+  if (!layers) return fail(SDV_EINVAL, "layers is NULL");
+  if (L < 1 || L > 65535) return fail(SDV_EINVAL, "L=%d outside 1..65535", L);
+  if ((st = check_ptr(table, "table"))) return st;
+  const size_t need = (size_t)L * sizeof(sdv_gdn_layer);
+  if (table_bytes < need) return fail(SDV_EINVAL, "table has %zu bytes, %d layers need %zu", table_bytes, L, need);
+  if ((st = check_width(k))) return st;
+  std::vector<Range> outs((size_t)L * (k + 2) + 1), ins((size_t)L * 8);
+  for (int l = 0; l < L; ++l) {
+    const sdv_gdn_layer& g = layers[l];
+    if ((st = check_verify_prep(g.S_in, g.qkv, g.hist, g.conv_w, g.a, g.b, g.A_log, g.dt_bias, k, Hv, Hk, Dk, Dv,
+                                SDV_CONV_NONE, 0.0f, g.window, g.y, g.snaps, &outs[(size_t)l * (k + 2)],
+                                &ins[(size_t)l * 8]))) {
+      fail_note(" (layer %d)", l);
+      return st;
+    }
+  }
+  outs.back() = {table, need, "table"};
+  if ((st = check_alias(outs.data(), (int)outs.size(), ins.data(), (int)ins.size()))) return st;
+  return hip_status(hipMemcpy(table, layers, need, hipMemcpyHostToDevice), "sdv_gdn_layers_table copy");
+}
+
+int sdv_gdn_verify_prep_k_layers(const void* table, int L, int k, int Hv, int Hk, int Dk, int Dv, int conv_act,
+                                 float eps, sdv_stream_t stream) {
+  int st;
+  if ((st = check_ptr(table, "table"))) return st;
+  if (L < 1 || L > 65535) return fail(SDV_EINVAL, "L=%d outside 1..65535", L);
+  if ((st = check_width(k))) return st;
+  if (Hv <= 0 || Hk <= 0) return fail(SDV_EINVAL, "Hv=%d Hk=%d must be positive", Hv, Hk);
+  if (Hv % Hk) return fail(SDV_ELAYOUT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
+  if (Dk != Dv || (Dk != 64 && Dk != 128))
+    return fail(SDV_ELAYOUT, "Dk=%d Dv=%d: the preparation needs Dk = Dv in {64, 128}", Dk, Dv);
+  if ((long)Hv * Dv > (1L << 26)) return fail(SDV_EINVAL, "Hv*Dv=%ld too large", (long)Hv * Dv);
+  if (conv_act != SDV_CONV_NONE && conv_act != SDV_CONV_SILU) return fail(SDV_EINVAL, "conv_act=%d", conv_act);
+  if (!(eps >= 0.0f && eps <= 3.4e38f)) return fail(SDV_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+  return hip_status(sdv::gdn_verify_prep_layers_launch(static_cast<const sdv_gdn_layer*>(table), L, k, Hv, Hk, Dk,
+                                                       conv_act, eps, (hipStream_t)stream),
+                    "sdv_gdn_verify_prep_k_layers launch");
 }
 
 int sdv_gdn_verify_prep_norm_k(const float* S_in, const float* qkv, const float* hist, const float* conv_w,

@@ -54,9 +54,17 @@ struct GdnArgs {
   float neps;
   float* out;       // [k][Hv][Dv]
   int32_t* cnt;     // [Hv], zero between calls
+  // several layers in one launch (LAYERS): layer blockIdx.y's buffers replace
+  // S_in, qkv, hist, conv_w, ga, gb, A_log, dt_bias, window, y and snaps
+  const sdv_gdn_layer* layers;
 };
 
-constexpr int kRowsPerBlock = 16;  // 16 value rows x 16 lanes = 256 threads
+// Value rows per workgroup (16 lanes each): 16 (256 threads), or 32 (512
+// threads) for the one-launch preparation at Dk = 128 and up to 9 rows, where
+// every workgroup repeats the conv and norms of its qk head's 2Dk channels:
+// four workgroups per head instead of eight halve that repeated work.
+constexpr int kRowsPerBlock = 16;
+constexpr int kRowsPerBlockPrep = 32;
 
 // f(integral_constant<int, t>) for t = 0, 1, ... while t < k, in order.
 template <int... T, class F>
@@ -64,7 +72,7 @@ __device__ __forceinline__ void for_rows(std::integer_sequence<int, T...>, int k
   (void)((T < k ? (f(std::integral_constant<int, T>{}), true) : false) && ...);
 }
 
-// LDS_KQ: the block's 16 value rows belong to one v head (Dv % 16 == 0), so
+// LDS_KQ: the block's RB value rows belong to one v head (Dv % RB == 0), so
 // the per-row vectors k_t, q_t (for that head's qk head), v_t, g_t, beta_t of
 // all k rows are staged in LDS once and the serial t loop reads only LDS and
 // registers.  Otherwise they are read from global memory inside the loop.
@@ -74,29 +82,52 @@ __device__ __forceinline__ void for_rows(std::integer_sequence<int, T...>, int k
 // rows equal preparation followed by the recurrence, bit for bit.  Threads
 // 0..2Dk-1 take the q then k channels of the block's qk head (conv, per-wave
 // sums of squares; the factor rsqrt(sum of the waves in order + eps) is
-// applied as row t is read), 16 threads the block's 16 v channels, k threads
-// the gates of its v head; one barrier.  The qk columns of the window
+// applied as row t is read), RB threads the block's RB v channels, k threads
+// the gates of its v head; one barrier.  The waves' sums are the same at
+// either block size, so every output is too.  The qk columns of the window
 // are written by the first block of each qk head, the v columns by their
 // block.  Blocks of one qk head are placed on one XCD when the block count
 // allows, so its repeated q/k inputs are L2 hits.
 //
 // NORM (with PREP): the gated output norm of each head is applied by the
-// last of the head's Dv / 16 workgroups to finish.  Every workgroup stores
+// last of the head's Dv / RB workgroups to finish.  Every workgroup stores
 // its y rows with agent-scope coherent stores, and every thread issues an
 // agent-scope release fence before the workgroup counts itself in on the
 // head's counter (an acquire-release add); the workgroup
-// that brings the count to Dv / 16 resets it to zero, issues an acquire
+// that brings the count to Dv / RB resets it to zero, issues an acquire
 // fence, reads the head's y rows back (coherent loads) and runs the same arithmetic as
 // gdn_gated_norm_kernel, in the same order, so the output equals the
 // separate launch's bit for bit.  No workgroup waits for another.
-template <int DK, bool LDS_KQ, bool PREP, int R, bool NORM = false>
-__global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
+//
+// LAYERS (with PREP): blockIdx.y picks one of several independent layers of
+// one shape; each runs exactly as its own launch would.
+template <int DK, bool LDS_KQ, bool PREP, int R, bool NORM = false, int RB = kRowsPerBlock, bool LAYERS = false>
+__global__ __launch_bounds__(RB * 16) void gdn_verify_kernel(GdnArgs a_in) {
+  static_assert(!LAYERS || (PREP && !NORM), "the layer form is built for the preparation + recurrence");
+  GdnArgs a = a_in;
+  if constexpr (LAYERS) {
+    const sdv_gdn_layer& l = a_in.layers[blockIdx.y];
+    a.S_in = l.S_in;
+    a.qkv = l.qkv;
+    a.hist = l.hist;
+    a.conv_w = l.conv_w;
+    a.ga = l.a;
+    a.gb = l.b;
+    a.A_log = l.A_log;
+    a.dt_bias = l.dt_bias;
+    a.window = l.window;
+    a.y = l.y;
+#pragma unroll
+    for (int t = 0; t < R; ++t) a.snaps[t] = l.snaps[t];
+  }
   static_assert(!PREP || LDS_KQ, "the in-kernel preparation stages through LDS");
   static_assert(!NORM || PREP, "the output norm needs whole heads per workgroup group (Dv = Dk)");
+  static_assert(RB == 16 || (RB == 32 && DK == 128 && PREP), "32-row blocks are built for the preparation at Dk = 128");
+  constexpr int NT = RB * 16;  // threads: at least 2 DK, one q or k channel each
   constexpr int NV4 = DK / 64;  // float4 per lane
   __shared__ float4 s_k[LDS_KQ ? R * DK / 4 : 1];
   __shared__ float4 s_q[LDS_KQ ? R * DK / 4 : 1];
-  __shared__ float s_v[LDS_KQ ? R * kRowsPerBlock : 1];
+  __shared__ float s_v[LDS_KQ ? R * RB : 1];
   __shared__ float s_g[R], s_b[R];
   __shared__ float s_part[PREP ? 4 : 1][R];
 
@@ -108,7 +139,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   const int lrow = threadIdx.x >> 4;
   // value rows fit in int (Hv * Dv <= 2^26); with PREP, Dv = DK is known
   const int Dv = PREP ? DK : a.Dv;
-  const int row = lblk * kRowsPerBlock + lrow;  // h * Dv + i
+  const int row = lblk * RB + lrow;  // h * Dv + i
   const int nrows = a.Hv * Dv;
   const bool active = row < nrows;
   const int h = active ? row / Dv : 0;
@@ -119,32 +150,32 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   // the staging (KQ_PER_THREAD float4 of k and of q, V_PER_THREAD values of
   // v, one g and beta per thread), then the state.  Loads complete in issue order, so the LDS
   // writes wait only for the staging loads and overlap the state's arrival.
-  static_assert(kRowsPerBlock * 16 == 256, "staging assumes 256 threads");
   float4 S[NV4];
-  constexpr int KQ_PER_THREAD = (R * DK / 4 + 255) / 256;
+  constexpr int KQ_PER_THREAD = (R * DK / 4 + NT - 1) / NT;
   float4 ck[KQ_PER_THREAD], cq[KQ_PER_THREAD];
 #pragma unroll
   for (int u = 0; u < KQ_PER_THREAD; ++u) ck[u] = cq[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  constexpr int V_PER_THREAD = (R * kRowsPerBlock + 255) / 256;  // v values staged per thread
+  constexpr int V_PER_THREAD = (R * RB + NT - 1) / NT;  // v values staged per thread
   float cv[V_PER_THREAD], cg = 0.0f, cb = 0.0f;
 #pragma unroll
   for (int u = 0; u < V_PER_THREAD; ++u) cv[u] = 0.0f;
-  const int row0 = lblk * kRowsPerBlock;
+  const int row0 = lblk * RB;
   const int h0 = row0 / Dv;
   const int i0 = row0 - h0 * Dv;
   const int c0 = h0 / (a.Hv / a.Hk);
   const int n4 = a.k * DK / 4;
   // PREP: the inputs of the block's q/k channel (threads 0..2Dk-1), of its v
-  // channel (threads VB..VB+15) and of its gates (threads GB..GB+k-1); every
+  // channel (threads VB..VB+RB-1) and of its gates (threads GB..GB+k-1); every
   // thread issues all of them, clamped, so the waits are static
-  constexpr int VB = DK == 128 ? 0 : 128, GB = 192;
+  constexpr int VB = DK == 128 ? 0 : 128, GB = NT - 64;
+  static_assert(2 * DK <= NT && GB + SDV_MAX_ROWS <= NT && (DK == 128 || VB + RB <= GB), "preparation thread roles");
   float xq[PREP ? kConvWin<R> : 1], xv[PREP ? kConvWin<R> : 1];
   float4 wq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), wv = wq;
   float pa = 0.0f, pb = 0.0f, pal = 0.0f, pdb = 0.0f;
   const int ratio = a.Hv / a.Hk;
   const int cq_ch = min((int)threadIdx.x, 2 * DK - 1);
   const int c_qk = cq_ch < DK ? c0 * DK + cq_ch : (a.Hk + c0) * DK + cq_ch - DK;
-  const int rv = min(max((int)threadIdx.x - VB, 0), kRowsPerBlock - 1);
+  const int rv = min(max((int)threadIdx.x - VB, 0), RB - 1);
   const int c_v = 2 * a.Hk * DK + h0 * DK + i0 + rv;
   if constexpr (PREP) {
     // gate inputs first: their wave forms the gates while the rest arrives
@@ -165,15 +196,15 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     // discarded), so the compiler can count them exactly in its waits.
 #pragma unroll
     for (int u = 0; u < KQ_PER_THREAD; ++u) {
-      const int t = min((int)threadIdx.x + 256 * u, n4 - 1);
+      const int t = min((int)threadIdx.x + NT * u, n4 - 1);
       const int tt = t / (DK / 4), jj = t - tt * (DK / 4);
       ck[u] = reinterpret_cast<const float4*>(a.kk + ((long)tt * a.Hk + c0) * DK)[jj];
       cq[u] = reinterpret_cast<const float4*>(a.q + ((long)tt * a.Hk + c0) * DK)[jj];
     }
 #pragma unroll
     for (int u = 0; u < V_PER_THREAD; ++u) {
-      const int tv = min((int)threadIdx.x + 256 * u, a.k * kRowsPerBlock - 1);
-      const int tt = tv / kRowsPerBlock, r = min(tv - tt * kRowsPerBlock, (int)(nrows - 1 - row0));
+      const int tv = min((int)threadIdx.x + NT * u, a.k * RB - 1);
+      const int tt = tv / RB, r = min(tv - tt * RB, (int)(nrows - 1 - row0));
       cv[u] = a.v[((long)tt * a.Hv + h0) * Dv + i0 + r];
     }
     const int tg = min((int)threadIdx.x, a.k - 1);
@@ -211,18 +242,18 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
       for (int t = 0; t < R; ++t)
         if (t < k) dst[t * DK + ch] = o[t];
     }
-    if (tid >= VB && tid < VB + kRowsPerBlock) {
+    if (tid >= VB && tid < VB + RB) {
       float ov[R];
       gdn_conv_rows<R>(wv, xv, a.conv_act, ov);
 #pragma unroll
       for (int t = 0; t < R; ++t)
-        if (t < k) s_v[t * kRowsPerBlock + rv] = ov[t];
+        if (t < k) s_v[t * RB + rv] = ov[t];
     }
     __syncthreads();
   } else if (LDS_KQ) {
 #pragma unroll
     for (int u = 0; u < KQ_PER_THREAD; ++u) {
-      const int t = threadIdx.x + 256 * u;
+      const int t = threadIdx.x + NT * u;
       if (t < n4) {
         s_k[t] = ck[u];
         s_q[t] = cq[u];
@@ -230,8 +261,8 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < V_PER_THREAD; ++u) {
-      const int tv = threadIdx.x + 256 * u;
-      if (tv < a.k * kRowsPerBlock) s_v[tv] = (row0 + tv % kRowsPerBlock < nrows) ? cv[u] : 0.0f;
+      const int tv = threadIdx.x + NT * u;
+      if (tv < a.k * RB) s_v[tv] = (row0 + tv % RB < nrows) ? cv[u] : 0.0f;
     }
     if (threadIdx.x < a.k) {
       s_g[threadIdx.x] = cg;
@@ -247,7 +278,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
   // block of the qk head
   auto window_out = [&]() {
     const int tid = threadIdx.x, k = a.k;
-    if (tid >= VB && tid < VB + kRowsPerBlock) {
+    if (tid >= VB && tid < VB + RB) {
 #pragma unroll
       for (int j = 0; j < kConvWin<R>; ++j)
         if (j < kConvHist + k) a.window[(size_t)j * a.C + c_v] = xv[j];
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
       if (LDS_KQ) {
         gt = s_g[t];
         bt = s_b[t];
-        vt = s_v[t * kRowsPerBlock + lrow];
+        vt = s_v[t * RB + lrow];
   #pragma unroll
         for (int j = 0; j < NV4; ++j) {
           kt[j] = s_k[t * (DK / 4) + sub + 16 * j];
@@ -357,7 +388,7 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
 
   if constexpr (NORM) {
     __shared__ int s_last;
-    __shared__ float s_np[256 / 64];
+    __shared__ float s_np[NT / 64];
     // Release: every thread's y stores are visible at agent scope before its
     // workgroup counts itself in; the counter update is acquire-release, and
     // the last workgroup acquires before it reads the other workgroups' y.
@@ -365,16 +396,16 @@ __global__ __launch_bounds__(256) void gdn_verify_kernel(GdnArgs a) {
     __syncthreads();
     if (threadIdx.x == 0) {
       const int n = __hip_atomic_fetch_add(a.cnt + h0, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = n == DK / kRowsPerBlock - 1;
+      const int last = n == DK / RB - 1;
       if (last) __hip_atomic_store(a.cnt + h0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last;
     }
     __syncthreads();
     if (s_last) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      // 256 / DK rows of the head at a time, DK threads per row; wave w of
+      // NT / DK rows of the head at a time, DK threads per row; wave w of
       // a row sums the squares of elements 64 w .. 64 w + 63
-      constexpr int kRowsAtOnce = 256 / DK, kWavesPerRow = DK / 64;
+      constexpr int kRowsAtOnce = NT / DK, kWavesPerRow = DK / 64;
       const int d = threadIdx.x % DK, rsub = threadIdx.x / DK, wave = threadIdx.x >> 6;
       const float wd = a.nw[d];
       for (int t0 = 0; t0 < a.k; t0 += kRowsAtOnce) {
@@ -462,17 +493,42 @@ hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const flo
   a.conv_act = conv_act;
   a.eps = eps;
   a.window = window;
-  const dim3 grid((unsigned)((long)Hv * D / kRowsPerBlock)), block(kRowsPerBlock * 16);
   if (D != 64 && D != 128) return hipErrorInvalidValue;
   const bool wide = k > kPassRows;
+  // 32-row blocks for Dk = 128 up to 9 rows; 16-row blocks otherwise
+  const int rb = (D == 128 && !wide) ? kRowsPerBlockPrep : kRowsPerBlock;
+  const dim3 grid((unsigned)((long)Hv * D / rb)), block(rb * 16);
   auto kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows> : gdn_verify_kernel<64, true, true, kPassRows>)
                       : (wide ? gdn_verify_kernel<128, true, true, kWideRows>
-                              : gdn_verify_kernel<128, true, true, kPassRows>);
+                              : gdn_verify_kernel<128, true, true, kPassRows, false, kRowsPerBlockPrep>);
   if (out)
     kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows, true>
                            : gdn_verify_kernel<64, true, true, kPassRows, true>)
                    : (wide ? gdn_verify_kernel<128, true, true, kWideRows, true>
-                           : gdn_verify_kernel<128, true, true, kPassRows, true>);
+                           : gdn_verify_kernel<128, true, true, kPassRows, true, kRowsPerBlockPrep>);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t gdn_verify_prep_layers_launch(const sdv_gdn_layer* table, int L, int k, int Hv, int Hk, int D,
+                                         int conv_act, float eps, hipStream_t st) {
+  GdnArgs a{};
+  a.layers = table;
+  a.k = k;
+  a.Hv = Hv;
+  a.Hk = Hk;
+  a.Dv = D;
+  a.C = 2 * Hk * D + Hv * D;
+  a.conv_act = conv_act;
+  a.eps = eps;
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  const bool wide = k > kPassRows;
+  const int rb = (D == 128 && !wide) ? kRowsPerBlockPrep : kRowsPerBlock;
+  const dim3 grid((unsigned)((long)Hv * D / rb), (unsigned)L), block(rb * 16);
+  auto kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows, false, kRowsPerBlock, true>
+                              : gdn_verify_kernel<64, true, true, kPassRows, false, kRowsPerBlock, true>)
+                      : (wide ? gdn_verify_kernel<128, true, true, kWideRows, false, kRowsPerBlock, true>
+                              : gdn_verify_kernel<128, true, true, kPassRows, false, kRowsPerBlockPrep, true>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
 }

@@ -12,11 +12,11 @@ from collections import namedtuple
 import torch
 
 from ._lib import (ACT_BF16, ACT_F32, CONV_NONE, CONV_SILU, FMT_AFFINE_Q3, FMT_AFFINE_Q4, FMT_Q8_0, GATE_SIGMOID,
-                   GATE_SILU, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvQ3, SdvQ4,
-                   SdvQ4T, SdvQ8_0, check, lib)
+                   GATE_SILU, MODE_GATEUP_SWIGLU, MODE_PLAIN, ROUTE_SIGMOID, ROUTE_SOFTMAX, SdvError, SdvGdnLayer,
+                   SdvQ3, SdvQ4, SdvQ4T, SdvQ8_0, check, lib)
 
 __all__ = ["Q4Weight", "Q8Weight", "Q3Weight", "TiledQ4", "FMT_AFFINE_Q4", "FMT_Q8_0", "FMT_AFFINE_Q3", "RouteResult", "qmv_k", "moe_route_k", "gather_qmv_k", "moe_experts_k", "moe_route_experts_k", "moe_combine_k",
-           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_verify_prep_norm_k", "gdn_norm_counters", "gdn_gated_norm_k",
+           "gdn_verify_k", "gdn_rollback", "gdn_rollback_copy", "gdn_prepare_k", "gdn_verify_prep_k", "gdn_verify_prep_norm_k", "gdn_norm_counters", "gdn_gated_norm_k", "GdnLayersLaunch",
            "CONV_NONE", "CONV_SILU", "GATE_SIGMOID", "GATE_SILU", "SdvError", "MODE_PLAIN",
            "MODE_GATEUP_SWIGLU", "ACT_BF16", "ACT_F32", "ROUTE_SOFTMAX", "ROUTE_SIGMOID"]
 
@@ -665,6 +665,47 @@ def verify_accept_k_noalloc(logits, drafts, tokens, accepted, noise=None, inv_te
 def bind_verify_accept_k(logits, drafts, tokens, accepted, workspace, noise=None, inv_temp=1.0, eos=-1):
     return BoundCall("sdv_verify_accept_k",
                      _accept_args(logits, drafts, noise, inv_temp, eos, tokens, accepted, workspace))
+
+
+class GdnLayersLaunch:
+    """sdv_gdn_verify_prep_k_layers over the layers of bound
+    sdv_gdn_verify_prep_k calls (``bind_gdn_verify_prep_k``,
+    ``GdnLayer.prep_call``): independent layers of one shape in one launch, a
+    measurement form.  The device table is checked and written once, from the
+    calls' buffers; calling the object re-issues the launch."""
+
+    # argument positions of sdv_gdn_verify_prep_k
+    _PTRS = {"S_in": 0, "qkv": 1, "hist": 2, "conv_w": 3, "a": 4, "b": 5, "A_log": 6, "dt_bias": 7,
+             "window": 15, "y": 16}
+    _SHAPE = slice(8, 15)  # k, Hv, Hk, Dk, Dv, conv_act, eps
+    _SNAPS, _STREAM = 17, 18
+
+    def __init__(self, calls, device):
+        if not calls or any(c.name != "sdv_gdn_verify_prep_k" for c in calls):
+            raise ValueError("GdnLayersLaunch takes bound sdv_gdn_verify_prep_k calls")
+        args = [c._args for c in calls]
+        val = lambda v: v.value if isinstance(v, ctypes.c_float) else v
+        shape = [val(v) for v in args[0][self._SHAPE]]
+        if any([val(v) for v in a[self._SHAPE]] != shape for a in args):
+            raise ValueError("the layers of one launch share k, Hv, Hk, Dk, Dv, conv_act and eps")
+        k = shape[0]
+        n = len(calls)
+        entries = (SdvGdnLayer * n)()
+        for e, a in zip(entries, args):
+            for name, i in self._PTRS.items():
+                setattr(e, name, a[i].value)
+            for t in range(k):
+                e.snaps[t] = a[self._SNAPS][t]
+        nbytes = n * ctypes.sizeof(SdvGdnLayer)
+        self.table = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+        check(lib().sdv_gdn_layers_table(ctypes.addressof(entries), n, *shape[:5],
+                                         ctypes.c_void_p(self.table.data_ptr()), nbytes))
+        self.layers = n
+        self._args = (ctypes.c_void_p(self.table.data_ptr()), n, *shape[:6], ctypes.c_float(shape[6]),
+                      args[0][self._STREAM])
+
+    def __call__(self):
+        check(lib().sdv_gdn_verify_prep_k_layers(*self._args))
 
 
 class BoundCall:

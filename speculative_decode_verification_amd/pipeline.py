@@ -306,19 +306,25 @@ class GdnLayer:
             norm_eps)
         return self
 
-    def run_from_proj_bound(self):
+    def prep_call(self):
+        """The bound call ``run_from_proj_bound`` issues next (the live state,
+        history, window and snapshot slots), without issuing it."""
         self.apply_rollback()
         key = (self.live, self.win, self.hist.data_ptr())
         call = self._fp_cache.get(key)
-        ids, arr = self._fp_snaps[self.live]
         if call is None:
+            ids, arr = self._fp_snaps[self.live]
             call = self._fp_template.replaced({
                 self._FP_S_IN: ctypes.c_void_p(self.state.data_ptr()),
                 self._FP_HIST: ctypes.c_void_p(self.hist.data_ptr()),
                 self._FP_WINDOW: ctypes.c_void_p(self.windows[self.win].data_ptr()),
                 self._FP_SNAPS: arr})
             self._fp_cache[key] = call
-        self.snap_ids = ids
+        return call
+
+    def run_from_proj_bound(self):
+        call = self.prep_call()
+        self.snap_ids = self._fp_snaps[self.live][0]
         call()
         self.prepped = True
         return self.y[:self._fp_rows]

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 30
+    assert len(names) == 32
     assert tuple(sorted(L.EXPORTS)) == tuple(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -579,3 +579,56 @@ def test_verify_prep_norm_validation(lib):
     assert verify_prep_norm(lib, out=P + 0x900000) == L.SDV_EALIAS                       # out over y
     assert verify_prep_norm(lib, counters=P + 0xB00000) == L.SDV_EALIAS                  # counters over norm_w
     assert verify_prep_norm(lib, counters=P + 0xC00000 + 4) == L.SDV_EALIAS              # counters over out
+
+
+def gdn_layer(base, k):
+    """A sdv_gdn_layer of fake addresses in its own 256 MB window."""
+    e = L.SdvGdnLayer()
+    for name, off in (("S_in", 0x4000000), ("qkv", 0), ("hist", 0x100000), ("conv_w", 0x200000), ("a", 0x300000),
+                      ("b", 0x310000), ("A_log", 0x320000), ("dt_bias", 0x330000), ("window", 0x800000),
+                      ("y", 0x900000)):
+        setattr(e, name, base + off)
+    for t in range(k):
+        e.snaps[t] = base + 0x5000000 + 0x1000000 * t
+    return e
+
+
+def test_gdn_layers_validation(lib):
+    """The layer table is checked layer by layer as sdv_gdn_verify_prep_k
+    checks its arguments, and for overlaps across layers and with the table;
+    the layered launch checks its shape, all before any HIP call."""
+    k, n = 2, 3
+    arr = (L.SdvGdnLayer * n)(*[gdn_layer(P + 0x10000000 * (l + 1), k) for l in range(n)])
+    size = n * ctypes.sizeof(L.SdvGdnLayer)
+    assert ctypes.sizeof(L.SdvGdnLayer) == 42 * 8
+    table = P + 0x80000000
+    tab = lambda a=arr, nl=n, kk=k, Hv=4, Hk=2, D=64, t=table, nb=size: lib.sdv_gdn_layers_table(
+        ctypes.addressof(a), nl, kk, Hv, Hk, D, D, t, nb)
+    assert lib.sdv_gdn_layers_table(None, n, k, 4, 2, 64, 64, table, size) == L.SDV_EINVAL
+    assert tab(nl=0) == L.SDV_EINVAL
+    assert tab(nl=65536) == L.SDV_EINVAL
+    assert tab(t=0) == L.SDV_EINVAL
+    assert tab(t=table + 8) == L.SDV_EINVAL                              # misaligned
+    assert tab(nb=size - 1) == L.SDV_EINVAL
+    assert tab(kk=33) == L.SDV_EWIDTH
+    assert tab(Hv=5) == L.SDV_ELAYOUT
+    arr[1].conv_w = 0
+    assert tab() == L.SDV_EINVAL
+    assert lib.sdv_last_error().decode() == "conv_w is NULL (layer 1)"
+    arr[1].conv_w = P + 0x20000000 + 0x200000
+    arr[2].y = arr[0].window                                             # y of one layer over another's window
+    assert tab() == L.SDV_EALIAS
+    arr[2].y = arr[1].S_in                                               # an output over another layer's input
+    assert tab() == L.SDV_EALIAS
+    arr[2].y = P + 0x30000000 + 0x900000
+    assert tab(t=arr[0].qkv) == L.SDV_EALIAS                             # the table over an input
+    assert lib.sdv_last_error().decode() == "output table overlaps input qkv"
+    launch = lambda nl=n, kk=k, Hv=4, Hk=2, D=64, Dv=None, act=0, eps=1e-6, t=table: \
+        lib.sdv_gdn_verify_prep_k_layers(t, nl, kk, Hv, Hk, D, D if Dv is None else Dv, act, eps, None)
+    assert launch(t=0) == L.SDV_EINVAL
+    assert launch(nl=0) == L.SDV_EINVAL
+    assert launch(kk=0) == L.SDV_EWIDTH
+    assert launch(Hv=6, Hk=4) == L.SDV_ELAYOUT
+    assert launch(D=128, Dv=64) == L.SDV_ELAYOUT
+    assert launch(act=9) == L.SDV_EINVAL
+    assert launch(eps=-1.0) == L.SDV_ERANGE
