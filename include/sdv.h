@@ -223,9 +223,10 @@ SDV_API int sdv_q4_repack(const sdv_q4 *src, int fused_gateup, void *codes_out, 
  * sdv_qmv_k -- dense multi-row affine-Q4 matvec (E must be 1).
  * The width-k product decodes each weight once for all k rows; each row
  * equals the width-1 result bit for bit (mere.run report, "Exact verification
- * kernels and benchmark admission": small-batch Q4 kernel against serial QMV
- * with exact agreement at widths 4, 8, 9; Red Lite dev45 "What it is": decode
- * each weight once and compute each row in the 1-row kernel's order).
+ * kernels and benchmark admission": the few-row Q4 product agrees bit for bit
+ * with one-row products at widths 4, 8 and 9; Red Lite dev45 "What it is": one
+ * decode of the weights serves every row, each row summed in the one-row
+ * kernel's order).
  *   W         tiled weight descriptor (host struct, device arrays)
  *   act       device, [k][K]: bf16 bits (act_dtype SDV_ACT_BF16) or fp32 (SDV_ACT_F32)
  *   k         rows, 1..SDV_MAX_ROWS
@@ -442,10 +443,11 @@ SDV_API int sdv_gdn_rollback_copy(float *dst, const float *S_in, float *const *s
 
 /*
  * sdv_gdn_prepare_k -- the inputs of the k-row recurrence from their
- * projections (Flash-Next plan, "2.1 Gated DeltaNet": a short causal depthwise
- * conv1d over the concatenated q/k/v channels whose last kernel - 1 input
- * columns are persistent state, per-head L2 normalisation of q and k, the
- * decay gate from A_log and dt_bias via softplus and exp, beta = sigmoid(b);
+ * projections (Flash-Next plan, "2.1 Gated DeltaNet": every q, k and v
+ * channel is filtered along time by its own short filter that sees only the
+ * current and earlier inputs, the last three inputs carried from call to
+ * call; q and k are scaled to unit L2 norm per head; g comes from A_log and
+ * dt_bias through softplus and exp, and beta = sigmoid(b);
  * "5.1 Gated DeltaNet": 4 taps; Red Lite dev45, "What it is": the per-row
  * conv shift, q/k norm and beta/decay kernels).
  *   qkv      device fp32 [k][C], C = 2 Hk Dk + Hv Dv, channels [q heads | k heads | v heads]
@@ -528,7 +530,7 @@ SDV_API int sdv_gdn_verify_prep_k_layers(const void *table, int L, int k, int Hv
 
 /*
  * sdv_gdn_gated_norm_k -- the GDN output before its projection (Flash-Next plan,
- * "2.1 Gated DeltaNet": gated RMSNorm rmsnorm(y) * act(gate); "5.1": sigmoid gate
+ * "2.1 Gated DeltaNet": y scaled by its reciprocal RMS, times act(gate); "5.1": sigmoid gate
  * for this model; Red Lite dev45 "What it is": the tail norm).
  *   y, z     device fp32 [k][Hv][Dv]: the recurrence output and the gate projection
  *   w        device fp32 [Dv]: the norm weight
@@ -574,10 +576,10 @@ SDV_API size_t sdv_verify_accept_workspace_bytes(int k, int V);
 /*
  * sdv_verify_accept_k -- acceptance of a verified block: the token sampled from
  * each row and the number of leading drafts accepted (Red Lite dev45,
- * "Acceptance": a draft is accepted when the token sampled from the previous
- * row's logits equals it, so the output is that of ordinary decoding with any
- * sampler; dev45b: a draft whose sampled token is the end-of-answer token is
- * rejected, so that token never enters the state).
+ * "Acceptance": draft t stands when it equals the token sampled from row
+ * t-1's logits, so the output distribution is that of plain decoding for any
+ * sampler; dev45b: a draft that matches the end-of-answer token is refused, so
+ * that token never enters the state).
  *   logits    device fp32 [k][V]: row t's next-token logits (row 0 follows the
  *             pending token, row t > 0 follows draft t)
  *   noise     device fp32 [k][V] Gumbel(0, 1) noise, or NULL for greedy

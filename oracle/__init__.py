@@ -21,21 +21,23 @@ definition written out.  Sources, by page and section:
 * Red Lite dev45 ("speculative decoding with the Qwen3-Next MTP block"),
   "What it is": each row of a multi-row product is computed separately; row
   t of the DeltaNet runs from the state after row t-1 and that state is
-  snapshotted; one router dispatch and the union of the rows' experts; a
-  rejected draft is undone by selecting the snapshot.
-* Red Lite dev45, "Acceptance": a draft is accepted when the token sampled
-  from the previous row's logits equals it (exact with any sampler); dev45b:
-  a draft whose sampled token is the end-of-answer token is rejected.
+  snapshotted; one router dispatch and the union of the rows' experts;
+  rolling back means picking the snapshot of the accepted prefix.
+* Red Lite dev45, "Acceptance": draft t stands when it equals the token
+  sampled from row t-1's logits, which leaves the output distribution that of
+  plain decoding for any sampler; dev45b: a draft that matches the
+  end-of-answer token is refused.
 * Flash-Next plan, "2.1 Gated DeltaNet" and "5.1 Gated DeltaNet": the
-  preparation (causal depthwise conv1d of kernel 4 over the q/k/v channels
-  with a carried tail, per-head L2 norm of q and k, g from A_log and dt_bias
+  preparation (a 4-tap filter along time per q, k and v channel over the
+  current and the three earlier inputs, the earlier ones carried between
+  calls; q and k scaled to unit L2 norm per head; g from A_log and dt_bias
   by softplus and exp, beta = sigmoid(b)) and the gated RMSNorm output.
 * mere.run transfer report, "Shared architecture and implemented paths": the
   gathered expert kernel's Flash-Next Q3 specialization (affine, group 64,
   3-bit codes; the bit packing is our definition).
 * Red Lite dev45, "What it is": the MTP block's experts are Q8_0 (GGUF
-  blocks of 32 signed 8-bit codes and one half-precision scale), decoded as
-  the dense Q8_0 dequantizer does.
+  blocks of 32 signed 8-bit codes and one half-precision scale), with the
+  same value per code as the dense Q8_0 decode.
 * Flash-Next plan (QWEN38FLASH.md): "2.1 Gated DeltaNet" (decay, kv_mem,
   delta, rank-1 update, readout on fp32 [Hv, Dv, Dk]), "2.3 MoE" (routed +
   shared experts, SwiGLU, gate+up concatenated), "3.1 Overlap" (per-head

@@ -54,7 +54,7 @@ def qmv(codes, scales, biases, x):
     ``x``: fp64 ``[k, K]``; returns fp64 ``[k, N]`` with ``y[r] = W @ x[r]``.
     A width-k verification row must equal the serial width-1 product (mere.run
     transfer report, "Exact verification kernels and benchmark admission";
-    Red Lite dev45, "What it is": each row in exactly the 1-row order), so the
+    Red Lite dev45, "What it is": each row summed as the one-row product sums it), so the
     definition is the 1-row product applied per row."""
     w = dequant(codes, scales, biases)
     x = np.asarray(x, dtype=np.float64)
@@ -67,8 +67,8 @@ def qmv(codes, scales, biases, x):
 # ---------------------------------------------------------------------------
 # routing and union (mere.run report: 256-expert top-8 gathered experts;
 # Red Lite "What it is": one router dispatch for both rows, the (expert, row)
-# pairs of the rows' union; Flash-Next plan "2.3 MoE": 512 experts, 10 routed
-# + 1 shared)
+# pairs of the rows' union; Flash-Next plan "2.3 MoE": a bank of 512 experts,
+# each row routed to 10 of them, plus one shared expert)
 # ---------------------------------------------------------------------------
 
 # ---------------------------------------------------------------------------
@@ -107,8 +107,8 @@ def qmv_q3(codes, scales, biases, x):
 
 
 # ---------------------------------------------------------------------------
-# Q8_0 (Red Lite dev45, "What it is": the MTP block's 512 experts are Q8_0 and
-# decode bit-identically to the dense Q8_0 dequantizer; mere.run transfer
+# Q8_0 (Red Lite dev45, "What it is": the MTP block keeps its 512 experts in
+# Q8_0, each code decoding to the same value as in the dense decode; mere.run transfer
 # report, "Shared architecture and implemented paths": the checkpoint's Q8
 # router and shared-gate weights).  The GGUF Q8_0 block: 32 signed 8-bit codes
 # sharing one IEEE half scale.
@@ -294,7 +294,7 @@ def moe_verify(x, logits, gate_up, down, topk, mode, renorm, z=None, shared_gate
 
 
 # ---------------------------------------------------------------------------
-# Gated DeltaNet (Flash-Next plan, "2.1 Gated DeltaNet (GDN) - 36 layers";
+# Gated DeltaNet (Flash-Next plan, section 2.1 on the model's GDN layers;
 # "3.1 Overlap": per-head scalar decay and beta, k heads shared by v heads;
 # Red Lite dev45 "What it is": row t runs from row t-1's state, the state
 # after each row is snapshotted; rejection selects the snapshot)
@@ -358,11 +358,10 @@ def rollback(S_in, snaps, j):
 
 
 # ---------------------------------------------------------------------------
-# acceptance (Red Lite dev45, "Acceptance": a draft is accepted when the token
-# sampled from the previous row's logits equals it, which keeps the output that
-# of ordinary decoding with any sampler; dev45b: a draft row whose sampled
-# token is the end-of-answer token is rejected, so that token never enters the
-# state)
+# acceptance (Red Lite dev45, "Acceptance": draft t stands when it equals the
+# token sampled from row t-1's logits, so the output distribution stays that
+# of plain decoding for any sampler; dev45b: a draft that matches the
+# end-of-answer token is refused, so that token is kept out of the state)
 # ---------------------------------------------------------------------------
 
 def sample_tokens(logits, noise=None, inv_temp=1.0):
@@ -418,12 +417,12 @@ def verify_cycle(logits, drafts, eos=-1, noise=None, inv_temp=1.0):
 
 
 # ---------------------------------------------------------------------------
-# GDN preparation and tail (Flash-Next plan, "2.1 Gated DeltaNet": a short
-# causal depthwise conv1d over the concatenated q/k/v channels, per-head L2
-# normalisation of q and k, the decay gate from A_log and dt_bias via
-# softplus and exp, beta = sigmoid(b), and the gated RMSNorm output
-# rmsnorm(y) * act(gate); persistent conv tail = the last kernel - 1 input
-# columns; "5.1 Gated DeltaNet": kernel size 4, sigmoid gate for this model)
+# GDN preparation and tail (Flash-Next plan, "2.1 Gated DeltaNet": each q,
+# k and v channel filtered along time by its own filter over the current and
+# earlier inputs, the earlier inputs kept between calls; q and k scaled to
+# unit L2 norm per head; g from A_log and dt_bias through softplus and exp,
+# beta = sigmoid(b); the output is the RMS-normalised y times act(gate);
+# "5.1 Gated DeltaNet": 4 taps, sigmoid gate for this model)
 # ---------------------------------------------------------------------------
 
 CONV_TAPS = 4

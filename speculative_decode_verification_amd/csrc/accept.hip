@@ -1,9 +1,9 @@
 // Acceptance of a verified block on the device: the token sampled from each
 // row and the number of leading drafts accepted (Red Lite dev45,
-// "Acceptance": a draft is accepted when the token sampled from the previous
-// row's logits equals it, which keeps the output that of ordinary decoding
-// with any sampler; dev45b: a draft whose sampled token is the end-of-answer
-// token is rejected, so that token never enters the state).
+// "Acceptance": draft t stands when it equals the token sampled from row
+// t-1's logits, so the output distribution stays that of plain decoding for
+// any sampler; dev45b: a draft that matches the end-of-answer token is refused,
+// so that token is kept out of the state).
 //
 // A row's sample is its largest score, ties to the lower index.  Greedy
 // scores are the logits; with Gumbel noise g (passed in) a score is

@@ -5,8 +5,8 @@
 // d = beta (v - m), rank-1 update S += d k^T, readout y = S q.  "3.1": g and
 // beta are per-head scalars and each qk head serves Hv/Hk consecutive v heads.
 // Red Lite dev45, "What it is": row t runs from row t-1's state and the state
-// after each row is written to a snapshot from inside the kernel, so a
-// rejected draft is undone by selecting a snapshot.
+// after each row is written to a snapshot from inside the kernel; rolling
+// back after a rejection is the choice of one snapshot as the live state.
 //
 // Every value row S_h[i, :] is independent; only t is serial.  A value row
 // lives in registers of 16 lanes (one DPP row) for all k rows of the call:

@@ -1,11 +1,11 @@
 // k-row Gated DeltaNet preparation and output norm (gfx950).
 //
-// Flash-Next plan, "2.1 Gated DeltaNet": before the recurrence, a short
-// causal depthwise conv1d over the concatenated q/k/v channels (the conv
-// keeps the last kernel - 1 input columns as persistent state), L2
-// normalisation of q and k per head, the decay gate from A_log and dt_bias
-// through softplus and exp, and beta = sigmoid(b); after it, the gated
-// RMSNorm rmsnorm(y) * act(gate).  "5.1 Gated DeltaNet": 4 taps, sigmoid gate
+// Flash-Next plan, "2.1 Gated DeltaNet": before the recurrence, every q, k
+// and v channel passes its own short filter along time (current and earlier
+// inputs only; the earlier inputs are kept between calls), q and k are
+// scaled to unit L2 norm per head, g comes from A_log and dt_bias through
+// softplus and exp, and beta = sigmoid(b); after it, y is RMS-normalised and
+// multiplied by the weight and act(gate).  "5.1 Gated DeltaNet": 4 taps, sigmoid gate
 // for this model.  Red Lite dev45, "What it is", runs these per row pair
 // (dn_conv_shift2, dn_qk_l2_2, dn_ba_params2, dn_tail_norm2).
 //

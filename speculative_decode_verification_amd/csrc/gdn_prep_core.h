@@ -2,10 +2,11 @@
 // stand-alone preparation kernel and the recurrence kernel that prepares its
 // own inputs, so both compute every value with the same instructions.
 //
-// Flash-Next plan, "2.1 Gated DeltaNet": causal depthwise conv1d over the
-// concatenated q/k/v channels with the last kernel - 1 inputs kept as state,
-// L2 norm of q and k per head, decay gate exp(-exp(A_log) softplus(a +
-// dt_bias)), beta = sigmoid(b); "5.1 Gated DeltaNet": 4 taps.
+// Flash-Next plan, "2.1 Gated DeltaNet": a per-channel filter along time over
+// the q, k and v channels (current and earlier inputs only, the earlier ones
+// carried between calls), q and k scaled to unit L2 norm per head, decay
+// gate exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b); "5.1 Gated
+// DeltaNet": 4 taps.
 #pragma once
 
 #include "common.h"

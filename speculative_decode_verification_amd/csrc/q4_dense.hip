@@ -3,9 +3,10 @@
 //
 // Each packed weight is read from HBM once and decoded once for all k rows
 // (mere.run transfer report, "Exact verification kernels and benchmark
-// admission": the small-batch Q4 projection against serial QMV, exact at
-// widths 4, 8, 9; Red Lite dev45, "What it is": decode each weight once and
-// compute each row in the 1-row kernel's order).
+// admission": the few-row Q4 projection checked bit for bit against one-row
+// products at widths 4, 8 and 9; Red Lite dev45, "What it is": one decode of
+// the weights serves every row, and each row keeps the summation order of
+// the one-row kernel).
 //
 // A dense projection has few tiles (160 for 5120 outputs) and a long K, so
 // the time of one launch is a latency chain: load, stage, the tile's group

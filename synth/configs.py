@@ -2,7 +2,8 @@
 
 Shapes follow the pages: the mere.run transfer report ("Shared architecture
 and implemented paths"; "Exact verification kernels and benchmark admission")
-for the 5,120-wide dense projections and the 2,048/512, 256-expert top-8 MoE;
+for the 5,120-wide dense projections and the MoE of 256 experts (hidden
+2,048, intermediate 512) with 8 routed per row;
 the Flash-Next plan ("2.1 Gated DeltaNet", "2.3 MoE") for the 48-layer
 hybrid with 16/48 GDN heads of dimension 128 and the 512-expert top-10 MoE
 with intermediate 640 and one shared expert.
