@@ -338,7 +338,13 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
 
   // ---- unit: a union expert's rows, or the shared expert's k rows.  The
   // routing words are loaded together before any is tested.
-  const int u = blockIdx.y, j = blockIdx.x;
+  // The shared expert (every row: the unit with the most staging and output)
+  // takes grid row ysh, inside the first 192 workgroups in dispatch order,
+  // instead of the last row: dispatched last, its workgroups shared CUs and
+  // ended last (47.6-48.7 against 46.4-47.1 us per flashnext launch).  The
+  // rows from ysh on shift up by one; unused units stay at the end.
+  const int ny = gridDim.y, ysh = min(ny - 1, 192 / (int)gridDim.x);
+  const int u = blockIdx.y == ysh ? ny - 1 : (int)blockIdx.y - ((int)blockIdx.y > ysh), j = blockIdx.x;
   const int pass0 = WIDE ? (int)blockIdx.z * kPassRows : 0;
   const bool shared = u == k * a.topk;
   int e = 0, p0 = 0, nrows = k;
