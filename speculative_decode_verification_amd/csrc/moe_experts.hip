@@ -184,6 +184,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, (int)kBufferDword3);
 }
 
+// A wave's issue priority from its progress through its stream: 3 in the
+// first quarter, down to 0 in the last.  Two workgroups that share a CU
+// otherwise issue oldest first, and the second workgroup placed on a CU
+// (which also learns its routing words later) falls behind and ends last;
+// with the wave furthest behind issuing first, the two progress together
+// (45.1-46.1 against 46.1-46.9 us per flashnext launch).
+__device__ __forceinline__ void prio_by_progress(int done, int total) {
+  const int q = (4 * done) / total;  // wave-uniform
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Phase B of one wave: down tiles wave, wave + 8, ... over the slice's two
 // groups.  The stream is padded to whole ring rounds, so every round is the
 // same straight-line code (static load counter waits); padding steps compute
@@ -216,6 +230,7 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const Blk<FMT> (&cb
   float y[5];
   int t = wave;
   auto round = [&](int s0) {
+    prio_by_progress(s0, s_end);
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       // The slice's activations are the same for every tile; an opaque zero
@@ -510,6 +525,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     // whole rounds, then a last round whose steps past nA compute nothing
     const int nAfull = nA / kRing * kRing;
     for (int s0 = 0; s0 < nAfull; s0 += kRing) {
+      prio_by_progress(s0, total);
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = s0 + i;
