@@ -22,11 +22,12 @@
 // depends on K only, so every row is computed in the same order at every
 // width: a width-k row equals the width-1 row bit for bit.
 //
-// A launch over several weights that share the rows (sdv_qmv_k_multi) gives
-// each workgroup mw of them for its tile when that still leaves about 640
-// workgroups: the rows are staged once, each wave streams its K range of
-// every weight in turn through the same ring, and each weight's sums are
-// taken in a table beside the staging as its last group completes.
+// A launch over several weights that share the rows (sdv_qmv_k_multi) has
+// T x nmulti (tile, weight) items; when they outnumber the compute units, one
+// workgroup per compute unit takes an equal share of them: the rows are
+// staged once per workgroup, each wave streams its K range of every item in
+// turn through the same ring, and each item's sums are taken in a table
+// beside the staging as its last group completes.
 //
 // The arithmetic of a group step is the one of the other Q4 kernels: codes
 // decode exactly to bf16 128 + q, the matrix core returns P = sum (128 + q) x
@@ -47,6 +48,19 @@ constexpr int kDenseMaxWaves = 16;
 constexpr size_t kDenseMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
 constexpr int kDenseMulti = 16;  // weights of one multi-weight launch
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 struct DenseArgs {
   // weight blockIdx.y of the launch (one for sdv_qmv_k)
   const uint4* codes[kDenseMulti];  // tiled: [T][G][64] uint4
@@ -54,7 +68,8 @@ struct DenseArgs {
   float* out[kDenseMulti];          // [k][n_out]
   const void* act;       // [k][K] bf16 bits or fp32, shared by the weights
   int N, K, T, G, k, n_out, nw;
-  int nmulti, mw;        // weights of the launch; weights per workgroup (blockIdx.y takes weights mw y ..)
+  int nmulti, mw;        // weights of the launch; mw > 1: workgroups take several (tile, weight) items
+  int items;             // T * nmulti: item i is tile i % T of weight i / T
   int gwmax;             // groups of the widest wave range
   int cap;               // staged rows per wave (k or 3k); row cap is all zero
   int region;            // bytes of one wave's LDS region
@@ -129,21 +144,26 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
                                   : reinterpret_cast<const uint4*>(static_cast<const float*>(a.act) + e0)[q];
   }
 
-  // ---- the wave's weight blocks: the workgroup's weights m0 .. m0 + nm - 1
-  // one after the other, step s reads block (t, gb + s % gw) of weight
-  // m0 + s / gw (steps past the end re-read the last block)
-  const int m0 = MW ? blockIdx.y * a.mw : blockIdx.y;
-  const int nm = MW ? min(a.mw, a.nmulti - m0) : 1;
+  // ---- the wave's weight blocks.  One item: tile t (blockIdx.x) of weight
+  // blockIdx.y.  MW: the workgroup's items it0 .. it0 + nm - 1 of the (tile,
+  // weight) space, an equal share for every workgroup, one after the other;
+  // step s reads block gb + s % gw of item it0 + s / gw (steps past the end
+  // re-read the last block)
+  const int it0 = MW ? (int)(((long)blockIdx.x * a.items) / gridDim.x) : 0;
+  const int nm = MW ? (int)(((long)(blockIdx.x + 1) * a.items) / gridDim.x) - it0 : 1;
   const int ns = nm * gw;
-  const size_t blk0 = (size_t)t * G + gb;
+  // the tile and weight of item mi of the workgroup
+  auto item_tile = [&](int mi) { return MW ? __builtin_amdgcn_readfirstlane((it0 + mi) % a.T) : t; };
+  auto item_weight = [&](int mi) { return MW ? __builtin_amdgcn_readfirstlane((it0 + mi) / a.T) : (int)blockIdx.y; };
   uint4 cbuf[PF], cbuf2[Q8 ? PF : 1];
   uint32_t sbuf[PF];
   auto issue = [&](int slot, int s) {
     s = min(s, ns - 1);
     const int mi = MW ? __builtin_amdgcn_readfirstlane(s / gw) : 0;
-    const uint4* const codes = a.codes[m0 + mi];
-    const uint32_t* const sbp = a.sb[m0 + mi];
-    const size_t blk = blk0 + (s - mi * gw);
+    const int m = item_weight(mi);
+    const uint4* const codes = a.codes[m];
+    const uint32_t* const sbp = a.sb[m];
+    const size_t blk = (size_t)item_tile(mi) * G + gb + (s - mi * gw);
     if constexpr (Q8) {
       cbuf[slot] = load_nt(codes + blk * 128 + lane);  // weights: read once per call
       cbuf2[slot] = load_nt(codes + blk * 128 + 64 + lane);
@@ -256,7 +276,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   }
   const DecodeK dk = decode_k();
   float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  // ---- cross-wave sum of weight m0 + mi in wave order, then its epilogue
+  // ---- cross-wave sum of item mi in wave order, then its epilogue
   float* red = reinterpret_cast<float*>(smem + (MW ? (size_t)nw * a.region : 0));
   const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
   auto finish = [&](int mi) {
@@ -269,7 +289,8 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
       y[i] = 0.0f;
     }
     __syncthreads();
-    float* const out = a.out[m0 + mi];
+    float* const out = a.out[item_weight(mi)];
+    const int tt = item_tile(mi);
     for (int q = tid; q < k * cols_out; q += blockDim.x) {
       const int i = q / cols_out, cc = q - i * cols_out;
       float val[2];
@@ -281,15 +302,15 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
         val[h2] = sum;
       }
       if (MODE == SDV_MODE_PLAIN) {
-        const int on = t * 32 + cc;
+        const int on = tt * 32 + cc;
         if (on < a.N) out[(size_t)i * a.n_out + on] = val[0];
       } else {
-        const int on = t * 16 + cc;
+        const int on = tt * 16 + cc;
         if (on < a.n_out) out[(size_t)i * a.n_out + on] = siluf_(val[0]) * val[1];
       }
     }
   };
-  // group s % gw of weight s / gw; rounds before the last refill their slot
+  // group s % gw of item s / gw; rounds before the last refill their slot
   // after the step, the last does not
   auto gstep = [&](int i, int s) {
     const int g = MW ? s % gw : s;
@@ -542,14 +563,15 @@ hipError_t raise_dense_lds(size_t lds) {
 template <int FMT, int MODE, int ACT, int PF>
 hipError_t dense_launch_one(const DenseArgs& a, int nmulti, size_t lds, hipStream_t st) {
   (void)nmulti;
-  // (a ring of 8 for the several-weight stream measured slower than the
-  // range's own depth: 3.56 against 3.32 us per projection at one row)
+  // (rings of 6 or 8 for the several-item stream measured no faster than the
+  // range's own depth)
   constexpr auto one = q4_dense_k_kernel<FMT, MODE, ACT, PF, false>;
   constexpr auto several = q4_dense_k_kernel<FMT, MODE, ACT, PF, true>;
   const hipError_t err = a.mw > 1 ? raise_dense_lds<several>(lds) : raise_dense_lds<one>(lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(a.mw > 1 ? several : one, dim3(a.T, (a.nmulti + a.mw - 1) / a.mw), dim3(64 * a.nw), lds, st,
-                     a);
+  // several: one workgroup per compute unit, sharing the items evenly
+  const dim3 grid = a.mw > 1 ? dim3((unsigned)min(a.items, device_cus())) : dim3(a.T, a.nmulti);
+  hipLaunchKernelGGL(a.mw > 1 ? several : one, grid, dim3(64 * a.nw), lds, st, a);
   return hipGetLastError();
 }
 
@@ -597,12 +619,14 @@ size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt, int mw) {
   return regions > red ? regions : red;
 }
 
-// Weights per narrow workgroup in a launch over nmulti weights of T tiles:
-// at least about 640 workgroups, and as few stagings of the rows as that allows.
-int dense_weights_per_wg(int T, int nmulti) {
-  const int want_y = (640 + T - 1) / T;
-  const int y = nmulti < want_y ? nmulti : want_y;
-  return (nmulti + y - 1) / y;
+// Items (tile, weight) per narrow workgroup in a launch over nmulti weights
+// of T tiles: one per workgroup while they fit one workgroup per compute
+// unit; beyond that one workgroup per compute unit, each taking an equal
+// share of the items, so the rows are staged once per compute unit and no
+// second round of workgroups leaves CUs idle at the end.
+int dense_items_per_wg(int T, int nmulti) {
+  const int items = T * nmulti, cus = device_cus();
+  return items > cus ? (items + cus - 1) / cus : 1;
 }
 
 namespace {
@@ -630,6 +654,7 @@ DenseArgs dense_args(const sdv_q4t* Ws, int nmulti, int mode, const void* act, i
   a.cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   a.region = (int)dense_region_bytes(a.cap, a.gwmax, W.format == SDV_FMT_Q8_0 ? 2 : 1);
   a.nmulti = nmulti;
+  a.items = a.T * nmulti;
   a.mw = 1;  // the wide form takes one weight per workgroup; the narrow pass sets its own
   return a;
 }
@@ -658,10 +683,10 @@ hipError_t dense_launch_pass(const sdv_q4t* Ws, int nmulti, int mode, const void
                              float* const* outs, hipStream_t st) {
   const sdv_q4t& W = Ws[0];
   DenseArgs a = dense_args(Ws, nmulti, mode, act, act_dtype, k, outs);
-  a.mw = dense_weights_per_wg(a.T, nmulti);
-  // several weights per workgroup keep the staged rows and add the sums'
-  // table; past the LDS a workgroup takes one weight (the size checked on
-  // the host before the launch)
+  a.mw = dense_items_per_wg(a.T, nmulti);
+  // several items per workgroup keep the staged rows and add the sums'
+  // table; past the LDS a workgroup takes one item (the size checked on the
+  // host before the launch)
   if (a.mw > 1 && dense_lds_bytes(W.K, act_dtype, k, W.format, a.mw) > kDenseMaxLds) a.mw = 1;
   const size_t lds = dense_lds_bytes(W.K, act_dtype, k, W.format, a.mw);
 #define SDV_DENSE(F, M, A) \
