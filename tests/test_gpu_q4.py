@@ -182,7 +182,7 @@ def test_mode_must_match_layout():
 MULTI_CASES = [("q4", 0, False, 9, 336, 1024, 5), ("q4", 0, True, 5, 336, 1024, 5), ("q4", 1, False, 9, 320, 1024, 5),
                ("q4", 0, False, 32, 336, 1024, 5), ("q8", 0, False, 9, 336, 1024, 5), ("q3", 0, False, 4, 336, 1024, 5),
                ("q3", 1, False, 20, 320, 1024, 5), ("q8", 0, False, 16, 336, 1024, 5),
-               # several weights per workgroup (one staging of the rows for all of them)
+               # several (tile, weight) items per workgroup (one staging of the rows for all of them)
                ("q4", 0, False, 9, 2560, 5120, 12), ("q4", 1, False, 7, 5120, 1024, 9),
                ("q4", 0, True, 5, 10240, 512, 5), ("q8", 0, False, 9, 2560, 1024, 12),
                ("q3", 0, False, 9, 2560, 1024, 12)]
@@ -193,9 +193,9 @@ def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k, N, 
     """sdv_qmv_k_multi over several weights of one shape that share the
     activation rows: every output equals its own sdv_qmv_k call bit for bit
     (ragged N, the gate/up mode, fp32 rows, 32 rows, Q8_0, Q3, and launches
-    whose workgroups take several weights: 2560 x 5120 x 12, 5120 x 1024 x 9,
-    10240 x 512 x 5 with an uneven last workgroup), and the first and last
-    weights match the oracle."""
+    whose workgroups take several (tile, weight) items, in shares that differ
+    by one: 2560 x 5120 x 12, 5120 x 1024 x 9, 10240 x 512 x 5), and the first
+    and last weights match the oracle."""
     ops = _ops()
     from speculative_decode_verification_amd.ops import Q3Weight, Q8Weight
     banner(f"qmv multi {fmt_name} mode={mode} f32={act_f32} k={k} N={N} K={K} nw={nw}")
