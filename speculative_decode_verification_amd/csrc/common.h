@@ -8,6 +8,9 @@
 
 namespace sdv {
 
+// Compute units of the current device (host; cached per device).
+int device_cus();
+
 // Rows of one pass of the Q4 kernels: a 32-row MFMA operand holds 9
 // activation rows (as three bf16 parts each for fp32 activations).  Wider
 // calls run a unit or launch per pass of at most kPassRows rows.

@@ -80,6 +80,7 @@ struct ExpertArgs {
   int TA, GA, TB, GB, S;
   float* partial;  // [S][k][topk + 1][H]
   uint32_t partial_bytes;
+  int balance;     // more workgroups than compute units: issue priority from stream progress
   // the router dispatch inside the kernel (RPL > 0): its inputs, and the
   // global copies of its outputs (written by workgroup (0, 0))
   const float* logits;
@@ -189,7 +190,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t by
 // otherwise issue oldest first, and the second workgroup placed on a CU
 // (which also learns its routing words later) falls behind and ends last;
 // with the wave furthest behind issuing first, the two progress together
-// (45.1-46.1 against 46.1-46.9 us per flashnext launch).
+// (45.1-46.1 against 46.1-46.9 us per flashnext launch).  Used only when the
+// grid is well above one workgroup per CU (balance_grid): with one workgroup
+// per CU it measured slower (256-expert layers at 5 rows: 23.7-25.6 against
+// 22.9-23.0 us; at 9 rows, 288 workgroups of which about 250 have a unit:
+// 28.5-30.1 against 27.7-28.4 us).
 __device__ __forceinline__ void prio_by_progress(int done, int total) {
   const int q = (4 * done) / total;  // wave-uniform
   if (q <= 0) __builtin_amdgcn_s_setprio(3);
@@ -230,7 +235,7 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const Blk<FMT> (&cb
   float y[5];
   int t = wave;
   auto round = [&](int s0) {
-    prio_by_progress(s0, s_end);
+    if (a.balance) prio_by_progress(s0, s_end);
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       // The slice's activations are the same for every tile; an opaque zero
@@ -357,8 +362,9 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // takes grid row ysh, inside the first 192 workgroups in dispatch order,
   // instead of the last row: dispatched last, its workgroups shared CUs and
   // ended last (47.6-48.7 against 46.4-47.1 us per flashnext launch).  The
-  // rows from ysh on shift up by one; unused units stay at the end.
-  const int ny = gridDim.y, ysh = min(ny - 1, 192 / (int)gridDim.x);
+  // rows from ysh on shift up by one; unused units stay at the end.  Without
+  // a shared expert the order is kept.
+  const int ny = gridDim.y, ysh = a.sgu_codes ? min(ny - 1, 192 / (int)gridDim.x) : ny - 1;
   const int u = blockIdx.y == ysh ? ny - 1 : (int)blockIdx.y - ((int)blockIdx.y > ysh), j = blockIdx.x;
   const int pass0 = WIDE ? (int)blockIdx.z * kPassRows : 0;
   const bool shared = u == k * a.topk;
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     // whole rounds, then a last round whose steps past nA compute nothing
     const int nAfull = nA / kRing * kRing;
     for (int s0 = 0; s0 < nAfull; s0 += kRing) {
-      prio_by_progress(s0, total);
+      if (a.balance) prio_by_progress(s0, total);
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = s0 + i;
@@ -634,6 +640,11 @@ hipError_t launch_experts(const ExpertArgs& a, dim3 grid, size_t lds, hipStream_
   return hipGetLastError();
 }
 
+// Whether the launch takes the progress priorities: a grid over 5/4 of the
+// compute units.  Units past the union exit at once, so a grid just above
+// one workgroup per CU still leaves most CUs with one working workgroup.
+bool balance_grid(dim3 grid) { return (long)grid.x * grid.y * grid.z * 4 > (long)device_cus() * 5; }
+
 ExpertArgs expert_args(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4t* sgu, const sdv_q4t* sdn, const void* x,
                        int k, int topk, float* partial) {
   ExpertArgs a{};
@@ -680,6 +691,7 @@ hipError_t moe_experts_launch(const sdv_q4t& gu, const sdv_q4t& dn, const sdv_q4
   // instead of all k)
   const int passes = (k + kPassRows - 1) / kPassRows;
   const dim3 grid(a.S, units, passes);
+  a.balance = balance_grid(grid);
   switch (gu.format) {
     case SDV_FMT_AFFINE_Q4: return launch_experts<true, 0, SDV_FMT_AFFINE_Q4>(a, grid, lds, st);
     case SDV_FMT_Q8_0: return launch_experts<true, 0, SDV_FMT_Q8_0>(a, grid, lds, st);
@@ -728,6 +740,7 @@ hipError_t moe_route_experts_launch(const float* logits, int mode, int renorm, c
   a.r_slot = pair_slot;
   const size_t lds = route_experts_lds_bytes(k, E, a.H);
   const dim3 grid(a.S, k * topk + (sgu ? 1 : 0));
+  a.balance = balance_grid(grid);
   const int per_lane = (E + 63) / 64;
   if (per_lane <= 1) return launch_experts<false, 1>(a, grid, lds, st);
   if (per_lane <= 2) return launch_experts<false, 2>(a, grid, lds, st);

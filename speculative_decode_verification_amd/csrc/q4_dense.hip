@@ -40,14 +40,6 @@
 
 namespace sdv {
 
-namespace {
-
-using namespace q4;
-
-constexpr int kDenseMaxWaves = 16;
-constexpr size_t kDenseMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
-constexpr int kDenseMulti = 16;  // weights of one multi-weight launch
-
 // Compute units of the current device (cached per device).
 int device_cus() {
   static std::atomic<int> cus[64];
@@ -60,6 +52,14 @@ int device_cus() {
   }
   return n;
 }
+
+namespace {
+
+using namespace q4;
+
+constexpr int kDenseMaxWaves = 16;
+constexpr size_t kDenseMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
+constexpr int kDenseMulti = 16;  // weights of one multi-weight launch
 
 struct DenseArgs {
   // weight blockIdx.y of the launch (one for sdv_qmv_k)
