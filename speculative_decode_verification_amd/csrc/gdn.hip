@@ -60,9 +60,9 @@ struct GdnArgs {
 };
 
 // Value rows per workgroup (16 lanes each): 16 (256 threads), or 32 (512
-// threads) for the one-launch preparation at Dk = 128 and up to 9 rows, where
-// every workgroup repeats the conv and norms of its qk head's 2Dk channels:
-// four workgroups per head instead of eight halve that repeated work.
+// threads) for the one-launch preparation at Dk = 128, where every workgroup
+// repeats the conv and norms of its qk head's 2Dk channels: four workgroups
+// per head instead of eight halve that repeated work.
 constexpr int kRowsPerBlock = 16;
 constexpr int kRowsPerBlockPrep = 32;
 
@@ -124,6 +124,7 @@ __global__ __launch_bounds__(RB * 16) void gdn_verify_kernel(GdnArgs a_in) {
   static_assert(!NORM || PREP, "the output norm needs whole heads per workgroup group (Dv = Dk)");
   static_assert(RB == 16 || (RB == 32 && DK == 128 && PREP), "32-row blocks are built for the preparation at Dk = 128");
   constexpr int NT = RB * 16;  // threads: at least 2 DK, one q or k channel each
+  if (blockDim.x != NT) return;  // a launch of another block size would index past its rows
   constexpr int NV4 = DK / 64;  // float4 per lane
   __shared__ float4 s_k[LDS_KQ ? R * DK / 4 : 1];
   __shared__ float4 s_q[LDS_KQ ? R * DK / 4 : 1];
@@ -495,16 +496,16 @@ hipError_t gdn_verify_prep_launch(const float* S_in, const float* qkv, const flo
   a.window = window;
   if (D != 64 && D != 128) return hipErrorInvalidValue;
   const bool wide = k > kPassRows;
-  // 32-row blocks for Dk = 128 up to 9 rows; 16-row blocks otherwise
-  const int rb = (D == 128 && !wide) ? kRowsPerBlockPrep : kRowsPerBlock;
+  // 32-row blocks for Dk = 128; 16-row blocks otherwise
+  const int rb = D == 128 ? kRowsPerBlockPrep : kRowsPerBlock;
   const dim3 grid((unsigned)((long)Hv * D / rb)), block(rb * 16);
   auto kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows> : gdn_verify_kernel<64, true, true, kPassRows>)
-                      : (wide ? gdn_verify_kernel<128, true, true, kWideRows>
+                      : (wide ? gdn_verify_kernel<128, true, true, kWideRows, false, kRowsPerBlockPrep>
                               : gdn_verify_kernel<128, true, true, kPassRows, false, kRowsPerBlockPrep>);
   if (out)
     kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows, true>
                            : gdn_verify_kernel<64, true, true, kPassRows, true>)
-                   : (wide ? gdn_verify_kernel<128, true, true, kWideRows, true>
+                   : (wide ? gdn_verify_kernel<128, true, true, kWideRows, true, kRowsPerBlockPrep>
                            : gdn_verify_kernel<128, true, true, kPassRows, true, kRowsPerBlockPrep>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
@@ -523,11 +524,11 @@ hipError_t gdn_verify_prep_layers_launch(const sdv_gdn_layer* table, int L, int 
   a.eps = eps;
   if (D != 64 && D != 128) return hipErrorInvalidValue;
   const bool wide = k > kPassRows;
-  const int rb = (D == 128 && !wide) ? kRowsPerBlockPrep : kRowsPerBlock;
+  const int rb = D == 128 ? kRowsPerBlockPrep : kRowsPerBlock;
   const dim3 grid((unsigned)((long)Hv * D / rb), (unsigned)L), block(rb * 16);
   auto kern = D == 64 ? (wide ? gdn_verify_kernel<64, true, true, kWideRows, false, kRowsPerBlock, true>
                               : gdn_verify_kernel<64, true, true, kPassRows, false, kRowsPerBlock, true>)
-                      : (wide ? gdn_verify_kernel<128, true, true, kWideRows, false, kRowsPerBlock, true>
+                      : (wide ? gdn_verify_kernel<128, true, true, kWideRows, false, kRowsPerBlockPrep, true>
                               : gdn_verify_kernel<128, true, true, kPassRows, false, kRowsPerBlockPrep, true>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
