@@ -68,7 +68,7 @@ struct DenseArgs {
   float* out[kDenseMulti];          // [k][n_out]
   const void* act;       // [k][K] bf16 bits or fp32, shared by the weights
   int N, K, T, G, k, n_out, nw;
-  int nmulti, mw;        // weights of the launch; mw > 1: workgroups take several (tile, weight) items
+  int nmulti, mw;        // weights of the launch; items per workgroup (at most; > 1: the several-item form)
   int items;             // T * nmulti: item i is tile i % T of weight i / T
   int gwmax;             // groups of the widest wave range
   int cap;               // staged rows per wave (k or 3k); row cap is all zero
@@ -615,7 +615,7 @@ size_t dense_lds_bytes(int K, int act_dtype, int k, int fmt, int mw) {
   const int cap = act_dtype == SDV_ACT_F32 ? 3 * k : k;
   const size_t regions = (size_t)nw * dense_region_bytes(cap, gwmax, fmt == SDV_FMT_Q8_0 ? 2 : 1);
   const size_t red = dense_red_bytes(nw);
-  if (mw > 1) return regions + red;  // the staged rows serve every weight of the workgroup
+  if (mw > 1) return regions + red;  // the staged rows serve every item of the workgroup
   return regions > red ? regions : red;
 }
 
@@ -655,7 +655,7 @@ DenseArgs dense_args(const sdv_q4t* Ws, int nmulti, int mode, const void* act, i
   a.region = (int)dense_region_bytes(a.cap, a.gwmax, W.format == SDV_FMT_Q8_0 ? 2 : 1);
   a.nmulti = nmulti;
   a.items = a.T * nmulti;
-  a.mw = 1;  // the wide form takes one weight per workgroup; the narrow pass sets its own
+  a.mw = 1;  // the wide form takes one item per workgroup; the narrow pass sets its own
   return a;
 }
 
