@@ -245,7 +245,11 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, const RouteSmem&
       }
     }
   }
-  __syncthreads();
+  // the slots of row r read only what wave r wrote while selecting (its
+  // candidates, count and softmax terms): a wave-level order suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   for (int r = wave; r < a.k; r += NT / 64) {
     // lane c takes the c-th selected candidate (index order) and places it by
     // its rank among the row's selected keys: slot order is larger logit
