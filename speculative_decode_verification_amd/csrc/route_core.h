@@ -314,7 +314,7 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, const RouteSmem&
 #pragma unroll
   for (int w2 = 0; w2 < NT / 64; ++w2) base += w2 < wave ? sm.wave[w2] : 0;
   if (tid == NT - 1) *sm.total = base + incl;
-  __syncthreads();
+  // thread tid alone read cnt[tid] (its scan input), so it may overwrite it
   if (tid < E) sm.cnt[tid] = base + incl - packed;  // exclusive prefix of expert tid
   __syncthreads();
   if (tid < total) {
