@@ -149,11 +149,11 @@ typedef struct sdv_q4t {
  *   scales, biases  [E][N][K/64] bf16;  value = scales * q + biases per group
  * The tiled form (sdv_q3_repack; format = SDV_FMT_AFFINE_Q3) keeps the Q4
  * tiles and sb words; codes [E][T][K/64][3][64] uint32: for tile t and group
- * g, word w of chunk l = 32h + c holds, of the tile's row c and elements
- * 32h + 8j + i (step j, i < 8): w = 0, 1: the low two bits of steps 2w, 2w+1
- * (element i < 4 at bit 8 (j & 1) + 2i, element i + 4 sixteen bits higher);
- * w = 2: bit 2 of step j's element i < 4 at bit 4j + i, of i + 4 sixteen
- * bits higher.  Sizes: sdv_q3t_codes_bytes; sdv_q4t_sb_bytes.
+ * g, the three words w of chunk l = 32h + c hold the tile's row c, elements
+ * 32h + 8j + i (step j, i < 8), as code pairs P = 4j + i (i < 4): element i
+ * at bits 3 (P % 5) .. +2 of word P / 5 and element i + 4 sixteen bits
+ * higher for P < 15; for P = 15, bit b of element i in bit 15 of word b and
+ * of element i + 4 in bit 31.  Sizes: sdv_q3t_codes_bytes; sdv_q4t_sb_bytes.
  */
 typedef struct sdv_q3 {
   const uint8_t *codes;

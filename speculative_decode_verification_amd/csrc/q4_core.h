@@ -38,19 +38,26 @@ __device__ __forceinline__ bf16x8 decode_word(uint32_t w, DecodeK d) {
 }
 
 // Affine Q3: a lane's 32 codes of a group in three words (the tiled layout
-// of SDV_FMT_AFFINE_Q3).  Words 0 and 1 hold the low two bits of steps 0-1
-// and 2-3: step j's element i (i < 4) at bit 8 (j & 1) + 2 i and element
-// i + 4 sixteen bits higher; word 2 holds bit 2 of every code: step j's
-// element i at bit 4 j + i, element i + 4 sixteen bits higher.  A pair
-// decodes, like Q4, to the bf16 values 128 + q of elements (i, i + 4).
+// of SDV_FMT_AFFINE_Q3).  Code pair P = 4 j + i (MFMA step j, elements i and
+// i + 4, i < 4) holds element i's three bits at bit 3 (P % 5) of word P / 5
+// and element i + 4's sixteen bits higher, for P < 15, so the pair decodes
+// like a Q4 nibble pair: one shift and one and-or give the bf16 values
+// 128 + q of elements (i, i + 4).  Pair 15 keeps bit b of its two codes in
+// bits 15 and 31 of word b (the bits the five 3-bit fields of each half
+// leave over).
+__device__ __forceinline__ uint32_t q3_pair(uint32_t w, int s, DecodeK d) { return ((w >> s) & 0x00070007u) | d.bias; }
+
 __device__ __forceinline__ bf16x8 decode_q3(const uint4 cw, int j, DecodeK d) {
-  const uint32_t lo = j < 2 ? cw.x : cw.y;
   uint32_t p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t l2 = (lo >> (8 * (j & 1) + 2 * i)) & 0x00030003u;
-    const uint32_t b2 = ((cw.z >> (4 * j + i)) & 0x00010001u) << 2;
-    p[i] = l2 | b2 | d.bias;
+    const int P = 4 * j + i;
+    if (P < 15) {
+      const uint32_t w = P < 5 ? cw.x : (P < 10 ? cw.y : cw.z);
+      p[i] = q3_pair(w, 3 * (P % 5), d);
+    } else {
+      p[i] = ((cw.x >> 15) & 0x00010001u) | ((cw.y >> 14) & 0x00020002u) | ((cw.z >> 13) & 0x00040004u) | d.bias;
+    }
   }
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(p));
 }

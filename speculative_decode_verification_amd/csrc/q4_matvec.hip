@@ -474,9 +474,24 @@ __global__ __launch_bounds__(256) void q3_repack_kernel(Q3RepackArgs r) {
           q = (uint32_t)((lo >> b) | ((uint64_t)hi << (64 - b))) & 7u;
         else
           q = (hi >> (b - 64)) & 7u;
+        // pair P = 4 j + i of MFMA step j holds elements i (low half) and
+        // i + 4 (high half): bits 3 (P % 5) .. +2 of word P / 5, or, for P =
+        // 15, bit b of the code in bit 15 of word b
         const int j = el >> 3, i8 = el & 7, i = i8 & 3, up = (i8 >> 2) * 16;
-        w[j >> 1] |= (q & 3u) << (up + 8 * (j & 1) + 2 * i);
-        w[2] |= (q >> 2) << (up + 4 * j + i);
+        const int P = 4 * j + i;
+        if (P < 15) {
+          const uint32_t v = q << (up + 3 * (P % 5));
+          if (P < 5)
+            w[0] |= v;
+          else if (P < 10)
+            w[1] |= v;
+          else
+            w[2] |= v;
+        } else {
+          w[0] |= (q & 1u) << (up + 15);
+          w[1] |= ((q >> 1) & 1u) << (up + 15);
+          w[2] |= ((q >> 2) & 1u) << (up + 15);
+        }
       }
     }
 #pragma unroll
