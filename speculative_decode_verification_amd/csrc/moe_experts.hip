@@ -150,18 +150,22 @@ struct Blk<SDV_FMT_Q8_0> {
   uint4 c, c2;
 };
 
-// Block blk (in block units of the format) of a tiled code array.
+// Bytes of one (tile, group) block of the format.
 template <int FMT>
-__device__ __forceinline__ void load_block(Blk<FMT>& b, const void* codes, size_t blk, int lane) {
+constexpr int block_bytes() { return FMT == SDV_FMT_Q8_0 ? 2048 : (FMT == SDV_FMT_AFFINE_Q3 ? 768 : 1024); }
+
+// The lane's part of the block that starts at byte address p.
+template <int FMT>
+__device__ __forceinline__ void load_block(Blk<FMT>& b, const unsigned char* p, int lane) {
   if constexpr (FMT == SDV_FMT_Q8_0) {
-    const uint4* p = static_cast<const uint4*>(codes) + blk * 128;
-    b.c = load_nt(p + lane);  // weights: read once per call
-    b.c2 = load_nt(p + 64 + lane);
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    b.c = load_nt(q + lane);  // weights: read once per call
+    b.c2 = load_nt(q + 64 + lane);
   } else if constexpr (FMT == SDV_FMT_AFFINE_Q3) {
-    const uint32_t* w = static_cast<const uint32_t*>(codes) + blk * 192 + lane;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p) + lane;
     b.c = make_uint4(load_nt(w), load_nt(w + 64), load_nt(w + 128), 0u);
   } else {
-    b.c = load_nt(static_cast<const uint4*>(codes) + blk * 64 + lane);
+    b.c = load_nt(reinterpret_cast<const uint4*>(p) + lane);
   }
 }
 
@@ -422,14 +426,21 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
   // loads in the same order.
   // The block is selected without branches, so a ring round is one
   // straight-line block the compiler can schedule across steps.
+  // Each phase's step-0 block as a byte address (codes) and its sb line,
+  // taken once, so a refill adds a 32-bit block offset to one of two bases.
+  const unsigned char* const cA = reinterpret_cast<const unsigned char*>(guc) + baseA * block_bytes<FMT>();
+  const unsigned char* const cB = reinterpret_cast<const unsigned char*>(dnc) + baseB * block_bytes<FMT>();
+  const uint32_t* const sA = gus + baseA * 32;
+  const uint32_t* const sB = dns + baseB * 32;
+  const int strideB = kWaves * GB;  // blocks from one of the wave's down tiles to its next
   auto issue = [&](int slot, int s) {
     s = max(min(s, total - 1), 0);
     const bool inA = s < nA8;                               // then nA > 0
     const int q = max(min(s - nA8, nB - 1), 0);
-    const int g = min(gB0 + (q & 1), gBlast);               // a 64-wide slice re-reads its only group
-    const long blk = inA ? (long)baseA + min(s, nA - 1) : (long)baseB + (long)(q >> 1) * kWaves * GB + g;
-    load_block<FMT>(cbuf[slot], inA ? guc : dnc, (size_t)blk, lane);  // weights: read once per call
-    sbuf[slot] = load_nt((inA ? gus : dns) + blk * 32 + col);
+    // a 64-wide slice re-reads its only group
+    const int off = inA ? min(s, nA - 1) : (q >> 1) * strideB + min(gB0 + (q & 1), gBlast);
+    load_block<FMT>(cbuf[slot], (inA ? cA : cB) + (unsigned)off * (unsigned)block_bytes<FMT>(), lane);
+    sbuf[slot] = load_nt((inA ? sA : sB) + (unsigned)off * 32u + col);
   };
   // the unit's (row, slot) pairs go out before the ring, so waiting for them
   // does not wait for the ring (loads complete in issue order)
