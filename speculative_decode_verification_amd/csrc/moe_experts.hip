@@ -199,11 +199,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, uint32_t by
 // per CU it measured slower (256-expert layers at 5 rows: 23.7-25.6 against
 // 22.9-23.0 us; at 9 rows, 288 workgroups of which about 250 have a unit:
 // 28.5-30.1 against 27.7-28.4 us).
-__device__ __forceinline__ void prio_by_progress(int done, int total) {
-  const int q = (4 * done) / total;  // wave-uniform
-  if (q <= 0) __builtin_amdgcn_s_setprio(3);
-  else if (q == 1) __builtin_amdgcn_s_setprio(2);
-  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+// The quarters of a stream of `total` steps start at steps ceil(m total / 4),
+// m = 1, 2, 3 (taken once per wave, so a round compares instead of dividing).
+struct Quarters {
+  int t1, t2, t3;
+};
+__device__ __forceinline__ Quarters quarters_of(int total) {
+  return {(total + 3) >> 2, (2 * total + 3) >> 2, (3 * total + 3) >> 2};
+}
+__device__ __forceinline__ void prio_by_progress(int done, const Quarters& q) {
+  if (done < q.t1) __builtin_amdgcn_s_setprio(3);  // wave-uniform
+  else if (done < q.t2) __builtin_amdgcn_s_setprio(2);
+  else if (done < q.t3) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
@@ -238,8 +245,9 @@ __device__ __forceinline__ void phase_b(const ExpertArgs& a, const Blk<FMT> (&cb
   }
   float y[5];
   int t = wave;
+  const Quarters quarters = quarters_of(s_end);
   auto round = [&](int s0) {
-    if (a.balance) prio_by_progress(s0, s_end);
+    if (a.balance) prio_by_progress(s0, quarters);
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       // The slice's activations are the same for every tile; an opaque zero
@@ -541,8 +549,9 @@ __global__ __launch_bounds__(512, 4) void moe_experts_kernel(ExpertArgs a) {
     float y[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     // whole rounds, then a last round whose steps past nA compute nothing
     const int nAfull = nA / kRing * kRing;
+    const Quarters quarters = quarters_of(total);
     for (int s0 = 0; s0 < nAfull; s0 += kRing) {
-      if (a.balance) prio_by_progress(s0, total);
+      if (a.balance) prio_by_progress(s0, quarters);
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int s = s0 + i;
