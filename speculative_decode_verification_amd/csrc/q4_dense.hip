@@ -157,13 +157,28 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   auto item_weight = [&](int mi) { return MW ? __builtin_amdgcn_readfirstlane((it0 + mi) / a.T) : (int)blockIdx.y; };
   uint4 cbuf[PF], cbuf2[Q8 ? PF : 1];
   uint32_t sbuf[PF];
+  // MW: the loads walk the steps in order, so a cursor (step, group in the
+  // item, the item's tile and weight) advances by one step per load, by
+  // selects, and stops at the last step: no step divides.
+  int ls = 0, lg = 0, lt = item_tile(0), lw = item_weight(0);
   auto issue = [&](int slot, int s) {
-    s = min(s, ns - 1);
-    const int mi = MW ? __builtin_amdgcn_readfirstlane(s / gw) : 0;
-    const int m = item_weight(mi);
-    const uint4* const codes = a.codes[m];
-    const uint32_t* const sbp = a.sb[m];
-    const size_t blk = (size_t)item_tile(mi) * G + gb + (s - mi * gw);
+    const uint4* codes;
+    const uint32_t* sbp;
+    size_t blk;
+    if constexpr (MW) {
+      codes = a.codes[lw];
+      sbp = a.sb[lw];
+      blk = (size_t)lt * G + gb + lg;
+      const bool adv = ls + 1 < ns, wg = adv && lg + 1 == gw, wt = wg && lt + 1 == a.T;
+      ls += adv;
+      lg = wg ? 0 : lg + adv;
+      lt = wt ? 0 : lt + wg;
+      lw += wt;
+    } else {
+      codes = a.codes[blockIdx.y];
+      sbp = a.sb[blockIdx.y];
+      blk = (size_t)t * G + gb + min(s, ns - 1);
+    }
     if constexpr (Q8) {
       cbuf[slot] = load_nt(codes + blk * 128 + lane);  // weights: read once per call
       cbuf2[slot] = load_nt(codes + blk * 128 + 64 + lane);
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
   // ---- cross-wave sum of item mi in wave order, then its epilogue
   float* red = reinterpret_cast<float*>(smem + (MW ? (size_t)nw * a.region : 0));
   const int cols_out = (MODE == SDV_MODE_PLAIN) ? 32 : 16;
-  auto finish = [&](int mi) {
+  auto finish = [&](int tt, int wt) {
     __syncthreads();  // every wave is done with its region (one weight), or with the last weight's sums
     float* myred = red + (size_t)wave * kPassRows * 33;
 #pragma unroll
@@ -289,8 +304,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
       y[i] = 0.0f;
     }
     __syncthreads();
-    float* const out = a.out[item_weight(mi)];
-    const int tt = item_tile(mi);
+    float* const out = a.out[wt];
     for (int q = tid; q < k * cols_out; q += blockDim.x) {
       const int i = q / cols_out, cc = q - i * cols_out;
       float val[2];
@@ -310,16 +324,29 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
       }
     }
   };
-  // group s % gw of item s / gw; rounds before the last refill their slot
-  // after the step, the last does not
+  // step s: group cg of the item with tile ct and weight cw (MW: a cursor
+  // that advances by one step per call; an item's sums are taken after its
+  // last group).  Rounds before the last refill their slot after the step,
+  // the last does not.
+  int cg = 0, ct = item_tile(0), cw = item_weight(0);
   auto gstep = [&](int i, int s) {
-    const int g = MW ? s % gw : s;
+    const int g = MW ? cg : s;
     if constexpr (Q8) {
       group_mac_rows_q8<ACT>(cbuf[i], cbuf2[i], sbuf[i], ap + g * 64, xr, g, y);
     } else {
       group_mac_rows<ACT, FMT>(cbuf[i], sbuf[i], ap + g * 64, xr, g, y, dk);
     }
-    if (MW && g == gw - 1) finish(s / gw);
+    if constexpr (MW) {
+      if (cg + 1 == gw) {
+        finish(ct, cw);
+        cg = 0;
+        const bool wt = ct + 1 == a.T;
+        ct = wt ? 0 : ct + 1;
+        cw += wt;
+      } else {
+        ++cg;
+      }
+    }
   };
   const int nround = (ns + PF - 1) / PF;
   for (int r = 0; r + 1 < nround; ++r) {
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(1024, 1) void q4_dense_k_kernel(DenseArgs a) {
     for (int i = 0; i < PF; ++i)
       if (s0 + i < ns) gstep(i, s0 + i);
   }
-  if (!MW) finish(0);
+  if (!MW) finish(t, (int)blockIdx.y);
 }
 
 // Wide form: bf16 activations, more rows than one narrow pass (up to 32),
