@@ -185,7 +185,10 @@ MULTI_CASES = [("q4", 0, False, 9, 336, 1024, 5), ("q4", 0, True, 5, 336, 1024, 
                # several (tile, weight) items per workgroup (one staging of the rows for all of them)
                ("q4", 0, False, 9, 2560, 5120, 12), ("q4", 1, False, 7, 5120, 1024, 9),
                ("q4", 0, True, 5, 10240, 512, 5), ("q8", 0, False, 9, 2560, 1024, 12),
-               ("q3", 0, False, 9, 2560, 1024, 12)]
+               ("q3", 0, False, 9, 2560, 1024, 12),
+               # K = 1088: 17 groups over 16 waves, so one wave's K range has two
+               # groups and the others one (the step cursors of the several-item form)
+               ("q4", 0, False, 9, 2560, 1088, 12), ("q8", 1, False, 5, 2560, 1088, 12)]
 
 
 @pytest.mark.parametrize("fmt_name,mode,act_f32,k,N,K,nw", MULTI_CASES)
@@ -194,8 +197,9 @@ def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k, N, 
     activation rows: every output equals its own sdv_qmv_k call bit for bit
     (ragged N, the gate/up mode, fp32 rows, 32 rows, Q8_0, Q3, and launches
     whose workgroups take several (tile, weight) items, in shares that differ
-    by one: 2560 x 5120 x 12, 5120 x 1024 x 9, 10240 x 512 x 5), and the first
-    and last weights match the oracle."""
+    by one: 2560 x 5120 x 12, 5120 x 1024 x 9, 10240 x 512 x 5, and K ranges
+    of different lengths: K = 1088), and the first and last weights match the
+    oracle."""
     ops = _ops()
     from speculative_decode_verification_amd.ops import Q3Weight, Q8Weight
     banner(f"qmv multi {fmt_name} mode={mode} f32={act_f32} k={k} N={N} K={K} nw={nw}")
