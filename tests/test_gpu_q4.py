@@ -188,7 +188,11 @@ MULTI_CASES = [("q4", 0, False, 9, 336, 1024, 5), ("q4", 0, True, 5, 336, 1024, 
                ("q3", 0, False, 9, 2560, 1024, 12),
                # K = 1088: 17 groups over 16 waves, so one wave's K range has two
                # groups and the others one (the step cursors of the several-item form)
-               ("q4", 0, False, 9, 2560, 1088, 12), ("q8", 1, False, 5, 2560, 1088, 12)]
+               ("q4", 0, False, 9, 2560, 1088, 12), ("q8", 1, False, 5, 2560, 1088, 12),
+               # 2560 items: ten per workgroup, as in the 16-weight launches of 5120 x 5120
+               ("q4", 0, False, 9, 5120, 1024, 16), ("q4", 0, False, 1, 5120, 1024, 16),
+               ("q4", 1, False, 9, 5120, 1024, 16), ("q8", 0, False, 5, 5120, 1024, 16),
+               ("q3", 0, False, 9, 5120, 1088, 16)]
 
 
 @pytest.mark.parametrize("fmt_name,mode,act_f32,k,N,K,nw", MULTI_CASES)
@@ -198,8 +202,8 @@ def test_multi_weight_launch_equals_single_calls(fmt_name, mode, act_f32, k, N, 
     (ragged N, the gate/up mode, fp32 rows, 32 rows, Q8_0, Q3, and launches
     whose workgroups take several (tile, weight) items, in shares that differ
     by one: 2560 x 5120 x 12, 5120 x 1024 x 9, 10240 x 512 x 5, and K ranges
-    of different lengths: K = 1088), and the first and last weights match the
-    oracle."""
+    of different lengths: K = 1088; ten items per workgroup), and the first
+    and last weights match the oracle."""
     ops = _ops()
     from speculative_decode_verification_amd.ops import Q3Weight, Q8Weight
     banner(f"qmv multi {fmt_name} mode={mode} f32={act_f32} k={k} N={N} K={K} nw={nw}")
